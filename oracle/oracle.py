@@ -1,0 +1,248 @@
+"""ctypes harness around the C oracle (gs_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module; the product path (the HIP library
+and its binding) never does, and this module imports nothing from it.
+
+Everything is float64.  Scene parameters arrive as float32 arrays and are
+widened once; all arithmetic happens in the C oracle in double precision.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "gs_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(force=False):
+    """Compile the oracle with gcc (plain C99, no fused multiply-add contraction)."""
+    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+        return LIB
+    tmp = LIB + ".tmp"
+    subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+                           "-shared", "-Wall", "-o", tmp, SRC, "-lm"])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+class _Cam(C.Structure):
+    _fields_ = [("fx", C.c_double), ("fy", C.c_double), ("cx", C.c_double), ("cy", C.c_double),
+                ("width", C.c_int32), ("height", C.c_int32), ("R", C.c_double * 9), ("t", C.c_double * 3)]
+
+
+class _Set(C.Structure):
+    _fields_ = [("near_z", C.c_double), ("alpha_min", C.c_double), ("alpha_max", C.c_double),
+                ("T_min", C.c_double), ("dilation", C.c_double), ("bg", C.c_double * 3), ("tile", C.c_int32)]
+
+
+@dataclass
+class Settings:
+    near_z: float = 0.2
+    alpha_min: float = 1.0 / 255.0
+    alpha_max: float = 0.99
+    T_min: float = 1e-4
+    dilation: float = 0.3
+    bg: tuple = (0.0, 0.0, 0.0)
+    tile: int = 16
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = C.CDLL(LIB)
+        _lib.orc_bin.restype = C.c_int64
+        _lib.orc_loss.restype = C.c_double
+    return _lib
+
+
+def _p(a, ctype=C.c_double):
+    return a.ctypes.data_as(C.POINTER(ctype))
+
+
+def _d(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def cam_struct(cam):
+    c = _Cam()
+    c.fx, c.fy, c.cx, c.cy = cam.fx, cam.fy, cam.cx, cam.cy
+    c.width, c.height = cam.width, cam.height
+    for i, v in enumerate(np.asarray(cam.R, dtype=np.float64).reshape(-1)):
+        c.R[i] = v
+    for i, v in enumerate(np.asarray(cam.t, dtype=np.float64).reshape(-1)):
+        c.t[i] = v
+    return c
+
+
+def set_struct(s: Settings):
+    o = _Set()
+    o.near_z, o.alpha_min, o.alpha_max, o.T_min, o.dilation = s.near_z, s.alpha_min, s.alpha_max, s.T_min, s.dilation
+    for i in range(3):
+        o.bg[i] = s.bg[i]
+    o.tile = s.tile
+    return o
+
+
+def sh_basis(deg, d):
+    """Real SH values Y[K] and their gradients dY[K,3] at direction d (oracle routine)."""
+    K = (deg + 1) ** 2
+    Y = np.zeros(16)
+    g = np.zeros(48)
+    lib().orc_sh_basis(C.c_int(deg), _p(_d(d)), _p(Y), _p(g))
+    return Y[:K].copy(), g.reshape(16, 3)[:K].copy()
+
+
+def quat_to_rot(q):
+    R = np.zeros(9)
+    lib().orc_quat_to_rot(_p(_d(q)), _p(R))
+    return R.reshape(3, 3)
+
+
+def preprocess(cam, deg, params, s: Settings = None):
+    s = s or Settings()
+    means, ls, qs, op, sh = (_d(params[k]) for k in ("means", "log_scales", "quats", "opacity_logits", "sh"))
+    N = means.shape[0]
+    out = dict(uv=np.zeros((N, 2)), depth=np.zeros(N), conic=np.zeros((N, 3)), cov2d=np.zeros((N, 3)),
+               opacity=np.zeros(N), rgb=np.zeros((N, 3)), clamp=np.zeros(N, np.uint8), ext=np.zeros((N, 2)),
+               rect=np.zeros((N, 4), np.int32), tiles_touched=np.zeros(N, np.int32), valid=np.zeros(N, np.uint8))
+    lib().orc_preprocess(C.byref(cam_struct(cam)), C.byref(set_struct(s)), C.c_int(N), C.c_int(deg),
+                         _p(means), _p(ls), _p(qs), _p(op), _p(sh),
+                         _p(out["uv"]), _p(out["depth"]), _p(out["conic"]), _p(out["cov2d"]), _p(out["opacity"]),
+                         _p(out["rgb"]), _p(out["clamp"], C.c_uint8), _p(out["ext"]), _p(out["rect"], C.c_int),
+                         _p(out["tiles_touched"], C.c_int), _p(out["valid"], C.c_uint8))
+    return out
+
+
+def depth_key(depth):
+    """The sort key is the float32 depth (ties broken by Gaussian index)."""
+    return np.asarray(depth, dtype=np.float32).astype(np.float64)
+
+
+def bin_gaussians(cam, rect, tiles_touched, depth_k, s: Settings = None):
+    s = s or Settings()
+    rect = np.ascontiguousarray(rect, dtype=np.int32)
+    tt = np.ascontiguousarray(tiles_touched, dtype=np.int32)
+    dk = _d(depth_k)
+    N = rect.shape[0]
+    ntx = (cam.width + s.tile - 1) // s.tile
+    nty = (cam.height + s.tile - 1) // s.tile
+    ranges = np.zeros((ntx * nty, 2), np.int64)
+    cap = int(tt.astype(np.int64).sum())
+    pl = np.zeros(max(cap, 1), np.int32)
+    K = lib().orc_bin(C.c_int(N), C.c_int(cam.width), C.c_int(cam.height), C.c_int(s.tile),
+                      _p(rect, C.c_int), _p(tt, C.c_int), _p(dk), _p(pl, C.c_int), C.c_int64(cap),
+                      _p(ranges, C.c_int64))
+    assert K == cap
+    return pl[:K].copy(), ranges
+
+
+def global_list(valid, depth_k):
+    """All non-culled Gaussians in (depth key, index) order: the brute-force list."""
+    idx = np.nonzero(np.asarray(valid) != 0)[0]
+    order = np.lexsort((idx, np.asarray(depth_k)[idx]))
+    pl = idx[order].astype(np.int32)
+    return pl, np.array([[0, len(pl)]], np.int64)
+
+
+def render_fwd(cam, pre, point_list, ranges, s: Settings = None, brute=False, amb_rel=1e-4):
+    s = s or Settings()
+    W, H = cam.width, cam.height
+    out = dict(image=np.zeros((3, H, W)), final_T=np.zeros((H, W)), n_contrib=np.zeros((H, W), np.int32),
+               wsum=np.zeros((H, W)), ambiguous=np.zeros((H, W), np.uint8), hash=np.zeros((H, W), np.uint64),
+               counts=np.zeros(3, np.int64))
+    pl = np.ascontiguousarray(point_list, dtype=np.int32)
+    rg = np.ascontiguousarray(ranges, dtype=np.int64)
+    lib().orc_render_fwd(C.byref(cam_struct(cam)), C.byref(set_struct(s)), C.c_int(1 if brute else 0),
+                         _p(pl, C.c_int), _p(rg, C.c_int64), _p(_d(pre["uv"])), _p(_d(pre["conic"])),
+                         _p(_d(pre["opacity"])), _p(_d(pre["rgb"])), _p(out["image"]), _p(out["final_T"]),
+                         _p(out["n_contrib"], C.c_int), _p(out["wsum"]), _p(out["ambiguous"], C.c_uint8),
+                         C.c_double(amb_rel), _p(out["hash"], C.c_uint64), _p(out["counts"], C.c_int64))
+    return out
+
+
+def render_bwd(cam, pre, point_list, ranges, dL_dimage, s: Settings = None, brute=False):
+    s = s or Settings()
+    N = pre["uv"].shape[0]
+    out = dict(dxy=np.zeros((N, 2)), dconic=np.zeros((N, 3)), dopacity=np.zeros(N), drgb=np.zeros((N, 3)))
+    pl = np.ascontiguousarray(point_list, dtype=np.int32)
+    rg = np.ascontiguousarray(ranges, dtype=np.int64)
+    lib().orc_render_bwd(C.byref(cam_struct(cam)), C.byref(set_struct(s)), C.c_int(1 if brute else 0),
+                         _p(pl, C.c_int), _p(rg, C.c_int64), _p(_d(pre["uv"])), _p(_d(pre["conic"])),
+                         _p(_d(pre["opacity"])), _p(_d(pre["rgb"])), _p(_d(dL_dimage)),
+                         _p(out["dxy"]), _p(out["dconic"]), _p(out["dopacity"]), _p(out["drgb"]), C.c_int(N))
+    return out
+
+
+def preprocess_bwd(cam, deg, params, tiles_touched, g2d, s: Settings = None):
+    s = s or Settings()
+    means, ls, qs, op, sh = (_d(params[k]) for k in ("means", "log_scales", "quats", "opacity_logits", "sh"))
+    N = means.shape[0]
+    K = (deg + 1) ** 2
+    out = dict(means=np.zeros((N, 3)), log_scales=np.zeros((N, 3)), quats=np.zeros((N, 4)),
+               opacity_logits=np.zeros(N), sh=np.zeros((N, K, 3)))
+    tt = np.ascontiguousarray(tiles_touched, dtype=np.int32)
+    lib().orc_preprocess_bwd(C.byref(cam_struct(cam)), C.byref(set_struct(s)), C.c_int(N), C.c_int(deg),
+                             _p(means), _p(ls), _p(qs), _p(op), _p(sh), _p(tt, C.c_int),
+                             _p(_d(g2d["dxy"])), _p(_d(g2d["dconic"])), _p(_d(g2d["dopacity"])),
+                             _p(_d(g2d["drgb"])), _p(out["means"]), _p(out["log_scales"]), _p(out["quats"]),
+                             _p(out["opacity_logits"]), _p(out["sh"]))
+    return out
+
+
+def loss(mode, pred, target):
+    """mode 'l1' or 'l2'; returns (L, dL/dpred)."""
+    pred = _d(pred)
+    g = np.zeros_like(pred)
+    L = lib().orc_loss(C.c_int(1 if mode == "l1" else 2), C.c_int64(pred.size), _p(pred), _p(_d(target)), _p(g))
+    return L, g
+
+
+def densify(tiles_touched, dxy, accum, count):
+    accum = _d(accum).copy()
+    count = np.ascontiguousarray(count, dtype=np.int32).copy()
+    lib().orc_densify(C.c_int(len(accum)), _p(np.ascontiguousarray(tiles_touched, dtype=np.int32), C.c_int),
+                      _p(_d(dxy)), _p(accum), _p(count, C.c_int))
+    return accum, count
+
+
+def adam(p, g, m, v, lr, step, b1=0.9, b2=0.999, eps=1e-8):
+    p, m, v = _d(p).copy(), _d(m).copy(), _d(v).copy()
+    lib().orc_adam(C.c_int64(p.size), _p(p), _p(_d(g)), _p(m), _p(v), C.c_double(lr), C.c_double(b1),
+                   C.c_double(b2), C.c_double(eps), C.c_int(step))
+    return p, m, v
+
+
+def quat_renorm(q):
+    q = _d(q).copy()
+    lib().orc_quat_renorm(C.c_int(q.shape[0]), _p(q))
+    return q
+
+
+def render(cam, deg, params, s: Settings = None, dL_dimage=None, brute=False, amb_rel=1e-4, backward=True):
+    """Full oracle pipeline: preprocess, bin, forward and (optionally) backward."""
+    s = s or Settings()
+    pre = preprocess(cam, deg, params, s)
+    dk = depth_key(pre["depth"])
+    if brute:
+        pl, rg = global_list(pre["valid"], dk)
+    else:
+        pl, rg = bin_gaussians(cam, pre["rect"], pre["tiles_touched"], dk, s)
+    fwd = render_fwd(cam, pre, pl, rg, s, brute=brute, amb_rel=amb_rel)
+    res = dict(pre=pre, point_list=pl, ranges=rg, **fwd)
+    if backward and dL_dimage is not None:
+        g2d = render_bwd(cam, pre, pl, rg, dL_dimage, s, brute=brute)
+        g3d = preprocess_bwd(cam, deg, params, pre["tiles_touched"], g2d, s)
+        res["g2d"] = g2d
+        res["g3d"] = g3d
+    return res
