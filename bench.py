@@ -1,0 +1,266 @@
+"""Benchmark of the differentiable tile rasterizer on one MI355X.
+
+One step = the whole hot path on the 1M-Gaussian 1920x1080 cluster-mixture
+scene: preprocess, binning + depth sort, forward compositing, L1 loss against a
+random target, reverse-walk backward, 2D->3D backward, densification statistic
+and the Adam update of all parameter groups (with quaternion renormalisation).
+Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is Gaussian-pixel blend pairs per second over the
+whole step: (evaluated forward pairs + walked backward pairs) / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd rasterize ms/iter & blend pairs/s, 1M Gaussians @1080p; % roofline"
+PEAK_FP32_TFLOPS = 157.3   # MI355X published fp32 vector peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+# Algorithmic operations per pair, counted from the method's arithmetic (each
+# add, mul, compare, exp and divide is one operation):
+#   evaluate alpha:  d (2), d^T conic d (9), exp (1), opacity*G (1), min (1) = 14
+#   forward blend:   1 - alpha, T(1 - alpha), stop test, w = alpha T, C += w c (6) = 10
+#   backward blend:  T / (1 - alpha) (2), w (1), dL/dc (3), dL/dalpha (9), C_next (6),
+#                    dsigma, dG, dpower (3), dconic (5), dmean2D (8), 9 accumulations = 47
+FLOPS_EVAL, FLOPS_FWD_BLEND, FLOPS_BWD_BLEND = 14, 10, 47
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tile-fraction", type=float, default=1.0)
+    return ap.parse_args()
+
+
+def sha_of(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(kernel, launches_per_step=1):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None when
+    the summary is missing or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_clusters1m_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"source_sha256:\s*(\w+)", text)
+    src = os.path.join(ROOT, "differentiable_gaussian_splatting_dgs_amd", "csrc", "render.hip")
+    if not m_sha or m_sha.group(1) != sha_of(src):
+        return None
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    return float(m_b.group(1)) if m_b else None
+
+
+class Step:
+    """All buffers of the training step; run() enqueues one step on the current stream."""
+
+    def __init__(self, sc):
+        import torch
+        from differentiable_gaussian_splatting_dgs_amd import gs, scenes
+        self.gs, self.torch, self.sc = gs, torch, sc
+        dev = "cuda"
+        self.p = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in sc.params().items()}
+        self.target = torch.from_numpy(sc.target).to(dev)
+        self.rast = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
+        self.dL = torch.empty_like(self.target)
+        self.loss = torch.zeros(1 + gs.LOSS_PARTIALS, dtype=torch.float64, device=dev)
+        self.grads = {k: torch.empty_like(v) for k, v in self.p.items()}
+        self.m = {k: torch.zeros_like(v) for k, v in self.p.items()}
+        self.v = {k: torch.zeros_like(v) for k, v in self.p.items()}
+        self.accum = torch.zeros(sc.n, dtype=torch.float32, device=dev)
+        self.count = torch.zeros(sc.n, dtype=torch.int32, device=dev)
+        lr = scenes.ADAM_LR
+        N = sc.n
+        K = sc.sh.shape[1]
+        spec = [("means", 3, 0, 3, lr["means"], 0), ("log_scales", 3, 0, 3, lr["log_scales"], 0),
+                ("quats", 4, 0, 4, lr["quats"], 1), ("opacity_logits", 1, 0, 1, lr["opacity_logits"], 0),
+                ("sh", 3 * K, 0, 3, lr["sh_dc"], 0), ("sh", 3 * K, 3, 3 * K, lr["sh_rest"], 0)]
+        self.groups = [dict(param=self.p[k], grad=self.grads[k], exp_avg=self.m[k], exp_avg_sq=self.v[k], rows=N,
+                            row_len=rl, col_begin=cb, col_end=ce, normalize_rows=nr, lr=l)
+                       for k, rl, cb, ce, l, nr in spec]
+        self.step_no = 0
+        self.stages = ["preprocess", "bin_sort", "render_fwd", "loss", "render_bwd", "preprocess_bwd", "densify",
+                       "adam"]
+
+    def run(self, events=None, check=False):
+        gs, r, p = self.gs, self.rast, self.p
+        self.step_no += 1
+        ev = events
+
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        r.preprocess(p)
+        mark(1)
+        r.bin()
+        if check and int(r.overflow.item()) != 0:
+            K = int(r.num_keys.item())
+            r._alloc_lists(int(K * 1.25) + 1024)
+            r.bin()
+        mark(2)
+        r.render()
+        mark(3)
+        gs.gs_image_loss("l1", r.image, self.target, self.dL, self.loss)
+        mark(4)
+        r.backward_2d(self.dL)
+        mark(5)
+        gs.gs_preprocess_bwd(r.cam, r.settings, r.deg, p["means"], p["log_scales"], p["quats"],
+                             p["opacity_logits"], p["sh"], r.tiles_touched, r.clamp, r.grad2d, self.grads["means"],
+                             self.grads["log_scales"], self.grads["quats"], self.grads["opacity_logits"],
+                             self.grads["sh"])
+        mark(6)
+        gs.gs_densify_accum(self.sc.n, r.tiles_touched, r.grad2d, self.accum, self.count)
+        mark(7)
+        gs.gs_adam_step(self.groups, 0.9, 0.999, 1e-8, self.step_no)
+        mark(8)
+
+
+def cpu_baseline(sc, frac, seed=0):
+    """The oracle on a bounded sample of the same step, scaled to blend pairs/s.
+
+    Sample: full preprocess and binning of all Gaussians; forward, L1 loss and
+    backward over a random `frac` of the tiles; 2D->3D backward, densification and
+    Adam over the same fraction of the Gaussians.  Each stage's time is scaled by
+    its sampled fraction (pixel stages by pairs, per-Gaussian stages by count)."""
+    from oracle import oracle as O
+    s = O.Settings()
+    params = sc.params()
+    t = {}
+    t0 = time.perf_counter()
+    pre = O.preprocess(sc.cam, sc.sh_degree, params, s)
+    t["preprocess"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    pl, rg = O.bin_gaussians(sc.cam, pre["rect"], pre["tiles_touched"], O.depth_key(pre["depth"]), s)
+    t["bin"] = time.perf_counter() - t0
+    ntiles = rg.shape[0]
+    rng = np.random.default_rng(seed)
+    tmask = np.zeros(ntiles, np.uint8)
+    tmask[rng.permutation(ntiles)[: max(1, int(frac * ntiles))]] = 1
+    t0 = time.perf_counter()
+    fwd = O.render_fwd(sc.cam, pre, pl, rg, s, tile_mask=tmask)
+    t["fwd"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    _, dL = O.loss("l1", fwd["image"], sc.target)
+    t["loss"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    g2 = O.render_bwd(sc.cam, pre, pl, rg, dL, s, tile_mask=tmask)
+    t["bwd"] = time.perf_counter() - t0
+    n_s = max(1, int(frac * sc.n))
+    sub = {k: v[:n_s] for k, v in params.items()}
+    g2s = {k: v[:n_s] for k, v in g2.items()}
+    t0 = time.perf_counter()
+    g3 = O.preprocess_bwd(sc.cam, sc.sh_degree, sub, pre["tiles_touched"][:n_s], g2s, s)
+    t["preprocess_bwd"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.densify(pre["tiles_touched"][:n_s], g2s["dxy"], np.zeros(n_s), np.zeros(n_s, np.int32))
+    for k in ("means", "log_scales", "quats", "opacity_logits", "sh"):
+        O.adam(sub[k], g3[k], np.zeros(sub[k].shape), np.zeros(sub[k].shape), 1e-3, 1)
+    O.quat_renorm(sub["quats"])
+    t["densify_adam"] = time.perf_counter() - t0
+    pairs_sample = int(fwd["counts"][0] + fwd["counts"][1])
+    # fraction of the full step's pairs covered by the tile sample
+    pix_frac = float(tmask.mean())
+    est = (t["preprocess"] + t["bin"] + (t["fwd"] + t["bwd"]) / pix_frac + t["loss"]
+           + (t["preprocess_bwd"] + t["densify_adam"]) * sc.n / n_s)
+    work = sum(t.values())
+    return dict(est_step_s=est, work_s=work, pairs_sample=pairs_sample, tile_fraction=pix_frac,
+                gauss_fraction=n_s / sc.n, stage_s={k: round(v, 3) for k, v in t.items()})
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on a single "
+              "MI355X; see DESIGN.md for how the path would shard).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from differentiable_gaussian_splatting_dgs_amd import scenes
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    t_gen = time.time()
+    sc = scenes.training1m()
+    print(f"# scene {sc.name}: n={sc.n} {sc.cam.width}x{sc.cam.height} ({time.time() - t_gen:.1f}s)", file=sys.stderr,
+          flush=True)
+    st = Step(sc)
+    torch.cuda.synchronize()
+    st.run(check=True)             # sizes the list capacity
+    for _ in range(max(0, args.warmup - 1)):
+        st.run()
+    torch.cuda.synchronize()
+    c0 = st.rast.count_pairs().cpu().numpy()
+    nst = len(st.stages)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st.run(events=evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert int(st.rast.overflow.item()) == 0, "list capacity overflow during timing"
+    c1 = st.rast.count_pairs().cpu().numpy()
+    torch.cuda.synchronize()
+    stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+                for j, name in enumerate(st.stages)}
+    ms = elapsed * 1e3 / args.steps
+    counts = (c0.astype(np.float64) + c1) / 2
+    p_fwd, p_bwd, p_blend = counts
+    pairs = p_fwd + p_bwd
+    value = pairs / (ms * 1e-3)
+    raster_ms = sum(stage_ms[k] for k in ("preprocess", "bin_sort", "render_fwd", "render_bwd", "preprocess_bwd"))
+
+    # roofline of the dominant kernel (render_bwd: FP32 VALU bound)
+    dom = max(("render_fwd", "render_bwd"), key=lambda k: stage_ms[k])
+    if dom == "render_bwd":
+        flops = FLOPS_EVAL * p_bwd + FLOPS_BWD_BLEND * p_blend
+    else:
+        flops = FLOPS_EVAL * p_fwd + FLOPS_FWD_BLEND * p_blend
+    # the render_bwd stage also holds the 48 MB gradient clear; time the kernel alone from the stage
+    achieved = flops / (stage_ms[dom] * 1e-3) / 1e12
+    traffic = read_traffic(dom)
+    roof = dict(kernel=dom, bound="alu", achieved=round(achieved, 3), peak=PEAK_FP32_TFLOPS, unit="TFLOP/s",
+                frac=round(achieved / PEAK_FP32_TFLOPS, 4), traffic=traffic,
+                flops_per_launch=float(flops), launch_ms=round(stage_ms[dom], 4))
+
+    out = dict(metric=METRIC, value=float(value), unit="blend pairs/s", n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="f32", data="synthetic",
+               config=dict(workload="train1m: 1M Gaussians, 1920x1080, SH3, cluster-mixture scene; "
+                                    "fwd + L1 + bwd + densify stat + Adam",
+                           gaussians=sc.n, width=sc.cam.width, height=sc.cam.height, sh_degree=sc.sh_degree,
+                           tile=16, parallelism="single-gpu"),
+               fwd_bwd_ms=round(raster_ms, 4), stage_ms={k: round(v, 4) for k, v in stage_ms.items()},
+               pairs=dict(fwd_evaluated=float(p_fwd), bwd_walked=float(p_bwd), blended=float(p_blend),
+                          keys=int(st.rast.num_keys.item())),
+               roofline=roof)
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        cb = cpu_baseline(sc, args.cpu_tile_fraction)
+        out["cpu_baseline"] = dict(value=float(pairs / cb["est_step_s"]), unit="blend pairs/s", cores=1,
+                                   kind="oracle",
+                                   sample=(f"float64 C oracle, single thread, {platform.processor() or 'x86_64'}: "
+                                           f"full preprocess+binning, fwd/L1/bwd over {cb['tile_fraction']:.0%} of "
+                                           f"tiles, 2D->3D bwd/densify/Adam over {cb['gauss_fraction']:.0%} of "
+                                           f"Gaussians; {cb['work_s']:.1f}s of work, stage times scaled to the "
+                                           f"full step ({cb['est_step_s']:.1f}s)"),
+                                   stage_s=cb["stage_s"])
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,476 @@
+// Tile binning and per-tile depth order.
+//
+// Method sources: 3DGS training notes (huajishe), section E.3 (cull against
+// tiles with an AABB, sort by depth inside each tile, tiles independent);
+// Gaussian Splatting backward CUDA page (lshu.cn), sections 1 and 5 (the
+// sorted list and the tile ranges are reused by the backward).
+//
+// The required order is (tile, float32 depth, Gaussian index).  Instead of
+// one radix sort over 64-bit (tile | depth) keys for every (tile, Gaussian)
+// pair, the work is split so the wide key is sorted over N items and only
+// the narrow tile id over K items:
+//   1. depth keys: key = float32 depth bits (visible) or 0xffffffff, val = index;
+//      digit histograms for the 4 depth passes.
+//   2. LSD onesweep radix sort of (depth key, index) over N, 4 x 8-bit passes.
+//      Stable, so equal depths stay in index order.
+//   3. emit: an exclusive scan of tiles_touched in depth order (decoupled
+//      look-back) fused with writing (tile id, Gaussian) for every tile of
+//      every Gaussian, plus the tile-digit histograms.
+//   4. LSD onesweep radix sort of (tile id, Gaussian) over K, 1-2 x 8-bit passes.
+//      Stable, so each tile keeps the depth order of step 2.
+//   5. tile ranges from the sorted tile ids.
+// The onesweep pass (one kernel per digit: stable wave-level ranking by
+// ballot matching, then decoupled look-back across partitions for the digit
+// offsets) follows Adinets and Merrill, "Onesweep" (2022), with partitions
+// claimed from an atomic ticket so look-back only waits on running blocks.
+#include "gs_internal.h"
+
+namespace gs {
+namespace {
+
+constexpr int kSortThreads = 256;
+constexpr int kSortIPT = 8;
+constexpr int kSortPart = kSortThreads * kSortIPT;  // 2048 items per partition
+constexpr int kRadix = 256;
+constexpr uint32_t kFlagAgg = 1u << 30;
+constexpr uint32_t kFlagInc = 2u << 30;
+constexpr uint32_t kValMask = (1u << 30) - 1u;
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+constexpr int kEmitThreads = 256;
+constexpr int kEmitIPT = 4;
+constexpr int kEmitPart = kEmitThreads * kEmitIPT;  // 1024 Gaussians per partition
+
+__device__ inline uint32_t ld_acquire(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_release(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint64_t lanemask_lt() {
+    const uint32_t lane = threadIdx.x & 63;
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Workspace layout (all offsets 256-byte aligned).
+struct Layout {
+    size_t hist;        // uint32 [4 depth digits + 2 tile digits][256]
+    size_t tickets;     // uint32 [8]
+    size_t err;         // uint32 [1] look-back spin-limit flag
+    size_t dstatus;     // uint32 [4][dparts][256]
+    size_t estatus;     // uint32 [eparts]
+    size_t tstatus;     // uint32 [2][tparts][256]
+    size_t zero_end;    // everything above is zeroed per call
+    size_t dkeys0, dvals0, dkeys1, dvals1;  // uint32 [n] each
+    size_t tkeys0, tkeys1, tvals0;          // uint32 [cap] each
+    size_t total;
+    uint32_t dparts, eparts, tparts;
+};
+
+inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline Layout make_layout(int32_t n, int64_t cap) {
+    Layout L;
+    L.dparts = (uint32_t)((n + kSortPart - 1) / kSortPart);
+    L.eparts = (uint32_t)((n + kEmitPart - 1) / kEmitPart);
+    L.tparts = (uint32_t)((cap + kSortPart - 1) / kSortPart);
+    size_t o = 0;
+    L.hist = o; o = up256(o + 6 * kRadix * 4);
+    L.tickets = o; o = up256(o + 8 * 4);
+    L.err = o; o = up256(o + 4);
+    L.dstatus = o; o = up256(o + (size_t)4 * L.dparts * kRadix * 4);
+    L.estatus = o; o = up256(o + (size_t)L.eparts * 4);
+    L.tstatus = o; o = up256(o + (size_t)2 * L.tparts * kRadix * 4);
+    L.zero_end = o;
+    L.dkeys0 = o; o = up256(o + (size_t)n * 4);
+    L.dvals0 = o; o = up256(o + (size_t)n * 4);
+    L.dkeys1 = o; o = up256(o + (size_t)n * 4);
+    L.dvals1 = o; o = up256(o + (size_t)n * 4);
+    L.tkeys0 = o; o = up256(o + (size_t)cap * 4);
+    L.tkeys1 = o; o = up256(o + (size_t)cap * 4);
+    L.tvals0 = o; o = up256(o + (size_t)cap * 4);
+    L.total = o;
+    return L;
+}
+
+__global__ void k_zero_u32(uint32_t* p, size_t count) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < count; i += stride) p[i] = 0u;
+}
+
+// 1. depth keys + histograms of the 4 depth digits
+__global__ __launch_bounds__(256) void k_depth_keys(int32_t n, const float* depth, const int32_t* tt,
+                                                    uint32_t* keys, uint32_t* vals, uint32_t* hist) {
+    __shared__ uint32_t sh[4 * kRadix];
+    for (int i = threadIdx.x; i < 4 * kRadix; i += blockDim.x) sh[i] = 0;
+    __syncthreads();
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const uint32_t k = tt[i] > 0 ? __float_as_uint(depth[i]) : 0xffffffffu;
+        keys[i] = k;
+        vals[i] = (uint32_t)i;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) atomicAdd(&sh[d * kRadix + ((k >> (8 * d)) & 255u)], 1u);
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < 4 * kRadix; b += blockDim.x)
+        if (sh[b]) atomicAdd(&hist[b], sh[b]);
+}
+
+struct PassArgs {
+    const uint32_t* keys_in;
+    const uint32_t* vals_in;
+    uint32_t* keys_out;  // may be null: keys not needed after this pass
+    uint32_t* vals_out;
+    const uint32_t* count_dev;  // items = min(*count_dev, cap) when non-null, else count_host
+    uint32_t count_host;
+    uint32_t cap;
+    const uint32_t* hist;  // [256] this digit over all items
+    uint32_t* status;      // [parts][256], zeroed
+    uint32_t* ticket;      // zeroed
+    uint32_t* err;
+    int shift;
+};
+
+// 2/4. one onesweep pass over 8 bits of a 32-bit key.
+__global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
+    __shared__ uint32_t s_off[kRadix];          // global exclusive digit offsets
+    __shared__ uint32_t s_wave[4][kRadix];      // per-wave digit counts -> prefixes
+    __shared__ uint32_t s_base[kRadix];         // digit offset of this partition
+    __shared__ uint32_t s_part;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    if (tid == 0) s_part = atomicAdd(p.ticket, 1u);
+    for (int i = tid; i < 4 * kRadix; i += kSortThreads) (&s_wave[0][0])[i] = 0;
+    // exclusive scan of the digit histogram (256 entries, one per thread)
+    {
+        uint32_t h = p.hist[tid];
+        uint32_t x = h;
+        // wave inclusive scan by shuffles
+        for (int o = 1; o < 64; o <<= 1) {
+            uint32_t y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        __shared__ uint32_t s_wsum[4];
+        if (lane == 63) s_wsum[wave] = x;
+        __syncthreads();
+        uint32_t add = 0;
+        for (int w = 0; w < wave; ++w) add += s_wsum[w];
+        s_off[tid] = x - h + add;
+    }
+    __syncthreads();
+    const uint32_t part = s_part;
+    uint32_t count = p.count_dev ? *p.count_dev : p.count_host;
+    if (count > p.cap) count = p.cap;
+    const uint32_t nparts = (count + kSortPart - 1) / kSortPart;
+    if (part >= nparts) return;
+
+    // load: wave w owns [part*P + w*64*IPT, +64*IPT), item i of lane l at + i*64 + l
+    const uint32_t base = part * kSortPart + wave * 64 * kSortIPT;
+    uint32_t key[kSortIPT], val[kSortIPT], rank[kSortIPT];
+#pragma unroll
+    for (int i = 0; i < kSortIPT; ++i) {
+        const uint32_t idx = base + i * 64 + lane;
+        if (idx < count) {
+            key[i] = p.keys_in[idx];
+            val[i] = p.vals_in[idx];
+        } else {
+            key[i] = 0u;
+            val[i] = 0xffffffffu;  // marks padding
+        }
+    }
+    const uint64_t lt = lanemask_lt();
+#pragma unroll
+    for (int i = 0; i < kSortIPT; ++i) {
+        const bool valid = (base + i * 64 + lane) < count;
+        const uint32_t d = (key[i] >> p.shift) & 255u;
+        uint64_t m = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint64_t bb = __ballot((d >> b) & 1u);
+            m &= ((d >> b) & 1u) ? bb : ~bb;
+        }
+        const uint32_t below = (uint32_t)__popcll(m & lt);
+        const uint32_t prev = valid ? s_wave[wave][d] : 0u;
+        rank[i] = prev + below;
+        __builtin_amdgcn_wave_barrier();
+        if (valid && below == 0) s_wave[wave][d] = prev + (uint32_t)__popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    // per digit: prefix over waves, block total, look-back over partitions
+    {
+        const int d = tid;
+        const uint32_t c0 = s_wave[0][d], c1 = s_wave[1][d], c2 = s_wave[2][d], c3 = s_wave[3][d];
+        const uint32_t total = c0 + c1 + c2 + c3;
+        s_wave[0][d] = 0; s_wave[1][d] = c0; s_wave[2][d] = c0 + c1; s_wave[3][d] = c0 + c1 + c2;
+        uint32_t* st = p.status + (size_t)part * kRadix + d;
+        uint32_t prefix = 0;
+        if (part == 0) {
+            st_release(st, kFlagInc | total);
+        } else {
+            st_release(st, kFlagAgg | total);
+            int j = (int)part - 1;
+            uint32_t spins = 0;
+            while (j >= 0) {
+                const uint32_t s = ld_acquire(p.status + (size_t)j * kRadix + d);
+                if ((s & ~kValMask) == 0u) {
+                    if (++spins > kSpinLimit) { atomicOr(p.err, 1u); break; }
+                    __builtin_amdgcn_s_sleep(1);
+                    continue;
+                }
+                prefix += s & kValMask;
+                if (s & kFlagInc) break;
+                --j;
+            }
+            st_release(st, kFlagInc | ((prefix + total) & kValMask));
+        }
+        s_base[d] = s_off[d] + prefix;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSortIPT; ++i) {
+        const uint32_t idx = base + i * 64 + lane;
+        if (idx < count) {
+            const uint32_t d = (key[i] >> p.shift) & 255u;
+            const uint32_t pos = s_base[d] + s_wave[wave][d] + rank[i];
+            if (pos < count) {  // always true for a consistent histogram; guards the buffers
+                if (p.keys_out) p.keys_out[pos] = key[i];
+                p.vals_out[pos] = val[i];
+            }
+        }
+    }
+}
+
+struct EmitArgs {
+    int32_t n;
+    int32_t tiles_x;
+    uint32_t cap;
+    const uint32_t* order;   // Gaussians in depth order
+    const int16_t* rect;
+    const int32_t* tt;
+    uint32_t* tkeys;         // [cap] tile id
+    uint32_t* tvals;         // [cap] Gaussian
+    uint32_t* status;        // [eparts], zeroed
+    uint32_t* ticket;        // zeroed
+    uint32_t* hist;          // [2][256] tile digits
+    uint32_t* num_keys;
+    uint32_t* overflow;
+    uint32_t* err;
+};
+
+// 3. scan of tiles_touched in depth order + emit of (tile, Gaussian) pairs.
+__global__ __launch_bounds__(kEmitThreads) void k_emit(EmitArgs a) {
+    __shared__ uint32_t s_hist[2 * kRadix];
+    __shared__ uint32_t s_wsum[4];
+    __shared__ uint32_t s_prefix;
+    __shared__ uint32_t s_part;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) s_part = atomicAdd(a.ticket, 1u);
+    for (int i = tid; i < 2 * kRadix; i += kEmitThreads) s_hist[i] = 0;
+    __syncthreads();
+    const uint32_t part = s_part;
+    const int64_t j0 = (int64_t)part * kEmitPart + tid * kEmitIPT;
+    uint32_t g[kEmitIPT], cnt[kEmitIPT], tsum = 0;
+#pragma unroll
+    for (int k = 0; k < kEmitIPT; ++k) {
+        const int64_t j = j0 + k;
+        g[k] = j < a.n ? a.order[j] : 0xffffffffu;
+        cnt[k] = (g[k] < (uint32_t)a.n) ? (uint32_t)max(a.tt[g[k]], 0) : 0u;
+        tsum += cnt[k];
+    }
+    // block exclusive scan of the per-thread sums
+    uint32_t x = tsum;
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wsum[wave] = x;
+    __syncthreads();
+    uint32_t wadd = 0, btotal = 0;
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave) wadd += s_wsum[w];
+        btotal += s_wsum[w];
+    }
+    uint32_t excl = x - tsum + wadd;
+    // decoupled look-back for the partition prefix
+    if (tid == 0) {
+        uint32_t prefix = 0;
+        uint32_t* st = a.status + part;
+        if (part == 0) {
+            st_release(st, kFlagInc | btotal);
+        } else {
+            st_release(st, kFlagAgg | btotal);
+            int j = (int)part - 1;
+            uint32_t spins = 0;
+            while (j >= 0) {
+                const uint32_t s = ld_acquire(a.status + j);
+                if ((s & ~kValMask) == 0u) {
+                    if (++spins > kSpinLimit) { atomicOr(a.err, 1u); break; }
+                    __builtin_amdgcn_s_sleep(1);
+                    continue;
+                }
+                prefix += s & kValMask;
+                if (s & kFlagInc) break;
+                --j;
+            }
+            st_release(st, kFlagInc | ((prefix + btotal) & kValMask));
+        }
+        s_prefix = prefix;
+        const uint32_t nparts = (uint32_t)((a.n + kEmitPart - 1) / kEmitPart);
+        if (part == nparts - 1) {
+            const uint32_t K = prefix + btotal;
+            *a.num_keys = K;
+            *a.overflow = K > a.cap ? 1u : 0u;
+        }
+    }
+    __syncthreads();
+    uint32_t off = s_prefix + excl;
+#pragma unroll
+    for (int k = 0; k < kEmitIPT; ++k) {
+        if (cnt[k] == 0) continue;
+        const uint2 r = reinterpret_cast<const uint2*>(a.rect)[g[k]];
+        const int x0 = (int)(int16_t)(r.x & 0xffffu), y0 = (int)(int16_t)(r.x >> 16);
+        const int x1 = (int)(int16_t)(r.y & 0xffffu), y1 = (int)(int16_t)(r.y >> 16);
+        for (int ty = y0; ty < y1; ++ty)
+            for (int tx = x0; tx < x1; ++tx) {
+                const uint32_t tile = (uint32_t)(ty * a.tiles_x + tx);
+                if (off < a.cap) {
+                    a.tkeys[off] = tile;
+                    a.tvals[off] = g[k];
+                    atomicAdd(&s_hist[tile & 255u], 1u);
+                    atomicAdd(&s_hist[kRadix + ((tile >> 8) & 255u)], 1u);
+                }
+                ++off;
+            }
+    }
+    __syncthreads();
+    for (int b = tid; b < 2 * kRadix; b += kEmitThreads)
+        if (s_hist[b]) atomicAdd(&a.hist[b], s_hist[b]);
+}
+
+// 5. tile ranges from sorted tile ids (ranges zeroed beforehand).
+__global__ void k_ranges(const uint32_t* tkeys, const uint32_t* num_keys, uint32_t cap,
+                         const uint32_t* overflow, uint32_t* ranges, uint32_t ntiles) {
+    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (*overflow) return;
+    const uint32_t K = min(*num_keys, cap);
+    if (k >= K) return;
+    const uint32_t t = tkeys[k];
+    if (t >= ntiles) return;
+    if (k == 0 || tkeys[k - 1] != t) ranges[2 * t] = k;
+    if (k == K - 1 || tkeys[k + 1] != t) ranges[2 * t + 1] = k + 1;
+}
+
+__global__ void k_keys(const uint32_t* ranges, const uint32_t* list, const float* depth, uint64_t* keys,
+                       int ntiles) {
+    const int t = blockIdx.x;
+    if (t >= ntiles) return;
+    const uint32_t b = ranges[2 * t], e = ranges[2 * t + 1];
+    for (uint32_t k = b + threadIdx.x; k < e; k += blockDim.x)
+        keys[k] = ((uint64_t)t << 32) | (uint64_t)__float_as_uint(depth[list[k]]);  // list entries < n by construction
+}
+
+}  // namespace
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" int gs_bin_workspace_size(int32_t n, const gs_camera* cam, int64_t key_capacity, size_t* bytes) {
+    if (n < 0 || !camera_ok(cam) || key_capacity < 0 || !bytes) return GS_EINVAL;
+    if (key_capacity > (int64_t)kValMask) return GS_ECAPACITY;
+    *bytes = make_layout(n, key_capacity).total;
+    return GS_OK;
+}
+
+extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, const int16_t* rect,
+                           const int32_t* tiles_touched, int64_t key_capacity, uint32_t* point_list,
+                           uint32_t* tile_ranges, uint32_t* num_keys_dev, uint32_t* overflow_dev,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 0 || !camera_ok(cam) || key_capacity < 0) return GS_EINVAL;
+    if (key_capacity > (int64_t)kValMask || n > (int32_t)kValMask) return GS_ECAPACITY;
+    if (!tile_ranges || !num_keys_dev || !overflow_dev || !workspace) return GS_EINVAL;
+    if (n > 0 && (!depth || !rect || !tiles_touched)) return GS_EINVAL;
+    if (key_capacity > 0 && !point_list) return GS_EINVAL;
+    if (!aligned16(rect) || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GS_EALIGN;
+    const Layout L = make_layout(n, key_capacity);
+    if (workspace_bytes < L.total) return GS_EWORKSPACE;
+    const int ntiles = tiles_x(cam) * tiles_y(cam);
+    const int tile_passes = ntiles <= 256 ? 1 : (ntiles <= 65536 ? 2 : 3);
+    if (tile_passes > 2) return GS_ECAPACITY;
+    hipStream_t s = as_stream(stream);
+    char* ws = static_cast<char*>(workspace);
+    auto U = [&](size_t off) { return reinterpret_cast<uint32_t*>(ws + off); };
+
+    // zero counters, histograms, look-back status, ranges, K and the overflow flag
+    hipLaunchKernelGGL(k_zero_u32, dim3(1024), dim3(256), 0, s, U(0), L.zero_end / 4);
+    hipLaunchKernelGGL(k_zero_u32, dim3((2 * ntiles + 255) / 256), dim3(256), 0, s, tile_ranges,
+                       (size_t)2 * ntiles);
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, num_keys_dev, (size_t)1);
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, overflow_dev, (size_t)1);
+    if (n == 0) return launch_status();
+
+    uint32_t* hist = U(L.hist);
+    uint32_t* tickets = U(L.tickets);
+    uint32_t* err = U(L.err);
+    hipLaunchKernelGGL(k_depth_keys, dim3((n + 255) / 256), dim3(256), 0, s, n, depth, tiles_touched,
+                       U(L.dkeys0), U(L.dvals0), hist);
+    // depth sort: 4 passes, 0 -> 1 -> 0 -> 1 -> 0
+    uint32_t* dk[2] = {U(L.dkeys0), U(L.dkeys1)};
+    uint32_t* dv[2] = {U(L.dvals0), U(L.dvals1)};
+    for (int pass = 0; pass < 4; ++pass) {
+        PassArgs p;
+        p.keys_in = dk[pass & 1]; p.vals_in = dv[pass & 1];
+        p.keys_out = pass < 3 ? dk[(pass + 1) & 1] : nullptr;
+        p.vals_out = dv[(pass + 1) & 1];
+        p.count_dev = nullptr; p.count_host = (uint32_t)n; p.cap = (uint32_t)n;
+        p.hist = hist + pass * kRadix;
+        p.status = U(L.dstatus) + (size_t)pass * L.dparts * kRadix;
+        p.ticket = tickets + pass;
+        p.err = err;
+        p.shift = 8 * pass;
+        hipLaunchKernelGGL(k_onesweep, dim3(L.dparts), dim3(kSortThreads), 0, s, p);
+    }
+    // emit (tile, Gaussian) pairs in depth order, then the stable tile sort.
+    // Buffers are routed so the final values land in point_list:
+    //   1 pass : emit -> (tkeys0, tvals0) -> (tkeys1, point_list)
+    //   2 passes: emit -> (tkeys0, point_list) -> (tkeys1, tvals0) -> (tkeys0, point_list)
+    EmitArgs e;
+    e.n = n; e.tiles_x = tiles_x(cam); e.cap = (uint32_t)key_capacity;
+    e.order = dv[0]; e.rect = rect; e.tt = tiles_touched;
+    e.tkeys = U(L.tkeys0); e.tvals = tile_passes == 1 ? U(L.tvals0) : point_list;
+    e.status = U(L.estatus); e.ticket = tickets + 4; e.hist = hist + 4 * kRadix;
+    e.num_keys = num_keys_dev; e.overflow = overflow_dev; e.err = err;
+    hipLaunchKernelGGL(k_emit, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
+    if (key_capacity == 0) return launch_status();
+    PassArgs p;
+    p.count_dev = num_keys_dev; p.count_host = 0; p.cap = (uint32_t)key_capacity; p.err = err;
+    p.keys_in = U(L.tkeys0); p.vals_in = e.tvals;
+    p.keys_out = U(L.tkeys1); p.vals_out = tile_passes == 1 ? point_list : U(L.tvals0);
+    p.hist = hist + 4 * kRadix; p.status = U(L.tstatus); p.ticket = tickets + 5; p.shift = 0;
+    hipLaunchKernelGGL(k_onesweep, dim3(L.tparts), dim3(kSortThreads), 0, s, p);
+    const uint32_t* tk_final = U(L.tkeys1);
+    if (tile_passes == 2) {
+        PassArgs p2 = p;
+        p2.keys_in = U(L.tkeys1); p2.vals_in = U(L.tvals0);
+        p2.keys_out = U(L.tkeys0); p2.vals_out = point_list;
+        p2.hist = hist + 5 * kRadix; p2.status = U(L.tstatus) + (size_t)L.tparts * kRadix;
+        p2.ticket = tickets + 6; p2.shift = 8;
+        hipLaunchKernelGGL(k_onesweep, dim3(L.tparts), dim3(kSortThreads), 0, s, p2);
+        tk_final = U(L.tkeys0);
+    }
+    hipLaunchKernelGGL(k_ranges, dim3((uint32_t)((key_capacity + 255) / 256)), dim3(256), 0, s, tk_final,
+                       num_keys_dev, (uint32_t)key_capacity, overflow_dev, tile_ranges, (uint32_t)ntiles);
+    return launch_status();
+}
+
+extern "C" int gs_bin_keys(const gs_camera* cam, const uint32_t* tile_ranges, const uint32_t* point_list,
+                           const float* depth, uint64_t* keys, void* stream) {
+    if (!camera_ok(cam) || !tile_ranges || !point_list || !depth || !keys) return GS_EINVAL;
+    const int ntiles = tiles_x(cam) * tiles_y(cam);
+    hipLaunchKernelGGL(k_keys, dim3(ntiles), dim3(256), 0, as_stream(stream), tile_ranges, point_list, depth,
+                       keys, ntiles);
+    return launch_status();
+}

@@ -1,0 +1,74 @@
+// Internal helpers of the HIP rasterizer library (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gs.h"
+
+namespace gs {
+
+constexpr int kTile = GS_TILE;                 // 16 x 16 pixel tiles
+constexpr int kBlock = kTile * kTile;          // one workgroup per tile: 4 wave64
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int launch_status() { return hipGetLastError() == hipSuccess ? GS_OK : GS_EHIP; }
+
+inline bool camera_ok(const gs_camera* c) {
+    return c && c->width > 0 && c->height > 0 && c->width <= 32768 && c->height <= 32768 && c->fx > 0 &&
+           c->fy > 0;
+}
+
+inline int tiles_x(const gs_camera* c) { return (c->width + kTile - 1) / kTile; }
+inline int tiles_y(const gs_camera* c) { return (c->height + kTile - 1) / kTile; }
+
+// Camera and settings as plain kernel arguments.
+struct CamArgs {
+    double fx, fy, cx, cy;
+    double R[9];
+    double t[3];
+    int32_t width, height;
+};
+
+inline CamArgs cam_args(const gs_camera* c) {
+    CamArgs a;
+    a.fx = c->fx; a.fy = c->fy; a.cx = c->cx; a.cy = c->cy;
+    for (int i = 0; i < 9; ++i) a.R[i] = c->R[i];
+    for (int i = 0; i < 3; ++i) a.t[i] = c->t[i];
+    a.width = c->width; a.height = c->height;
+    return a;
+}
+
+// Blend-side constants in float32 (the precision the blend decides in).
+struct BlendArgs {
+    float alpha_min, alpha_max, T_min;
+    float bg[3];
+    int32_t width, height, tiles_x, tiles_y;
+};
+
+inline BlendArgs blend_args(const gs_camera* c, const gs_settings* s) {
+    BlendArgs b;
+    b.alpha_min = (float)s->alpha_min;
+    b.alpha_max = (float)s->alpha_max;
+    b.T_min = (float)s->T_min;
+    for (int i = 0; i < 3; ++i) b.bg[i] = (float)s->bg[i];
+    b.width = c->width; b.height = c->height;
+    b.tiles_x = tiles_x(c); b.tiles_y = tiles_y(c);
+    return b;
+}
+
+// Blocks are dealt to the 8 XCDs round robin; give each XCD a contiguous
+// band of tiles so neighbouring tiles (which share Gaussians) meet in one L2.
+__device__ inline int xcd_tile(int block, int ntiles) {
+    const int per = (ntiles + 7) / 8;
+    const int xcd = block & 7, slot = block >> 3;
+    const int t = xcd * per + slot;
+    return t;  // may be >= ntiles for the last XCD; caller checks
+}
+
+}  // namespace gs

@@ -1,0 +1,480 @@
+// Forward compositing and reverse-walk backward of the tile rasterizer.
+//
+// Method sources: chain-rule gradients page (qqiyuan.cn), compositing
+// equation I = sum_i alpha_i c_i prod_{j<i} (1 - alpha_j); Gaussian Splatting
+// backward CUDA page (lshu.cn), section 2 (alpha = min(0.99, opacity G), the
+// recursion C_i = alpha_i c_i + (1 - alpha_i) C_{i+1} and the table of 2D
+// gradients), section 3 (per-tile blocks, Gaussians staged in shared memory in
+// batches, the reverse walk starting from the stored final transmittance and
+// the last contributor, atomic accumulation), section 5 (merging the atomic
+// updates of neighbouring pixels).
+//
+// Layout on CDNA4: one 256-lane workgroup per 16x16 tile, four wave64 each
+// owning an 8x8 quadrant.  A batch of up to 256 list entries is staged in LDS
+// (tile-relative mean, conic Cholesky factor, opacity, colour).  While staging,
+// each entry's alpha >= alpha_min bounding box (slightly enlarged) is tested
+// against the four quadrants; each wave then walks only the entries that can
+// reach its quadrant, in list order.  Entries it drops have alpha < alpha_min
+// at every pixel of the quadrant and would be skipped anyway, so the result is
+// that of walking the whole list.
+//
+// Gaussian evaluation: with e = L^T d, L the scaled Cholesky factor of the
+// conic, G = exp2(-|e|^2) = exp(-d^T conic d / 2).  The factor form keeps the
+// float32 rounding error of the exponent proportional to sqrt(condition) of the
+// 2D covariance instead of its condition number, and the tile-relative mean
+// (float32 mean + float32 residual, less the tile origin) keeps the pixel
+// offset d accurate at 4K.
+#include "gs_internal.h"
+
+namespace gs {
+namespace {
+
+struct RenderArgs {
+    BlendArgs b;
+    uint32_t n;
+    const uint32_t* ranges;
+    const uint32_t* list;
+    const float* splats;
+    float* image;
+    float* final_T;
+    int32_t* n_contrib;
+    const float* dL_dimage;
+    float* grad2d;
+};
+
+// The alpha of one (pixel, Gaussian) pair.  Shared verbatim by the forward,
+// the backward and the pair counter so all three take identical decisions.
+struct Pair {
+    float dx, dy, e1, e2, G, sG, alpha;
+};
+
+__device__ __forceinline__ Pair eval_pair(float fx, float fy, float4 g0, float4 g1, float amax) {
+#pragma clang fp contract(off)
+    Pair p;
+    p.dx = fx - g0.x;
+    p.dy = fy - g0.y;
+    p.e1 = __builtin_fmaf(g0.z, p.dx, g0.w * p.dy);
+    p.e2 = g1.x * p.dy;
+    const float q = __builtin_fmaf(p.e1, p.e1, p.e2 * p.e2);
+    p.G = __builtin_amdgcn_exp2f(-q);
+    p.sG = g1.y * p.G;
+    p.alpha = fminf(amax, p.sG);
+    return p;
+}
+
+// Stage list entry k of the tile into LDS slot `slot`; returns the quadrant mask.
+struct Stage {
+    float4* g0;
+    float4* g1;
+    float* g2;
+};
+
+__device__ __forceinline__ uint32_t stage_entry(const RenderArgs& a, uint32_t g, float x0, float y0,
+                                                float inv_amin, Stage st, int slot) {
+    const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
+    const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
+    const float ut = (r0.x - x0) + r0.z;
+    const float vt = (r0.y - y0) + r0.w;
+    st.g0[slot] = make_float4(ut, vt, r1.x, r1.y);
+    st.g1[slot] = make_float4(r1.z, r1.w, r2.x, r2.y);
+    st.g2[slot] = r2.z;
+    // |L^T d|^2 <= k2 = log2(opacity / alpha_min): bounding box of that ellipse
+    const float k2 = fmaxf(__log2f(r1.w * inv_amin), 0.f);
+    const float l00 = r1.x, l10 = r1.y, l11 = r1.z;
+    const float sk = sqrtf(k2);
+    float ey = sk / l11;
+    float ex = sk * sqrtf(l10 * l10 + l11 * l11) / (l00 * l11);
+    ex = ex * (1.f + 1.f / 256.f) + 1.f / 32.f;
+    ey = ey * (1.f + 1.f / 256.f) + 1.f / 32.f;
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float qx = (float)((q & 1) * 8), qy = (float)((q >> 1) * 8);
+        const bool hit = (ut + ex >= qx + 0.5f) && (ut - ex <= qx + 7.5f) && (vt + ey >= qy + 0.5f) &&
+                         (vt - ey <= qy + 7.5f);
+        m |= hit ? (1u << q) : 0u;
+    }
+    return m;
+}
+
+// Compact the slots whose mask has this wave's bit, in slot order.
+__device__ __forceinline__ int compact(const uint8_t* s_mask, uint16_t* list, int wave, int lane) {
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool on = (s_mask[lane + 64 * i] >> wave) & 1u;
+        const uint64_t b = __ballot(on);
+        if (on) {
+            const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+            list[cnt + pos] = (uint16_t)(lane + 64 * i);
+        }
+        cnt += __popcll(b);
+    }
+    __builtin_amdgcn_wave_barrier();
+    return cnt;
+}
+
+__global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
+    __shared__ float4 s_g0[kBlock];
+    __shared__ float4 s_g1[kBlock];
+    __shared__ float s_g2[kBlock];
+    __shared__ uint8_t s_mask[kBlock];
+    __shared__ uint16_t s_list[4][kBlock];
+
+    const BlendArgs& b = a.b;
+    const int ntiles = b.tiles_x * b.tiles_y;
+    const int tile = xcd_tile(blockIdx.x, ntiles);
+    if (tile >= ntiles) return;
+    const int tx = tile % b.tiles_x, ty = tile / b.tiles_x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lx = (wave & 1) * 8 + (lane & 7), ly = (wave >> 1) * 8 + (lane >> 3);
+    const int px = tx * kTile + lx, py = ty * kTile + ly;
+    const bool inside = px < b.width && py < b.height;
+    const float fx = (float)lx + 0.5f, fy = (float)ly + 0.5f;
+    const float x0 = (float)(tx * kTile), y0 = (float)(ty * kTile);
+    const float inv_amin = 1.f / b.alpha_min;
+    const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
+    const Stage st{s_g0, s_g1, s_g2};
+
+    float T = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f;
+    int last = 0;
+    bool done = !inside;
+    bool wave_done = __ballot(!done) == 0;
+    for (uint32_t start = range.x; start < range.y; start += kBlock) {
+        const uint32_t k = start + tid;
+        uint32_t m = 0;
+        if (k < range.y) {
+            const uint32_t g = a.list[k];
+            if (g < a.n) m = stage_entry(a, g, x0, y0, inv_amin, st, tid);
+        }
+        s_mask[tid] = (uint8_t)m;
+        __syncthreads();
+        const int cnt = wave_done ? 0 : compact(s_mask, s_list[wave], wave, lane);
+        const int base = (int)(start - range.x);
+        for (int j = 0; j < cnt; ++j) {
+            const int e = s_list[wave][j];
+            const float4 g0 = s_g0[e], g1 = s_g1[e];
+            const float cb = s_g2[e];
+            const Pair p = eval_pair(fx, fy, g0, g1, b.alpha_max);
+            bool ok = !done && p.alpha >= b.alpha_min;
+            const float om = 1.f - p.alpha;
+            const float Tn = T * om;
+            const bool stop = ok && Tn < b.T_min;
+            done = done || stop;
+            ok = ok && !stop;
+            if (ok) {
+                const float w = p.alpha * T;
+                C0 = __builtin_fmaf(w, g1.z, C0);
+                C1 = __builtin_fmaf(w, g1.w, C1);
+                C2 = __builtin_fmaf(w, cb, C2);
+                T = Tn;
+                last = base + e + 1;
+            }
+            if (__ballot(!done) == 0) break;
+        }
+        wave_done = __ballot(!done) == 0;
+        if (__syncthreads_count(done ? 1 : 0) == kBlock) break;
+    }
+    if (inside) {
+        const size_t pix = (size_t)py * b.width + px;
+        const size_t plane = (size_t)b.width * b.height;
+        a.image[pix] = C0 + T * b.bg[0];
+        a.image[plane + pix] = C1 + T * b.bg[1];
+        a.image[2 * plane + pix] = C2 + T * b.bg[2];
+        a.final_T[pix] = T;
+        a.n_contrib[pix] = last;
+    }
+}
+
+// ---- cross-lane reduction helpers (wave64) ----
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowRor8 = 0x128;
+
+// a <- [a_lo, b_lo], b <- [a_hi, b_hi] (lo/hi = lanes 0-31 / 32-63)
+__device__ __forceinline__ void xchg32(float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+// a <- [a.r0, b.r0, a.r2, b.r2], b <- [a.r1, b.r1, a.r3, b.r3] (rows of 16 lanes)
+__device__ __forceinline__ void xchg16(float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+// Sums v[0..7] and v8 over the 64 lanes.  On return, every lane of 8-lane
+// group j (lanes 8j..8j+7) holds the total of v[j], and every lane holds the
+// total of v8 in v8.
+__device__ __forceinline__ float reduce9(float v[8], float& v8, int lane) {
+    float s[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        xchg32(v[k], v[k + 4]);
+        s[k] = v[k] + v[k + 4];  // lo lanes: value k, hi lanes: value k+4
+    }
+    xchg16(s[0], s[2]);
+    const float t0 = s[0] + s[2];  // rows: v0 v2 v4 v6
+    xchg16(s[1], s[3]);
+    const float t1 = s[1] + s[3];  // rows: v1 v3 v5 v7
+    const bool hi8 = (lane & 8) != 0;
+    const float keep = hi8 ? t1 : t0;
+    const float send = hi8 ? t0 : t1;
+    float u = keep + dpp<kRowRor8>(send);  // group j = lane >> 3 holds v_j over 8 lanes
+    u += dpp<kQuadXor1>(u);
+    u += dpp<kQuadXor2>(u);
+    u += dpp<kRowHalfMirror>(u);
+    // v8
+    float x = v8, y = v8;
+    xchg32(x, y);
+    float w = x + y;
+    float w2 = w;
+    xchg16(w, w2);
+    w = w + w2;
+    w += dpp<kRowRor8>(w);
+    w += dpp<kQuadXor1>(w);
+    w += dpp<kQuadXor2>(w);
+    w += dpp<kRowHalfMirror>(w);
+    v8 = w;
+    return u;
+}
+
+__global__ __launch_bounds__(kBlock) void k_render_bwd(RenderArgs a) {
+    __shared__ float4 s_g0[kBlock];
+    __shared__ float4 s_g1[kBlock];
+    __shared__ float s_g2[kBlock];
+    __shared__ uint8_t s_mask[kBlock];
+    __shared__ uint16_t s_list[4][kBlock];
+    __shared__ uint32_t s_gid[kBlock];
+    __shared__ int s_wmax[4];
+    __shared__ int s_bmax;
+
+    const BlendArgs& b = a.b;
+    const int ntiles = b.tiles_x * b.tiles_y;
+    const int tile = xcd_tile(blockIdx.x, ntiles);
+    if (tile >= ntiles) return;
+    const int tx = tile % b.tiles_x, ty = tile / b.tiles_x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lx = (wave & 1) * 8 + (lane & 7), ly = (wave >> 1) * 8 + (lane >> 3);
+    const int px = tx * kTile + lx, py = ty * kTile + ly;
+    const bool inside = px < b.width && py < b.height;
+    const float fx = (float)lx + 0.5f, fy = (float)ly + 0.5f;
+    const float x0 = (float)(tx * kTile), y0 = (float)(ty * kTile);
+    const float inv_amin = 1.f / b.alpha_min;
+    const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
+    const Stage st{s_g0, s_g1, s_g2};
+
+    float T = 1.f, g0c = 0.f, g1c = 0.f, g2c = 0.f;
+    int nc = 0;
+    if (inside) {
+        const size_t pix = (size_t)py * b.width + px;
+        const size_t plane = (size_t)b.width * b.height;
+        T = a.final_T[pix];
+        nc = a.n_contrib[pix];
+        g0c = a.dL_dimage[pix];
+        g1c = a.dL_dimage[plane + pix];
+        g2c = a.dL_dimage[2 * plane + pix];
+    }
+    float Cn0 = b.bg[0], Cn1 = b.bg[1], Cn2 = b.bg[2];
+    if (tid < 4) s_wmax[tid] = 0;
+    if (tid == 0) s_bmax = 0;
+    __syncthreads();
+    atomicMax(&s_wmax[wave], nc);
+    atomicMax(&s_bmax, nc);
+    __syncthreads();
+    const int wmax = s_wmax[wave];
+    const uint32_t end = range.x + (uint32_t)s_bmax;
+    constexpr float k2ln2 = 1.3862943611198906f;  // 2 ln 2: conic d = 2 ln2 L e
+
+    for (int32_t hi = (int32_t)end; hi > (int32_t)range.x; hi -= kBlock) {
+        const int32_t k = hi - 1 - tid;  // slot tid holds list position k (descending)
+        uint32_t m = 0;
+        const uint32_t g = k >= (int32_t)range.x ? a.list[k] : 0xffffffffu;
+        if (g < a.n) {
+            s_gid[tid] = g;
+            m = stage_entry(a, g, x0, y0, inv_amin, st, tid);
+            const int pos = k - (int)range.x;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (pos >= s_wmax[q]) m &= ~(1u << q);
+        }
+        s_mask[tid] = (uint8_t)m;
+        __syncthreads();
+        const int cnt = wmax > 0 ? compact(s_mask, s_list[wave], wave, lane) : 0;
+        const int top = hi - 1 - (int)range.x;  // list position of slot 0
+        for (int j = 0; j < cnt; ++j) {
+            const int e = s_list[wave][j];
+            const int pos = top - e;
+            const float4 g0 = s_g0[e], g1 = s_g1[e];
+            const float cb = s_g2[e];
+            const Pair p = eval_pair(fx, fy, g0, g1, b.alpha_max);
+            const bool ok = pos < nc && p.alpha >= b.alpha_min;
+            float v[8], v8;
+            if (ok) {
+                const float om = 1.f - p.alpha;
+                T = T * __builtin_amdgcn_rcpf(om);  // transmittance before this entry
+                const float w = p.alpha * T;
+                const float d0 = g1.z - Cn0, d1 = g1.w - Cn1, d2 = cb - Cn2;
+                const float dalpha = T * (g0c * d0 + g1c * d1 + g2c * d2);
+                Cn0 = __builtin_fmaf(p.alpha, d0, Cn0);
+                Cn1 = __builtin_fmaf(p.alpha, d1, Cn1);
+                Cn2 = __builtin_fmaf(p.alpha, d2, Cn2);
+                const float dsG = p.sG > b.alpha_max ? 0.f : dalpha;  // clamped: no dependence
+                const float dpow = dsG * g1.y * p.G;                   // d/dpower, G = exp(power)
+                const float qx = k2ln2 * g0.z * p.e1;                  // (conic d)_x
+                const float qy = k2ln2 * (g0.w * p.e1 + g1.x * p.e2);  // (conic d)_y
+                v[0] = qx * dpow;
+                v[1] = qy * dpow;
+                v[2] = -0.5f * p.dx * p.dx * dpow;
+                v[3] = -p.dx * p.dy * dpow;
+                v[4] = -0.5f * p.dy * p.dy * dpow;
+                v[5] = dsG * p.G;
+                v[6] = w * g0c;
+                v[7] = w * g1c;
+                v8 = w * g2c;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = 0.f;
+                v8 = 0.f;
+            }
+            if (__ballot(ok) != 0) {
+                const float u = reduce9(v, v8, lane);
+                const bool head = (lane & 7) == 0;
+                if (head || lane == 1) {
+                    const int idx = lane == 1 ? 8 : (lane >> 3);
+                    unsafeAtomicAdd(a.grad2d + (size_t)s_gid[e] * GS_GRAD2D_STRIDE + idx, lane == 1 ? v8 : u);
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void k_zero_f32(float* p, size_t count) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < count; i += stride) p[i] = 0.f;
+}
+
+// Pair counts: one thread per pixel, walking the whole tile list.
+__global__ __launch_bounds__(256) void k_count_pairs(RenderArgs a, unsigned long long* counts) {
+    __shared__ unsigned long long s_c[3];
+    const BlendArgs& b = a.b;
+    if (threadIdx.x < 3) s_c[threadIdx.x] = 0;
+    __syncthreads();
+    const int px = blockIdx.x * 16 + (threadIdx.x & 15);
+    const int py = blockIdx.y * 16 + (threadIdx.x >> 4);
+    unsigned long long ev = 0, nc = 0, nb = 0;
+    if (px < b.width && py < b.height) {
+        const int tile = blockIdx.y * b.tiles_x + blockIdx.x;
+        const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
+        const float fx = (float)(px % kTile) + 0.5f, fy = (float)(py % kTile) + 0.5f;
+        const float x0 = (float)(blockIdx.x * kTile), y0 = (float)(blockIdx.y * kTile);
+        float T = 1.f;
+        for (uint32_t k = range.x; k < range.y; ++k) {
+            const uint32_t g = a.list[k];
+            if (g >= a.n) continue;
+            const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
+            const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
+            const float4 g0 = make_float4((r0.x - x0) + r0.z, (r0.y - y0) + r0.w, r1.x, r1.y);
+            const float4 g1 = make_float4(r1.z, r1.w, r2.x, r2.y);
+            const Pair p = eval_pair(fx, fy, g0, g1, b.alpha_max);
+            ++ev;
+            if (p.alpha < b.alpha_min) continue;
+            const float Tn = T * (1.f - p.alpha);
+            if (Tn < b.T_min) break;
+            T = Tn;
+            ++nb;
+            nc = k - range.x + 1;
+        }
+    }
+    atomicAdd(&s_c[0], ev);
+    atomicAdd(&s_c[1], nc);
+    atomicAdd(&s_c[2], nb);
+    __syncthreads();
+    if (threadIdx.x < 3) atomicAdd(&counts[threadIdx.x], s_c[threadIdx.x]);
+}
+
+__global__ void k_zero_i64(unsigned long long* p, int n) {
+    if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
+}
+
+inline int render_common_checks(const gs_camera* cam, const gs_settings* set, const uint32_t* ranges,
+                                const float* splats) {
+    if (!camera_ok(cam) || !set || !ranges) return GS_EINVAL;
+    if (!aligned16(splats) || !aligned16(ranges)) return GS_EALIGN;
+    return GS_OK;
+}
+
+inline int render_grid(const gs_camera* cam) {
+    const int nt = tiles_x(cam) * tiles_y(cam);
+    return 8 * ((nt + 7) / 8);
+}
+
+}  // namespace
+}  // namespace gs
+
+using namespace gs;
+
+extern "C" int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
+                             const uint32_t* point_list, const float* splats, float* image, float* final_T,
+                             int32_t* n_contrib, void* stream) {
+    int rc = render_common_checks(cam, set, tile_ranges, splats);
+    if (rc) return rc;
+    if (n < 0 || !image || !final_T || !n_contrib) return GS_EINVAL;
+    if (n > 0 && (!point_list || !splats)) return GS_EINVAL;
+    RenderArgs a{};
+    a.b = blend_args(cam, set);
+    a.n = (uint32_t)n;
+    a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
+    a.image = image; a.final_T = final_T; a.n_contrib = n_contrib;
+    hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam)), dim3(kBlock), 0, as_stream(stream), a);
+    return launch_status();
+}
+
+extern "C" int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
+                             const uint32_t* point_list, const float* splats, const float* final_T,
+                             const int32_t* n_contrib, const float* dL_dimage, float* grad2d, void* stream) {
+    int rc = render_common_checks(cam, set, tile_ranges, splats);
+    if (rc) return rc;
+    if (n < 0 || !final_T || !n_contrib || !dL_dimage) return GS_EINVAL;
+    if (n > 0 && (!point_list || !splats || !grad2d)) return GS_EINVAL;
+    if (n > 0 && !aligned16(grad2d)) return GS_EALIGN;
+    hipStream_t s = as_stream(stream);
+    if (n > 0) {
+        const size_t cnt = (size_t)n * GS_GRAD2D_STRIDE;
+        hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)std::min<size_t>((cnt + 255) / 256, 4096)), dim3(256), 0, s,
+                           grad2d, cnt);
+    }
+    RenderArgs a{};
+    a.b = blend_args(cam, set);
+    a.n = (uint32_t)n;
+    a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
+    a.final_T = const_cast<float*>(final_T); a.n_contrib = const_cast<int32_t*>(n_contrib);
+    a.dL_dimage = dL_dimage; a.grad2d = grad2d;
+    hipLaunchKernelGGL(k_render_bwd, dim3(render_grid(cam)), dim3(kBlock), 0, s, a);
+    return launch_status();
+}
+
+extern "C" int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
+                              const uint32_t* point_list, const float* splats, int64_t* counts, void* stream) {
+    int rc = render_common_checks(cam, set, tile_ranges, splats);
+    if (rc) return rc;
+    if (!counts || n < 0) return GS_EINVAL;
+    hipStream_t s = as_stream(stream);
+    RenderArgs a{};
+    a.b = blend_args(cam, set);
+    a.n = (uint32_t)n;
+    a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
+    auto* c = reinterpret_cast<unsigned long long*>(counts);
+    hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(64), 0, s, c, 3);
+    hipLaunchKernelGGL(k_count_pairs, dim3(tiles_x(cam), tiles_y(cam)), dim3(256), 0, s, a, c);
+    return launch_status();
+}

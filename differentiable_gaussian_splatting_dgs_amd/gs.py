@@ -1,0 +1,368 @@
+"""Thin Python binding of the C ABI in include/gs.h (libgs.so).
+
+Argument marshalling only: every step runs in the HIP kernels of libgs.so.
+PyTorch supplies device memory (tensors) and the current HIP stream.  If the
+library is missing or no GPU is present the calls raise; there is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+from dataclasses import dataclass, field
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgs.so")
+
+TILE = 16
+SPLAT_STRIDE = 12
+GRAD2D_STRIDE = 12
+
+
+class GsError(RuntimeError):
+    pass
+
+
+class GsCamera(C.Structure):
+    _fields_ = [("fx", C.c_double), ("fy", C.c_double), ("cx", C.c_double), ("cy", C.c_double),
+                ("width", C.c_int32), ("height", C.c_int32), ("R", C.c_double * 9), ("t", C.c_double * 3)]
+
+
+class GsSettings(C.Structure):
+    _fields_ = [("near_z", C.c_double), ("alpha_min", C.c_double), ("alpha_max", C.c_double),
+                ("T_min", C.c_double), ("dilation", C.c_double), ("bg", C.c_double * 3)]
+
+
+class GsAdamGroup(C.Structure):
+    _fields_ = [("param", C.c_void_p), ("grad", C.c_void_p), ("exp_avg", C.c_void_p), ("exp_avg_sq", C.c_void_p),
+                ("rows", C.c_int64), ("row_len", C.c_int32), ("col_begin", C.c_int32), ("col_end", C.c_int32),
+                ("normalize_rows", C.c_int32), ("lr", C.c_float)]
+
+
+SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_bin_workspace_size",
+           "gs_bin_sort", "gs_bin_keys", "gs_render_fwd", "gs_render_bwd", "gs_preprocess_bwd", "gs_image_loss",
+           "gs_densify_accum", "gs_adam_step", "gs_count_pairs"]
+
+_lib = None
+_vp = C.c_void_p
+_i32 = C.c_int32
+_i64 = C.c_int64
+
+
+def load_library(path=LIB_PATH):
+    """Load libgs.so (no GPU needed to load it) and declare the signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise GsError(f"{path} is not built: run `python -m differentiable_gaussian_splatting_dgs_amd.build`")
+    lib = C.CDLL(path)
+    P = C.POINTER
+    lib.gs_error_string.restype = C.c_char_p
+    lib.gs_error_string.argtypes = [C.c_int]
+    lib.gs_version.argtypes = []
+    lib.gs_tile_grid.argtypes = [P(GsCamera), P(_i32), P(_i32)]
+    lib.gs_preprocess.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 10 + [_vp]
+    lib.gs_bin_workspace_size.argtypes = [_i32, P(GsCamera), _i64, P(C.c_size_t)]
+    lib.gs_bin_sort.argtypes = [P(GsCamera), _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
+    lib.gs_bin_keys.argtypes = [P(GsCamera), _vp, _vp, _vp, _vp, _vp]
+    lib.gs_render_fwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 7 + [_vp]
+    lib.gs_preprocess_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
+    lib.gs_image_loss.argtypes = [_i32, _i64, _vp, _vp, _vp, _vp, _vp]
+    lib.gs_densify_accum.argtypes = [_i32, _vp, _vp, _vp, _vp, _vp]
+    lib.gs_adam_step.argtypes = [_i32, P(GsAdamGroup), C.c_float, C.c_float, C.c_float, _i32, _vp]
+    lib.gs_count_pairs.argtypes = [P(GsCamera), P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp]
+    for name in SYMBOLS:
+        if name not in ("gs_error_string",):
+            getattr(lib, name).restype = C.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise GsError(f"{name} failed: {load_library().gs_error_string(rc).decode()} ({rc})")
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise GsError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise GsError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise GsError(f"{name} must be {dtype}, got {t.dtype}")
+    return C.c_void_p(t.data_ptr())
+
+
+@dataclass
+class Settings:
+    near_z: float = 0.2
+    alpha_min: float = 1.0 / 255.0
+    alpha_max: float = 0.99
+    T_min: float = 1e-4
+    dilation: float = 0.3
+    bg: tuple = (0.0, 0.0, 0.0)
+
+    def struct(self):
+        s = GsSettings()
+        s.near_z, s.alpha_min, s.alpha_max, s.T_min, s.dilation = (self.near_z, self.alpha_min, self.alpha_max,
+                                                                   self.T_min, self.dilation)
+        for i in range(3):
+            s.bg[i] = self.bg[i]
+        return s
+
+
+def camera_struct(cam):
+    """From any object with width, height, fx, fy, cx, cy, R [3,3], t [3]."""
+    c = GsCamera()
+    c.fx, c.fy, c.cx, c.cy = float(cam.fx), float(cam.fy), float(cam.cx), float(cam.cy)
+    c.width, c.height = int(cam.width), int(cam.height)
+    R = [float(v) for row in cam.R for v in row]
+    for i in range(9):
+        c.R[i] = R[i]
+    for i in range(3):
+        c.t[i] = float(cam.t[i])
+    return c
+
+
+# ---------------------------------------------------------------------------
+# One wrapper per C entry point, same names.
+# ---------------------------------------------------------------------------
+
+def gs_tile_grid(cam):
+    tx, ty = _i32(), _i32()
+    _check(load_library().gs_tile_grid(C.byref(camera_struct(cam)), C.byref(tx), C.byref(ty)), "gs_tile_grid")
+    return tx.value, ty.value
+
+
+def gs_preprocess(cam, settings, sh_degree, means, log_scales, quats, opacity_logits, sh,
+                  splats, depth, rect, tiles_touched, clamp_mask):
+    f32, n = torch.float32, means.shape[0]
+    rc = load_library().gs_preprocess(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, sh_degree,
+        _p(means, f32, "means"), _p(log_scales, f32, "log_scales"), _p(quats, f32, "quats"),
+        _p(opacity_logits, f32, "opacity_logits"), _p(sh, f32, "sh"), _p(splats, f32, "splats"),
+        _p(depth, f32, "depth"), _p(rect, torch.int16, "rect"), _p(tiles_touched, torch.int32, "tiles_touched"),
+        _p(clamp_mask, torch.uint8, "clamp_mask"), _stream())
+    _check(rc, "gs_preprocess")
+
+
+def gs_bin_workspace_size(n, cam, key_capacity):
+    b = C.c_size_t()
+    _check(load_library().gs_bin_workspace_size(n, C.byref(camera_struct(cam)), key_capacity, C.byref(b)),
+           "gs_bin_workspace_size")
+    return b.value
+
+
+def gs_bin_sort(cam, n, depth, rect, tiles_touched, key_capacity, point_list, tile_ranges, num_keys, overflow,
+                workspace):
+    rc = load_library().gs_bin_sort(
+        C.byref(camera_struct(cam)), n, _p(depth, torch.float32, "depth"), _p(rect, torch.int16, "rect"),
+        _p(tiles_touched, torch.int32, "tiles_touched"), key_capacity, _p(point_list, torch.int32, "point_list"),
+        _p(tile_ranges, torch.int32, "tile_ranges"), _p(num_keys, torch.int32, "num_keys"),
+        _p(overflow, torch.int32, "overflow"), _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _check(rc, "gs_bin_sort")
+
+
+def gs_bin_keys(cam, tile_ranges, point_list, depth, keys):
+    rc = load_library().gs_bin_keys(C.byref(camera_struct(cam)), _p(tile_ranges, torch.int32), _p(point_list, torch.int32),
+                                    _p(depth, torch.float32), _p(keys, torch.int64), _stream())
+    _check(rc, "gs_bin_keys")
+
+
+def gs_render_fwd(cam, settings, n, tile_ranges, point_list, splats, image, final_T, n_contrib):
+    rc = load_library().gs_render_fwd(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
+        _p(point_list, torch.int32, "point_list"), _p(splats, torch.float32, "splats"),
+        _p(image, torch.float32, "image"), _p(final_T, torch.float32, "final_T"),
+        _p(n_contrib, torch.int32, "n_contrib"), _stream())
+    _check(rc, "gs_render_fwd")
+
+
+def gs_render_bwd(cam, settings, n, tile_ranges, point_list, splats, final_T, n_contrib, dL_dimage, grad2d):
+    rc = load_library().gs_render_bwd(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
+        _p(point_list, torch.int32, "point_list"), _p(splats, torch.float32, "splats"),
+        _p(final_T, torch.float32, "final_T"), _p(n_contrib, torch.int32, "n_contrib"),
+        _p(dL_dimage, torch.float32, "dL_dimage"), _p(grad2d, torch.float32, "grad2d"), _stream())
+    _check(rc, "gs_render_bwd")
+
+
+def gs_preprocess_bwd(cam, settings, sh_degree, means, log_scales, quats, opacity_logits, sh, tiles_touched,
+                      clamp_mask, grad2d, dmeans, dlog_scales, dquats, dopacity_logits, dsh):
+    f32, n = torch.float32, means.shape[0]
+    rc = load_library().gs_preprocess_bwd(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, sh_degree,
+        _p(means, f32, "means"), _p(log_scales, f32, "log_scales"), _p(quats, f32, "quats"),
+        _p(opacity_logits, f32, "opacity_logits"), _p(sh, f32, "sh"),
+        _p(tiles_touched, torch.int32, "tiles_touched"), _p(clamp_mask, torch.uint8, "clamp_mask"),
+        _p(grad2d, f32, "grad2d"), _p(dmeans, f32, "dmeans"), _p(dlog_scales, f32, "dlog_scales"),
+        _p(dquats, f32, "dquats"), _p(dopacity_logits, f32, "dopacity_logits"), _p(dsh, f32, "dsh"), _stream())
+    _check(rc, "gs_preprocess_bwd")
+
+
+LOSS_PARTIALS = 1024
+
+
+def gs_image_loss(mode, pred, target, dL_dpred, loss):
+    """loss: float64 CUDA tensor with at least 1 + LOSS_PARTIALS entries; loss[0] receives L."""
+    m = {"l1": 1, "l2": 2}[mode] if isinstance(mode, str) else int(mode)
+    if loss.numel() < 1 + LOSS_PARTIALS:
+        raise GsError(f"loss buffer needs {1 + LOSS_PARTIALS} float64 entries")
+    rc = load_library().gs_image_loss(m, pred.numel(), _p(pred, torch.float32, "pred"),
+                                      _p(target, torch.float32, "target"), _p(dL_dpred, torch.float32, "dL_dpred"),
+                                      _p(loss, torch.float64, "loss"), _stream())
+    _check(rc, "gs_image_loss")
+
+
+def gs_densify_accum(n, tiles_touched, grad2d, accum, count):
+    rc = load_library().gs_densify_accum(n, _p(tiles_touched, torch.int32), _p(grad2d, torch.float32),
+                                         _p(accum, torch.float32), _p(count, torch.int32), _stream())
+    _check(rc, "gs_densify_accum")
+
+
+def gs_adam_step(groups, beta1, beta2, eps, step):
+    """groups: list of dicts with param, grad, exp_avg, exp_avg_sq (tensors), rows, row_len,
+    col_begin, col_end, normalize_rows, lr."""
+    arr = (GsAdamGroup * max(len(groups), 1))()
+    for i, g in enumerate(groups):
+        a = arr[i]
+        a.param, a.grad = _p(g["param"], torch.float32).value, _p(g["grad"], torch.float32).value
+        a.exp_avg, a.exp_avg_sq = _p(g["exp_avg"], torch.float32).value, _p(g["exp_avg_sq"], torch.float32).value
+        a.rows, a.row_len = int(g["rows"]), int(g["row_len"])
+        a.col_begin, a.col_end = int(g.get("col_begin", 0)), int(g.get("col_end", g["row_len"]))
+        a.normalize_rows, a.lr = int(g.get("normalize_rows", 0)), float(g["lr"])
+    rc = load_library().gs_adam_step(len(groups), arr, beta1, beta2, eps, step, _stream())
+    _check(rc, "gs_adam_step")
+
+
+def gs_count_pairs(cam, settings, n, tile_ranges, point_list, splats, counts):
+    rc = load_library().gs_count_pairs(C.byref(camera_struct(cam)), C.byref(settings.struct()), n,
+                                       _p(tile_ranges, torch.int32), _p(point_list, torch.int32),
+                                       _p(splats, torch.float32), _p(counts, torch.int64), _stream())
+    _check(rc, "gs_count_pairs")
+
+
+# ---------------------------------------------------------------------------
+# Buffer owner for one camera and one Gaussian count (plumbing: allocation).
+# ---------------------------------------------------------------------------
+
+class Rasterizer:
+    """Owns the forward/backward buffers of one view and runs the C ABI calls.
+
+    forward(params) runs gs_preprocess, gs_bin_sort and gs_render_fwd;
+    backward(params, dL_dimage) runs gs_render_bwd and gs_preprocess_bwd.
+    The number of (tile, Gaussian) pairs K is data dependent: the list buffer has
+    `key_capacity` entries and binning raises a device flag when K exceeds it.
+    `forward(check=True)` synchronises once, grows the capacity and re-bins when
+    that happened; with check=False nothing synchronises.
+    """
+
+    def __init__(self, cam, n, sh_degree, settings=None, key_capacity=None, device="cuda"):
+        load_library()
+        self.cam, self.n, self.deg = cam, int(n), int(sh_degree)
+        self.settings = settings or Settings()
+        self.device = torch.device(device)
+        dev, n = self.device, self.n
+        self.tiles_x, self.tiles_y = gs_tile_grid(cam)
+        self.ntiles = self.tiles_x * self.tiles_y
+        self.splats = torch.empty((n, SPLAT_STRIDE), dtype=torch.float32, device=dev)
+        self.depth = torch.empty(n, dtype=torch.float32, device=dev)
+        self.rect = torch.empty((n, 4), dtype=torch.int16, device=dev)
+        self.tiles_touched = torch.empty(n, dtype=torch.int32, device=dev)
+        self.clamp = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.tile_ranges = torch.empty((self.ntiles, 2), dtype=torch.int32, device=dev)
+        self.num_keys = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.overflow = torch.zeros(1, dtype=torch.int32, device=dev)
+        H, W = cam.height, cam.width
+        self.image = torch.empty((3, H, W), dtype=torch.float32, device=dev)
+        self.final_T = torch.empty((H, W), dtype=torch.float32, device=dev)
+        self.n_contrib = torch.empty((H, W), dtype=torch.int32, device=dev)
+        self.grad2d = torch.empty((n, GRAD2D_STRIDE), dtype=torch.float32, device=dev)
+        self._alloc_lists(key_capacity if key_capacity is not None else max(4 * n, 1 << 16))
+
+    def _alloc_lists(self, cap):
+        self.key_capacity = int(cap)
+        self.point_list = torch.empty(max(self.key_capacity, 1), dtype=torch.int32, device=self.device)
+        ws = gs_bin_workspace_size(self.n, self.cam, self.key_capacity)
+        self.workspace = torch.empty(ws + 256, dtype=torch.uint8, device=self.device)
+        off = (-self.workspace.data_ptr()) % 256
+        self.workspace = self.workspace[off:off + ws]
+
+    def preprocess(self, p):
+        gs_preprocess(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
+                      p["opacity_logits"], p["sh"], self.splats, self.depth, self.rect, self.tiles_touched,
+                      self.clamp)
+
+    def bin(self):
+        gs_bin_sort(self.cam, self.n, self.depth, self.rect, self.tiles_touched, self.key_capacity, self.point_list,
+                    self.tile_ranges, self.num_keys, self.overflow, self.workspace)
+
+    def render(self):
+        gs_render_fwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, self.image,
+                      self.final_T, self.n_contrib)
+
+    def forward(self, p, check=True):
+        self.preprocess(p)
+        self.bin()
+        if check and int(self.overflow.item()) != 0:
+            K = int(self.num_keys.item())
+            self._alloc_lists(int(K * 1.25) + 1024)
+            self.bin()
+            assert int(self.overflow.item()) == 0
+        self.render()
+        return self.image
+
+    def backward_2d(self, dL_dimage):
+        gs_render_bwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats,
+                      self.final_T, self.n_contrib, dL_dimage, self.grad2d)
+        return self.grad2d
+
+    def backward(self, p, dL_dimage, out=None):
+        self.backward_2d(dL_dimage)
+        if out is None:
+            out = {k: torch.empty_like(p[k]) for k in ("means", "log_scales", "quats", "opacity_logits", "sh")}
+        gs_preprocess_bwd(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
+                          p["opacity_logits"], p["sh"], self.tiles_touched, self.clamp, self.grad2d,
+                          out["means"], out["log_scales"], out["quats"], out["opacity_logits"], out["sh"])
+        return out
+
+    def count_pairs(self):
+        c = torch.zeros(3, dtype=torch.int64, device=self.device)
+        gs_count_pairs(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, c)
+        return c
+
+
+class RasterizeFunction(torch.autograd.Function):
+    """image = rasterize(means, log_scales, quats, opacity_logits, sh) for one Rasterizer."""
+
+    @staticmethod
+    def forward(ctx, rast, means, log_scales, quats, opacity_logits, sh):
+        p = dict(means=means.contiguous(), log_scales=log_scales.contiguous(), quats=quats.contiguous(),
+                 opacity_logits=opacity_logits.contiguous(), sh=sh.contiguous())
+        img = rast.forward(p).clone()
+        ctx.rast = rast
+        ctx.save_for_backward(p["means"], p["log_scales"], p["quats"], p["opacity_logits"], p["sh"])
+        return img
+
+    @staticmethod
+    def backward(ctx, dL_dimage):
+        m, s, q, o, c = ctx.saved_tensors
+        p = dict(means=m, log_scales=s, quats=q, opacity_logits=o, sh=c)
+        g = ctx.rast.backward(p, dL_dimage.contiguous())
+        return None, g["means"], g["log_scales"], g["quats"], g["opacity_logits"], g["sh"]
+
+
+def rasterize(rast, means, log_scales, quats, opacity_logits, sh):
+    return RasterizeFunction.apply(rast, means, log_scales, quats, opacity_logits, sh)

@@ -1,0 +1,251 @@
+/*
+ * gs.h -- C ABI of the MI355X (gfx950) differentiable tile rasterizer for
+ * 3D Gaussian Splatting.
+ *
+ * Sources cited by tag and section:
+ *  [P3] lshu.cn/news/59090, "CUDA implementation of Gaussian Splatting
+ *       backpropagation: from pixel gradients to 3D Gaussian parameter updates"
+ *       (section 1 architecture and buffer reuse, section 2 gradient math,
+ *       section 3 reverse per-pixel walk, section 4 2D -> 3D conversion,
+ *       section 5 buffer reuse without dynamic allocation).
+ *  [P4] notes.huajishe.fun, "3DGS training and optimisation" (C.2 Adam with
+ *       per-parameter learning rates, D.1 densification statistic, D.4
+ *       quaternion renormalisation, E.1 training loop, E.3 tile rasterization).
+ *  [P1] qqiyuan.cn, "3D Gaussian splatting backward propagation: chain-rule
+ *       gradients explained" (the compositing equation).
+ *
+ * Conventions shared by every call
+ *  - Every array pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA
+ *    tensor's data_ptr), contiguous, in the row-major layout stated, aligned to
+ *    16 bytes.  gs_camera / gs_settings / gs_adam_group arguments are HOST
+ *    pointers, read during the call only.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work on that stream and return; none synchronises the
+ *    host, none allocates device memory.  Scratch comes from caller-owned
+ *    buffers ([P3] section 5: reuse buffers, no dynamic memory management).
+ *  - The caller owns every buffer.  The library keeps no state between calls
+ *    apart from its loaded code object; calls on different streams with
+ *    disjoint buffers may run concurrently.
+ *  - Return value: GS_OK (0) or a negative error code; on error nothing has
+ *    been enqueued.  GS_EHIP means a kernel launch failed (the HIP error is
+ *    left for hipGetLastError).  gs_error_string() names each code.
+ *  - Tiles are 16 x 16 pixels.  Pixel (x, y) is sampled at (x + 0.5, y + 0.5).
+ *    Images are planar [3, H, W] float32.
+ */
+#ifndef GS_MI355X_H
+#define GS_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GS_TILE 16
+#define GS_SPLAT_STRIDE 12  /* floats per projected-Gaussian record */
+#define GS_GRAD2D_STRIDE 12 /* floats per 2D-gradient record */
+#define GS_MAX_SH_DEGREE 3
+
+enum {
+    GS_OK = 0,
+    GS_EINVAL = -1,     /* null pointer, negative size, unsupported degree, bad camera */
+    GS_EALIGN = -2,     /* a pointer is not 16-byte aligned */
+    GS_EWORKSPACE = -3, /* workspace_bytes smaller than gs_bin_workspace_size() */
+    GS_EHIP = -4,       /* a kernel launch failed */
+    GS_ECAPACITY = -5   /* a size exceeds what the kernels index (e.g. key_capacity > 2^30) */
+};
+
+/* Pinhole camera.  world -> camera: t = R mu + t.  u = fx t_x / t_z + cx. */
+typedef struct gs_camera {
+    double fx, fy, cx, cy;
+    int32_t width, height;
+    double R[9]; /* row-major */
+    double t[3];
+} gs_camera;
+
+/* Rasterizer constants.  Defaults: near_z 0.2, alpha_min 1/255, alpha_max 0.99,
+   T_min 1e-4, dilation 0.3 (pixels^2 added to the 2D covariance diagonal),
+   bg = (0, 0, 0). */
+typedef struct gs_settings {
+    double near_z;
+    double alpha_min;
+    double alpha_max;
+    double T_min;
+    double dilation;
+    double bg[3];
+} gs_settings;
+
+const char* gs_error_string(int code);
+int gs_version(void);
+
+/* Number of tiles along x and y for the camera's image. */
+int gs_tile_grid(const gs_camera* cam, int32_t* tiles_x, int32_t* tiles_y);
+
+/*
+ * gs_preprocess -- per-Gaussian projection ([P3] sections 1 and 4 name the
+ * forward intermediates the backward reuses; [P4] E.3: project, then cull
+ * against tiles).  Computed in float64, stored in float32.
+ *
+ * In:  means [n,3], log_scales [n,3], quats [n,4] (w, x, y, z; any length,
+ *      normalised inside), opacity_logits [n], sh [n, (deg+1)^2, 3]
+ *      (index l*l + l + m, real SH with the Condon-Shortley phase).
+ * Out (every Gaussian, culled ones zeroed):
+ *   splats [n,12]: u, v        2D mean rounded to float32
+ *                  u_res, v_res  (exact mean - rounded mean), float32
+ *                  L00, L10, L11  lower Cholesky factor of the conic (inverse
+ *                               2D covariance) times sqrt(log2(e)/2), so that
+ *                               e = L^T d gives G = exp2(-|e|^2)
+ *                  opacity     sigmoid(logit)
+ *                  r, g, b     max(0, SH colour + 0.5)
+ *                  0           (padding)
+ *   depth [n]: camera-space z (sort key); rect [n,4] int16: tile rectangle
+ *   [x0, x1) x [y0, y1) stored x0, y0, x1, y1 -- the bounding box of the exact
+ *   alpha >= alpha_min ellipse; tiles_touched [n] int32: its area (0 = culled
+ *   or off screen); clamp_mask [n] uint8: bit c set if colour channel c was
+ *   clamped at 0.
+ * Culling: t_z <= near_z, sigmoid(logit) < alpha_min, or det <= 0.
+ */
+int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                  const float* means, const float* log_scales, const float* quats,
+                  const float* opacity_logits, const float* sh,
+                  float* splats, float* depth, int16_t* rect, int32_t* tiles_touched,
+                  uint8_t* clamp_mask, void* stream);
+
+/* Bytes of workspace gs_bin_sort needs for n Gaussians and key_capacity list
+   entries. */
+int gs_bin_workspace_size(int32_t n, const gs_camera* cam, int64_t key_capacity, size_t* bytes);
+
+/*
+ * gs_bin_sort -- tile binning and depth sort ([P4] E.3: cull against tiles,
+ * sort by depth inside each tile; [P3] sections 1 and 5: the sorted list and
+ * the tile ranges are reused by the backward).
+ *
+ * Produces, for every tile, the indices of the Gaussians whose rect covers it,
+ * ordered by (float32 depth, Gaussian index): point_list [key_capacity] uint32
+ * holds the lists tile after tile; tile_ranges [tiles, 2] uint32 holds each
+ * tile's [begin, end) in point_list ([0, 0) when empty).
+ * num_keys_dev [1] uint32 receives K = sum of tiles_touched (device memory; the
+ * call does not read it back).  If K > key_capacity, *overflow_dev is set to 1,
+ * every range is written empty and point_list holds no valid list: the caller
+ * checks overflow_dev after its next synchronisation and retries with a larger
+ * capacity.  Otherwise *overflow_dev = 0.
+ * workspace: device scratch of at least gs_bin_workspace_size() bytes, 256-byte
+ * aligned; its contents on entry do not matter.
+ */
+int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, const int16_t* rect,
+                const int32_t* tiles_touched, int64_t key_capacity,
+                uint32_t* point_list, uint32_t* tile_ranges, uint32_t* num_keys_dev,
+                uint32_t* overflow_dev, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Diagnostic: the 64-bit sort keys (tile << 32 | float32 depth bits) of the
+   sorted list, keys [key_capacity]; entries at and beyond K are left alone. */
+int gs_bin_keys(const gs_camera* cam, const uint32_t* tile_ranges, const uint32_t* point_list,
+                const float* depth, uint64_t* keys, void* stream);
+
+/*
+ * gs_render_fwd -- front-to-back compositing per pixel ([P1] compositing
+ * equation; [P3] section 2: alpha = min(alpha_max, opacity G)).
+ * A pair is skipped when alpha < alpha_min; a pixel stops before the entry
+ * whose T (1 - alpha) would fall below T_min.
+ * Out: image [3,H,W] = C + T_final bg; final_T [H,W]; n_contrib [H,W] int32 =
+ * position in the tile's list of the last blended entry + 1 (0 if none).
+ */
+int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
+                  const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                  float* image, float* final_T, int32_t* n_contrib, void* stream);
+
+/*
+ * gs_render_bwd -- reverse per-pixel walk from the stored final
+ * transmittance ([P3] section 3), gradients per [P3] section 2:
+ *   dL/dc = T alpha dL/dpix;  dL/dalpha = T sum_ch dL/dpix_ch (c_ch - C_next,ch)
+ * with C_next starting at the background; then through alpha = opacity G
+ * (zero when clamped) and G = exp(power).
+ * In: dL_dimage [3,H,W].  Out: grad2d [n,12] (zeroed by the call, then
+ * accumulated): dL/du, dL/dv, dL/dA, dL/dB, dL/dC (conic [[A,B],[B,C]],
+ * power = -A dx^2/2 - B dx dy - C dy^2/2, d = pixel - mean), dL/dopacity,
+ * dL/dr, dL/dg, dL/db, 0, 0, 0.  Accumulation order is not fixed, so the
+ * float32 result varies in the last bits between runs.
+ */
+int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32_t n,
+                  const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                  const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
+                  float* grad2d, void* stream);
+
+/*
+ * gs_preprocess_bwd -- 2D -> 3D gradients ([P3] section 4: through the view
+ * transform and perspective Jacobian, dSigma = T^T dSigma2D T, the SH basis,
+ * and Sigma = R S S^T R^T; [P4] D.4 quaternion).  Gaussians with
+ * tiles_touched == 0 get zero gradients.  Outputs have the parameters' shapes
+ * and are overwritten: dmeans [n,3], dlog_scales [n,3], dquats [n,4] (w.r.t.
+ * the raw, unnormalised quaternion), dopacity_logits [n], dsh [n,(deg+1)^2,3].
+ */
+int gs_preprocess_bwd(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                      const float* means, const float* log_scales, const float* quats,
+                      const float* opacity_logits, const float* sh,
+                      const int32_t* tiles_touched, const uint8_t* clamp_mask, const float* grad2d,
+                      float* dmeans, float* dlog_scales, float* dquats, float* dopacity_logits,
+                      float* dsh, void* stream);
+
+/*
+ * gs_image_loss -- image reconstruction loss ([P4] E.1).  mode 1: L1,
+ * L = sum |pred - target|, dL/dpred = sign(pred - target) with sign(0) = 0;
+ * mode 2: L2, L = sum (pred - target)^2, dL/dpred = 2 (pred - target).
+ * pred, target, dL_dpred [count] float32.  loss_dev [1 + GS_LOSS_PARTIALS]
+ * float64: loss_dev[0] receives L (summed in a fixed order, so the value is
+ * deterministic); the other entries are scratch.
+ */
+#define GS_LOSS_PARTIALS 1024
+int gs_image_loss(int32_t mode, int64_t count, const float* pred, const float* target,
+                  float* dL_dpred, double* loss_dev, void* stream);
+
+/*
+ * gs_densify_accum -- densification statistic ([P4] D.1, E.1 step 2): for
+ * each Gaussian with tiles_touched > 0, accum[i] += |(dL/du, dL/dv)| (this
+ * view's 2D-mean gradient, pixel units) and count[i] += 1.  accum [n] float32,
+ * count [n] int32 are read-modify-written.
+ */
+int gs_densify_accum(int32_t n, const int32_t* tiles_touched, const float* grad2d,
+                     float* accum, int32_t* count, void* stream);
+
+/* One Adam parameter group ([P4] C.2: per-parameter learning rates).  The
+   group covers columns [col_begin, col_end) of a [rows, row_len] array; all
+   four arrays share that layout.  normalize_rows != 0 renormalises each row
+   to unit length after the update ([P4] D.4, quaternions) and requires the
+   group to cover whole rows. */
+typedef struct gs_adam_group {
+    float* param;
+    const float* grad;
+    float* exp_avg;
+    float* exp_avg_sq;
+    int64_t rows;
+    int32_t row_len;
+    int32_t col_begin;
+    int32_t col_end;
+    int32_t normalize_rows;
+    float lr;
+} gs_adam_group;
+
+#define GS_ADAM_MAX_GROUPS 16
+
+/*
+ * gs_adam_step -- one Adam step (Kingma and Ba): m = b1 m + (1 - b1) g,
+ * v = b2 v + (1 - b2) g^2, p -= lr (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps),
+ * for up to GS_ADAM_MAX_GROUPS groups in one launch.  step >= 1.
+ */
+int gs_adam_step(int32_t n_groups, const gs_adam_group* groups, float beta1, float beta2,
+                 float eps, int32_t step, void* stream);
+
+/*
+ * gs_count_pairs -- diagnostic pair counts of a forward pass (device int64
+ * counters, overwritten): counts[0] = evaluated pairs (entries walked by the
+ * forward up to and including the one that stops a pixel), counts[1] = sum of
+ * n_contrib (entries walked by the backward), counts[2] = blended pairs.
+ */
+int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
+                   const uint32_t* point_list, const float* splats, int64_t* counts, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -415,18 +415,23 @@ static int walk_pixel(const orc_settings* set, double px, double py, const int* 
 }
 
 /* counts[0] = P_fwd (evaluated pairs), counts[1] = sum of n_contrib (walked by
-   the backward), counts[2] = blended pairs. */
+   the backward), counts[2] = blended pairs.  With tile_mask != NULL only the
+   pixels of tiles whose mask byte is non-zero are composited (the others are
+   left untouched); the backward then equals the full backward for an upstream
+   gradient that is zero outside those tiles. */
 int orc_render_fwd(const orc_camera* cam, const orc_settings* set, int global_list,
                    const int* point_list, const int64_t* ranges,
                    const double* uv, const double* conic, const double* opacity, const double* rgb,
                    double* image, double* final_T, int* n_contrib, double* wsum,
-                   unsigned char* ambiguous, double amb_rel, uint64_t* decision_hash, int64_t* counts)
+                   unsigned char* ambiguous, double amb_rel, uint64_t* decision_hash, int64_t* counts,
+                   const unsigned char* tile_mask)
 {
     const int W = cam->width, H = cam->height, ts = set->tile;
     const int tx = (W + ts - 1) / ts;
     counts[0] = counts[1] = counts[2] = 0;
     for (int y = 0; y < H; ++y)
         for (int x = 0; x < W; ++x) {
+            if (tile_mask && !tile_mask[(y / ts) * tx + (x / ts)]) continue;
             int t = global_list ? 0 : (y / ts) * tx + (x / ts);
             int64_t b = ranges[2 * t], e = ranges[2 * t + 1];
             double C[3], T, ws;
@@ -463,7 +468,7 @@ int orc_render_bwd(const orc_camera* cam, const orc_settings* set, int global_li
                    const int* point_list, const int64_t* ranges,
                    const double* uv, const double* conic, const double* opacity, const double* rgb,
                    const double* dL_dimage, double* dL_dxy, double* dL_dconic, double* dL_dopacity,
-                   double* dL_drgb, int N)
+                   double* dL_drgb, int N, const unsigned char* tile_mask)
 {
     const int W = cam->width, H = cam->height, ts = set->tile;
     const int tx = (W + ts - 1) / ts;
@@ -481,6 +486,7 @@ int orc_render_bwd(const orc_camera* cam, const orc_settings* set, int global_li
     orc_blend* st = (orc_blend*)malloc(sizeof(orc_blend) * (size_t)(maxlen + 1));
     for (int y = 0; y < H; ++y)
         for (int x = 0; x < W; ++x) {
+            if (tile_mask && !tile_mask[(y / ts) * tx + (x / ts)]) continue;
             int t = global_list ? 0 : (y / ts) * tx + (x / ts);
             int64_t b = ranges[2 * t], e = ranges[2 * t + 1];
             double C[3], T, ws;

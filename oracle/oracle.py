@@ -155,8 +155,16 @@ def global_list(valid, depth_k):
     return pl, np.array([[0, len(pl)]], np.int64)
 
 
-def render_fwd(cam, pre, point_list, ranges, s: Settings = None, brute=False, amb_rel=1e-4):
+def _tmask(tile_mask):
+    if tile_mask is None:
+        return None, None
+    m = np.ascontiguousarray(tile_mask, dtype=np.uint8)
+    return m, _p(m, C.c_uint8)
+
+
+def render_fwd(cam, pre, point_list, ranges, s: Settings = None, brute=False, amb_rel=1e-5, tile_mask=None):
     s = s or Settings()
+    tm, tmp = _tmask(tile_mask)
     W, H = cam.width, cam.height
     out = dict(image=np.zeros((3, H, W)), final_T=np.zeros((H, W)), n_contrib=np.zeros((H, W), np.int32),
                wsum=np.zeros((H, W)), ambiguous=np.zeros((H, W), np.uint8), hash=np.zeros((H, W), np.uint64),
@@ -167,12 +175,13 @@ def render_fwd(cam, pre, point_list, ranges, s: Settings = None, brute=False, am
                          _p(pl, C.c_int), _p(rg, C.c_int64), _p(_d(pre["uv"])), _p(_d(pre["conic"])),
                          _p(_d(pre["opacity"])), _p(_d(pre["rgb"])), _p(out["image"]), _p(out["final_T"]),
                          _p(out["n_contrib"], C.c_int), _p(out["wsum"]), _p(out["ambiguous"], C.c_uint8),
-                         C.c_double(amb_rel), _p(out["hash"], C.c_uint64), _p(out["counts"], C.c_int64))
+                         C.c_double(amb_rel), _p(out["hash"], C.c_uint64), _p(out["counts"], C.c_int64), tmp)
     return out
 
 
-def render_bwd(cam, pre, point_list, ranges, dL_dimage, s: Settings = None, brute=False):
+def render_bwd(cam, pre, point_list, ranges, dL_dimage, s: Settings = None, brute=False, tile_mask=None):
     s = s or Settings()
+    tm, tmp = _tmask(tile_mask)
     N = pre["uv"].shape[0]
     out = dict(dxy=np.zeros((N, 2)), dconic=np.zeros((N, 3)), dopacity=np.zeros(N), drgb=np.zeros((N, 3)))
     pl = np.ascontiguousarray(point_list, dtype=np.int32)
@@ -180,7 +189,7 @@ def render_bwd(cam, pre, point_list, ranges, dL_dimage, s: Settings = None, brut
     lib().orc_render_bwd(C.byref(cam_struct(cam)), C.byref(set_struct(s)), C.c_int(1 if brute else 0),
                          _p(pl, C.c_int), _p(rg, C.c_int64), _p(_d(pre["uv"])), _p(_d(pre["conic"])),
                          _p(_d(pre["opacity"])), _p(_d(pre["rgb"])), _p(_d(dL_dimage)),
-                         _p(out["dxy"]), _p(out["dconic"]), _p(out["dopacity"]), _p(out["drgb"]), C.c_int(N))
+                         _p(out["dxy"]), _p(out["dconic"]), _p(out["dopacity"]), _p(out["drgb"]), C.c_int(N), tmp)
     return out
 
 
@@ -229,7 +238,7 @@ def quat_renorm(q):
     return q
 
 
-def render(cam, deg, params, s: Settings = None, dL_dimage=None, brute=False, amb_rel=1e-4, backward=True):
+def render(cam, deg, params, s: Settings = None, dL_dimage=None, brute=False, amb_rel=1e-5, backward=True):
     """Full oracle pipeline: preprocess, bin, forward and (optionally) backward."""
     s = s or Settings()
     pre = preprocess(cam, deg, params, s)
