@@ -29,8 +29,8 @@ namespace gs {
 namespace {
 
 constexpr int kSortThreads = 256;
-constexpr int kSortIPT = 8;
-constexpr int kSortPart = kSortThreads * kSortIPT;  // 2048 items per partition
+constexpr int kSortIPT = 16;
+constexpr int kSortPart = kSortThreads * kSortIPT;  // 4096 items per partition
 constexpr int kRadix = 256;
 constexpr uint32_t kFlagAgg = 1u << 30;
 constexpr uint32_t kFlagInc = 2u << 30;
@@ -51,6 +51,23 @@ __device__ inline void st_release(uint32_t* p, uint32_t v) {
 __device__ inline uint64_t lanemask_lt() {
     const uint32_t lane = threadIdx.x & 63;
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Lanes whose 8-bit value equals this lane's (among lanes with valid set).
+__device__ inline uint64_t match8(uint32_t d, bool valid) {
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const uint64_t bb = __ballot((d >> b) & 1u);
+        m &= ((d >> b) & 1u) ? bb : ~bb;
+    }
+    return m;
+}
+
+// s_hist[bin] += 1 for every valid lane, one LDS atomic per distinct bin.
+__device__ inline void wave_hist_add(uint32_t* s_hist, uint32_t bin, bool valid) {
+    const uint64_t m = match8(bin, valid);
+    if (valid && (m & lanemask_lt()) == 0) atomicAdd(&s_hist[bin], (uint32_t)__popcll(m));
 }
 
 // Workspace layout (all offsets 256-byte aligned).
@@ -111,9 +128,10 @@ __global__ __launch_bounds__(256) void k_depth_keys(int32_t n, const float* dept
         const uint32_t k = tt[i] > 0 ? __float_as_uint(depth[i]) : 0xffffffffu;
         keys[i] = k;
         vals[i] = (uint32_t)i;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) atomicAdd(&sh[d * kRadix + ((k >> (8 * d)) & 255u)], 1u);
     }
+    const uint32_t k = i < n ? (tt[i] > 0 ? __float_as_uint(depth[i]) : 0xffffffffu) : 0u;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) wave_hist_add(sh + d * kRadix, (k >> (8 * d)) & 255u, i < n);
     __syncthreads();
     for (int b = threadIdx.x; b < 4 * kRadix; b += blockDim.x)
         if (sh[b]) atomicAdd(&hist[b], sh[b]);
@@ -138,7 +156,11 @@ struct PassArgs {
 __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
     __shared__ uint32_t s_off[kRadix];          // global exclusive digit offsets
     __shared__ uint32_t s_wave[4][kRadix];      // per-wave digit counts -> prefixes
-    __shared__ uint32_t s_base[kRadix];         // digit offset of this partition
+    __shared__ uint32_t s_base[kRadix];         // global offset of this partition's first item of digit d
+    __shared__ uint32_t s_blk[kRadix];          // block-local exclusive digit offsets
+    __shared__ uint32_t s_keys[kSortPart];      // partition in digit order
+    __shared__ uint32_t s_vals[kSortPart];
+    __shared__ uint32_t s_wsum[4];
     __shared__ uint32_t s_part;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -146,14 +168,12 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
     for (int i = tid; i < 4 * kRadix; i += kSortThreads) (&s_wave[0][0])[i] = 0;
     // exclusive scan of the digit histogram (256 entries, one per thread)
     {
-        uint32_t h = p.hist[tid];
+        const uint32_t h = p.hist[tid];
         uint32_t x = h;
-        // wave inclusive scan by shuffles
         for (int o = 1; o < 64; o <<= 1) {
-            uint32_t y = __shfl_up(x, o, 64);
+            const uint32_t y = __shfl_up(x, o, 64);
             if (lane >= o) x += y;
         }
-        __shared__ uint32_t s_wsum[4];
         if (lane == 63) s_wsum[wave] = x;
         __syncthreads();
         uint32_t add = 0;
@@ -173,25 +193,15 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
 #pragma unroll
     for (int i = 0; i < kSortIPT; ++i) {
         const uint32_t idx = base + i * 64 + lane;
-        if (idx < count) {
-            key[i] = p.keys_in[idx];
-            val[i] = p.vals_in[idx];
-        } else {
-            key[i] = 0u;
-            val[i] = 0xffffffffu;  // marks padding
-        }
+        key[i] = idx < count ? p.keys_in[idx] : 0u;
+        val[i] = idx < count ? p.vals_in[idx] : 0u;
     }
     const uint64_t lt = lanemask_lt();
 #pragma unroll
     for (int i = 0; i < kSortIPT; ++i) {
         const bool valid = (base + i * 64 + lane) < count;
         const uint32_t d = (key[i] >> p.shift) & 255u;
-        uint64_t m = __ballot(valid);
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const uint64_t bb = __ballot((d >> b) & 1u);
-            m &= ((d >> b) & 1u) ? bb : ~bb;
-        }
+        const uint64_t m = match8(d, valid);
         const uint32_t below = (uint32_t)__popcll(m & lt);
         const uint32_t prev = valid ? s_wave[wave][d] : 0u;
         rank[i] = prev + below;
@@ -200,12 +210,26 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
-    // per digit: prefix over waves, block total, look-back over partitions
+    // per digit: prefix over waves, block-local digit offsets, look-back over partitions
     {
         const int d = tid;
         const uint32_t c0 = s_wave[0][d], c1 = s_wave[1][d], c2 = s_wave[2][d], c3 = s_wave[3][d];
         const uint32_t total = c0 + c1 + c2 + c3;
         s_wave[0][d] = 0; s_wave[1][d] = c0; s_wave[2][d] = c0 + c1; s_wave[3][d] = c0 + c1 + c2;
+        // block-local exclusive scan of the digit totals
+        uint32_t x = total;
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        __syncthreads();  // s_wsum reuse
+        if (lane == 63) s_wsum[wave] = x;
+        __syncthreads();
+        uint32_t add = 0;
+        for (int w = 0; w < wave; ++w) add += s_wsum[w];
+        const uint32_t blk = x - total + add;
+        s_blk[d] = blk;
+
         uint32_t* st = p.status + (size_t)part * kRadix + d;
         uint32_t prefix = 0;
         if (part == 0) {
@@ -215,31 +239,43 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
             int j = (int)part - 1;
             uint32_t spins = 0;
             while (j >= 0) {
-                const uint32_t s = ld_acquire(p.status + (size_t)j * kRadix + d);
-                if ((s & ~kValMask) == 0u) {
+                const uint32_t sv = ld_acquire(p.status + (size_t)j * kRadix + d);
+                if ((sv & ~kValMask) == 0u) {
                     if (++spins > kSpinLimit) { atomicOr(p.err, 1u); break; }
                     __builtin_amdgcn_s_sleep(1);
                     continue;
                 }
-                prefix += s & kValMask;
-                if (s & kFlagInc) break;
+                prefix += sv & kValMask;
+                if (sv & kFlagInc) break;
                 --j;
             }
             st_release(st, kFlagInc | ((prefix + total) & kValMask));
         }
-        s_base[d] = s_off[d] + prefix;
+        // global position of local slot q (digit d) = s_base[d] + q
+        s_base[d] = s_off[d] + prefix - blk;
     }
     __syncthreads();
+    // stage the partition in digit order in LDS ...
 #pragma unroll
     for (int i = 0; i < kSortIPT; ++i) {
-        const uint32_t idx = base + i * 64 + lane;
-        if (idx < count) {
+        if (base + i * 64 + lane < count) {
             const uint32_t d = (key[i] >> p.shift) & 255u;
-            const uint32_t pos = s_base[d] + s_wave[wave][d] + rank[i];
-            if (pos < count) {  // always true for a consistent histogram; guards the buffers
-                if (p.keys_out) p.keys_out[pos] = key[i];
-                p.vals_out[pos] = val[i];
+            const uint32_t q = s_blk[d] + s_wave[wave][d] + rank[i];
+            if (q < (uint32_t)kSortPart) {  // always true for a consistent ranking
+                s_keys[q] = key[i];
+                s_vals[q] = val[i];
             }
+        }
+    }
+    __syncthreads();
+    // ... and write it out: consecutive slots of one digit go to consecutive addresses
+    const uint32_t nloc = min((uint32_t)kSortPart, count - part * kSortPart);
+    for (uint32_t q = tid; q < nloc; q += kSortThreads) {
+        const uint32_t k = s_keys[q];
+        const uint32_t pos = s_base[(k >> p.shift) & 255u] + q;
+        if (pos < count) {  // always true for a consistent histogram; guards the buffers
+            if (p.keys_out) p.keys_out[pos] = k;
+            p.vals_out[pos] = s_vals[q];
         }
     }
 }
@@ -262,8 +298,15 @@ struct EmitArgs {
 };
 
 // 3. scan of tiles_touched in depth order + emit of (tile, Gaussian) pairs.
+// Each block scans its 1024 depth-sorted Gaussians, gets its output offset by
+// decoupled look-back, then expands entry-parallel: thread t writes entries
+// t, t+256, ... of the block's output range, finding each entry's Gaussian
+// by binary search over the block's offsets in LDS (balanced and coalesced).
 __global__ __launch_bounds__(kEmitThreads) void k_emit(EmitArgs a) {
     __shared__ uint32_t s_hist[2 * kRadix];
+    __shared__ uint32_t s_off[kEmitPart];   // block-local exclusive offsets
+    __shared__ uint32_t s_g[kEmitPart];     // Gaussian ids
+    __shared__ uint2 s_rect[kEmitPart];
     __shared__ uint32_t s_wsum[4];
     __shared__ uint32_t s_prefix;
     __shared__ uint32_t s_part;
@@ -284,7 +327,7 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(EmitArgs a) {
     // block exclusive scan of the per-thread sums
     uint32_t x = tsum;
     for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o, 64);
+        const uint32_t y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
     }
     if (lane == 63) s_wsum[wave] = x;
@@ -294,7 +337,15 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(EmitArgs a) {
         if (w < wave) wadd += s_wsum[w];
         btotal += s_wsum[w];
     }
-    uint32_t excl = x - tsum + wadd;
+    uint32_t off = x - tsum + wadd;
+#pragma unroll
+    for (int k = 0; k < kEmitIPT; ++k) {
+        const int q = tid * kEmitIPT + k;
+        s_off[q] = off;
+        s_g[q] = g[k];
+        s_rect[q] = cnt[k] ? reinterpret_cast<const uint2*>(a.rect)[g[k]] : make_uint2(0u, 0u);
+        off += cnt[k];
+    }
     // decoupled look-back for the partition prefix
     if (tid == 0) {
         uint32_t prefix = 0;
@@ -306,14 +357,14 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(EmitArgs a) {
             int j = (int)part - 1;
             uint32_t spins = 0;
             while (j >= 0) {
-                const uint32_t s = ld_acquire(a.status + j);
-                if ((s & ~kValMask) == 0u) {
+                const uint32_t sv = ld_acquire(a.status + j);
+                if ((sv & ~kValMask) == 0u) {
                     if (++spins > kSpinLimit) { atomicOr(a.err, 1u); break; }
                     __builtin_amdgcn_s_sleep(1);
                     continue;
                 }
-                prefix += s & kValMask;
-                if (s & kFlagInc) break;
+                prefix += sv & kValMask;
+                if (sv & kFlagInc) break;
                 --j;
             }
             st_release(st, kFlagInc | ((prefix + btotal) & kValMask));
@@ -327,24 +378,30 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(EmitArgs a) {
         }
     }
     __syncthreads();
-    uint32_t off = s_prefix + excl;
-#pragma unroll
-    for (int k = 0; k < kEmitIPT; ++k) {
-        if (cnt[k] == 0) continue;
-        const uint2 r = reinterpret_cast<const uint2*>(a.rect)[g[k]];
+    const uint32_t prefix = s_prefix;
+    for (uint32_t o = tid; o < btotal; o += kEmitThreads) {
+        // last q with s_off[q] <= o (entries of empty Gaussians share offsets; the
+        // last one wins, which is the non-empty Gaussian owning entry o)
+        int lo = 0, hi = kEmitPart - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= o) lo = mid; else hi = mid - 1;
+        }
+        const uint2 r = s_rect[lo];
         const int x0 = (int)(int16_t)(r.x & 0xffffu), y0 = (int)(int16_t)(r.x >> 16);
-        const int x1 = (int)(int16_t)(r.y & 0xffffu), y1 = (int)(int16_t)(r.y >> 16);
-        for (int ty = y0; ty < y1; ++ty)
-            for (int tx = x0; tx < x1; ++tx) {
-                const uint32_t tile = (uint32_t)(ty * a.tiles_x + tx);
-                if (off < a.cap) {
-                    a.tkeys[off] = tile;
-                    a.tvals[off] = g[k];
-                    atomicAdd(&s_hist[tile & 255u], 1u);
-                    atomicAdd(&s_hist[kRadix + ((tile >> 8) & 255u)], 1u);
-                }
-                ++off;
-            }
+        const int x1 = (int)(int16_t)(r.y & 0xffffu);
+        const int w = x1 - x0;
+        const int local = (int)(o - s_off[lo]);
+        const int ty = y0 + local / w, tx = x0 + local % w;
+        const uint32_t tile = (uint32_t)(ty * a.tiles_x + tx);
+        const uint32_t out = prefix + o;
+        const bool ok = out < a.cap;
+        if (ok) {
+            a.tkeys[out] = tile;
+            a.tvals[out] = s_g[lo];
+        }
+        wave_hist_add(s_hist, tile & 255u, ok);
+        wave_hist_add(s_hist + kRadix, (tile >> 8) & 255u, ok);
     }
     __syncthreads();
     for (int b = tid; b < 2 * kRadix; b += kEmitThreads)

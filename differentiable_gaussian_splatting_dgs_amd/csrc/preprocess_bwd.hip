@@ -15,23 +15,36 @@
 namespace gs {
 namespace {
 
+constexpr int kG = 128;        // Gaussians per block: one per thread in the per-Gaussian phase
+constexpr int kThreads = 256;  // threads per block for the staging and element-wise phases
+
+struct AdamHyper {
+    float* m[5];  // first moments: means, log_scales, quats, opacity_logits, sh
+    float* v[5];  // second moments, same order
+    float lr[6];  // means, log_scales, quats, opacity_logits, sh band 0, sh bands >= 1
+    float b1, b2, eps, inv_c1, inv_sqrt_c2;
+};
+
 struct BwdArgs {
     CamArgs cam;
     float dilation;
     int32_t n;
-    const float* means;
-    const float* log_scales;
-    const float* quats;
-    const float* opac;
-    const float* sh;
+    float* means;  // read; updated in place by the Adam variant
+    float* log_scales;
+    float* quats;
+    float* opac;
+    float* sh;
     const int32_t* tt;
     const uint8_t* clamp;
     const float* grad2d;
-    float* dmeans;
+    float* dmeans;  // gradient outputs, each optional in the Adam variant
     float* dls;
     float* dquats;
     float* dopac;
     float* dsh;
+    float* accum;   // densification statistic, optional
+    int32_t* count;
+    AdamHyper adam;
 };
 
 // SH values Y[k] at unit direction (x, y, z) and the gradient of
@@ -92,23 +105,23 @@ __device__ __forceinline__ void sh_grad(float x, float y, float z, const float* 
     }
 }
 
+__device__ __forceinline__ void adam1(float& p, float g, float* m, float* v, size_t i, float lr,
+                                      const AdamHyper& h) {
+    const float mm = h.b1 * m[i] + (1.f - h.b1) * g;
+    const float vv = h.b2 * v[i] + (1.f - h.b2) * g * g;
+    m[i] = mm;
+    v[i] = vv;
+    p -= lr * (mm * h.inv_c1) / (sqrtf(vv) * h.inv_sqrt_c2 + h.eps);
+}
+
+// The per-Gaussian part of the chain: gradients of the mean, log-scales, raw
+// quaternion and opacity logit, plus the SH basis and the clamp-masked colour
+// gradient the SH coefficients need.  ddir needs the SH coefficients, read
+// from the block's LDS copy (coefficient-major, row stride ldg).
 template <int DEG>
-__global__ __launch_bounds__(256) void k_preprocess_bwd(BwdArgs a) {
+__device__ __forceinline__ void chain(const BwdArgs& a, int i, const float* s_sh, int col, int ldg, float dmu[3],
+                                      float dls[3], float dq[4], float& dop, float Y[16], float drgb[3]) {
     constexpr int K = (DEG + 1) * (DEG + 1);
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= a.n) return;
-    float* dmu = a.dmeans + 3 * (size_t)i;
-    float* dls = a.dls + 3 * (size_t)i;
-    float4* dq4 = reinterpret_cast<float4*>(a.dquats) + i;
-    float* dshi = a.dsh + (size_t)i * K * 3;
-    if (a.tt[i] <= 0) {
-        dmu[0] = dmu[1] = dmu[2] = 0.f;
-        dls[0] = dls[1] = dls[2] = 0.f;
-        *dq4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        a.dopac[i] = 0.f;
-        for (int k = 0; k < 3 * K; ++k) dshi[k] = 0.f;
-        return;
-    }
     const CamArgs& c = a.cam;
     const float Rv[9] = {(float)c.R[0], (float)c.R[1], (float)c.R[2], (float)c.R[3], (float)c.R[4],
                          (float)c.R[5], (float)c.R[6], (float)c.R[7], (float)c.R[8]};
@@ -122,35 +135,29 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(BwdArgs a) {
     const float4 g1 = reinterpret_cast<const float4*>(a.grad2d)[3 * (size_t)i + 1];
     const float4 g2 = reinterpret_cast<const float4*>(a.grad2d)[3 * (size_t)i + 2];
     const float du = g0.x, dv = g0.y, dA = g0.z, dB = g0.w, dC = g1.x, dsig = g1.y;
-    float drgb[3] = {g1.z, g1.w, g2.x};
+    drgb[0] = g1.z; drgb[1] = g1.w; drgb[2] = g2.x;
 
     // opacity
     const float sig = 1.f / (1.f + __expf(-a.opac[i]));
-    a.dopac[i] = dsig * sig * (1.f - sig);
+    dop = dsig * sig * (1.f - sig);
 
-    // colour -> SH
+    // colour -> SH; the view direction depends on the mean
     const float cpx = -(float)(c.R[0] * c.t[0] + c.R[3] * c.t[1] + c.R[6] * c.t[2]);
     const float cpy = -(float)(c.R[1] * c.t[0] + c.R[4] * c.t[1] + c.R[7] * c.t[2]);
     const float cpz = -(float)(c.R[2] * c.t[0] + c.R[5] * c.t[1] + c.R[8] * c.t[2]);
     const float vx = mx - cpx, vy = my - cpy, vz = mz - cpz;
-    const float vlen = sqrtf(vx * vx + vy * vy + vz * vz);
-    const float il = 1.f / vlen;
+    const float il = 1.f / sqrtf(vx * vx + vy * vy + vz * vz);
     const float dx = vx * il, dy = vy * il, dz = vz * il;
     const uint8_t cm = a.clamp[i];
 #pragma unroll
     for (int ch = 0; ch < 3; ++ch)
         if ((cm >> ch) & 1u) drgb[ch] = 0.f;
-    float Y[16], w[16];
     sh_values<DEG>(dx, dy, dz, Y);
-    const float* shi = a.sh + (size_t)i * K * 3;
+    float w[16];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const float s0 = shi[3 * k], s1 = shi[3 * k + 1], s2 = shi[3 * k + 2];
-        w[k] = drgb[0] * s0 + drgb[1] * s1 + drgb[2] * s2;
-        dshi[3 * k] = Y[k] * drgb[0];
-        dshi[3 * k + 1] = Y[k] * drgb[1];
-        dshi[3 * k + 2] = Y[k] * drgb[2];
-    }
+    for (int k = 0; k < K; ++k)
+        w[k] = drgb[0] * s_sh[(3 * k) * ldg + col] + drgb[1] * s_sh[(3 * k + 1) * ldg + col] +
+               drgb[2] * s_sh[(3 * k + 2) * ldg + col];
     float gdx, gdy, gdz;
     sh_grad<DEG>(dx, dy, dz, w, gdx, gdy, gdz);
     const float dot = dx * gdx + dy * gdy + dz * gdz;
@@ -158,11 +165,9 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(BwdArgs a) {
 
     // rotation and scale: M = R(q/|q|) diag(s)
     const float4 q = reinterpret_cast<const float4*>(a.quats)[i];
-    const float qn = sqrtf(q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w);
-    const float iq = 1.f / qn;
+    const float iq = 1.f / sqrtf(q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w);
     const float qw = q.x * iq, qx = q.y * iq, qy = q.z * iq, qz = q.w * iq;
-    const float s[3] = {__expf(a.log_scales[3 * i]), __expf(a.log_scales[3 * i + 1]),
-                        __expf(a.log_scales[3 * i + 2])};
+    const float s[3] = {__expf(a.log_scales[3 * i]), __expf(a.log_scales[3 * i + 1]), __expf(a.log_scales[3 * i + 2])};
     float R[9];
     R[0] = 1.f - 2.f * (qy * qy + qz * qz); R[1] = 2.f * (qx * qy - qw * qz); R[2] = 2.f * (qx * qz + qw * qy);
     R[3] = 2.f * (qx * qy + qw * qz); R[4] = 1.f - 2.f * (qx * qx + qz * qz); R[5] = 2.f * (qy * qz - qw * qx);
@@ -176,7 +181,8 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 3; ++r)
 #pragma unroll
-        for (int k = 0; k < 3; ++k) Sig[3 * r + k] = M[3 * r] * M[3 * k] + M[3 * r + 1] * M[3 * k + 1] + M[3 * r + 2] * M[3 * k + 2];
+        for (int k = 0; k < 3; ++k)
+            Sig[3 * r + k] = M[3 * r] * M[3 * k] + M[3 * r + 1] * M[3 * k + 1] + M[3 * r + 2] * M[3 * k + 2];
 
     // T = J R_view
     const float iz = 1.f / tz, iz2 = iz * iz;
@@ -256,7 +262,132 @@ __global__ __launch_bounds__(256) void k_preprocess_bwd(BwdArgs a) {
     const float gz = 2.f * (-2.f * qz * dR[0] - qw * dR[1] + qx * dR[2] + qw * dR[3] - 2.f * qz * dR[4] +
                             qy * dR[5] + qx * dR[6] + qy * dR[7]);
     const float pr = qw * gw + qx * gx + qy * gy + qz * gz;
-    *dq4 = make_float4((gw - qw * pr) * iq, (gx - qx * pr) * iq, (gy - qy * pr) * iq, (gz - qz * pr) * iq);
+    dq[0] = (gw - qw * pr) * iq;
+    dq[1] = (gx - qx * pr) * iq;
+    dq[2] = (gy - qy * pr) * iq;
+    dq[3] = (gz - qz * pr) * iq;
+}
+
+// One block of kThreads threads per kG Gaussians.
+//  phase 0: the block's SH coefficients, contiguous in HBM, are copied into LDS
+//           coefficient-major (row stride kG + 1: conflict-free both ways);
+//  phase 1: one thread per Gaussian (the first kG threads) runs the chain, writes or applies (Adam)
+//           the mean / scale / quaternion / opacity gradients and the
+//           densification statistic, and leaves Y and the colour gradient in LDS;
+//  phase 2: the SH gradients Y_k dL/dc, element by element in HBM order, so
+//           gradient writes and the Adam read-modify-write are coalesced.
+template <int DEG, bool ADAM>
+__global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    constexpr int J = 3 * K;
+    constexpr int LDG = kG + 1;
+    __shared__ float s_sh[J * LDG];
+    __shared__ float s_y[K * LDG];
+    __shared__ float s_c[3 * LDG];
+    const int t = threadIdx.x;
+    const int g0 = blockIdx.x * kG;
+    const int ng = min(kG, a.n - g0);
+    const int cnt = ng * J;
+    const size_t base = (size_t)g0 * J;
+
+#pragma unroll 4
+    for (int e = t; e < cnt; e += kThreads) {
+        const int g = e / J, j = e - g * J;
+        s_sh[j * LDG + g] = a.sh[base + e];
+    }
+    __syncthreads();
+
+    if (t < ng) {
+        const int i = g0 + t;
+        float dmu[3] = {0.f, 0.f, 0.f}, dls[3] = {0.f, 0.f, 0.f}, dq[4] = {0.f, 0.f, 0.f, 0.f}, dop = 0.f;
+        float Y[16], drgb[3] = {0.f, 0.f, 0.f};
+        const bool vis = a.tt[i] > 0;
+        if (vis) {
+            chain<DEG>(a, i, s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb);
+            if (a.accum) {
+                const float2 d2 = *reinterpret_cast<const float2*>(a.grad2d + (size_t)i * GS_GRAD2D_STRIDE);
+                a.accum[i] += sqrtf(d2.x * d2.x + d2.y * d2.y);
+                a.count[i] += 1;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) Y[k] = 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) s_y[k * LDG + t] = Y[k];
+        s_c[t] = drgb[0];
+        s_c[LDG + t] = drgb[1];
+        s_c[2 * LDG + t] = drgb[2];
+        if (a.dmeans) {
+            a.dmeans[3 * (size_t)i] = dmu[0]; a.dmeans[3 * (size_t)i + 1] = dmu[1]; a.dmeans[3 * (size_t)i + 2] = dmu[2];
+            a.dls[3 * (size_t)i] = dls[0]; a.dls[3 * (size_t)i + 1] = dls[1]; a.dls[3 * (size_t)i + 2] = dls[2];
+            reinterpret_cast<float4*>(a.dquats)[i] = make_float4(dq[0], dq[1], dq[2], dq[3]);
+            a.dopac[i] = dop;
+        }
+        if (ADAM) {
+            const AdamHyper& h = a.adam;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                float p = a.means[3 * (size_t)i + k];
+                adam1(p, dmu[k], h.m[0], h.v[0], 3 * (size_t)i + k, h.lr[0], h);
+                a.means[3 * (size_t)i + k] = p;
+                float ps = a.log_scales[3 * (size_t)i + k];
+                adam1(ps, dls[k], h.m[1], h.v[1], 3 * (size_t)i + k, h.lr[1], h);
+                a.log_scales[3 * (size_t)i + k] = ps;
+            }
+            float4 q = reinterpret_cast<float4*>(a.quats)[i];
+            float qv[4] = {q.x, q.y, q.z, q.w};
+            float ss = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                adam1(qv[k], dq[k], h.m[2], h.v[2], 4 * (size_t)i + k, h.lr[2], h);
+                ss += qv[k] * qv[k];
+            }
+            const float inv = 1.f / sqrtf(ss);  // renormalise after the update
+            reinterpret_cast<float4*>(a.quats)[i] = make_float4(qv[0] * inv, qv[1] * inv, qv[2] * inv, qv[3] * inv);
+            float po = a.opac[i];
+            adam1(po, dop, h.m[3], h.v[3], i, h.lr[3], h);
+            a.opac[i] = po;
+        }
+    }
+    __syncthreads();
+
+#pragma unroll 4
+    for (int e = t; e < cnt; e += kThreads) {
+        const int g = e / J, j = e - g * J;
+        const int k = j / 3, ch = j - 3 * k;
+        const float grad = s_y[k * LDG + g] * s_c[ch * LDG + g];
+        if (a.dsh) a.dsh[base + e] = grad;
+        if (ADAM) {
+            const AdamHyper& h = a.adam;
+            float p = s_sh[j * LDG + g];
+            adam1(p, grad, h.m[4], h.v[4], base + e, k == 0 ? h.lr[4] : h.lr[5], h);
+            a.sh[base + e] = p;
+        }
+    }
+}
+
+template <bool ADAM>
+inline void launch_grad3d(int deg, const BwdArgs& a, hipStream_t s) {
+    const dim3 grid((a.n + kG - 1) / kG), block(kThreads);
+    switch (deg) {
+        case 0: hipLaunchKernelGGL((k_grad3d<0, ADAM>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((k_grad3d<1, ADAM>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_grad3d<2, ADAM>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_grad3d<3, ADAM>), grid, block, 0, s, a); break;
+    }
+}
+
+inline void fill_common(BwdArgs& a, const gs_camera* cam, const gs_settings* set, int32_t n, const float* means,
+                        const float* log_scales, const float* quats, const float* opacity_logits, const float* sh,
+                        const int32_t* tt, const uint8_t* clamp, const float* grad2d) {
+    a = BwdArgs{};
+    a.cam = cam_args(cam);
+    a.dilation = (float)set->dilation;
+    a.n = n;
+    a.means = const_cast<float*>(means); a.log_scales = const_cast<float*>(log_scales);
+    a.quats = const_cast<float*>(quats); a.opac = const_cast<float*>(opacity_logits); a.sh = const_cast<float*>(sh);
+    a.tt = tt; a.clamp = clamp; a.grad2d = grad2d;
 }
 
 }  // namespace
@@ -277,19 +408,39 @@ extern "C" int gs_preprocess_bwd(const gs_camera* cam, const gs_settings* set, i
         return GS_EINVAL;
     if (!aligned16(quats) || !aligned16(grad2d) || !aligned16(dquats)) return GS_EALIGN;
     BwdArgs a;
-    a.cam = cam_args(cam);
-    a.dilation = (float)set->dilation;
-    a.n = n;
-    a.means = means; a.log_scales = log_scales; a.quats = quats; a.opac = opacity_logits; a.sh = sh;
-    a.tt = tiles_touched; a.clamp = clamp_mask; a.grad2d = grad2d;
+    fill_common(a, cam, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
     a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
-    const dim3 grid((n + 255) / 256), block(256);
-    hipStream_t s = as_stream(stream);
-    switch (sh_degree) {
-        case 0: hipLaunchKernelGGL(k_preprocess_bwd<0>, grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL(k_preprocess_bwd<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(k_preprocess_bwd<2>, grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL(k_preprocess_bwd<3>, grid, block, 0, s, a); break;
-    }
+    launch_grad3d<false>(sh_degree, a, as_stream(stream));
+    return launch_status();
+}
+
+extern "C" int gs_preprocess_bwd_adam(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                                      float* means, float* log_scales, float* quats, float* opacity_logits,
+                                      float* sh, const int32_t* tiles_touched, const uint8_t* clamp_mask,
+                                      const float* grad2d, const gs_adam_state* adam, float* densify_accum,
+                                      int32_t* densify_count, float* dmeans, float* dlog_scales, float* dquats,
+                                      float* dopacity_logits, float* dsh, void* stream) {
+    if (!camera_ok(cam) || !set || !adam || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE)
+        return GS_EINVAL;
+    if (adam->step < 1) return GS_EINVAL;
+    if (n == 0) return GS_OK;
+    if (!means || !log_scales || !quats || !opacity_logits || !sh || !tiles_touched || !clamp_mask || !grad2d)
+        return GS_EINVAL;
+    for (int k = 0; k < 5; ++k)
+        if (!adam->exp_avg[k] || !adam->exp_avg_sq[k]) return GS_EINVAL;
+    if ((densify_accum == nullptr) != (densify_count == nullptr)) return GS_EINVAL;
+    const bool any_grad = dmeans || dlog_scales || dquats || dopacity_logits;
+    if (any_grad && !(dmeans && dlog_scales && dquats && dopacity_logits)) return GS_EINVAL;
+    if (!aligned16(quats) || !aligned16(grad2d) || (dquats && !aligned16(dquats))) return GS_EALIGN;
+    BwdArgs a;
+    fill_common(a, cam, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
+    a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
+    a.accum = densify_accum; a.count = densify_count;
+    for (int k = 0; k < 5; ++k) { a.adam.m[k] = adam->exp_avg[k]; a.adam.v[k] = adam->exp_avg_sq[k]; }
+    for (int k = 0; k < 6; ++k) a.adam.lr[k] = adam->lr[k];
+    a.adam.b1 = adam->beta1; a.adam.b2 = adam->beta2; a.adam.eps = adam->eps;
+    a.adam.inv_c1 = (float)(1.0 / (1.0 - pow((double)adam->beta1, adam->step)));
+    a.adam.inv_sqrt_c2 = (float)(1.0 / sqrt(1.0 - pow((double)adam->beta2, adam->step)));
+    launch_grad3d<true>(sh_degree, a, as_stream(stream));
     return launch_status();
 }

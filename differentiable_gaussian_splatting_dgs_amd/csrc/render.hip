@@ -69,6 +69,15 @@ struct Stage {
     float* g2;
 };
 
+// Minimum over the segment t in [t0, t1] of (a*c + b*t)^2 + (l*t)^2, the exponent
+// |L^T d|^2 along an axis-parallel edge of a rectangle (c is the fixed coordinate).
+__device__ __forceinline__ float edge_min(float a, float b, float l, float c, float t0, float t1, float slope) {
+    const float t = fminf(fmaxf(c * slope, t0), t1);
+    const float e1 = __builtin_fmaf(a, c, b * t);
+    const float e2 = l * t;
+    return __builtin_fmaf(e1, e1, e2 * e2);
+}
+
 __device__ __forceinline__ uint32_t stage_entry(const RenderArgs& a, uint32_t g, float x0, float y0,
                                                 float inv_amin, Stage st, int slot) {
     const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
@@ -78,21 +87,29 @@ __device__ __forceinline__ uint32_t stage_entry(const RenderArgs& a, uint32_t g,
     st.g0[slot] = make_float4(ut, vt, r1.x, r1.y);
     st.g1[slot] = make_float4(r1.z, r1.w, r2.x, r2.y);
     st.g2[slot] = r2.z;
-    // |L^T d|^2 <= k2 = log2(opacity / alpha_min): bounding box of that ellipse
-    const float k2 = fmaxf(__log2f(r1.w * inv_amin), 0.f);
+    // A quadrant can see the Gaussian only if min over its pixel centres of
+    // q = |L^T d|^2 (d = p - mean) is <= k2 = log2(opacity / alpha_min).  The test
+    // is exact for the rectangle of pixel centres; the threshold gets a relative
+    // margin of 1/64 plus 1/16 so float32 rounding can only keep extra entries,
+    // never drop one that a pixel would blend.
     const float l00 = r1.x, l10 = r1.y, l11 = r1.z;
-    const float sk = sqrtf(k2);
-    float ey = sk / l11;
-    float ex = sk * sqrtf(l10 * l10 + l11 * l11) / (l00 * l11);
-    ex = ex * (1.f + 1.f / 256.f) + 1.f / 32.f;
-    ey = ey * (1.f + 1.f / 256.f) + 1.f / 32.f;
+    const float k2 = fmaxf(__log2f(r1.w * inv_amin), 0.f);
+    const float kq = __builtin_fmaf(k2, 1.f + 1.f / 64.f, 1.f / 16.f);
+    const float sv = -l00 * l10 / __builtin_fmaf(l10, l10, l11 * l11);  // minimiser slope on vertical edges
+    const float sh = -l10 / l00;                                         // and on horizontal edges
     uint32_t m = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const float qx = (float)((q & 1) * 8), qy = (float)((q >> 1) * 8);
-        const bool hit = (ut + ex >= qx + 0.5f) && (ut - ex <= qx + 7.5f) && (vt + ey >= qy + 0.5f) &&
-                         (vt - ey <= qy + 7.5f);
-        m |= hit ? (1u << q) : 0u;
+        const float rx0 = (float)((q & 1) * 8) + 0.5f - ut, rx1 = rx0 + 7.f;
+        const float ry0 = (float)((q >> 1) * 8) + 0.5f - vt, ry1 = ry0 + 7.f;
+        const bool inside = rx0 <= 0.f && rx1 >= 0.f && ry0 <= 0.f && ry1 >= 0.f;
+        // vertical edges: dx fixed, dy free in [ry0, ry1]; horizontal: dy fixed, dx free
+        float mn = fminf(edge_min(l00, l10, l11, rx0, ry0, ry1, sv), edge_min(l00, l10, l11, rx1, ry0, ry1, sv));
+        const float th0 = fminf(fmaxf(ry0 * sh, rx0), rx1), th1 = fminf(fmaxf(ry1 * sh, rx0), rx1);
+        const float a0 = __builtin_fmaf(l00, th0, l10 * ry0), b0 = l11 * ry0;
+        const float a1 = __builtin_fmaf(l00, th1, l10 * ry1), b1 = l11 * ry1;
+        mn = fminf(mn, fminf(__builtin_fmaf(a0, a0, b0 * b0), __builtin_fmaf(a1, a1, b1 * b1)));
+        m |= (inside || mn <= kq) ? (1u << q) : 0u;
     }
     return m;
 }
@@ -152,24 +169,40 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
         __syncthreads();
         const int cnt = wave_done ? 0 : compact(s_mask, s_list[wave], wave, lane);
         const int base = (int)(start - range.x);
-        for (int j = 0; j < cnt; ++j) {
-            const int e = s_list[wave][j];
-            const float4 g0 = s_g0[e], g1 = s_g1[e];
-            const float cb = s_g2[e];
-            const Pair p = eval_pair(fx, fy, g0, g1, b.alpha_max);
-            bool ok = !done && p.alpha >= b.alpha_min;
-            const float om = 1.f - p.alpha;
-            const float Tn = T * om;
-            const bool stop = ok && Tn < b.T_min;
-            done = done || stop;
-            ok = ok && !stop;
-            if (ok) {
-                const float w = p.alpha * T;
-                C0 = __builtin_fmaf(w, g1.z, C0);
-                C1 = __builtin_fmaf(w, g1.w, C1);
-                C2 = __builtin_fmaf(w, cb, C2);
-                T = Tn;
-                last = base + e + 1;
+        for (int j = 0; j < cnt; j += 2) {
+            const bool has2 = j + 1 < cnt;
+            const int ea = s_list[wave][j];
+            const int eb = has2 ? s_list[wave][j + 1] : ea;
+            const float4 ga0 = s_g0[ea], ga1 = s_g1[ea];
+            const float4 gb0 = s_g0[eb], gb1 = s_g1[eb];
+            const float cba = s_g2[ea], cbb = s_g2[eb];
+            const Pair pa = eval_pair(fx, fy, ga0, ga1, b.alpha_max);
+            const Pair pb = eval_pair(fx, fy, gb0, gb1, b.alpha_max);
+            {
+                bool ok = !done && pa.alpha >= b.alpha_min;
+                const float Tn = T * (1.f - pa.alpha);
+                const bool stop = ok && Tn < b.T_min;
+                done = done || stop;
+                ok = ok && !stop;
+                const float w = ok ? pa.alpha * T : 0.f;
+                C0 = __builtin_fmaf(w, ga1.z, C0);
+                C1 = __builtin_fmaf(w, ga1.w, C1);
+                C2 = __builtin_fmaf(w, cba, C2);
+                T = ok ? Tn : T;
+                last = ok ? base + ea + 1 : last;
+            }
+            {
+                bool ok = has2 && !done && pb.alpha >= b.alpha_min;
+                const float Tn = T * (1.f - pb.alpha);
+                const bool stop = ok && Tn < b.T_min;
+                done = done || stop;
+                ok = ok && !stop;
+                const float w = ok ? pb.alpha * T : 0.f;
+                C0 = __builtin_fmaf(w, gb1.z, C0);
+                C1 = __builtin_fmaf(w, gb1.w, C1);
+                C2 = __builtin_fmaf(w, cbb, C2);
+                T = ok ? Tn : T;
+                last = ok ? base + eb + 1 : last;
             }
             if (__ballot(!done) == 0) break;
         }
@@ -316,35 +349,34 @@ __global__ __launch_bounds__(kBlock) void k_render_bwd(RenderArgs a) {
             const float cb = s_g2[e];
             const Pair p = eval_pair(fx, fy, g0, g1, b.alpha_max);
             const bool ok = pos < nc && p.alpha >= b.alpha_min;
+            if (__ballot(ok) == 0) continue;
+            // branch-free: lanes that do not blend this entry get zero weights
+            const float ae = ok ? p.alpha : 0.f;
+            const float Tp = T * __builtin_amdgcn_rcpf(1.f - p.alpha);  // transmittance before this entry
+            T = ok ? Tp : T;
+            const float w = ae * T;
+            const float d0 = g1.z - Cn0, d1 = g1.w - Cn1, d2 = cb - Cn2;
+            const float dalpha = T * __builtin_fmaf(g2c, d2, __builtin_fmaf(g1c, d1, g0c * d0));
+            Cn0 = __builtin_fmaf(ae, d0, Cn0);
+            Cn1 = __builtin_fmaf(ae, d1, Cn1);
+            Cn2 = __builtin_fmaf(ae, d2, Cn2);
+            const float dsG = (ok && !(p.sG > b.alpha_max)) ? dalpha : 0.f;  // clamped: no dependence
             float v[8], v8;
-            if (ok) {
-                const float om = 1.f - p.alpha;
-                T = T * __builtin_amdgcn_rcpf(om);  // transmittance before this entry
-                const float w = p.alpha * T;
-                const float d0 = g1.z - Cn0, d1 = g1.w - Cn1, d2 = cb - Cn2;
-                const float dalpha = T * (g0c * d0 + g1c * d1 + g2c * d2);
-                Cn0 = __builtin_fmaf(p.alpha, d0, Cn0);
-                Cn1 = __builtin_fmaf(p.alpha, d1, Cn1);
-                Cn2 = __builtin_fmaf(p.alpha, d2, Cn2);
-                const float dsG = p.sG > b.alpha_max ? 0.f : dalpha;  // clamped: no dependence
-                const float dpow = dsG * g1.y * p.G;                   // d/dpower, G = exp(power)
-                const float qx = k2ln2 * g0.z * p.e1;                  // (conic d)_x
-                const float qy = k2ln2 * (g0.w * p.e1 + g1.x * p.e2);  // (conic d)_y
-                v[0] = qx * dpow;
-                v[1] = qy * dpow;
-                v[2] = -0.5f * p.dx * p.dx * dpow;
-                v[3] = -p.dx * p.dy * dpow;
-                v[4] = -0.5f * p.dy * p.dy * dpow;
-                v[5] = dsG * p.G;
-                v[6] = w * g0c;
-                v[7] = w * g1c;
-                v8 = w * g2c;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = 0.f;
-                v8 = 0.f;
-            }
-            if (__ballot(ok) != 0) {
+            v[5] = dsG * p.G;                       // dL/dopacity
+            const float dpow = v[5] * g1.y;         // dL/dpower, G = exp(power)
+            const float h = -0.5f * dpow;
+            const float hx = h * p.dx, hy = h * p.dy;
+            v[2] = hx * p.dx;                       // -dx^2/2 dpower
+            v[3] = (hx + hx) * p.dy;                // -dx dy dpower
+            v[4] = hy * p.dy;                       // -dy^2/2 dpower
+            const float kd = k2ln2 * dpow;          // conic d = 2 ln2 L e
+            const float t1 = kd * p.e1;
+            v[0] = t1 * g0.z;
+            v[1] = __builtin_fmaf(t1, g0.w, (kd * p.e2) * g1.x);
+            v[6] = w * g0c;
+            v[7] = w * g1c;
+            v8 = w * g2c;
+            {
                 const float u = reduce9(v, v8, lane);
                 const bool head = (lane & 7) == 0;
                 if (head || lane == 1) {

@@ -42,9 +42,15 @@ class GsAdamGroup(C.Structure):
                 ("normalize_rows", C.c_int32), ("lr", C.c_float)]
 
 
+class GsAdamState(C.Structure):
+    _fields_ = [("exp_avg", C.c_void_p * 5), ("exp_avg_sq", C.c_void_p * 5), ("lr", C.c_float * 6),
+                ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("step", C.c_int32)]
+
+
 SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_bin_workspace_size",
-           "gs_bin_sort", "gs_bin_keys", "gs_render_fwd", "gs_render_bwd", "gs_preprocess_bwd", "gs_image_loss",
-           "gs_densify_accum", "gs_adam_step", "gs_count_pairs"]
+           "gs_bin_sort", "gs_bin_keys", "gs_render_fwd", "gs_render_bwd", "gs_preprocess_bwd",
+           "gs_preprocess_bwd_adam", "gs_image_loss", "gs_densify_accum", "gs_adam_step", "gs_count_pairs"]
+PARAM_ORDER = ("means", "log_scales", "quats", "opacity_logits", "sh")
 
 _lib = None
 _vp = C.c_void_p
@@ -72,6 +78,8 @@ def load_library(path=LIB_PATH):
     lib.gs_render_fwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 7 + [_vp]
     lib.gs_preprocess_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
+    lib.gs_preprocess_bwd_adam.argtypes = ([P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 8 +
+                                           [P(GsAdamState)] + [_vp] * 7 + [_vp])
     lib.gs_image_loss.argtypes = [_i32, _i64, _vp, _vp, _vp, _vp, _vp]
     lib.gs_densify_accum.argtypes = [_i32, _vp, _vp, _vp, _vp, _vp]
     lib.gs_adam_step.argtypes = [_i32, P(GsAdamGroup), C.c_float, C.c_float, C.c_float, _i32, _vp]
@@ -213,6 +221,31 @@ def gs_preprocess_bwd(cam, settings, sh_degree, means, log_scales, quats, opacit
 
 
 LOSS_PARTIALS = 1024
+
+
+def gs_preprocess_bwd_adam(cam, settings, sh_degree, params, tiles_touched, clamp_mask, grad2d, exp_avg,
+                           exp_avg_sq, lr, step, beta1=0.9, beta2=0.999, eps=1e-8, densify_accum=None,
+                           densify_count=None, grads=None):
+    """Fused 2D->3D backward + densification statistic + Adam step, updating `params` in place.
+
+    params, exp_avg, exp_avg_sq, grads: dicts keyed by PARAM_ORDER; lr: dict with keys means,
+    log_scales, quats, opacity_logits, sh_dc, sh_rest; grads=None skips the gradient writes."""
+    f32, n = torch.float32, params["means"].shape[0]
+    st = GsAdamState()
+    for i, k in enumerate(PARAM_ORDER):
+        st.exp_avg[i] = _p(exp_avg[k], f32, "exp_avg." + k).value
+        st.exp_avg_sq[i] = _p(exp_avg_sq[k], f32, "exp_avg_sq." + k).value
+    for i, k in enumerate(("means", "log_scales", "quats", "opacity_logits", "sh_dc", "sh_rest")):
+        st.lr[i] = float(lr[k])
+    st.beta1, st.beta2, st.eps, st.step = beta1, beta2, eps, int(step)
+    g = grads or {}
+    rc = load_library().gs_preprocess_bwd_adam(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, sh_degree,
+        *[_p(params[k], f32, k) for k in PARAM_ORDER], _p(tiles_touched, torch.int32, "tiles_touched"),
+        _p(clamp_mask, torch.uint8, "clamp_mask"), _p(grad2d, f32, "grad2d"), C.byref(st),
+        _p(densify_accum, f32, "densify_accum"), _p(densify_count, torch.int32, "densify_count"),
+        *[_p(g.get(k), f32, "grad." + k) for k in PARAM_ORDER], _stream())
+    _check(rc, "gs_preprocess_bwd_adam")
 
 
 def gs_image_loss(mode, pred, target, dL_dpred, loss):

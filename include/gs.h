@@ -236,6 +236,38 @@ typedef struct gs_adam_group {
 int gs_adam_step(int32_t n_groups, const gs_adam_group* groups, float beta1, float beta2,
                  float eps, int32_t step, void* stream);
 
+/* Adam state and hyper-parameters of the fused training-step tail.  Moment
+   buffers have the shapes of the parameters they follow, in the order means,
+   log_scales, quats, opacity_logits, sh.  lr: means, log_scales, quats,
+   opacity_logits, SH band 0 (the DC coefficients), SH bands >= 1. */
+typedef struct gs_adam_state {
+    float* exp_avg[5];
+    float* exp_avg_sq[5];
+    float lr[6];
+    float beta1, beta2, eps;
+    int32_t step;
+} gs_adam_state;
+
+/*
+ * gs_preprocess_bwd_adam -- the training-step tail fused into one pass over
+ * the Gaussians ([P4] E.1 steps 2-3: backpropagate, accumulate the position
+ * gradient statistic, Adam update; C.2 per-parameter learning rates; D.4
+ * renormalise the quaternion after the update).  Computes exactly the
+ * gradients of gs_preprocess_bwd and, in the same kernel, applies one Adam
+ * step (as gs_adam_step) to the parameters IN PLACE, and adds the
+ * densification statistic (as gs_densify_accum) when densify_accum and
+ * densify_count are both non-NULL.  The gradient outputs are optional: pass
+ * all of dmeans, dlog_scales, dquats, dopacity_logits (and optionally dsh) to
+ * also receive the gradients, or NULL to skip those writes.  Gaussians with
+ * tiles_touched == 0 receive a zero gradient and still take the Adam step.
+ */
+int gs_preprocess_bwd_adam(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                           float* means, float* log_scales, float* quats, float* opacity_logits, float* sh,
+                           const int32_t* tiles_touched, const uint8_t* clamp_mask, const float* grad2d,
+                           const gs_adam_state* adam, float* densify_accum, int32_t* densify_count,
+                           float* dmeans, float* dlog_scales, float* dquats, float* dopacity_logits,
+                           float* dsh, void* stream);
+
 /*
  * gs_count_pairs -- diagnostic pair counts of a forward pass (device int64
  * counters, overwritten): counts[0] = evaluated pairs (entries walked by the

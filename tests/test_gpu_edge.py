@@ -231,3 +231,55 @@ def test_training_tail_matches_oracle():
             err = np.abs(params[k].cpu().numpy() - ref[k]).max()
             assert err <= 2e-6, (k, step, err)
     log("training tail ok")
+
+
+def test_fused_tail_matches_separate_calls():
+    """gs_preprocess_bwd_adam == gs_preprocess_bwd + gs_densify_accum + gs_adam_step from the
+    same state and the same 2D gradients, for steps 1 and 2, on a scene with SH degree 3 and a
+    ragged last block."""
+    import torch
+    gs = _gs()
+    sc = scenes.random_small(60, n=1000, width=80, height=64, sh_degree=3, scale_mu=-2.4)
+    N = sc.n
+    lr = scenes.ADAM_LR
+    pa = to_dev(sc.params())
+    ma = {k: torch.zeros_like(v) for k, v in pa.items()}
+    va = {k: torch.zeros_like(v) for k, v in pa.items()}
+    acc_a = torch.zeros(N, device="cuda")
+    cnt_a = torch.zeros(N, dtype=torch.int32, device="cuda")
+    dL = torch.from_numpy(sc.dL_dimage).cuda()
+    for step in (1, 2):
+        r = gs.Rasterizer(sc.cam, N, 3)
+        r.forward(pa)
+        r.backward_2d(dL)
+        pb = {k: v.clone() for k, v in pa.items()}
+        mb = {k: v.clone() for k, v in ma.items()}
+        vb = {k: v.clone() for k, v in va.items()}
+        acc_b, cnt_b = acc_a.clone(), cnt_a.clone()
+        # separate calls on state a
+        ga = {k: torch.empty_like(v) for k, v in pa.items()}
+        gs.gs_preprocess_bwd(r.cam, r.settings, 3, pa["means"], pa["log_scales"], pa["quats"], pa["opacity_logits"],
+                             pa["sh"], r.tiles_touched, r.clamp, r.grad2d, ga["means"], ga["log_scales"], ga["quats"],
+                             ga["opacity_logits"], ga["sh"])
+        gs.gs_densify_accum(N, r.tiles_touched, r.grad2d, acc_a, cnt_a)
+        groups = []
+        for k, rl, cb, ce, key in (("means", 3, 0, 3, "means"), ("log_scales", 3, 0, 3, "log_scales"),
+                                   ("quats", 4, 0, 4, "quats"), ("opacity_logits", 1, 0, 1, "opacity_logits"),
+                                   ("sh", 48, 0, 3, "sh_dc"), ("sh", 48, 3, 48, "sh_rest")):
+            groups.append(dict(param=pa[k], grad=ga[k], exp_avg=ma[k], exp_avg_sq=va[k], rows=N, row_len=rl,
+                               col_begin=cb, col_end=ce, normalize_rows=1 if k == "quats" else 0, lr=lr[key]))
+        gs.gs_adam_step(groups, 0.9, 0.999, 1e-8, step)
+        # fused call on state b, same 2D gradients
+        gb = {k: torch.empty_like(v) for k, v in pb.items()}
+        gs.gs_preprocess_bwd_adam(r.cam, r.settings, 3, pb, r.tiles_touched, r.clamp, r.grad2d, mb, vb, lr, step,
+                                  densify_accum=acc_b, densify_count=cnt_b, grads=gb)
+        torch.cuda.synchronize()
+        for k in pa:
+            scale = max(1.0, ga[k].abs().max().item())
+            assert (ga[k] - gb[k]).abs().max().item() <= 1e-6 * scale, ("grad", k, step)
+            for x, y, name in ((pa[k], pb[k], "param"), (ma[k], mb[k], "m"), (va[k], vb[k], "v")):
+                err = (x - y).abs().max().item()
+                assert err <= 1e-6 * max(1.0, x.abs().max().item()), (name, k, step, err)
+        assert torch.equal(cnt_a, cnt_b)
+        assert (acc_a - acc_b).abs().max().item() <= 1e-6 * max(1.0, acc_a.abs().max().item())
+    log("fused tail ok")

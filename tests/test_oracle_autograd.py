@@ -17,7 +17,7 @@ import torch
 
 from differentiable_gaussian_splatting_dgs_amd import scenes
 
-torch.set_default_dtype(torch.float64)
+F64 = torch.float64
 
 
 def _assoc_legendre(l, m, z, s):
@@ -66,8 +66,8 @@ def _quat_rot(q):
 
 
 def _project(cam, deg, P, dil=0.3):
-    Rv = torch.tensor(np.asarray(cam.R, np.float64))
-    tv = torch.tensor(np.asarray(cam.t, np.float64))
+    Rv = torch.tensor(np.asarray(cam.R, np.float64), dtype=F64)
+    tv = torch.tensor(np.asarray(cam.t, np.float64), dtype=F64)
     t = P["means"] @ Rv.T + tv
     R = _quat_rot(P["quats"])
     S = torch.diag_embed(torch.exp(P["log_scales"]))
@@ -78,7 +78,7 @@ def _project(cam, deg, P, dil=0.3):
     J = torch.stack([torch.stack([cam.fx / tz, zero, -cam.fx * tx / tz ** 2], 1),
                      torch.stack([zero, cam.fy / tz, -cam.fy * ty / tz ** 2], 1)], 1)
     Tm = J @ Rv
-    cov = Tm @ Sig @ Tm.transpose(1, 2) + dil * torch.eye(2)
+    cov = Tm @ Sig @ Tm.transpose(1, 2) + dil * torch.eye(2, dtype=F64)
     conic = torch.linalg.inv(cov)
     uv = torch.stack([cam.fx * tx / tz + cam.cx, cam.fy * ty / tz + cam.cy], 1)
     sigma = torch.sigmoid(P["opacity_logits"])
@@ -98,8 +98,7 @@ def _render_frozen(cam, deg, P, visible, amin=1 / 255, amax=0.99, tmin=1e-4):
     idx = np.nonzero(visible)[0]
     order = torch.tensor(idx[np.lexsort((idx, depth32[idx]))])
     H, W = cam.height, cam.width
-    ys, xs = torch.meshgrid(torch.arange(H, dtype=torch.float64) + 0.5,
-                            torch.arange(W, dtype=torch.float64) + 0.5, indexing="ij")
+    ys, xs = torch.meshgrid(torch.arange(H, dtype=F64) + 0.5, torch.arange(W, dtype=F64) + 0.5, indexing="ij")
     px = torch.stack([xs.reshape(-1), ys.reshape(-1)], 1)          # [P, 2]
     d = px[:, None, :] - uv[order][None, :, :]                     # [P, G, 2]
     Q = conic[order]
@@ -108,7 +107,7 @@ def _render_frozen(cam, deg, P, visible, amin=1 / 255, amax=0.99, tmin=1e-4):
     with torch.no_grad():
         a = torch.clamp(sG, max=amax)
         blend = torch.zeros_like(a, dtype=torch.bool)
-        T = torch.ones(a.shape[0])
+        T = torch.ones(a.shape[0], dtype=F64)
         alive = torch.ones(a.shape[0], dtype=torch.bool)
         for k in range(a.shape[1]):
             ok = alive & (a[:, k] >= amin)
@@ -120,7 +119,7 @@ def _render_frozen(cam, deg, P, visible, amin=1 / 255, amax=0.99, tmin=1e-4):
             T = torch.where(ok, Tn, T)
         clamped = sG > amax
     alpha = torch.where(clamped, torch.full_like(sG, amax), sG) * blend
-    Tex = torch.cumprod(torch.cat([torch.ones(alpha.shape[0], 1), 1 - alpha[:, :-1]], 1), 1)
+    Tex = torch.cumprod(torch.cat([torch.ones(alpha.shape[0], 1, dtype=F64), 1 - alpha[:, :-1]], 1), 1)
     img = torch.einsum("pg,pg,gc->pc", alpha, Tex, rgb[order])
     return img.T.reshape(3, H, W)
 
@@ -140,10 +139,10 @@ def test_backward_matches_autograd(oracle, which):
     params = {k: np.asarray(v, np.float64) for k, v in sc.params().items()}
     r = oracle.render(sc.cam, sc.sh_degree, params, dL_dimage=sc.dL_dimage)
     assert r["pre"]["valid"].sum() > 0.5 * sc.n
-    P = {k: torch.tensor(v, requires_grad=True) for k, v in params.items()}
+    P = {k: torch.tensor(v, dtype=F64, requires_grad=True) for k, v in params.items()}
     img = _render_frozen(sc.cam, sc.sh_degree, P, r["pre"]["valid"])
     assert np.abs(img.detach().numpy() - r["image"]).max() < 1e-12
-    loss = (img * torch.tensor(np.asarray(sc.dL_dimage, np.float64))).sum()
+    loss = (img * torch.tensor(np.asarray(sc.dL_dimage, np.float64), dtype=F64)).sum()
     loss.backward()
     for k in P:
         a = r["g3d"][k]
