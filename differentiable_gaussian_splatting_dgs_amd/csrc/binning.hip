@@ -23,14 +23,22 @@
 // ballot matching, then decoupled look-back across partitions for the digit
 // offsets) follows Adinets and Merrill, "Onesweep" (2022), with partitions
 // claimed from an atomic ticket so look-back only waits on running blocks.
+#include <algorithm>
+
 #include "gs_internal.h"
 
 namespace gs {
 namespace {
 
 constexpr int kSortThreads = 256;
-constexpr int kSortIPT = 16;
-constexpr int kSortPart = kSortThreads * kSortIPT;  // 4096 items per partition
+constexpr int kDepthIPT = 16;                       // depth sort over N: 4096 items per partition
+constexpr int kTileIPT = 16;                        // tile sort over K: 4096 items per partition
+constexpr int kDepthPart = kSortThreads * kDepthIPT;
+constexpr int kTilePart = kSortThreads * kTileIPT;
+constexpr int kKeyBlocks = 512;                     // grid of the depth-key/histogram pass
+constexpr int kStripes = 32;                        // histogram copies that blocks add into
+constexpr int kHistBins = 6 * 256;                  // 4 depth digits + 2 tile digits
+constexpr int kLookWindow = 8;                      // predecessors read at once per digit
 constexpr int kRadix = 256;
 constexpr uint32_t kFlagAgg = 1u << 30;
 constexpr uint32_t kFlagInc = 2u << 30;
@@ -76,9 +84,10 @@ struct Layout {
     size_t tickets;     // uint32 [8]
     size_t err;         // uint32 [1] look-back spin-limit flag
     size_t dstatus;     // uint32 [4][dparts][256]
-    size_t estatus;     // uint32 [eparts]
+    size_t etotal;      // uint32 [eparts] entries per emit partition, then their exclusive offsets
     size_t tstatus;     // uint32 [2][tparts][256]
     size_t zero_end;    // everything above is zeroed per call
+    size_t stripes;     // uint32 [kStripes][kHistBins] striped digit counts (zeroed)
     size_t dkeys0, dvals0, dkeys1, dvals1;  // uint32 [n] each
     size_t tkeys0, tkeys1, tvals0;          // uint32 [cap] each
     size_t total;
@@ -89,16 +98,17 @@ inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline Layout make_layout(int32_t n, int64_t cap) {
     Layout L;
-    L.dparts = (uint32_t)((n + kSortPart - 1) / kSortPart);
+    L.dparts = (uint32_t)((n + kDepthPart - 1) / kDepthPart);
     L.eparts = (uint32_t)((n + kEmitPart - 1) / kEmitPart);
-    L.tparts = (uint32_t)((cap + kSortPart - 1) / kSortPart);
+    L.tparts = (uint32_t)((cap + kTilePart - 1) / kTilePart);
     size_t o = 0;
     L.hist = o; o = up256(o + 6 * kRadix * 4);
     L.tickets = o; o = up256(o + 8 * 4);
     L.err = o; o = up256(o + 4);
     L.dstatus = o; o = up256(o + (size_t)4 * L.dparts * kRadix * 4);
-    L.estatus = o; o = up256(o + (size_t)L.eparts * 4);
+    L.etotal = o; o = up256(o + (size_t)L.eparts * 4);
     L.tstatus = o; o = up256(o + (size_t)2 * L.tparts * kRadix * 4);
+    L.stripes = o; o = up256(o + (size_t)kStripes * kHistBins * 4);
     L.zero_end = o;
     L.dkeys0 = o; o = up256(o + (size_t)n * 4);
     L.dvals0 = o; o = up256(o + (size_t)n * 4);
@@ -111,30 +121,54 @@ inline Layout make_layout(int32_t n, int64_t cap) {
     return L;
 }
 
-__global__ void k_zero_u32(uint32_t* p, size_t count) {
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Clears up to four buffers in one launch.
+struct ClearArgs {
+    uint32_t* p[4];
+    size_t count[4];
+};
+
+__global__ void k_clear(ClearArgs c) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (; i < count; i += stride) p[i] = 0u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < c.count[b]; i += stride) c.p[b][i] = 0u;
 }
 
-// 1. depth keys + histograms of the 4 depth digits
+// 1. depth keys + counts of the 4 depth digits.  Blocks add their counts into
+// one of kStripes histogram copies (so no address sees more than a few dozen
+// atomics); k_hist_reduce sums the copies.
 __global__ __launch_bounds__(256) void k_depth_keys(int32_t n, const float* depth, const int32_t* tt,
-                                                    uint32_t* keys, uint32_t* vals, uint32_t* hist) {
+                                                    uint32_t* keys, uint32_t* vals, uint32_t* stripes) {
     __shared__ uint32_t sh[4 * kRadix];
     for (int i = threadIdx.x; i < 4 * kRadix; i += blockDim.x) sh[i] = 0;
     __syncthreads();
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) {
-        const uint32_t k = tt[i] > 0 ? __float_as_uint(depth[i]) : 0xffffffffu;
-        keys[i] = k;
-        vals[i] = (uint32_t)i;
-    }
-    const uint32_t k = i < n ? (tt[i] > 0 ? __float_as_uint(depth[i]) : 0xffffffffu) : 0u;
+    const int stride = gridDim.x * blockDim.x;
+    for (int base = blockIdx.x * blockDim.x; base < n; base += stride) {
+        const int i = base + threadIdx.x;
+        const bool valid = i < n;
+        uint32_t k = 0u;
+        if (valid) {
+            k = tt[i] > 0 ? __float_as_uint(depth[i]) : 0xffffffffu;
+            keys[i] = k;
+            vals[i] = (uint32_t)i;
+        }
 #pragma unroll
-    for (int d = 0; d < 4; ++d) wave_hist_add(sh + d * kRadix, (k >> (8 * d)) & 255u, i < n);
+        for (int d = 0; d < 4; ++d) wave_hist_add(sh + d * kRadix, (k >> (8 * d)) & 255u, valid);
+    }
     __syncthreads();
+    uint32_t* out = stripes + (size_t)(blockIdx.x % kStripes) * kHistBins;
     for (int b = threadIdx.x; b < 4 * kRadix; b += blockDim.x)
-        if (sh[b]) atomicAdd(&hist[b], sh[b]);
+        if (sh[b]) atomicAdd(&out[b], sh[b]);
+}
+
+// hist[b] = sum of the kStripes copies, for bins [b0, b0 + nbins).
+__global__ void k_hist_reduce(const uint32_t* stripes, int b0, int nbins, uint32_t* hist) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nbins) return;
+    uint32_t acc = 0;
+#pragma unroll
+    for (int p = 0; p < kStripes; ++p) acc += stripes[(size_t)p * kHistBins + b0 + b];
+    hist[b0 + b] = acc;
 }
 
 struct PassArgs {
@@ -152,8 +186,11 @@ struct PassArgs {
     int shift;
 };
 
-// 2/4. one onesweep pass over 8 bits of a 32-bit key.
+// 2/4. one onesweep pass over 8 bits of a 32-bit key, IPT items per thread.
+template <int IPT>
 __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
+    constexpr int kSortIPT = IPT;
+    constexpr int kSortPart = kSortThreads * IPT;
     __shared__ uint32_t s_off[kRadix];          // global exclusive digit offsets
     __shared__ uint32_t s_wave[4][kRadix];      // per-wave digit counts -> prefixes
     __shared__ uint32_t s_base[kRadix];         // global offset of this partition's first item of digit d
@@ -236,18 +273,31 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
             st_release(st, kFlagInc | total);
         } else {
             st_release(st, kFlagAgg | total);
+            // look back with kLookWindow loads in flight; partitions below 0 read
+            // as an inclusive prefix of 0
             int j = (int)part - 1;
             uint32_t spins = 0;
-            while (j >= 0) {
-                const uint32_t sv = ld_acquire(p.status + (size_t)j * kRadix + d);
-                if ((sv & ~kValMask) == 0u) {
+            while (true) {
+                uint32_t sv[kLookWindow];
+#pragma unroll
+                for (int w = 0; w < kLookWindow; ++w)
+                    sv[w] = j - w >= 0 ? ld_acquire(p.status + (size_t)(j - w) * kRadix + d) : kFlagInc;
+                int used = 0;
+                bool found = false, stall = false;
+#pragma unroll
+                for (int w = 0; w < kLookWindow; ++w) {
+                    if (found || stall) continue;
+                    if ((sv[w] & ~kValMask) == 0u) { stall = true; continue; }
+                    prefix += sv[w] & kValMask;
+                    ++used;
+                    if (sv[w] & kFlagInc) found = true;
+                }
+                if (found) break;
+                j -= used;
+                if (stall) {
                     if (++spins > kSpinLimit) { atomicOr(p.err, 1u); break; }
                     __builtin_amdgcn_s_sleep(1);
-                    continue;
                 }
-                prefix += sv & kValMask;
-                if (sv & kFlagInc) break;
-                --j;
             }
             st_release(st, kFlagInc | ((prefix + total) & kValMask));
         }
@@ -284,38 +334,149 @@ struct EmitArgs {
     int32_t n;
     int32_t tiles_x;
     uint32_t cap;
+    uint32_t eparts;
     const uint32_t* order;   // Gaussians in depth order
     const int16_t* rect;
     const int32_t* tt;
     uint32_t* tkeys;         // [cap] tile id
     uint32_t* tvals;         // [cap] Gaussian
-    uint32_t* status;        // [eparts], zeroed
-    uint32_t* ticket;        // zeroed
-    uint32_t* hist;          // [2][256] tile digits
+    uint32_t* part;          // [eparts] entries per partition -> exclusive offsets
+    uint32_t* stripes;       // [kStripes][kHistBins] striped digit counts
+    uint32_t* hist;          // [kHistBins]
     uint32_t* num_keys;
     uint32_t* overflow;
-    uint32_t* err;
 };
 
-// 3. scan of tiles_touched in depth order + emit of (tile, Gaussian) pairs.
-// Each block scans its 1024 depth-sorted Gaussians, gets its output offset by
-// decoupled look-back, then expands entry-parallel: thread t writes entries
-// t, t+256, ... of the block's output range, finding each entry's Gaussian
-// by binary search over the block's offsets in LDS (balanced and coalesced).
-__global__ __launch_bounds__(kEmitThreads) void k_emit(EmitArgs a) {
-    __shared__ uint32_t s_hist[2 * kRadix];
+__device__ inline void unpack_rect(uint2 r, int& x0, int& y0, int& x1, int& y1) {
+    x0 = (int)(int16_t)(r.x & 0xffffu); y0 = (int)(int16_t)(r.x >> 16);
+    x1 = (int)(int16_t)(r.y & 0xffffu); y1 = (int)(int16_t)(r.y >> 16);
+}
+
+// Adds the digit counts of the tiles of rect to the block histograms: per row
+// the tile ids form one run [t0, t0 + w); its low bytes are a cyclic run of
+// bins (recorded as a difference array, +1 at the start and -1 past the end,
+// whole wraps as a uniform add) and its high bytes cover at most a few bins.
+__device__ inline void rect_hist(int x0, int y0, int x1, int y1, int tiles_x, uint32_t* s_lo_diff,
+                                 uint32_t* s_lo_all, uint32_t* s_hi) {
+    const uint32_t w = (uint32_t)(x1 - x0);
+    for (int y = y0; y < y1; ++y) {
+        const uint32_t t0 = (uint32_t)(y * tiles_x + x0), t1 = t0 + w;  // [t0, t1)
+        // low byte: w / 256 full cycles plus a cyclic run of w % 256 bins from t0 & 255
+        const uint32_t full = w >> 8, rem = w & 255u;
+        if (full) atomicAdd(s_lo_all, full);
+        if (rem) {
+            const uint32_t b0 = t0 & 255u, b1 = (t0 + rem) & 255u;
+            atomicAdd(&s_lo_diff[b0], 1u);
+            atomicAdd(&s_lo_diff[b1], 0xffffffffu);  // -1
+            if (b1 <= b0 && b1 != 0u) atomicAdd(s_lo_all, 1u);  // the run wraps past bin 255
+            if (b1 <= b0 && b1 == 0u) { /* ends exactly at 256: the -1 at bin 0 cancels the wrap */
+                atomicAdd(s_lo_all, 1u);
+            }
+        }
+        // high byte: bins (t0 >> 8) .. ((t1 - 1) >> 8)
+        for (uint32_t hb = t0 >> 8; hb <= ((t1 - 1u) >> 8); ++hb) {
+            const uint32_t lo = max(t0, hb << 8), hi = min(t1, (hb + 1u) << 8);
+            atomicAdd(&s_hi[hb & 255u], hi - lo);
+        }
+    }
+}
+
+// 3a. entries per partition of 1024 depth-sorted Gaussians, and the tile-digit counts.
+__global__ __launch_bounds__(kEmitThreads) void k_emit_count(EmitArgs a) {
+    __shared__ uint32_t s_lo_diff[kRadix];
+    __shared__ uint32_t s_hi[kRadix];
+    __shared__ uint32_t s_lo_all;
+    __shared__ uint32_t s_wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    s_lo_diff[tid] = 0;
+    s_hi[tid] = 0;
+    if (tid == 0) s_lo_all = 0;
+    __syncthreads();
+    uint32_t tsum = 0;
+#pragma unroll
+    for (int k = 0; k < kEmitIPT; ++k) {
+        const int64_t j = (int64_t)blockIdx.x * kEmitPart + k * kEmitThreads + tid;
+        const uint32_t g = j < a.n ? a.order[j] : 0xffffffffu;
+        const uint32_t c = g < (uint32_t)a.n ? (uint32_t)max(a.tt[g], 0) : 0u;
+        if (c) {
+            int x0, y0, x1, y1;
+            unpack_rect(reinterpret_cast<const uint2*>(a.rect)[g], x0, y0, x1, y1);
+            rect_hist(x0, y0, x1, y1, a.tiles_x, s_lo_diff, &s_lo_all, s_hi);
+        }
+        tsum += c;
+    }
+    for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
+    if (lane == 0) s_wsum[wave] = tsum;
+    __syncthreads();
+    if (tid == 0) a.part[blockIdx.x] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    // low-byte counts = inclusive prefix sum of the difference array + whole cycles
+    uint32_t x = s_lo_diff[tid];
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) s_wsum[wave] = x;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) x += s_wsum[w];
+    const uint32_t lo = x + s_lo_all;
+    uint32_t* out = a.stripes + (size_t)(blockIdx.x % kStripes) * kHistBins + 4 * kRadix;
+    if (lo) atomicAdd(&out[tid], lo);
+    if (s_hi[tid]) atomicAdd(&out[kRadix + tid], s_hi[tid]);
+}
+
+// 3b. one block: exclusive scan of the partition totals, K, the overflow flag,
+// and the tile-digit histogram summed over the stripes.
+__global__ __launch_bounds__(1024) void k_emit_scan(EmitArgs a) {
+    __shared__ uint32_t s_wsum[16];
+    __shared__ uint32_t s_carry;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    for (uint32_t base = 0; base < a.eparts; base += 1024) {
+        const uint32_t i = base + tid;
+        const uint32_t v = i < a.eparts ? a.part[i] : 0u;
+        uint32_t x = v;
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) s_wsum[wave] = x;
+        __syncthreads();
+        uint32_t add = s_carry, tot = 0;
+        for (int w = 0; w < 16; ++w) {
+            if (w < wave) add += s_wsum[w];
+            tot += s_wsum[w];
+        }
+        if (i < a.eparts) a.part[i] = x - v + add;
+        __syncthreads();
+        if (tid == 0) s_carry += tot;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const uint32_t K = s_carry;
+        *a.num_keys = K;
+        *a.overflow = K > a.cap ? 1u : 0u;
+    }
+    if (tid < 2 * kRadix) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int p = 0; p < kStripes; ++p) acc += a.stripes[(size_t)p * kHistBins + 4 * kRadix + tid];
+        a.hist[4 * kRadix + tid] = acc;
+    }
+}
+
+// 3c. expansion: each block rescans its 1024 Gaussians, then writes (tile,
+// Gaussian) entries entry-parallel: thread t writes entries t, t+256, ... of the
+// block's range, finding each entry's Gaussian by binary search over the block's
+// offsets in LDS (balanced and coalesced).
+__global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
     __shared__ uint32_t s_off[kEmitPart];   // block-local exclusive offsets
     __shared__ uint32_t s_g[kEmitPart];     // Gaussian ids
     __shared__ uint2 s_rect[kEmitPart];
     __shared__ uint32_t s_wsum[4];
-    __shared__ uint32_t s_prefix;
-    __shared__ uint32_t s_part;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) s_part = atomicAdd(a.ticket, 1u);
-    for (int i = tid; i < 2 * kRadix; i += kEmitThreads) s_hist[i] = 0;
-    __syncthreads();
-    const uint32_t part = s_part;
-    const int64_t j0 = (int64_t)part * kEmitPart + tid * kEmitIPT;
+    const int64_t j0 = (int64_t)blockIdx.x * kEmitPart + tid * kEmitIPT;
     uint32_t g[kEmitIPT], cnt[kEmitIPT], tsum = 0;
 #pragma unroll
     for (int k = 0; k < kEmitIPT; ++k) {
@@ -324,7 +485,6 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(EmitArgs a) {
         cnt[k] = (g[k] < (uint32_t)a.n) ? (uint32_t)max(a.tt[g[k]], 0) : 0u;
         tsum += cnt[k];
     }
-    // block exclusive scan of the per-thread sums
     uint32_t x = tsum;
     for (int o = 1; o < 64; o <<= 1) {
         const uint32_t y = __shfl_up(x, o, 64);
@@ -346,79 +506,40 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit(EmitArgs a) {
         s_rect[q] = cnt[k] ? reinterpret_cast<const uint2*>(a.rect)[g[k]] : make_uint2(0u, 0u);
         off += cnt[k];
     }
-    // decoupled look-back for the partition prefix
-    if (tid == 0) {
-        uint32_t prefix = 0;
-        uint32_t* st = a.status + part;
-        if (part == 0) {
-            st_release(st, kFlagInc | btotal);
-        } else {
-            st_release(st, kFlagAgg | btotal);
-            int j = (int)part - 1;
-            uint32_t spins = 0;
-            while (j >= 0) {
-                const uint32_t sv = ld_acquire(a.status + j);
-                if ((sv & ~kValMask) == 0u) {
-                    if (++spins > kSpinLimit) { atomicOr(a.err, 1u); break; }
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
-                }
-                prefix += sv & kValMask;
-                if (sv & kFlagInc) break;
-                --j;
-            }
-            st_release(st, kFlagInc | ((prefix + btotal) & kValMask));
-        }
-        s_prefix = prefix;
-        const uint32_t nparts = (uint32_t)((a.n + kEmitPart - 1) / kEmitPart);
-        if (part == nparts - 1) {
-            const uint32_t K = prefix + btotal;
-            *a.num_keys = K;
-            *a.overflow = K > a.cap ? 1u : 0u;
-        }
-    }
     __syncthreads();
-    const uint32_t prefix = s_prefix;
+    const uint32_t prefix = a.part[blockIdx.x];
     for (uint32_t o = tid; o < btotal; o += kEmitThreads) {
-        // last q with s_off[q] <= o (entries of empty Gaussians share offsets; the
-        // last one wins, which is the non-empty Gaussian owning entry o)
+        // last q with s_off[q] <= o: the Gaussian owning entry o (it has cnt > 0)
         int lo = 0, hi = kEmitPart - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (s_off[mid] <= o) lo = mid; else hi = mid - 1;
         }
-        const uint2 r = s_rect[lo];
-        const int x0 = (int)(int16_t)(r.x & 0xffffu), y0 = (int)(int16_t)(r.x >> 16);
-        const int x1 = (int)(int16_t)(r.y & 0xffffu);
+        int x0, y0, x1, y1;
+        unpack_rect(s_rect[lo], x0, y0, x1, y1);
         const int w = x1 - x0;
         const int local = (int)(o - s_off[lo]);
         const int ty = y0 + local / w, tx = x0 + local % w;
-        const uint32_t tile = (uint32_t)(ty * a.tiles_x + tx);
         const uint32_t out = prefix + o;
-        const bool ok = out < a.cap;
-        if (ok) {
-            a.tkeys[out] = tile;
+        if (out < a.cap) {
+            a.tkeys[out] = (uint32_t)(ty * a.tiles_x + tx);
             a.tvals[out] = s_g[lo];
         }
-        wave_hist_add(s_hist, tile & 255u, ok);
-        wave_hist_add(s_hist + kRadix, (tile >> 8) & 255u, ok);
     }
-    __syncthreads();
-    for (int b = tid; b < 2 * kRadix; b += kEmitThreads)
-        if (s_hist[b]) atomicAdd(&a.hist[b], s_hist[b]);
 }
 
 // 5. tile ranges from sorted tile ids (ranges zeroed beforehand).
 __global__ void k_ranges(const uint32_t* tkeys, const uint32_t* num_keys, uint32_t cap,
                          const uint32_t* overflow, uint32_t* ranges, uint32_t ntiles) {
-    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
     if (*overflow) return;
     const uint32_t K = min(*num_keys, cap);
-    if (k >= K) return;
-    const uint32_t t = tkeys[k];
-    if (t >= ntiles) return;
-    if (k == 0 || tkeys[k - 1] != t) ranges[2 * t] = k;
-    if (k == K - 1 || tkeys[k + 1] != t) ranges[2 * t + 1] = k + 1;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    for (uint32_t k = blockIdx.x * blockDim.x + threadIdx.x; k < K; k += stride) {
+        const uint32_t t = tkeys[k];
+        if (t >= ntiles) continue;
+        if (k == 0 || tkeys[k - 1] != t) ranges[2 * t] = k;
+        if (k == K - 1 || tkeys[k + 1] != t) ranges[2 * t + 1] = k + 1;
+    }
 }
 
 __global__ void k_keys(const uint32_t* ranges, const uint32_t* list, const float* depth, uint64_t* keys,
@@ -462,18 +583,23 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
     auto U = [&](size_t off) { return reinterpret_cast<uint32_t*>(ws + off); };
 
     // zero counters, histograms, look-back status, ranges, K and the overflow flag
-    hipLaunchKernelGGL(k_zero_u32, dim3(1024), dim3(256), 0, s, U(0), L.zero_end / 4);
-    hipLaunchKernelGGL(k_zero_u32, dim3((2 * ntiles + 255) / 256), dim3(256), 0, s, tile_ranges,
-                       (size_t)2 * ntiles);
-    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, num_keys_dev, (size_t)1);
-    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, overflow_dev, (size_t)1);
+    {
+        ClearArgs c;
+        c.p[0] = U(0); c.count[0] = L.zero_end / 4;
+        c.p[1] = tile_ranges; c.count[1] = (size_t)2 * ntiles;
+        c.p[2] = num_keys_dev; c.count[2] = 1;
+        c.p[3] = overflow_dev; c.count[3] = 1;
+        hipLaunchKernelGGL(k_clear, dim3(512), dim3(256), 0, s, c);
+    }
     if (n == 0) return launch_status();
 
     uint32_t* hist = U(L.hist);
     uint32_t* tickets = U(L.tickets);
     uint32_t* err = U(L.err);
-    hipLaunchKernelGGL(k_depth_keys, dim3((n + 255) / 256), dim3(256), 0, s, n, depth, tiles_touched,
-                       U(L.dkeys0), U(L.dvals0), hist);
+    const int key_blocks = (int)std::min<int64_t>(kKeyBlocks, (n + 255) / 256);
+    hipLaunchKernelGGL(k_depth_keys, dim3(key_blocks), dim3(256), 0, s, n, depth, tiles_touched, U(L.dkeys0),
+                       U(L.dvals0), U(L.stripes));
+    hipLaunchKernelGGL(k_hist_reduce, dim3(4), dim3(256), 0, s, U(L.stripes), 0, 4 * kRadix, hist);
     // depth sort: 4 passes, 0 -> 1 -> 0 -> 1 -> 0
     uint32_t* dk[2] = {U(L.dkeys0), U(L.dkeys1)};
     uint32_t* dv[2] = {U(L.dvals0), U(L.dvals1)};
@@ -488,26 +614,28 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
         p.ticket = tickets + pass;
         p.err = err;
         p.shift = 8 * pass;
-        hipLaunchKernelGGL(k_onesweep, dim3(L.dparts), dim3(kSortThreads), 0, s, p);
+        hipLaunchKernelGGL(k_onesweep<kDepthIPT>, dim3(L.dparts), dim3(kSortThreads), 0, s, p);
     }
     // emit (tile, Gaussian) pairs in depth order, then the stable tile sort.
     // Buffers are routed so the final values land in point_list:
     //   1 pass : emit -> (tkeys0, tvals0) -> (tkeys1, point_list)
     //   2 passes: emit -> (tkeys0, point_list) -> (tkeys1, tvals0) -> (tkeys0, point_list)
     EmitArgs e;
-    e.n = n; e.tiles_x = tiles_x(cam); e.cap = (uint32_t)key_capacity;
+    e.n = n; e.tiles_x = tiles_x(cam); e.cap = (uint32_t)key_capacity; e.eparts = L.eparts;
     e.order = dv[0]; e.rect = rect; e.tt = tiles_touched;
     e.tkeys = U(L.tkeys0); e.tvals = tile_passes == 1 ? U(L.tvals0) : point_list;
-    e.status = U(L.estatus); e.ticket = tickets + 4; e.hist = hist + 4 * kRadix;
-    e.num_keys = num_keys_dev; e.overflow = overflow_dev; e.err = err;
-    hipLaunchKernelGGL(k_emit, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
+    e.part = U(L.etotal); e.stripes = U(L.stripes); e.hist = hist;
+    e.num_keys = num_keys_dev; e.overflow = overflow_dev;
+    hipLaunchKernelGGL(k_emit_count, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
+    hipLaunchKernelGGL(k_emit_scan, dim3(1), dim3(1024), 0, s, e);
+    hipLaunchKernelGGL(k_emit_expand, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
     if (key_capacity == 0) return launch_status();
     PassArgs p;
     p.count_dev = num_keys_dev; p.count_host = 0; p.cap = (uint32_t)key_capacity; p.err = err;
     p.keys_in = U(L.tkeys0); p.vals_in = e.tvals;
     p.keys_out = U(L.tkeys1); p.vals_out = tile_passes == 1 ? point_list : U(L.tvals0);
     p.hist = hist + 4 * kRadix; p.status = U(L.tstatus); p.ticket = tickets + 5; p.shift = 0;
-    hipLaunchKernelGGL(k_onesweep, dim3(L.tparts), dim3(kSortThreads), 0, s, p);
+    hipLaunchKernelGGL(k_onesweep<kTileIPT>, dim3(L.tparts), dim3(kSortThreads), 0, s, p);
     const uint32_t* tk_final = U(L.tkeys1);
     if (tile_passes == 2) {
         PassArgs p2 = p;
@@ -515,11 +643,12 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
         p2.keys_out = U(L.tkeys0); p2.vals_out = point_list;
         p2.hist = hist + 5 * kRadix; p2.status = U(L.tstatus) + (size_t)L.tparts * kRadix;
         p2.ticket = tickets + 6; p2.shift = 8;
-        hipLaunchKernelGGL(k_onesweep, dim3(L.tparts), dim3(kSortThreads), 0, s, p2);
+        hipLaunchKernelGGL(k_onesweep<kTileIPT>, dim3(L.tparts), dim3(kSortThreads), 0, s, p2);
         tk_final = U(L.tkeys0);
     }
-    hipLaunchKernelGGL(k_ranges, dim3((uint32_t)((key_capacity + 255) / 256)), dim3(256), 0, s, tk_final,
-                       num_keys_dev, (uint32_t)key_capacity, overflow_dev, tile_ranges, (uint32_t)ntiles);
+    const uint32_t rblocks = (uint32_t)std::min<int64_t>(2048, (key_capacity + 255) / 256);
+    hipLaunchKernelGGL(k_ranges, dim3(rblocks), dim3(256), 0, s, tk_final, num_keys_dev, (uint32_t)key_capacity,
+                       overflow_dev, tile_ranges, (uint32_t)ntiles);
     return launch_status();
 }
 

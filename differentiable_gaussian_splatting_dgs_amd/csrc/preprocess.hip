@@ -61,11 +61,31 @@ __device__ inline void sh_eval(double x, double y, double z, double* Y) {
     }
 }
 
+constexpr int kPreBlock = 256;  // Gaussians (= threads) per block
+
+// The block's SH coefficients are contiguous in HBM: they are copied into LDS
+// with coalesced loads, coefficient-major with row stride kPreBlock + 1 so both
+// the copy and the per-thread reads are free of bank conflicts.
 template <int DEG>
-__global__ __launch_bounds__(256) void k_preprocess(PreArgs a) {
+__global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     constexpr int K = (DEG + 1) * (DEG + 1);
+    constexpr int J = 3 * K;
+    constexpr int LDG = kPreBlock + 1;
+    __shared__ float s_sh[J * LDG];
+    {
+        const int g0 = blockIdx.x * kPreBlock;
+        const int cnt = min(kPreBlock, a.n - g0) * J;
+        const float* src = a.sh + (size_t)g0 * J;
+#pragma unroll 4
+        for (int e = threadIdx.x; e < cnt; e += kPreBlock) {
+            const int g = e / J, j = e - g * J;
+            s_sh[j * LDG + g] = src[e];
+        }
+    }
+    __syncthreads();
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= a.n) return;
+    const int col = threadIdx.x;
 
     float4* sp = reinterpret_cast<float4*>(a.splats + (size_t)i * GS_SPLAT_STRIDE);
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -154,17 +174,16 @@ __global__ __launch_bounds__(256) void k_preprocess(PreArgs a) {
     dx *= dinv; dy *= dinv; dz *= dinv;
     double Y[16];
     sh_eval<DEG>(dx, dy, dz, Y);
-    const float* shi = a.sh + (size_t)i * K * 3;
-    double col[3] = {0.5, 0.5, 0.5};
+    double rgb[3] = {0.5, 0.5, 0.5};
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        col[0] += Y[k] * (double)shi[3 * k];
-        col[1] += Y[k] * (double)shi[3 * k + 1];
-        col[2] += Y[k] * (double)shi[3 * k + 2];
+        rgb[0] += Y[k] * (double)s_sh[(3 * k) * LDG + col];
+        rgb[1] += Y[k] * (double)s_sh[(3 * k + 1) * LDG + col];
+        rgb[2] += Y[k] * (double)s_sh[(3 * k + 2) * LDG + col];
     }
     uint8_t cm = 0;
     for (int ch = 0; ch < 3; ++ch)
-        if (col[ch] < 0.0) { cm |= (uint8_t)(1u << ch); col[ch] = 0.0; }
+        if (rgb[ch] < 0.0) { cm |= (uint8_t)(1u << ch); rgb[ch] = 0.0; }
 
     // Cholesky factor of the conic, scaled so that G = exp2(-|L^T d|^2):
     // conic = [[cc, -cb], [-cb, ca]] / det = L L^T with
@@ -177,7 +196,7 @@ __global__ __launch_bounds__(256) void k_preprocess(PreArgs a) {
     const float uf = (float)u, vf = (float)v;
     sp[0] = make_float4(uf, vf, (float)(u - (double)uf), (float)(v - (double)vf));
     sp[1] = make_float4((float)l00, (float)l10, (float)l11, (float)sigma);
-    sp[2] = make_float4((float)col[0], (float)col[1], (float)col[2], 0.f);
+    sp[2] = make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
     a.depth[i] = (float)tz;
     const uint32_t r0 = (uint32_t)(uint16_t)tx0 | ((uint32_t)(uint16_t)ty0 << 16);
     const uint32_t r1 = (uint32_t)(uint16_t)tx1 | ((uint32_t)(uint16_t)ty1 << 16);
@@ -207,7 +226,7 @@ extern "C" int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32
     a.n = n;
     a.means = means; a.log_scales = log_scales; a.quats = quats; a.opac = opacity_logits; a.sh = sh;
     a.splats = splats; a.depth = depth; a.rect = rect; a.tiles_touched = tiles_touched; a.clamp = clamp_mask;
-    const dim3 grid((n + 255) / 256), block(256);
+    const dim3 grid((n + kPreBlock - 1) / kPreBlock), block(kPreBlock);
     hipStream_t s = as_stream(stream);
     switch (sh_degree) {
         case 0: hipLaunchKernelGGL(k_preprocess<0>, grid, block, 0, s, a); break;

@@ -38,6 +38,7 @@ struct RenderArgs {
     float* image;
     float* final_T;
     int32_t* n_contrib;
+    uint8_t* contrib;   // [K] per list entry: bit q set if a pixel of quadrant q blends it
     const float* dL_dimage;
     float* grad2d;
 };
@@ -68,6 +69,15 @@ struct Stage {
     float4* g1;
     float* g2;
 };
+
+// Stages one entry's tile-relative data into LDS slot `slot` (no culling test).
+__device__ __forceinline__ void stage_data(const RenderArgs& a, uint32_t g, float x0, float y0, Stage st, int slot) {
+    const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
+    const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
+    st.g0[slot] = make_float4((r0.x - x0) + r0.z, (r0.y - y0) + r0.w, r1.x, r1.y);
+    st.g1[slot] = make_float4(r1.z, r1.w, r2.x, r2.y);
+    st.g2[slot] = r2.z;
+}
 
 // Minimum over the segment t in [t0, t1] of (a*c + b*t)^2 + (l*t)^2, the exponent
 // |L^T d|^2 along an axis-parallel edge of a rectangle (c is the fixed coordinate).
@@ -138,6 +148,7 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
     __shared__ float s_g2[kBlock];
     __shared__ uint8_t s_mask[kBlock];
     __shared__ uint16_t s_list[4][kBlock];
+    __shared__ uint32_t s_flag[kBlock];
 
     const BlendArgs& b = a.b;
     const int ntiles = b.tiles_x * b.tiles_y;
@@ -153,11 +164,13 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
     const float inv_amin = 1.f / b.alpha_min;
     const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
     const Stage st{s_g0, s_g1, s_g2};
+    const uint32_t wbit = 1u << wave;
 
     float T = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f;
     int last = 0;
     bool done = !inside;
     bool wave_done = __ballot(!done) == 0;
+    uint32_t kprev = 0xffffffffu;  // list position whose blend flags this thread writes out
     for (uint32_t start = range.x; start < range.y; start += kBlock) {
         const uint32_t k = start + tid;
         uint32_t m = 0;
@@ -165,7 +178,11 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
             const uint32_t g = a.list[k];
             if (g < a.n) m = stage_entry(a, g, x0, y0, inv_amin, st, tid);
         }
+        // the previous batch's flags are final (the loop ends with a barrier)
+        if (kprev != 0xffffffffu) a.contrib[kprev] = (uint8_t)s_flag[tid];
+        kprev = k < range.y ? k : 0xffffffffu;
         s_mask[tid] = (uint8_t)m;
+        s_flag[tid] = 0u;
         __syncthreads();
         const int cnt = wave_done ? 0 : compact(s_mask, s_list[wave], wave, lane);
         const int base = (int)(start - range.x);
@@ -190,6 +207,7 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
                 C2 = __builtin_fmaf(w, cba, C2);
                 T = ok ? Tn : T;
                 last = ok ? base + ea + 1 : last;
+                if (__ballot(ok) != 0 && lane == 0) atomicOr(&s_flag[ea], wbit);
             }
             {
                 bool ok = has2 && !done && pb.alpha >= b.alpha_min;
@@ -203,12 +221,14 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
                 C2 = __builtin_fmaf(w, cbb, C2);
                 T = ok ? Tn : T;
                 last = ok ? base + eb + 1 : last;
+                if (__ballot(ok) != 0 && lane == 0) atomicOr(&s_flag[eb], wbit);
             }
             if (__ballot(!done) == 0) break;
         }
         wave_done = __ballot(!done) == 0;
         if (__syncthreads_count(done ? 1 : 0) == kBlock) break;
     }
+    if (kprev != 0xffffffffu) a.contrib[kprev] = (uint8_t)s_flag[tid];
     if (inside) {
         const size_t pix = (size_t)py * b.width + px;
         const size_t plane = (size_t)b.width * b.height;
@@ -300,7 +320,6 @@ __global__ __launch_bounds__(kBlock) void k_render_bwd(RenderArgs a) {
     const bool inside = px < b.width && py < b.height;
     const float fx = (float)lx + 0.5f, fy = (float)ly + 0.5f;
     const float x0 = (float)(tx * kTile), y0 = (float)(ty * kTile);
-    const float inv_amin = 1.f / b.alpha_min;
     const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
     const Stage st{s_g0, s_g1, s_g2};
 
@@ -331,12 +350,12 @@ __global__ __launch_bounds__(kBlock) void k_render_bwd(RenderArgs a) {
         uint32_t m = 0;
         const uint32_t g = k >= (int32_t)range.x ? a.list[k] : 0xffffffffu;
         if (g < a.n) {
-            s_gid[tid] = g;
-            m = stage_entry(a, g, x0, y0, inv_amin, st, tid);
-            const int pos = k - (int)range.x;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (pos >= s_wmax[q]) m &= ~(1u << q);
+            // only the quadrants in which the forward blended this entry at some pixel
+            m = a.contrib[k];
+            if (m) {
+                s_gid[tid] = g;
+                stage_data(a, g, x0, y0, st, tid);
+            }
         }
         s_mask[tid] = (uint8_t)m;
         __syncthreads();
@@ -457,27 +476,28 @@ using namespace gs;
 
 extern "C" int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                              const uint32_t* point_list, const float* splats, float* image, float* final_T,
-                             int32_t* n_contrib, void* stream) {
+                             int32_t* n_contrib, uint8_t* contrib, void* stream) {
     int rc = render_common_checks(cam, set, tile_ranges, splats);
     if (rc) return rc;
     if (n < 0 || !image || !final_T || !n_contrib) return GS_EINVAL;
-    if (n > 0 && (!point_list || !splats)) return GS_EINVAL;
+    if (n > 0 && (!point_list || !splats || !contrib)) return GS_EINVAL;
     RenderArgs a{};
     a.b = blend_args(cam, set);
     a.n = (uint32_t)n;
     a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
-    a.image = image; a.final_T = final_T; a.n_contrib = n_contrib;
+    a.image = image; a.final_T = final_T; a.n_contrib = n_contrib; a.contrib = contrib;
     hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam)), dim3(kBlock), 0, as_stream(stream), a);
     return launch_status();
 }
 
 extern "C" int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                              const uint32_t* point_list, const float* splats, const float* final_T,
-                             const int32_t* n_contrib, const float* dL_dimage, float* grad2d, void* stream) {
+                             const int32_t* n_contrib, const uint8_t* contrib, const float* dL_dimage,
+                             float* grad2d, void* stream) {
     int rc = render_common_checks(cam, set, tile_ranges, splats);
     if (rc) return rc;
     if (n < 0 || !final_T || !n_contrib || !dL_dimage) return GS_EINVAL;
-    if (n > 0 && (!point_list || !splats || !grad2d)) return GS_EINVAL;
+    if (n > 0 && (!point_list || !splats || !grad2d || !contrib)) return GS_EINVAL;
     if (n > 0 && !aligned16(grad2d)) return GS_EALIGN;
     hipStream_t s = as_stream(stream);
     if (n > 0) {
@@ -490,6 +510,7 @@ extern "C" int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32
     a.n = (uint32_t)n;
     a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
     a.final_T = const_cast<float*>(final_T); a.n_contrib = const_cast<int32_t*>(n_contrib);
+    a.contrib = const_cast<uint8_t*>(contrib);
     a.dL_dimage = dL_dimage; a.grad2d = grad2d;
     hipLaunchKernelGGL(k_render_bwd, dim3(render_grid(cam)), dim3(kBlock), 0, s, a);
     return launch_status();

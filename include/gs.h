@@ -149,11 +149,16 @@ int gs_bin_keys(const gs_camera* cam, const uint32_t* tile_ranges, const uint32_
  * A pair is skipped when alpha < alpha_min; a pixel stops before the entry
  * whose T (1 - alpha) would fall below T_min.
  * Out: image [3,H,W] = C + T_final bg; final_T [H,W]; n_contrib [H,W] int32 =
- * position in the tile's list of the last blended entry + 1 (0 if none).
+ * position in the tile's list of the last blended entry + 1 (0 if none);
+ * contrib [key_capacity] uint8, one byte per point_list entry: bit q (q = 0..3,
+ * the 8x8 quadrants of the tile in row-major order) is set if some pixel of
+ * quadrant q blended the entry.  Only entries up to the last one any pixel of
+ * the tile blends are written.  gs_render_bwd reads it back ([P3] sections 1
+ * and 5: the backward reuses the forward's intermediates).
  */
 int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
                   const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
-                  float* image, float* final_T, int32_t* n_contrib, void* stream);
+                  float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib, void* stream);
 
 /*
  * gs_render_bwd -- reverse per-pixel walk from the stored final
@@ -161,7 +166,9 @@ int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
  *   dL/dc = T alpha dL/dpix;  dL/dalpha = T sum_ch dL/dpix_ch (c_ch - C_next,ch)
  * with C_next starting at the background; then through alpha = opacity G
  * (zero when clamped) and G = exp(power).
- * In: dL_dimage [3,H,W].  Out: grad2d [n,12] (zeroed by the call, then
+ * In: final_T, n_contrib and contrib from gs_render_fwd (only entries whose
+ * contrib bit is set for a quadrant are walked by that quadrant's pixels),
+ * dL_dimage [3,H,W].  Out: grad2d [n,12] (zeroed by the call, then
  * accumulated): dL/du, dL/dv, dL/dA, dL/dB, dL/dC (conic [[A,B],[B,C]],
  * power = -A dx^2/2 - B dx dy - C dy^2/2, d = pixel - mean), dL/dopacity,
  * dL/dr, dL/dg, dL/db, 0, 0, 0.  Accumulation order is not fixed, so the
@@ -169,8 +176,8 @@ int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
  */
 int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32_t n,
                   const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
-                  const float* final_T, const int32_t* n_contrib, const float* dL_dimage,
-                  float* grad2d, void* stream);
+                  const float* final_T, const int32_t* n_contrib, const uint8_t* contrib,
+                  const float* dL_dimage, float* grad2d, void* stream);
 
 /*
  * gs_preprocess_bwd -- 2D -> 3D gradients ([P3] section 4: through the view

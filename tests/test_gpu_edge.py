@@ -164,7 +164,9 @@ def test_abi_errors():
     assert lib.gs_bin_workspace_size(n, C.byref(cam), 1 << 31, C.byref(sz)) == -5
     bad = gs.camera_struct(scenes.Camera.identity(32, 32, 30.0))
     bad.width = 0
-    assert lib.gs_render_fwd(C.byref(bad), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, None) == -1
+    assert lib.gs_render_fwd(C.byref(bad), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None) == -1
+    # missing contrib buffer
+    assert lib.gs_render_fwd(C.byref(cam), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, None, None) == -1
     assert lib.gs_error_string(-3) == b"workspace too small"
 
 
