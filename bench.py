@@ -8,6 +8,9 @@ Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is Gaussian-pixel blend pairs per second over the
 whole step: (evaluated forward pairs + walked backward pairs) / step time.
+`fwd_bwd` reports the rasterizer alone on the same scene and state: preprocess,
+binning, forward, backward blend and the unfused 2D->3D backward that writes
+the 3D gradients (no loss, no optimizer).
 """
 from __future__ import annotations
 
@@ -89,7 +92,9 @@ class Step:
         lr = scenes.ADAM_LR
         self.lr = dict(lr)
         self.step_no = 0
-        self.stages = ["preprocess", "bin_sort", "render_fwd", "loss", "render_bwd", "grad3d_densify_adam"]
+        self.stages = ["preprocess", "bin_sort", "render_fwd", "loss", "zero_grad2d", "render_bwd",
+                       "grad3d_densify_adam"]
+        self.g3 = {k: torch.empty_like(v) for k, v in self.p.items()}
 
     def run(self, events=None, check=False):
         gs, r, p = self.gs, self.rast, self.p
@@ -112,11 +117,20 @@ class Step:
         mark(3)
         gs.gs_image_loss("l1", r.image, self.target, self.dL, self.loss)
         mark(4)
-        r.backward_2d(self.dL)
+        r.grad2d.zero_()
         mark(5)
+        r.backward_2d(self.dL, accumulate=True)
+        mark(6)
         gs.gs_preprocess_bwd_adam(r.cam, r.settings, r.deg, p, r.tiles_touched, r.clamp, r.grad2d, self.m, self.v,
                                   self.lr, self.step_no, densify_accum=self.accum, densify_count=self.count)
-        mark(6)
+        mark(7)
+
+    def preprocess_bwd(self):
+        """The unfused 2D->3D backward with its gradients written out (the rasterizer's own backward)."""
+        r, p, g = self.rast, self.p, self.g3
+        self.gs.gs_preprocess_bwd(r.cam, r.settings, r.deg, p["means"], p["log_scales"], p["quats"],
+                                  p["opacity_logits"], p["sh"], r.tiles_touched, r.clamp, r.grad2d, g["means"],
+                                  g["log_scales"], g["quats"], g["opacity_logits"], g["sh"])
 
 
 def cpu_baseline(sc, frac, seed=0):
@@ -209,6 +223,14 @@ def main():
     assert int(st.rast.overflow.item()) == 0, "list capacity overflow during timing"
     c1 = st.rast.count_pairs().cpu().numpy()
     torch.cuda.synchronize()
+    # the rasterizer's own 2D->3D backward (gradients written, no Adam), timed on the same state
+    pe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        pe[i][0].record()
+        st.preprocess_bwd()
+        pe[i][1].record()
+    torch.cuda.synchronize()
+    pbwd_ms = float(np.mean([a.elapsed_time(b) for a, b in pe]))
     stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, name in enumerate(st.stages)}
     ms = elapsed * 1e3 / args.steps
@@ -216,7 +238,9 @@ def main():
     p_fwd, p_bwd, p_blend = counts
     pairs = p_fwd + p_bwd
     value = pairs / (ms * 1e-3)
-    raster_ms = sum(stage_ms[k] for k in ("preprocess", "bin_sort", "render_fwd", "render_bwd"))
+    # the rasterizer alone, forward + backward down to the 3D gradients (no loss, no optimizer)
+    raster_ms = sum(stage_ms[k] for k in ("preprocess", "bin_sort", "render_fwd", "zero_grad2d", "render_bwd"))
+    raster_ms += pbwd_ms
 
     # roofline of the dominant kernel (render_bwd: FP32 VALU bound)
     dom = max(("render_fwd", "render_bwd"), key=lambda k: stage_ms[k])
@@ -224,7 +248,6 @@ def main():
         flops = FLOPS_EVAL * p_bwd + FLOPS_BWD_BLEND * p_blend
     else:
         flops = FLOPS_EVAL * p_fwd + FLOPS_FWD_BLEND * p_blend
-    # the render_bwd stage also holds the 48 MB gradient clear; time the kernel alone from the stage
     achieved = flops / (stage_ms[dom] * 1e-3) / 1e12
     traffic = read_traffic(dom)
     roof = dict(kernel=dom, bound="alu", achieved=round(achieved, 3), peak=PEAK_FP32_TFLOPS, unit="TFLOP/s",
@@ -238,7 +261,10 @@ def main():
                                     "fwd + L1 + bwd + densify stat + Adam",
                            gaussians=sc.n, width=sc.cam.width, height=sc.cam.height, sh_degree=sc.sh_degree,
                            tile=16, parallelism="single-gpu"),
-               fwd_bwd_ms_excl_grad3d=round(raster_ms, 4), stage_ms={k: round(v, 4) for k, v in stage_ms.items()},
+               fwd_bwd=dict(ms=round(raster_ms, 4), pairs_per_s=float(pairs / (raster_ms * 1e-3)),
+                            stages="preprocess + bin_sort + render_fwd + zero_grad2d + render_bwd + preprocess_bwd",
+                            preprocess_bwd_ms=round(pbwd_ms, 4)),
+               stage_ms={k: round(v, 4) for k, v in stage_ms.items()},
                pairs=dict(fwd_evaluated=float(p_fwd), bwd_walked=float(p_bwd), blended=float(p_blend),
                           keys=int(st.rast.num_keys.item())),
                roofline=roof)

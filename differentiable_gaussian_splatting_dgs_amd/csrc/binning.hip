@@ -13,9 +13,10 @@
 //      digit histograms for the 4 depth passes.
 //   2. LSD onesweep radix sort of (depth key, index) over N, 4 x 8-bit passes.
 //      Stable, so equal depths stay in index order.
-//   3. emit: an exclusive scan of tiles_touched in depth order (decoupled
-//      look-back) fused with writing (tile id, Gaussian) for every tile of
-//      every Gaussian, plus the tile-digit histograms.
+//   3. emit: an exclusive scan of tiles_touched in depth order gives every
+//      Gaussian its first output slot; then fixed-size blocks of output slots
+//      each write (tile id, Gaussian) for their slots (balanced however many
+//      tiles a Gaussian covers) and count the tile digits.
 //   4. LSD onesweep radix sort of (tile id, Gaussian) over K, 1-2 x 8-bit passes.
 //      Stable, so each tile keeps the depth order of step 2.
 //   5. tile ranges from the sorted tile ids.
@@ -47,7 +48,9 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 
 constexpr int kEmitThreads = 256;
 constexpr int kEmitIPT = 4;
-constexpr int kEmitPart = kEmitThreads * kEmitIPT;  // 1024 Gaussians per partition
+constexpr int kEmitPart = kEmitThreads * kEmitIPT;  // 1024 Gaussians per scan partition
+constexpr int kSlotsPT = 8;
+constexpr int kSlots = kEmitThreads * kSlotsPT;     // 2048 output slots per expand block
 
 __device__ inline uint32_t ld_acquire(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -78,10 +81,25 @@ __device__ inline void wave_hist_add(uint32_t* s_hist, uint32_t bin, bool valid)
     if (valid && (m & lanemask_lt()) == 0) atomicAdd(&s_hist[bin], (uint32_t)__popcll(m));
 }
 
+// Sum over the kStripes histogram copies of bin b.
+__device__ inline uint32_t stripe_sum(const uint32_t* stripes, int b) {
+    uint32_t acc = 0;
+#pragma unroll
+    for (int p = 0; p < kStripes; ++p) acc += stripes[(size_t)p * kHistBins + b];
+    return acc;
+}
+
+// Partitions are claimed in groups so that no single counter sees more than
+// 1/kTicketGroups of the blocks' atomics (same-address atomics from many
+// blocks serialise): block b takes the next ticket t of group b % kTicketGroups
+// and works on partition t * kTicketGroups + b % kTicketGroups.  Claims stay in
+// dispatch order within each group, which keeps the look-back deadlock-free.
+constexpr int kTicketGroups = 64;
+constexpr int kTicketStride = 16;  // one 64-byte line per counter
+
 // Workspace layout (all offsets 256-byte aligned).
 struct Layout {
-    size_t hist;        // uint32 [4 depth digits + 2 tile digits][256]
-    size_t tickets;     // uint32 [8]
+    size_t tickets;     // uint32 [6 passes][kTicketGroups][kTicketStride] partition tickets
     size_t err;         // uint32 [1] look-back spin-limit flag
     size_t dstatus;     // uint32 [4][dparts][256]
     size_t etotal;      // uint32 [eparts] entries per emit partition, then their exclusive offsets
@@ -89,9 +107,11 @@ struct Layout {
     size_t zero_end;    // everything above is zeroed per call
     size_t stripes;     // uint32 [kStripes][kHistBins] striped digit counts (zeroed)
     size_t dkeys0, dvals0, dkeys1, dvals1;  // uint32 [n] each
+    size_t goff;                            // uint32 [n] first output slot, depth order
+    size_t bstart;                          // uint32 [xblocks + 1] first Gaussian (depth order) of each expand block
     size_t tkeys0, tkeys1, tvals0;          // uint32 [cap] each
     size_t total;
-    uint32_t dparts, eparts, tparts;
+    uint32_t dparts, eparts, tparts, xblocks;
 };
 
 inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -101,9 +121,9 @@ inline Layout make_layout(int32_t n, int64_t cap) {
     L.dparts = (uint32_t)((n + kDepthPart - 1) / kDepthPart);
     L.eparts = (uint32_t)((n + kEmitPart - 1) / kEmitPart);
     L.tparts = (uint32_t)((cap + kTilePart - 1) / kTilePart);
+    L.xblocks = (uint32_t)((cap + kSlots - 1) / kSlots);
     size_t o = 0;
-    L.hist = o; o = up256(o + 6 * kRadix * 4);
-    L.tickets = o; o = up256(o + 8 * 4);
+    L.tickets = o; o = up256(o + (size_t)6 * kTicketGroups * kTicketStride * 4);
     L.err = o; o = up256(o + 4);
     L.dstatus = o; o = up256(o + (size_t)4 * L.dparts * kRadix * 4);
     L.etotal = o; o = up256(o + (size_t)L.eparts * 4);
@@ -114,6 +134,8 @@ inline Layout make_layout(int32_t n, int64_t cap) {
     L.dvals0 = o; o = up256(o + (size_t)n * 4);
     L.dkeys1 = o; o = up256(o + (size_t)n * 4);
     L.dvals1 = o; o = up256(o + (size_t)n * 4);
+    L.goff = o; o = up256(o + (size_t)n * 4);
+    L.bstart = o; o = up256(o + ((size_t)L.xblocks + 1) * 4);
     L.tkeys0 = o; o = up256(o + (size_t)cap * 4);
     L.tkeys1 = o; o = up256(o + (size_t)cap * 4);
     L.tvals0 = o; o = up256(o + (size_t)cap * 4);
@@ -161,16 +183,6 @@ __global__ __launch_bounds__(256) void k_depth_keys(int32_t n, const float* dept
         if (sh[b]) atomicAdd(&out[b], sh[b]);
 }
 
-// hist[b] = sum of the kStripes copies, for bins [b0, b0 + nbins).
-__global__ void k_hist_reduce(const uint32_t* stripes, int b0, int nbins, uint32_t* hist) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= nbins) return;
-    uint32_t acc = 0;
-#pragma unroll
-    for (int p = 0; p < kStripes; ++p) acc += stripes[(size_t)p * kHistBins + b0 + b];
-    hist[b0 + b] = acc;
-}
-
 struct PassArgs {
     const uint32_t* keys_in;
     const uint32_t* vals_in;
@@ -179,9 +191,10 @@ struct PassArgs {
     const uint32_t* count_dev;  // items = min(*count_dev, cap) when non-null, else count_host
     uint32_t count_host;
     uint32_t cap;
-    const uint32_t* hist;  // [256] this digit over all items
+    const uint32_t* stripes;  // striped digit counts; this pass's bins start at hist_bin
+    int hist_bin;
     uint32_t* status;      // [parts][256], zeroed
-    uint32_t* ticket;      // zeroed
+    uint32_t* ticket;      // [kTicketGroups][kTicketStride], zeroed
     uint32_t* err;
     int shift;
 };
@@ -201,11 +214,14 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
     __shared__ uint32_t s_part;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    if (tid == 0) s_part = atomicAdd(p.ticket, 1u);
+    if (tid == 0) {
+        const uint32_t grp = blockIdx.x % kTicketGroups;
+        s_part = atomicAdd(p.ticket + grp * kTicketStride, 1u) * kTicketGroups + grp;
+    }
     for (int i = tid; i < 4 * kRadix; i += kSortThreads) (&s_wave[0][0])[i] = 0;
     // exclusive scan of the digit histogram (256 entries, one per thread)
     {
-        const uint32_t h = p.hist[tid];
+        const uint32_t h = stripe_sum(p.stripes, p.hist_bin + tid);
         uint32_t x = h;
         for (int o = 1; o < 64; o <<= 1) {
             const uint32_t y = __shfl_up(x, o, 64);
@@ -335,14 +351,16 @@ struct EmitArgs {
     int32_t tiles_x;
     uint32_t cap;
     uint32_t eparts;
-    const uint32_t* order;   // Gaussians in depth order
+    uint32_t xblocks;
+    const uint32_t* order;   // Gaussians in depth order (visible ones first)
     const int16_t* rect;
     const int32_t* tt;
+    uint32_t* part;          // [eparts] entries per scan partition -> exclusive offsets
+    uint32_t* goff;          // [n] first output slot of the j-th Gaussian in depth order
+    uint32_t* bstart;        // [xblocks + 1] depth-order index of each expand block's first Gaussian
     uint32_t* tkeys;         // [cap] tile id
     uint32_t* tvals;         // [cap] Gaussian
-    uint32_t* part;          // [eparts] entries per partition -> exclusive offsets
     uint32_t* stripes;       // [kStripes][kHistBins] striped digit counts
-    uint32_t* hist;          // [kHistBins]
     uint32_t* num_keys;
     uint32_t* overflow;
 };
@@ -352,65 +370,10 @@ __device__ inline void unpack_rect(uint2 r, int& x0, int& y0, int& x1, int& y1) 
     x1 = (int)(int16_t)(r.y & 0xffffu); y1 = (int)(int16_t)(r.y >> 16);
 }
 
-// Adds the digit counts of the tiles of rect to the block histograms: per row
-// the tile ids form one run [t0, t0 + w); its low bytes are a cyclic run of
-// bins (recorded as a difference array, +1 at the start and -1 past the end,
-// whole wraps as a uniform add) and its high bytes cover at most a few bins.
-__device__ inline void rect_hist(int x0, int y0, int x1, int y1, int tiles_x, uint32_t* s_lo_diff,
-                                 uint32_t* s_lo_all, uint32_t* s_hi) {
-    const uint32_t w = (uint32_t)(x1 - x0);
-    for (int y = y0; y < y1; ++y) {
-        const uint32_t t0 = (uint32_t)(y * tiles_x + x0), t1 = t0 + w;  // [t0, t1)
-        // low byte: w / 256 full cycles plus a cyclic run of w % 256 bins from t0 & 255
-        const uint32_t full = w >> 8, rem = w & 255u;
-        if (full) atomicAdd(s_lo_all, full);
-        if (rem) {
-            const uint32_t b0 = t0 & 255u, b1 = (t0 + rem) & 255u;
-            atomicAdd(&s_lo_diff[b0], 1u);
-            atomicAdd(&s_lo_diff[b1], 0xffffffffu);  // -1
-            if (b1 <= b0 && b1 != 0u) atomicAdd(s_lo_all, 1u);  // the run wraps past bin 255
-            if (b1 <= b0 && b1 == 0u) { /* ends exactly at 256: the -1 at bin 0 cancels the wrap */
-                atomicAdd(s_lo_all, 1u);
-            }
-        }
-        // high byte: bins (t0 >> 8) .. ((t1 - 1) >> 8)
-        for (uint32_t hb = t0 >> 8; hb <= ((t1 - 1u) >> 8); ++hb) {
-            const uint32_t lo = max(t0, hb << 8), hi = min(t1, (hb + 1u) << 8);
-            atomicAdd(&s_hi[hb & 255u], hi - lo);
-        }
-    }
-}
-
-// 3a. entries per partition of 1024 depth-sorted Gaussians, and the tile-digit counts.
-__global__ __launch_bounds__(kEmitThreads) void k_emit_count(EmitArgs a) {
-    __shared__ uint32_t s_lo_diff[kRadix];
-    __shared__ uint32_t s_hi[kRadix];
-    __shared__ uint32_t s_lo_all;
-    __shared__ uint32_t s_wsum[4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    s_lo_diff[tid] = 0;
-    s_hi[tid] = 0;
-    if (tid == 0) s_lo_all = 0;
-    __syncthreads();
-    uint32_t tsum = 0;
-#pragma unroll
-    for (int k = 0; k < kEmitIPT; ++k) {
-        const int64_t j = (int64_t)blockIdx.x * kEmitPart + k * kEmitThreads + tid;
-        const uint32_t g = j < a.n ? a.order[j] : 0xffffffffu;
-        const uint32_t c = g < (uint32_t)a.n ? (uint32_t)max(a.tt[g], 0) : 0u;
-        if (c) {
-            int x0, y0, x1, y1;
-            unpack_rect(reinterpret_cast<const uint2*>(a.rect)[g], x0, y0, x1, y1);
-            rect_hist(x0, y0, x1, y1, a.tiles_x, s_lo_diff, &s_lo_all, s_hi);
-        }
-        tsum += c;
-    }
-    for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, 64);
-    if (lane == 0) s_wsum[wave] = tsum;
-    __syncthreads();
-    if (tid == 0) a.part[blockIdx.x] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    // low-byte counts = inclusive prefix sum of the difference array + whole cycles
-    uint32_t x = s_lo_diff[tid];
+// Block-wide exclusive sum over 256 threads; returns this thread's prefix and the total.
+__device__ inline uint32_t block_excl_sum(uint32_t v, uint32_t* s_wsum, uint32_t& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
     for (int o = 1; o < 64; o <<= 1) {
         const uint32_t y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
@@ -418,113 +381,148 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_count(EmitArgs a) {
     __syncthreads();
     if (lane == 63) s_wsum[wave] = x;
     __syncthreads();
-    for (int w = 0; w < wave; ++w) x += s_wsum[w];
-    const uint32_t lo = x + s_lo_all;
-    uint32_t* out = a.stripes + (size_t)(blockIdx.x % kStripes) * kHistBins + 4 * kRadix;
-    if (lo) atomicAdd(&out[tid], lo);
-    if (s_hi[tid]) atomicAdd(&out[kRadix + tid], s_hi[tid]);
+    uint32_t add = 0;
+    total = 0;
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave) add += s_wsum[w];
+        total += s_wsum[w];
+    }
+    return x - v + add;
 }
 
-// 3b. one block: exclusive scan of the partition totals, K, the overflow flag,
-// and the tile-digit histogram summed over the stripes.
-__global__ __launch_bounds__(1024) void k_emit_scan(EmitArgs a) {
-    __shared__ uint32_t s_wsum[16];
-    __shared__ uint32_t s_carry;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) s_carry = 0;
-    __syncthreads();
-    for (uint32_t base = 0; base < a.eparts; base += 1024) {
-        const uint32_t i = base + tid;
-        const uint32_t v = i < a.eparts ? a.part[i] : 0u;
-        uint32_t x = v;
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        if (lane == 63) s_wsum[wave] = x;
-        __syncthreads();
-        uint32_t add = s_carry, tot = 0;
-        for (int w = 0; w < 16; ++w) {
-            if (w < wave) add += s_wsum[w];
-            tot += s_wsum[w];
-        }
-        if (i < a.eparts) a.part[i] = x - v + add;
-        __syncthreads();
-        if (tid == 0) s_carry += tot;
-        __syncthreads();
-    }
-    if (tid == 0) {
-        const uint32_t K = s_carry;
+__device__ inline uint32_t tiles_of(const EmitArgs& a, int64_t j) {
+    if (j >= a.n) return 0u;
+    const uint32_t g = a.order[j];
+    return g < (uint32_t)a.n ? (uint32_t)max(a.tt[g], 0) : 0u;
+}
+
+// 3a. entries per scan partition of 1024 depth-ordered Gaussians.
+__global__ __launch_bounds__(kEmitThreads) void k_emit_count(EmitArgs a) {
+    __shared__ uint32_t s_wsum[4];
+    const int tid = threadIdx.x;
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kEmitIPT; ++k) c += tiles_of(a, (int64_t)blockIdx.x * kEmitPart + k * kEmitThreads + tid);
+    uint32_t total;
+    block_excl_sum(c, s_wsum, total);
+    if (tid == 0) a.part[blockIdx.x] = total;
+}
+
+// 3b. first output slot of every Gaussian (depth order), and for every expand
+// block (kSlots consecutive slots) the Gaussian whose range holds its first slot.
+// The partition's offset is the sum of the earlier partitions' totals (at most
+// a few thousand L2-resident words per block, no separate scan pass); the last
+// partition also writes K and the overflow flag.
+__global__ __launch_bounds__(kEmitThreads) void k_emit_offsets(EmitArgs a) {
+    __shared__ uint32_t s_wsum[4];
+    const int tid = threadIdx.x;
+    uint32_t before = 0;
+    for (uint32_t i = tid; i < blockIdx.x; i += kEmitThreads) before += a.part[i];
+    uint32_t pbase;
+    block_excl_sum(before, s_wsum, pbase);
+    const int64_t j0 = (int64_t)blockIdx.x * kEmitPart + (int64_t)tid * kEmitIPT;
+    uint32_t c[kEmitIPT], sum = 0;
+#pragma unroll
+    for (int k = 0; k < kEmitIPT; ++k) { c[k] = tiles_of(a, j0 + k); sum += c[k]; }
+    uint32_t total;
+    uint32_t off = pbase + block_excl_sum(sum, s_wsum, total);
+    if (blockIdx.x == gridDim.x - 1 && tid == 0) {
+        const uint32_t K = pbase + total;
         *a.num_keys = K;
         *a.overflow = K > a.cap ? 1u : 0u;
     }
-    if (tid < 2 * kRadix) {
-        uint32_t acc = 0;
-#pragma unroll
-        for (int p = 0; p < kStripes; ++p) acc += a.stripes[(size_t)p * kHistBins + 4 * kRadix + tid];
-        a.hist[4 * kRadix + tid] = acc;
-    }
-}
-
-// 3c. expansion: each block rescans its 1024 Gaussians, then writes (tile,
-// Gaussian) entries entry-parallel: thread t writes entries t, t+256, ... of the
-// block's range, finding each entry's Gaussian by binary search over the block's
-// offsets in LDS (balanced and coalesced).
-__global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
-    __shared__ uint32_t s_off[kEmitPart];   // block-local exclusive offsets
-    __shared__ uint32_t s_g[kEmitPart];     // Gaussian ids
-    __shared__ uint2 s_rect[kEmitPart];
-    __shared__ uint32_t s_wsum[4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t j0 = (int64_t)blockIdx.x * kEmitPart + tid * kEmitIPT;
-    uint32_t g[kEmitIPT], cnt[kEmitIPT], tsum = 0;
 #pragma unroll
     for (int k = 0; k < kEmitIPT; ++k) {
         const int64_t j = j0 + k;
-        g[k] = j < a.n ? a.order[j] : 0xffffffffu;
-        cnt[k] = (g[k] < (uint32_t)a.n) ? (uint32_t)max(a.tt[g[k]], 0) : 0u;
-        tsum += cnt[k];
+        if (j < a.n) a.goff[j] = off;
+        if (c[k]) {
+            // expand blocks whose first slot lies in [off, off + c)
+            for (uint32_t b = (off + kSlots - 1) / kSlots; (uint64_t)b * kSlots < (uint64_t)off + c[k] &&
+                                                             b < a.xblocks; ++b)
+                a.bstart[b] = (uint32_t)j;
+        }
+        off += c[k];
     }
-    uint32_t x = tsum;
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) s_wsum[wave] = x;
-    __syncthreads();
-    uint32_t wadd = 0, btotal = 0;
-    for (int w = 0; w < 4; ++w) {
-        if (w < wave) wadd += s_wsum[w];
-        btotal += s_wsum[w];
-    }
-    uint32_t off = x - tsum + wadd;
+}
+
+// 3c. expansion over output slots: block b writes slots [b kSlots, (b+1) kSlots).
+// Its Gaussians are a run of the depth order starting at bstart[b]; each slot's
+// owner is the last Gaussian whose first slot is at or before it (a max-scan over
+// the heads), and the slot's rank inside the owner's rect gives the tile
+// (row-major).  Also counts the two tile-id digits for the sort.
+__global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
+    __shared__ uint32_t s_gid[kSlots];
+    __shared__ uint32_t s_goff[kSlots];
+    __shared__ uint2 s_rect[kSlots];
+    __shared__ uint32_t s_owner[kSlots];
+    __shared__ uint32_t s_hist[2 * kRadix];
+    __shared__ uint32_t s_wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t K = min(*a.num_keys, a.cap);
+    const uint32_t base = blockIdx.x * (uint32_t)kSlots;
+    const bool active = !*a.overflow && base < K;
+    for (int i = tid; i < 2 * kRadix; i += kEmitThreads) s_hist[i] = 0;
+    if (active) {
+        const uint32_t nout = min((uint32_t)kSlots, K - base);
+        const uint32_t jb = a.bstart[blockIdx.x];
+        for (int s = tid; s < kSlots; s += kEmitThreads) s_owner[s] = 0;
+        __syncthreads();
+        // the block's Gaussians: jb + q (q < nout) whose first slot is < base + nout
+        for (uint32_t q0 = 0; q0 < nout; q0 += kEmitThreads) {
+            const uint32_t q = q0 + tid;
+            const int64_t j = (int64_t)jb + q;
+            const uint32_t go = (q < nout && j < a.n) ? a.goff[j] : 0xffffffffu;
+            const bool in = go < base + nout;
+            if (in) {
+                const uint32_t g = a.order[j];
+                s_goff[q] = go;
+                s_gid[q] = g;
+                s_rect[q] = reinterpret_cast<const uint2*>(a.rect)[g];
+                // head: the slot where this Gaussian's run starts (0 for the first)
+                const uint32_t h = q == 0 ? 0u : go - base;
+                if (h < (uint32_t)kSlots) s_owner[h] = q;
+            }
+            if (!__syncthreads_or(in)) break;  // first slots increase with q
+        }
+        __syncthreads();
+        // inclusive max-scan of s_owner: kSlotsPT consecutive slots per thread
+        uint32_t v[kSlotsPT], run = 0;
 #pragma unroll
-    for (int k = 0; k < kEmitIPT; ++k) {
-        const int q = tid * kEmitIPT + k;
-        s_off[q] = off;
-        s_g[q] = g[k];
-        s_rect[q] = cnt[k] ? reinterpret_cast<const uint2*>(a.rect)[g[k]] : make_uint2(0u, 0u);
-        off += cnt[k];
-    }
-    __syncthreads();
-    const uint32_t prefix = a.part[blockIdx.x];
-    for (uint32_t o = tid; o < btotal; o += kEmitThreads) {
-        // last q with s_off[q] <= o: the Gaussian owning entry o (it has cnt > 0)
-        int lo = 0, hi = kEmitPart - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_off[mid] <= o) lo = mid; else hi = mid - 1;
+        for (int k = 0; k < kSlotsPT; ++k) { run = max(run, s_owner[tid * kSlotsPT + k]); v[k] = run; }
+        uint32_t x = run;
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(x, o, 64);
+            if (lane >= o) x = max(x, y);
         }
-        int x0, y0, x1, y1;
-        unpack_rect(s_rect[lo], x0, y0, x1, y1);
-        const int w = x1 - x0;
-        const int local = (int)(o - s_off[lo]);
-        const int ty = y0 + local / w, tx = x0 + local % w;
-        const uint32_t out = prefix + o;
-        if (out < a.cap) {
-            a.tkeys[out] = (uint32_t)(ty * a.tiles_x + tx);
-            a.tvals[out] = s_g[lo];
+        if (lane == 63) s_wsum[wave] = x;
+        __syncthreads();
+        uint32_t pre = __shfl_up(x, 1, 64);
+        if (lane == 0) pre = 0;
+        for (int w = 0; w < wave; ++w) pre = max(pre, s_wsum[w]);
+#pragma unroll
+        for (int k = 0; k < kSlotsPT; ++k) s_owner[tid * kSlotsPT + k] = max(pre, v[k]);
+        __syncthreads();
+        for (uint32_t s = tid; s < (uint32_t)kSlots; s += kEmitThreads) {
+            const bool ok = s < nout;
+            uint32_t tile = 0;
+            if (ok) {
+                const uint32_t q = s_owner[s];
+                int x0, y0, x1, y1;
+                unpack_rect(s_rect[q], x0, y0, x1, y1);
+                const uint32_t w = (uint32_t)(x1 - x0);
+                const uint32_t r = base + s - s_goff[q];
+                const uint32_t ry = r / w;
+                tile = (uint32_t)(y0 + (int)ry) * (uint32_t)a.tiles_x + (uint32_t)x0 + (r - ry * w);
+                a.tkeys[base + s] = tile;
+                a.tvals[base + s] = s_gid[q];
+            }
+            wave_hist_add(s_hist, tile & 255u, ok);
+            wave_hist_add(s_hist + kRadix, (tile >> 8) & 255u, ok);
         }
+        __syncthreads();
+        uint32_t* out = a.stripes + (size_t)(blockIdx.x % kStripes) * kHistBins + 4 * kRadix;
+        for (int i = tid; i < 2 * kRadix; i += kEmitThreads)
+            if (s_hist[i]) atomicAdd(&out[i], s_hist[i]);
     }
 }
 
@@ -593,13 +591,12 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
     }
     if (n == 0) return launch_status();
 
-    uint32_t* hist = U(L.hist);
     uint32_t* tickets = U(L.tickets);
+    auto ticket = [&](int pass) { return tickets + (size_t)pass * kTicketGroups * kTicketStride; };
     uint32_t* err = U(L.err);
     const int key_blocks = (int)std::min<int64_t>(kKeyBlocks, (n + 255) / 256);
     hipLaunchKernelGGL(k_depth_keys, dim3(key_blocks), dim3(256), 0, s, n, depth, tiles_touched, U(L.dkeys0),
                        U(L.dvals0), U(L.stripes));
-    hipLaunchKernelGGL(k_hist_reduce, dim3(4), dim3(256), 0, s, U(L.stripes), 0, 4 * kRadix, hist);
     // depth sort: 4 passes, 0 -> 1 -> 0 -> 1 -> 0
     uint32_t* dk[2] = {U(L.dkeys0), U(L.dkeys1)};
     uint32_t* dv[2] = {U(L.dvals0), U(L.dvals1)};
@@ -609,9 +606,9 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
         p.keys_out = pass < 3 ? dk[(pass + 1) & 1] : nullptr;
         p.vals_out = dv[(pass + 1) & 1];
         p.count_dev = nullptr; p.count_host = (uint32_t)n; p.cap = (uint32_t)n;
-        p.hist = hist + pass * kRadix;
+        p.stripes = U(L.stripes); p.hist_bin = pass * kRadix;
         p.status = U(L.dstatus) + (size_t)pass * L.dparts * kRadix;
-        p.ticket = tickets + pass;
+        p.ticket = ticket(pass);
         p.err = err;
         p.shift = 8 * pass;
         hipLaunchKernelGGL(k_onesweep<kDepthIPT>, dim3(L.dparts), dim3(kSortThreads), 0, s, p);
@@ -622,27 +619,29 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
     //   2 passes: emit -> (tkeys0, point_list) -> (tkeys1, tvals0) -> (tkeys0, point_list)
     EmitArgs e;
     e.n = n; e.tiles_x = tiles_x(cam); e.cap = (uint32_t)key_capacity; e.eparts = L.eparts;
+    e.xblocks = L.xblocks;
     e.order = dv[0]; e.rect = rect; e.tt = tiles_touched;
+    e.part = U(L.etotal); e.goff = U(L.goff); e.bstart = U(L.bstart);
     e.tkeys = U(L.tkeys0); e.tvals = tile_passes == 1 ? U(L.tvals0) : point_list;
-    e.part = U(L.etotal); e.stripes = U(L.stripes); e.hist = hist;
+    e.stripes = U(L.stripes);
     e.num_keys = num_keys_dev; e.overflow = overflow_dev;
     hipLaunchKernelGGL(k_emit_count, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
-    hipLaunchKernelGGL(k_emit_scan, dim3(1), dim3(1024), 0, s, e);
-    hipLaunchKernelGGL(k_emit_expand, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
+    hipLaunchKernelGGL(k_emit_offsets, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
     if (key_capacity == 0) return launch_status();
+    hipLaunchKernelGGL(k_emit_expand, dim3(L.xblocks), dim3(kEmitThreads), 0, s, e);
     PassArgs p;
     p.count_dev = num_keys_dev; p.count_host = 0; p.cap = (uint32_t)key_capacity; p.err = err;
     p.keys_in = U(L.tkeys0); p.vals_in = e.tvals;
     p.keys_out = U(L.tkeys1); p.vals_out = tile_passes == 1 ? point_list : U(L.tvals0);
-    p.hist = hist + 4 * kRadix; p.status = U(L.tstatus); p.ticket = tickets + 5; p.shift = 0;
+    p.stripes = U(L.stripes); p.hist_bin = 4 * kRadix; p.status = U(L.tstatus); p.ticket = ticket(4); p.shift = 0;
     hipLaunchKernelGGL(k_onesweep<kTileIPT>, dim3(L.tparts), dim3(kSortThreads), 0, s, p);
     const uint32_t* tk_final = U(L.tkeys1);
     if (tile_passes == 2) {
         PassArgs p2 = p;
         p2.keys_in = U(L.tkeys1); p2.vals_in = U(L.tvals0);
         p2.keys_out = U(L.tkeys0); p2.vals_out = point_list;
-        p2.hist = hist + 5 * kRadix; p2.status = U(L.tstatus) + (size_t)L.tparts * kRadix;
-        p2.ticket = tickets + 6; p2.shift = 8;
+        p2.hist_bin = 5 * kRadix; p2.status = U(L.tstatus) + (size_t)L.tparts * kRadix;
+        p2.ticket = ticket(5); p2.shift = 8;
         hipLaunchKernelGGL(k_onesweep<kTileIPT>, dim3(L.tparts), dim3(kSortThreads), 0, s, p2);
         tk_final = U(L.tkeys0);
     }

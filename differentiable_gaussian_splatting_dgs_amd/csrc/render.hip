@@ -493,14 +493,15 @@ extern "C" int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32
 extern "C" int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                              const uint32_t* point_list, const float* splats, const float* final_T,
                              const int32_t* n_contrib, const uint8_t* contrib, const float* dL_dimage,
-                             float* grad2d, void* stream) {
+                             float* grad2d, int32_t accumulate, void* stream) {
     int rc = render_common_checks(cam, set, tile_ranges, splats);
     if (rc) return rc;
     if (n < 0 || !final_T || !n_contrib || !dL_dimage) return GS_EINVAL;
     if (n > 0 && (!point_list || !splats || !grad2d || !contrib)) return GS_EINVAL;
     if (n > 0 && !aligned16(grad2d)) return GS_EALIGN;
     hipStream_t s = as_stream(stream);
-    if (n > 0) {
+    if (accumulate != 0 && accumulate != 1) return GS_EINVAL;
+    if (n > 0 && !accumulate) {
         const size_t cnt = (size_t)n * GS_GRAD2D_STRIDE;
         hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)std::min<size_t>((cnt + 255) / 256, 4096)), dim3(256), 0, s,
                            grad2d, cnt);

@@ -76,7 +76,7 @@ def load_library(path=LIB_PATH):
     lib.gs_bin_sort.argtypes = [P(GsCamera), _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
     lib.gs_bin_keys.argtypes = [P(GsCamera), _vp, _vp, _vp, _vp, _vp]
     lib.gs_render_fwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 7 + [_vp]
-    lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_vp]
+    lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_i32, _vp]
     lib.gs_preprocess_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
     lib.gs_preprocess_bwd_adam.argtypes = ([P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 8 +
                                            [P(GsAdamState)] + [_vp] * 7 + [_vp])
@@ -198,13 +198,14 @@ def gs_render_fwd(cam, settings, n, tile_ranges, point_list, splats, image, fina
     _check(rc, "gs_render_fwd")
 
 
-def gs_render_bwd(cam, settings, n, tile_ranges, point_list, splats, final_T, n_contrib, contrib, dL_dimage, grad2d):
+def gs_render_bwd(cam, settings, n, tile_ranges, point_list, splats, final_T, n_contrib, contrib, dL_dimage, grad2d,
+                  accumulate=False):
     rc = load_library().gs_render_bwd(
         C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
         _p(point_list, torch.int32, "point_list"), _p(splats, torch.float32, "splats"),
         _p(final_T, torch.float32, "final_T"), _p(n_contrib, torch.int32, "n_contrib"),
         _p(contrib, torch.uint8, "contrib"), _p(dL_dimage, torch.float32, "dL_dimage"),
-        _p(grad2d, torch.float32, "grad2d"), _stream())
+        _p(grad2d, torch.float32, "grad2d"), 1 if accumulate else 0, _stream())
     _check(rc, "gs_render_bwd")
 
 
@@ -359,9 +360,9 @@ class Rasterizer:
         self.render()
         return self.image
 
-    def backward_2d(self, dL_dimage):
+    def backward_2d(self, dL_dimage, accumulate=False):
         gs_render_bwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats,
-                      self.final_T, self.n_contrib, self.contrib, dL_dimage, self.grad2d)
+                      self.final_T, self.n_contrib, self.contrib, dL_dimage, self.grad2d, accumulate)
         return self.grad2d
 
     def backward(self, p, dL_dimage, out=None):

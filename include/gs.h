@@ -168,8 +168,9 @@ int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
  * (zero when clamped) and G = exp(power).
  * In: final_T, n_contrib and contrib from gs_render_fwd (only entries whose
  * contrib bit is set for a quadrant are walked by that quadrant's pixels),
- * dL_dimage [3,H,W].  Out: grad2d [n,12] (zeroed by the call, then
- * accumulated): dL/du, dL/dv, dL/dA, dL/dB, dL/dC (conic [[A,B],[B,C]],
+ * dL_dimage [3,H,W].  Out: grad2d [n,12]; with accumulate = 0 the call clears
+ * it first, with accumulate = 1 the gradients are added to what it holds (the
+ * caller cleared it, or sums several calls): dL/du, dL/dv, dL/dA, dL/dB, dL/dC (conic [[A,B],[B,C]],
  * power = -A dx^2/2 - B dx dy - C dy^2/2, d = pixel - mean), dL/dopacity,
  * dL/dr, dL/dg, dL/db, 0, 0, 0.  Accumulation order is not fixed, so the
  * float32 result varies in the last bits between runs.
@@ -177,7 +178,7 @@ int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
 int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32_t n,
                   const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
                   const float* final_T, const int32_t* n_contrib, const uint8_t* contrib,
-                  const float* dL_dimage, float* grad2d, void* stream);
+                  const float* dL_dimage, float* grad2d, int32_t accumulate, void* stream);
 
 /*
  * gs_preprocess_bwd -- 2D -> 3D gradients ([P3] section 4: through the view

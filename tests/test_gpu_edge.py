@@ -167,7 +167,26 @@ def test_abi_errors():
     assert lib.gs_render_fwd(C.byref(bad), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None) == -1
     # missing contrib buffer
     assert lib.gs_render_fwd(C.byref(cam), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, None, None) == -1
+    # accumulate must be 0 or 1
+    assert lib.gs_render_bwd(C.byref(cam), C.byref(st), n, *([ptr] * 8), 2, None) == -1
     assert lib.gs_error_string(-3) == b"workspace too small"
+
+
+def test_backward_accumulate():
+    """accumulate=1 adds the call's gradients to what grad2d holds; accumulate=0 overwrites."""
+    import torch
+    gs = _gs()
+    sc = scenes.random_small(31, n=800, width=72, height=56, sh_degree=1, scale_mu=-2.4)
+    r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
+    r.forward(to_dev(sc.params()))
+    dL = torch.from_numpy(sc.dL_dimage).cuda()
+    g1 = r.backward_2d(dL).clone()
+    g2 = r.backward_2d(dL, accumulate=True).clone()
+    g3 = r.backward_2d(dL).clone()
+    torch.cuda.synchronize()
+    assert float(g1.abs().sum()) > 0
+    assert rel_l2(g2.cpu().numpy(), 2 * g1.cpu().numpy()) < 1e-6
+    assert rel_l2(g3.cpu().numpy(), g1.cpu().numpy()) < 1e-6
 
 
 def test_training_tail_matches_oracle():
