@@ -105,13 +105,11 @@ __device__ __forceinline__ void sh_grad(float x, float y, float z, const float* 
     }
 }
 
-__device__ __forceinline__ void adam1(float& p, float g, float* m, float* v, size_t i, float lr,
-                                      const AdamHyper& h) {
-    const float mm = h.b1 * m[i] + (1.f - h.b1) * g;
-    const float vv = h.b2 * v[i] + (1.f - h.b2) * g * g;
-    m[i] = mm;
-    v[i] = vv;
-    p -= lr * (mm * h.inv_c1) / (sqrtf(vv) * h.inv_sqrt_c2 + h.eps);
+// One Adam update on values already in registers: moments m, v and parameter p.
+__device__ __forceinline__ void adam_reg(float& p, float g, float& m, float& v, float lr, const AdamHyper& h) {
+    m = h.b1 * m + (1.f - h.b1) * g;
+    v = h.b2 * v + (1.f - h.b2) * g * g;
+    p -= lr * (m * h.inv_c1) / (sqrtf(v) * h.inv_sqrt_c2 + h.eps);
 }
 
 // The per-Gaussian part of the chain: gradients of the mean, log-scales, raw
@@ -299,6 +297,28 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
 
     if (t < ng) {
         const int i = g0 + t;
+        // Every global load of this phase is issued before any store: the
+        // parameter, moment and statistic arrays do not alias, but the compiler
+        // cannot know that and would otherwise serialise each load behind the
+        // previous store.
+        float pm[3], pl[3], mm[3], vm[3], ml[3], vl[3], po = 0.f, mo = 0.f, vo = 0.f;
+        float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f), mq4 = q4, vq4 = q4;
+        const AdamHyper& h = a.adam;
+        if (ADAM) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                pm[k] = a.means[3 * (size_t)i + k]; pl[k] = a.log_scales[3 * (size_t)i + k];
+                mm[k] = h.m[0][3 * (size_t)i + k]; vm[k] = h.v[0][3 * (size_t)i + k];
+                ml[k] = h.m[1][3 * (size_t)i + k]; vl[k] = h.v[1][3 * (size_t)i + k];
+            }
+            q4 = reinterpret_cast<const float4*>(a.quats)[i];
+            mq4 = reinterpret_cast<const float4*>(h.m[2])[i];
+            vq4 = reinterpret_cast<const float4*>(h.v[2])[i];
+            po = a.opac[i]; mo = h.m[3][i]; vo = h.v[3][i];
+        }
+        float acc = 0.f;
+        int32_t nvis = 0;
+        if (a.accum) { acc = a.accum[i]; nvis = a.count[i]; }
         float dmu[3] = {0.f, 0.f, 0.f}, dls[3] = {0.f, 0.f, 0.f}, dq[4] = {0.f, 0.f, 0.f, 0.f}, dop = 0.f;
         float Y[16], drgb[3] = {0.f, 0.f, 0.f};
         const bool vis = a.tt[i] > 0;
@@ -306,8 +326,8 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
             chain<DEG>(a, i, s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb);
             if (a.accum) {
                 const float2 d2 = *reinterpret_cast<const float2*>(a.grad2d + (size_t)i * GS_GRAD2D_STRIDE);
-                a.accum[i] += sqrtf(d2.x * d2.x + d2.y * d2.y);
-                a.count[i] += 1;
+                a.accum[i] = acc + sqrtf(d2.x * d2.x + d2.y * d2.y);
+                a.count[i] = nvis + 1;
             }
         } else {
 #pragma unroll
@@ -325,44 +345,63 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
             a.dopac[i] = dop;
         }
         if (ADAM) {
-            const AdamHyper& h = a.adam;
+            float qv[4] = {q4.x, q4.y, q4.z, q4.w}, mq[4] = {mq4.x, mq4.y, mq4.z, mq4.w};
+            float vq[4] = {vq4.x, vq4.y, vq4.z, vq4.w};
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                float p = a.means[3 * (size_t)i + k];
-                adam1(p, dmu[k], h.m[0], h.v[0], 3 * (size_t)i + k, h.lr[0], h);
-                a.means[3 * (size_t)i + k] = p;
-                float ps = a.log_scales[3 * (size_t)i + k];
-                adam1(ps, dls[k], h.m[1], h.v[1], 3 * (size_t)i + k, h.lr[1], h);
-                a.log_scales[3 * (size_t)i + k] = ps;
+                adam_reg(pm[k], dmu[k], mm[k], vm[k], h.lr[0], h);
+                adam_reg(pl[k], dls[k], ml[k], vl[k], h.lr[1], h);
             }
-            float4 q = reinterpret_cast<float4*>(a.quats)[i];
-            float qv[4] = {q.x, q.y, q.z, q.w};
             float ss = 0.f;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                adam1(qv[k], dq[k], h.m[2], h.v[2], 4 * (size_t)i + k, h.lr[2], h);
+                adam_reg(qv[k], dq[k], mq[k], vq[k], h.lr[2], h);
                 ss += qv[k] * qv[k];
             }
             const float inv = 1.f / sqrtf(ss);  // renormalise after the update
+            adam_reg(po, dop, mo, vo, h.lr[3], h);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                a.means[3 * (size_t)i + k] = pm[k]; a.log_scales[3 * (size_t)i + k] = pl[k];
+                h.m[0][3 * (size_t)i + k] = mm[k]; h.v[0][3 * (size_t)i + k] = vm[k];
+                h.m[1][3 * (size_t)i + k] = ml[k]; h.v[1][3 * (size_t)i + k] = vl[k];
+            }
             reinterpret_cast<float4*>(a.quats)[i] = make_float4(qv[0] * inv, qv[1] * inv, qv[2] * inv, qv[3] * inv);
-            float po = a.opac[i];
-            adam1(po, dop, h.m[3], h.v[3], i, h.lr[3], h);
-            a.opac[i] = po;
+            reinterpret_cast<float4*>(h.m[2])[i] = make_float4(mq[0], mq[1], mq[2], mq[3]);
+            reinterpret_cast<float4*>(h.v[2])[i] = make_float4(vq[0], vq[1], vq[2], vq[3]);
+            a.opac[i] = po; h.m[3][i] = mo; h.v[3][i] = vo;
         }
     }
     __syncthreads();
 
-#pragma unroll 4
-    for (int e = t; e < cnt; e += kThreads) {
-        const int g = e / J, j = e - g * J;
-        const int k = j / 3, ch = j - 3 * k;
-        const float grad = s_y[k * LDG + g] * s_c[ch * LDG + g];
-        if (a.dsh) a.dsh[base + e] = grad;
+    // element-wise SH part, kChunk elements per thread at a time, loads first
+    constexpr int kChunk = 8;
+    for (int e0 = t; e0 < cnt; e0 += kChunk * kThreads) {
+        float mv[kChunk], vv[kChunk];
         if (ADAM) {
-            const AdamHyper& h = a.adam;
-            float p = s_sh[j * LDG + g];
-            adam1(p, grad, h.m[4], h.v[4], base + e, k == 0 ? h.lr[4] : h.lr[5], h);
-            a.sh[base + e] = p;
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) {
+                const int e = e0 + c * kThreads;
+                mv[c] = e < cnt ? a.adam.m[4][base + e] : 0.f;
+                vv[c] = e < cnt ? a.adam.v[4][base + e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int e = e0 + c * kThreads;
+            if (e >= cnt) break;
+            const int g = e / J, j = e - g * J;
+            const int k = j / 3, ch = j - 3 * k;
+            const float grad = s_y[k * LDG + g] * s_c[ch * LDG + g];
+            if (a.dsh) a.dsh[base + e] = grad;
+            if (ADAM) {
+                const AdamHyper& h = a.adam;
+                float p = s_sh[j * LDG + g];
+                adam_reg(p, grad, mv[c], vv[c], k == 0 ? h.lr[4] : h.lr[5], h);
+                a.sh[base + e] = p;
+                h.m[4][base + e] = mv[c];
+                h.v[4][base + e] = vv[c];
+            }
         }
     }
 }

@@ -299,110 +299,144 @@ __device__ __forceinline__ float reduce9(float v[8], float& v8, int lane) {
     return u;
 }
 
-__global__ __launch_bounds__(kBlock) void k_render_bwd(RenderArgs a) {
-    __shared__ float4 s_g0[kBlock];
-    __shared__ float4 s_g1[kBlock];
-    __shared__ float s_g2[kBlock];
-    __shared__ uint8_t s_mask[kBlock];
-    __shared__ uint16_t s_list[4][kBlock];
-    __shared__ uint32_t s_gid[kBlock];
-    __shared__ int s_wmax[4];
-    __shared__ int s_bmax;
+// Backward: one wave64 per tile, each lane owning one pixel of each of the four
+// 8x8 quadrants (pixel q of lane l sits at ((q & 1) 8 + l % 8, (q >> 1) 8 + l / 8)).
+// Entries are walked in reverse list order in batches of 64, only those the
+// forward blended somewhere in the tile; for an entry, only its flagged
+// quadrants run the per-pixel recursion, each adding its partials into the same
+// nine per-lane accumulators, so the cross-lane reduction and the atomic update
+// happen once per entry rather than once per quadrant.
+//
+// The accumulators hold moments: S_t = sum dpow dx, S_s = sum dpow dy,
+// sum dpow dx^2, sum dpow dx dy, sum dpow dy^2 (dpow = dL/dpower), the opacity
+// and colour sums.  After the reduction they become gradients with the entry's
+// conic (A, B, C): dL/dmean2D = (A S_t + B S_s, B S_t + C S_s) since
+// dpower/dmean = conic d, and dL/d(A, B, C) = (-1/2, -1, -1/2) times the second
+// moments.
+constexpr int kBwdBatch = 64;
+
+__global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
+    __shared__ float4 s_g0[kBwdBatch];   // u', v', L00, L10
+    __shared__ float4 s_g1[kBwdBatch];   // L11, opacity, r, g
+    __shared__ float4 s_g2[kBwdBatch];   // b, A, B, C (conic)
+    __shared__ uint32_t s_gid[kBwdBatch];
+    __shared__ uint16_t s_list[kBwdBatch];  // slot | quadrant mask << 8, in walk order
 
     const BlendArgs& b = a.b;
     const int ntiles = b.tiles_x * b.tiles_y;
     const int tile = xcd_tile(blockIdx.x, ntiles);
     if (tile >= ntiles) return;
     const int tx = tile % b.tiles_x, ty = tile / b.tiles_x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lx = (wave & 1) * 8 + (lane & 7), ly = (wave >> 1) * 8 + (lane >> 3);
-    const int px = tx * kTile + lx, py = ty * kTile + ly;
-    const bool inside = px < b.width && py < b.height;
-    const float fx = (float)lx + 0.5f, fy = (float)ly + 0.5f;
+    const int lane = threadIdx.x;
     const float x0 = (float)(tx * kTile), y0 = (float)(ty * kTile);
     const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
-    const Stage st{s_g0, s_g1, s_g2};
+    constexpr float k2ln2 = 1.3862943611198906f;  // conic = 2 ln2 L L^T
 
-    float T = 1.f, g0c = 0.f, g1c = 0.f, g2c = 0.f;
-    int nc = 0;
-    if (inside) {
-        const size_t pix = (size_t)py * b.width + px;
-        const size_t plane = (size_t)b.width * b.height;
-        T = a.final_T[pix];
-        nc = a.n_contrib[pix];
-        g0c = a.dL_dimage[pix];
-        g1c = a.dL_dimage[plane + pix];
-        g2c = a.dL_dimage[2 * plane + pix];
-    }
-    float Cn0 = b.bg[0], Cn1 = b.bg[1], Cn2 = b.bg[2];
-    if (tid < 4) s_wmax[tid] = 0;
-    if (tid == 0) s_bmax = 0;
-    __syncthreads();
-    atomicMax(&s_wmax[wave], nc);
-    atomicMax(&s_bmax, nc);
-    __syncthreads();
-    const int wmax = s_wmax[wave];
-    const uint32_t end = range.x + (uint32_t)s_bmax;
-    constexpr float k2ln2 = 1.3862943611198906f;  // 2 ln 2: conic d = 2 ln2 L e
-
-    for (int32_t hi = (int32_t)end; hi > (int32_t)range.x; hi -= kBlock) {
-        const int32_t k = hi - 1 - tid;  // slot tid holds list position k (descending)
-        uint32_t m = 0;
-        const uint32_t g = k >= (int32_t)range.x ? a.list[k] : 0xffffffffu;
-        if (g < a.n) {
-            // only the quadrants in which the forward blended this entry at some pixel
-            m = a.contrib[k];
-            if (m) {
-                s_gid[tid] = g;
-                stage_data(a, g, x0, y0, st, tid);
-            }
+    float T[4], Cn0[4], Cn1[4], Cn2[4], gp0[4], gp1[4], gp2[4], fxq[4], fyq[4];
+    int nc[4];
+    int ncmax = 0;
+    const size_t plane = (size_t)b.width * b.height;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int lx = (q & 1) * 8 + (lane & 7), ly = (q >> 1) * 8 + (lane >> 3);
+        const int px = tx * kTile + lx, py = ty * kTile + ly;
+        fxq[q] = (float)lx + 0.5f;
+        fyq[q] = (float)ly + 0.5f;
+        T[q] = 1.f; nc[q] = 0; gp0[q] = gp1[q] = gp2[q] = 0.f;
+        Cn0[q] = b.bg[0]; Cn1[q] = b.bg[1]; Cn2[q] = b.bg[2];
+        if (px < b.width && py < b.height) {
+            const size_t pix = (size_t)py * b.width + px;
+            T[q] = a.final_T[pix];
+            nc[q] = a.n_contrib[pix];
+            gp0[q] = a.dL_dimage[pix];
+            gp1[q] = a.dL_dimage[plane + pix];
+            gp2[q] = a.dL_dimage[2 * plane + pix];
         }
-        s_mask[tid] = (uint8_t)m;
-        __syncthreads();
-        const int cnt = wmax > 0 ? compact(s_mask, s_list[wave], wave, lane) : 0;
-        const int top = hi - 1 - (int)range.x;  // list position of slot 0
-        for (int j = 0; j < cnt; ++j) {
-            const int e = s_list[wave][j];
-            const int pos = top - e;
-            const float4 g0 = s_g0[e], g1 = s_g1[e];
-            const float cb = s_g2[e];
-            const Pair p = eval_pair(fx, fy, g0, g1, b.alpha_max);
-            const bool ok = pos < nc && p.alpha >= b.alpha_min;
-            if (__ballot(ok) == 0) continue;
-            // branch-free: lanes that do not blend this entry get zero weights
-            const float ae = ok ? p.alpha : 0.f;
-            const float Tp = T * __builtin_amdgcn_rcpf(1.f - p.alpha);  // transmittance before this entry
-            T = ok ? Tp : T;
-            const float w = ae * T;
-            const float d0 = g1.z - Cn0, d1 = g1.w - Cn1, d2 = cb - Cn2;
-            const float dalpha = T * __builtin_fmaf(g2c, d2, __builtin_fmaf(g1c, d1, g0c * d0));
-            Cn0 = __builtin_fmaf(ae, d0, Cn0);
-            Cn1 = __builtin_fmaf(ae, d1, Cn1);
-            Cn2 = __builtin_fmaf(ae, d2, Cn2);
-            const float dsG = (ok && !(p.sG > b.alpha_max)) ? dalpha : 0.f;  // clamped: no dependence
-            float v[8], v8;
-            v[5] = dsG * p.G;                       // dL/dopacity
-            const float dpow = v[5] * g1.y;         // dL/dpower, G = exp(power)
-            const float h = -0.5f * dpow;
-            const float hx = h * p.dx, hy = h * p.dy;
-            v[2] = hx * p.dx;                       // -dx^2/2 dpower
-            v[3] = (hx + hx) * p.dy;                // -dx dy dpower
-            v[4] = hy * p.dy;                       // -dy^2/2 dpower
-            const float kd = k2ln2 * dpow;          // conic d = 2 ln2 L e
-            const float t1 = kd * p.e1;
-            v[0] = t1 * g0.z;
-            v[1] = __builtin_fmaf(t1, g0.w, (kd * p.e2) * g1.x);
-            v[6] = w * g0c;
-            v[7] = w * g1c;
-            v8 = w * g2c;
-            {
-                const float u = reduce9(v, v8, lane);
-                const bool head = (lane & 7) == 0;
-                if (head || lane == 1) {
-                    const int idx = lane == 1 ? 8 : (lane >> 3);
-                    unsafeAtomicAdd(a.grad2d + (size_t)s_gid[e] * GS_GRAD2D_STRIDE + idx, lane == 1 ? v8 : u);
+        ncmax = max(ncmax, nc[q]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ncmax = max(ncmax, __shfl_xor(ncmax, o, 64));
+
+    // per-lane roles after the reduction: lane 8j writes value j, lane 1 the ninth
+    const int grp = lane >> 3;
+    const bool writer = (lane & 7) == 0 || lane == 1;
+    const int widx = lane == 1 ? 8 : grp;
+    const float scl = grp == 2 ? -0.5f : grp == 3 ? -1.f : grp == 4 ? -0.5f : 1.f;
+
+    const uint32_t end = range.x + (uint32_t)ncmax;
+    for (int32_t hi = (int32_t)end; hi > (int32_t)range.x; hi -= kBwdBatch) {
+        const int32_t k = hi - 1 - lane;  // slot `lane` holds list position k (descending)
+        uint32_t m = 0;
+        if (k >= (int32_t)range.x) {
+            const uint32_t g = a.list[k];
+            if (g < a.n) {
+                m = a.contrib[k];
+                if (m) {
+                    const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
+                    const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
+                    s_g0[lane] = make_float4((r0.x - x0) + r0.z, (r0.y - y0) + r0.w, r1.x, r1.y);
+                    s_g1[lane] = make_float4(r1.z, r1.w, r2.x, r2.y);
+                    const float l00 = r1.x, l10 = r1.y, l11 = r1.z;
+                    s_g2[lane] = make_float4(r2.z, k2ln2 * (l00 * l00), k2ln2 * (l00 * l10),
+                                             k2ln2 * __builtin_fmaf(l10, l10, l11 * l11));
+                    s_gid[lane] = g;
                 }
             }
+        }
+        const uint64_t bal = __ballot(m != 0);
+        if (m) {
+            const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            s_list[at] = (uint16_t)(lane | (m << 8));
+        }
+        const int cnt = __popcll(bal);
+        __syncthreads();
+        const int top = hi - 1 - (int)range.x;  // list position of slot 0
+        for (int j = 0; j < cnt; ++j) {
+            const uint32_t le = __builtin_amdgcn_readfirstlane((uint32_t)s_list[j]);
+            const int e = (int)(le & 63u);
+            const uint32_t mm = le >> 8;
+            const int pos = top - e;
+            const float4 G0 = s_g0[e], G1 = s_g1[e], G2 = s_g2[e];
+            // -0 is the additive identity (x + -0 == x for every x), so the first
+            // quadrant's accumulation folds to a plain product
+            float v[8] = {-0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f};
+            float v8 = -0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (mm & (1u << q)) {
+                    const Pair p = eval_pair(fxq[q], fyq[q], G0, G1, b.alpha_max);
+                    const bool ok = pos < nc[q] && p.alpha >= b.alpha_min;
+                    const float ae = ok ? p.alpha : 0.f;
+                    const float Tp = T[q] * __builtin_amdgcn_rcpf(1.f - p.alpha);  // transmittance before the entry
+                    T[q] = ok ? Tp : T[q];
+                    const float w = ae * T[q];
+                    const float d0 = G1.z - Cn0[q], d1 = G1.w - Cn1[q], d2 = G2.x - Cn2[q];
+                    const float dalpha = T[q] * __builtin_fmaf(gp2[q], d2, __builtin_fmaf(gp1[q], d1, gp0[q] * d0));
+                    Cn0[q] = __builtin_fmaf(ae, d0, Cn0[q]);
+                    Cn1[q] = __builtin_fmaf(ae, d1, Cn1[q]);
+                    Cn2[q] = __builtin_fmaf(ae, d2, Cn2[q]);
+                    const float dsG = (ok && !(p.sG > b.alpha_max)) ? dalpha : 0.f;  // clamped: no dependence
+                    const float gG = dsG * p.G;            // dL/dopacity
+                    const float dpow = gG * G1.y;          // dL/dpower, G = exp(power)
+                    const float t = dpow * p.dx, sy = dpow * p.dy;
+                    v[0] += t;
+                    v[1] += sy;
+                    v[2] = __builtin_fmaf(t, p.dx, v[2]);
+                    v[3] = __builtin_fmaf(t, p.dy, v[3]);
+                    v[4] = __builtin_fmaf(sy, p.dy, v[4]);
+                    v[5] += gG;
+                    v[6] = __builtin_fmaf(w, gp0[q], v[6]);
+                    v[7] = __builtin_fmaf(w, gp1[q], v[7]);
+                    v8 = __builtin_fmaf(w, gp2[q], v8);
+                }
+            }
+            const float u = reduce9(v, v8, lane);
+            // group 0: A S_t + B S_s; group 1: C S_s + B S_t; others: scale * moment
+            const float x = dpp<kRowRor8>(u);
+            const float P = grp == 0 ? G2.y : (grp == 1 ? G2.w : scl);
+            const float Bx = grp < 2 ? G2.z * x : 0.f;
+            const float out = lane == 1 ? v8 : __builtin_fmaf(P, u, Bx);
+            if (writer) unsafeAtomicAdd(a.grad2d + (size_t)s_gid[e] * GS_GRAD2D_STRIDE + widx, out);
         }
         __syncthreads();
     }
@@ -513,7 +547,7 @@ extern "C" int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32
     a.final_T = const_cast<float*>(final_T); a.n_contrib = const_cast<int32_t*>(n_contrib);
     a.contrib = const_cast<uint8_t*>(contrib);
     a.dL_dimage = dL_dimage; a.grad2d = grad2d;
-    hipLaunchKernelGGL(k_render_bwd, dim3(render_grid(cam)), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(k_render_bwd, dim3(render_grid(cam)), dim3(64), 0, s, a);
     return launch_status();
 }
 
