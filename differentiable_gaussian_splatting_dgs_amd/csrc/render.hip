@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
     __shared__ float s_g2[kBlock];
     __shared__ uint8_t s_mask[kBlock];
     __shared__ uint16_t s_list[4][kBlock];
-    __shared__ uint32_t s_flag[kBlock];
+    __shared__ uint32_t s_fb[kBlock];        // per slot: byte w set if a pixel of wave w blended it
 
     const BlendArgs& b = a.b;
     const int ntiles = b.tiles_x * b.tiles_y;
@@ -164,13 +164,13 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
     const float inv_amin = 1.f / b.alpha_min;
     const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
     const Stage st{s_g0, s_g1, s_g2};
-    const uint32_t wbit = 1u << wave;
 
     float T = 1.f, C0 = 0.f, C1 = 0.f, C2 = 0.f;
     int last = 0;
     bool done = !inside;
     bool wave_done = __ballot(!done) == 0;
     uint32_t kprev = 0xffffffffu;  // list position whose blend flags this thread writes out
+    uint8_t* const fb = reinterpret_cast<uint8_t*>(s_fb) + wave;  // this wave's flag byte of slot e: fb[4 e]
     for (uint32_t start = range.x; start < range.y; start += kBlock) {
         const uint32_t k = start + tid;
         uint32_t m = 0;
@@ -179,10 +179,13 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
             if (g < a.n) m = stage_entry(a, g, x0, y0, inv_amin, st, tid);
         }
         // the previous batch's flags are final (the loop ends with a barrier)
-        if (kprev != 0xffffffffu) a.contrib[kprev] = (uint8_t)s_flag[tid];
+        if (kprev != 0xffffffffu) {
+            const uint32_t f = s_fb[tid];
+            a.contrib[kprev] = (uint8_t)((f & 1u) | ((f >> 7) & 2u) | ((f >> 14) & 4u) | ((f >> 21) & 8u));
+        }
         kprev = k < range.y ? k : 0xffffffffu;
         s_mask[tid] = (uint8_t)m;
-        s_flag[tid] = 0u;
+        s_fb[tid] = 0u;
         __syncthreads();
         const int cnt = wave_done ? 0 : compact(s_mask, s_list[wave], wave, lane);
         const int base = (int)(start - range.x);
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
                 C2 = __builtin_fmaf(w, cba, C2);
                 T = ok ? Tn : T;
                 last = ok ? base + ea + 1 : last;
-                if (__ballot(ok) != 0 && lane == 0) atomicOr(&s_flag[ea], wbit);
+                if (ok) fb[4 * ea] = 1;  // lanes that blend all store the same byte
             }
             {
                 bool ok = has2 && !done && pb.alpha >= b.alpha_min;
@@ -221,14 +224,17 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
                 C2 = __builtin_fmaf(w, cbb, C2);
                 T = ok ? Tn : T;
                 last = ok ? base + eb + 1 : last;
-                if (__ballot(ok) != 0 && lane == 0) atomicOr(&s_flag[eb], wbit);
+                if (ok) fb[4 * eb] = 1;
             }
-            if (__ballot(!done) == 0) break;
+            if ((j & 2) && __ballot(!done) == 0) break;  // checked every other pair
         }
         wave_done = __ballot(!done) == 0;
         if (__syncthreads_count(done ? 1 : 0) == kBlock) break;
     }
-    if (kprev != 0xffffffffu) a.contrib[kprev] = (uint8_t)s_flag[tid];
+    if (kprev != 0xffffffffu) {
+        const uint32_t f = s_fb[tid];
+        a.contrib[kprev] = (uint8_t)((f & 1u) | ((f >> 7) & 2u) | ((f >> 14) & 4u) | ((f >> 21) & 8u));
+    }
     if (inside) {
         const size_t pix = (size_t)py * b.width + px;
         const size_t plane = (size_t)b.width * b.height;
