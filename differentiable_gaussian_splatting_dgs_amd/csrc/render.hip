@@ -39,9 +39,23 @@ struct RenderArgs {
     float* final_T;
     int32_t* n_contrib;
     uint8_t* contrib;   // [K] per list entry: bit q set if a pixel of quadrant q blends it
+    const int32_t* sched;  // [tiles] tile of each block (null: image order, XCD-banded)
+    int32_t* work;         // forward: [tiles] backward work estimate per tile (optional)
     const float* dL_dimage;
     float* grad2d;
 };
+
+// The tile a block works on: sched[block] when a schedule is given, else image
+// order banded over the XCDs; -1 for padding blocks or an out-of-range entry.
+__device__ __forceinline__ int block_tile(const int32_t* sched, int ntiles) {
+    if (sched) {
+        if ((int)blockIdx.x >= ntiles) return -1;
+        const int t = sched[blockIdx.x];
+        return (t >= 0 && t < ntiles) ? t : -1;
+    }
+    const int t = xcd_tile(blockIdx.x, ntiles);
+    return t < ntiles ? t : -1;
+}
 
 // The alpha of one (pixel, Gaussian) pair.  Shared verbatim by the forward,
 // the backward and the pair counter so all three take identical decisions.
@@ -152,8 +166,8 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
 
     const BlendArgs& b = a.b;
     const int ntiles = b.tiles_x * b.tiles_y;
-    const int tile = xcd_tile(blockIdx.x, ntiles);
-    if (tile >= ntiles) return;
+    const int tile = block_tile(a.sched, ntiles);
+    if (tile < 0) return;
     const int tx = tile % b.tiles_x, ty = tile / b.tiles_x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lx = (wave & 1) * 8 + (lane & 7), ly = (wave >> 1) * 8 + (lane >> 3);
@@ -170,7 +184,16 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
     bool done = !inside;
     bool wave_done = __ballot(!done) == 0;
     uint32_t kprev = 0xffffffffu;  // list position whose blend flags this thread writes out
+    uint32_t work = 0;             // backward work of the entries this thread flags
     uint8_t* const fb = reinterpret_cast<uint8_t*>(s_fb) + wave;  // this wave's flag byte of slot e: fb[4 e]
+    // Backward cost model of one flagged entry: a fixed part (staging, the wave
+    // reduction and the atomic update) plus a part per flagged quadrant.
+    auto flag_out = [&](uint32_t kk) {
+        const uint32_t f = s_fb[tid];
+        const uint32_t mq = (f & 1u) | ((f >> 7) & 2u) | ((f >> 14) & 4u) | ((f >> 21) & 8u);
+        a.contrib[kk] = (uint8_t)mq;
+        work += mq ? 3u + 2u * (uint32_t)__popc(mq) : 0u;
+    };
     for (uint32_t start = range.x; start < range.y; start += kBlock) {
         const uint32_t k = start + tid;
         uint32_t m = 0;
@@ -179,10 +202,7 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
             if (g < a.n) m = stage_entry(a, g, x0, y0, inv_amin, st, tid);
         }
         // the previous batch's flags are final (the loop ends with a barrier)
-        if (kprev != 0xffffffffu) {
-            const uint32_t f = s_fb[tid];
-            a.contrib[kprev] = (uint8_t)((f & 1u) | ((f >> 7) & 2u) | ((f >> 14) & 4u) | ((f >> 21) & 8u));
-        }
+        if (kprev != 0xffffffffu) flag_out(kprev);
         kprev = k < range.y ? k : 0xffffffffu;
         s_mask[tid] = (uint8_t)m;
         s_fb[tid] = 0u;
@@ -231,9 +251,13 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
         wave_done = __ballot(!done) == 0;
         if (__syncthreads_count(done ? 1 : 0) == kBlock) break;
     }
-    if (kprev != 0xffffffffu) {
-        const uint32_t f = s_fb[tid];
-        a.contrib[kprev] = (uint8_t)((f & 1u) | ((f >> 7) & 2u) | ((f >> 14) & 4u) | ((f >> 21) & 8u));
+    if (kprev != 0xffffffffu) flag_out(kprev);
+    if (a.work) {
+        for (int o = 32; o > 0; o >>= 1) work += __shfl_xor(work, o, 64);
+        __syncthreads();
+        if (lane == 0) s_fb[wave] = work;
+        __syncthreads();
+        if (tid == 0) a.work[tile] = (int32_t)(s_fb[0] + s_fb[1] + s_fb[2] + s_fb[3]);
     }
     if (inside) {
         const size_t pix = (size_t)py * b.width + px;
@@ -330,8 +354,8 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
 
     const BlendArgs& b = a.b;
     const int ntiles = b.tiles_x * b.tiles_y;
-    const int tile = xcd_tile(blockIdx.x, ntiles);
-    if (tile >= ntiles) return;
+    const int tile = block_tile(a.sched, ntiles);
+    if (tile < 0) return;
     const int tx = tile % b.tiles_x, ty = tile / b.tiles_x;
     const int lane = threadIdx.x;
     const float x0 = (float)(tx * kTile), y0 = (float)(ty * kTile);
@@ -448,6 +472,61 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     }
 }
 
+// Tile schedules: a one-block bucket sort of per-tile work estimates into tile
+// ids, heaviest first, so that the longest tiles start first and a kernel does
+// not end on a few late, long tiles.  The work of tile t is the length of its
+// list (ranges given) or work[t]; order may alias work.  Buckets are
+// quarter-octaves of the work; order inside a bucket is arbitrary.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBuckets = 128;
+constexpr int kOrderMaxTiles = 65536;
+
+__device__ __forceinline__ uint32_t work_bucket(uint32_t w) {
+    if (w == 0) return 0;
+    const uint32_t oct = 31u - __clz(w);  // floor(log2 w)
+    const uint32_t sub = oct >= 2 ? (w >> (oct - 2)) & 3u : (w << (2 - oct)) & 3u;
+    return min(1u + 4u * oct + sub, (uint32_t)kOrderBuckets - 1u);
+}
+
+__global__ __launch_bounds__(kOrderThreads) void k_tile_order(const uint32_t* ranges, const int32_t* work,
+                                                              int32_t* order, int ntiles) {
+    __shared__ uint8_t s_b[kOrderMaxTiles];
+    __shared__ uint32_t s_cnt[kOrderBuckets];
+    __shared__ uint32_t s_w1;
+    const int tid = threadIdx.x;
+    if (tid < kOrderBuckets) s_cnt[tid] = 0;
+    __syncthreads();
+    for (int t = tid; t < ntiles; t += kOrderThreads) {
+        const uint32_t w = ranges ? ranges[2 * t + 1] - ranges[2 * t] : (uint32_t)max(work[t], 0);
+        const uint32_t bk = work_bucket(w);
+        s_b[t] = (uint8_t)bk;
+        atomicAdd(&s_cnt[bk], 1u);
+    }
+    __syncthreads();
+    // exclusive offsets, heaviest bucket first: a scan over the reversed buckets by two waves
+    uint32_t x = 0, c = 0;
+    if (tid < kOrderBuckets) {
+        const int lane = tid & 63;
+        c = s_cnt[kOrderBuckets - 1 - tid];
+        x = c;
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (tid == 63) s_w1 = x;
+    }
+    __syncthreads();
+    if (tid < kOrderBuckets) s_cnt[kOrderBuckets - 1 - tid] = x - c + (tid >= 64 ? s_w1 : 0u);
+    __syncthreads();
+    for (int t = tid; t < ntiles; t += kOrderThreads) order[atomicAdd(&s_cnt[s_b[t]], 1u)] = t;
+}
+
+// p[i] = i mod period for i < 2 period.
+__global__ void k_iota(int32_t* p, int period) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < 2 * period) p[i] = i < period ? i : i - period;
+}
+
 __global__ void k_zero_f32(float* p, size_t count) {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -516,7 +595,7 @@ using namespace gs;
 
 extern "C" int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                              const uint32_t* point_list, const float* splats, float* image, float* final_T,
-                             int32_t* n_contrib, uint8_t* contrib, void* stream) {
+                             int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order, void* stream) {
     int rc = render_common_checks(cam, set, tile_ranges, splats);
     if (rc) return rc;
     if (n < 0 || !image || !final_T || !n_contrib) return GS_EINVAL;
@@ -526,14 +605,29 @@ extern "C" int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32
     a.n = (uint32_t)n;
     a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
     a.image = image; a.final_T = final_T; a.n_contrib = n_contrib; a.contrib = contrib;
-    hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam)), dim3(kBlock), 0, as_stream(stream), a);
+    const int ntiles = tiles_x(cam) * tiles_y(cam);
+    hipStream_t s = as_stream(stream);
+    if (tile_order && ntiles <= kOrderMaxTiles) {
+        // row 0: the forward's own schedule (list lengths); row 1: the backward's (flag counts)
+        int32_t* fwd_order = tile_order;
+        int32_t* bwd_order = tile_order + ntiles;
+        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, tile_ranges, nullptr, fwd_order, ntiles);
+        a.sched = fwd_order;
+        a.work = bwd_order;
+        hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam)), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, nullptr, bwd_order, bwd_order, ntiles);
+    } else {
+        hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam)), dim3(kBlock), 0, s, a);
+        if (tile_order)  // too many tiles for the one-block sort: image order
+            hipLaunchKernelGGL(k_iota, dim3((2 * ntiles + 255) / 256), dim3(256), 0, s, tile_order, ntiles);
+    }
     return launch_status();
 }
 
 extern "C" int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                              const uint32_t* point_list, const float* splats, const float* final_T,
-                             const int32_t* n_contrib, const uint8_t* contrib, const float* dL_dimage,
-                             float* grad2d, int32_t accumulate, void* stream) {
+                             const int32_t* n_contrib, const uint8_t* contrib, const int32_t* tile_order,
+                             const float* dL_dimage, float* grad2d, int32_t accumulate, void* stream) {
     int rc = render_common_checks(cam, set, tile_ranges, splats);
     if (rc) return rc;
     if (n < 0 || !final_T || !n_contrib || !dL_dimage) return GS_EINVAL;
@@ -553,6 +647,7 @@ extern "C" int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32
     a.final_T = const_cast<float*>(final_T); a.n_contrib = const_cast<int32_t*>(n_contrib);
     a.contrib = const_cast<uint8_t*>(contrib);
     a.dL_dimage = dL_dimage; a.grad2d = grad2d;
+    a.sched = tile_order;
     hipLaunchKernelGGL(k_render_bwd, dim3(render_grid(cam)), dim3(64), 0, s, a);
     return launch_status();
 }

@@ -75,8 +75,8 @@ def load_library(path=LIB_PATH):
     lib.gs_bin_workspace_size.argtypes = [_i32, P(GsCamera), _i64, P(C.c_size_t)]
     lib.gs_bin_sort.argtypes = [P(GsCamera), _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
     lib.gs_bin_keys.argtypes = [P(GsCamera), _vp, _vp, _vp, _vp, _vp]
-    lib.gs_render_fwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 7 + [_vp]
-    lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_i32, _vp]
+    lib.gs_render_fwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_vp]
+    lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 9 + [_i32, _vp]
     lib.gs_preprocess_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
     lib.gs_preprocess_bwd_adam.argtypes = ([P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 8 +
                                            [P(GsAdamState)] + [_vp] * 7 + [_vp])
@@ -189,22 +189,25 @@ def gs_bin_keys(cam, tile_ranges, point_list, depth, keys):
     _check(rc, "gs_bin_keys")
 
 
-def gs_render_fwd(cam, settings, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib):
+def gs_render_fwd(cam, settings, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
+                  tile_order=None):
     rc = load_library().gs_render_fwd(
         C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
         _p(point_list, torch.int32, "point_list"), _p(splats, torch.float32, "splats"),
         _p(image, torch.float32, "image"), _p(final_T, torch.float32, "final_T"),
-        _p(n_contrib, torch.int32, "n_contrib"), _p(contrib, torch.uint8, "contrib"), _stream())
+        _p(n_contrib, torch.int32, "n_contrib"), _p(contrib, torch.uint8, "contrib"),
+        _p(tile_order, torch.int32, "tile_order"), _stream())
     _check(rc, "gs_render_fwd")
 
 
 def gs_render_bwd(cam, settings, n, tile_ranges, point_list, splats, final_T, n_contrib, contrib, dL_dimage, grad2d,
-                  accumulate=False):
+                  accumulate=False, tile_order=None):
     rc = load_library().gs_render_bwd(
         C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
         _p(point_list, torch.int32, "point_list"), _p(splats, torch.float32, "splats"),
         _p(final_T, torch.float32, "final_T"), _p(n_contrib, torch.int32, "n_contrib"),
-        _p(contrib, torch.uint8, "contrib"), _p(dL_dimage, torch.float32, "dL_dimage"),
+        _p(contrib, torch.uint8, "contrib"), _p(tile_order, torch.int32, "tile_order"),
+        _p(dL_dimage, torch.float32, "dL_dimage"),
         _p(grad2d, torch.float32, "grad2d"), 1 if accumulate else 0, _stream())
     _check(rc, "gs_render_bwd")
 
@@ -318,6 +321,8 @@ class Rasterizer:
         self.tiles_touched = torch.empty(n, dtype=torch.int32, device=dev)
         self.clamp = torch.empty(n, dtype=torch.uint8, device=dev)
         self.tile_ranges = torch.empty((self.ntiles, 2), dtype=torch.int32, device=dev)
+        # row 0: forward schedule, row 1: backward schedule (written by the forward)
+        self.tile_order = torch.empty((2, self.ntiles), dtype=torch.int32, device=dev)
         self.num_keys = torch.zeros(1, dtype=torch.int32, device=dev)
         self.overflow = torch.zeros(1, dtype=torch.int32, device=dev)
         H, W = cam.height, cam.width
@@ -347,7 +352,7 @@ class Rasterizer:
 
     def render(self):
         gs_render_fwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, self.image,
-                      self.final_T, self.n_contrib, self.contrib)
+                      self.final_T, self.n_contrib, self.contrib, self.tile_order)
 
     def forward(self, p, check=True):
         self.preprocess(p)
@@ -362,7 +367,8 @@ class Rasterizer:
 
     def backward_2d(self, dL_dimage, accumulate=False):
         gs_render_bwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats,
-                      self.final_T, self.n_contrib, self.contrib, dL_dimage, self.grad2d, accumulate)
+                      self.final_T, self.n_contrib, self.contrib, dL_dimage, self.grad2d, accumulate,
+                      self.tile_order[1])
         return self.grad2d
 
     def backward(self, p, dL_dimage, out=None):

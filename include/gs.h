@@ -155,10 +155,16 @@ int gs_bin_keys(const gs_camera* cam, const uint32_t* tile_ranges, const uint32_
  * quadrant q blended the entry.  Only entries up to the last one any pixel of
  * the tile blends are written.  gs_render_bwd reads it back ([P3] sections 1
  * and 5: the backward reuses the forward's intermediates).
+ * tile_order [2, tiles] int32, optional (NULL: tiles in image order): schedules,
+ * each a permutation of the tile ids with the heaviest tiles first so that long
+ * tiles start first.  Row 0 is the forward's own (work = list length), row 1
+ * the backward's (work estimated from the flags): pass tile_order + tiles to
+ * gs_render_bwd.
  */
 int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
                   const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
-                  float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib, void* stream);
+                  float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
+                  int32_t* tile_order, void* stream);
 
 /*
  * gs_render_bwd -- reverse per-pixel walk from the stored final
@@ -168,6 +174,8 @@ int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
  * (zero when clamped) and G = exp(power).
  * In: final_T, n_contrib and contrib from gs_render_fwd (only entries whose
  * contrib bit is set for a quadrant are walked by that quadrant's pixels),
+ * tile_order [tiles]: row 1 of gs_render_fwd's tile_order, or NULL (tiles in
+ * image order; any other content must be a permutation of the tile ids),
  * dL_dimage [3,H,W].  Out: grad2d [n,12]; with accumulate = 0 the call clears
  * it first, with accumulate = 1 the gradients are added to what it holds (the
  * caller cleared it, or sums several calls): dL/du, dL/dv, dL/dA, dL/dB, dL/dC (conic [[A,B],[B,C]],
@@ -178,7 +186,8 @@ int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
 int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32_t n,
                   const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
                   const float* final_T, const int32_t* n_contrib, const uint8_t* contrib,
-                  const float* dL_dimage, float* grad2d, int32_t accumulate, void* stream);
+                  const int32_t* tile_order, const float* dL_dimage, float* grad2d, int32_t accumulate,
+                  void* stream);
 
 /*
  * gs_preprocess_bwd -- 2D -> 3D gradients ([P3] section 4: through the view

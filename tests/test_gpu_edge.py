@@ -164,12 +164,44 @@ def test_abi_errors():
     assert lib.gs_bin_workspace_size(n, C.byref(cam), 1 << 31, C.byref(sz)) == -5
     bad = gs.camera_struct(scenes.Camera.identity(32, 32, 30.0))
     bad.width = 0
-    assert lib.gs_render_fwd(C.byref(bad), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None) == -1
+    assert lib.gs_render_fwd(C.byref(bad), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None, None) == -1
     # missing contrib buffer
-    assert lib.gs_render_fwd(C.byref(cam), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, None, None) == -1
+    assert lib.gs_render_fwd(C.byref(cam), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, None, None, None) == -1
     # accumulate must be 0 or 1
-    assert lib.gs_render_bwd(C.byref(cam), C.byref(st), n, *([ptr] * 8), 2, None) == -1
+    assert lib.gs_render_bwd(C.byref(cam), C.byref(st), n, *([ptr] * 9), 2, None) == -1
     assert lib.gs_error_string(-3) == b"workspace too small"
+
+
+def test_tile_order_is_a_permutation_and_optional():
+    """The forward's tile schedule is a permutation of the tiles, heaviest first by its own work
+    estimate, and the backward gives the same gradients with it, without it (image order), and with
+    an arbitrary permutation."""
+    import torch
+    gs = _gs()
+    sc = scenes.random_small(33, n=3000, width=200, height=120, sh_degree=1, scale_mu=-2.2)
+    r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
+    r.forward(to_dev(sc.params()))
+    torch.cuda.synchronize()
+    order = r.tile_order.cpu().numpy()
+    assert order.shape == (2, r.ntiles)
+    for row in order:
+        assert sorted(row.tolist()) == list(range(r.ntiles))
+    # the forward's schedule is by list length, heaviest first (buckets of a quarter octave)
+    lengths = (r.tile_ranges[:, 1] - r.tile_ranges[:, 0]).cpu().numpy()
+    assert lengths[order[0][0]] * 1.25 >= lengths.max()
+    dL = torch.from_numpy(sc.dL_dimage).cuda()
+    g_sched = r.backward_2d(dL).clone()
+    args = (r.cam, r.settings, r.n, r.tile_ranges, r.point_list, r.splats, r.final_T, r.n_contrib, r.contrib)
+    g_plain = torch.empty_like(g_sched)
+    gs.gs_render_bwd(*args, dL, g_plain, tile_order=None)
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(r.ntiles).astype(np.int32)).cuda()
+    g_perm = torch.empty_like(g_sched)
+    gs.gs_render_bwd(*args, dL, g_perm, tile_order=perm)
+    torch.cuda.synchronize()
+    a = g_sched.cpu().numpy()
+    assert np.abs(a).sum() > 0
+    assert rel_l2(g_plain.cpu().numpy(), a) < 1e-6
+    assert rel_l2(g_perm.cpu().numpy(), a) < 1e-6
 
 
 def test_backward_accumulate():
