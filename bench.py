@@ -60,7 +60,7 @@ def sha_of(path):
 def read_traffic(kernel, launches_per_step=1):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None when
     the summary is missing or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_clusters1m_pmc.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_train1m_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
