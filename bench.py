@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tile-fraction", type=float, default=0.5)
+    ap.add_argument("--cpu-tile-fraction", type=float, default=1.0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one device copy of this many MiB first (scales HBM byte counters)")
     return ap.parse_args()
