@@ -63,29 +63,29 @@ __device__ inline void sh_eval(double x, double y, double z, double* Y) {
 
 constexpr int kPreBlock = 256;  // Gaussians (= threads) per block
 
-// The block's SH coefficients are contiguous in HBM: they are copied into LDS
-// with coalesced loads, coefficient-major with row stride kPreBlock + 1 so both
-// the copy and the per-thread reads are free of bank conflicts.
-template <int DEG>
+// One thread per Gaussian.  Each thread loads its own SH coefficients (3 (DEG+1)^2
+// consecutive floats), as 16-byte loads when the row length and the pointer allow
+// (VEC): neighbouring lanes' rows are adjacent, so the lines a wave touches are
+// fetched once and served from the cache for its remaining loads.
+template <int DEG, bool VEC>
 __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     constexpr int K = (DEG + 1) * (DEG + 1);
     constexpr int J = 3 * K;
-    constexpr int LDG = kPreBlock + 1;
-    __shared__ float s_sh[J * LDG];
-    {
-        const int g0 = blockIdx.x * kPreBlock;
-        const int cnt = min(kPreBlock, a.n - g0) * J;
-        const float* src = a.sh + (size_t)g0 * J;
-#pragma unroll 4
-        for (int e = threadIdx.x; e < cnt; e += kPreBlock) {
-            const int g = e / J, j = e - g * J;
-            s_sh[j * LDG + g] = src[e];
-        }
-    }
-    __syncthreads();
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= a.n) return;
-    const int col = threadIdx.x;
+    float shv[J];
+    if constexpr (VEC) {
+        static_assert(J % 4 == 0, "vector SH loads need a row length that is a multiple of 4");
+        const float4* src = reinterpret_cast<const float4*>(a.sh + (size_t)i * J);
+#pragma unroll
+        for (int k = 0; k < J / 4; ++k) {
+            const float4 v = src[k];
+            shv[4 * k] = v.x; shv[4 * k + 1] = v.y; shv[4 * k + 2] = v.z; shv[4 * k + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < J; ++k) shv[k] = a.sh[(size_t)i * J + k];
+    }
 
     float4* sp = reinterpret_cast<float4*>(a.splats + (size_t)i * GS_SPLAT_STRIDE);
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -177,9 +177,9 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     double rgb[3] = {0.5, 0.5, 0.5};
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        rgb[0] += Y[k] * (double)s_sh[(3 * k) * LDG + col];
-        rgb[1] += Y[k] * (double)s_sh[(3 * k + 1) * LDG + col];
-        rgb[2] += Y[k] * (double)s_sh[(3 * k + 2) * LDG + col];
+        rgb[0] += Y[k] * (double)shv[3 * k];
+        rgb[1] += Y[k] * (double)shv[3 * k + 1];
+        rgb[2] += Y[k] * (double)shv[3 * k + 2];
     }
     uint8_t cm = 0;
     for (int ch = 0; ch < 3; ++ch)
@@ -229,10 +229,16 @@ extern "C" int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32
     const dim3 grid((n + kPreBlock - 1) / kPreBlock), block(kPreBlock);
     hipStream_t s = as_stream(stream);
     switch (sh_degree) {
-        case 0: hipLaunchKernelGGL(k_preprocess<0>, grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL(k_preprocess<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(k_preprocess<2>, grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL(k_preprocess<3>, grid, block, 0, s, a); break;
+        case 0: hipLaunchKernelGGL((k_preprocess<0, false>), grid, block, 0, s, a); break;
+        case 1:
+            if (aligned16(sh)) hipLaunchKernelGGL((k_preprocess<1, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_preprocess<1, false>), grid, block, 0, s, a);
+            break;
+        case 2: hipLaunchKernelGGL((k_preprocess<2, false>), grid, block, 0, s, a); break;
+        default:
+            if (aligned16(sh)) hipLaunchKernelGGL((k_preprocess<3, true>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_preprocess<3, false>), grid, block, 0, s, a);
+            break;
     }
     return launch_status();
 }

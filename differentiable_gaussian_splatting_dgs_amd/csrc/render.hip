@@ -362,7 +362,11 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
     constexpr float k2ln2 = 1.3862943611198906f;  // conic = 2 ln2 L L^T
 
-    float T[4], Cn0[4], Cn1[4], Cn2[4], gp0[4], gp1[4], gp2[4], fxq[4], fyq[4];
+    // Per pixel: T, S = dL/dpixel . C_next (the colour accumulated behind the
+    // current entry, starting at the background), dL/dpixel and the centre.
+    // dL/dalpha = T (dL/dpixel . c - S) and S <- S + alpha (dL/dpixel . c - S)
+    // is C_next <- alpha c + (1 - alpha) C_next dotted with dL/dpixel.
+    float T[4], S[4], gp0[4], gp1[4], gp2[4], fxq[4], fyq[4];
     int nc[4];
     int ncmax = 0;
     const size_t plane = (size_t)b.width * b.height;
@@ -373,7 +377,6 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
         fxq[q] = (float)lx + 0.5f;
         fyq[q] = (float)ly + 0.5f;
         T[q] = 1.f; nc[q] = 0; gp0[q] = gp1[q] = gp2[q] = 0.f;
-        Cn0[q] = b.bg[0]; Cn1[q] = b.bg[1]; Cn2[q] = b.bg[2];
         if (px < b.width && py < b.height) {
             const size_t pix = (size_t)py * b.width + px;
             T[q] = a.final_T[pix];
@@ -382,6 +385,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
             gp1[q] = a.dL_dimage[plane + pix];
             gp2[q] = a.dL_dimage[2 * plane + pix];
         }
+        S[q] = __builtin_fmaf(gp2[q], b.bg[2], __builtin_fmaf(gp1[q], b.bg[1], gp0[q] * b.bg[0]));
         ncmax = max(ncmax, nc[q]);
     }
 #pragma unroll
@@ -440,11 +444,10 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
                     const float Tp = T[q] * __builtin_amdgcn_rcpf(1.f - p.alpha);  // transmittance before the entry
                     T[q] = ok ? Tp : T[q];
                     const float w = ae * T[q];
-                    const float d0 = G1.z - Cn0[q], d1 = G1.w - Cn1[q], d2 = G2.x - Cn2[q];
-                    const float dalpha = T[q] * __builtin_fmaf(gp2[q], d2, __builtin_fmaf(gp1[q], d1, gp0[q] * d0));
-                    Cn0[q] = __builtin_fmaf(ae, d0, Cn0[q]);
-                    Cn1[q] = __builtin_fmaf(ae, d1, Cn1[q]);
-                    Cn2[q] = __builtin_fmaf(ae, d2, Cn2[q]);
+                    const float gc = __builtin_fmaf(gp2[q], G2.x, __builtin_fmaf(gp1[q], G1.w, gp0[q] * G1.z));
+                    const float dS = gc - S[q];
+                    const float dalpha = T[q] * dS;
+                    S[q] = __builtin_fmaf(ae, dS, S[q]);
                     const float dsG = (ok && !(p.sG > b.alpha_max)) ? dalpha : 0.f;  // clamped: no dependence
                     const float gG = dsG * p.G;            // dL/dopacity
                     const float dpow = gG * G1.y;          // dL/dpower, G = exp(power)

@@ -204,6 +204,26 @@ def test_tile_order_is_a_permutation_and_optional():
     assert rel_l2(g_perm.cpu().numpy(), a) < 1e-6
 
 
+def test_preprocess_sh_pointer_alignment():
+    """An SH array that is not 16-byte aligned takes the scalar-load path and gives the same
+    projected records bit for bit."""
+    import torch
+    gs = _gs()
+    sc = scenes.random_small(34, n=999, width=64, height=48, sh_degree=3)
+    p = to_dev(sc.params())
+    r = gs.Rasterizer(sc.cam, sc.n, 3)
+    r.preprocess(p)
+    ref = r.splats.clone()
+    buf = torch.empty(p["sh"].numel() + 1, dtype=torch.float32, device="cuda")
+    buf[1:] = p["sh"].reshape(-1)
+    p2 = dict(p)
+    p2["sh"] = buf[1:].view_as(p["sh"])
+    assert p2["sh"].data_ptr() % 16 != 0
+    r.preprocess(p2)
+    torch.cuda.synchronize()
+    assert torch.equal(r.splats, ref)
+
+
 def test_backward_accumulate():
     """accumulate=1 adds the call's gradients to what grad2d holds; accumulate=0 overwrites."""
     import torch
