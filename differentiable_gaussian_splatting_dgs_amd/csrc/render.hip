@@ -77,6 +77,10 @@ __device__ __forceinline__ Pair eval_pair(float fx, float fy, float4 g0, float4 
     return p;
 }
 
+// Transmittance after blending alpha: T (1 - alpha) as one fused operation.  The
+// forward and the pair counter both use it, so they stop at the same entry.
+__device__ __forceinline__ float trans_after(float T, float alpha) { return __builtin_fmaf(-alpha, T, T); }
+
 // Stage list entry k of the tile into LDS slot `slot`; returns the quadrant mask.
 struct Stage {
     float4* g0;
@@ -219,11 +223,11 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
             const Pair pa = eval_pair(fx, fy, ga0, ga1, b.alpha_max);
             const Pair pb = eval_pair(fx, fy, gb0, gb1, b.alpha_max);
             {
-                bool ok = !done && pa.alpha >= b.alpha_min;
-                const float Tn = T * (1.f - pa.alpha);
-                const bool stop = ok && Tn < b.T_min;
-                done = done || stop;
-                ok = ok && !stop;
+                const bool pass = !done && pa.alpha >= b.alpha_min;
+                const float Tn = trans_after(T, pa.alpha);
+                const bool low = Tn < b.T_min;
+                done = done || (pass && low);
+                const bool ok = pass && !low;
                 const float w = ok ? pa.alpha * T : 0.f;
                 C0 = __builtin_fmaf(w, ga1.z, C0);
                 C1 = __builtin_fmaf(w, ga1.w, C1);
@@ -233,11 +237,11 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
                 if (ok) fb[4 * ea] = 1;  // lanes that blend all store the same byte
             }
             {
-                bool ok = has2 && !done && pb.alpha >= b.alpha_min;
-                const float Tn = T * (1.f - pb.alpha);
-                const bool stop = ok && Tn < b.T_min;
-                done = done || stop;
-                ok = ok && !stop;
+                const bool pass = has2 && !done && pb.alpha >= b.alpha_min;
+                const float Tn = trans_after(T, pb.alpha);
+                const bool low = Tn < b.T_min;
+                done = done || (pass && low);
+                const bool ok = pass && !low;
                 const float w = ok ? pb.alpha * T : 0.f;
                 C0 = __builtin_fmaf(w, gb1.z, C0);
                 C1 = __builtin_fmaf(w, gb1.w, C1);
@@ -329,6 +333,46 @@ __device__ __forceinline__ float reduce9(float v[8], float& v8, int lane) {
     return u;
 }
 
+// Sums two entries' nine values over the 64 lanes at once (one transposing
+// tree for 16 of them, a half tree for the two ninth values).  On return lane
+// quad q (lanes 4q..4q+3) holds the total of value q & 7 of entry a (q < 8) or
+// entry b (q >= 8) in the return value, and lanes 0..31 hold the total of a[8],
+// lanes 32..63 that of b[8], in z.
+__device__ __forceinline__ float reduce2x9(float a[9], float b[9], float& z, int lane) {
+    float s[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        xchg32(a[k], b[k]);
+        s[k] = a[k] + b[k];  // lanes 0-31: a_k, lanes 32-63: b_k
+    }
+    float t[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        xchg16(s[k], s[k + 4]);
+        t[k] = s[k] + s[k + 4];  // rows: a_k, a_k+4, b_k, b_k+4
+    }
+    const bool hi8 = (lane & 8) != 0;
+    const float u0 = (hi8 ? t[2] : t[0]) + dpp<kRowRor8>(hi8 ? t[0] : t[2]);  // half-rows: t0 | t2
+    const float u1 = (hi8 ? t[3] : t[1]) + dpp<kRowRor8>(hi8 ? t[1] : t[3]);  // half-rows: t1 | t3
+    const bool hi4 = (lane & 4) != 0;
+    float w = (hi4 ? u1 : u0) + dpp<kRowHalfMirror>(hi4 ? u0 : u1);          // quads: u0 | u1
+    w += dpp<kQuadXor1>(w);
+    w += dpp<kQuadXor2>(w);
+    // ninth values
+    float p = a[8], r = b[8];
+    xchg32(p, r);
+    float y = p + r;  // lanes 0-31: a8, 32-63: b8
+    float y2 = y;
+    xchg16(y, y2);    // y: rows r0 r0 r2 r2, y2: rows r1 r1 r3 r3
+    y += y2;
+    y += dpp<kRowRor8>(y);
+    y += dpp<kRowHalfMirror>(y);
+    y += dpp<kQuadXor1>(y);
+    y += dpp<kQuadXor2>(y);
+    z = y;
+    return w;
+}
+
 // Backward: one wave64 per tile, each lane owning one pixel of each of the four
 // 8x8 quadrants (pixel q of lane l sits at ((q & 1) 8 + l % 8, (q >> 1) 8 + l / 8)).
 // Entries are walked in reverse list order in batches of 64, only those the
@@ -391,11 +435,48 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) ncmax = max(ncmax, __shfl_xor(ncmax, o, 64));
 
-    // per-lane roles after the reduction: lane 8j writes value j, lane 1 the ninth
-    const int grp = lane >> 3;
-    const bool writer = (lane & 7) == 0 || lane == 1;
-    const int widx = lane == 1 ? 8 : grp;
-    const float scl = grp == 2 ? -0.5f : grp == 3 ? -1.f : grp == 4 ? -0.5f : 1.f;
+    // Per-lane roles after a two-entry reduction: quad q (lanes 4q..4q+3) holds
+    // value q & 7 of entry q >> 3; its first lane writes it, and lanes 1 and 33
+    // write the two ninth values.
+    const int vi = (lane >> 2) & 7;
+    const bool entb = lane >= 32;
+    const bool ninth = (lane & 31) == 1;
+    const bool writer = (lane & 3) == 0 || ninth;
+    const int widx = ninth ? 8 : vi;
+    const float scl = vi == 2 ? -0.5f : vi == 3 ? -1.f : vi == 4 ? -0.5f : 1.f;
+
+    // One entry's flagged quadrants, accumulated into v[0..8].
+    auto walk = [&](int e, uint32_t mm, int pos, float v[9]) {
+        const float4 G0 = s_g0[e], G1 = s_g1[e], G2 = s_g2[e];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (mm & (1u << q)) {
+                const Pair p = eval_pair(fxq[q], fyq[q], G0, G1, b.alpha_max);
+                const bool ok = pos < nc[q] && p.alpha >= b.alpha_min;
+                const float ae = ok ? p.alpha : 0.f;
+                const float Tp = T[q] * __builtin_amdgcn_rcpf(1.f - p.alpha);  // transmittance before the entry
+                T[q] = ok ? Tp : T[q];
+                const float w = ae * T[q];
+                const float gc = __builtin_fmaf(gp2[q], G2.x, __builtin_fmaf(gp1[q], G1.w, gp0[q] * G1.z));
+                const float dS = gc - S[q];
+                const float dalpha = T[q] * dS;
+                S[q] = __builtin_fmaf(ae, dS, S[q]);
+                const float dsG = (ok && !(p.sG > b.alpha_max)) ? dalpha : 0.f;  // clamped: no dependence
+                const float gG = dsG * p.G;            // dL/dopacity
+                const float dpow = gG * G1.y;          // dL/dpower, G = exp(power)
+                const float t = dpow * p.dx, sy = dpow * p.dy;
+                v[0] += t;
+                v[1] += sy;
+                v[2] = __builtin_fmaf(t, p.dx, v[2]);
+                v[3] = __builtin_fmaf(t, p.dy, v[3]);
+                v[4] = __builtin_fmaf(sy, p.dy, v[4]);
+                v[5] += gG;
+                v[6] = __builtin_fmaf(w, gp0[q], v[6]);
+                v[7] = __builtin_fmaf(w, gp1[q], v[7]);
+                v[8] = __builtin_fmaf(w, gp2[q], v[8]);
+            }
+        }
+    };
 
     const uint32_t end = range.x + (uint32_t)ncmax;
     for (int32_t hi = (int32_t)end; hi > (int32_t)range.x; hi -= kBwdBatch) {
@@ -425,51 +506,31 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
         const int cnt = __popcll(bal);
         __syncthreads();
         const int top = hi - 1 - (int)range.x;  // list position of slot 0
-        for (int j = 0; j < cnt; ++j) {
-            const uint32_t le = __builtin_amdgcn_readfirstlane((uint32_t)s_list[j]);
-            const int e = (int)(le & 63u);
-            const uint32_t mm = le >> 8;
-            const int pos = top - e;
-            const float4 G0 = s_g0[e], G1 = s_g1[e], G2 = s_g2[e];
+        // entries in pairs: the walk order is kept (a before b), the reduction and
+        // the atomic update are shared
+        for (int j = 0; j < cnt; j += 2) {
+            const bool two = j + 1 < cnt;
+            const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)s_list[j]);
+            const uint32_t lb = two ? __builtin_amdgcn_readfirstlane((uint32_t)s_list[j + 1]) : 0u;
+            const int ea = (int)(la & 63u), eb = (int)(lb & 63u);
             // -0 is the additive identity (x + -0 == x for every x), so the first
             // quadrant's accumulation folds to a plain product
-            float v[8] = {-0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f, -0.f};
-            float v8 = -0.f;
+            float va[9], vb[9];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (mm & (1u << q)) {
-                    const Pair p = eval_pair(fxq[q], fyq[q], G0, G1, b.alpha_max);
-                    const bool ok = pos < nc[q] && p.alpha >= b.alpha_min;
-                    const float ae = ok ? p.alpha : 0.f;
-                    const float Tp = T[q] * __builtin_amdgcn_rcpf(1.f - p.alpha);  // transmittance before the entry
-                    T[q] = ok ? Tp : T[q];
-                    const float w = ae * T[q];
-                    const float gc = __builtin_fmaf(gp2[q], G2.x, __builtin_fmaf(gp1[q], G1.w, gp0[q] * G1.z));
-                    const float dS = gc - S[q];
-                    const float dalpha = T[q] * dS;
-                    S[q] = __builtin_fmaf(ae, dS, S[q]);
-                    const float dsG = (ok && !(p.sG > b.alpha_max)) ? dalpha : 0.f;  // clamped: no dependence
-                    const float gG = dsG * p.G;            // dL/dopacity
-                    const float dpow = gG * G1.y;          // dL/dpower, G = exp(power)
-                    const float t = dpow * p.dx, sy = dpow * p.dy;
-                    v[0] += t;
-                    v[1] += sy;
-                    v[2] = __builtin_fmaf(t, p.dx, v[2]);
-                    v[3] = __builtin_fmaf(t, p.dy, v[3]);
-                    v[4] = __builtin_fmaf(sy, p.dy, v[4]);
-                    v[5] += gG;
-                    v[6] = __builtin_fmaf(w, gp0[q], v[6]);
-                    v[7] = __builtin_fmaf(w, gp1[q], v[7]);
-                    v8 = __builtin_fmaf(w, gp2[q], v8);
-                }
-            }
-            const float u = reduce9(v, v8, lane);
-            // group 0: A S_t + B S_s; group 1: C S_s + B S_t; others: scale * moment
-            const float x = dpp<kRowRor8>(u);
-            const float P = grp == 0 ? G2.y : (grp == 1 ? G2.w : scl);
-            const float Bx = grp < 2 ? G2.z * x : 0.f;
-            const float out = lane == 1 ? v8 : __builtin_fmaf(P, u, Bx);
-            if (writer) unsafeAtomicAdd(a.grad2d + (size_t)s_gid[e] * GS_GRAD2D_STRIDE + widx, out);
+            for (int i = 0; i < 9; ++i) { va[i] = -0.f; vb[i] = -0.f; }
+            walk(ea, la >> 8, top - ea, va);
+            walk(eb, lb >> 8, top - eb, vb);  // no quadrant when there is no second entry
+            float z;
+            const float wv = reduce2x9(va, vb, z, lane);
+            // quads 0 / 8: A S_t + B S_s; quads 1 / 9: C S_s + B S_t; others: scale * moment
+            const int e = entb ? eb : ea;
+            const float4 G2 = s_g2[e];
+            const float x = dpp<kRowHalfMirror>(wv);  // the other first moment of the same entry
+            const float P = vi == 0 ? G2.y : (vi == 1 ? G2.w : scl);
+            const float Bx = vi < 2 ? G2.z * x : 0.f;
+            const float out = ninth ? z : __builtin_fmaf(P, wv, Bx);
+            if (writer && (two || !entb))
+                unsafeAtomicAdd(a.grad2d + (size_t)s_gid[e] * GS_GRAD2D_STRIDE + widx, out);
         }
         __syncthreads();
     }
@@ -561,7 +622,7 @@ __global__ __launch_bounds__(256) void k_count_pairs(RenderArgs a, unsigned long
             const Pair p = eval_pair(fx, fy, g0, g1, b.alpha_max);
             ++ev;
             if (p.alpha < b.alpha_min) continue;
-            const float Tn = T * (1.f - p.alpha);
+            const float Tn = trans_after(T, p.alpha);
             if (Tn < b.T_min) break;
             T = Tn;
             ++nb;
