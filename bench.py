@@ -1,16 +1,17 @@
 """Benchmark of the differentiable tile rasterizer on one MI355X.
 
 One step = the whole hot path on the 1M-Gaussian 1920x1080 cluster-mixture
-scene: preprocess, binning + depth sort, forward compositing, L1 loss against a
-random target, reverse-walk backward, 2D->3D backward, densification statistic
-and the Adam update of all parameter groups (with quaternion renormalisation).
-Inputs are resident in HBM before timing starts.
+scene: preprocess, binning + depth sort, forward compositing with the L1 loss
+against a random target fused in, reverse-walk backward, 2D->3D backward,
+densification statistic and the Adam update of all parameter groups (with
+quaternion renormalisation).  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is Gaussian-pixel blend pairs per second over the
 whole step: (evaluated forward pairs + walked backward pairs) / step time.
-`fwd_bwd` reports the rasterizer alone on the same scene and state: preprocess,
-binning, forward, backward blend and the unfused 2D->3D backward that writes
-the 3D gradients (no loss, no optimizer).
+`fwd_bwd` reports the rasterizer on the same scene and state: preprocess,
+binning, forward (with the per-pixel loss gradient the backward starts from),
+backward blend and the unfused 2D->3D backward that writes the 3D gradients
+(no optimizer).
 """
 from __future__ import annotations
 
@@ -84,7 +85,7 @@ class Step:
         self.target = torch.from_numpy(sc.target).to(dev)
         self.rast = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
         self.dL = torch.empty_like(self.target)
-        self.loss = torch.zeros(1 + gs.LOSS_PARTIALS, dtype=torch.float64, device=dev)
+        self.loss = torch.zeros(1 + self.rast.ntiles, dtype=torch.float64, device=dev)
         self.m = {k: torch.zeros_like(v) for k, v in self.p.items()}
         self.v = {k: torch.zeros_like(v) for k, v in self.p.items()}
         self.accum = torch.zeros(sc.n, dtype=torch.float32, device=dev)
@@ -92,8 +93,7 @@ class Step:
         lr = scenes.ADAM_LR
         self.lr = dict(lr)
         self.step_no = 0
-        self.stages = ["preprocess", "bin_sort", "render_fwd", "loss", "zero_grad2d", "render_bwd",
-                       "grad3d_densify_adam"]
+        self.stages = ["preprocess", "bin_sort", "render_fwd_loss", "render_bwd", "grad3d_densify_adam"]
         self.g3 = {k: torch.empty_like(v) for k, v in self.p.items()}
 
     def run(self, events=None, check=False):
@@ -113,17 +113,14 @@ class Step:
             r._alloc_lists(int(K * 1.25) + 1024)
             r.bin()
         mark(2)
-        r.render()
+        # forward blend with the L1 loss fused in; it also clears the 2D-gradient buffer
+        r.render_loss(self.target, "l1", self.dL, self.loss, clear_grad2d=True)
         mark(3)
-        gs.gs_image_loss("l1", r.image, self.target, self.dL, self.loss)
-        mark(4)
-        r.grad2d.zero_()
-        mark(5)
         r.backward_2d(self.dL, accumulate=True)
-        mark(6)
+        mark(4)
         gs.gs_preprocess_bwd_adam(r.cam, r.settings, r.deg, p, r.tiles_touched, r.clamp, r.grad2d, self.m, self.v,
                                   self.lr, self.step_no, densify_accum=self.accum, densify_count=self.count)
-        mark(7)
+        mark(5)
 
     def preprocess_bwd(self):
         """The unfused 2D->3D backward with its gradients written out (the rasterizer's own backward)."""
@@ -238,12 +235,13 @@ def main():
     p_fwd, p_bwd, p_blend = counts
     pairs = p_fwd + p_bwd
     value = pairs / (ms * 1e-3)
-    # the rasterizer alone, forward + backward down to the 3D gradients (no loss, no optimizer)
-    raster_ms = sum(stage_ms[k] for k in ("preprocess", "bin_sort", "render_fwd", "zero_grad2d", "render_bwd"))
+    # the rasterizer, forward + backward down to the 3D gradients (no optimizer; the forward carries the fused
+    # per-pixel loss gradient, which the backward needs as its input)
+    raster_ms = sum(stage_ms[k] for k in ("preprocess", "bin_sort", "render_fwd_loss", "render_bwd"))
     raster_ms += pbwd_ms
 
     # roofline of the dominant kernel (render_bwd: FP32 VALU bound)
-    dom = max(("render_fwd", "render_bwd"), key=lambda k: stage_ms[k])
+    dom = max(("render_fwd_loss", "render_bwd"), key=lambda k: stage_ms[k])
     if dom == "render_bwd":
         flops = FLOPS_EVAL * p_bwd + FLOPS_BWD_BLEND * p_blend
     else:
@@ -262,7 +260,7 @@ def main():
                            gaussians=sc.n, width=sc.cam.width, height=sc.cam.height, sh_degree=sc.sh_degree,
                            tile=16, parallelism="single-gpu"),
                fwd_bwd=dict(ms=round(raster_ms, 4), pairs_per_s=float(pairs / (raster_ms * 1e-3)),
-                            stages="preprocess + bin_sort + render_fwd + zero_grad2d + render_bwd + preprocess_bwd",
+                            stages="preprocess + bin_sort + render_fwd_loss + render_bwd + preprocess_bwd",
                             preprocess_bwd_ms=round(pbwd_ms, 4)),
                stage_ms={k: round(v, 4) for k, v in stage_ms.items()},
                pairs=dict(fwd_evaluated=float(p_fwd), bwd_walked=float(p_bwd), blended=float(p_blend),

@@ -43,6 +43,13 @@ struct RenderArgs {
     int32_t* work;         // forward: [tiles] backward work estimate per tile (optional)
     const float* dL_dimage;
     float* grad2d;
+    // forward with a fused image loss (mode 0: none, 1: L1, 2: L2)
+    int32_t loss_mode;
+    const float* target;  // [3,H,W]
+    float* dL_out;        // [3,H,W] dL/dimage
+    double* loss_part;    // [tiles] loss of each tile's pixels
+    float4* clear;        // [clear4] float4s set to zero by the forward's blocks (optional)
+    size_t clear4;
 };
 
 // The tile a block works on: sched[block] when a schedule is given, else image
@@ -168,6 +175,11 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
     __shared__ uint16_t s_list[4][kBlock];
     __shared__ uint32_t s_fb[kBlock];        // per slot: byte w set if a pixel of wave w blended it
 
+    if (a.clear) {  // every block of the grid, before any may leave: the stores overlap the blending
+        const size_t stride = (size_t)gridDim.x * blockDim.x;
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.clear4; i += stride)
+            a.clear[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     const BlendArgs& b = a.b;
     const int ntiles = b.tiles_x * b.tiles_y;
     const int tile = block_tile(a.sched, ntiles);
@@ -263,14 +275,35 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
         __syncthreads();
         if (tid == 0) a.work[tile] = (int32_t)(s_fb[0] + s_fb[1] + s_fb[2] + s_fb[3]);
     }
+    double lsum = 0.0;
     if (inside) {
         const size_t pix = (size_t)py * b.width + px;
         const size_t plane = (size_t)b.width * b.height;
-        a.image[pix] = C0 + T * b.bg[0];
-        a.image[plane + pix] = C1 + T * b.bg[1];
-        a.image[2 * plane + pix] = C2 + T * b.bg[2];
+        const float out[3] = {C0 + T * b.bg[0], C1 + T * b.bg[1], C2 + T * b.bg[2]};
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) a.image[ch * plane + pix] = out[ch];
         a.final_T[pix] = T;
         a.n_contrib[pix] = last;
+        if (a.loss_mode) {
+#pragma unroll
+            for (int ch = 0; ch < 3; ++ch) {
+                const float r = out[ch] - a.target[ch * plane + pix];
+                if (a.loss_mode == 1) {
+                    lsum += (double)fabsf(r);
+                    a.dL_out[ch * plane + pix] = r > 0.f ? 1.f : (r < 0.f ? -1.f : 0.f);
+                } else {
+                    lsum += (double)r * (double)r;
+                    a.dL_out[ch * plane + pix] = 2.f * r;
+                }
+            }
+        }
+    }
+    if (a.loss_mode) {  // the tile's loss, summed in a fixed order
+        __shared__ double s_loss[4];
+        for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o, 64);
+        if (lane == 0) s_loss[wave] = lsum;
+        __syncthreads();
+        if (tid == 0) a.loss_part[tile] = (s_loss[0] + s_loss[1]) + (s_loss[2] + s_loss[3]);
     }
 }
 
@@ -552,12 +585,34 @@ __device__ __forceinline__ uint32_t work_bucket(uint32_t w) {
     return min(1u + 4u * oct + sub, (uint32_t)kOrderBuckets - 1u);
 }
 
+// Sum of part[0..n) in a fixed order by one block (1024 threads) into *out.
+__device__ void block_sum_f64(const double* part, int n, double* out) {
+    __shared__ double s_w[kOrderThreads / 64];
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) acc += part[i];
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double t = 0.0;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += s_w[w];
+        *out = t;
+    }
+}
+
+// One block: the total of per-tile loss partials (when the forward has no schedule to sort).
+__global__ __launch_bounds__(kOrderThreads) void k_sum_tiles(const double* part, int n, double* out) {
+    block_sum_f64(part, n, out);
+}
+
 __global__ __launch_bounds__(kOrderThreads) void k_tile_order(const uint32_t* ranges, const int32_t* work,
-                                                              int32_t* order, int ntiles) {
+                                                              int32_t* order, int ntiles, const double* loss_part,
+                                                              double* loss_out) {
     __shared__ uint8_t s_b[kOrderMaxTiles];
     __shared__ uint32_t s_cnt[kOrderBuckets];
     __shared__ uint32_t s_w1;
     const int tid = threadIdx.x;
+    if (loss_part) block_sum_f64(loss_part, ntiles, loss_out);  // the one-block pass also totals the loss
     if (tid < kOrderBuckets) s_cnt[tid] = 0;
     __syncthreads();
     for (int t = tid; t < ntiles; t += kOrderThreads) {
@@ -657,35 +712,80 @@ inline int render_grid(const gs_camera* cam) {
 
 using namespace gs;
 
-extern "C" int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
-                             const uint32_t* point_list, const float* splats, float* image, float* final_T,
-                             int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order, void* stream) {
-    int rc = render_common_checks(cam, set, tile_ranges, splats);
-    if (rc) return rc;
-    if (n < 0 || !image || !final_T || !n_contrib) return GS_EINVAL;
-    if (n > 0 && (!point_list || !splats || !contrib)) return GS_EINVAL;
-    RenderArgs a{};
-    a.b = blend_args(cam, set);
-    a.n = (uint32_t)n;
-    a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
-    a.image = image; a.final_T = final_T; a.n_contrib = n_contrib; a.contrib = contrib;
+namespace gs {
+namespace {
+
+// Forward blend, its tile schedules and, when a.loss_mode != 0, the fused loss.
+int render_fwd_impl(const gs_camera* cam, RenderArgs& a, int32_t* tile_order, double* loss_dev, hipStream_t s) {
     const int ntiles = tiles_x(cam) * tiles_y(cam);
-    hipStream_t s = as_stream(stream);
     if (tile_order && ntiles <= kOrderMaxTiles) {
         // row 0: the forward's own schedule (list lengths); row 1: the backward's (flag counts)
         int32_t* fwd_order = tile_order;
         int32_t* bwd_order = tile_order + ntiles;
-        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, tile_ranges, nullptr, fwd_order, ntiles);
+        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, a.ranges, nullptr, fwd_order, ntiles,
+                           nullptr, nullptr);
         a.sched = fwd_order;
         a.work = bwd_order;
         hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam)), dim3(kBlock), 0, s, a);
-        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, nullptr, bwd_order, bwd_order, ntiles);
+        hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, nullptr, bwd_order, bwd_order, ntiles,
+                           a.loss_part, loss_dev);
     } else {
         hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam)), dim3(kBlock), 0, s, a);
         if (tile_order)  // too many tiles for the one-block sort: image order
             hipLaunchKernelGGL(k_iota, dim3((2 * ntiles + 255) / 256), dim3(256), 0, s, tile_order, ntiles);
+        if (a.loss_mode)
+            hipLaunchKernelGGL(k_sum_tiles, dim3(1), dim3(kOrderThreads), 0, s, a.loss_part, ntiles, loss_dev);
     }
     return launch_status();
+}
+
+int fwd_args(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
+             const uint32_t* point_list, const float* splats, float* image, float* final_T, int32_t* n_contrib,
+             uint8_t* contrib, RenderArgs& a) {
+    int rc = render_common_checks(cam, set, tile_ranges, splats);
+    if (rc) return rc;
+    if (n < 0 || !image || !final_T || !n_contrib) return GS_EINVAL;
+    if (n > 0 && (!point_list || !splats || !contrib)) return GS_EINVAL;
+    a = RenderArgs{};
+    a.b = blend_args(cam, set);
+    a.n = (uint32_t)n;
+    a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
+    a.image = image; a.final_T = final_T; a.n_contrib = n_contrib; a.contrib = contrib;
+    return GS_OK;
+}
+
+}  // namespace
+}  // namespace gs
+
+extern "C" int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
+                             const uint32_t* point_list, const float* splats, float* image, float* final_T,
+                             int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order, void* stream) {
+    RenderArgs a;
+    const int rc = fwd_args(cam, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib, a);
+    if (rc) return rc;
+    return render_fwd_impl(cam, a, tile_order, nullptr, as_stream(stream));
+}
+
+extern "C" int gs_render_fwd_loss(const gs_camera* cam, const gs_settings* set, int32_t n,
+                                  const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                                  float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
+                                  int32_t* tile_order, int32_t loss_mode, const float* target, float* dL_dimage,
+                                  double* loss_dev, float* grad2d_clear, void* stream) {
+    RenderArgs a;
+    const int rc = fwd_args(cam, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib, a);
+    if (rc) return rc;
+    if (loss_mode != 1 && loss_mode != 2) return GS_EINVAL;
+    if (!target || !dL_dimage || !loss_dev) return GS_EINVAL;
+    if (grad2d_clear && !aligned16(grad2d_clear)) return GS_EALIGN;
+    a.loss_mode = loss_mode;
+    a.target = target;
+    a.dL_out = dL_dimage;
+    a.loss_part = loss_dev + 1;
+    if (grad2d_clear && n > 0) {
+        a.clear = reinterpret_cast<float4*>(grad2d_clear);
+        a.clear4 = (size_t)n * GS_GRAD2D_STRIDE / 4;
+    }
+    return render_fwd_impl(cam, a, tile_order, loss_dev, as_stream(stream));
 }
 
 extern "C" int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,

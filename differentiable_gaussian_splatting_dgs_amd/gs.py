@@ -48,7 +48,7 @@ class GsAdamState(C.Structure):
 
 
 SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_bin_workspace_size",
-           "gs_bin_sort", "gs_bin_keys", "gs_render_fwd", "gs_render_bwd", "gs_preprocess_bwd",
+           "gs_bin_sort", "gs_bin_keys", "gs_render_fwd", "gs_render_fwd_loss", "gs_render_bwd", "gs_preprocess_bwd",
            "gs_preprocess_bwd_adam", "gs_image_loss", "gs_densify_accum", "gs_adam_step", "gs_count_pairs"]
 PARAM_ORDER = ("means", "log_scales", "quats", "opacity_logits", "sh")
 
@@ -76,6 +76,7 @@ def load_library(path=LIB_PATH):
     lib.gs_bin_sort.argtypes = [P(GsCamera), _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
     lib.gs_bin_keys.argtypes = [P(GsCamera), _vp, _vp, _vp, _vp, _vp]
     lib.gs_render_fwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_vp]
+    lib.gs_render_fwd_loss.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_i32] + [_vp] * 4 + [_vp]
     lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 9 + [_i32, _vp]
     lib.gs_preprocess_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
     lib.gs_preprocess_bwd_adam.argtypes = ([P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 8 +
@@ -198,6 +199,24 @@ def gs_render_fwd(cam, settings, n, tile_ranges, point_list, splats, image, fina
         _p(n_contrib, torch.int32, "n_contrib"), _p(contrib, torch.uint8, "contrib"),
         _p(tile_order, torch.int32, "tile_order"), _stream())
     _check(rc, "gs_render_fwd")
+
+
+def gs_render_fwd_loss(cam, settings, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
+                       tile_order, mode, target, dL_dimage, loss_dev, grad2d_clear=None):
+    """gs_render_fwd with the L1/L2 image loss fused in (loss_dev [1 + tiles] float64; loss_dev[0] = loss)."""
+    mode_id = {"l1": 1, "l2": 2}[mode]
+    tx, ty = gs_tile_grid(cam)
+    if loss_dev.numel() < 1 + tx * ty:
+        raise GsError(f"loss buffer needs {1 + tx * ty} float64 entries (1 + tiles)")
+    rc = load_library().gs_render_fwd_loss(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
+        _p(point_list, torch.int32, "point_list"), _p(splats, torch.float32, "splats"),
+        _p(image, torch.float32, "image"), _p(final_T, torch.float32, "final_T"),
+        _p(n_contrib, torch.int32, "n_contrib"), _p(contrib, torch.uint8, "contrib"),
+        _p(tile_order, torch.int32, "tile_order"), mode_id, _p(target, torch.float32, "target"),
+        _p(dL_dimage, torch.float32, "dL_dimage"), _p(loss_dev, torch.float64, "loss_dev"),
+        _p(grad2d_clear, torch.float32, "grad2d_clear"), _stream())
+    _check(rc, "gs_render_fwd_loss")
 
 
 def gs_render_bwd(cam, settings, n, tile_ranges, point_list, splats, final_T, n_contrib, contrib, dL_dimage, grad2d,
@@ -353,6 +372,13 @@ class Rasterizer:
     def render(self):
         gs_render_fwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, self.image,
                       self.final_T, self.n_contrib, self.contrib, self.tile_order)
+
+    def render_loss(self, target, mode, dL_dimage, loss_dev, clear_grad2d=True):
+        """Forward blend with the fused image loss; with clear_grad2d the 2D-gradient buffer is zeroed too,
+        for backward_2d(..., accumulate=True).  loss_dev: [1 + ntiles] float64."""
+        gs_render_fwd_loss(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats,
+                           self.image, self.final_T, self.n_contrib, self.contrib, self.tile_order, mode, target,
+                           dL_dimage, loss_dev, self.grad2d if clear_grad2d else None)
 
     def forward(self, p, check=True):
         self.preprocess(p)

@@ -167,6 +167,23 @@ int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
                   int32_t* tile_order, void* stream);
 
 /*
+ * gs_render_fwd_loss -- gs_render_fwd with the image loss of gs_image_loss
+ * fused into the blend ([P4] E.1: render, then the reconstruction loss): each
+ * pixel's dL/dimage is written as soon as its colour is known.  loss_mode 1:
+ * L1 (dL/dimage = sign(image - target), sign(0) = 0); 2: L2 (2 (image -
+ * target)).  target, dL_dimage [3,H,W] float32.  loss_dev [1 + tiles] float64:
+ * loss_dev[0] receives the loss (tile sums added in a fixed order:
+ * deterministic), loss_dev[1 + t] the sum over tile t.  grad2d_clear [n,12]
+ * float32, optional: set to zero by the same kernel, for a gs_render_bwd call
+ * with accumulate = 1.  Other arguments and outputs as gs_render_fwd.
+ */
+int gs_render_fwd_loss(const gs_camera* cam, const gs_settings* set, int32_t n,
+                       const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                       float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
+                       int32_t* tile_order, int32_t loss_mode, const float* target, float* dL_dimage,
+                       double* loss_dev, float* grad2d_clear, void* stream);
+
+/*
  * gs_render_bwd -- reverse per-pixel walk from the stored final
  * transmittance ([P3] section 3), gradients per [P3] section 2:
  *   dL/dc = T alpha dL/dpix;  dL/dalpha = T sum_ch dL/dpix_ch (c_ch - C_next,ch)

@@ -224,6 +224,37 @@ def test_preprocess_sh_pointer_alignment():
     assert torch.equal(r.splats, ref)
 
 
+@pytest.mark.parametrize("mode", ["l1", "l2"])
+def test_fused_forward_loss_matches_separate_calls(mode):
+    """gs_render_fwd_loss == gs_render_fwd + gs_image_loss: the same image bit for bit, the same
+    dL/dimage, the same loss up to summation order, and the 2D-gradient buffer cleared."""
+    import torch
+    gs = _gs()
+    sc = scenes.random_small(35, n=2000, width=150, height=100, sh_degree=2, scale_mu=-2.4)
+    p = to_dev(sc.params())
+    r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
+    r.forward(p)
+    target = torch.from_numpy(np.random.default_rng(3).uniform(0, 1, (3, 100, 150)).astype(np.float32)).cuda()
+    # some pixels equal to the image: sign(0) = 0 in L1
+    target[:, :5, :5] = r.image[:, :5, :5]
+    img_a = r.image.clone()
+    dl_a = torch.empty_like(target)
+    loss_a = torch.zeros(1 + gs.LOSS_PARTIALS, dtype=torch.float64, device="cuda")
+    gs.gs_image_loss(mode, r.image, target, dl_a, loss_a)
+    r.grad2d.fill_(7.0)
+    dl_b = torch.empty_like(target)
+    loss_b = torch.zeros(1 + r.ntiles, dtype=torch.float64, device="cuda")
+    r.render_loss(target, mode, dl_b, loss_b, clear_grad2d=True)
+    torch.cuda.synchronize()
+    assert torch.equal(r.image, img_a)
+    assert torch.equal(dl_b, dl_a)
+    la, lb = float(loss_a[0]), float(loss_b[0])
+    assert abs(la - lb) <= 1e-12 * abs(la), (la, lb)
+    assert float(r.grad2d.abs().max()) == 0.0
+    if mode == "l1":
+        assert float(dl_b[:, :5, :5].abs().max()) == 0.0
+
+
 def test_backward_accumulate():
     """accumulate=1 adds the call's gradients to what grad2d holds; accumulate=0 overwrites."""
     import torch
