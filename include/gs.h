@@ -272,8 +272,9 @@ int gs_adam_step(int32_t n_groups, const gs_adam_group* groups, float beta1, flo
 
 /* Adam state and hyper-parameters of the fused training-step tail.  Moment
    buffers have the shapes of the parameters they follow, in the order means,
-   log_scales, quats, opacity_logits, sh.  lr: means, log_scales, quats,
-   opacity_logits, SH band 0 (the DC coefficients), SH bands >= 1. */
+   log_scales, quats, opacity_logits, sh; the quats moments are 16-byte
+   aligned like quats.  lr: means, log_scales, quats, opacity_logits, SH band 0
+   (the DC coefficients), SH bands >= 1. */
 typedef struct gs_adam_state {
     float* exp_avg[5];
     float* exp_avg_sq[5];
