@@ -8,6 +8,10 @@ quaternion renormalisation).  Inputs are resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is Gaussian-pixel blend pairs per second over the
 whole step: (evaluated forward pairs + walked backward pairs) / step time.
+The step runs on one stream by default; --overlap color|sh moves the SH work to a
+second stream (see Step).  On MI355X both overlaps are slower than one stream:
+the SH passes are HBM-bound and slow the latency-bound projection and binning
+they run beside more than they hide.
 `fwd_bwd` reports the rasterizer on the same scene and state: preprocess,
 binning, forward (with the per-pixel loss gradient the backward starts from),
 backward blend and the unfused 2D->3D backward that writes the 3D gradients
@@ -48,6 +52,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap", choices=("none", "color", "sh"), default="none",
+                    help="work moved to a second stream: none, the SH colour pass (color), or the colour pass and "
+                         "the SH half of the Adam tail (sh)")
     ap.add_argument("--cpu-tile-fraction", type=float, default=1.0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one device copy of this many MiB first (scales HBM byte counters)")
@@ -74,9 +81,25 @@ def read_traffic(kernel, launches_per_step=1):
 
 
 class Step:
-    """All buffers of the training step; run() enqueues one step on the current stream."""
+    """All buffers of the training step.  run() enqueues one step.
 
-    def __init__(self, sc):
+    Without overlap (the default) a step is the single-stream sequence
+    preprocess, bin, fwd+loss, bwd, fused tail.
+
+    overlap="sh" runs the SH work on a second stream: the SH coefficients are
+    needed again only by the next step's colour pass, not by its projection and
+    binning, so step i's SH update and step i+1's colour pass run while step
+    i+1 bins its tiles.  Events keep every read after the write it depends on,
+    so each step computes what the single-stream order computes:
+
+      main:  project(i) -> bin(i) -> [wait colour(i)] -> fwd+loss(i) -> bwd(i) -> geometry tail(i)
+      side:  [wait geometry tail(i-1)] -> SH tail(i-1) -> colour(i)
+
+    overlap="color" keeps the fused tail on the main stream and moves only the
+    colour pass.  finish() enqueues the last SH tail and joins the streams.
+    """
+
+    def __init__(self, sc, overlap="none"):
         import torch
         from differentiable_gaussian_splatting_dgs_amd import gs, scenes
         self.gs, self.torch, self.sc = gs, torch, sc
@@ -93,19 +116,55 @@ class Step:
         lr = scenes.ADAM_LR
         self.lr = dict(lr)
         self.step_no = 0
-        self.stages = ["preprocess", "bin_sort", "render_fwd_loss", "render_bwd", "grad3d_densify_adam"]
+        # overlap: "none" (one stream), "color" (the colour pass on a second stream) or "sh" (the colour pass
+        # and the SH half of the tail on a second stream)
+        if overlap is True:
+            overlap = "sh"
+        elif overlap is False or overlap is None:
+            overlap = "none"
+        assert overlap in ("none", "color", "sh"), overlap
+        self.overlap = overlap if overlap != "none" else None
+        self.ev_geom = None
+        self.sh_step = 0
+        if self.overlap:
+            self.stages = ["project", "bin_sort", "render_fwd_loss", "render_bwd",
+                           "geometry_tail" if self.overlap == "sh" else "grad3d_densify_adam"]
+            self.side = torch.cuda.Stream()  # default priority
+            self.view_dir = torch.empty((sc.n, 3), dtype=torch.float32, device=dev)
+        else:
+            self.stages = ["preprocess", "bin_sort", "render_fwd_loss", "render_bwd", "grad3d_densify_adam"]
         self.g3 = {k: torch.empty_like(v) for k, v in self.p.items()}
 
+    def _sh_tail(self):
+        r = self.rast
+        self.gs.gs_preprocess_bwd_adam_sh(r.deg, self.p["sh"], r.clamp, r.grad2d, self.view_dir, self.m["sh"],
+                                          self.v["sh"], self.lr, self.sh_step)
+
     def run(self, events=None, check=False):
-        gs, r, p = self.gs, self.rast, self.p
+        gs, torch, r, p = self.gs, self.torch, self.rast, self.p
         self.step_no += 1
         ev = events
 
         def mark(i):
             if ev is not None:
                 ev[i].record()
-        mark(0)
-        r.preprocess(p)
+        if self.overlap:
+            main = torch.cuda.current_stream()
+            with torch.cuda.stream(self.side):
+                if self.ev_geom is not None:
+                    self.side.wait_event(self.ev_geom)
+                    if self.overlap == "sh":
+                        self._sh_tail()
+                else:
+                    self.side.wait_stream(main)
+                gs.gs_shade(r.cam, r.deg, p["means"], p["sh"], r.splats, r.clamp)
+                ev_color = torch.cuda.Event()
+                ev_color.record(self.side)
+            mark(0)
+            gs.gs_project(r.cam, r.settings, p, r.splats, r.depth, r.rect, r.tiles_touched)
+        else:
+            mark(0)
+            r.preprocess(p)
         mark(1)
         r.bin()
         if check and int(r.overflow.item()) != 0:
@@ -113,14 +172,37 @@ class Step:
             r._alloc_lists(int(K * 1.25) + 1024)
             r.bin()
         mark(2)
+        if self.overlap:
+            main.wait_event(ev_color)
         # forward blend with the L1 loss fused in; it also clears the 2D-gradient buffer
         r.render_loss(self.target, "l1", self.dL, self.loss, clear_grad2d=True)
         mark(3)
         r.backward_2d(self.dL, accumulate=True)
         mark(4)
-        gs.gs_preprocess_bwd_adam(r.cam, r.settings, r.deg, p, r.tiles_touched, r.clamp, r.grad2d, self.m, self.v,
-                                  self.lr, self.step_no, densify_accum=self.accum, densify_count=self.count)
+        if self.overlap == "sh":
+            gs.gs_preprocess_bwd_adam_geom(r.cam, r.settings, r.deg, p, r.tiles_touched, r.clamp, r.grad2d, self.m,
+                                           self.v, self.lr, self.step_no, self.view_dir, densify_accum=self.accum,
+                                           densify_count=self.count)
+        else:
+            gs.gs_preprocess_bwd_adam(r.cam, r.settings, r.deg, p, r.tiles_touched, r.clamp, r.grad2d, self.m,
+                                      self.v, self.lr, self.step_no, densify_accum=self.accum,
+                                      densify_count=self.count)
+        if self.overlap:
+            self.ev_geom = torch.cuda.Event()
+            self.ev_geom.record(main)
+            self.sh_step = self.step_no
         mark(5)
+
+    def finish(self):
+        """Enqueue the last step's SH update and make the current stream wait for it."""
+        if self.overlap and self.ev_geom is not None:
+            torch = self.torch
+            if self.overlap == "sh":
+                with torch.cuda.stream(self.side):
+                    self.side.wait_event(self.ev_geom)
+                    self._sh_tail()
+            torch.cuda.current_stream().wait_stream(self.side)
+            self.ev_geom = None
 
     def preprocess_bwd(self):
         """The unfused 2D->3D backward with its gradients written out (the rasterizer's own backward)."""
@@ -195,7 +277,7 @@ def main():
     sc = scenes.training1m()
     print(f"# scene {sc.name}: n={sc.n} {sc.cam.width}x{sc.cam.height} ({time.time() - t_gen:.1f}s)", file=sys.stderr,
           flush=True)
-    st = Step(sc)
+    st = Step(sc, overlap=args.overlap)
     if args.copy_calibration_mb:
         src = torch.empty(args.copy_calibration_mb * (1 << 20) // 4, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
@@ -207,6 +289,7 @@ def main():
     st.run(check=True)             # sizes the list capacity
     for _ in range(max(0, args.warmup - 1)):
         st.run()
+    st.finish()
     torch.cuda.synchronize()
     c0 = st.rast.count_pairs().cpu().numpy()
     nst = len(st.stages)
@@ -215,6 +298,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         st.run(events=evs[i])
+    st.finish()                    # the last step's SH update belongs to the timed steps
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     assert int(st.rast.overflow.item()) == 0, "list capacity overflow during timing"
@@ -237,7 +321,7 @@ def main():
     value = pairs / (ms * 1e-3)
     # the rasterizer, forward + backward down to the 3D gradients (no optimizer; the forward carries the fused
     # per-pixel loss gradient, which the backward needs as its input)
-    raster_ms = sum(stage_ms[k] for k in ("preprocess", "bin_sort", "render_fwd_loss", "render_bwd"))
+    raster_ms = sum(stage_ms[k] for k in (st.stages[0], "bin_sort", "render_fwd_loss", "render_bwd"))
     raster_ms += pbwd_ms
 
     # roofline of the dominant kernel (render_bwd: FP32 VALU bound)
@@ -260,9 +344,15 @@ def main():
                            gaussians=sc.n, width=sc.cam.width, height=sc.cam.height, sh_degree=sc.sh_degree,
                            tile=16, parallelism="single-gpu"),
                fwd_bwd=dict(ms=round(raster_ms, 4), pairs_per_s=float(pairs / (raster_ms * 1e-3)),
-                            stages="preprocess + bin_sort + render_fwd_loss + render_bwd + preprocess_bwd",
+                            stages=f"{st.stages[0]} + bin_sort + render_fwd_loss + render_bwd + preprocess_bwd",
                             preprocess_bwd_ms=round(pbwd_ms, 4)),
                stage_ms={k: round(v, 4) for k, v in stage_ms.items()},
+               schedule={"none": "one stream",
+                         "color": "two streams: the SH colour pass runs on a second stream while the main stream "
+                                  "projects and bins; stage_ms are main-stream intervals",
+                         "sh": "two streams: the SH colour pass and the previous step's SH Adam update run on a "
+                               "second stream while the main stream projects and bins; stage_ms are main-stream "
+                               "intervals"}[st.overlap or "none"],
                pairs=dict(fwd_evaluated=float(p_fwd), bwd_walked=float(p_bwd), blended=float(p_blend),
                           keys=int(st.rast.num_keys.item())),
                roofline=roof)

@@ -63,20 +63,16 @@ __device__ inline void sh_eval(double x, double y, double z, double* Y) {
 
 constexpr int kPreBlock = 256;  // Gaussians (= threads) per block
 
-// One thread per Gaussian.  Each thread loads its own SH coefficients (3 (DEG+1)^2
-// consecutive floats), as 16-byte loads when the row length and the pointer allow
-// (VEC): neighbouring lanes' rows are adjacent, so the lines a wave touches are
-// fetched once and served from the cache for its remaining loads.
+// Gaussian i's SH row (3 (DEG+1)^2 consecutive floats), as 16-byte loads when the
+// row length and the pointer allow (VEC): neighbouring lanes' rows are adjacent,
+// so the lines a wave touches are fetched once and served from the cache for
+// its remaining loads.
 template <int DEG, bool VEC>
-__global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
-    constexpr int K = (DEG + 1) * (DEG + 1);
-    constexpr int J = 3 * K;
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= a.n) return;
-    float shv[J];
+__device__ __forceinline__ void load_sh(const float* sh, int i, float* shv) {
+    constexpr int J = 3 * (DEG + 1) * (DEG + 1);
     if constexpr (VEC) {
         static_assert(J % 4 == 0, "vector SH loads need a row length that is a multiple of 4");
-        const float4* src = reinterpret_cast<const float4*>(a.sh + (size_t)i * J);
+        const float4* src = reinterpret_cast<const float4*>(sh + (size_t)i * J);
 #pragma unroll
         for (int k = 0; k < J / 4; ++k) {
             const float4 v = src[k];
@@ -84,17 +80,75 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < J; ++k) shv[k] = a.sh[(size_t)i * J + k];
+        for (int k = 0; k < J; ++k) shv[k] = sh[(size_t)i * J + k];
     }
+}
+
+// Colour max(0, sum_k sh_k Y_k(dir) + 0.5) with dir the unit vector from the
+// camera centre -R^T t to the mean; cm gets bit c when channel c was clamped.
+template <int DEG>
+__device__ __forceinline__ void shade(const CamArgs& c, double mx, double my, double mz, const float* shv,
+                                      double rgb[3], uint8_t& cm) {
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    const double cpx = -(c.R[0] * c.t[0] + c.R[3] * c.t[1] + c.R[6] * c.t[2]);
+    const double cpy = -(c.R[1] * c.t[0] + c.R[4] * c.t[1] + c.R[7] * c.t[2]);
+    const double cpz = -(c.R[2] * c.t[0] + c.R[5] * c.t[1] + c.R[8] * c.t[2]);
+    double dx = mx - cpx, dy = my - cpy, dz = mz - cpz;
+    const double dinv = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
+    dx *= dinv; dy *= dinv; dz *= dinv;
+    double Y[16];
+    sh_eval<DEG>(dx, dy, dz, Y);
+    rgb[0] = rgb[1] = rgb[2] = 0.5;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        rgb[0] += Y[k] * (double)shv[3 * k];
+        rgb[1] += Y[k] * (double)shv[3 * k + 1];
+        rgb[2] += Y[k] * (double)shv[3 * k + 2];
+    }
+    cm = 0;
+    for (int ch = 0; ch < 3; ++ch)
+        if (rgb[ch] < 0.0) { cm |= (uint8_t)(1u << ch); rgb[ch] = 0.0; }
+}
+
+// Colour only: the SH colour pass on its own (rgb row of the splat record and
+// the clamp mask), for every Gaussian, culled or not.
+template <int DEG, bool VEC>
+__global__ __launch_bounds__(kPreBlock) void k_shade(PreArgs a) {
+    constexpr int J = 3 * (DEG + 1) * (DEG + 1);
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= a.n) return;
+    float shv[J];
+    load_sh<DEG, VEC>(a.sh, i, shv);
+    double rgb[3];
+    uint8_t cm;
+    shade<DEG>(a.cam, a.means[3 * i], a.means[3 * i + 1], a.means[3 * i + 2], shv, rgb, cm);
+    reinterpret_cast<float4*>(a.splats + (size_t)i * GS_SPLAT_STRIDE)[2] =
+        make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
+    a.clamp[i] = cm;
+}
+
+// One thread per Gaussian: projection, tile rectangle and (with COLOR) the SH
+// colour.  Without COLOR the rgb row of the splat record and the clamp mask are
+// left alone (k_shade writes them).
+template <int DEG, bool VEC, bool COLOR>
+__global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
+    constexpr int J = 3 * (DEG + 1) * (DEG + 1);
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= a.n) return;
+    float shv[COLOR ? J : 1];
+    if constexpr (COLOR) load_sh<DEG, VEC>(a.sh, i, shv);
 
     float4* sp = reinterpret_cast<float4*>(a.splats + (size_t)i * GS_SPLAT_STRIDE);
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     auto cull = [&]() {
-        sp[0] = z4; sp[1] = z4; sp[2] = z4;
+        sp[0] = z4; sp[1] = z4;
+        if constexpr (COLOR) {
+            sp[2] = z4;
+            a.clamp[i] = 0;
+        }
         a.depth[i] = 0.f;
         reinterpret_cast<uint2*>(a.rect)[i] = make_uint2(0u, 0u);
         a.tiles_touched[i] = 0;
-        a.clamp[i] = 0;
     };
 
     const CamArgs& c = a.cam;
@@ -166,24 +220,9 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     }
 
     // colour: max(0, sum sh Y(dir) + 0.5), dir from the camera centre
-    const double cpx = -(c.R[0] * c.t[0] + c.R[3] * c.t[1] + c.R[6] * c.t[2]);
-    const double cpy = -(c.R[1] * c.t[0] + c.R[4] * c.t[1] + c.R[7] * c.t[2]);
-    const double cpz = -(c.R[2] * c.t[0] + c.R[5] * c.t[1] + c.R[8] * c.t[2]);
-    double dx = mx - cpx, dy = my - cpy, dz = mz - cpz;
-    const double dinv = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
-    dx *= dinv; dy *= dinv; dz *= dinv;
-    double Y[16];
-    sh_eval<DEG>(dx, dy, dz, Y);
-    double rgb[3] = {0.5, 0.5, 0.5};
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        rgb[0] += Y[k] * (double)shv[3 * k];
-        rgb[1] += Y[k] * (double)shv[3 * k + 1];
-        rgb[2] += Y[k] * (double)shv[3 * k + 2];
-    }
+    double rgb[3];
     uint8_t cm = 0;
-    for (int ch = 0; ch < 3; ++ch)
-        if (rgb[ch] < 0.0) { cm |= (uint8_t)(1u << ch); rgb[ch] = 0.0; }
+    if constexpr (COLOR) shade<DEG>(c, mx, my, mz, shv, rgb, cm);
 
     // Cholesky factor of the conic, scaled so that G = exp2(-|L^T d|^2):
     // conic = [[cc, -cb], [-cb, ca]] / det = L L^T with
@@ -196,13 +235,15 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     const float uf = (float)u, vf = (float)v;
     sp[0] = make_float4(uf, vf, (float)(u - (double)uf), (float)(v - (double)vf));
     sp[1] = make_float4((float)l00, (float)l10, (float)l11, (float)sigma);
-    sp[2] = make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
+    if constexpr (COLOR) {
+        sp[2] = make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
+        a.clamp[i] = cm;
+    }
     a.depth[i] = (float)tz;
     const uint32_t r0 = (uint32_t)(uint16_t)tx0 | ((uint32_t)(uint16_t)ty0 << 16);
     const uint32_t r1 = (uint32_t)(uint16_t)tx1 | ((uint32_t)(uint16_t)ty1 << 16);
     reinterpret_cast<uint2*>(a.rect)[i] = make_uint2(r0, r1);
     a.tiles_touched[i] = touched;
-    a.clamp[i] = cm;
 }
 
 }  // namespace
@@ -210,35 +251,71 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
 
 using namespace gs;
 
-extern "C" int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
-                             const float* means, const float* log_scales, const float* quats,
-                             const float* opacity_logits, const float* sh, float* splats, float* depth,
-                             int16_t* rect, int32_t* tiles_touched, uint8_t* clamp_mask, void* stream) {
-    if (!camera_ok(cam) || !set || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
+namespace gs {
+namespace {
+
+enum class Part { kAll, kGeometry, kColor };
+
+template <int DEG, bool VEC>
+void launch_pre(Part part, dim3 grid, dim3 block, hipStream_t s, const PreArgs& a) {
+    switch (part) {
+        case Part::kAll: hipLaunchKernelGGL((k_preprocess<DEG, VEC, true>), grid, block, 0, s, a); break;
+        case Part::kGeometry: hipLaunchKernelGGL((k_preprocess<DEG, false, false>), grid, block, 0, s, a); break;
+        case Part::kColor: hipLaunchKernelGGL((k_shade<DEG, VEC>), grid, block, 0, s, a); break;
+    }
+}
+
+int preprocess_impl(Part part, const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                    const float* means, const float* log_scales, const float* quats, const float* opacity_logits,
+                    const float* sh, float* splats, float* depth, int16_t* rect, int32_t* tiles_touched,
+                    uint8_t* clamp_mask, void* stream) {
+    if (!camera_ok(cam) || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
+    if (part != Part::kColor && !set) return GS_EINVAL;
     if (n == 0) return GS_OK;
-    if (!means || !log_scales || !quats || !opacity_logits || !sh || !splats || !depth || !rect ||
-        !tiles_touched || !clamp_mask)
+    if (!means || !splats) return GS_EINVAL;
+    if (part != Part::kColor && (!log_scales || !quats || !opacity_logits || !depth || !rect || !tiles_touched))
         return GS_EINVAL;
-    if (!aligned16(quats) || !aligned16(splats) || !aligned16(rect)) return GS_EALIGN;
-    PreArgs a;
+    if (part != Part::kGeometry && (!sh || !clamp_mask)) return GS_EINVAL;
+    if (!aligned16(splats)) return GS_EALIGN;
+    if (part != Part::kColor && (!aligned16(quats) || !aligned16(rect))) return GS_EALIGN;
+    PreArgs a{};
     a.cam = cam_args(cam);
-    a.near_z = set->near_z; a.alpha_min = set->alpha_min; a.dilation = set->dilation;
+    if (set) { a.near_z = set->near_z; a.alpha_min = set->alpha_min; a.dilation = set->dilation; }
     a.n = n;
     a.means = means; a.log_scales = log_scales; a.quats = quats; a.opac = opacity_logits; a.sh = sh;
     a.splats = splats; a.depth = depth; a.rect = rect; a.tiles_touched = tiles_touched; a.clamp = clamp_mask;
     const dim3 grid((n + kPreBlock - 1) / kPreBlock), block(kPreBlock);
     hipStream_t s = as_stream(stream);
+    const bool vec = sh && aligned16(sh);
     switch (sh_degree) {
-        case 0: hipLaunchKernelGGL((k_preprocess<0, false>), grid, block, 0, s, a); break;
-        case 1:
-            if (aligned16(sh)) hipLaunchKernelGGL((k_preprocess<1, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_preprocess<1, false>), grid, block, 0, s, a);
-            break;
-        case 2: hipLaunchKernelGGL((k_preprocess<2, false>), grid, block, 0, s, a); break;
-        default:
-            if (aligned16(sh)) hipLaunchKernelGGL((k_preprocess<3, true>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_preprocess<3, false>), grid, block, 0, s, a);
-            break;
+        case 0: launch_pre<0, false>(part, grid, block, s, a); break;
+        case 1: vec ? launch_pre<1, true>(part, grid, block, s, a) : launch_pre<1, false>(part, grid, block, s, a); break;
+        case 2: launch_pre<2, false>(part, grid, block, s, a); break;
+        default: vec ? launch_pre<3, true>(part, grid, block, s, a) : launch_pre<3, false>(part, grid, block, s, a); break;
     }
     return launch_status();
+}
+
+}  // namespace
+}  // namespace gs
+
+extern "C" int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                             const float* means, const float* log_scales, const float* quats,
+                             const float* opacity_logits, const float* sh, float* splats, float* depth,
+                             int16_t* rect, int32_t* tiles_touched, uint8_t* clamp_mask, void* stream) {
+    return preprocess_impl(Part::kAll, cam, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh, splats,
+                           depth, rect, tiles_touched, clamp_mask, stream);
+}
+
+extern "C" int gs_project(const gs_camera* cam, const gs_settings* set, int32_t n, const float* means,
+                          const float* log_scales, const float* quats, const float* opacity_logits, float* splats,
+                          float* depth, int16_t* rect, int32_t* tiles_touched, void* stream) {
+    return preprocess_impl(Part::kGeometry, cam, set, n, 0, means, log_scales, quats, opacity_logits, nullptr,
+                           splats, depth, rect, tiles_touched, nullptr, stream);
+}
+
+extern "C" int gs_shade(const gs_camera* cam, int32_t n, int32_t sh_degree, const float* means, const float* sh,
+                        float* splats, uint8_t* clamp_mask, void* stream) {
+    return preprocess_impl(Part::kColor, cam, nullptr, n, sh_degree, means, nullptr, nullptr, nullptr, sh, splats,
+                           nullptr, nullptr, nullptr, clamp_mask, stream);
 }

@@ -44,6 +44,7 @@ struct BwdArgs {
     float* dsh;
     float* accum;   // densification statistic, optional
     int32_t* count;
+    float* view_dir;  // [n,3] unit camera-to-mean directions the SH gradient uses (split tail)
     AdamHyper adam;
 };
 
@@ -51,6 +52,8 @@ struct BwdArgs {
 // sum_k w[k] Y_k with respect to (x, y, z).
 template <int DEG>
 __device__ __forceinline__ void sh_values(float x, float y, float z, float* Y) {
+    // no contraction: the fused tail and its SH half must round these identically
+#pragma clang fp contract(off)
     Y[0] = 0.28209479177387814f;
     if (DEG >= 1) {
         Y[1] = -0.48860251190291992f * y;
@@ -136,7 +139,8 @@ __device__ __forceinline__ void adam_reg(float& p, float g, float& m, float& v, 
 // from the block's LDS copy (coefficient-major, row stride ldg).
 template <int DEG>
 __device__ __forceinline__ void chain(const BwdArgs& a, int i, const float* s_sh, int col, int ldg, float dmu[3],
-                                      float dls[3], float dq[4], float& dop, float Y[16], float drgb[3]) {
+                                      float dls[3], float dq[4], float& dop, float Y[16], float drgb[3],
+                                      float dir[3]) {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const CamArgs& c = a.cam;
     const float Rv[9] = {(float)c.R[0], (float)c.R[1], (float)c.R[2], (float)c.R[3], (float)c.R[4],
@@ -164,6 +168,7 @@ __device__ __forceinline__ void chain(const BwdArgs& a, int i, const float* s_sh
     const float vx = mx - cpx, vy = my - cpy, vz = mz - cpz;
     const float il = 1.f / sqrtf(vx * vx + vy * vy + vz * vz);
     const float dx = vx * il, dy = vy * il, dz = vz * il;
+    dir[0] = dx; dir[1] = dy; dir[2] = dz;
     const uint8_t cm = a.clamp[i];
 #pragma unroll
     for (int ch = 0; ch < 3; ++ch)
@@ -284,6 +289,46 @@ __device__ __forceinline__ void chain(const BwdArgs& a, int i, const float* s_sh
     dq[3] = (gz - qz * pr) * iq;
 }
 
+// Element-wise SH part: the gradient Y_k dL/dc of each coefficient in HBM order
+// (coalesced), written out and/or applied with Adam; kChunk elements per thread
+// at a time, loads first.  The parameter comes from s_sh (the block's LDS copy)
+// when given, else from HBM.
+template <int DEG, bool ADAM>
+__device__ __forceinline__ void sh_elements(const BwdArgs& a, const float* s_sh, int LDG, const float* s_y,
+                                            const float* s_c, int cnt, size_t base, int t) {
+    constexpr int J = 3 * (DEG + 1) * (DEG + 1);
+    constexpr int kChunk = 8;
+    for (int e0 = t; e0 < cnt; e0 += kChunk * kThreads) {
+        float mv[kChunk], vv[kChunk], pv[kChunk];
+        if (ADAM) {
+#pragma unroll
+            for (int c = 0; c < kChunk; ++c) {
+                const int e = e0 + c * kThreads;
+                mv[c] = e < cnt ? nt_ld(&a.adam.m[4][base + e]) : 0.f;
+                vv[c] = e < cnt ? nt_ld(&a.adam.v[4][base + e]) : 0.f;
+                pv[c] = (!s_sh && e < cnt) ? a.sh[base + e] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int e = e0 + c * kThreads;
+            if (e >= cnt) break;
+            const int g = e / J, j = e - g * J;
+            const int k = j / 3, ch = j - 3 * k;
+            const float grad = s_y[k * LDG + g] * s_c[ch * LDG + g];
+            if (a.dsh) a.dsh[base + e] = grad;
+            if (ADAM) {
+                const AdamHyper& h = a.adam;
+                float p = s_sh ? s_sh[j * LDG + g] : pv[c];
+                adam_reg(p, grad, mv[c], vv[c], k == 0 ? h.lr[4] : h.lr[5], h);
+                a.sh[base + e] = p;
+                nt_st(mv[c], &h.m[4][base + e]);
+                nt_st(vv[c], &h.v[4][base + e]);
+            }
+        }
+    }
+}
+
 // One block of kThreads threads per kG Gaussians.
 //  phase 0: the block's SH coefficients, contiguous in HBM, are copied into LDS
 //           coefficient-major (row stride kG + 1: conflict-free both ways);
@@ -292,7 +337,9 @@ __device__ __forceinline__ void chain(const BwdArgs& a, int i, const float* s_sh
 //           densification statistic, and leaves Y and the colour gradient in LDS;
 //  phase 2: the SH gradients Y_k dL/dc, element by element in HBM order, so
 //           gradient writes and the Adam read-modify-write are coalesced.
-template <int DEG, bool ADAM>
+// SH = false: the geometry half of the tail (no phase 2); the view directions
+// go to a.view_dir (zero for Gaussians outside every tile) for k_grad3d_sh.
+template <int DEG, bool ADAM, bool SH = true>
 __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
     constexpr int K = (DEG + 1) * (DEG + 1);
     constexpr int J = 3 * K;
@@ -338,10 +385,10 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
         int32_t nvis = 0;
         if (a.accum) { acc = a.accum[i]; nvis = a.count[i]; }
         float dmu[3] = {0.f, 0.f, 0.f}, dls[3] = {0.f, 0.f, 0.f}, dq[4] = {0.f, 0.f, 0.f, 0.f}, dop = 0.f;
-        float Y[16], drgb[3] = {0.f, 0.f, 0.f};
+        float Y[16], drgb[3] = {0.f, 0.f, 0.f}, dir[3] = {0.f, 0.f, 0.f};
         const bool vis = a.tt[i] > 0;
         if (vis) {
-            chain<DEG>(a, i, s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb);
+            chain<DEG>(a, i, s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb, dir);
             if (a.accum) {
                 const float2 d2 = *reinterpret_cast<const float2*>(a.grad2d + (size_t)i * GS_GRAD2D_STRIDE);
                 a.accum[i] = acc + sqrtf(d2.x * d2.x + d2.y * d2.y);
@@ -351,11 +398,17 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
 #pragma unroll
             for (int k = 0; k < K; ++k) Y[k] = 0.f;
         }
+        if constexpr (SH) {
 #pragma unroll
-        for (int k = 0; k < K; ++k) s_y[k * LDG + t] = Y[k];
-        s_c[t] = drgb[0];
-        s_c[LDG + t] = drgb[1];
-        s_c[2 * LDG + t] = drgb[2];
+            for (int k = 0; k < K; ++k) s_y[k * LDG + t] = Y[k];
+            s_c[t] = drgb[0];
+            s_c[LDG + t] = drgb[1];
+            s_c[2 * LDG + t] = drgb[2];
+        } else {
+            a.view_dir[3 * (size_t)i] = dir[0];
+            a.view_dir[3 * (size_t)i + 1] = dir[1];
+            a.view_dir[3 * (size_t)i + 2] = dir[2];
+        }
         if (a.dmeans) {
             a.dmeans[3 * (size_t)i] = dmu[0]; a.dmeans[3 * (size_t)i + 1] = dmu[1]; a.dmeans[3 * (size_t)i + 2] = dmu[2];
             a.dls[3 * (size_t)i] = dls[0]; a.dls[3 * (size_t)i + 1] = dls[1]; a.dls[3 * (size_t)i + 2] = dls[2];
@@ -390,49 +443,74 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
             a.opac[i] = po; nt_st(mo, &h.m[3][i]); nt_st(vo, &h.v[3][i]);
         }
     }
+    if constexpr (!SH) return;
     __syncthreads();
-
-    // element-wise SH part, kChunk elements per thread at a time, loads first
-    constexpr int kChunk = 8;
-    for (int e0 = t; e0 < cnt; e0 += kChunk * kThreads) {
-        float mv[kChunk], vv[kChunk];
-        if (ADAM) {
-#pragma unroll
-            for (int c = 0; c < kChunk; ++c) {
-                const int e = e0 + c * kThreads;
-                mv[c] = e < cnt ? nt_ld(&a.adam.m[4][base + e]) : 0.f;
-                vv[c] = e < cnt ? nt_ld(&a.adam.v[4][base + e]) : 0.f;
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < kChunk; ++c) {
-            const int e = e0 + c * kThreads;
-            if (e >= cnt) break;
-            const int g = e / J, j = e - g * J;
-            const int k = j / 3, ch = j - 3 * k;
-            const float grad = s_y[k * LDG + g] * s_c[ch * LDG + g];
-            if (a.dsh) a.dsh[base + e] = grad;
-            if (ADAM) {
-                const AdamHyper& h = a.adam;
-                float p = s_sh[j * LDG + g];
-                adam_reg(p, grad, mv[c], vv[c], k == 0 ? h.lr[4] : h.lr[5], h);
-                a.sh[base + e] = p;
-                nt_st(mv[c], &h.m[4][base + e]);
-                nt_st(vv[c], &h.v[4][base + e]);
-            }
-        }
-    }
+    sh_elements<DEG, ADAM>(a, s_sh, LDG, s_y, s_c, cnt, base, t);
 }
 
-template <bool ADAM>
+// The SH half of the tail on its own: Y from the stored view direction, the
+// clamp-masked colour gradient from grad2d, then the same element-wise update
+// as the fused kernel (so both give the same bits).
+template <int DEG>
+__global__ __launch_bounds__(kThreads) void k_grad3d_sh(BwdArgs a) {
+    constexpr int K = (DEG + 1) * (DEG + 1);
+    constexpr int J = 3 * K;
+    constexpr int LDG = kG + 1;
+    __shared__ float s_y[K * LDG];
+    __shared__ float s_c[3 * LDG];
+    const int t = threadIdx.x;
+    const int g0 = blockIdx.x * kG;
+    const int ng = min(kG, a.n - g0);
+    const int cnt = ng * J;
+    const size_t base = (size_t)g0 * J;
+    if (t < ng) {
+        const int i = g0 + t;
+        float Y[16];
+        sh_values<DEG>(a.view_dir[3 * (size_t)i], a.view_dir[3 * (size_t)i + 1], a.view_dir[3 * (size_t)i + 2], Y);
+        const float4 g1 = reinterpret_cast<const float4*>(a.grad2d)[3 * (size_t)i + 1];
+        const float4 g2 = reinterpret_cast<const float4*>(a.grad2d)[3 * (size_t)i + 2];
+        const uint8_t cm = a.clamp[i];
+        float drgb[3] = {g1.z, g1.w, g2.x};
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch)
+            if ((cm >> ch) & 1u) drgb[ch] = 0.f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) s_y[k * LDG + t] = Y[k];
+        s_c[t] = drgb[0];
+        s_c[LDG + t] = drgb[1];
+        s_c[2 * LDG + t] = drgb[2];
+    }
+    __syncthreads();
+    sh_elements<DEG, true>(a, nullptr, LDG, s_y, s_c, cnt, base, t);
+}
+
+template <bool ADAM, bool SH = true>
 inline void launch_grad3d(int deg, const BwdArgs& a, hipStream_t s) {
     const dim3 grid((a.n + kG - 1) / kG), block(kThreads);
     switch (deg) {
-        case 0: hipLaunchKernelGGL((k_grad3d<0, ADAM>), grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL((k_grad3d<1, ADAM>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_grad3d<2, ADAM>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((k_grad3d<3, ADAM>), grid, block, 0, s, a); break;
+        case 0: hipLaunchKernelGGL((k_grad3d<0, ADAM, SH>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((k_grad3d<1, ADAM, SH>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_grad3d<2, ADAM, SH>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_grad3d<3, ADAM, SH>), grid, block, 0, s, a); break;
     }
+}
+
+inline void launch_grad3d_sh(int deg, const BwdArgs& a, hipStream_t s) {
+    const dim3 grid((a.n + kG - 1) / kG), block(kThreads);
+    switch (deg) {
+        case 0: hipLaunchKernelGGL((k_grad3d_sh<0>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((k_grad3d_sh<1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_grad3d_sh<2>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_grad3d_sh<3>), grid, block, 0, s, a); break;
+    }
+}
+
+inline void fill_adam(BwdArgs& a, const gs_adam_state* adam) {
+    for (int k = 0; k < 5; ++k) { a.adam.m[k] = adam->exp_avg[k]; a.adam.v[k] = adam->exp_avg_sq[k]; }
+    for (int k = 0; k < 6; ++k) a.adam.lr[k] = adam->lr[k];
+    a.adam.b1 = adam->beta1; a.adam.b2 = adam->beta2; a.adam.eps = adam->eps;
+    a.adam.inv_c1 = (float)(1.0 / (1.0 - pow((double)adam->beta1, adam->step)));
+    a.adam.inv_sqrt_c2 = (float)(1.0 / sqrt(1.0 - pow((double)adam->beta2, adam->step)));
 }
 
 inline void fill_common(BwdArgs& a, const gs_camera* cam, const gs_settings* set, int32_t n, const float* means,
@@ -494,11 +572,53 @@ extern "C" int gs_preprocess_bwd_adam(const gs_camera* cam, const gs_settings* s
     fill_common(a, cam, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
     a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
     a.accum = densify_accum; a.count = densify_count;
-    for (int k = 0; k < 5; ++k) { a.adam.m[k] = adam->exp_avg[k]; a.adam.v[k] = adam->exp_avg_sq[k]; }
-    for (int k = 0; k < 6; ++k) a.adam.lr[k] = adam->lr[k];
-    a.adam.b1 = adam->beta1; a.adam.b2 = adam->beta2; a.adam.eps = adam->eps;
-    a.adam.inv_c1 = (float)(1.0 / (1.0 - pow((double)adam->beta1, adam->step)));
-    a.adam.inv_sqrt_c2 = (float)(1.0 / sqrt(1.0 - pow((double)adam->beta2, adam->step)));
+    fill_adam(a, adam);
     launch_grad3d<true>(sh_degree, a, as_stream(stream));
+    return launch_status();
+}
+
+extern "C" int gs_preprocess_bwd_adam_geom(const gs_camera* cam, const gs_settings* set, int32_t n,
+                                           int32_t sh_degree, float* means, float* log_scales, float* quats,
+                                           float* opacity_logits, const float* sh, const int32_t* tiles_touched,
+                                           const uint8_t* clamp_mask, const float* grad2d,
+                                           const gs_adam_state* adam, float* densify_accum,
+                                           int32_t* densify_count, float* view_dir, void* stream) {
+    if (!camera_ok(cam) || !set || !adam || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE)
+        return GS_EINVAL;
+    if (adam->step < 1) return GS_EINVAL;
+    if (n == 0) return GS_OK;
+    if (!means || !log_scales || !quats || !opacity_logits || !sh || !tiles_touched || !clamp_mask || !grad2d ||
+        !view_dir)
+        return GS_EINVAL;
+    for (int k = 0; k < 4; ++k)
+        if (!adam->exp_avg[k] || !adam->exp_avg_sq[k]) return GS_EINVAL;
+    if ((densify_accum == nullptr) != (densify_count == nullptr)) return GS_EINVAL;
+    if (!aligned16(quats) || !aligned16(grad2d)) return GS_EALIGN;
+    if (!aligned16(adam->exp_avg[2]) || !aligned16(adam->exp_avg_sq[2])) return GS_EALIGN;
+    BwdArgs a;
+    fill_common(a, cam, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
+    a.accum = densify_accum; a.count = densify_count;
+    a.view_dir = view_dir;
+    fill_adam(a, adam);
+    launch_grad3d<true, false>(sh_degree, a, as_stream(stream));
+    return launch_status();
+}
+
+extern "C" int gs_preprocess_bwd_adam_sh(int32_t n, int32_t sh_degree, float* sh, const uint8_t* clamp_mask,
+                                         const float* grad2d, const float* view_dir, const gs_adam_state* adam,
+                                         void* stream) {
+    if (!adam || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
+    if (adam->step < 1) return GS_EINVAL;
+    if (n == 0) return GS_OK;
+    if (!sh || !clamp_mask || !grad2d || !view_dir || !adam->exp_avg[4] || !adam->exp_avg_sq[4]) return GS_EINVAL;
+    if (!aligned16(grad2d)) return GS_EALIGN;
+    BwdArgs a{};
+    a.n = n;
+    a.sh = sh;
+    a.clamp = clamp_mask;
+    a.grad2d = grad2d;
+    a.view_dir = const_cast<float*>(view_dir);
+    fill_adam(a, adam);
+    launch_grad3d_sh(sh_degree, a, as_stream(stream));
     return launch_status();
 }

@@ -47,9 +47,10 @@ class GsAdamState(C.Structure):
                 ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("step", C.c_int32)]
 
 
-SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_bin_workspace_size",
-           "gs_bin_sort", "gs_bin_keys", "gs_render_fwd", "gs_render_fwd_loss", "gs_render_bwd", "gs_preprocess_bwd",
-           "gs_preprocess_bwd_adam", "gs_image_loss", "gs_densify_accum", "gs_adam_step", "gs_count_pairs"]
+SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_project", "gs_shade",
+           "gs_bin_workspace_size", "gs_bin_sort", "gs_bin_keys", "gs_render_fwd", "gs_render_fwd_loss",
+           "gs_render_bwd", "gs_preprocess_bwd", "gs_preprocess_bwd_adam", "gs_preprocess_bwd_adam_geom",
+           "gs_preprocess_bwd_adam_sh", "gs_image_loss", "gs_densify_accum", "gs_adam_step", "gs_count_pairs"]
 PARAM_ORDER = ("means", "log_scales", "quats", "opacity_logits", "sh")
 
 _lib = None
@@ -81,6 +82,11 @@ def load_library(path=LIB_PATH):
     lib.gs_preprocess_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
     lib.gs_preprocess_bwd_adam.argtypes = ([P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 8 +
                                            [P(GsAdamState)] + [_vp] * 7 + [_vp])
+    lib.gs_preprocess_bwd_adam_geom.argtypes = ([P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 8 +
+                                                [P(GsAdamState)] + [_vp] * 3 + [_vp])
+    lib.gs_preprocess_bwd_adam_sh.argtypes = [_i32, _i32] + [_vp] * 4 + [P(GsAdamState), _vp]
+    lib.gs_project.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_vp]
+    lib.gs_shade.argtypes = [P(GsCamera), _i32, _i32] + [_vp] * 4 + [_vp]
     lib.gs_image_loss.argtypes = [_i32, _i64, _vp, _vp, _vp, _vp, _vp]
     lib.gs_densify_accum.argtypes = [_i32, _vp, _vp, _vp, _vp, _vp]
     lib.gs_adam_step.argtypes = [_i32, P(GsAdamGroup), C.c_float, C.c_float, C.c_float, _i32, _vp]
@@ -270,6 +276,64 @@ def gs_preprocess_bwd_adam(cam, settings, sh_degree, params, tiles_touched, clam
         _p(densify_accum, f32, "densify_accum"), _p(densify_count, torch.int32, "densify_count"),
         *[_p(g.get(k), f32, "grad." + k) for k in PARAM_ORDER], _stream())
     _check(rc, "gs_preprocess_bwd_adam")
+
+
+def _adam_struct(exp_avg, exp_avg_sq, lr, step, beta1, beta2, eps):
+    f32 = torch.float32
+    st = GsAdamState()
+    for i, k in enumerate(PARAM_ORDER):
+        if k in exp_avg:
+            st.exp_avg[i] = _p(exp_avg[k], f32, "exp_avg." + k).value
+            st.exp_avg_sq[i] = _p(exp_avg_sq[k], f32, "exp_avg_sq." + k).value
+    for i, k in enumerate(("means", "log_scales", "quats", "opacity_logits", "sh_dc", "sh_rest")):
+        st.lr[i] = float(lr[k])
+    st.beta1, st.beta2, st.eps, st.step = beta1, beta2, eps, int(step)
+    return st
+
+
+def gs_preprocess_bwd_adam_geom(cam, settings, sh_degree, params, tiles_touched, clamp_mask, grad2d, exp_avg,
+                                exp_avg_sq, lr, step, view_dir, beta1=0.9, beta2=0.999, eps=1e-8,
+                                densify_accum=None, densify_count=None):
+    """Geometry half of the fused tail: mean / log-scale / quaternion / opacity gradients and Adam in place,
+    densification statistic, and the view directions [n,3] the SH half needs."""
+    f32, n = torch.float32, params["means"].shape[0]
+    st = _adam_struct(exp_avg, exp_avg_sq, lr, step, beta1, beta2, eps)
+    rc = load_library().gs_preprocess_bwd_adam_geom(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, sh_degree,
+        *[_p(params[k], f32, k) for k in PARAM_ORDER], _p(tiles_touched, torch.int32, "tiles_touched"),
+        _p(clamp_mask, torch.uint8, "clamp_mask"), _p(grad2d, f32, "grad2d"), C.byref(st),
+        _p(densify_accum, f32, "densify_accum"), _p(densify_count, torch.int32, "densify_count"),
+        _p(view_dir, f32, "view_dir"), _stream())
+    _check(rc, "gs_preprocess_bwd_adam_geom")
+
+
+def gs_preprocess_bwd_adam_sh(sh_degree, sh, clamp_mask, grad2d, view_dir, exp_avg, exp_avg_sq, lr, step,
+                              beta1=0.9, beta2=0.999, eps=1e-8):
+    """SH half of the fused tail: SH gradients and Adam on sh in place (exp_avg / exp_avg_sq: the sh moments)."""
+    f32 = torch.float32
+    st = _adam_struct({"sh": exp_avg}, {"sh": exp_avg_sq}, lr, step, beta1, beta2, eps)
+    rc = load_library().gs_preprocess_bwd_adam_sh(
+        sh.shape[0], sh_degree, _p(sh, f32, "sh"), _p(clamp_mask, torch.uint8, "clamp_mask"),
+        _p(grad2d, f32, "grad2d"), _p(view_dir, f32, "view_dir"), C.byref(st), _stream())
+    _check(rc, "gs_preprocess_bwd_adam_sh")
+
+
+def gs_project(cam, settings, params, splats, depth, rect, tiles_touched):
+    f32, n = torch.float32, params["means"].shape[0]
+    rc = load_library().gs_project(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(params["means"], f32, "means"),
+        _p(params["log_scales"], f32, "log_scales"), _p(params["quats"], f32, "quats"),
+        _p(params["opacity_logits"], f32, "opacity_logits"), _p(splats, f32, "splats"), _p(depth, f32, "depth"),
+        _p(rect, torch.int16, "rect"), _p(tiles_touched, torch.int32, "tiles_touched"), _stream())
+    _check(rc, "gs_project")
+
+
+def gs_shade(cam, sh_degree, means, sh, splats, clamp_mask):
+    f32 = torch.float32
+    rc = load_library().gs_shade(C.byref(camera_struct(cam)), means.shape[0], sh_degree, _p(means, f32, "means"),
+                                 _p(sh, f32, "sh"), _p(splats, f32, "splats"),
+                                 _p(clamp_mask, torch.uint8, "clamp_mask"), _stream())
+    _check(rc, "gs_shade")
 
 
 def gs_image_loss(mode, pred, target, dL_dpred, loss):

@@ -112,6 +112,23 @@ int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32_t n, int32
                   float* splats, float* depth, int16_t* rect, int32_t* tiles_touched,
                   uint8_t* clamp_mask, void* stream);
 
+/*
+ * gs_project and gs_shade -- the two halves of gs_preprocess, for callers that
+ * run the SH colour on another stream while the geometry goes on to binning.
+ * gs_project writes rows 0-1 of each splat record (mean, conic factor,
+ * opacity), depth, rect and tiles_touched exactly as gs_preprocess does, and
+ * leaves row 2 and the clamp mask alone.  gs_shade writes row 2 (r, g, b, 0)
+ * and clamp_mask for every Gaussian, culled or not (the colour of a culled
+ * Gaussian is computed but never read); for a visible Gaussian both equal
+ * gs_preprocess's bit for bit.  Writes of the two calls touch disjoint bytes.
+ */
+int gs_project(const gs_camera* cam, const gs_settings* set, int32_t n,
+               const float* means, const float* log_scales, const float* quats,
+               const float* opacity_logits, float* splats, float* depth, int16_t* rect,
+               int32_t* tiles_touched, void* stream);
+int gs_shade(const gs_camera* cam, int32_t n, int32_t sh_degree, const float* means, const float* sh,
+             float* splats, uint8_t* clamp_mask, void* stream);
+
 /* Bytes of workspace gs_bin_sort needs for n Gaussians and key_capacity list
    entries. */
 int gs_bin_workspace_size(int32_t n, const gs_camera* cam, int64_t key_capacity, size_t* bytes);
@@ -302,6 +319,32 @@ int gs_preprocess_bwd_adam(const gs_camera* cam, const gs_settings* set, int32_t
                            const gs_adam_state* adam, float* densify_accum, int32_t* densify_count,
                            float* dmeans, float* dlog_scales, float* dquats, float* dopacity_logits,
                            float* dsh, void* stream);
+
+/*
+ * gs_preprocess_bwd_adam_geom and gs_preprocess_bwd_adam_sh -- the two halves
+ * of gs_preprocess_bwd_adam (without the optional gradient outputs), for
+ * callers that move the SH update off the critical path: the SH coefficients
+ * are needed again only by the next step's colour pass, not by its projection
+ * and binning.
+ * _geom: the mean / log-scale / quaternion / opacity gradients (the mean's
+ * includes the view-direction term, which reads sh), their Adam step in place,
+ * the densification statistic, and view_dir [n,3] float32: each Gaussian's
+ * unit camera-to-mean direction (0 for Gaussians with tiles_touched == 0).
+ * _sh: the SH gradients from view_dir, the clamp mask and grad2d, and their
+ * Adam step on sh in place (moments exp_avg[4], exp_avg_sq[4], lr[4], lr[5]).
+ * Ordering the caller keeps: _sh after _geom (it reads view_dir and _geom
+ * reads sh), and before anything that rewrites grad2d, clamp_mask or
+ * view_dir, or reads sh.  Together they give gs_preprocess_bwd_adam's result
+ * bit for bit.
+ */
+int gs_preprocess_bwd_adam_geom(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                                float* means, float* log_scales, float* quats, float* opacity_logits,
+                                const float* sh, const int32_t* tiles_touched, const uint8_t* clamp_mask,
+                                const float* grad2d, const gs_adam_state* adam, float* densify_accum,
+                                int32_t* densify_count, float* view_dir, void* stream);
+int gs_preprocess_bwd_adam_sh(int32_t n, int32_t sh_degree, float* sh, const uint8_t* clamp_mask,
+                              const float* grad2d, const float* view_dir, const gs_adam_state* adam,
+                              void* stream);
 
 /*
  * gs_count_pairs -- diagnostic pair counts of a forward pass (device int64

@@ -3,6 +3,7 @@ ragged image sizes, capacity overflow, depth ties, huge splats, argument
 errors, and the training-step tail against the oracle."""
 import ctypes as C
 import math
+import os
 
 import numpy as np
 import pytest
@@ -253,6 +254,97 @@ def test_fused_forward_loss_matches_separate_calls(mode):
     assert float(r.grad2d.abs().max()) == 0.0
     if mode == "l1":
         assert float(dl_b[:, :5, :5].abs().max()) == 0.0
+
+
+def test_split_preprocess_matches_combined():
+    """gs_project + gs_shade == gs_preprocess: geometry for every Gaussian, colour and clamp mask for
+    the visible ones, bit for bit."""
+    import torch
+    gs = _gs()
+    sc = scenes.random_small(36, n=1500, width=96, height=72, sh_degree=3, scale_mu=-2.4)
+    p = to_dev(sc.params())
+    r = gs.Rasterizer(sc.cam, sc.n, 3)
+    r.preprocess(p)
+    ref = {k: getattr(r, k).clone() for k in ("splats", "depth", "rect", "tiles_touched", "clamp")}
+    r.splats.fill_(-1.0)
+    r.clamp.fill_(255)
+    gs.gs_shade(r.cam, 3, p["means"], p["sh"], r.splats, r.clamp)
+    gs.gs_project(r.cam, r.settings, p, r.splats, r.depth, r.rect, r.tiles_touched)
+    torch.cuda.synchronize()
+    vis = ref["tiles_touched"] > 0
+    assert int(vis.sum()) > 100
+    for k in ("depth", "rect", "tiles_touched"):
+        assert torch.equal(getattr(r, k), ref[k]), k
+    assert torch.equal(r.splats[:, :8], ref["splats"][:, :8])
+    assert torch.equal(r.splats[vis], ref["splats"][vis])
+    assert torch.equal(r.clamp[vis], ref["clamp"][vis])
+
+
+def test_split_tail_matches_fused():
+    """gs_preprocess_bwd_adam_geom + gs_preprocess_bwd_adam_sh == gs_preprocess_bwd_adam from the same
+    state and 2D gradients: parameters, moments and densification statistic bit for bit."""
+    import torch
+    gs = _gs()
+    sc = scenes.random_small(37, n=1300, width=96, height=72, sh_degree=3, scale_mu=-2.4)
+    N = sc.n
+    lr = scenes.ADAM_LR
+    p0 = to_dev(sc.params())
+    r = gs.Rasterizer(sc.cam, N, 3)
+    r.forward(p0)
+    r.backward_2d(torch.from_numpy(sc.dL_dimage).cuda())
+    rng = np.random.default_rng(8)
+    m0 = {k: torch.from_numpy(rng.normal(0, 1e-3, v.shape).astype(np.float32)).cuda() for k, v in p0.items()}
+    v0 = {k: torch.from_numpy(rng.uniform(0, 1e-6, v.shape).astype(np.float32)).cuda() for k, v in p0.items()}
+    out = []
+    for split in (False, True):
+        p = {k: v.clone() for k, v in p0.items()}
+        m = {k: v.clone() for k, v in m0.items()}
+        v = {k: x.clone() for k, x in v0.items()}
+        acc = torch.zeros(N, device="cuda")
+        cnt = torch.zeros(N, dtype=torch.int32, device="cuda")
+        if split:
+            vd = torch.full((N, 3), float("nan"), device="cuda")
+            gs.gs_preprocess_bwd_adam_geom(r.cam, r.settings, 3, p, r.tiles_touched, r.clamp, r.grad2d, m, v, lr,
+                                           3, vd, densify_accum=acc, densify_count=cnt)
+            gs.gs_preprocess_bwd_adam_sh(3, p["sh"], r.clamp, r.grad2d, vd, m["sh"], v["sh"], lr, 3)
+            assert not torch.isnan(vd).any()
+        else:
+            gs.gs_preprocess_bwd_adam(r.cam, r.settings, 3, p, r.tiles_touched, r.clamp, r.grad2d, m, v, lr, 3,
+                                      densify_accum=acc, densify_count=cnt)
+        out.append((p, m, v, acc, cnt))
+    torch.cuda.synchronize()
+    (pa, ma, va, aa, ca), (pb, mb, vb, ab, cb) = out
+    for k in pa:
+        assert torch.equal(pa[k], pb[k]), k
+        assert torch.equal(ma[k], mb[k]), k
+        assert torch.equal(va[k], vb[k]), k
+    assert torch.equal(aa, ab) and torch.equal(ca, cb)
+
+
+def test_two_stream_steps_match_one_stream():
+    """Training steps with the SH work on a second stream compute what the single-stream steps compute
+    (up to the order of the backward's atomic additions)."""
+    import sys
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    sc = scenes.random_small(38, n=3000, width=160, height=96, sh_degree=3, scale_mu=-2.4)
+    sc.target = np.random.default_rng(4).uniform(0, 1, (3, 96, 160)).astype(np.float32)
+    res = []
+    for overlap in ("none", "color", "sh"):
+        st = bench.Step(sc, overlap=overlap)
+        st.run(check=True)
+        for _ in range(3):
+            st.run()
+        st.finish()
+        torch.cuda.synchronize()
+        res.append({k: v.cpu().numpy() for k, v in st.p.items()})
+    for other in res[1:]:
+        for k in res[0]:
+            p0 = np.asarray(sc.params()[k])
+            e = rel_l2(other[k], res[0][k])           # the parameters
+            d = rel_l2(other[k] - p0, res[0][k] - p0)  # the updates (Adam may flip the sign of a near-zero gradient)
+            assert e < 1e-5 and d < 2e-2, (k, e, d)
 
 
 def test_backward_accumulate():
