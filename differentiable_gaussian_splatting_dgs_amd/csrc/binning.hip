@@ -31,12 +31,17 @@
 namespace gs {
 namespace {
 
-constexpr int kSortThreads = 256;
-constexpr int kDepthIPT = 16;                       // depth sort over N: 4096 items per partition
-constexpr int kTileIPT = 16;                        // tile sort over K: 4096 items per partition
-constexpr int kDepthPart = kSortThreads * kDepthIPT;
-constexpr int kTilePart = kSortThreads * kTileIPT;
-constexpr int kKeyBlocks = 512;                     // grid of the depth-key/histogram pass
+// Sort passes: THREADS x IPT items per partition.  More waves with fewer items
+// each shorten every wave's serial ranking and write-out chains, which set the
+// time of a pass when there is about one block per CU.
+constexpr int kDepthThreads = 512;
+constexpr int kDepthIPT = 8;                        // depth sort over N: 4096 items per partition
+constexpr int kTileThreads = 512;
+constexpr int kTileIPT = 8;                         // tile sort over K: 4096 items per partition
+constexpr int kDepthPart = kDepthThreads * kDepthIPT;
+constexpr int kTilePart = kTileThreads * kTileIPT;
+constexpr int kKeyIPT = 8;                          // depth-key pass: Gaussians per thread
+constexpr int kRangeIPT = 8;                        // tile-range pass: keys per thread
 constexpr int kStripes = 32;                        // histogram copies that blocks add into
 constexpr int kHistBins = 6 * 256;                  // 4 depth digits + 2 tile digits
 constexpr int kLookWindow = 8;                      // predecessors read at once per digit
@@ -156,26 +161,41 @@ __global__ void k_clear(ClearArgs c) {
         for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < c.count[b]; i += stride) c.p[b][i] = 0u;
 }
 
-// 1. depth keys + counts of the 4 depth digits.  Blocks add their counts into
-// one of kStripes histogram copies (so no address sees more than a few dozen
-// atomics); k_hist_reduce sums the copies.
+// 1. depth keys + counts of the 4 depth digits.  Each thread loads its
+// kKeyIPT Gaussians before using any (one memory latency per thread, not one
+// per item).  Blocks add their counts into one of kStripes histogram copies, so
+// no address sees more than a few dozen global atomics; the sort passes sum the
+// copies.
 __global__ __launch_bounds__(256) void k_depth_keys(int32_t n, const float* depth, const int32_t* tt,
                                                     uint32_t* keys, uint32_t* vals, uint32_t* stripes) {
     __shared__ uint32_t sh[4 * kRadix];
     for (int i = threadIdx.x; i < 4 * kRadix; i += blockDim.x) sh[i] = 0;
-    __syncthreads();
-    const int stride = gridDim.x * blockDim.x;
-    for (int base = blockIdx.x * blockDim.x; base < n; base += stride) {
-        const int i = base + threadIdx.x;
-        const bool valid = i < n;
-        uint32_t k = 0u;
-        if (valid) {
-            k = tt[i] > 0 ? __float_as_uint(depth[i]) : 0xffffffffu;
-            keys[i] = k;
+    const int64_t base = (int64_t)blockIdx.x * 256 * kKeyIPT + threadIdx.x;
+    float dep[kKeyIPT];
+    int32_t cnt[kKeyIPT];
+#pragma unroll
+    for (int u = 0; u < kKeyIPT; ++u) {
+        const int64_t i = base + u * 256;
+        dep[u] = i < n ? depth[i] : 0.f;
+        cnt[u] = i < n ? tt[i] : 0;
+    }
+    uint32_t k[kKeyIPT];
+#pragma unroll
+    for (int u = 0; u < kKeyIPT; ++u) {
+        const int64_t i = base + u * 256;
+        k[u] = cnt[u] > 0 ? __float_as_uint(dep[u]) : 0xffffffffu;
+        if (i < n) {
+            keys[i] = k[u];
             vals[i] = (uint32_t)i;
         }
+    }
+    __syncthreads();
 #pragma unroll
-        for (int d = 0; d < 4; ++d) wave_hist_add(sh + d * kRadix, (k >> (8 * d)) & 255u, valid);
+    for (int u = 0; u < kKeyIPT; ++u) {
+        if (base + u * 256 < n) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) atomicAdd(&sh[d * kRadix + ((k[u] >> (8 * d)) & 255u)], 1u);
+        }
     }
     __syncthreads();
     uint32_t* out = stripes + (size_t)(blockIdx.x % kStripes) * kHistBins;
@@ -199,59 +219,71 @@ struct PassArgs {
     int shift;
 };
 
-// 2/4. one onesweep pass over 8 bits of a 32-bit key, IPT items per thread.
-template <int IPT>
-__global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
-    constexpr int kSortIPT = IPT;
-    constexpr int kSortPart = kSortThreads * IPT;
+// Inclusive sum over the 64 lanes of a wave.
+__device__ inline uint32_t wave_incl_sum(uint32_t v) {
+    const int lane = threadIdx.x & 63;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(v, o, 64);
+        if (lane >= o) v += y;
+    }
+    return v;
+}
+
+// 2/4. one onesweep pass over 8 bits of a 32-bit key, THREADS threads with IPT
+// items each.  Threads 0..255 (waves 0-3) also own one digit each for the
+// histogram scan and the look-back.
+template <int THREADS, int IPT>
+__global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
+    constexpr int kWaves = THREADS / 64;
+    constexpr int kSortPart = THREADS * IPT;
+    static_assert(THREADS >= kRadix && THREADS % 64 == 0, "one thread per digit");
     __shared__ uint32_t s_off[kRadix];          // global exclusive digit offsets
-    __shared__ uint32_t s_wave[4][kRadix];      // per-wave digit counts -> prefixes
+    __shared__ uint32_t s_wave[kWaves][kRadix]; // per-wave digit counts -> prefixes
     __shared__ uint32_t s_base[kRadix];         // global offset of this partition's first item of digit d
     __shared__ uint32_t s_blk[kRadix];          // block-local exclusive digit offsets
     __shared__ uint32_t s_keys[kSortPart];      // partition in digit order
     __shared__ uint32_t s_vals[kSortPart];
-    __shared__ uint32_t s_wsum[4];
+    __shared__ uint32_t s_wsum[2][4];
     __shared__ uint32_t s_part;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool digit_thread = tid < kRadix;
 
     if (tid == 0) {
         const uint32_t grp = blockIdx.x % kTicketGroups;
         s_part = atomicAdd(p.ticket + grp * kTicketStride, 1u) * kTicketGroups + grp;
     }
-    for (int i = tid; i < 4 * kRadix; i += kSortThreads) (&s_wave[0][0])[i] = 0;
-    // exclusive scan of the digit histogram (256 entries, one per thread)
-    {
-        const uint32_t h = stripe_sum(p.stripes, p.hist_bin + tid);
-        uint32_t x = h;
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        if (lane == 63) s_wsum[wave] = x;
-        __syncthreads();
-        uint32_t add = 0;
-        for (int w = 0; w < wave; ++w) add += s_wsum[w];
-        s_off[tid] = x - h + add;
+    for (int i = tid; i < kWaves * kRadix; i += THREADS) (&s_wave[0][0])[i] = 0;
+    // exclusive scan of the digit histogram (256 entries, one per digit thread)
+    uint32_t h = 0, hx = 0;
+    if (digit_thread) {
+        h = stripe_sum(p.stripes, p.hist_bin + tid);
+        hx = wave_incl_sum(h);
+        if (lane == 63) s_wsum[0][wave] = hx;
     }
     __syncthreads();
+    if (digit_thread) {
+        uint32_t add = 0;
+        for (int w = 0; w < wave; ++w) add += s_wsum[0][w];
+        s_off[tid] = hx - h + add;
+    }
     const uint32_t part = s_part;
     uint32_t count = p.count_dev ? *p.count_dev : p.count_host;
     if (count > p.cap) count = p.cap;
     const uint32_t nparts = (count + kSortPart - 1) / kSortPart;
-    if (part >= nparts) return;
+    if (part >= nparts) return;  // uniform over the block
 
     // load: wave w owns [part*P + w*64*IPT, +64*IPT), item i of lane l at + i*64 + l
-    const uint32_t base = part * kSortPart + wave * 64 * kSortIPT;
-    uint32_t key[kSortIPT], val[kSortIPT], rank[kSortIPT];
+    const uint32_t base = part * kSortPart + wave * 64 * IPT;
+    uint32_t key[IPT], val[IPT], rank[IPT];
 #pragma unroll
-    for (int i = 0; i < kSortIPT; ++i) {
+    for (int i = 0; i < IPT; ++i) {
         const uint32_t idx = base + i * 64 + lane;
         key[i] = idx < count ? p.keys_in[idx] : 0u;
         val[i] = idx < count ? p.vals_in[idx] : 0u;
     }
     const uint64_t lt = lanemask_lt();
 #pragma unroll
-    for (int i = 0; i < kSortIPT; ++i) {
+    for (int i = 0; i < IPT; ++i) {
         const bool valid = (base + i * 64 + lane) < count;
         const uint32_t d = (key[i] >> p.shift) & 255u;
         const uint64_t m = match8(d, valid);
@@ -263,26 +295,29 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
-    // per digit: prefix over waves, block-local digit offsets, look-back over partitions
-    {
-        const int d = tid;
-        const uint32_t c0 = s_wave[0][d], c1 = s_wave[1][d], c2 = s_wave[2][d], c3 = s_wave[3][d];
-        const uint32_t total = c0 + c1 + c2 + c3;
-        s_wave[0][d] = 0; s_wave[1][d] = c0; s_wave[2][d] = c0 + c1; s_wave[3][d] = c0 + c1 + c2;
-        // block-local exclusive scan of the digit totals
-        uint32_t x = total;
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
+    // per digit: prefix over waves, then a block-local exclusive scan of the digit totals
+    uint32_t total = 0, tx = 0;
+    if (digit_thread) {
+        uint32_t run = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t c = s_wave[w][tid];
+            s_wave[w][tid] = run;
+            run += c;
         }
-        __syncthreads();  // s_wsum reuse
-        if (lane == 63) s_wsum[wave] = x;
-        __syncthreads();
+        total = run;
+        tx = wave_incl_sum(total);
+        if (lane == 63) s_wsum[1][wave] = tx;
+    }
+    __syncthreads();
+    if (digit_thread) {
+        const int d = tid;
         uint32_t add = 0;
-        for (int w = 0; w < wave; ++w) add += s_wsum[w];
-        const uint32_t blk = x - total + add;
+        for (int w = 0; w < wave; ++w) add += s_wsum[1][w];
+        const uint32_t blk = tx - total + add;
         s_blk[d] = blk;
 
+        // decoupled look-back over the earlier partitions
         uint32_t* st = p.status + (size_t)part * kRadix + d;
         uint32_t prefix = 0;
         if (part == 0) {
@@ -323,7 +358,7 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
     __syncthreads();
     // stage the partition in digit order in LDS ...
 #pragma unroll
-    for (int i = 0; i < kSortIPT; ++i) {
+    for (int i = 0; i < IPT; ++i) {
         if (base + i * 64 + lane < count) {
             const uint32_t d = (key[i] >> p.shift) & 255u;
             const uint32_t q = s_blk[d] + s_wave[wave][d] + rank[i];
@@ -336,12 +371,16 @@ __global__ __launch_bounds__(kSortThreads) void k_onesweep(PassArgs p) {
     __syncthreads();
     // ... and write it out: consecutive slots of one digit go to consecutive addresses
     const uint32_t nloc = min((uint32_t)kSortPart, count - part * kSortPart);
-    for (uint32_t q = tid; q < nloc; q += kSortThreads) {
-        const uint32_t k = s_keys[q];
-        const uint32_t pos = s_base[(k >> p.shift) & 255u] + q;
-        if (pos < count) {  // always true for a consistent histogram; guards the buffers
-            if (p.keys_out) p.keys_out[pos] = k;
-            p.vals_out[pos] = s_vals[q];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const uint32_t q = (uint32_t)(i * THREADS + tid);
+        if (q < nloc) {
+            const uint32_t k = s_keys[q];
+            const uint32_t pos = s_base[(k >> p.shift) & 255u] + q;
+            if (pos < count) {  // always true for a consistent histogram; guards the buffers
+                if (p.keys_out) p.keys_out[pos] = k;
+                p.vals_out[pos] = s_vals[q];
+            }
         }
     }
 }
@@ -516,8 +555,10 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
                 a.tkeys[base + s] = tile;
                 a.tvals[base + s] = s_gid[q];
             }
-            wave_hist_add(s_hist, tile & 255u, ok);
-            wave_hist_add(s_hist + kRadix, (tile >> 8) & 255u, ok);
+            if (ok) {
+                atomicAdd(&s_hist[tile & 255u], 1u);
+                atomicAdd(&s_hist[kRadix + ((tile >> 8) & 255u)], 1u);
+            }
         }
         __syncthreads();
         uint32_t* out = a.stripes + (size_t)(blockIdx.x % kStripes) * kHistBins + 4 * kRadix;
@@ -526,17 +567,35 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
     }
 }
 
-// 5. tile ranges from sorted tile ids (ranges zeroed beforehand).
-__global__ void k_ranges(const uint32_t* tkeys, const uint32_t* num_keys, uint32_t cap,
-                         const uint32_t* overflow, uint32_t* ranges, uint32_t ntiles) {
+// 5. tile ranges from sorted tile ids (ranges zeroed beforehand).  Each thread
+// reads kRangeIPT consecutive keys with vector loads, plus one neighbour on
+// each side.
+__global__ __launch_bounds__(256) void k_ranges(const uint32_t* tkeys, const uint32_t* num_keys, uint32_t cap,
+                                                const uint32_t* overflow, uint32_t* ranges, uint32_t ntiles) {
     if (*overflow) return;
     const uint32_t K = min(*num_keys, cap);
-    const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t k = blockIdx.x * blockDim.x + threadIdx.x; k < K; k += stride) {
-        const uint32_t t = tkeys[k];
-        if (t >= ntiles) continue;
-        if (k == 0 || tkeys[k - 1] != t) ranges[2 * t] = k;
-        if (k == K - 1 || tkeys[k + 1] != t) ranges[2 * t + 1] = k + 1;
+    const uint32_t k0 = (blockIdx.x * blockDim.x + threadIdx.x) * (uint32_t)kRangeIPT;
+    if (k0 >= K) return;
+    constexpr uint32_t kNone = 0xffffffffu;  // never a tile id
+    uint32_t t[kRangeIPT];
+    if (k0 + kRangeIPT <= K) {  // tkeys is 256-byte aligned and k0 a multiple of 8
+        const uint4 a = *reinterpret_cast<const uint4*>(tkeys + k0);
+        const uint4 b = *reinterpret_cast<const uint4*>(tkeys + k0 + 4);
+        t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w; t[4] = b.x; t[5] = b.y; t[6] = b.z; t[7] = b.w;
+    } else {
+#pragma unroll
+        for (int u = 0; u < kRangeIPT; ++u) t[u] = k0 + u < K ? tkeys[k0 + u] : kNone;
+    }
+    const uint32_t prev = k0 > 0 ? tkeys[k0 - 1] : kNone;
+    const uint32_t next = k0 + kRangeIPT < K ? tkeys[k0 + kRangeIPT] : kNone;
+#pragma unroll
+    for (int u = 0; u < kRangeIPT; ++u) {
+        const uint32_t k = k0 + u, cur = t[u];
+        if (k >= K || cur >= ntiles) continue;
+        const uint32_t left = u == 0 ? prev : t[u - 1];
+        const uint32_t right = u == kRangeIPT - 1 ? next : t[u + 1];
+        if (left != cur) ranges[2 * cur] = k;
+        if (right != cur) ranges[2 * cur + 1] = k + 1;
     }
 }
 
@@ -594,7 +653,7 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
     uint32_t* tickets = U(L.tickets);
     auto ticket = [&](int pass) { return tickets + (size_t)pass * kTicketGroups * kTicketStride; };
     uint32_t* err = U(L.err);
-    const int key_blocks = (int)std::min<int64_t>(kKeyBlocks, (n + 255) / 256);
+    const int key_blocks = (int)((n + 256 * kKeyIPT - 1) / (256 * kKeyIPT));
     hipLaunchKernelGGL(k_depth_keys, dim3(key_blocks), dim3(256), 0, s, n, depth, tiles_touched, U(L.dkeys0),
                        U(L.dvals0), U(L.stripes));
     // depth sort: 4 passes, 0 -> 1 -> 0 -> 1 -> 0
@@ -611,7 +670,7 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
         p.ticket = ticket(pass);
         p.err = err;
         p.shift = 8 * pass;
-        hipLaunchKernelGGL(k_onesweep<kDepthIPT>, dim3(L.dparts), dim3(kSortThreads), 0, s, p);
+        hipLaunchKernelGGL((k_onesweep<kDepthThreads, kDepthIPT>), dim3(L.dparts), dim3(kDepthThreads), 0, s, p);
     }
     // emit (tile, Gaussian) pairs in depth order, then the stable tile sort.
     // Buffers are routed so the final values land in point_list:
@@ -634,7 +693,7 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
     p.keys_in = U(L.tkeys0); p.vals_in = e.tvals;
     p.keys_out = U(L.tkeys1); p.vals_out = tile_passes == 1 ? point_list : U(L.tvals0);
     p.stripes = U(L.stripes); p.hist_bin = 4 * kRadix; p.status = U(L.tstatus); p.ticket = ticket(4); p.shift = 0;
-    hipLaunchKernelGGL(k_onesweep<kTileIPT>, dim3(L.tparts), dim3(kSortThreads), 0, s, p);
+    hipLaunchKernelGGL((k_onesweep<kTileThreads, kTileIPT>), dim3(L.tparts), dim3(kTileThreads), 0, s, p);
     const uint32_t* tk_final = U(L.tkeys1);
     if (tile_passes == 2) {
         PassArgs p2 = p;
@@ -642,10 +701,10 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
         p2.keys_out = U(L.tkeys0); p2.vals_out = point_list;
         p2.hist_bin = 5 * kRadix; p2.status = U(L.tstatus) + (size_t)L.tparts * kRadix;
         p2.ticket = ticket(5); p2.shift = 8;
-        hipLaunchKernelGGL(k_onesweep<kTileIPT>, dim3(L.tparts), dim3(kSortThreads), 0, s, p2);
+        hipLaunchKernelGGL((k_onesweep<kTileThreads, kTileIPT>), dim3(L.tparts), dim3(kTileThreads), 0, s, p2);
         tk_final = U(L.tkeys0);
     }
-    const uint32_t rblocks = (uint32_t)std::min<int64_t>(2048, (key_capacity + 255) / 256);
+    const uint32_t rblocks = (uint32_t)((key_capacity + 256 * kRangeIPT - 1) / (256 * kRangeIPT));
     hipLaunchKernelGGL(k_ranges, dim3(rblocks), dim3(256), 0, s, tk_final, num_keys_dev, (uint32_t)key_capacity,
                        overflow_dev, tile_ranges, (uint32_t)ntiles);
     return launch_status();
