@@ -700,3 +700,102 @@ void orc_quat_renorm(int N, double* q)
         for (int k = 0; k < 4; ++k) q[4 * i + k] /= n;
     }
 }
+
+/*
+ * Densification and pruning, [P4] D.1-D.3 and E.1 steps 4-5: every 100
+ * iterations, Gaussians whose accumulated position gradient is large are
+ * densified -- split in two along the long axis when Sigma is anisotropic
+ * (large eigenvalue ratio), cloned to a slightly offset copy when isotropic --
+ * and Gaussians of low opacity are removed.  The pages give the rules and
+ * leave the numbers out; prm[] carries them:
+ *   prm[0] grad_threshold: densify when count > 0 and accum / count >= it;
+ *   prm[1] prune_logit:    remove when the opacity logit is below it (the
+ *                          outputs would inherit the opacity and go too);
+ *   prm[2] split_log_gap:  split (else clone) when the largest minus the
+ *                          smallest log-scale is at least it; the eigenvalue
+ *                          ratio of Sigma is exp(2 gap);
+ *   prm[3] split_shrink:   the children's log-scales are the parent's minus it;
+ *   prm[4] split_offset, prm[5] clone_offset: displacements along the long
+ *                          axis e (the column of R for the largest scale
+ *                          s_max, first on ties), in units of s_max.
+ * Each Gaussian is replaced, in index order, by its outputs:
+ *   removed: none;  kept: itself;
+ *   cloned: itself, then a copy at mean + clone_offset s_max e;
+ *   split:  mean + split_offset s_max e, then mean - split_offset s_max e,
+ *           both with log-scales minus split_shrink; rotation, opacity and
+ *           SH copied.
+ * Adam moments (mom_in / mom_out: m of the five groups, then v, or NULL): an
+ * original keeps its own, a copy or a child starts at zero.  action[i] is 0
+ * removed, 1 kept, 2 cloned, 3 split.  K = SH coefficients per Gaussian.
+ * Returns the number of outputs (the arrays hold at least 2 N rows).
+ */
+int orc_densify_apply(int N, int K, const double* prm, const double* means, const double* log_scales,
+                      const double* quats, const double* opacity, const double* sh, const double* accum,
+                      const int* count, const double* const* mom_in, double* o_means, double* o_log_scales,
+                      double* o_quats, double* o_opacity, double* o_sh, double* const* mom_out,
+                      unsigned char* action)
+{
+    const int width[5] = {3, 3, 4, 1, 3 * K};
+    const double* src[5] = {means, log_scales, quats, opacity, sh};
+    double* dst[5] = {o_means, o_log_scales, o_quats, o_opacity, o_sh};
+    int out = 0;
+    for (int i = 0; i < N; ++i) {
+        const double* ls = log_scales + 3 * i;
+        int densify = count[i] > 0 && accum[i] / (double)count[i] >= prm[0];
+        int removed = opacity[i] < prm[1];
+        int a = 0; /* the longest axis */
+        for (int j = 1; j < 3; ++j)
+            if (ls[j] > ls[a]) a = j;
+        double lmin = ls[0];
+        for (int j = 1; j < 3; ++j)
+            if (ls[j] < lmin) lmin = ls[j];
+        int split = ls[a] - lmin >= prm[2];
+        int act = removed ? 0 : (!densify ? 1 : (split ? 3 : 2));
+        action[i] = (unsigned char)act;
+        if (act == 0) continue;
+        int nout = act == 1 ? 1 : 2;
+        /* copy every group, then adjust */
+        for (int o = 0; o < nout; ++o) {
+            for (int g = 0; g < 5; ++g) {
+                for (int c = 0; c < width[g]; ++c) {
+                    dst[g][(size_t)(out + o) * width[g] + c] = src[g][(size_t)i * width[g] + c];
+                    if (mom_in) {
+                        int fresh = act == 3 || o == 1; /* a child or the copy */
+                        for (int mv = 0; mv < 2; ++mv)
+                            mom_out[5 * mv + g][(size_t)(out + o) * width[g] + c] =
+                                fresh ? 0.0 : mom_in[5 * mv + g][(size_t)i * width[g] + c];
+                    }
+                }
+            }
+        }
+        if (act >= 2) {
+            double R[9];
+            orc_quat_to_rot(quats + 4 * i, R);
+            double smax = exp(ls[a]);
+            double e[3] = {R[0 * 3 + a], R[1 * 3 + a], R[2 * 3 + a]};
+            if (act == 2) {
+                for (int c = 0; c < 3; ++c) o_means[(size_t)(out + 1) * 3 + c] = means[3 * i + c] + prm[5] * smax * e[c];
+            } else {
+                for (int c = 0; c < 3; ++c) {
+                    o_means[(size_t)out * 3 + c] = means[3 * i + c] + prm[4] * smax * e[c];
+                    o_means[(size_t)(out + 1) * 3 + c] = means[3 * i + c] - prm[4] * smax * e[c];
+                }
+                for (int o = 0; o < 2; ++o)
+                    for (int c = 0; c < 3; ++c) o_log_scales[(size_t)(out + o) * 3 + c] = ls[c] - prm[3];
+            }
+        }
+        out += nout;
+    }
+    return out;
+}
+
+/* Opacity reset, [P4] E.1 step 6: every 3000 iterations the opacity of every
+   Gaussian is scaled by a factor (0.3 on the pages), written back as a logit. */
+void orc_opacity_reset(int N, double factor, double* logit)
+{
+    for (int i = 0; i < N; ++i) {
+        double s = 1.0 / (1.0 + exp(-logit[i]));
+        double y = factor * s;
+        logit[i] = log(y / (1.0 - y));
+    }
+}

@@ -255,3 +255,71 @@ def render(cam, deg, params, s: Settings = None, dL_dimage=None, brute=False, am
         res["g2d"] = g2d
         res["g3d"] = g3d
     return res
+
+
+@dataclass
+class DensifyParams:
+    """The numbers [P4] D.1-D.3 leave out (see orc_densify_apply).  Values are
+    rounded to float32, as the HIP library receives them."""
+    grad_threshold: float
+    prune_logit: float
+    split_log_gap: float
+    split_shrink: float
+    split_offset: float
+    clone_offset: float
+
+    def array(self):
+        return np.array([np.float32(x) for x in (self.grad_threshold, self.prune_logit, self.split_log_gap,
+                                                 self.split_shrink, self.split_offset, self.clone_offset)],
+                        dtype=np.float64)
+
+
+GROUPS = ("means", "log_scales", "quats", "opacity_logits", "sh")
+
+
+def densify_apply(params, accum, count, dp: DensifyParams, moments=None):
+    """Densify and prune ([P4] D.1-D.3, E.1 steps 4-5).  params: the five groups;
+    moments: None or dict group -> (m, v).  Returns (action, out_params, out_moments)
+    with out arrays of the exact output count."""
+    p = {k: _d(params[k]) for k in GROUPS}
+    N = p["means"].shape[0]
+    K = p["sh"].reshape(N, -1).shape[1] // 3 if N else 1
+    width = {"means": 3, "log_scales": 3, "quats": 4, "opacity_logits": 1, "sh": 3 * K}
+    outs = {k: np.zeros((2 * N, width[k])) for k in GROUPS}
+    action = np.zeros(N, np.uint8)
+    PP = C.POINTER(C.c_double)
+    mom_in = mom_out = None
+    keep = []
+    if moments is not None:
+        ins = [_d(moments[k][0]) for k in GROUPS] + [_d(moments[k][1]) for k in GROUPS]
+        outs_m = [np.zeros((2 * N, width[k])) for k in GROUPS] + [np.zeros((2 * N, width[k])) for k in GROUPS]
+        keep = ins + outs_m
+        mom_in = (PP * 10)(*[_p(a) for a in ins])
+        mom_out = (PP * 10)(*[_p(a) for a in outs_m])
+    prm = dp.array()
+    n_out = lib().orc_densify_apply(
+        C.c_int(N), C.c_int(K), _p(prm), _p(p["means"]), _p(p["log_scales"]), _p(p["quats"]),
+        _p(p["opacity_logits"]), _p(p["sh"]), _p(_d(accum)), _p(np.ascontiguousarray(count, dtype=np.int32), C.c_int),
+        mom_in, _p(outs["means"]), _p(outs["log_scales"]), _p(outs["quats"]), _p(outs["opacity_logits"]),
+        _p(outs["sh"]), mom_out, _p(action, C.c_uint8))
+    out_params = {k: outs[k][:n_out].copy() for k in GROUPS}
+    out_params["opacity_logits"] = out_params["opacity_logits"].reshape(n_out)
+    out_params["sh"] = out_params["sh"].reshape(n_out, K, 3)
+    out_moments = None
+    if moments is not None:
+        out_moments = {}
+        for gi, k in enumerate(GROUPS):
+            m, v = keep[10 + gi][:n_out].copy(), keep[15 + gi][:n_out].copy()
+            if k == "opacity_logits":
+                m, v = m.reshape(n_out), v.reshape(n_out)
+            elif k == "sh":
+                m, v = m.reshape(n_out, K, 3), v.reshape(n_out, K, 3)
+            out_moments[k] = (m, v)
+    return action, out_params, out_moments
+
+
+def opacity_reset(logits, factor):
+    """[P4] E.1 step 6: sigma <- factor sigma, as a logit."""
+    x = _d(logits).copy()
+    lib().orc_opacity_reset(C.c_int(x.size), C.c_double(factor), _p(x))
+    return x
