@@ -47,10 +47,22 @@ class GsAdamState(C.Structure):
                 ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("step", C.c_int32)]
 
 
+class GsDensifyParams(C.Structure):
+    _fields_ = [("grad_threshold", C.c_float), ("prune_logit", C.c_float), ("split_log_gap", C.c_float),
+                ("split_shrink", C.c_float), ("split_offset", C.c_float), ("clone_offset", C.c_float)]
+
+
+class GsGaussianSet(C.Structure):
+    _fields_ = [("means", C.c_void_p), ("log_scales", C.c_void_p), ("quats", C.c_void_p),
+                ("opacity_logits", C.c_void_p), ("sh", C.c_void_p), ("exp_avg", C.c_void_p * 5),
+                ("exp_avg_sq", C.c_void_p * 5), ("densify_accum", C.c_void_p), ("densify_count", C.c_void_p)]
+
+
 SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_project", "gs_shade",
            "gs_bin_workspace_size", "gs_bin_sort", "gs_bin_keys", "gs_render_fwd", "gs_render_fwd_loss",
            "gs_render_bwd", "gs_preprocess_bwd", "gs_preprocess_bwd_adam", "gs_preprocess_bwd_adam_geom",
-           "gs_preprocess_bwd_adam_sh", "gs_image_loss", "gs_densify_accum", "gs_adam_step", "gs_count_pairs"]
+           "gs_preprocess_bwd_adam_sh", "gs_image_loss", "gs_densify_accum", "gs_adam_step", "gs_count_pairs",
+           "gs_densify_workspace_size", "gs_densify", "gs_opacity_reset"]
 PARAM_ORDER = ("means", "log_scales", "quats", "opacity_logits", "sh")
 
 _lib = None
@@ -91,6 +103,10 @@ def load_library(path=LIB_PATH):
     lib.gs_densify_accum.argtypes = [_i32, _vp, _vp, _vp, _vp, _vp]
     lib.gs_adam_step.argtypes = [_i32, P(GsAdamGroup), C.c_float, C.c_float, C.c_float, _i32, _vp]
     lib.gs_count_pairs.argtypes = [P(GsCamera), P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.gs_densify_workspace_size.argtypes = [_i32, P(C.c_size_t)]
+    lib.gs_densify.argtypes = [P(GsDensifyParams), _i32, _i32, P(GsGaussianSet), _i64, P(GsGaussianSet),
+                               _vp, _vp, _vp, _vp, C.c_size_t, _vp]
+    lib.gs_opacity_reset.argtypes = [_i32, C.c_float, _vp, _vp, _vp, _vp]
     for name in SYMBOLS:
         if name not in ("gs_error_string",):
             getattr(lib, name).restype = C.c_int
@@ -373,6 +389,118 @@ def gs_count_pairs(cam, settings, n, tile_ranges, point_list, splats, counts):
                                        _p(tile_ranges, torch.int32), _p(point_list, torch.int32),
                                        _p(splats, torch.float32), _p(counts, torch.int64), _stream())
     _check(rc, "gs_count_pairs")
+
+
+@dataclass
+class DensifyParams:
+    """The numbers the training notes ([P4] D.1-D.3) leave out, as readings.
+
+    grad_threshold: mean |dL/d(u,v)| (pixels, summed image loss) at or above which a
+        Gaussian is densified.  It has no default: it scales with the loss
+        normalisation and the image size.  threshold_for(height) gives the value
+        matching Kerbl et al.'s 2e-4 (a per-pixel mean L1 of weight 0.8, NDC units):
+        2e-4 * 6 * height / 0.8.
+    min_opacity: Gaussians below it are removed (Kerbl et al.: 0.005).
+    split_ratio: eigenvalue ratio of Sigma at or above which a densified Gaussian is
+        split rather than cloned (4: the longest axis twice the shortest).
+    split_factor: the children's scales are the parent's divided by it (Kerbl et al.: 1.6).
+    split_offset, clone_offset: displacements along the longest axis, in units of
+        its scale (children one standard deviation out; the copy a tenth).
+    """
+    grad_threshold: float
+    min_opacity: float = 0.005
+    split_ratio: float = 4.0
+    split_factor: float = 1.6
+    split_offset: float = 1.0
+    clone_offset: float = 0.1
+
+    @staticmethod
+    def threshold_for(height):
+        return 2e-4 * 6.0 * height / 0.8
+
+    def struct(self):
+        return GsDensifyParams(self.grad_threshold, math.log(self.min_opacity / (1.0 - self.min_opacity)),
+                               0.5 * math.log(self.split_ratio), math.log(self.split_factor), self.split_offset,
+                               self.clone_offset)
+
+
+OPACITY_RESET_FACTOR = 0.3  # [P4] E.1 step 6
+
+
+def _set_struct(d, with_stats, name):
+    """GsGaussianSet from a dict: the five groups, optional 'exp_avg' / 'exp_avg_sq' dicts and
+    'densify_accum' / 'densify_count'."""
+    f32 = torch.float32
+    st = GsGaussianSet()
+    for k in PARAM_ORDER:
+        setattr(st, k, _p(d.get(k), f32, f"{name}.{k}"))
+    for i, k in enumerate(PARAM_ORDER):
+        if d.get("exp_avg") is not None:
+            st.exp_avg[i] = _p(d["exp_avg"][k], f32, f"{name}.exp_avg.{k}").value
+            st.exp_avg_sq[i] = _p(d["exp_avg_sq"][k], f32, f"{name}.exp_avg_sq.{k}").value
+    if with_stats:
+        st.densify_accum = _p(d.get("densify_accum"), f32, f"{name}.densify_accum")
+        st.densify_count = _p(d.get("densify_count"), torch.int32, f"{name}.densify_count")
+    return st
+
+
+def gs_densify_workspace_size(n):
+    b = C.c_size_t()
+    _check(load_library().gs_densify_workspace_size(n, C.byref(b)), "gs_densify_workspace_size")
+    return b.value
+
+
+def gs_densify(dp, sh_degree, inp, capacity, out, n_out, overflow, workspace, action=None):
+    """inp / out: dicts as _set_struct takes; out holds `capacity` rows."""
+    n = inp["means"].shape[0]
+    rc = load_library().gs_densify(
+        C.byref(dp.struct() if isinstance(dp, DensifyParams) else dp), n, sh_degree,
+        C.byref(_set_struct(inp, True, "in")), capacity, C.byref(_set_struct(out, True, "out")),
+        _p(n_out, torch.int32, "n_out"), _p(overflow, torch.int32, "overflow"), _p(action, torch.uint8, "action"),
+        _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _check(rc, "gs_densify")
+
+
+def densify_and_prune(dp, sh_degree, params, densify_accum, densify_count, exp_avg=None, exp_avg_sq=None):
+    """Allocates outputs for the worst case (2 n rows), runs gs_densify and returns
+    (params, exp_avg, exp_avg_sq, densify_accum, densify_count, action), each trimmed to
+    the output count (exp_avg / exp_avg_sq None when not given).  Synchronises once to
+    read the count."""
+    n = params["means"].shape[0]
+    dev = params["means"].device
+    cap = 2 * n
+
+    def like(t):
+        return torch.empty((cap,) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+
+    out = {k: like(params[k]) for k in PARAM_ORDER}
+    if exp_avg is not None:
+        out["exp_avg"] = {k: like(exp_avg[k]) for k in PARAM_ORDER}
+        out["exp_avg_sq"] = {k: like(exp_avg_sq[k]) for k in PARAM_ORDER}
+    out["densify_accum"] = like(densify_accum)
+    out["densify_count"] = like(densify_count)
+    inp = dict(params, densify_accum=densify_accum, densify_count=densify_count, exp_avg=exp_avg,
+               exp_avg_sq=exp_avg_sq)
+    n_out = torch.zeros(1, dtype=torch.int32, device=dev)
+    overflow = torch.zeros(1, dtype=torch.int32, device=dev)
+    action = torch.empty(n, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(gs_densify_workspace_size(n), 1) + 256, dtype=torch.uint8, device=dev)
+    off = (-ws.data_ptr()) % 256
+    gs_densify(dp, sh_degree, inp, cap, out, n_out, overflow, ws[off:off + gs_densify_workspace_size(n)], action)
+    m = int(n_out.item())
+    if int(overflow.item()):
+        raise GsError("gs_densify overflowed a 2 n capacity")
+    trim = {k: out[k][:m] for k in PARAM_ORDER}
+    ea = {k: out["exp_avg"][k][:m] for k in PARAM_ORDER} if exp_avg is not None else None
+    eq = {k: out["exp_avg_sq"][k][:m] for k in PARAM_ORDER} if exp_avg is not None else None
+    return trim, ea, eq, out["densify_accum"][:m], out["densify_count"][:m], action
+
+
+def gs_opacity_reset(opacity_logits, factor=OPACITY_RESET_FACTOR, exp_avg=None, exp_avg_sq=None):
+    f32 = torch.float32
+    rc = load_library().gs_opacity_reset(opacity_logits.numel(), factor, _p(opacity_logits, f32, "opacity_logits"),
+                                         _p(exp_avg, f32, "exp_avg"), _p(exp_avg_sq, f32, "exp_avg_sq"), _stream())
+    _check(rc, "gs_opacity_reset")
 
 
 # ---------------------------------------------------------------------------

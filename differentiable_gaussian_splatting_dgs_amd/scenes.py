@@ -236,3 +236,35 @@ def random_small(seed, n=48, width=48, height=40, f=50.0, sh_degree=3, scale_mu=
     dL = rng.standard_normal((3, height, width))
     m, s, q, o, c, g = _f32(means, log_scales, quats, opac, sh, dL)
     return Scene(f"random{seed}", cam, sh_degree, m, s, q, o, c, dL_dimage=g)
+
+
+def densify_case(seed, n, sh_degree=3, with_moments=True):
+    """Inputs of a densification step: a Gaussian set after some training views.
+
+    Parameters as in the scenes above (log-scales spread so both isotropic and
+    elongated Gaussians occur), Adam moments, and the densification statistic:
+    count = views that saw the Gaussian (0-4), accum = a sum of per-view gradient
+    norms (exponential, so a tail of large mean gradients exists).  Returns a dict
+    with the five groups, 'exp_avg' / 'exp_avg_sq' (dicts) or None, 'densify_accum'
+    float32 [n] and 'densify_count' int32 [n].
+    """
+    rng = np.random.default_rng(seed)
+    K = (sh_degree + 1) ** 2
+    means = rng.normal(0.0, 1.0, (n, 3))
+    log_scales = rng.normal(-3.5, 0.3, (n, 1)) + rng.normal(0.0, 0.6, (n, 3))
+    quats = _unit_rows(rng, n, 4)
+    opacity = rng.normal(-1.0, 2.5, n)
+    sh = rng.normal(0.0, 0.3, (n, K, 3))
+    count = rng.integers(0, 5, n)
+    accum = rng.exponential(1.0, n) * count
+    out = dict(means=means, log_scales=log_scales, quats=quats, opacity_logits=opacity, sh=sh)
+    out = {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in out.items()}
+    out["densify_accum"] = accum.astype(np.float32)
+    out["densify_count"] = count.astype(np.int32)
+    out["exp_avg"] = out["exp_avg_sq"] = None
+    if with_moments:
+        out["exp_avg"] = {k: rng.normal(0.0, 1e-3, np.shape(out[k])).astype(np.float32)
+                          for k in ("means", "log_scales", "quats", "opacity_logits", "sh")}
+        out["exp_avg_sq"] = {k: rng.uniform(0.0, 1e-5, np.shape(out[k])).astype(np.float32)
+                             for k in ("means", "log_scales", "quats", "opacity_logits", "sh")}
+    return out

@@ -347,6 +347,81 @@ int gs_preprocess_bwd_adam_sh(int32_t n, int32_t sh_degree, float* sh, const uin
                               void* stream);
 
 /*
+ * Densification, pruning and opacity reset ([P4] D.1: Gaussians whose
+ * accumulated position gradient is large are densified, a split replacing one
+ * Gaussian by two smaller ones; D.2: split along the long axis when Sigma is
+ * anisotropic (large eigenvalue ratio), clone to a slightly offset copy when
+ * isotropic; D.3: remove Gaussians of low opacity; E.1 steps 4-6: densify
+ * and prune every 100 iterations, scale every opacity by 0.3 every 3000).
+ * The numbers the pages leave out are the fields below.
+ */
+typedef struct gs_densify_params {
+    float grad_threshold; /* densify when count > 0 and accum / count >= this (mean |dL/d(u,v)|, pixels) */
+    float prune_logit;    /* remove when the opacity logit is below this */
+    float split_log_gap;  /* split (else clone) when max - min log-scale >= this; Sigma's eigenvalue ratio is exp(2 gap) */
+    float split_shrink;   /* the children's log-scales are the parent's minus this (log of the shrink factor) */
+    float split_offset;   /* children at mean +/- split_offset * s_max * e (e: the axis of the largest scale s_max) */
+    float clone_offset;   /* the copy at mean + clone_offset * s_max * e */
+} gs_densify_params;
+
+/* A set of Gaussians: the five parameter groups ([n,3], [n,3], [n,4] 16-byte
+   aligned, [n], [n, (deg+1)^2, 3] 16-byte aligned), optionally their Adam
+   moments (all ten pointers, in the group order, the quats and sh moments
+   16-byte aligned, or all NULL) and the densification statistic
+   (densify_accum [n] float32, densify_count [n] int32, both or neither). */
+typedef struct gs_gaussian_set {
+    float* means;
+    float* log_scales;
+    float* quats;
+    float* opacity_logits;
+    float* sh;
+    float* exp_avg[5];
+    float* exp_avg_sq[5];
+    float* densify_accum;
+    int32_t* densify_count;
+} gs_gaussian_set;
+
+/* Bytes of workspace gs_densify needs for n Gaussians. */
+int gs_densify_workspace_size(int32_t n, size_t* bytes);
+
+/*
+ * gs_densify -- densify and prune, out of place.  Gaussian i of `in` is
+ * replaced, in index order, by consecutive rows of `out`:
+ *   removed (opacity logit < prune_logit):             none;
+ *   kept (not densified):                              itself;
+ *   cloned (densified, max - min log-scale < gap):     itself, then a copy at
+ *                                                      mean + clone_offset s_max e;
+ *   split (densified, gap reached):                    mean + split_offset s_max e,
+ *                                                      then mean - split_offset s_max e,
+ *                                                      log-scales minus split_shrink.
+ * Rotation, opacity and SH are copied.  e is the column of R(q / |q|) for the
+ * largest log-scale (the first on ties).  The decisions compare the float32
+ * inputs exactly (accum / count in double).  An original keeps its Adam
+ * moments; a copy or a child gets zero moments.  Every output's statistic
+ * (when out has one) is zero.  in needs the statistic.  Each side has all ten
+ * moments or none; with capacity > 0 the two sides must agree (with capacity
+ * 0 nothing is written and out's pointers are not used).
+ * Outputs: *n_out_dev = number of output rows (at most 2 n); if it exceeds
+ * capacity (rows the out arrays hold), *overflow_dev = 1 and nothing else is
+ * written; else *overflow_dev = 0.  action [n] uint8 (optional) receives 0
+ * removed, 1 kept, 2 cloned, 3 split.  `in` and `out` must not overlap.
+ * workspace: device scratch of gs_densify_workspace_size() bytes, 256-byte
+ * aligned, contents on entry irrelevant (may be NULL when n == 0).
+ */
+int gs_densify(const gs_densify_params* dp, int32_t n, int32_t sh_degree, const gs_gaussian_set* in,
+               int64_t capacity, const gs_gaussian_set* out, uint32_t* n_out_dev, uint32_t* overflow_dev,
+               uint8_t* action, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gs_opacity_reset -- [P4] E.1 step 6: opacity <- factor * opacity for every
+ * Gaussian (factor in (0, 1]; the pages use 0.3), written back in place as a
+ * logit.  exp_avg / exp_avg_sq (optional, [n]): the opacity group's Adam
+ * moments, set to zero, as for a parameter that starts afresh.
+ */
+int gs_opacity_reset(int32_t n, float factor, float* opacity_logits, float* exp_avg, float* exp_avg_sq,
+                     void* stream);
+
+/*
  * gs_count_pairs -- diagnostic pair counts of a forward pass (device int64
  * counters, overwritten): counts[0] = evaluated pairs (entries walked by the
  * forward up to and including the one that stops a pixel), counts[1] = sum of
