@@ -212,6 +212,54 @@ class Step:
                                   g["log_scales"], g["quats"], g["opacity_logits"], g["sh"])
 
 
+def densify_measure(st, reps):
+    """gs_densify (densify, split or clone, prune) on the trained state: the parameters, Adam moments
+    and the statistic the steps above accumulated.  Out of place, so every repetition does the same
+    work.  Algorithmic bytes: every surviving Gaussian's row read once (parameters, moments,
+    statistic), a removed one's decision fields (log-scales, opacity, statistic: 24 B), every output
+    row written once."""
+    gs, torch, sc = st.gs, st.torch, st.sc
+    n, K = sc.n, (sc.sh_degree + 1) ** 2
+    dp = gs.DensifyParams(gs.DensifyParams.threshold_for(sc.cam.height))
+    cap = 2 * n
+
+    def like(t):
+        return torch.empty((cap,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+
+    inp = dict(st.p, densify_accum=st.accum, densify_count=st.count, exp_avg=st.m, exp_avg_sq=st.v)
+    out = {k: like(v) for k, v in st.p.items()}
+    out["exp_avg"] = {k: like(v) for k, v in st.m.items()}
+    out["exp_avg_sq"] = {k: like(v) for k, v in st.v.items()}
+    out["densify_accum"], out["densify_count"] = like(st.accum), like(st.count)
+    n_out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    action = torch.empty(n, dtype=torch.uint8, device="cuda")
+    wsz = gs.gs_densify_workspace_size(n)
+    ws = torch.empty(wsz + 256, dtype=torch.uint8, device="cuda")
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + wsz]
+    gs.gs_densify(dp, sc.sh_degree, inp, cap, out, n_out, ovf, ws, action)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record()
+        gs.gs_densify(dp, sc.sh_degree, inp, cap, out, n_out, ovf, ws, action)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    acts = np.bincount(action.cpu().numpy(), minlength=4)
+    rows = int(n_out.item())
+    row_bytes = 4 * (2 * 3 + 4 + 1 + 3 * K) * 3 + 8          # parameters, two moments, statistic
+    nbytes = row_bytes * (n - int(acts[0])) + 24 * int(acts[0]) + row_bytes * rows
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del out, inp
+    return dict(ms=round(ms, 4), n_in=n, n_out=rows,
+                actions=dict(removed=int(acts[0]), kept=int(acts[1]), cloned=int(acts[2]), split=int(acts[3])),
+                grad_threshold=round(dp.grad_threshold, 4), algorithmic_bytes=int(nbytes),
+                roofline=dict(bound="hbm", achieved=round(gbs, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(gbs / PEAK_HBM_GBS, 4)))
+
+
 def cpu_baseline(sc, frac, seed=0):
     """The oracle on a bounded sample of the same step, scaled to blend pairs/s.
 
@@ -312,6 +360,7 @@ def main():
         pe[i][1].record()
     torch.cuda.synchronize()
     pbwd_ms = float(np.mean([a.elapsed_time(b) for a, b in pe]))
+    dens = densify_measure(st, max(3, min(args.steps, 10)))
     stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, name in enumerate(st.stages)}
     ms = elapsed * 1e3 / args.steps
@@ -355,7 +404,8 @@ def main():
                                "intervals"}[st.overlap or "none"],
                pairs=dict(fwd_evaluated=float(p_fwd), bwd_walked=float(p_bwd), blended=float(p_blend),
                           keys=int(st.rast.num_keys.item())),
-               roofline=roof)
+               roofline=roof,
+               densify=dens)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         cb = cpu_baseline(sc, args.cpu_tile_fraction)
