@@ -18,11 +18,12 @@
 //      L2-resident words); the last partition writes the row count and the
 //      overflow flag.
 //   3. k_dens_write<K>: a block of kWriteBlock Gaussians owns one contiguous
-//      run of output rows.  Each thread writes its Gaussian's narrow groups
-//      (mean, log-scales, quaternion, opacity, their moments, the statistic);
-//      then the block copies the SH coefficients and their moments row after
-//      row with coalesced float4 loads and stores, which carry most of the
-//      bytes (3 x 48 of the 177 floats per row at degree 3).
+//      run of output rows.  Each thread records where its Gaussian's rows
+//      come from (and, for a split or a clone, the displacement along the
+//      long axis); then the block writes every array over the run with
+//      coalesced accesses, streaming the float4-wide ones (the quaternion and
+//      the SH coefficients with their moments: 3 x 52 of the 177 floats per
+//      row at degree 3) past the caches.
 #include "gs_internal.h"
 
 namespace gs {
@@ -159,114 +160,126 @@ __device__ inline void rot_column(const float4 q4, int axis, float e[3]) {
     }
 }
 
-// Copies `width` floats of one row (or writes zeros).
-template <int W>
-__device__ inline void put_row(float* dst, const float* src, bool zero) {
-#pragma unroll
-    for (int c = 0; c < W; ++c) dst[c] = zero ? 0.f : src[c];
+typedef float v4f __attribute__((ext_vector_type(4)));
+// Streaming (non-temporal) float4 access: every byte is read or written once.
+__device__ __forceinline__ float4 nt_ld4(const float4* p) {
+    const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_st4(float4 v, float4* p) {
+    v4f w;
+    w.x = v.x; w.y = v.y; w.z = v.z; w.w = v.w;
+    __builtin_nontemporal_store(w, reinterpret_cast<v4f*>(p));
+}
+
+// Per output row of a write block: its source Gaussian (| kFresh for a copy
+// or a child), the displacement of its mean and the shift of its log-scales.
+struct RowInfo {
+    uint32_t src[2 * kWriteBlock];
+    float disp[2 * kWriteBlock][3];
+    float shift[2 * kWriteBlock];
+};
+
+// The block's rows [obase, obase + nrows) of one array of W floats per row,
+// from the source rows.  MODE 0: copy; 1: copy, zero for fresh rows (Adam
+// moments); 2: add the row's mean displacement; 3: subtract the row's
+// log-scale shift; 4: zero (the statistic).  Writes are contiguous and
+// coalesced; reads follow the source rows, which are consecutive too.
+template <int W, int MODE, typename T>
+__device__ inline void copy_rows(const T* src, T* dst, uint32_t obase, uint32_t nrows, const RowInfo& ri) {
+    if constexpr (W % 4 == 0 && MODE <= 1 && sizeof(T) == 4) {
+        constexpr int W4 = W / 4;
+        const float4* s4 = reinterpret_cast<const float4*>(src);
+        float4* d4 = reinterpret_cast<float4*>(dst) + (uint64_t)obase * W4;
+        for (uint32_t e = threadIdx.x; e < nrows * W4; e += kWriteBlock) {
+            const uint32_t r = e / W4, c = e - r * W4;
+            const uint32_t sv = ri.src[r];
+            const bool z = MODE == 1 && (sv & kFresh);
+            nt_st4(z ? make_float4(0.f, 0.f, 0.f, 0.f) : nt_ld4(s4 + (uint64_t)(sv & ~kFresh) * W4 + c), d4 + e);
+        }
+    } else {
+        T* d = dst + (uint64_t)obase * W;
+        for (uint32_t e = threadIdx.x; e < nrows * W; e += kWriteBlock) {
+            const uint32_t r = e / W, c = e - r * W;
+            const uint32_t sv = ri.src[r];
+            T v = T(0);
+            if (MODE != 4) v = src[(uint64_t)(sv & ~kFresh) * W + c];
+            if (MODE == 1 && (sv & kFresh)) v = T(0);
+            if constexpr (MODE == 2) v += ri.disp[r][c];
+            if constexpr (MODE == 3) v -= ri.shift[r];
+            d[e] = v;
+        }
+    }
 }
 
 // 3. the outputs of kWriteBlock consecutive Gaussians.  K = SH coefficients.
+// Each thread records its Gaussian's output rows in RowInfo (a split or a
+// clone also computes the long axis and its displacement); the block then
+// writes every array over its contiguous run of output rows.
 template <int K>
 __global__ __launch_bounds__(kWriteBlock) void k_dens_write(DensArgs a) {
-    constexpr int W = 3 * K;                    // floats per SH row
-    __shared__ uint32_t s_src[2 * kWriteBlock];  // output row -> source Gaussian | kFresh
+    __shared__ RowInfo ri;
     if (*a.overflow) return;  // uniform: nothing is written past the capacity
     const int64_t g0 = (int64_t)blockIdx.x * kWriteBlock;
     const int64_t g = g0 + threadIdx.x;
     const int64_t glast = min((int64_t)a.n, g0 + kWriteBlock) - 1;
     const uint32_t obase = a.off[g0];
     const uint32_t nrows = a.off[glast] + rows_of(a.act[glast]) - obase;  // <= 2 kWriteBlock
-    const bool moments = a.min[0] != nullptr;
     if (g < a.n) {
         const uint32_t act = a.act[g];
-        const uint32_t o = a.off[g];
+        const uint32_t o = a.off[g] - obase;
         const uint32_t nr = rows_of(act);
-        for (uint32_t r = 0; r < nr; ++r) {
-            const bool fresh = act == kSplit || r == 1;  // a child or the copy
-            s_src[o - obase + r] = (uint32_t)g | (fresh ? kFresh : 0u);
-        }
-        if (nr) {
-            const float* m = a.in[0] + 3 * g;
+        // x + (-0) == x for every x, so an undisplaced mean is copied bit for bit
+        float d[2][3] = {{-0.f, -0.f, -0.f}, {-0.f, -0.f, -0.f}};
+        if (act == kCloned || act == kSplit) {
             const float* ls = a.in[1] + 3 * g;
-            const float4 q = reinterpret_cast<const float4*>(a.in[2])[g];
-            const float op = a.in[3][g];
-            float mu[2][3], l[3];
+            const float l[3] = {ls[0], ls[1], ls[2]};
+            int axis = 0;
+            if (l[1] > l[axis]) axis = 1;
+            if (l[2] > l[axis]) axis = 2;
+            float e[3];
+            rot_column(reinterpret_cast<const float4*>(a.in[2])[g], axis, e);
+            const float smax = expf(l[axis]);
+            if (act == kCloned) {
+                const float dd = a.clone_offset * smax;
 #pragma unroll
-            for (int c = 0; c < 3; ++c) { mu[0][c] = m[c]; mu[1][c] = m[c]; l[c] = ls[c]; }
-            if (act == kCloned || act == kSplit) {
-                int axis = 0;
-                if (l[1] > l[axis]) axis = 1;
-                if (l[2] > l[axis]) axis = 2;
-                float e[3];
-                rot_column(q, axis, e);
-                const float smax = expf(l[axis]);
-                if (act == kCloned) {
-                    const float d = a.clone_offset * smax;
-#pragma unroll
-                    for (int c = 0; c < 3; ++c) mu[1][c] = m[c] + d * e[c];
-                } else {
-                    const float d = a.split_offset * smax;
-#pragma unroll
-                    for (int c = 0; c < 3; ++c) {
-                        mu[0][c] = m[c] + d * e[c];
-                        mu[1][c] = m[c] - d * e[c];
-                        l[c] = l[c] - a.split_shrink;
-                    }
-                }
-            }
-            for (uint32_t r = 0; r < nr; ++r) {
-                const uint64_t row = (uint64_t)o + r;
-                const bool fresh = act == kSplit || r == 1;
+                for (int c = 0; c < 3; ++c) d[1][c] = dd * e[c];
+            } else {
+                const float dd = a.split_offset * smax;
 #pragma unroll
                 for (int c = 0; c < 3; ++c) {
-                    a.out[0][3 * row + c] = mu[r][c];
-                    a.out[1][3 * row + c] = l[c];
+                    d[0][c] = dd * e[c];
+                    d[1][c] = -(dd * e[c]);
                 }
-                reinterpret_cast<float4*>(a.out[2])[row] = q;
-                a.out[3][row] = op;
-                if (moments) {
-#pragma unroll
-                    for (int mv = 0; mv < 2; ++mv) {
-                        put_row<3>(a.mout[5 * mv + 0] + 3 * row, a.min[5 * mv + 0] + 3 * g, fresh);
-                        put_row<3>(a.mout[5 * mv + 1] + 3 * row, a.min[5 * mv + 1] + 3 * g, fresh);
-                        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-                        reinterpret_cast<float4*>(a.mout[5 * mv + 2])[row] =
-                            fresh ? z : reinterpret_cast<const float4*>(a.min[5 * mv + 2])[g];
-                        a.mout[5 * mv + 3][row] = fresh ? 0.f : a.min[5 * mv + 3][g];
-                    }
-                }
-                if (a.oaccum) a.oaccum[row] = 0.f;
-                if (a.ocount) a.ocount[row] = 0;
             }
+        }
+        for (uint32_t r = 0; r < nr; ++r) {
+            const bool fresh = act == kSplit || r == 1;  // a child or the copy
+            ri.src[o + r] = (uint32_t)g | (fresh ? kFresh : 0u);
+#pragma unroll
+            for (int c = 0; c < 3; ++c) ri.disp[o + r][c] = d[r][c];
+            ri.shift[o + r] = act == kSplit ? a.split_shrink : 0.f;
         }
     }
     __syncthreads();
-    // the wide rows: SH, then its two moments, nrows x W floats each, contiguous in the output
-    const int narr = moments ? 3 : 1;
-    for (int t = 0; t < narr; ++t) {
-        const float* src = t == 0 ? a.in[4] : a.min[t == 1 ? 4 : 9];
-        float* dst = t == 0 ? a.out[4] : a.mout[t == 1 ? 4 : 9];
-        const bool zero_fresh = t != 0;
-        if constexpr (W % 4 == 0) {
-            constexpr int W4 = W / 4;
-            const float4* s4 = reinterpret_cast<const float4*>(src);
-            float4* d4 = reinterpret_cast<float4*>(dst) + (uint64_t)obase * W4;
-            for (uint32_t e = threadIdx.x; e < nrows * W4; e += kWriteBlock) {
-                const uint32_t r = e / W4, c = e - r * W4;
-                const uint32_t sv = s_src[r];
-                const bool z = zero_fresh && (sv & kFresh);
-                d4[e] = z ? make_float4(0.f, 0.f, 0.f, 0.f) : s4[(uint64_t)(sv & ~kFresh) * W4 + c];
-            }
-        } else {
-            float* d = dst + (uint64_t)obase * W;
-            for (uint32_t e = threadIdx.x; e < nrows * W; e += kWriteBlock) {
-                const uint32_t r = e / W, c = e - r * W;
-                const uint32_t sv = s_src[r];
-                const bool z = zero_fresh && (sv & kFresh);
-                d[e] = z ? 0.f : src[(uint64_t)(sv & ~kFresh) * W + c];
-            }
+    copy_rows<3, 2>(a.in[0], a.out[0], obase, nrows, ri);
+    copy_rows<3, 3>(a.in[1], a.out[1], obase, nrows, ri);
+    copy_rows<4, 0>(a.in[2], a.out[2], obase, nrows, ri);
+    copy_rows<1, 0>(a.in[3], a.out[3], obase, nrows, ri);
+    copy_rows<3 * K, 0>(a.in[4], a.out[4], obase, nrows, ri);
+    if (a.min[0]) {
+#pragma unroll
+        for (int mv = 0; mv < 2; ++mv) {
+            copy_rows<3, 1>(a.min[5 * mv + 0], a.mout[5 * mv + 0], obase, nrows, ri);
+            copy_rows<3, 1>(a.min[5 * mv + 1], a.mout[5 * mv + 1], obase, nrows, ri);
+            copy_rows<4, 1>(a.min[5 * mv + 2], a.mout[5 * mv + 2], obase, nrows, ri);
+            copy_rows<1, 1>(a.min[5 * mv + 3], a.mout[5 * mv + 3], obase, nrows, ri);
+            copy_rows<3 * K, 1>(a.min[5 * mv + 4], a.mout[5 * mv + 4], obase, nrows, ri);
         }
+    }
+    if (a.oaccum) {
+        copy_rows<1, 4>(a.oaccum, a.oaccum, obase, nrows, ri);
+        copy_rows<1, 4>(a.ocount, a.ocount, obase, nrows, ri);
     }
 }
 
