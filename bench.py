@@ -15,7 +15,8 @@ they run beside more than they hide.
 `fwd_bwd` reports the rasterizer on the same scene and state: preprocess,
 binning, forward (with the per-pixel loss gradient the backward starts from),
 backward blend and the unfused 2D->3D backward that writes the 3D gradients
-(no optimizer).
+(no optimizer).  `densify` times the densify / split / clone / prune pass
+(run every 100 training steps, so not part of the step) on the trained state.
 """
 from __future__ import annotations
 
