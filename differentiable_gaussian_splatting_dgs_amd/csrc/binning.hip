@@ -386,8 +386,11 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
 }
 
 struct EmitArgs {
-    int32_t n;
+    int32_t n;               // Gaussians over all views
     int32_t tiles_x;
+    int32_t n_view;          // Gaussians per view (batched views: entry v n_view + i is Gaussian i in view v)
+    int32_t tiles_y;         // tile rows per view
+    int32_t views;
     uint32_t cap;
     uint32_t eparts;
     uint32_t xblocks;
@@ -516,7 +519,14 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
                 const uint32_t g = a.order[j];
                 s_goff[q] = go;
                 s_gid[q] = g;
-                s_rect[q] = reinterpret_cast<const uint2*>(a.rect)[g];
+                uint2 r = reinterpret_cast<const uint2*>(a.rect)[g];
+                if (a.views > 1) {
+                    // view v's tiles follow the earlier views' (v tiles_y rows down): shift the rect's rows
+                    const uint32_t dy = (g / (uint32_t)a.n_view) * (uint32_t)a.tiles_y;
+                    r.x += dy << 16;
+                    r.y += dy << 16;
+                }
+                s_rect[q] = r;
                 // head: the slot where this Gaussian's run starts (0 for the first)
                 const uint32_t h = q == 0 ? 0u : go - base;
                 if (h < (uint32_t)kSlots) s_owner[h] = q;
@@ -613,26 +623,41 @@ __global__ void k_keys(const uint32_t* ranges, const uint32_t* list, const float
 
 using namespace gs;
 
-extern "C" int gs_bin_workspace_size(int32_t n, const gs_camera* cam, int64_t key_capacity, size_t* bytes) {
-    if (n < 0 || !camera_ok(cam) || key_capacity < 0 || !bytes) return GS_EINVAL;
-    if (key_capacity > (int64_t)kValMask) return GS_ECAPACITY;
-    *bytes = make_layout(n, key_capacity).total;
+extern "C" int gs_bin_workspace_size_views(int32_t n, const gs_camera* cams, int32_t views, int64_t key_capacity,
+                                           size_t* bytes) {
+    if (n < 0 || !views_ok(cams, views) || key_capacity < 0 || !bytes) return GS_EINVAL;
+    if (key_capacity > (int64_t)kValMask || (int64_t)views * n > (int64_t)kValMask) return GS_ECAPACITY;
+    *bytes = make_layout(views * n, key_capacity).total;
     return GS_OK;
+}
+
+extern "C" int gs_bin_workspace_size(int32_t n, const gs_camera* cam, int64_t key_capacity, size_t* bytes) {
+    return gs_bin_workspace_size_views(n, cam, 1, key_capacity, bytes);
 }
 
 extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, const int16_t* rect,
                            const int32_t* tiles_touched, int64_t key_capacity, uint32_t* point_list,
                            uint32_t* tile_ranges, uint32_t* num_keys_dev, uint32_t* overflow_dev,
                            void* workspace, size_t workspace_bytes, void* stream) {
-    if (n < 0 || !camera_ok(cam) || key_capacity < 0) return GS_EINVAL;
-    if (key_capacity > (int64_t)kValMask || n > (int32_t)kValMask) return GS_ECAPACITY;
+    return gs_bin_sort_views(cam, 1, n, depth, rect, tiles_touched, key_capacity, point_list, tile_ranges,
+                             num_keys_dev, overflow_dev, workspace, workspace_bytes, stream);
+}
+
+extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n_view, const float* depth,
+                                 const int16_t* rect, const int32_t* tiles_touched, int64_t key_capacity,
+                                 uint32_t* point_list, uint32_t* tile_ranges, uint32_t* num_keys_dev,
+                                 uint32_t* overflow_dev, void* workspace, size_t workspace_bytes, void* stream) {
+    if (n_view < 0 || !views_ok(cams, views) || key_capacity < 0) return GS_EINVAL;
+    if (key_capacity > (int64_t)kValMask || (int64_t)views * n_view > (int64_t)kValMask) return GS_ECAPACITY;
+    const gs_camera* cam = cams;
+    const int32_t n = views * n_view;  // all views' Gaussians, view-major
     if (!tile_ranges || !num_keys_dev || !overflow_dev || !workspace) return GS_EINVAL;
     if (n > 0 && (!depth || !rect || !tiles_touched)) return GS_EINVAL;
     if (key_capacity > 0 && !point_list) return GS_EINVAL;
     if (!aligned16(rect) || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return GS_EALIGN;
     const Layout L = make_layout(n, key_capacity);
     if (workspace_bytes < L.total) return GS_EWORKSPACE;
-    const int ntiles = tiles_x(cam) * tiles_y(cam);
+    const int ntiles = views * tiles_x(cam) * tiles_y(cam);
     const int tile_passes = ntiles <= 256 ? 1 : (ntiles <= 65536 ? 2 : 3);
     if (tile_passes > 2) return GS_ECAPACITY;
     hipStream_t s = as_stream(stream);
@@ -677,7 +702,8 @@ extern "C" int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, 
     //   1 pass : emit -> (tkeys0, tvals0) -> (tkeys1, point_list)
     //   2 passes: emit -> (tkeys0, point_list) -> (tkeys1, tvals0) -> (tkeys0, point_list)
     EmitArgs e;
-    e.n = n; e.tiles_x = tiles_x(cam); e.cap = (uint32_t)key_capacity; e.eparts = L.eparts;
+    e.n = n; e.tiles_x = tiles_x(cam); e.n_view = n_view; e.tiles_y = tiles_y(cam); e.views = views;
+    e.cap = (uint32_t)key_capacity; e.eparts = L.eparts;
     e.xblocks = L.xblocks;
     e.order = dv[0]; e.rect = rect; e.tt = tiles_touched;
     e.part = U(L.etotal); e.goff = U(L.goff); e.bstart = U(L.bstart);

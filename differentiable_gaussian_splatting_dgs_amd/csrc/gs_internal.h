@@ -24,6 +24,14 @@ inline bool camera_ok(const gs_camera* c) {
            c->fy > 0;
 }
 
+// views cameras of one image size (the batched entry points take an array).
+inline bool views_ok(const gs_camera* cams, int32_t views) {
+    if (!cams || views < 1 || views > GS_MAX_VIEWS) return false;
+    for (int v = 0; v < views; ++v)
+        if (!camera_ok(cams + v) || cams[v].width != cams[0].width || cams[v].height != cams[0].height) return false;
+    return true;
+}
+
 inline int tiles_x(const gs_camera* c) { return (c->width + kTile - 1) / kTile; }
 inline int tiles_y(const gs_camera* c) { return (c->height + kTile - 1) / kTile; }
 
@@ -48,7 +56,8 @@ inline CamArgs cam_args(const gs_camera* c) {
 struct BlendArgs {
     float alpha_min, alpha_max, T_min;
     float bg[3];
-    int32_t width, height, tiles_x, tiles_y;
+    int32_t width, height, tiles_x, tiles_y;  // of one view
+    int32_t views;                            // tile t is tile t mod (tiles_x tiles_y) of view t / (tiles_x tiles_y)
 };
 
 inline BlendArgs blend_args(const gs_camera* c, const gs_settings* s) {
@@ -58,6 +67,7 @@ inline BlendArgs blend_args(const gs_camera* c, const gs_settings* s) {
     b.T_min = (float)s->T_min;
     for (int i = 0; i < 3; ++i) b.bg[i] = (float)s->bg[i];
     b.width = c->width; b.height = c->height;
+    b.views = 1;
     b.tiles_x = tiles_x(c); b.tiles_y = tiles_y(c);
     return b;
 }

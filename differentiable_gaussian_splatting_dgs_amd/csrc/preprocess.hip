@@ -15,7 +15,8 @@ namespace gs {
 namespace {
 
 struct PreArgs {
-    CamArgs cam;
+    CamArgs cams[GS_MAX_VIEWS];  // views of one size; outputs are [views, n, ...]
+    int32_t views;
     double near_z, alpha_min, dilation;
     int32_t n;
     const float* means;
@@ -119,17 +120,22 @@ __global__ __launch_bounds__(kPreBlock) void k_shade(PreArgs a) {
     if (i >= a.n) return;
     float shv[J];
     load_sh<DEG, VEC>(a.sh, i, shv);
-    double rgb[3];
-    uint8_t cm;
-    shade<DEG>(a.cam, a.means[3 * i], a.means[3 * i + 1], a.means[3 * i + 2], shv, rgb, cm);
-    reinterpret_cast<float4*>(a.splats + (size_t)i * GS_SPLAT_STRIDE)[2] =
-        make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
-    a.clamp[i] = cm;
+    const double mx = a.means[3 * i], my = a.means[3 * i + 1], mz = a.means[3 * i + 2];
+    for (int view = 0; view < a.views; ++view) {
+        const size_t o = (size_t)view * a.n + i;
+        double rgb[3];
+        uint8_t cm;
+        shade<DEG>(a.cams[view], mx, my, mz, shv, rgb, cm);
+        reinterpret_cast<float4*>(a.splats + o * GS_SPLAT_STRIDE)[2] =
+            make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
+        a.clamp[o] = cm;
+    }
 }
 
 // One thread per Gaussian: projection, tile rectangle and (with COLOR) the SH
-// colour.  Without COLOR the rgb row of the splat record and the clamp mask are
-// left alone (k_shade writes them).
+// colour, for each view in turn (the parameters are read once; the view-free
+// parts -- opacity, M = R S -- are computed once).  Without COLOR the rgb row
+// of the splat record and the clamp mask are left alone (k_shade writes them).
 template <int DEG, bool VEC, bool COLOR>
 __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     constexpr int J = 3 * (DEG + 1) * (DEG + 1);
@@ -138,30 +144,26 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     float shv[COLOR ? J : 1];
     if constexpr (COLOR) load_sh<DEG, VEC>(a.sh, i, shv);
 
-    float4* sp = reinterpret_cast<float4*>(a.splats + (size_t)i * GS_SPLAT_STRIDE);
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto cull = [&]() {
+    auto cull = [&](size_t o) {
+        float4* sp = reinterpret_cast<float4*>(a.splats + o * GS_SPLAT_STRIDE);
         sp[0] = z4; sp[1] = z4;
         if constexpr (COLOR) {
             sp[2] = z4;
-            a.clamp[i] = 0;
+            a.clamp[o] = 0;
         }
-        a.depth[i] = 0.f;
-        reinterpret_cast<uint2*>(a.rect)[i] = make_uint2(0u, 0u);
-        a.tiles_touched[i] = 0;
+        a.depth[o] = 0.f;
+        reinterpret_cast<uint2*>(a.rect)[o] = make_uint2(0u, 0u);
+        a.tiles_touched[o] = 0;
     };
 
-    const CamArgs& c = a.cam;
     const double mx = a.means[3 * i], my = a.means[3 * i + 1], mz = a.means[3 * i + 2];
-    const double tx = c.R[0] * mx + c.R[1] * my + c.R[2] * mz + c.t[0];
-    const double ty = c.R[3] * mx + c.R[4] * my + c.R[5] * mz + c.t[1];
-    const double tz = c.R[6] * mx + c.R[7] * my + c.R[8] * mz + c.t[2];
-    if (!(tz > a.near_z)) { cull(); return; }
-
     // opacity
     const double sigma = 1.0 / (1.0 + exp(-(double)a.opac[i]));
-    if (sigma < a.alpha_min) { cull(); return; }
-
+    if (sigma < a.alpha_min) {
+        for (int view = 0; view < a.views; ++view) cull((size_t)view * a.n + i);
+        return;
+    }
     // rotation of the normalised quaternion (w, x, y, z), M = R S
     const float4 qf = reinterpret_cast<const float4*>(a.quats)[i];
     double qw = qf.x, qx = qf.y, qy = qf.z, qz = qf.w;
@@ -180,70 +182,80 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     M[6] = 2.0 * (qx * qz - qw * qy) * s0;
     M[7] = 2.0 * (qy * qz + qw * qx) * s1;
     M[8] = (1.0 - 2.0 * (qx * qx + qy * qy)) * s2;
-
-    // T = J R_view (2x3), J the pinhole Jacobian at t; W = T M, cov2d = W W^T + dilation I
-    const double iz = 1.0 / tz;
-    const double j00 = c.fx * iz, j02 = -c.fx * tx * iz * iz;
-    const double j11 = c.fy * iz, j12 = -c.fy * ty * iz * iz;
-    double T0[3], T1[3];
-    for (int k = 0; k < 3; ++k) {
-        T0[k] = j00 * c.R[k] + j02 * c.R[6 + k];
-        T1[k] = j11 * c.R[3 + k] + j12 * c.R[6 + k];
-    }
-    double W0[3], W1[3];
-    for (int k = 0; k < 3; ++k) {
-        W0[k] = T0[0] * M[k] + T0[1] * M[3 + k] + T0[2] * M[6 + k];
-        W1[k] = T1[0] * M[k] + T1[1] * M[3 + k] + T1[2] * M[6 + k];
-    }
-    const double ca = W0[0] * W0[0] + W0[1] * W0[1] + W0[2] * W0[2] + a.dilation;
-    const double cb = W0[0] * W1[0] + W0[1] * W1[1] + W0[2] * W1[2];
-    const double cc = W1[0] * W1[0] + W1[1] * W1[1] + W1[2] * W1[2] + a.dilation;
-    const double det = ca * cc - cb * cb;
-    if (!(det > 0.0)) { cull(); return; }
-
-    const double u = c.fx * tx * iz + c.cx;
-    const double v = c.fy * ty * iz + c.cy;
-
-    // alpha >= alpha_min ellipse: d^T conic d <= k2 = 2 ln(sigma / alpha_min);
-    // its bounding box has half-widths sqrt(k2 ca), sqrt(k2 cc).
+    // alpha >= alpha_min ellipse: d^T conic d <= k2 = 2 ln(sigma / alpha_min)
     const double k2 = 2.0 * log(sigma / a.alpha_min);
-    const double ex = sqrt(k2 * ca), ey = sqrt(k2 * cc);
-    double xl = ceil(u - ex - 0.5), xh = floor(u + ex - 0.5);
-    double yl = ceil(v - ey - 0.5), yh = floor(v + ey - 0.5);
-    xl = fmax(xl, 0.0); yl = fmax(yl, 0.0);
-    xh = fmin(xh, (double)(c.width - 1)); yh = fmin(yh, (double)(c.height - 1));
-    int tx0 = 0, ty0 = 0, tx1 = 0, ty1 = 0, touched = 0;
-    if (xl <= xh && yl <= yh) {
-        tx0 = (int)xl / kTile; tx1 = (int)xh / kTile + 1;
-        ty0 = (int)yl / kTile; ty1 = (int)yh / kTile + 1;
-        touched = (tx1 - tx0) * (ty1 - ty0);
+
+    for (int view = 0; view < a.views; ++view) {
+        const size_t o = (size_t)view * a.n + i;
+        const CamArgs& c = a.cams[view];
+        const double tx = c.R[0] * mx + c.R[1] * my + c.R[2] * mz + c.t[0];
+        const double ty = c.R[3] * mx + c.R[4] * my + c.R[5] * mz + c.t[1];
+        const double tz = c.R[6] * mx + c.R[7] * my + c.R[8] * mz + c.t[2];
+        if (!(tz > a.near_z)) { cull(o); continue; }
+
+        // T = J R_view (2x3), J the pinhole Jacobian at t; W = T M, cov2d = W W^T + dilation I
+        const double iz = 1.0 / tz;
+        const double j00 = c.fx * iz, j02 = -c.fx * tx * iz * iz;
+        const double j11 = c.fy * iz, j12 = -c.fy * ty * iz * iz;
+        double T0[3], T1[3];
+        for (int k = 0; k < 3; ++k) {
+            T0[k] = j00 * c.R[k] + j02 * c.R[6 + k];
+            T1[k] = j11 * c.R[3 + k] + j12 * c.R[6 + k];
+        }
+        double W0[3], W1[3];
+        for (int k = 0; k < 3; ++k) {
+            W0[k] = T0[0] * M[k] + T0[1] * M[3 + k] + T0[2] * M[6 + k];
+            W1[k] = T1[0] * M[k] + T1[1] * M[3 + k] + T1[2] * M[6 + k];
+        }
+        const double ca = W0[0] * W0[0] + W0[1] * W0[1] + W0[2] * W0[2] + a.dilation;
+        const double cb = W0[0] * W1[0] + W0[1] * W1[1] + W0[2] * W1[2];
+        const double cc = W1[0] * W1[0] + W1[1] * W1[1] + W1[2] * W1[2] + a.dilation;
+        const double det = ca * cc - cb * cb;
+        if (!(det > 0.0)) { cull(o); continue; }
+
+        const double u = c.fx * tx * iz + c.cx;
+        const double v = c.fy * ty * iz + c.cy;
+
+        // bounding box of the alpha >= alpha_min ellipse: half-widths sqrt(k2 ca), sqrt(k2 cc)
+        const double ex = sqrt(k2 * ca), ey = sqrt(k2 * cc);
+        double xl = ceil(u - ex - 0.5), xh = floor(u + ex - 0.5);
+        double yl = ceil(v - ey - 0.5), yh = floor(v + ey - 0.5);
+        xl = fmax(xl, 0.0); yl = fmax(yl, 0.0);
+        xh = fmin(xh, (double)(c.width - 1)); yh = fmin(yh, (double)(c.height - 1));
+        int tx0 = 0, ty0 = 0, tx1 = 0, ty1 = 0, touched = 0;
+        if (xl <= xh && yl <= yh) {
+            tx0 = (int)xl / kTile; tx1 = (int)xh / kTile + 1;
+            ty0 = (int)yl / kTile; ty1 = (int)yh / kTile + 1;
+            touched = (tx1 - tx0) * (ty1 - ty0);
+        }
+
+        // colour: max(0, sum sh Y(dir) + 0.5), dir from the camera centre
+        double rgb[3];
+        uint8_t cm = 0;
+        if constexpr (COLOR) shade<DEG>(c, mx, my, mz, shv, rgb, cm);
+
+        // Cholesky factor of the conic, scaled so that G = exp2(-|L^T d|^2):
+        // conic = [[cc, -cb], [-cb, ca]] / det = L L^T with
+        // L00 = sqrt(cc / det), L10 = -cb / sqrt(cc det), L11 = 1 / sqrt(cc).
+        const double sc = 0.84932180028801907;  // sqrt(log2(e) / 2)
+        const double l00 = sqrt(cc / det) * sc;
+        const double l10 = -cb / sqrt(cc * det) * sc;
+        const double l11 = sc / sqrt(cc);
+
+        float4* sp = reinterpret_cast<float4*>(a.splats + o * GS_SPLAT_STRIDE);
+        const float uf = (float)u, vf = (float)v;
+        sp[0] = make_float4(uf, vf, (float)(u - (double)uf), (float)(v - (double)vf));
+        sp[1] = make_float4((float)l00, (float)l10, (float)l11, (float)sigma);
+        if constexpr (COLOR) {
+            sp[2] = make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
+            a.clamp[o] = cm;
+        }
+        a.depth[o] = (float)tz;
+        const uint32_t r0 = (uint32_t)(uint16_t)tx0 | ((uint32_t)(uint16_t)ty0 << 16);
+        const uint32_t r1 = (uint32_t)(uint16_t)tx1 | ((uint32_t)(uint16_t)ty1 << 16);
+        reinterpret_cast<uint2*>(a.rect)[o] = make_uint2(r0, r1);
+        a.tiles_touched[o] = touched;
     }
-
-    // colour: max(0, sum sh Y(dir) + 0.5), dir from the camera centre
-    double rgb[3];
-    uint8_t cm = 0;
-    if constexpr (COLOR) shade<DEG>(c, mx, my, mz, shv, rgb, cm);
-
-    // Cholesky factor of the conic, scaled so that G = exp2(-|L^T d|^2):
-    // conic = [[cc, -cb], [-cb, ca]] / det = L L^T with
-    // L00 = sqrt(cc / det), L10 = -cb / sqrt(cc det), L11 = 1 / sqrt(cc).
-    const double sc = 0.84932180028801907;  // sqrt(log2(e) / 2)
-    const double l00 = sqrt(cc / det) * sc;
-    const double l10 = -cb / sqrt(cc * det) * sc;
-    const double l11 = sc / sqrt(cc);
-
-    const float uf = (float)u, vf = (float)v;
-    sp[0] = make_float4(uf, vf, (float)(u - (double)uf), (float)(v - (double)vf));
-    sp[1] = make_float4((float)l00, (float)l10, (float)l11, (float)sigma);
-    if constexpr (COLOR) {
-        sp[2] = make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
-        a.clamp[i] = cm;
-    }
-    a.depth[i] = (float)tz;
-    const uint32_t r0 = (uint32_t)(uint16_t)tx0 | ((uint32_t)(uint16_t)ty0 << 16);
-    const uint32_t r1 = (uint32_t)(uint16_t)tx1 | ((uint32_t)(uint16_t)ty1 << 16);
-    reinterpret_cast<uint2*>(a.rect)[i] = make_uint2(r0, r1);
-    a.tiles_touched[i] = touched;
 }
 
 }  // namespace
@@ -265,11 +277,12 @@ void launch_pre(Part part, dim3 grid, dim3 block, hipStream_t s, const PreArgs& 
     }
 }
 
-int preprocess_impl(Part part, const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
-                    const float* means, const float* log_scales, const float* quats, const float* opacity_logits,
-                    const float* sh, float* splats, float* depth, int16_t* rect, int32_t* tiles_touched,
-                    uint8_t* clamp_mask, void* stream) {
-    if (!camera_ok(cam) || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
+int preprocess_impl(Part part, const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                    int32_t sh_degree, const float* means, const float* log_scales, const float* quats,
+                    const float* opacity_logits, const float* sh, float* splats, float* depth, int16_t* rect,
+                    int32_t* tiles_touched, uint8_t* clamp_mask, void* stream) {
+    if (!views_ok(cams, views) || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
+    if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
     if (part != Part::kColor && !set) return GS_EINVAL;
     if (n == 0) return GS_OK;
     if (!means || !splats) return GS_EINVAL;
@@ -279,7 +292,8 @@ int preprocess_impl(Part part, const gs_camera* cam, const gs_settings* set, int
     if (!aligned16(splats)) return GS_EALIGN;
     if (part != Part::kColor && (!aligned16(quats) || !aligned16(rect))) return GS_EALIGN;
     PreArgs a{};
-    a.cam = cam_args(cam);
+    for (int v = 0; v < views; ++v) a.cams[v] = cam_args(cams + v);
+    a.views = views;
     if (set) { a.near_z = set->near_z; a.alpha_min = set->alpha_min; a.dilation = set->dilation; }
     a.n = n;
     a.means = means; a.log_scales = log_scales; a.quats = quats; a.opac = opacity_logits; a.sh = sh;
@@ -303,19 +317,28 @@ extern "C" int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32
                              const float* means, const float* log_scales, const float* quats,
                              const float* opacity_logits, const float* sh, float* splats, float* depth,
                              int16_t* rect, int32_t* tiles_touched, uint8_t* clamp_mask, void* stream) {
-    return preprocess_impl(Part::kAll, cam, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh, splats,
-                           depth, rect, tiles_touched, clamp_mask, stream);
+    return preprocess_impl(Part::kAll, cam, 1, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
+                           splats, depth, rect, tiles_touched, clamp_mask, stream);
+}
+
+extern "C" int gs_preprocess_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                                   int32_t sh_degree, const float* means, const float* log_scales,
+                                   const float* quats, const float* opacity_logits, const float* sh, float* splats,
+                                   float* depth, int16_t* rect, int32_t* tiles_touched, uint8_t* clamp_mask,
+                                   void* stream) {
+    return preprocess_impl(Part::kAll, cams, views, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
+                           splats, depth, rect, tiles_touched, clamp_mask, stream);
 }
 
 extern "C" int gs_project(const gs_camera* cam, const gs_settings* set, int32_t n, const float* means,
                           const float* log_scales, const float* quats, const float* opacity_logits, float* splats,
                           float* depth, int16_t* rect, int32_t* tiles_touched, void* stream) {
-    return preprocess_impl(Part::kGeometry, cam, set, n, 0, means, log_scales, quats, opacity_logits, nullptr,
+    return preprocess_impl(Part::kGeometry, cam, 1, set, n, 0, means, log_scales, quats, opacity_logits, nullptr,
                            splats, depth, rect, tiles_touched, nullptr, stream);
 }
 
 extern "C" int gs_shade(const gs_camera* cam, int32_t n, int32_t sh_degree, const float* means, const float* sh,
                         float* splats, uint8_t* clamp_mask, void* stream) {
-    return preprocess_impl(Part::kColor, cam, nullptr, n, sh_degree, means, nullptr, nullptr, nullptr, sh, splats,
-                           nullptr, nullptr, nullptr, clamp_mask, stream);
+    return preprocess_impl(Part::kColor, cam, 1, nullptr, n, sh_degree, means, nullptr, nullptr, nullptr, sh,
+                           splats, nullptr, nullptr, nullptr, clamp_mask, stream);
 }

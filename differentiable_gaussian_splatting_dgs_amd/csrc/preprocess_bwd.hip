@@ -26,7 +26,8 @@ struct AdamHyper {
 };
 
 struct BwdArgs {
-    CamArgs cam;
+    CamArgs cams[GS_MAX_VIEWS];  // batched views: grad2d, tt, clamp are [views, n, ...]; gradients are summed
+    int32_t views;
     float dilation;
     int32_t n;
     float* means;  // read; updated in place by the Adam variant
@@ -137,12 +138,12 @@ __device__ __forceinline__ void adam_reg(float& p, float g, float& m, float& v, 
 // quaternion and opacity logit, plus the SH basis and the clamp-masked colour
 // gradient the SH coefficients need.  ddir needs the SH coefficients, read
 // from the block's LDS copy (coefficient-major, row stride ldg).
+// Gaussian i seen by camera c; iv indexes its view's 2D gradient and clamp mask.
 template <int DEG>
-__device__ __forceinline__ void chain(const BwdArgs& a, int i, const float* s_sh, int col, int ldg, float dmu[3],
-                                      float dls[3], float dq[4], float& dop, float Y[16], float drgb[3],
-                                      float dir[3]) {
+__device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i, size_t iv, const float* s_sh,
+                                      int col, int ldg, float dmu[3], float dls[3], float dq[4], float& dop,
+                                      float Y[16], float drgb[3], float dir[3]) {
     constexpr int K = (DEG + 1) * (DEG + 1);
-    const CamArgs& c = a.cam;
     const float Rv[9] = {(float)c.R[0], (float)c.R[1], (float)c.R[2], (float)c.R[3], (float)c.R[4],
                          (float)c.R[5], (float)c.R[6], (float)c.R[7], (float)c.R[8]};
     const float fx = (float)c.fx, fy = (float)c.fy;
@@ -151,9 +152,9 @@ __device__ __forceinline__ void chain(const BwdArgs& a, int i, const float* s_sh
     const float ty = Rv[3] * mx + Rv[4] * my + Rv[5] * mz + (float)c.t[1];
     const float tz = Rv[6] * mx + Rv[7] * my + Rv[8] * mz + (float)c.t[2];
 
-    const float4 g0 = reinterpret_cast<const float4*>(a.grad2d)[3 * (size_t)i];
-    const float4 g1 = reinterpret_cast<const float4*>(a.grad2d)[3 * (size_t)i + 1];
-    const float4 g2 = reinterpret_cast<const float4*>(a.grad2d)[3 * (size_t)i + 2];
+    const float4 g0 = reinterpret_cast<const float4*>(a.grad2d)[3 * iv];
+    const float4 g1 = reinterpret_cast<const float4*>(a.grad2d)[3 * iv + 1];
+    const float4 g2 = reinterpret_cast<const float4*>(a.grad2d)[3 * iv + 2];
     const float du = g0.x, dv = g0.y, dA = g0.z, dB = g0.w, dC = g1.x, dsig = g1.y;
     drgb[0] = g1.z; drgb[1] = g1.w; drgb[2] = g2.x;
 
@@ -169,7 +170,7 @@ __device__ __forceinline__ void chain(const BwdArgs& a, int i, const float* s_sh
     const float il = 1.f / sqrtf(vx * vx + vy * vy + vz * vz);
     const float dx = vx * il, dy = vy * il, dz = vz * il;
     dir[0] = dx; dir[1] = dy; dir[2] = dz;
-    const uint8_t cm = a.clamp[i];
+    const uint8_t cm = a.clamp[iv];
 #pragma unroll
     for (int ch = 0; ch < 3; ++ch)
         if ((cm >> ch) & 1u) drgb[ch] = 0.f;
@@ -293,7 +294,7 @@ __device__ __forceinline__ void chain(const BwdArgs& a, int i, const float* s_sh
 // (coalesced), written out and/or applied with Adam; kChunk elements per thread
 // at a time, loads first.  The parameter comes from s_sh (the block's LDS copy)
 // when given, else from HBM.
-template <int DEG, bool ADAM>
+template <int DEG, bool ADAM, bool MV = false>
 __device__ __forceinline__ void sh_elements(const BwdArgs& a, const float* s_sh, int LDG, const float* s_y,
                                             const float* s_c, int cnt, size_t base, int t) {
     constexpr int J = 3 * (DEG + 1) * (DEG + 1);
@@ -315,7 +316,8 @@ __device__ __forceinline__ void sh_elements(const BwdArgs& a, const float* s_sh,
             if (e >= cnt) break;
             const int g = e / J, j = e - g * J;
             const int k = j / 3, ch = j - 3 * k;
-            const float grad = s_y[k * LDG + g] * s_c[ch * LDG + g];
+            // MV: s_y holds the gradient itself (summed over the views), coefficient-major
+            const float grad = MV ? s_y[j * LDG + g] : s_y[k * LDG + g] * s_c[ch * LDG + g];
             if (a.dsh) a.dsh[base + e] = grad;
             if (ADAM) {
                 const AdamHyper& h = a.adam;
@@ -339,14 +341,17 @@ __device__ __forceinline__ void sh_elements(const BwdArgs& a, const float* s_sh,
 //           gradient writes and the Adam read-modify-write are coalesced.
 // SH = false: the geometry half of the tail (no phase 2); the view directions
 // go to a.view_dir (zero for Gaussians outside every tile) for k_grad3d_sh.
-template <int DEG, bool ADAM, bool SH = true>
+// MV: a batch of a.views views; phase 1 runs the chain once per view in which
+// the Gaussian touches a tile and sums the gradients (and the statistic over
+// the views), and keeps the summed SH gradient itself in LDS for phase 2.
+template <int DEG, bool ADAM, bool SH = true, bool MV = false>
 __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
     constexpr int K = (DEG + 1) * (DEG + 1);
     constexpr int J = 3 * K;
     constexpr int LDG = kG + 1;
     __shared__ float s_sh[J * LDG];
-    __shared__ float s_y[K * LDG];
-    __shared__ float s_c[3 * LDG];
+    __shared__ float s_y[(MV ? J : K) * LDG];
+    __shared__ float s_c[(MV ? 1 : 3) * LDG];
     const int t = threadIdx.x;
     const int g0 = blockIdx.x * kG;
     const int ng = min(kG, a.n - g0);
@@ -386,19 +391,51 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
         if (a.accum) { acc = a.accum[i]; nvis = a.count[i]; }
         float dmu[3] = {0.f, 0.f, 0.f}, dls[3] = {0.f, 0.f, 0.f}, dq[4] = {0.f, 0.f, 0.f, 0.f}, dop = 0.f;
         float Y[16], drgb[3] = {0.f, 0.f, 0.f}, dir[3] = {0.f, 0.f, 0.f};
-        const bool vis = a.tt[i] > 0;
-        if (vis) {
-            chain<DEG>(a, i, s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb, dir);
-            if (a.accum) {
-                const float2 d2 = *reinterpret_cast<const float2*>(a.grad2d + (size_t)i * GS_GRAD2D_STRIDE);
-                a.accum[i] = acc + sqrtf(d2.x * d2.x + d2.y * d2.y);
-                a.count[i] = nvis + 1;
+        if constexpr (MV) {
+#pragma unroll
+            for (int j = 0; j < J; ++j) s_y[j * LDG + t] = 0.f;
+            bool seen = false;
+            for (int view = 0; view < a.views; ++view) {
+                const size_t iv = (size_t)view * a.n + i;
+                if (a.tt[iv] <= 0) continue;
+                seen = true;
+                float vmu[3], vls[3], vq[4], vop;
+                chain<DEG>(a, a.cams[view], i, iv, s_sh, t, LDG, vmu, vls, vq, vop, Y, drgb, dir);
+#pragma unroll
+                for (int k = 0; k < 3; ++k) { dmu[k] += vmu[k]; dls[k] += vls[k]; }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) dq[k] += vq[k];
+                dop += vop;
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+#pragma unroll
+                    for (int ch = 0; ch < 3; ++ch) s_y[(3 * k + ch) * LDG + t] += Y[k] * drgb[ch];
+                if (a.accum) {
+                    const float2 d2 = *reinterpret_cast<const float2*>(a.grad2d + iv * GS_GRAD2D_STRIDE);
+                    acc += sqrtf(d2.x * d2.x + d2.y * d2.y);
+                    nvis += 1;
+                }
+            }
+            if (a.accum && seen) {
+                a.accum[i] = acc;
+                a.count[i] = nvis;
             }
         } else {
+            const bool vis = a.tt[i] > 0;
+            if (vis) {
+                chain<DEG>(a, a.cams[0], i, (size_t)i, s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb, dir);
+                if (a.accum) {
+                    const float2 d2 = *reinterpret_cast<const float2*>(a.grad2d + (size_t)i * GS_GRAD2D_STRIDE);
+                    a.accum[i] = acc + sqrtf(d2.x * d2.x + d2.y * d2.y);
+                    a.count[i] = nvis + 1;
+                }
+            } else {
 #pragma unroll
-            for (int k = 0; k < K; ++k) Y[k] = 0.f;
+                for (int k = 0; k < K; ++k) Y[k] = 0.f;
+            }
         }
-        if constexpr (SH) {
+        if constexpr (MV) {
+        } else if constexpr (SH) {
 #pragma unroll
             for (int k = 0; k < K; ++k) s_y[k * LDG + t] = Y[k];
             s_c[t] = drgb[0];
@@ -445,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
     }
     if constexpr (!SH) return;
     __syncthreads();
-    sh_elements<DEG, ADAM>(a, s_sh, LDG, s_y, s_c, cnt, base, t);
+    sh_elements<DEG, ADAM, MV>(a, s_sh, LDG, s_y, s_c, cnt, base, t);
 }
 
 // The SH half of the tail on its own: Y from the stored view direction, the
@@ -484,14 +521,14 @@ __global__ __launch_bounds__(kThreads) void k_grad3d_sh(BwdArgs a) {
     sh_elements<DEG, true>(a, nullptr, LDG, s_y, s_c, cnt, base, t);
 }
 
-template <bool ADAM, bool SH = true>
+template <bool ADAM, bool SH = true, bool MV = false>
 inline void launch_grad3d(int deg, const BwdArgs& a, hipStream_t s) {
     const dim3 grid((a.n + kG - 1) / kG), block(kThreads);
     switch (deg) {
-        case 0: hipLaunchKernelGGL((k_grad3d<0, ADAM, SH>), grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL((k_grad3d<1, ADAM, SH>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_grad3d<2, ADAM, SH>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((k_grad3d<3, ADAM, SH>), grid, block, 0, s, a); break;
+        case 0: hipLaunchKernelGGL((k_grad3d<0, ADAM, SH, MV>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((k_grad3d<1, ADAM, SH, MV>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_grad3d<2, ADAM, SH, MV>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_grad3d<3, ADAM, SH, MV>), grid, block, 0, s, a); break;
     }
 }
 
@@ -513,11 +550,12 @@ inline void fill_adam(BwdArgs& a, const gs_adam_state* adam) {
     a.adam.inv_sqrt_c2 = (float)(1.0 / sqrt(1.0 - pow((double)adam->beta2, adam->step)));
 }
 
-inline void fill_common(BwdArgs& a, const gs_camera* cam, const gs_settings* set, int32_t n, const float* means,
-                        const float* log_scales, const float* quats, const float* opacity_logits, const float* sh,
-                        const int32_t* tt, const uint8_t* clamp, const float* grad2d) {
+inline void fill_common(BwdArgs& a, const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                        const float* means, const float* log_scales, const float* quats, const float* opacity_logits,
+                        const float* sh, const int32_t* tt, const uint8_t* clamp, const float* grad2d) {
     a = BwdArgs{};
-    a.cam = cam_args(cam);
+    for (int v = 0; v < views; ++v) a.cams[v] = cam_args(cams + v);
+    a.views = views;
     a.dilation = (float)set->dilation;
     a.n = n;
     a.means = const_cast<float*>(means); a.log_scales = const_cast<float*>(log_scales);
@@ -543,7 +581,7 @@ extern "C" int gs_preprocess_bwd(const gs_camera* cam, const gs_settings* set, i
         return GS_EINVAL;
     if (!aligned16(quats) || !aligned16(grad2d) || !aligned16(dquats)) return GS_EALIGN;
     BwdArgs a;
-    fill_common(a, cam, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
+    fill_common(a, cam, 1, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
     a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
     launch_grad3d<false>(sh_degree, a, as_stream(stream));
     return launch_status();
@@ -569,7 +607,7 @@ extern "C" int gs_preprocess_bwd_adam(const gs_camera* cam, const gs_settings* s
     if (!aligned16(quats) || !aligned16(grad2d) || (dquats && !aligned16(dquats))) return GS_EALIGN;
     if (!aligned16(adam->exp_avg[2]) || !aligned16(adam->exp_avg_sq[2])) return GS_EALIGN;
     BwdArgs a;
-    fill_common(a, cam, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
+    fill_common(a, cam, 1, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
     a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
     a.accum = densify_accum; a.count = densify_count;
     fill_adam(a, adam);
@@ -596,7 +634,7 @@ extern "C" int gs_preprocess_bwd_adam_geom(const gs_camera* cam, const gs_settin
     if (!aligned16(quats) || !aligned16(grad2d)) return GS_EALIGN;
     if (!aligned16(adam->exp_avg[2]) || !aligned16(adam->exp_avg_sq[2])) return GS_EALIGN;
     BwdArgs a;
-    fill_common(a, cam, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
+    fill_common(a, cam, 1, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
     a.accum = densify_accum; a.count = densify_count;
     a.view_dir = view_dir;
     fill_adam(a, adam);
@@ -620,5 +658,57 @@ extern "C" int gs_preprocess_bwd_adam_sh(int32_t n, int32_t sh_degree, float* sh
     a.view_dir = const_cast<float*>(view_dir);
     fill_adam(a, adam);
     launch_grad3d_sh(sh_degree, a, as_stream(stream));
+    return launch_status();
+}
+
+extern "C" int gs_preprocess_bwd_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                                       int32_t sh_degree, const float* means, const float* log_scales,
+                                       const float* quats, const float* opacity_logits, const float* sh,
+                                       const int32_t* tiles_touched, const uint8_t* clamp_mask, const float* grad2d,
+                                       float* dmeans, float* dlog_scales, float* dquats, float* dopacity_logits,
+                                       float* dsh, void* stream) {
+    if (!views_ok(cams, views) || !set || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
+    if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
+    if (n == 0) return GS_OK;
+    if (!means || !log_scales || !quats || !opacity_logits || !sh || !tiles_touched || !clamp_mask || !grad2d ||
+        !dmeans || !dlog_scales || !dquats || !dopacity_logits || !dsh)
+        return GS_EINVAL;
+    if (!aligned16(quats) || !aligned16(grad2d) || !aligned16(dquats)) return GS_EALIGN;
+    BwdArgs a;
+    fill_common(a, cams, views, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask,
+                grad2d);
+    a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
+    launch_grad3d<false, true, true>(sh_degree, a, as_stream(stream));
+    return launch_status();
+}
+
+extern "C" int gs_preprocess_bwd_adam_views(const gs_camera* cams, int32_t views, const gs_settings* set,
+                                            int32_t n, int32_t sh_degree, float* means, float* log_scales,
+                                            float* quats, float* opacity_logits, float* sh,
+                                            const int32_t* tiles_touched, const uint8_t* clamp_mask,
+                                            const float* grad2d, const gs_adam_state* adam, float* densify_accum,
+                                            int32_t* densify_count, float* dmeans, float* dlog_scales,
+                                            float* dquats, float* dopacity_logits, float* dsh, void* stream) {
+    if (!views_ok(cams, views) || !set || !adam || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE)
+        return GS_EINVAL;
+    if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
+    if (adam->step < 1) return GS_EINVAL;
+    if (n == 0) return GS_OK;
+    if (!means || !log_scales || !quats || !opacity_logits || !sh || !tiles_touched || !clamp_mask || !grad2d)
+        return GS_EINVAL;
+    for (int k = 0; k < 5; ++k)
+        if (!adam->exp_avg[k] || !adam->exp_avg_sq[k]) return GS_EINVAL;
+    if ((densify_accum == nullptr) != (densify_count == nullptr)) return GS_EINVAL;
+    const bool any_grad = dmeans || dlog_scales || dquats || dopacity_logits;
+    if (any_grad && !(dmeans && dlog_scales && dquats && dopacity_logits)) return GS_EINVAL;
+    if (!aligned16(quats) || !aligned16(grad2d) || (dquats && !aligned16(dquats))) return GS_EALIGN;
+    if (!aligned16(adam->exp_avg[2]) || !aligned16(adam->exp_avg_sq[2])) return GS_EALIGN;
+    BwdArgs a;
+    fill_common(a, cams, views, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask,
+                grad2d);
+    a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
+    a.accum = densify_accum; a.count = densify_count;
+    fill_adam(a, adam);
+    launch_grad3d<true, true, true>(sh_degree, a, as_stream(stream));
     return launch_status();
 }

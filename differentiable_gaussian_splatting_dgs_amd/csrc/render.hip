@@ -181,10 +181,11 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
             a.clear[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     const BlendArgs& b = a.b;
-    const int ntiles = b.tiles_x * b.tiles_y;
-    const int tile = block_tile(a.sched, ntiles);
+    const int ntv = b.tiles_x * b.tiles_y;
+    const int tile = block_tile(a.sched, ntv * b.views);
     if (tile < 0) return;
-    const int tx = tile % b.tiles_x, ty = tile / b.tiles_x;
+    const int view = tile / ntv, vtile = tile - view * ntv;
+    const int tx = vtile % b.tiles_x, ty = vtile / b.tiles_x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lx = (wave & 1) * 8 + (lane & 7), ly = (wave >> 1) * 8 + (lane >> 3);
     const int px = tx * kTile + lx, py = ty * kTile + ly;
@@ -277,23 +278,24 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
     }
     double lsum = 0.0;
     if (inside) {
-        const size_t pix = (size_t)py * b.width + px;
         const size_t plane = (size_t)b.width * b.height;
+        const size_t pix = (size_t)py * b.width + px + (size_t)view * plane;  // final_T, n_contrib: [views, H, W]
+        const size_t pix3 = pix + (size_t)view * 2 * plane;                  // planar images: [views, 3, H, W]
         const float out[3] = {C0 + T * b.bg[0], C1 + T * b.bg[1], C2 + T * b.bg[2]};
 #pragma unroll
-        for (int ch = 0; ch < 3; ++ch) a.image[ch * plane + pix] = out[ch];
+        for (int ch = 0; ch < 3; ++ch) a.image[ch * plane + pix3] = out[ch];
         a.final_T[pix] = T;
         a.n_contrib[pix] = last;
         if (a.loss_mode) {
 #pragma unroll
             for (int ch = 0; ch < 3; ++ch) {
-                const float r = out[ch] - a.target[ch * plane + pix];
+                const float r = out[ch] - a.target[ch * plane + pix3];
                 if (a.loss_mode == 1) {
                     lsum += (double)fabsf(r);
-                    a.dL_out[ch * plane + pix] = r > 0.f ? 1.f : (r < 0.f ? -1.f : 0.f);
+                    a.dL_out[ch * plane + pix3] = r > 0.f ? 1.f : (r < 0.f ? -1.f : 0.f);
                 } else {
                     lsum += (double)r * (double)r;
-                    a.dL_out[ch * plane + pix] = 2.f * r;
+                    a.dL_out[ch * plane + pix3] = 2.f * r;
                 }
             }
         }
@@ -430,10 +432,11 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     __shared__ uint16_t s_list[kBwdBatch];  // slot | quadrant mask << 8, in walk order
 
     const BlendArgs& b = a.b;
-    const int ntiles = b.tiles_x * b.tiles_y;
-    const int tile = block_tile(a.sched, ntiles);
+    const int ntv = b.tiles_x * b.tiles_y;
+    const int tile = block_tile(a.sched, ntv * b.views);
     if (tile < 0) return;
-    const int tx = tile % b.tiles_x, ty = tile / b.tiles_x;
+    const int view = tile / ntv, vtile = tile - view * ntv;
+    const int tx = vtile % b.tiles_x, ty = vtile / b.tiles_x;
     const int lane = threadIdx.x;
     const float x0 = (float)(tx * kTile), y0 = (float)(ty * kTile);
     const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
@@ -455,12 +458,13 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
         fyq[q] = (float)ly + 0.5f;
         T[q] = 1.f; nc[q] = 0; gp0[q] = gp1[q] = gp2[q] = 0.f;
         if (px < b.width && py < b.height) {
-            const size_t pix = (size_t)py * b.width + px;
+            const size_t pix = (size_t)py * b.width + px + (size_t)view * plane;
+            const size_t pix3 = pix + (size_t)view * 2 * plane;
             T[q] = a.final_T[pix];
             nc[q] = a.n_contrib[pix];
-            gp0[q] = a.dL_dimage[pix];
-            gp1[q] = a.dL_dimage[plane + pix];
-            gp2[q] = a.dL_dimage[2 * plane + pix];
+            gp0[q] = a.dL_dimage[pix3];
+            gp1[q] = a.dL_dimage[plane + pix3];
+            gp2[q] = a.dL_dimage[2 * plane + pix3];
         }
         S[q] = __builtin_fmaf(gp2[q], b.bg[2], __builtin_fmaf(gp1[q], b.bg[1], gp0[q] * b.bg[0]));
         ncmax = max(ncmax, nc[q]);
@@ -662,7 +666,7 @@ __global__ __launch_bounds__(256) void k_count_pairs(RenderArgs a, unsigned long
     const int py = blockIdx.y * 16 + (threadIdx.x >> 4);
     unsigned long long ev = 0, nc = 0, nb = 0;
     if (px < b.width && py < b.height) {
-        const int tile = blockIdx.y * b.tiles_x + blockIdx.x;
+        const int tile = (blockIdx.z * b.tiles_y + blockIdx.y) * b.tiles_x + blockIdx.x;
         const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
         const float fx = (float)(px % kTile) + 0.5f, fy = (float)(py % kTile) + 0.5f;
         const float x0 = (float)(blockIdx.x * kTile), y0 = (float)(blockIdx.y * kTile);
@@ -695,16 +699,22 @@ __global__ void k_zero_i64(unsigned long long* p, int n) {
     if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
 }
 
-inline int render_common_checks(const gs_camera* cam, const gs_settings* set, const uint32_t* ranges,
-                                const float* splats) {
-    if (!camera_ok(cam) || !set || !ranges) return GS_EINVAL;
+inline int render_common_checks(const gs_camera* cams, int32_t views, const gs_settings* set,
+                                const uint32_t* ranges, const float* splats) {
+    if (!views_ok(cams, views) || !set || !ranges) return GS_EINVAL;
     if (!aligned16(splats) || !aligned16(ranges)) return GS_EALIGN;
     return GS_OK;
 }
 
-inline int render_grid(const gs_camera* cam) {
-    const int nt = tiles_x(cam) * tiles_y(cam);
+inline int render_grid(const gs_camera* cam, int32_t views) {
+    const int nt = views * tiles_x(cam) * tiles_y(cam);
     return 8 * ((nt + 7) / 8);
+}
+
+inline BlendArgs blend_views(const gs_camera* cam, int32_t views, const gs_settings* set) {
+    BlendArgs b = blend_args(cam, set);
+    b.views = views;
+    return b;
 }
 
 }  // namespace
@@ -717,7 +727,8 @@ namespace {
 
 // Forward blend, its tile schedules and, when a.loss_mode != 0, the fused loss.
 int render_fwd_impl(const gs_camera* cam, RenderArgs& a, int32_t* tile_order, double* loss_dev, hipStream_t s) {
-    const int ntiles = tiles_x(cam) * tiles_y(cam);
+    const int views = a.b.views;
+    const int ntiles = views * tiles_x(cam) * tiles_y(cam);
     if (tile_order && ntiles <= kOrderMaxTiles) {
         // row 0: the forward's own schedule (list lengths); row 1: the backward's (flag counts)
         int32_t* fwd_order = tile_order;
@@ -726,11 +737,11 @@ int render_fwd_impl(const gs_camera* cam, RenderArgs& a, int32_t* tile_order, do
                            nullptr, nullptr);
         a.sched = fwd_order;
         a.work = bwd_order;
-        hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam)), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam, views)), dim3(kBlock), 0, s, a);
         hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(kOrderThreads), 0, s, nullptr, bwd_order, bwd_order, ntiles,
                            a.loss_part, loss_dev);
     } else {
-        hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam)), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam, views)), dim3(kBlock), 0, s, a);
         if (tile_order)  // too many tiles for the one-block sort: image order
             hipLaunchKernelGGL(k_iota, dim3((2 * ntiles + 255) / 256), dim3(256), 0, s, tile_order, ntiles);
         if (a.loss_mode)
@@ -739,16 +750,18 @@ int render_fwd_impl(const gs_camera* cam, RenderArgs& a, int32_t* tile_order, do
     return launch_status();
 }
 
-int fwd_args(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
+// n: Gaussians per view; the splat records are [views, n, 12] and list entries index them.
+int fwd_args(const gs_camera* cam, int32_t views, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
              const uint32_t* point_list, const float* splats, float* image, float* final_T, int32_t* n_contrib,
              uint8_t* contrib, RenderArgs& a) {
-    int rc = render_common_checks(cam, set, tile_ranges, splats);
+    int rc = render_common_checks(cam, views, set, tile_ranges, splats);
     if (rc) return rc;
     if (n < 0 || !image || !final_T || !n_contrib) return GS_EINVAL;
+    if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
     if (n > 0 && (!point_list || !splats || !contrib)) return GS_EINVAL;
     a = RenderArgs{};
-    a.b = blend_args(cam, set);
-    a.n = (uint32_t)n;
+    a.b = blend_views(cam, views, set);
+    a.n = (uint32_t)(views * n);
     a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
     a.image = image; a.final_T = final_T; a.n_contrib = n_contrib; a.contrib = contrib;
     return GS_OK;
@@ -757,23 +770,19 @@ int fwd_args(const gs_camera* cam, const gs_settings* set, int32_t n, const uint
 }  // namespace
 }  // namespace gs
 
-extern "C" int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
-                             const uint32_t* point_list, const float* splats, float* image, float* final_T,
-                             int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order, void* stream) {
-    RenderArgs a;
-    const int rc = fwd_args(cam, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib, a);
-    if (rc) return rc;
-    return render_fwd_impl(cam, a, tile_order, nullptr, as_stream(stream));
-}
+namespace gs {
+namespace {
 
-extern "C" int gs_render_fwd_loss(const gs_camera* cam, const gs_settings* set, int32_t n,
-                                  const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
-                                  float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
-                                  int32_t* tile_order, int32_t loss_mode, const float* target, float* dL_dimage,
-                                  double* loss_dev, float* grad2d_clear, void* stream) {
+int render_fwd_loss_impl(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                         const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats, float* image,
+                         float* final_T, int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order,
+                         int32_t loss_mode, const float* target, float* dL_dimage, double* loss_dev,
+                         float* grad2d_clear, void* stream) {
     RenderArgs a;
-    const int rc = fwd_args(cam, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib, a);
+    const int rc = fwd_args(cams, views, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
+                            a);
     if (rc) return rc;
+    if (loss_mode == 0) return render_fwd_impl(cams, a, tile_order, nullptr, as_stream(stream));
     if (loss_mode != 1 && loss_mode != 2) return GS_EINVAL;
     if (!target || !dL_dimage || !loss_dev) return GS_EINVAL;
     if (grad2d_clear && !aligned16(grad2d_clear)) return GS_EALIGN;
@@ -783,51 +792,121 @@ extern "C" int gs_render_fwd_loss(const gs_camera* cam, const gs_settings* set, 
     a.loss_part = loss_dev + 1;
     if (grad2d_clear && n > 0) {
         a.clear = reinterpret_cast<float4*>(grad2d_clear);
-        a.clear4 = (size_t)n * GS_GRAD2D_STRIDE / 4;
+        a.clear4 = (size_t)a.n * GS_GRAD2D_STRIDE / 4;
     }
-    return render_fwd_impl(cam, a, tile_order, loss_dev, as_stream(stream));
+    return render_fwd_impl(cams, a, tile_order, loss_dev, as_stream(stream));
+}
+
+int render_bwd_impl(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                    const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                    const float* final_T, const int32_t* n_contrib, const uint8_t* contrib, const int32_t* tile_order,
+                    const float* dL_dimage, float* grad2d, int32_t accumulate, void* stream) {
+    int rc = render_common_checks(cams, views, set, tile_ranges, splats);
+    if (rc) return rc;
+    if (n < 0 || !final_T || !n_contrib || !dL_dimage) return GS_EINVAL;
+    if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
+    if (n > 0 && (!point_list || !splats || !grad2d || !contrib)) return GS_EINVAL;
+    if (n > 0 && !aligned16(grad2d)) return GS_EALIGN;
+    hipStream_t s = as_stream(stream);
+    if (accumulate != 0 && accumulate != 1) return GS_EINVAL;
+    const int32_t ntot = views * n;
+    if (n > 0 && !accumulate) {
+        const size_t cnt = (size_t)ntot * GS_GRAD2D_STRIDE;
+        hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)std::min<size_t>((cnt + 255) / 256, 4096)), dim3(256), 0, s,
+                           grad2d, cnt);
+    }
+    RenderArgs a{};
+    a.b = blend_views(cams, views, set);
+    a.n = (uint32_t)ntot;
+    a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
+    a.final_T = const_cast<float*>(final_T); a.n_contrib = const_cast<int32_t*>(n_contrib);
+    a.contrib = const_cast<uint8_t*>(contrib);
+    a.dL_dimage = dL_dimage; a.grad2d = grad2d;
+    a.sched = tile_order;
+    hipLaunchKernelGGL(k_render_bwd, dim3(render_grid(cams, views)), dim3(64), 0, s, a);
+    return launch_status();
+}
+
+int count_pairs_impl(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                     const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats, int64_t* counts,
+                     void* stream) {
+    int rc = render_common_checks(cams, views, set, tile_ranges, splats);
+    if (rc) return rc;
+    if (!counts || n < 0) return GS_EINVAL;
+    if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
+    hipStream_t s = as_stream(stream);
+    RenderArgs a{};
+    a.b = blend_views(cams, views, set);
+    a.n = (uint32_t)(views * n);
+    a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
+    auto* c = reinterpret_cast<unsigned long long*>(counts);
+    hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(64), 0, s, c, 3);
+    hipLaunchKernelGGL(k_count_pairs, dim3(tiles_x(cams), tiles_y(cams), views), dim3(256), 0, s, a, c);
+    return launch_status();
+}
+
+}  // namespace
+}  // namespace gs
+
+extern "C" int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
+                             const uint32_t* point_list, const float* splats, float* image, float* final_T,
+                             int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order, void* stream) {
+    return render_fwd_loss_impl(cam, 1, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
+                                tile_order, 0, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+extern "C" int gs_render_fwd_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                                   const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                                   float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
+                                   int32_t* tile_order, void* stream) {
+    return render_fwd_loss_impl(cams, views, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib,
+                                contrib, tile_order, 0, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+extern "C" int gs_render_fwd_loss(const gs_camera* cam, const gs_settings* set, int32_t n,
+                                  const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                                  float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
+                                  int32_t* tile_order, int32_t loss_mode, const float* target, float* dL_dimage,
+                                  double* loss_dev, float* grad2d_clear, void* stream) {
+    if (loss_mode == 0) return GS_EINVAL;
+    return render_fwd_loss_impl(cam, 1, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
+                                tile_order, loss_mode, target, dL_dimage, loss_dev, grad2d_clear, stream);
+}
+
+extern "C" int gs_render_fwd_loss_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                                        const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                                        float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
+                                        int32_t* tile_order, int32_t loss_mode, const float* target,
+                                        float* dL_dimage, double* loss_dev, float* grad2d_clear, void* stream) {
+    if (loss_mode == 0) return GS_EINVAL;
+    return render_fwd_loss_impl(cams, views, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib,
+                                contrib, tile_order, loss_mode, target, dL_dimage, loss_dev, grad2d_clear, stream);
 }
 
 extern "C" int gs_render_bwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                              const uint32_t* point_list, const float* splats, const float* final_T,
                              const int32_t* n_contrib, const uint8_t* contrib, const int32_t* tile_order,
                              const float* dL_dimage, float* grad2d, int32_t accumulate, void* stream) {
-    int rc = render_common_checks(cam, set, tile_ranges, splats);
-    if (rc) return rc;
-    if (n < 0 || !final_T || !n_contrib || !dL_dimage) return GS_EINVAL;
-    if (n > 0 && (!point_list || !splats || !grad2d || !contrib)) return GS_EINVAL;
-    if (n > 0 && !aligned16(grad2d)) return GS_EALIGN;
-    hipStream_t s = as_stream(stream);
-    if (accumulate != 0 && accumulate != 1) return GS_EINVAL;
-    if (n > 0 && !accumulate) {
-        const size_t cnt = (size_t)n * GS_GRAD2D_STRIDE;
-        hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)std::min<size_t>((cnt + 255) / 256, 4096)), dim3(256), 0, s,
-                           grad2d, cnt);
-    }
-    RenderArgs a{};
-    a.b = blend_args(cam, set);
-    a.n = (uint32_t)n;
-    a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
-    a.final_T = const_cast<float*>(final_T); a.n_contrib = const_cast<int32_t*>(n_contrib);
-    a.contrib = const_cast<uint8_t*>(contrib);
-    a.dL_dimage = dL_dimage; a.grad2d = grad2d;
-    a.sched = tile_order;
-    hipLaunchKernelGGL(k_render_bwd, dim3(render_grid(cam)), dim3(64), 0, s, a);
-    return launch_status();
+    return render_bwd_impl(cam, 1, set, n, tile_ranges, point_list, splats, final_T, n_contrib, contrib, tile_order,
+                           dL_dimage, grad2d, accumulate, stream);
+}
+
+extern "C" int gs_render_bwd_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                                   const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                                   const float* final_T, const int32_t* n_contrib, const uint8_t* contrib,
+                                   const int32_t* tile_order, const float* dL_dimage, float* grad2d,
+                                   int32_t accumulate, void* stream) {
+    return render_bwd_impl(cams, views, set, n, tile_ranges, point_list, splats, final_T, n_contrib, contrib,
+                           tile_order, dL_dimage, grad2d, accumulate, stream);
 }
 
 extern "C" int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                               const uint32_t* point_list, const float* splats, int64_t* counts, void* stream) {
-    int rc = render_common_checks(cam, set, tile_ranges, splats);
-    if (rc) return rc;
-    if (!counts || n < 0) return GS_EINVAL;
-    hipStream_t s = as_stream(stream);
-    RenderArgs a{};
-    a.b = blend_args(cam, set);
-    a.n = (uint32_t)n;
-    a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
-    auto* c = reinterpret_cast<unsigned long long*>(counts);
-    hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(64), 0, s, c, 3);
-    hipLaunchKernelGGL(k_count_pairs, dim3(tiles_x(cam), tiles_y(cam)), dim3(256), 0, s, a, c);
-    return launch_status();
+    return count_pairs_impl(cam, 1, set, n, tile_ranges, point_list, splats, counts, stream);
+}
+
+extern "C" int gs_count_pairs_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                                    const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                                    int64_t* counts, void* stream) {
+    return count_pairs_impl(cams, views, set, n, tile_ranges, point_list, splats, counts, stream);
 }

@@ -62,7 +62,11 @@ SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs
            "gs_bin_workspace_size", "gs_bin_sort", "gs_bin_keys", "gs_render_fwd", "gs_render_fwd_loss",
            "gs_render_bwd", "gs_preprocess_bwd", "gs_preprocess_bwd_adam", "gs_preprocess_bwd_adam_geom",
            "gs_preprocess_bwd_adam_sh", "gs_image_loss", "gs_densify_accum", "gs_adam_step", "gs_count_pairs",
-           "gs_densify_workspace_size", "gs_densify", "gs_opacity_reset"]
+           "gs_densify_workspace_size", "gs_densify", "gs_opacity_reset",
+           "gs_preprocess_views", "gs_bin_workspace_size_views", "gs_bin_sort_views", "gs_render_fwd_views",
+           "gs_render_fwd_loss_views", "gs_render_bwd_views", "gs_preprocess_bwd_views",
+           "gs_preprocess_bwd_adam_views", "gs_count_pairs_views"]
+MAX_VIEWS = 8
 PARAM_ORDER = ("means", "log_scales", "quats", "opacity_logits", "sh")
 
 _lib = None
@@ -107,6 +111,17 @@ def load_library(path=LIB_PATH):
     lib.gs_densify.argtypes = [P(GsDensifyParams), _i32, _i32, P(GsGaussianSet), _i64, P(GsGaussianSet),
                                _vp, _vp, _vp, _vp, C.c_size_t, _vp]
     lib.gs_opacity_reset.argtypes = [_i32, C.c_float, _vp, _vp, _vp, _vp]
+    V = [P(GsCamera), _i32]
+    lib.gs_preprocess_views.argtypes = V + [P(GsSettings), _i32, _i32] + [_vp] * 10 + [_vp]
+    lib.gs_bin_workspace_size_views.argtypes = [_i32, P(GsCamera), _i32, _i64, P(C.c_size_t)]
+    lib.gs_bin_sort_views.argtypes = V + [_i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
+    lib.gs_render_fwd_views.argtypes = V + [P(GsSettings), _i32] + [_vp] * 8 + [_vp]
+    lib.gs_render_fwd_loss_views.argtypes = V + [P(GsSettings), _i32] + [_vp] * 8 + [_i32] + [_vp] * 4 + [_vp]
+    lib.gs_render_bwd_views.argtypes = V + [P(GsSettings), _i32] + [_vp] * 9 + [_i32, _vp]
+    lib.gs_preprocess_bwd_views.argtypes = V + [P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
+    lib.gs_preprocess_bwd_adam_views.argtypes = (V + [P(GsSettings), _i32, _i32] + [_vp] * 8 + [P(GsAdamState)] +
+                                                 [_vp] * 7 + [_vp])
+    lib.gs_count_pairs_views.argtypes = V + [P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp]
     for name in SYMBOLS:
         if name not in ("gs_error_string",):
             getattr(lib, name).restype = C.c_int
@@ -503,6 +518,125 @@ def gs_opacity_reset(opacity_logits, factor=OPACITY_RESET_FACTOR, exp_avg=None, 
     _check(rc, "gs_opacity_reset")
 
 
+def camera_array(cams):
+    """A C array of GsCamera for the batched (views) calls."""
+    cams = list(cams)
+    if not 1 <= len(cams) <= MAX_VIEWS:
+        raise GsError(f"1 to {MAX_VIEWS} views, got {len(cams)}")
+    arr = (GsCamera * len(cams))()
+    for i, c in enumerate(cams):
+        arr[i] = camera_struct(c)
+    return arr, len(cams)
+
+
+def gs_preprocess_views(cams, settings, sh_degree, params, splats, depth, rect, tiles_touched, clamp_mask):
+    """Per-view outputs are [views, n, ...]."""
+    f32, n = torch.float32, params["means"].shape[0]
+    arr, v = camera_array(cams)
+    rc = load_library().gs_preprocess_views(
+        arr, v, C.byref(settings.struct()), n, sh_degree, *[_p(params[k], f32, k) for k in PARAM_ORDER],
+        _p(splats, f32, "splats"), _p(depth, f32, "depth"), _p(rect, torch.int16, "rect"),
+        _p(tiles_touched, torch.int32, "tiles_touched"), _p(clamp_mask, torch.uint8, "clamp_mask"), _stream())
+    _check(rc, "gs_preprocess_views")
+
+
+def gs_bin_workspace_size_views(n, cams, key_capacity):
+    arr, v = camera_array(cams)
+    b = C.c_size_t()
+    _check(load_library().gs_bin_workspace_size_views(n, arr, v, key_capacity, C.byref(b)),
+           "gs_bin_workspace_size_views")
+    return b.value
+
+
+def gs_bin_sort_views(cams, n, depth, rect, tiles_touched, key_capacity, point_list, tile_ranges, num_keys,
+                      overflow, workspace):
+    arr, v = camera_array(cams)
+    rc = load_library().gs_bin_sort_views(
+        arr, v, n, _p(depth, torch.float32, "depth"), _p(rect, torch.int16, "rect"),
+        _p(tiles_touched, torch.int32, "tiles_touched"), key_capacity, _p(point_list, torch.int32, "point_list"),
+        _p(tile_ranges, torch.int32, "tile_ranges"), _p(num_keys, torch.int32, "num_keys"),
+        _p(overflow, torch.int32, "overflow"), _p(workspace, torch.uint8, "workspace"), workspace.numel(), _stream())
+    _check(rc, "gs_bin_sort_views")
+
+
+def gs_render_fwd_views(cams, settings, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
+                        tile_order=None, mode=None, target=None, dL_dimage=None, loss_dev=None, grad2d_clear=None):
+    """Forward blend of a batch of views; with mode ('l1' / 'l2') the image loss is fused in
+    (loss_dev [1 + views tiles] float64; loss_dev[0] = the batch's loss)."""
+    arr, v = camera_array(cams)
+    common = (arr, v, C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
+              _p(point_list, torch.int32, "point_list"), _p(splats, torch.float32, "splats"),
+              _p(image, torch.float32, "image"), _p(final_T, torch.float32, "final_T"),
+              _p(n_contrib, torch.int32, "n_contrib"), _p(contrib, torch.uint8, "contrib"),
+              _p(tile_order, torch.int32, "tile_order"))
+    if mode is None:
+        _check(load_library().gs_render_fwd_views(*common, _stream()), "gs_render_fwd_views")
+        return
+    tx, ty = gs_tile_grid(cams[0])
+    if loss_dev.numel() < 1 + v * tx * ty:
+        raise GsError(f"loss buffer needs {1 + v * tx * ty} float64 entries (1 + views tiles)")
+    rc = load_library().gs_render_fwd_loss_views(
+        *common, {"l1": 1, "l2": 2}[mode], _p(target, torch.float32, "target"),
+        _p(dL_dimage, torch.float32, "dL_dimage"), _p(loss_dev, torch.float64, "loss_dev"),
+        _p(grad2d_clear, torch.float32, "grad2d_clear"), _stream())
+    _check(rc, "gs_render_fwd_loss_views")
+
+
+def gs_render_fwd_loss_views(cams, settings, n, tile_ranges, point_list, splats, image, final_T, n_contrib,
+                             contrib, tile_order, mode, target, dL_dimage, loss_dev, grad2d_clear=None):
+    gs_render_fwd_views(cams, settings, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
+                        tile_order, mode, target, dL_dimage, loss_dev, grad2d_clear)
+
+
+def gs_render_bwd_views(cams, settings, n, tile_ranges, point_list, splats, final_T, n_contrib, contrib, dL_dimage,
+                        grad2d, accumulate=False, tile_order=None):
+    arr, v = camera_array(cams)
+    rc = load_library().gs_render_bwd_views(
+        arr, v, C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
+        _p(point_list, torch.int32, "point_list"), _p(splats, torch.float32, "splats"),
+        _p(final_T, torch.float32, "final_T"), _p(n_contrib, torch.int32, "n_contrib"),
+        _p(contrib, torch.uint8, "contrib"), _p(tile_order, torch.int32, "tile_order"),
+        _p(dL_dimage, torch.float32, "dL_dimage"), _p(grad2d, torch.float32, "grad2d"), 1 if accumulate else 0,
+        _stream())
+    _check(rc, "gs_render_bwd_views")
+
+
+def gs_preprocess_bwd_views(cams, settings, sh_degree, params, tiles_touched, clamp_mask, grad2d, out):
+    """3D gradients summed over the views into out (dict of the five groups)."""
+    f32, n = torch.float32, params["means"].shape[0]
+    arr, v = camera_array(cams)
+    rc = load_library().gs_preprocess_bwd_views(
+        arr, v, C.byref(settings.struct()), n, sh_degree, *[_p(params[k], f32, k) for k in PARAM_ORDER],
+        _p(tiles_touched, torch.int32, "tiles_touched"), _p(clamp_mask, torch.uint8, "clamp_mask"),
+        _p(grad2d, f32, "grad2d"), *[_p(out[k], f32, "d" + k) for k in PARAM_ORDER], _stream())
+    _check(rc, "gs_preprocess_bwd_views")
+
+
+def gs_preprocess_bwd_adam_views(cams, settings, sh_degree, params, tiles_touched, clamp_mask, grad2d, exp_avg,
+                                 exp_avg_sq, lr, step, beta1=0.9, beta2=0.999, eps=1e-8, densify_accum=None,
+                                 densify_count=None, grads=None):
+    """One Adam step with the gradients summed over the views (params updated in place)."""
+    f32, n = torch.float32, params["means"].shape[0]
+    arr, v = camera_array(cams)
+    st = _adam_struct(exp_avg, exp_avg_sq, lr, step, beta1, beta2, eps)
+    g = grads or {}
+    rc = load_library().gs_preprocess_bwd_adam_views(
+        arr, v, C.byref(settings.struct()), n, sh_degree, *[_p(params[k], f32, k) for k in PARAM_ORDER],
+        _p(tiles_touched, torch.int32, "tiles_touched"), _p(clamp_mask, torch.uint8, "clamp_mask"),
+        _p(grad2d, f32, "grad2d"), C.byref(st), _p(densify_accum, f32, "densify_accum"),
+        _p(densify_count, torch.int32, "densify_count"), *[_p(g.get(k), f32, "grad." + k) for k in PARAM_ORDER],
+        _stream())
+    _check(rc, "gs_preprocess_bwd_adam_views")
+
+
+def gs_count_pairs_views(cams, settings, n, tile_ranges, point_list, splats, counts):
+    arr, v = camera_array(cams)
+    rc = load_library().gs_count_pairs_views(arr, v, C.byref(settings.struct()), n, _p(tile_ranges, torch.int32),
+                                             _p(point_list, torch.int32), _p(splats, torch.float32),
+                                             _p(counts, torch.int64), _stream())
+    _check(rc, "gs_count_pairs_views")
+
+
 # ---------------------------------------------------------------------------
 # Buffer owner for one camera and one Gaussian count (plumbing: allocation).
 # ---------------------------------------------------------------------------
@@ -626,3 +760,98 @@ class RasterizeFunction(torch.autograd.Function):
 
 def rasterize(rast, means, log_scales, quats, opacity_logits, sh):
     return RasterizeFunction.apply(rast, means, log_scales, quats, opacity_logits, sh)
+
+
+class RasterizerViews:
+    """Buffers of a batch of views of one Gaussian set ([P4] E.1: render a batch of
+    views, sum the losses, one optimizer step), all through the *_views calls.
+    Per-view arrays have a leading views dimension; list entries index
+    splats.view(-1, 12), i.e. entry v n + i is Gaussian i in view v."""
+
+    def __init__(self, cams, n, sh_degree, settings=None, key_capacity=None, device="cuda"):
+        load_library()
+        self.cams = list(cams)
+        self.views = len(self.cams)
+        camera_array(self.cams)  # checks the count
+        cam = self.cams[0]
+        if any(c.width != cam.width or c.height != cam.height for c in self.cams):
+            raise GsError("the views of a batch must share one image size")
+        self.n, self.deg = int(n), int(sh_degree)
+        self.settings = settings or Settings()
+        self.device = torch.device(device)
+        dev, n, V = self.device, self.n, self.views
+        self.tiles_x, self.tiles_y = gs_tile_grid(cam)
+        self.ntiles = V * self.tiles_x * self.tiles_y
+        self.splats = torch.empty((V, n, SPLAT_STRIDE), dtype=torch.float32, device=dev)
+        self.depth = torch.empty((V, n), dtype=torch.float32, device=dev)
+        self.rect = torch.empty((V, n, 4), dtype=torch.int16, device=dev)
+        self.tiles_touched = torch.empty((V, n), dtype=torch.int32, device=dev)
+        self.clamp = torch.empty((V, n), dtype=torch.uint8, device=dev)
+        self.tile_ranges = torch.empty((self.ntiles, 2), dtype=torch.int32, device=dev)
+        self.tile_order = torch.empty((2, self.ntiles), dtype=torch.int32, device=dev)
+        self.num_keys = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.overflow = torch.zeros(1, dtype=torch.int32, device=dev)
+        H, W = cam.height, cam.width
+        self.image = torch.empty((V, 3, H, W), dtype=torch.float32, device=dev)
+        self.final_T = torch.empty((V, H, W), dtype=torch.float32, device=dev)
+        self.n_contrib = torch.empty((V, H, W), dtype=torch.int32, device=dev)
+        self.grad2d = torch.empty((V, n, GRAD2D_STRIDE), dtype=torch.float32, device=dev)
+        self._alloc_lists(key_capacity if key_capacity is not None else max(4 * n * V, 1 << 16))
+
+    def _alloc_lists(self, cap):
+        self.key_capacity = int(cap)
+        self.point_list = torch.empty(max(self.key_capacity, 1), dtype=torch.int32, device=self.device)
+        self.contrib = torch.empty(max(self.key_capacity, 1), dtype=torch.uint8, device=self.device)
+        ws = gs_bin_workspace_size_views(self.n, self.cams, self.key_capacity)
+        self.workspace = torch.empty(ws + 256, dtype=torch.uint8, device=self.device)
+        off = (-self.workspace.data_ptr()) % 256
+        self.workspace = self.workspace[off:off + ws]
+
+    def preprocess(self, p):
+        gs_preprocess_views(self.cams, self.settings, self.deg, p, self.splats, self.depth, self.rect,
+                            self.tiles_touched, self.clamp)
+
+    def bin(self):
+        gs_bin_sort_views(self.cams, self.n, self.depth, self.rect, self.tiles_touched, self.key_capacity,
+                          self.point_list, self.tile_ranges, self.num_keys, self.overflow, self.workspace)
+
+    def render(self):
+        gs_render_fwd_views(self.cams, self.settings, self.n, self.tile_ranges, self.point_list, self.splats,
+                            self.image, self.final_T, self.n_contrib, self.contrib, self.tile_order)
+
+    def render_loss(self, target, mode, dL_dimage, loss_dev, clear_grad2d=True):
+        """loss_dev: [1 + views tiles] float64; loss_dev[0] = the loss summed over the views."""
+        gs_render_fwd_views(self.cams, self.settings, self.n, self.tile_ranges, self.point_list, self.splats,
+                            self.image, self.final_T, self.n_contrib, self.contrib, self.tile_order, mode, target,
+                            dL_dimage, loss_dev, self.grad2d if clear_grad2d else None)
+
+    def forward(self, p, check=True):
+        self.preprocess(p)
+        self.bin()
+        if check and int(self.overflow.item()) != 0:
+            K = int(self.num_keys.item())
+            self._alloc_lists(int(K * 1.25) + 1024)
+            self.bin()
+            assert int(self.overflow.item()) == 0
+        self.render()
+        return self.image
+
+    def backward_2d(self, dL_dimage, accumulate=False):
+        gs_render_bwd_views(self.cams, self.settings, self.n, self.tile_ranges, self.point_list, self.splats,
+                            self.final_T, self.n_contrib, self.contrib, dL_dimage, self.grad2d, accumulate,
+                            self.tile_order[1])
+        return self.grad2d
+
+    def backward(self, p, dL_dimage, out=None):
+        """3D gradients of sum_v <dL_dimage[v], image[v]>, summed over the views."""
+        self.backward_2d(dL_dimage)
+        if out is None:
+            out = {k: torch.empty_like(p[k]) for k in PARAM_ORDER}
+        gs_preprocess_bwd_views(self.cams, self.settings, self.deg, p, self.tiles_touched, self.clamp, self.grad2d,
+                                out)
+        return out
+
+    def count_pairs(self):
+        c = torch.zeros(3, dtype=torch.int64, device=self.device)
+        gs_count_pairs_views(self.cams, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, c)
+        return c

@@ -268,3 +268,21 @@ def densify_case(seed, n, sh_degree=3, with_moments=True):
         out["exp_avg_sq"] = {k: rng.uniform(0.0, 1e-5, np.shape(out[k])).astype(np.float32)
                              for k in ("means", "log_scales", "quats", "opacity_logits", "sh")}
     return out
+
+
+def orbit_cameras(cam, views, centre, step_deg=8.0):
+    """A batch of `views` cameras with cam's intrinsics on a horizontal arc around
+    `centre`: view v is cam turned by (v - (views - 1) / 2) step_deg about the
+    vertical axis through centre, so every view looks at the scene the way cam
+    does (for an odd count the middle view is cam itself)."""
+    c = np.asarray(centre, dtype=np.float64)
+    R0, t0 = np.asarray(cam.R, np.float64), np.asarray(cam.t, np.float64)
+    pos0 = -R0.T @ t0  # camera centre in world coordinates
+    out = []
+    for v in range(views):
+        th = math.radians((v - (views - 1) / 2.0) * step_deg)
+        Ry = np.array([[math.cos(th), 0.0, math.sin(th)], [0.0, 1.0, 0.0], [-math.sin(th), 0.0, math.cos(th)]])
+        pos = c + Ry @ (pos0 - c)
+        R = R0 @ Ry.T
+        out.append(Camera(cam.width, cam.height, cam.fx, cam.fy, cam.cx, cam.cy, R, -R @ pos))
+    return out

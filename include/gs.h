@@ -46,6 +46,7 @@ extern "C" {
 #define GS_SPLAT_STRIDE 12  /* floats per projected-Gaussian record */
 #define GS_GRAD2D_STRIDE 12 /* floats per 2D-gradient record */
 #define GS_MAX_SH_DEGREE 3
+#define GS_MAX_VIEWS 8      /* views one batched call renders */
 
 enum {
     GS_OK = 0,
@@ -429,6 +430,66 @@ int gs_opacity_reset(int32_t n, float factor, float* opacity_logits, float* exp_
  */
 int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                    const uint32_t* point_list, const float* splats, int64_t* counts, void* stream);
+
+/*
+ * Batched views ([P4] E.1 steps 1-3: an iteration renders a batch of views,
+ * sums their losses, back-propagates and takes one optimizer step).  The
+ * *_views calls take an array of `views` cameras (1 <= views <= GS_MAX_VIEWS),
+ * all of one image size, and lay per-view outputs out view-major:
+ *  - per-Gaussian arrays are [views, n, ...]: entry v n + i of splats, depth,
+ *    rect, tiles_touched, clamp_mask, grad2d and of the point list's values
+ *    is Gaussian i seen from view v (n = Gaussians, the same set in every
+ *    view; rect is in view v's own tile coordinates);
+ *  - tiles are numbered view after view: tile v T + t is tile t of view v
+ *    (T = tiles of one view), and tile_ranges [views T, 2], tile_order
+ *    [2, views T] and the loss partials loss_dev [1 + views T] cover them all;
+ *    views T must stay <= 65536 for gs_bin_sort_views;
+ *  - images are [views, 3, H, W], final_T and n_contrib [views, H, W].
+ * Otherwise each call means what its single-view counterpart means, view by
+ * view; with views == 1 it is that counterpart.  gs_preprocess_bwd_views
+ * returns the gradients summed over the views (the batch's loss is the sum of
+ * the views' losses); gs_preprocess_bwd_adam_views applies one Adam step with
+ * those sums, and its densification statistic adds, for every view in which a
+ * Gaussian touches a tile, that view's |dL/d(u,v)| and one count.
+ * Workspace: gs_bin_workspace_size_views.
+ */
+int gs_preprocess_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n, int32_t sh_degree,
+                        const float* means, const float* log_scales, const float* quats,
+                        const float* opacity_logits, const float* sh, float* splats, float* depth, int16_t* rect,
+                        int32_t* tiles_touched, uint8_t* clamp_mask, void* stream);
+int gs_bin_workspace_size_views(int32_t n, const gs_camera* cams, int32_t views, int64_t key_capacity,
+                                size_t* bytes);
+int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n, const float* depth, const int16_t* rect,
+                      const int32_t* tiles_touched, int64_t key_capacity, uint32_t* point_list,
+                      uint32_t* tile_ranges, uint32_t* num_keys_dev, uint32_t* overflow_dev, void* workspace,
+                      size_t workspace_bytes, void* stream);
+int gs_render_fwd_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                        const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats, float* image,
+                        float* final_T, int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order, void* stream);
+int gs_render_fwd_loss_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                             const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                             float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
+                             int32_t* tile_order, int32_t loss_mode, const float* target, float* dL_dimage,
+                             double* loss_dev, float* grad2d_clear, void* stream);
+int gs_render_bwd_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                        const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                        const float* final_T, const int32_t* n_contrib, const uint8_t* contrib,
+                        const int32_t* tile_order, const float* dL_dimage, float* grad2d, int32_t accumulate,
+                        void* stream);
+int gs_preprocess_bwd_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                            int32_t sh_degree, const float* means, const float* log_scales, const float* quats,
+                            const float* opacity_logits, const float* sh, const int32_t* tiles_touched,
+                            const uint8_t* clamp_mask, const float* grad2d, float* dmeans, float* dlog_scales,
+                            float* dquats, float* dopacity_logits, float* dsh, void* stream);
+int gs_preprocess_bwd_adam_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                                 int32_t sh_degree, float* means, float* log_scales, float* quats,
+                                 float* opacity_logits, float* sh, const int32_t* tiles_touched,
+                                 const uint8_t* clamp_mask, const float* grad2d, const gs_adam_state* adam,
+                                 float* densify_accum, int32_t* densify_count, float* dmeans, float* dlog_scales,
+                                 float* dquats, float* dopacity_logits, float* dsh, void* stream);
+int gs_count_pairs_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+                         const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
+                         int64_t* counts, void* stream);
 
 #ifdef __cplusplus
 }

@@ -257,6 +257,28 @@ def render(cam, deg, params, s: Settings = None, dL_dimage=None, brute=False, am
     return res
 
 
+def render_views(cams, deg, params, dL_dimages, s: Settings = None, mask_ambiguous=True):
+    """A batch of views ([P4] E.1 steps 1-2: render every view of the batch; the
+    batch's loss is the sum of the views' losses, so its gradient is the sum of
+    the views' gradients).  dL_dimages [views, 3, H, W].  With mask_ambiguous the
+    upstream gradient is zeroed at each view's ambiguous pixels (as in the
+    single-view parity tests).  Returns the per-view forward results and the 3D
+    gradients summed over the views."""
+    s = s or Settings()
+    per_view, total = [], None
+    for cam, dL in zip(cams, dL_dimages):
+        o = render(cam, deg, params, s, backward=False)
+        dL = np.asarray(dL, np.float64)
+        if mask_ambiguous:
+            dL = dL * ((o["ambiguous"] & 3) == 0)[None]
+        g2d = render_bwd(cam, o["pre"], o["point_list"], o["ranges"], dL, s)
+        g3d = preprocess_bwd(cam, deg, params, o["pre"]["tiles_touched"], g2d, s)
+        o["g2d"], o["g3d"], o["dL_used"] = g2d, g3d, dL
+        per_view.append(o)
+        total = {k: v.copy() for k, v in g3d.items()} if total is None else {k: total[k] + g3d[k] for k in total}
+    return per_view, total
+
+
 @dataclass
 class DensifyParams:
     """The numbers [P4] D.1-D.3 leave out (see orc_densify_apply).  Values are
