@@ -17,6 +17,7 @@ binning, forward (with the per-pixel loss gradient the backward starts from),
 backward blend and the unfused 2D->3D backward that writes the 3D gradients
 (no optimizer).  `densify` times the densify / split / clone / prune pass
 (run every 100 training steps, so not part of the step) on the trained state.
+`views` times a batched training step over --views orbit views of the same scene.
 """
 from __future__ import annotations
 
@@ -53,6 +54,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--views", type=int, default=4,
+                    help="views of the batched training step measured beside the main one (1 skips it)")
     ap.add_argument("--overlap", choices=("none", "color", "sh"), default="none",
                     help="work moved to a second stream: none, the SH colour pass (color), or the colour pass and "
                          "the SH half of the Adam tail (sh)")
@@ -213,6 +216,78 @@ class Step:
                                   g["log_scales"], g["quats"], g["opacity_logits"], g["sh"])
 
 
+def views_measure(sc, views, steps, warmup):
+    """A batched training step ([P4] E.1: a batch of views rendered, their L1 losses summed,
+    one Adam step): `views` orbit cameras around the train1m scene, each with its own
+    random target, through the *_views calls.  Fresh parameters and Adam state, so it
+    does not disturb the main measurement."""
+    import torch
+    from differentiable_gaussian_splatting_dgs_amd import gs, scenes
+    dev = "cuda"
+    centre = (0.0, 0.0, float(np.median(np.asarray(sc.means[:, 2], np.float64))))
+    cams = scenes.orbit_cameras(sc.cam, views, centre, step_deg=8.0)
+    rng = np.random.default_rng(11)
+    target = torch.from_numpy(rng.uniform(0, 1, (views, 3, sc.cam.height, sc.cam.width)).astype(np.float32)).to(dev)
+    p = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in sc.params().items()}
+    m = {k: torch.zeros_like(v) for k, v in p.items()}
+    v2 = {k: torch.zeros_like(v) for k, v in p.items()}
+    acc = torch.zeros(sc.n, dtype=torch.float32, device=dev)
+    cnt = torch.zeros(sc.n, dtype=torch.int32, device=dev)
+    rv = gs.RasterizerViews(cams, sc.n, sc.sh_degree)
+    dL = torch.empty_like(target)
+    loss = torch.zeros(1 + rv.ntiles, dtype=torch.float64, device=dev)
+    lr = dict(scenes.ADAM_LR)
+    stages = ["preprocess", "bin_sort", "render_fwd_loss", "render_bwd", "grad3d_densify_adam"]
+    step_no = [0]
+
+    def run(ev=None, check=False):
+        step_no[0] += 1
+
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        rv.preprocess(p)
+        mark(1)
+        rv.bin()
+        if check and int(rv.overflow.item()) != 0:
+            rv._alloc_lists(int(int(rv.num_keys.item()) * 1.25) + 1024)
+            rv.bin()
+        mark(2)
+        rv.render_loss(target, "l1", dL, loss, clear_grad2d=True)
+        mark(3)
+        rv.backward_2d(dL, accumulate=True)
+        mark(4)
+        gs.gs_preprocess_bwd_adam_views(cams, rv.settings, sc.sh_degree, p, rv.tiles_touched, rv.clamp, rv.grad2d,
+                                        m, v2, lr, step_no[0], densify_accum=acc, densify_count=cnt)
+        mark(5)
+
+    run(check=True)
+    for _ in range(max(0, warmup - 1)):
+        run()
+    torch.cuda.synchronize()
+    c0 = rv.count_pairs().cpu().numpy()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run(evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    assert int(rv.overflow.item()) == 0, "list capacity overflow during the batched timing"
+    c1 = rv.count_pairs().cpu().numpy()
+    stage_ms = {name: round(float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])), 4)
+                for j, name in enumerate(stages)}
+    pairs = float((c0[0] + c1[0]) / 2 + (c0[1] + c1[1]) / 2)
+    out = dict(workload=f"train1m x {views} views: {views} orbit cameras 8 degrees apart around the scene, "
+                        f"one L1 target each, losses summed, one Adam step",
+               views=views, ms_per_step=round(ms, 4), ms_per_view=round(ms / views, 4),
+               pairs_per_s=float(pairs / (ms * 1e-3)), keys=int(rv.num_keys.item()), stage_ms=stage_ms)
+    del rv, p, m, v2
+    torch.cuda.empty_cache()
+    return out
+
+
 def densify_measure(st, reps):
     """gs_densify (densify, split or clone, prune) on the trained state: the parameters, Adam moments
     and the statistic the steps above accumulated.  Out of place, so every repetition does the same
@@ -362,6 +437,7 @@ def main():
     torch.cuda.synchronize()
     pbwd_ms = float(np.mean([a.elapsed_time(b) for a, b in pe]))
     dens = densify_measure(st, max(3, min(args.steps, 10)))
+    mv = views_measure(sc, args.views, args.steps, args.warmup) if args.views > 1 else None
     stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, name in enumerate(st.stages)}
     ms = elapsed * 1e3 / args.steps
@@ -407,6 +483,8 @@ def main():
                           keys=int(st.rast.num_keys.item())),
                roofline=roof,
                densify=dens)
+    if mv is not None:
+        out["views"] = mv
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         cb = cpu_baseline(sc, args.cpu_tile_fraction)
