@@ -138,9 +138,27 @@ __device__ __forceinline__ void adam_reg(float& p, float g, float& m, float& v, 
 // quaternion and opacity logit, plus the SH basis and the clamp-masked colour
 // gradient the SH coefficients need.  ddir needs the SH coefficients, read
 // from the block's LDS copy (coefficient-major, row stride ldg).
-// Gaussian i seen by camera c; iv indexes its view's 2D gradient and clamp mask.
+// One view's inputs of the chain for one Gaussian: its 2D-gradient record,
+// clamp mask and tile count (loaded ahead of use so a view loop can prefetch).
+struct ViewIn {
+    float4 g0, g1, g2;
+    int32_t tt;
+    uint8_t cm;
+};
+
+__device__ __forceinline__ ViewIn load_view(const BwdArgs& a, size_t iv) {
+    ViewIn w;
+    w.g0 = reinterpret_cast<const float4*>(a.grad2d)[3 * iv];
+    w.g1 = reinterpret_cast<const float4*>(a.grad2d)[3 * iv + 1];
+    w.g2 = reinterpret_cast<const float4*>(a.grad2d)[3 * iv + 2];
+    w.tt = a.tt[iv];
+    w.cm = a.clamp[iv];
+    return w;
+}
+
+// Gaussian i seen by camera c, with that view's inputs w.
 template <int DEG>
-__device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i, size_t iv, const float* s_sh,
+__device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i, const ViewIn& w, const float* s_sh,
                                       int col, int ldg, float dmu[3], float dls[3], float dq[4], float& dop,
                                       float Y[16], float drgb[3], float dir[3]) {
     constexpr int K = (DEG + 1) * (DEG + 1);
@@ -152,9 +170,7 @@ __device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i,
     const float ty = Rv[3] * mx + Rv[4] * my + Rv[5] * mz + (float)c.t[1];
     const float tz = Rv[6] * mx + Rv[7] * my + Rv[8] * mz + (float)c.t[2];
 
-    const float4 g0 = reinterpret_cast<const float4*>(a.grad2d)[3 * iv];
-    const float4 g1 = reinterpret_cast<const float4*>(a.grad2d)[3 * iv + 1];
-    const float4 g2 = reinterpret_cast<const float4*>(a.grad2d)[3 * iv + 2];
+    const float4 g0 = w.g0, g1 = w.g1, g2 = w.g2;
     const float du = g0.x, dv = g0.y, dA = g0.z, dB = g0.w, dC = g1.x, dsig = g1.y;
     drgb[0] = g1.z; drgb[1] = g1.w; drgb[2] = g2.x;
 
@@ -170,18 +186,18 @@ __device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i,
     const float il = 1.f / sqrtf(vx * vx + vy * vy + vz * vz);
     const float dx = vx * il, dy = vy * il, dz = vz * il;
     dir[0] = dx; dir[1] = dy; dir[2] = dz;
-    const uint8_t cm = a.clamp[iv];
+    const uint8_t cm = w.cm;
 #pragma unroll
     for (int ch = 0; ch < 3; ++ch)
         if ((cm >> ch) & 1u) drgb[ch] = 0.f;
     sh_values<DEG>(dx, dy, dz, Y);
-    float w[16];
+    float wk[16];
 #pragma unroll
     for (int k = 0; k < K; ++k)
-        w[k] = drgb[0] * s_sh[(3 * k) * ldg + col] + drgb[1] * s_sh[(3 * k + 1) * ldg + col] +
-               drgb[2] * s_sh[(3 * k + 2) * ldg + col];
+        wk[k] = drgb[0] * s_sh[(3 * k) * ldg + col] + drgb[1] * s_sh[(3 * k + 1) * ldg + col] +
+                drgb[2] * s_sh[(3 * k + 2) * ldg + col];
     float gdx, gdy, gdz;
-    sh_grad<DEG>(dx, dy, dz, w, gdx, gdy, gdz);
+    sh_grad<DEG>(dx, dy, dz, wk, gdx, gdy, gdz);
     const float dot = dx * gdx + dy * gdy + dz * gdz;
     float dmx = (gdx - dx * dot) * il, dmy = (gdy - dy * dot) * il, dmz = (gdz - dz * dot) * il;
 
@@ -395,12 +411,15 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < J; ++j) s_y[j * LDG + t] = 0.f;
             bool seen = false;
+            ViewIn cur = load_view(a, (size_t)i);
             for (int view = 0; view < a.views; ++view) {
-                const size_t iv = (size_t)view * a.n + i;
-                if (a.tt[iv] <= 0) continue;
+                // the next view's loads go out before this view's chain
+                ViewIn nxt = cur;
+                if (view + 1 < a.views) nxt = load_view(a, (size_t)(view + 1) * a.n + i);
+                if (cur.tt <= 0) { cur = nxt; continue; }
                 seen = true;
                 float vmu[3], vls[3], vq[4], vop;
-                chain<DEG>(a, a.cams[view], i, iv, s_sh, t, LDG, vmu, vls, vq, vop, Y, drgb, dir);
+                chain<DEG>(a, a.cams[view], i, cur, s_sh, t, LDG, vmu, vls, vq, vop, Y, drgb, dir);
 #pragma unroll
                 for (int k = 0; k < 3; ++k) { dmu[k] += vmu[k]; dls[k] += vls[k]; }
 #pragma unroll
@@ -411,10 +430,10 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
 #pragma unroll
                     for (int ch = 0; ch < 3; ++ch) s_y[(3 * k + ch) * LDG + t] += Y[k] * drgb[ch];
                 if (a.accum) {
-                    const float2 d2 = *reinterpret_cast<const float2*>(a.grad2d + iv * GS_GRAD2D_STRIDE);
-                    acc += sqrtf(d2.x * d2.x + d2.y * d2.y);
+                    acc += sqrtf(cur.g0.x * cur.g0.x + cur.g0.y * cur.g0.y);
                     nvis += 1;
                 }
+                cur = nxt;
             }
             if (a.accum && seen) {
                 a.accum[i] = acc;
@@ -423,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
         } else {
             const bool vis = a.tt[i] > 0;
             if (vis) {
-                chain<DEG>(a, a.cams[0], i, (size_t)i, s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb, dir);
+                chain<DEG>(a, a.cams[0], i, load_view(a, (size_t)i), s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb, dir);
                 if (a.accum) {
                     const float2 d2 = *reinterpret_cast<const float2*>(a.grad2d + (size_t)i * GS_GRAD2D_STRIDE);
                     a.accum[i] = acc + sqrtf(d2.x * d2.x + d2.y * d2.y);
