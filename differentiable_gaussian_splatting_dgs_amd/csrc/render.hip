@@ -238,9 +238,9 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
             {
                 const bool pass = !done && pa.alpha >= b.alpha_min;
                 const float Tn = trans_after(T, pa.alpha);
-                const bool low = Tn < b.T_min;
-                done = done || (pass && low);
-                const bool ok = pass && !low;
+                const bool stop = pass && Tn < b.T_min;  // ok = pass and not stop (stop implies pass)
+                done = done || stop;
+                const bool ok = pass != stop;
                 const float w = ok ? pa.alpha * T : 0.f;
                 C0 = __builtin_fmaf(w, ga1.z, C0);
                 C1 = __builtin_fmaf(w, ga1.w, C1);
@@ -252,9 +252,9 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
             {
                 const bool pass = has2 && !done && pb.alpha >= b.alpha_min;
                 const float Tn = trans_after(T, pb.alpha);
-                const bool low = Tn < b.T_min;
-                done = done || (pass && low);
-                const bool ok = pass && !low;
+                const bool stop = pass && Tn < b.T_min;  // ok = pass and not stop (stop implies pass)
+                done = done || stop;
+                const bool ok = pass != stop;
                 const float w = ok ? pb.alpha * T : 0.f;
                 C0 = __builtin_fmaf(w, gb1.z, C0);
                 C1 = __builtin_fmaf(w, gb1.w, C1);
