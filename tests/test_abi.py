@@ -2,6 +2,7 @@
 include/gs.h declares, the binding wraps each under the same name, and the
 host-only calls (no device work) behave."""
 import ctypes as C
+import math
 import os
 import re
 
@@ -74,3 +75,42 @@ def test_scene_generators_deterministic():
     assert s.sh.shape == (100_000, 16, 3) and s.loss == "l2" and s.target.shape == (3, 800, 800)
     r = np.linalg.norm(s.means - np.array([0, 0, 4], np.float32), axis=1)
     assert r.max() <= 1.5 + 1e-5
+
+
+def test_views_and_densify_host_checks():
+    """Host-side sizes and argument checks of the batched-view and densify calls (no device work)."""
+    from differentiable_gaussian_splatting_dgs_amd import gs, scenes
+    lib = gs.load_library()
+    cam = scenes.Camera.identity(1920, 1080, 1500.0)
+    cams = scenes.orbit_cameras(cam, 4, (0.0, 0.0, 6.0))
+    # a batch bins views x n records: its workspace is the single-view one for that many Gaussians
+    assert gs.gs_bin_workspace_size_views(1000, cams, 50000) == gs.gs_bin_workspace_size(4000, cam, 50000)
+    with pytest.raises(gs.GsError):
+        gs.camera_array([])
+    with pytest.raises(gs.GsError):
+        gs.camera_array([cam] * 9)
+    b = C.c_size_t()
+    arr, v = gs.camera_array([cam, scenes.Camera.identity(1280, 720, 1000.0)])
+    assert lib.gs_bin_workspace_size_views(100, arr, v, 1000, C.byref(b)) == -1   # views of different sizes
+    arr9 = (gs.GsCamera * 9)(*([gs.camera_struct(cam)] * 9))
+    assert lib.gs_bin_workspace_size_views(100, arr9, 9, 1000, C.byref(b)) == -1   # more than GS_MAX_VIEWS
+    # densify workspace
+    w1, w2 = gs.gs_densify_workspace_size(1000), gs.gs_densify_workspace_size(2000)
+    assert w2 > w1 > 0 and w1 % 256 == 0 and gs.gs_densify_workspace_size(0) == 0
+    with pytest.raises(gs.GsError):
+        gs.gs_densify_workspace_size(-1)
+    # the readings' defaults reach the library as the thresholds the comparisons use
+    st = gs.DensifyParams(1.5).struct()
+    assert abs(st.prune_logit - math.log(0.005 / 0.995)) < 1e-6
+    assert abs(st.split_log_gap - math.log(2.0)) < 1e-7 and abs(st.split_shrink - math.log(1.6)) < 1e-7
+    assert abs(gs.DensifyParams.threshold_for(1080) - 1.62) < 1e-9
+    # checks that return before any launch
+    assert lib.gs_opacity_reset(10, 0.0, None, None, None, None) == -1
+    assert lib.gs_opacity_reset(10, 1.5, None, None, None, None) == -1
+    assert lib.gs_opacity_reset(0, 0.3, None, None, None, None) == 0
+    fake = C.c_void_p(1 << 20)  # never dereferenced: every call below fails its checks first
+    inp, out = gs.GsGaussianSet(), gs.GsGaussianSet()
+    assert lib.gs_densify(C.byref(st), 10, 4, C.byref(inp), 20, C.byref(out), fake, fake, None, fake, 1 << 20,
+                          None) == -1  # SH degree 4
+    assert lib.gs_densify(C.byref(st), 10, 3, C.byref(inp), 20, C.byref(out), fake, fake, None, fake, 0,
+                          None) == -3  # workspace too small
