@@ -428,14 +428,16 @@ def main():
     assert int(st.rast.overflow.item()) == 0, "list capacity overflow during timing"
     c1 = st.rast.count_pairs().cpu().numpy()
     torch.cuda.synchronize()
-    # the rasterizer's own 2D->3D backward (gradients written, no Adam), timed on the same state
-    pe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        pe[i][0].record()
+    # the rasterizer's own 2D->3D backward (gradients written, no Adam), timed on the same state: back-to-back
+    # launches behind an untimed one, so the host's per-call cost overlaps the kernels instead of adding idle gaps
+    pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    st.preprocess_bwd()
+    pe[0].record()
+    for _ in range(args.steps):
         st.preprocess_bwd()
-        pe[i][1].record()
+    pe[1].record()
     torch.cuda.synchronize()
-    pbwd_ms = float(np.mean([a.elapsed_time(b) for a, b in pe]))
+    pbwd_ms = float(pe[0].elapsed_time(pe[1])) / args.steps
     dens = densify_measure(st, max(3, min(args.steps, 10)))
     mv = views_measure(sc, args.views, args.steps, args.warmup) if args.views > 1 else None
     stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
@@ -449,6 +451,22 @@ def main():
     # per-pixel loss gradient, which the backward needs as its input)
     raster_ms = sum(stage_ms[k] for k in (st.stages[0], "bin_sort", "render_fwd_loss", "render_bwd"))
     raster_ms += pbwd_ms
+
+    # the rasterizer's roofline fraction: sum over its stages of the time the binding peak allows for the
+    # stage's algorithmic bytes or flops, over the measured fwd+bwd time
+    N, K = sc.n, float(st.rast.num_keys.item())
+    hbm = PEAK_HBM_GBS * 1e9
+    fl = PEAK_FP32_TFLOPS * 1e12
+    tmin = dict(
+        preprocess=301.0 * N / hbm,                                        # 236 B in, 65 B out
+        bin_sort=(16 * N + 4 * 16 * N + 20 * N + 8 * K + 2 * 16 * K + 4 * K) / hbm,  # keys, 4 depth passes,
+                                                                           # emission, 2 tile passes, ranges
+        render_fwd=(FLOPS_EVAL * p_fwd + FLOPS_FWD_BLEND * p_blend) / fl,
+        render_bwd=(FLOPS_EVAL * p_bwd + FLOPS_BWD_BLEND * p_blend) / fl,
+        preprocess_bwd=513.0 * N / hbm)        # 236 B params + 36 B 2D gradients + 5 B count/clamp in, 236 B out
+    raster_roof = dict(t_min_us={k: round(v * 1e6, 2) for k, v in tmin.items()},
+                       t_min_sum_us=round(sum(tmin.values()) * 1e6, 2),
+                       frac=round(sum(tmin.values()) / (raster_ms * 1e-3), 4))
 
     # roofline of the dominant kernel (render_bwd: FP32 VALU bound)
     dom = max(("render_fwd_loss", "render_bwd"), key=lambda k: stage_ms[k])
@@ -471,7 +489,7 @@ def main():
                            tile=16, parallelism="single-gpu"),
                fwd_bwd=dict(ms=round(raster_ms, 4), pairs_per_s=float(pairs / (raster_ms * 1e-3)),
                             stages=f"{st.stages[0]} + bin_sort + render_fwd_loss + render_bwd + preprocess_bwd",
-                            preprocess_bwd_ms=round(pbwd_ms, 4)),
+                            preprocess_bwd_ms=round(pbwd_ms, 4), roofline=raster_roof),
                stage_ms={k: round(v, 4) for k, v in stage_ms.items()},
                schedule={"none": "one stream",
                          "color": "two streams: the SH colour pass runs on a second stream while the main stream "

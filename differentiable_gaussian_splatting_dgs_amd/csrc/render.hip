@@ -491,23 +491,24 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
                 const Pair p = eval_pair(fxq[q], fyq[q], G0, G1, b.alpha_max);
                 const bool ok = pos < nc[q] && p.alpha >= b.alpha_min;
                 const float ae = ok ? p.alpha : 0.f;
-                const float Tp = T[q] * __builtin_amdgcn_rcpf(1.f - p.alpha);  // transmittance before the entry
-                T[q] = ok ? Tp : T[q];
+                // transmittance before the entry; a pair that is not blended divides by
+                // 1 - 0 = 1, whose reciprocal is exact, so T is left as it was
+                T[q] = T[q] * __builtin_amdgcn_rcpf(1.f - ae);
                 const float w = ae * T[q];
                 const float gc = __builtin_fmaf(gp2[q], G2.x, __builtin_fmaf(gp1[q], G1.w, gp0[q] * G1.z));
                 const float dS = gc - S[q];
                 const float dalpha = T[q] * dS;
                 S[q] = __builtin_fmaf(ae, dS, S[q]);
                 const float dsG = (ok && !(p.sG > b.alpha_max)) ? dalpha : 0.f;  // clamped: no dependence
-                const float gG = dsG * p.G;            // dL/dopacity
-                const float dpow = gG * G1.y;          // dL/dpower, G = exp(power)
+                // dL/dopacity = dsG G; dL/dpower = dsG opacity G, G = exp(power)
+                const float dpow = dsG * p.sG;
                 const float t = dpow * p.dx, sy = dpow * p.dy;
                 v[0] += t;
                 v[1] += sy;
                 v[2] = __builtin_fmaf(t, p.dx, v[2]);
                 v[3] = __builtin_fmaf(t, p.dy, v[3]);
                 v[4] = __builtin_fmaf(sy, p.dy, v[4]);
-                v[5] += gG;
+                v[5] = __builtin_fmaf(dsG, p.G, v[5]);
                 v[6] = __builtin_fmaf(w, gp0[q], v[6]);
                 v[7] = __builtin_fmaf(w, gp1[q], v[7]);
                 v[8] = __builtin_fmaf(w, gp2[q], v[8]);
