@@ -315,30 +315,41 @@ __device__ __forceinline__ void sh_elements(const BwdArgs& a, const float* s_sh,
                                             const float* s_c, int cnt, size_t base, int t) {
     constexpr int J = 3 * (DEG + 1) * (DEG + 1);
     constexpr int kChunk = 8;
+    const AdamHyper& h = a.adam;
+    float* const dsh = a.dsh;
     for (int e0 = t; e0 < cnt; e0 += kChunk * kThreads) {
-        float mv[kChunk], vv[kChunk], pv[kChunk];
+        // Every read of the chunk, from HBM and from LDS, is issued before its first
+        // store.  Indices past the end are clamped to the last element (cnt >= 1);
+        // their values are never stored.
+        float mv[kChunk], vv[kChunk], pv[kChunk], gr[kChunk];
+        bool band0[kChunk];
         if (ADAM) {
 #pragma unroll
             for (int c = 0; c < kChunk; ++c) {
-                const int e = e0 + c * kThreads;
-                mv[c] = e < cnt ? nt_ld(&a.adam.m[4][base + e]) : 0.f;
-                vv[c] = e < cnt ? nt_ld(&a.adam.v[4][base + e]) : 0.f;
-                pv[c] = (!s_sh && e < cnt) ? a.sh[base + e] : 0.f;
+                const int e = min(e0 + c * kThreads, cnt - 1);
+                mv[c] = nt_ld(&h.m[4][base + e]);
+                vv[c] = nt_ld(&h.v[4][base + e]);
+                pv[c] = s_sh ? 0.f : a.sh[base + e];
             }
+        }
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+            const int e = min(e0 + c * kThreads, cnt - 1);
+            const int g = e / J, j = e - g * J;
+            const int k = j / 3, ch = j - 3 * k;
+            // MV: s_y holds the gradient itself (summed over the views), coefficient-major
+            gr[c] = MV ? s_y[j * LDG + g] : s_y[k * LDG + g] * s_c[ch * LDG + g];
+            if (ADAM && s_sh) pv[c] = s_sh[j * LDG + g];
+            band0[c] = k == 0;
         }
 #pragma unroll
         for (int c = 0; c < kChunk; ++c) {
             const int e = e0 + c * kThreads;
             if (e >= cnt) break;
-            const int g = e / J, j = e - g * J;
-            const int k = j / 3, ch = j - 3 * k;
-            // MV: s_y holds the gradient itself (summed over the views), coefficient-major
-            const float grad = MV ? s_y[j * LDG + g] : s_y[k * LDG + g] * s_c[ch * LDG + g];
-            if (a.dsh) a.dsh[base + e] = grad;
+            if (dsh) dsh[base + e] = gr[c];
             if (ADAM) {
-                const AdamHyper& h = a.adam;
-                float p = s_sh ? s_sh[j * LDG + g] : pv[c];
-                adam_reg(p, grad, mv[c], vv[c], k == 0 ? h.lr[4] : h.lr[5], h);
+                float p = pv[c];
+                adam_reg(p, gr[c], mv[c], vv[c], band0[c] ? h.lr[4] : h.lr[5], h);
                 a.sh[base + e] = p;
                 nt_st(mv[c], &h.m[4][base + e]);
                 nt_st(vv[c], &h.v[4][base + e]);
@@ -374,10 +385,26 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
     const int cnt = ng * J;
     const size_t base = (size_t)g0 * J;
 
-#pragma unroll 4
-    for (int e = t; e < cnt; e += kThreads) {
-        const int g = e / J, j = e - g * J;
-        s_sh[j * LDG + g] = a.sh[base + e];
+    {
+        // every load of the thread's share is issued before the first LDS store,
+        // so the block waits for one memory latency instead of one per batch
+        constexpr int kPer = (J * kG + kThreads - 1) / kThreads;
+        // a copy of the thread index the compiler cannot see through, so that it does
+        // not keep this phase's index arithmetic alive for the element-wise phase
+        int tl = t;
+        asm volatile("" : "+v"(tl));
+        float r[kPer];
+#pragma unroll
+        for (int c = 0; c < kPer; ++c)  // clamped (cnt >= 1): no branch around the loads
+            r[c] = a.sh[base + min(tl + c * kThreads, cnt - 1)];
+#pragma unroll
+        for (int c = 0; c < kPer; ++c) {
+            const int e = tl + c * kThreads;
+            if (e < cnt) {
+                const int g = e / J, j = e - g * J;
+                s_sh[j * LDG + g] = r[c];
+            }
+        }
     }
     __syncthreads();
 
