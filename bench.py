@@ -288,6 +288,58 @@ def views_measure(sc, views, steps, warmup):
     return out
 
 
+def measure_peaks(reps=5):
+    """What this GPU delivers on the two binding resources, timed with HIP events:
+    HBM with the library's non-temporal copy over 1 GiB (2 GiB of traffic), fp32
+    with its FMA loop (8 independent chains per lane, 8 waves per SIMD).  Median
+    of `reps` timed calls after one untimed call."""
+    import torch
+    from differentiable_gaussian_splatting_dgs_amd import gs
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def timed(fn):
+        fn()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(out))
+    t_copy = timed(lambda: gs.gs_stream_copy(src, dst))
+    del src, dst
+    blocks, iters = 256 * 8, 512
+    out = torch.empty(blocks * gs.FMA_LOOP_THREADS, dtype=torch.float32, device="cuda")
+    t_fma = timed(lambda: gs.gs_fma_loop(blocks, iters, 1.0000001, 1e-7, out))
+    flops = blocks * gs.FMA_LOOP_THREADS * iters * gs.FMA_LOOP_FLOPS_PER_ITER
+    return dict(hbm_gbs=dict(spec=PEAK_HBM_GBS, measured=round(8.0 * n / t_copy / 1e9, 1),
+                             kernel="gs_stream_copy, 1 GiB"),
+                fp32_tflops=dict(spec=PEAK_FP32_TFLOPS, measured=round(flops / t_fma / 1e12, 2),
+                                 kernel="gs_fma_loop, 8 chains x 8 waves per SIMD"))
+
+
+def walked_entries(r):
+    """List entries the backward blend walks with at least one flagged quadrant: each
+    costs one nine-value reduction and nine float atomics (two entries share one
+    atomic instruction).  Counted on the device from the last step's buffers."""
+    import torch
+    K = int(r.num_keys.item())
+    T = r.ntiles
+    rng = r.tile_ranges.long()
+    H, W = r.n_contrib.shape
+    nc = torch.zeros((r.tiles_y * 16, r.tiles_x * 16), dtype=torch.int32, device=r.n_contrib.device)
+    nc[:H, :W] = r.n_contrib
+    ncmax = nc.view(r.tiles_y, 16, r.tiles_x, 16).amax(dim=(1, 3)).reshape(-1).long()
+    tile_of = torch.repeat_interleave(torch.arange(T, device=rng.device), rng[:, 1] - rng[:, 0])
+    pos = torch.arange(K, device=rng.device) - rng[tile_of, 0]
+    walked = (pos < ncmax[tile_of]) & (r.contrib[:K] != 0)
+    return int(walked.sum().item())
+
+
 def densify_measure(st, reps):
     """gs_densify (densify, split or clone, prune) on the trained state: the parameters, Adam moments
     and the statistic the steps above accumulated.  Out of place, so every repetition does the same
@@ -438,10 +490,13 @@ def main():
     pe[1].record()
     torch.cuda.synchronize()
     pbwd_ms = float(pe[0].elapsed_time(pe[1])) / args.steps
+    entries = walked_entries(st.rast)
     dens = densify_measure(st, max(3, min(args.steps, 10)))
     mv = views_measure(sc, args.views, args.steps, args.warmup) if args.views > 1 else None
     stage_ms = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
                 for j, name in enumerate(st.stages)}
+    step_ev = np.array([evs[i][0].elapsed_time(evs[i][nst]) for i in range(args.steps)])
+    peaks = measure_peaks()
     ms = elapsed * 1e3 / args.steps
     counts = (c0.astype(np.float64) + c1) / 2
     p_fwd, p_bwd, p_blend = counts
@@ -464,9 +519,18 @@ def main():
         render_fwd=(FLOPS_EVAL * p_fwd + FLOPS_FWD_BLEND * p_blend) / fl,
         render_bwd=(FLOPS_EVAL * p_bwd + FLOPS_BWD_BLEND * p_blend) / fl,
         preprocess_bwd=513.0 * N / hbm)        # 236 B params + 36 B 2D gradients + 5 B count/clamp in, 236 B out
+    # the same bound with the rates this GPU delivers (measured copy and FMA loop) as denominators
+    scale = dict(preprocess=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"],
+                 bin_sort=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"],
+                 render_fwd=PEAK_FP32_TFLOPS / peaks["fp32_tflops"]["measured"],
+                 render_bwd=PEAK_FP32_TFLOPS / peaks["fp32_tflops"]["measured"],
+                 preprocess_bwd=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"])
+    tmin_meas = sum(v * scale[k] for k, v in tmin.items())
     raster_roof = dict(t_min_us={k: round(v * 1e6, 2) for k, v in tmin.items()},
                        t_min_sum_us=round(sum(tmin.values()) * 1e6, 2),
-                       frac=round(sum(tmin.values()) / (raster_ms * 1e-3), 4))
+                       frac=round(sum(tmin.values()) / (raster_ms * 1e-3), 4),
+                       t_min_sum_us_measured_peaks=round(tmin_meas * 1e6, 2),
+                       frac_of_measured=round(tmin_meas / (raster_ms * 1e-3), 4))
 
     # roofline of the dominant kernel (render_bwd: FP32 VALU bound)
     dom = max(("render_fwd_loss", "render_bwd"), key=lambda k: stage_ms[k])
@@ -478,7 +542,9 @@ def main():
     traffic = read_traffic(dom)
     roof = dict(kernel=dom, bound="alu", achieved=round(achieved, 3), peak=PEAK_FP32_TFLOPS, unit="TFLOP/s",
                 frac=round(achieved / PEAK_FP32_TFLOPS, 4), traffic=traffic,
-                flops_per_launch=float(flops), launch_ms=round(stage_ms[dom], 4))
+                flops_per_launch=float(flops), launch_ms=round(stage_ms[dom], 4),
+                peak_measured=peaks["fp32_tflops"]["measured"],
+                frac_of_measured=round(achieved / peaks["fp32_tflops"]["measured"], 4))
 
     out = dict(metric=METRIC, value=float(value), unit="blend pairs/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak",
@@ -491,6 +557,14 @@ def main():
                             stages=f"{st.stages[0]} + bin_sort + render_fwd_loss + render_bwd + preprocess_bwd",
                             preprocess_bwd_ms=round(pbwd_ms, 4), roofline=raster_roof),
                stage_ms={k: round(v, 4) for k, v in stage_ms.items()},
+               step_ms_events=dict(p10=round(float(np.percentile(step_ev, 10)), 4),
+                                   median=round(float(np.median(step_ev)), 4),
+                                   p90=round(float(np.percentile(step_ev, 90)), 4)),
+               blend=dict(fwd_pairs_per_s=float(p_fwd / (stage_ms["render_fwd_loss"] * 1e-3)),
+                          bwd_pairs_per_s=float(p_bwd / (stage_ms["render_bwd"] * 1e-3)),
+                          bwd_walked_entries=entries, bwd_float_atomics=9 * entries,
+                          bwd_atomics_per_s=float(9 * entries / (stage_ms["render_bwd"] * 1e-3))),
+               peaks=peaks,
                schedule={"none": "one stream",
                          "color": "two streams: the SH colour pass runs on a second stream while the main stream "
                                   "projects and bins; stage_ms are main-stream intervals",

@@ -65,7 +65,7 @@ SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs
            "gs_densify_workspace_size", "gs_densify", "gs_opacity_reset",
            "gs_preprocess_views", "gs_bin_workspace_size_views", "gs_bin_sort_views", "gs_render_fwd_views",
            "gs_render_fwd_loss_views", "gs_render_bwd_views", "gs_preprocess_bwd_views",
-           "gs_preprocess_bwd_adam_views", "gs_count_pairs_views"]
+           "gs_preprocess_bwd_adam_views", "gs_count_pairs_views", "gs_stream_copy", "gs_fma_loop"]
 MAX_VIEWS = 8
 PARAM_ORDER = ("means", "log_scales", "quats", "opacity_logits", "sh")
 
@@ -122,6 +122,8 @@ def load_library(path=LIB_PATH):
     lib.gs_preprocess_bwd_adam_views.argtypes = (V + [P(GsSettings), _i32, _i32] + [_vp] * 8 + [P(GsAdamState)] +
                                                  [_vp] * 7 + [_vp])
     lib.gs_count_pairs_views.argtypes = V + [P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.gs_stream_copy.argtypes = [_vp, _vp, _i64, _vp]
+    lib.gs_fma_loop.argtypes = [_i32, _i32, C.c_float, C.c_float, _vp, _vp]
     for name in SYMBOLS:
         if name not in ("gs_error_string",):
             getattr(lib, name).restype = C.c_int
@@ -404,6 +406,24 @@ def gs_count_pairs(cam, settings, n, tile_ranges, point_list, splats, counts):
                                        _p(tile_ranges, torch.int32), _p(point_list, torch.int32),
                                        _p(splats, torch.float32), _p(counts, torch.int64), _stream())
     _check(rc, "gs_count_pairs")
+
+
+def gs_stream_copy(src, dst):
+    """dst <- src (float32, numel a multiple of 4) with the library's 16-byte non-temporal copy kernel."""
+    if src.numel() != dst.numel():
+        raise GsError("gs_stream_copy: src and dst differ in size")
+    _check(load_library().gs_stream_copy(_p(src, torch.float32, "src"), _p(dst, torch.float32, "dst"), src.numel(),
+                                         _stream()), "gs_stream_copy")
+
+
+FMA_LOOP_THREADS, FMA_LOOP_FLOPS_PER_ITER = 256, 128
+
+
+def gs_fma_loop(blocks, iters, a, b, out):
+    """The fp32 FMA loop kernel: blocks * 256 * iters * 128 flops; out holds blocks * 256 floats."""
+    if out.numel() < blocks * FMA_LOOP_THREADS:
+        raise GsError("gs_fma_loop: out holds fewer than blocks * 256 floats")
+    _check(load_library().gs_fma_loop(blocks, iters, a, b, _p(out, torch.float32, "out"), _stream()), "gs_fma_loop")
 
 
 @dataclass

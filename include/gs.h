@@ -432,6 +432,24 @@ int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, cons
                    const uint32_t* point_list, const float* splats, int64_t* counts, void* stream);
 
 /*
+ * Measurement helpers.  They compute nothing of the method: a benchmark times
+ * them to quote the rates this GPU delivers beside its published peaks.
+ *
+ * gs_stream_copy -- dst[i] = src[i] for i < count (float32, count a multiple
+ * of 4, both arrays 16-byte aligned, not overlapping), read and written with
+ * non-temporal 16-byte accesses: 8 count bytes of HBM traffic.
+ *
+ * gs_fma_loop -- `blocks` blocks of 256 lanes, each running 8 independent
+ * chains f <- f a + b (fp32 FMA), 8 steps of each chain per iteration for
+ * `iters` iterations, then writing the sum of its chains to
+ * out[block * 256 + lane] (out holds blocks * 256 floats):
+ * blocks * 256 * iters * 128 flops.  With a = 1, b = 0 each lane writes
+ * 8 lane + 28 exactly.
+ */
+int gs_stream_copy(const float* src, float* dst, int64_t count, void* stream);
+int gs_fma_loop(int32_t blocks, int32_t iters, float a, float b, float* out, void* stream);
+
+/*
  * Batched views ([P4] E.1 steps 1-3: an iteration renders a batch of views,
  * sums their losses, back-propagates and takes one optimizer step).  The
  * *_views calls take an array of `views` cameras (1 <= views <= GS_MAX_VIEWS),

@@ -479,3 +479,29 @@ def test_fused_tail_matches_separate_calls():
         assert torch.equal(cnt_a, cnt_b)
         assert (acc_a - acc_b).abs().max().item() <= 1e-6 * max(1.0, acc_a.abs().max().item())
     log("fused tail ok")
+
+
+def test_measurement_kernels():
+    """The copy and FMA-loop kernels the bench times for its measured peaks compute
+    what their header says: an exact copy, and with a = 1, b = 0 each lane's sum of
+    its eight untouched chain seeds, 8 lane + 28."""
+    import torch
+    gs = _gs()
+    n = (1 << 20) + 36  # several grid strides plus a ragged tail of float4s
+    src = torch.arange(n, dtype=torch.float32, device="cuda") * 0.5 - 7.0
+    dst = torch.full_like(src, float("nan"))
+    gs.gs_stream_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    blocks = 7
+    out = torch.full((blocks * gs.FMA_LOOP_THREADS,), float("nan"), dtype=torch.float32, device="cuda")
+    gs.gs_fma_loop(blocks, 1000, 1.0, 0.0, out)
+    torch.cuda.synchronize()
+    lane = torch.arange(gs.FMA_LOOP_THREADS, dtype=torch.float32, device="cuda").repeat(blocks)
+    assert torch.equal(out, 8.0 * lane + 28.0)
+    lib = gs.load_library()
+    p = C.c_void_p(src.data_ptr())
+    assert lib.gs_stream_copy(p, C.c_void_p(dst.data_ptr()), 6, None) == -1          # count not a multiple of 4
+    assert lib.gs_stream_copy(C.c_void_p(src.data_ptr() + 4), C.c_void_p(dst.data_ptr()), 8, None) == -2
+    assert lib.gs_fma_loop(0, 10, 1.0, 0.0, C.c_void_p(out.data_ptr()), None) == -1
+    log("measurement kernels ok")
