@@ -131,7 +131,9 @@ __device__ __forceinline__ void nt_st4(float4 v, float* p) {
 __device__ __forceinline__ void adam_reg(float& p, float g, float& m, float& v, float lr, const AdamHyper& h) {
     m = h.b1 * m + (1.f - h.b1) * g;
     v = h.b2 * v + (1.f - h.b2) * g * g;
-    p -= lr * (m * h.inv_c1) / (sqrtf(v) * h.inv_sqrt_c2 + h.eps);
+    // hardware square root and reciprocal (1 ulp each) instead of the correctly
+    // rounded sequences: a few instructions per element of a memory-bound pass
+    p -= lr * (m * h.inv_c1) * __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(v) * h.inv_sqrt_c2 + h.eps);
 }
 
 // The per-Gaussian part of the chain: gradients of the mean, log-scales, raw

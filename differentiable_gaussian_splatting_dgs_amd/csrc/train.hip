@@ -70,8 +70,9 @@ constexpr int kAdamIPT = 4;
 __device__ __forceinline__ void adam_one(float& p, float g, float& m, float& v, float lr, const AdamArgs& a) {
     m = a.b1 * m + (1.f - a.b1) * g;
     v = a.b2 * v + (1.f - a.b2) * g * g;
-    const float denom = sqrtf(v) * a.inv_sqrt_c2 + a.eps;
-    p -= lr * (m * a.inv_c1) / denom;
+    // the same arithmetic as the fused tail's update: hardware square root and reciprocal
+    const float denom = __builtin_amdgcn_sqrtf(v) * a.inv_sqrt_c2 + a.eps;
+    p -= lr * (m * a.inv_c1) * __builtin_amdgcn_rcpf(denom);
 }
 
 __global__ __launch_bounds__(kAdamThreads) void k_adam(AdamArgs a) {
