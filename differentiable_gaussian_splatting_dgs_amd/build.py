@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgs.so")
 OBJDIR = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "preprocess.hip", "binning.hip", "render.hip", "preprocess_bwd.hip", "train.hip",
-           "densify.hip", "calibrate.hip"]
+           "densify.hip", "calibrate.hip", "debug.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

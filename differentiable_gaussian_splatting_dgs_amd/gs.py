@@ -65,7 +65,8 @@ SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs
            "gs_densify_workspace_size", "gs_densify", "gs_opacity_reset",
            "gs_preprocess_views", "gs_bin_workspace_size_views", "gs_bin_sort_views", "gs_render_fwd_views",
            "gs_render_fwd_loss_views", "gs_render_bwd_views", "gs_preprocess_bwd_views",
-           "gs_preprocess_bwd_adam_views", "gs_count_pairs_views", "gs_stream_copy", "gs_fma_loop"]
+           "gs_preprocess_bwd_adam_views", "gs_count_pairs_views", "gs_stream_copy", "gs_fma_loop",
+           "gs_count_nonfinite"]
 MAX_VIEWS = 8
 PARAM_ORDER = ("means", "log_scales", "quats", "opacity_logits", "sh")
 
@@ -123,6 +124,7 @@ def load_library(path=LIB_PATH):
                                                  [_vp] * 7 + [_vp])
     lib.gs_count_pairs_views.argtypes = V + [P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp]
     lib.gs_stream_copy.argtypes = [_vp, _vp, _i64, _vp]
+    lib.gs_count_nonfinite.argtypes = [_vp, _i64, _vp, _vp]
     lib.gs_fma_loop.argtypes = [_i32, _i32, C.c_float, C.c_float, _vp, _vp]
     for name in SYMBOLS:
         if name not in ("gs_error_string",):
@@ -408,6 +410,27 @@ def gs_count_pairs(cam, settings, n, tile_ranges, point_list, splats, counts):
     _check(rc, "gs_count_pairs")
 
 
+def gs_count_nonfinite(x, out=None):
+    """Device int64 tensor [1] holding the number of NaN / infinite values of the float32 tensor x."""
+    if out is None:
+        out = torch.empty(1, dtype=torch.int64, device=x.device)
+    _check(load_library().gs_count_nonfinite(_p(x, torch.float32, "x"), x.numel(), _p(out, torch.int64, "out"),
+                                             _stream()), "gs_count_nonfinite")
+    return out
+
+
+def check_finite(tensors):
+    """Debug check: raise GsError naming every float32 tensor of `tensors` (a dict) that holds NaN or
+    infinite values.  Synchronises."""
+    bad = []
+    for name, t in tensors.items():
+        c = int(gs_count_nonfinite(t).item())
+        if c:
+            bad.append(f"{name} ({c} of {t.numel()})")
+    if bad:
+        raise GsError("non-finite values in " + ", ".join(bad))
+
+
 def gs_stream_copy(src, dst):
     """dst <- src (float32, numel a multiple of 4) with the library's 16-byte non-temporal copy kernel."""
     if src.numel() != dst.numel():
@@ -670,11 +693,15 @@ class Rasterizer:
     `key_capacity` entries and binning raises a device flag when K exceeds it.
     `forward(check=True)` synchronises once, grows the capacity and re-bins when
     that happened; with check=False nothing synchronises.
+    debug=True checks the parameters before the forward, and the image and the
+    gradients after each pass, for NaN and infinite values (gs_count_nonfinite),
+    raising GsError with the names of the tensors that hold them.
     """
 
-    def __init__(self, cam, n, sh_degree, settings=None, key_capacity=None, device="cuda"):
+    def __init__(self, cam, n, sh_degree, settings=None, key_capacity=None, device="cuda", debug=False):
         load_library()
         self.cam, self.n, self.deg = cam, int(n), int(sh_degree)
+        self.debug = bool(debug)
         self.settings = settings or Settings()
         self.device = torch.device(device)
         dev, n = self.device, self.n
@@ -727,6 +754,8 @@ class Rasterizer:
                            dL_dimage, loss_dev, self.grad2d if clear_grad2d else None)
 
     def forward(self, p, check=True):
+        if self.debug:
+            check_finite({k: p[k] for k in PARAM_ORDER})
         self.preprocess(p)
         self.bin()
         if check and int(self.overflow.item()) != 0:
@@ -735,6 +764,8 @@ class Rasterizer:
             self.bin()
             assert int(self.overflow.item()) == 0
         self.render()
+        if self.debug:
+            check_finite({"image": self.image, "final_T": self.final_T})
         return self.image
 
     def backward_2d(self, dL_dimage, accumulate=False):
@@ -750,6 +781,8 @@ class Rasterizer:
         gs_preprocess_bwd(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
                           p["opacity_logits"], p["sh"], self.tiles_touched, self.clamp, self.grad2d,
                           out["means"], out["log_scales"], out["quats"], out["opacity_logits"], out["sh"])
+        if self.debug:
+            check_finite({"dL_dimage": dL_dimage, "grad2d": self.grad2d, **{"d" + k: v for k, v in out.items()}})
         return out
 
     def count_pairs(self):

@@ -7,7 +7,8 @@
  *       backpropagation: from pixel gradients to 3D Gaussian parameter updates"
  *       (section 1 architecture and buffer reuse, section 2 gradient math,
  *       section 3 reverse per-pixel walk, section 4 2D -> 3D conversion,
- *       section 5 buffer reuse without dynamic allocation).
+ *       section 5 buffer reuse without dynamic allocation, section 6
+ *       troubleshooting).
  *  [P4] notes.huajishe.fun, "3DGS training and optimisation" (C.2 Adam with
  *       per-parameter learning rates, D.1 densification statistic, D.4
  *       quaternion renormalisation, E.1 training loop, E.3 tile rasterization).
@@ -430,6 +431,17 @@ int gs_opacity_reset(int32_t n, float factor, float* opacity_logits, float* exp_
  */
 int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                    const uint32_t* point_list, const float* splats, int64_t* counts, void* stream);
+
+/*
+ * gs_count_nonfinite -- *out (device int64, overwritten) = the number of NaN
+ * and infinite values among x[0, count) (float32, any alignment).  A debug
+ * check for the inputs and outputs of the calls above ([P3] section 6: NaN
+ * comes from invalid math; find the first tensor that holds one).  A NaN input
+ * does not make any call fault: a Gaussian with a non-finite mean, scale or
+ * rotation is culled by the preprocess, but a non-finite opacity or SH value
+ * reaches the image.
+ */
+int gs_count_nonfinite(const float* x, int64_t count, int64_t* out, void* stream);
 
 /*
  * Measurement helpers.  They compute nothing of the method: a benchmark times

@@ -114,3 +114,18 @@ def test_views_and_densify_host_checks():
                           None) == -1  # SH degree 4
     assert lib.gs_densify(C.byref(st), 10, 3, C.byref(inp), 20, C.byref(out), fake, fake, None, fake, 0,
                           None) == -3  # workspace too small
+
+
+def test_nonfinite_and_measurement_host_checks():
+    """Argument checks of the debug and measurement calls, answered on the host (no device work)."""
+    import ctypes as C
+    from differentiable_gaussian_splatting_dgs_amd import gs
+    lib = gs.load_library()
+    fake = C.c_void_p(1 << 20)  # never dereferenced: every call below fails its host checks
+    assert lib.gs_count_nonfinite(fake, -1, fake, None) == -1
+    assert lib.gs_count_nonfinite(fake, 4, None, None) == -1
+    assert lib.gs_count_nonfinite(None, 4, fake, None) == -1
+    assert lib.gs_stream_copy(fake, fake, 6, None) == -1
+    assert lib.gs_stream_copy(C.c_void_p((1 << 20) + 4), fake, 8, None) == -2
+    assert lib.gs_fma_loop(0, 1, 1.0, 0.0, fake, None) == -1
+    assert lib.gs_fma_loop(4, -1, 1.0, 0.0, fake, None) == -1

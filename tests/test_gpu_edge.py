@@ -505,3 +505,41 @@ def test_measurement_kernels():
     assert lib.gs_stream_copy(C.c_void_p(src.data_ptr() + 4), C.c_void_p(dst.data_ptr()), 8, None) == -2
     assert lib.gs_fma_loop(0, 10, 1.0, 0.0, C.c_void_p(out.data_ptr()), None) == -1
     log("measurement kernels ok")
+
+
+def test_nonfinite_count_and_debug_mode():
+    """gs_count_nonfinite counts NaN and infinities exactly; a Gaussian with a NaN mean
+    is culled (the call does not fault and the rest of the image is unchanged); the
+    Rasterizer's debug mode names the input tensor that holds the NaN."""
+    import torch
+    gs = _gs()
+    x = torch.linspace(-3.0, 3.0, 100003, dtype=torch.float32, device="cuda")
+    x[[5, 777, 100002]] = float("nan")
+    x[[10, 50000]] = float("inf")
+    x[99] = float("-inf")
+    x[11] = 1e-40                      # denormal: finite
+    x[12] = 3.4028234663852886e38      # largest finite
+    assert int(gs.gs_count_nonfinite(x).item()) == 6
+    assert int(gs.gs_count_nonfinite(x[13:40]).item()) == 0
+    sc = scenes.random_small(21, n=40)
+    params = sc.params()
+    bad = {k: v.copy() for k, v in params.items()}
+    bad["means"][7, 1] = np.nan
+    r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
+    img_bad = r.forward(to_dev(bad), check=True).clone()
+    torch.cuda.synchronize()
+    assert int(r.tiles_touched[7].item()) == 0
+    keep = np.arange(sc.n) != 7
+    ref = gs.Rasterizer(sc.cam, sc.n - 1, sc.sh_degree)
+    img_ref = ref.forward(to_dev({k: np.ascontiguousarray(v[keep]) for k, v in params.items()}), check=True)
+    torch.cuda.synchronize()
+    assert torch.equal(img_bad, img_ref)
+    dbg = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree, debug=True)
+    with pytest.raises(gs.GsError, match="means"):
+        dbg.forward(to_dev(bad))
+    bad2 = {k: v.copy() for k, v in params.items()}
+    bad2["opacity_logits"][3] = np.inf
+    with pytest.raises(gs.GsError, match="opacity_logits"):
+        dbg.forward(to_dev(bad2))
+    dbg.forward(to_dev(params))        # finite inputs pass
+    log("non-finite checks ok")
