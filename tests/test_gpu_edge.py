@@ -543,3 +543,33 @@ def test_nonfinite_count_and_debug_mode():
         dbg.forward(to_dev(bad2))
     dbg.forward(to_dev(params))        # finite inputs pass
     log("non-finite checks ok")
+
+
+def test_determinism():
+    """Two runs on the same inputs give the same bits for everything that is not summed
+    with float atomics: preprocess records, sorted lists, tile ranges, the image,
+    final_T, n_contrib and the blend flags.  The 2D gradients (atomic sums) agree
+    within float32 reassociation."""
+    import torch
+    gs = _gs()
+    sc = scenes.random_small(33, n=300, width=96, height=80, f=90.0)
+    p = to_dev(sc.params())
+    dL = torch.from_numpy(np.ascontiguousarray(sc.dL_dimage)).cuda()
+    runs = []
+    for _ in range(2):
+        r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
+        r.forward(p, check=True)
+        g = r.backward(p, dL)
+        torch.cuda.synchronize()
+        K = int(r.num_keys.item())
+        runs.append(dict(splats=r.splats.clone(), depth=r.depth.clone(), rect=r.rect.clone(),
+                         tt=r.tiles_touched.clone(), lists=r.point_list[:K].clone(), ranges=r.tile_ranges.clone(),
+                         image=r.image.clone(), final_T=r.final_T.clone(), n_contrib=r.n_contrib.clone(),
+                         contrib=r.contrib[:K].clone(), grad2d=r.grad2d.clone(), g3=g))
+    a, b = runs
+    for k in ("splats", "depth", "rect", "tt", "lists", "ranges", "image", "final_T", "n_contrib", "contrib"):
+        assert torch.equal(a[k], b[k]), k
+    assert rel_l2(a["grad2d"].cpu().numpy(), b["grad2d"].cpu().numpy()) <= 1e-6
+    for k in PARAM_KEYS:
+        assert rel_l2(a["g3"][k].cpu().numpy(), b["g3"][k].cpu().numpy()) <= 1e-6, k
+    log("determinism ok")
