@@ -60,6 +60,9 @@ def parse():
                     help="work moved to a second stream: none, the SH colour pass (color), or the colour pass and "
                          "the SH half of the Adam tail (sh)")
     ap.add_argument("--cpu-tile-fraction", type=float, default=1.0)
+    ap.add_argument("--workload", default="train1m",
+                    help="train1m (the training step, the default bench line) or tiny / ball100k / clusters1m / "
+                         "plane3m: the rasterizer's fwd+bwd alone on that scene")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run one device copy of this many MiB first (scales HBM byte counters)")
     return ap.parse_args()
@@ -440,6 +443,103 @@ def cpu_baseline(sc, frac, seed=0):
                 gauss_fraction=n_s / sc.n, stage_s={k: round(v, 3) for k, v in t.items()})
 
 
+def raster_roofline(N, K, deg, p_fwd, p_bwd, p_blend, raster_ms, peaks):
+    """The rasterizer's roofline fraction: the sum over its stages of the least time the binding peak allows
+    for the stage's algorithmic bytes (preprocess, binning, 2D->3D backward) or flops (the two blends), over
+    the measured fwd+bwd time; against the published peaks and against the measured ones."""
+    hbm = PEAK_HBM_GBS * 1e9
+    fl = PEAK_FP32_TFLOPS * 1e12
+    par = 4.0 * (3 + 3 + 4 + 1 + 3 * (deg + 1) ** 2)                      # parameter bytes per Gaussian
+    tmin = dict(
+        preprocess=(par + 65.0) * N / hbm,                                 # parameters in, 65 B records out
+        bin_sort=(16 * N + 4 * 16 * N + 20 * N + 8 * K + 2 * 16 * K + 4 * K) / hbm,  # keys, 4 depth passes,
+                                                                           # emission, 2 tile passes, ranges
+        render_fwd=(FLOPS_EVAL * p_fwd + FLOPS_FWD_BLEND * p_blend) / fl,
+        render_bwd=(FLOPS_EVAL * p_bwd + FLOPS_BWD_BLEND * p_blend) / fl,
+        preprocess_bwd=(2 * par + 41.0) * N / hbm)  # parameters + 36 B 2D gradients + 5 B count/clamp in, grads out
+    scale = dict(preprocess=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"],
+                 bin_sort=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"],
+                 render_fwd=PEAK_FP32_TFLOPS / peaks["fp32_tflops"]["measured"],
+                 render_bwd=PEAK_FP32_TFLOPS / peaks["fp32_tflops"]["measured"],
+                 preprocess_bwd=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"])
+    tmin_meas = sum(v * scale[k] for k, v in tmin.items())
+    return dict(t_min_us={k: round(v * 1e6, 2) for k, v in tmin.items()},
+                t_min_sum_us=round(sum(tmin.values()) * 1e6, 2),
+                frac=round(sum(tmin.values()) / (raster_ms * 1e-3), 4),
+                t_min_sum_us_measured_peaks=round(tmin_meas * 1e6, 2),
+                frac_of_measured=round(tmin_meas / (raster_ms * 1e-3), 4))
+
+
+def rasterizer_workload(name, steps, warmup):
+    """fwd+bwd of the rasterizer alone on another scene (no optimizer, so the workload does not drift):
+    preprocess, binning, forward (with the scene's loss fused in when it has one), backward blend and the
+    2D->3D backward.  Prints its own JSON line; the default bench line is the training step on train1m."""
+    import torch
+    from differentiable_gaussian_splatting_dgs_amd import gs, scenes
+    sc = scenes.make(name)
+    dev = "cuda"
+    p = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in sc.params().items()}
+    r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
+    g3 = {k: torch.empty_like(v) for k, v in p.items()}
+    loss = torch.zeros(1 + r.ntiles, dtype=torch.float64, device=dev)
+    if sc.loss:
+        target = torch.from_numpy(np.ascontiguousarray(sc.target)).to(dev)
+        dL = torch.empty_like(target)
+    else:
+        target = None
+        dL = torch.from_numpy(np.ascontiguousarray(sc.dL_dimage)).to(dev)
+    r.forward(p, check=True)                       # sizes the list capacity
+    stages = ["preprocess", "bin_sort", "render_fwd", "render_bwd", "preprocess_bwd"]
+
+    def run(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        r.preprocess(p)
+        mark(1)
+        r.bin()
+        mark(2)
+        if target is not None:
+            r.render_loss(target, sc.loss, dL, loss, clear_grad2d=False)
+        else:
+            r.render()
+        mark(3)
+        r.backward_2d(dL)
+        mark(4)
+        gs.gs_preprocess_bwd(r.cam, r.settings, r.deg, p["means"], p["log_scales"], p["quats"],
+                             p["opacity_logits"], p["sh"], r.tiles_touched, r.clamp, r.grad2d, g3["means"],
+                             g3["log_scales"], g3["quats"], g3["opacity_logits"], g3["sh"])
+        mark(5)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run(evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    assert int(r.overflow.item()) == 0, "list capacity overflow during timing"
+    p_fwd, p_bwd, p_blend = (float(x) for x in r.count_pairs().cpu().numpy())
+    stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+                for j, n in enumerate(stages)}
+    ev_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][5]) for i in range(steps)]))
+    peaks = measure_peaks()
+    K = float(r.num_keys.item())
+    out = dict(metric=METRIC, value=(p_fwd + p_bwd) / (ms * 1e-3), unit="blend pairs/s", n_gpus=1, steps=steps,
+               warmup=warmup, ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="f32", data="synthetic",
+               config=dict(workload=f"{name}: {sc.n} Gaussians, {sc.cam.width}x{sc.cam.height}, SH {sc.sh_degree}; "
+                                    "rasterizer fwd + bwd to the 3D gradients, no optimizer",
+                           gaussians=sc.n, width=sc.cam.width, height=sc.cam.height, sh_degree=sc.sh_degree,
+                           tile=16, parallelism="single-gpu"),
+               event_ms=round(ev_ms, 4), stage_ms={k: round(v, 4) for k, v in stage_ms.items()},
+               pairs=dict(fwd_evaluated=p_fwd, bwd_walked=p_bwd, blended=p_blend, keys=int(K)),
+               roofline=raster_roofline(sc.n, K, sc.sh_degree, p_fwd, p_bwd, p_blend, ev_ms, peaks), peaks=peaks)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -449,6 +549,9 @@ def main():
     import torch
     from differentiable_gaussian_splatting_dgs_amd import scenes
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload != "train1m":
+        rasterizer_workload(args.workload, args.steps, args.warmup)
+        return
     t_gen = time.time()
     sc = scenes.training1m()
     print(f"# scene {sc.name}: n={sc.n} {sc.cam.width}x{sc.cam.height} ({time.time() - t_gen:.1f}s)", file=sys.stderr,
@@ -507,30 +610,8 @@ def main():
     raster_ms = sum(stage_ms[k] for k in (st.stages[0], "bin_sort", "render_fwd_loss", "render_bwd"))
     raster_ms += pbwd_ms
 
-    # the rasterizer's roofline fraction: sum over its stages of the time the binding peak allows for the
-    # stage's algorithmic bytes or flops, over the measured fwd+bwd time
-    N, K = sc.n, float(st.rast.num_keys.item())
-    hbm = PEAK_HBM_GBS * 1e9
-    fl = PEAK_FP32_TFLOPS * 1e12
-    tmin = dict(
-        preprocess=301.0 * N / hbm,                                        # 236 B in, 65 B out
-        bin_sort=(16 * N + 4 * 16 * N + 20 * N + 8 * K + 2 * 16 * K + 4 * K) / hbm,  # keys, 4 depth passes,
-                                                                           # emission, 2 tile passes, ranges
-        render_fwd=(FLOPS_EVAL * p_fwd + FLOPS_FWD_BLEND * p_blend) / fl,
-        render_bwd=(FLOPS_EVAL * p_bwd + FLOPS_BWD_BLEND * p_blend) / fl,
-        preprocess_bwd=513.0 * N / hbm)        # 236 B params + 36 B 2D gradients + 5 B count/clamp in, 236 B out
-    # the same bound with the rates this GPU delivers (measured copy and FMA loop) as denominators
-    scale = dict(preprocess=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"],
-                 bin_sort=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"],
-                 render_fwd=PEAK_FP32_TFLOPS / peaks["fp32_tflops"]["measured"],
-                 render_bwd=PEAK_FP32_TFLOPS / peaks["fp32_tflops"]["measured"],
-                 preprocess_bwd=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"])
-    tmin_meas = sum(v * scale[k] for k, v in tmin.items())
-    raster_roof = dict(t_min_us={k: round(v * 1e6, 2) for k, v in tmin.items()},
-                       t_min_sum_us=round(sum(tmin.values()) * 1e6, 2),
-                       frac=round(sum(tmin.values()) / (raster_ms * 1e-3), 4),
-                       t_min_sum_us_measured_peaks=round(tmin_meas * 1e6, 2),
-                       frac_of_measured=round(tmin_meas / (raster_ms * 1e-3), 4))
+    raster_roof = raster_roofline(sc.n, float(st.rast.num_keys.item()), sc.sh_degree, p_fwd, p_bwd, p_blend,
+                                  raster_ms, peaks)
 
     # roofline of the dominant kernel (render_bwd: FP32 VALU bound)
     dom = max(("render_fwd_loss", "render_bwd"), key=lambda k: stage_ms[k])
