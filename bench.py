@@ -391,6 +391,20 @@ def densify_measure(st, reps):
                               frac=round(gbs / PEAK_HBM_GBS, 4)))
 
 
+def host_cpu():
+    """The host the CPU baseline ran on: CPU model (from /proc/cpuinfo) and the number of CPUs."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(cpu_model=model, nproc=os.cpu_count())
+
+
 def cpu_baseline(sc, frac, seed=0):
     """The oracle on a bounded sample of the same step, scaled to blend pairs/s.
 
@@ -668,7 +682,7 @@ def main():
                                            f"tiles, 2D->3D bwd/densify/Adam over {cb['gauss_fraction']:.0%} of "
                                            f"Gaussians; {cb['work_s']:.1f}s of work, stage times scaled to the "
                                            f"full step ({cb['est_step_s']:.1f}s)"),
-                                   stage_s=cb["stage_s"])
+                                   stage_s=cb["stage_s"], host=host_cpu())
     print(json.dumps(out))
 
 
