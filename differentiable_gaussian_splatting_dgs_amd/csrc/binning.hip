@@ -398,7 +398,7 @@ struct EmitArgs {
     const int16_t* rect;
     const int32_t* tt;
     uint32_t* part;          // [eparts] entries per scan partition -> exclusive offsets
-    uint32_t* goff;          // [n] first output slot of the j-th Gaussian in depth order
+    uint32_t* goff;          // [n] tile count, then first output slot, of the j-th Gaussian in depth order
     uint32_t* bstart;        // [xblocks + 1] depth-order index of each expand block's first Gaussian
     uint32_t* tkeys;         // [cap] tile id
     uint32_t* tvals;         // [cap] Gaussian
@@ -438,13 +438,20 @@ __device__ inline uint32_t tiles_of(const EmitArgs& a, int64_t j) {
     return g < (uint32_t)a.n ? (uint32_t)max(a.tt[g], 0) : 0u;
 }
 
-// 3a. entries per scan partition of 1024 depth-ordered Gaussians.
+// 3a. entries per scan partition of 1024 depth-ordered Gaussians.  The tile
+// count of the j-th Gaussian in depth order is gathered here once and left in
+// goff[j], where the offsets pass reads it with coalesced loads.
 __global__ __launch_bounds__(kEmitThreads) void k_emit_count(EmitArgs a) {
     __shared__ uint32_t s_wsum[4];
     const int tid = threadIdx.x;
     uint32_t c = 0;
 #pragma unroll
-    for (int k = 0; k < kEmitIPT; ++k) c += tiles_of(a, (int64_t)blockIdx.x * kEmitPart + k * kEmitThreads + tid);
+    for (int k = 0; k < kEmitIPT; ++k) {
+        const int64_t j = (int64_t)blockIdx.x * kEmitPart + k * kEmitThreads + tid;
+        const uint32_t t = tiles_of(a, j);
+        if (j < a.n) a.goff[j] = t;
+        c += t;
+    }
     uint32_t total;
     block_excl_sum(c, s_wsum, total);
     if (tid == 0) a.part[blockIdx.x] = total;
@@ -463,9 +470,18 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_offsets(EmitArgs a) {
     uint32_t pbase;
     block_excl_sum(before, s_wsum, pbase);
     const int64_t j0 = (int64_t)blockIdx.x * kEmitPart + (int64_t)tid * kEmitIPT;
+    // the depth-ordered tile counts k_emit_count left in goff (overwritten below by the offsets)
     uint32_t c[kEmitIPT], sum = 0;
+    static_assert(kEmitIPT == 4, "one 16-byte load per thread");
+    if (j0 + kEmitIPT <= a.n) {  // goff is 256-byte aligned and j0 a multiple of 4
+        const uint4 v = *reinterpret_cast<const uint4*>(a.goff + j0);
+        c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
+    } else {
 #pragma unroll
-    for (int k = 0; k < kEmitIPT; ++k) { c[k] = tiles_of(a, j0 + k); sum += c[k]; }
+        for (int k = 0; k < kEmitIPT; ++k) c[k] = j0 + k < a.n ? a.goff[j0 + k] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kEmitIPT; ++k) sum += c[k];
     uint32_t total;
     uint32_t off = pbase + block_excl_sum(sum, s_wsum, total);
     if (blockIdx.x == gridDim.x - 1 && tid == 0) {
