@@ -512,7 +512,7 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
     __shared__ uint32_t s_gid[kSlots];
     __shared__ uint32_t s_goff[kSlots];
     __shared__ uint2 s_rect[kSlots];
-    __shared__ uint32_t s_owner[kSlots];
+    __shared__ uint16_t s_owner[kSlots];  // owner q < kSlots; 16 bits keep the block under 40 KB of LDS (4 per CU)
     __shared__ uint32_t s_hist[2 * kRadix];
     __shared__ uint32_t s_wsum[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
