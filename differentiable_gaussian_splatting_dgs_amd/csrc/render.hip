@@ -54,14 +54,17 @@ struct RenderArgs {
 
 // The tile a block works on: sched[block] when a schedule is given, else image
 // order banded over the XCDs; -1 for padding blocks or an out-of-range entry.
-__device__ __forceinline__ int block_tile(const int32_t* sched, int ntiles) {
+__device__ __forceinline__ int block_tile(const int32_t* sched, int ntiles, int idx) {
     if (sched) {
-        if ((int)blockIdx.x >= ntiles) return -1;
-        const int t = sched[blockIdx.x];
+        if (idx >= ntiles) return -1;
+        const int t = sched[idx];
         return (t >= 0 && t < ntiles) ? t : -1;
     }
-    const int t = xcd_tile(blockIdx.x, ntiles);
+    const int t = xcd_tile(idx, ntiles);
     return t < ntiles ? t : -1;
+}
+__device__ __forceinline__ int block_tile(const int32_t* sched, int ntiles) {
+    return block_tile(sched, ntiles, (int)blockIdx.x);
 }
 
 // The alpha of one (pixel, Gaussian) pair.  Shared verbatim by the forward,
@@ -408,8 +411,12 @@ __device__ __forceinline__ float reduce2x9(float a[9], float b[9], float& z, int
     return w;
 }
 
-// Backward: one wave64 per tile, each lane owning one pixel of each of the four
-// 8x8 quadrants (pixel q of lane l sits at ((q & 1) 8 + l % 8, (q >> 1) 8 + l / 8)).
+// Backward: one wave64 per tile (QPW = 4), each lane owning one pixel of each of
+// the four 8x8 quadrants (pixel q of lane l sits at ((q & 1) 8 + l % 8,
+// (q >> 1) 8 + l / 8)); or, for images with few tiles, two waves per tile
+// (QPW = 2), wave h owning quadrants 2h and 2h + 1, so that the chip has twice
+// the waves to hide latency with, at the price of a second reduction and atomic
+// update for entries both halves blend.
 // Entries are walked in reverse list order in batches of 64, only those the
 // forward blended somewhere in the tile; for an entry, only its flagged
 // quadrants run the per-pixel recursion, each adding its partials into the same
@@ -423,8 +430,15 @@ __device__ __forceinline__ float reduce2x9(float a[9], float b[9], float& z, int
 // dpower/dmean = conic d, and dL/d(A, B, C) = (-1/2, -1, -1/2) times the second
 // moments.
 constexpr int kBwdBatch = 64;
+// Below this many tiles the backward runs two waves per tile: with one wave per
+// tile some of the 1024 SIMDs (256 CUs) would have none.  Above it the second
+// reduction and atomic update per entry cost more than the extra waves give.
+constexpr int kBwdSplitBelow = 1024;
 
+template <int QPW>
 __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
+    static_assert(QPW == 4 || QPW == 2, "four or two quadrants per wave");
+    constexpr int kSplit = 4 / QPW;
     __shared__ float4 s_g0[kBwdBatch];   // u', v', L00, L10
     __shared__ float4 s_g1[kBwdBatch];   // L11, opacity, r, g
     __shared__ float4 s_g2[kBwdBatch];   // b, A, B, C (conic)
@@ -433,8 +447,9 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
 
     const BlendArgs& b = a.b;
     const int ntv = b.tiles_x * b.tiles_y;
-    const int tile = block_tile(a.sched, ntv * b.views);
+    const int tile = block_tile(a.sched, ntv * b.views, (int)blockIdx.x / kSplit);
     if (tile < 0) return;
+    const int qbase = ((int)blockIdx.x % kSplit) * QPW;  // first quadrant of this wave
     const int view = tile / ntv, vtile = tile - view * ntv;
     const int tx = vtile % b.tiles_x, ty = vtile / b.tiles_x;
     const int lane = threadIdx.x;
@@ -446,13 +461,14 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     // current entry, starting at the background), dL/dpixel and the centre.
     // dL/dalpha = T (dL/dpixel . c - S) and S <- S + alpha (dL/dpixel . c - S)
     // is C_next <- alpha c + (1 - alpha) C_next dotted with dL/dpixel.
-    float T[4], S[4], gp0[4], gp1[4], gp2[4], fxq[4], fyq[4];
-    int nc[4];
+    float T[QPW], S[QPW], gp0[QPW], gp1[QPW], gp2[QPW], fxq[QPW], fyq[QPW];
+    int nc[QPW];
     int ncmax = 0;
     const size_t plane = (size_t)b.width * b.height;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int lx = (q & 1) * 8 + (lane & 7), ly = (q >> 1) * 8 + (lane >> 3);
+    for (int q = 0; q < QPW; ++q) {
+        const int qg = qbase + q;
+        const int lx = (qg & 1) * 8 + (lane & 7), ly = (qg >> 1) * 8 + (lane >> 3);
         const int px = tx * kTile + lx, py = ty * kTile + ly;
         fxq[q] = (float)lx + 0.5f;
         fyq[q] = (float)ly + 0.5f;
@@ -486,7 +502,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     auto walk = [&](int e, uint32_t mm, int pos, float v[9]) {
         const float4 G0 = s_g0[e], G1 = s_g1[e], G2 = s_g2[e];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < QPW; ++q) {
             if (mm & (1u << q)) {
                 const Pair p = eval_pair(fxq[q], fyq[q], G0, G1, b.alpha_max);
                 const bool ok = pos < nc[q] && p.alpha >= b.alpha_min;
@@ -523,7 +539,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
         if (k >= (int32_t)range.x) {
             const uint32_t g = a.list[k];
             if (g < a.n) {
-                m = a.contrib[k];
+                m = ((uint32_t)a.contrib[k] >> qbase) & ((1u << QPW) - 1u);  // this wave's quadrants
                 if (m) {
                     const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
                     const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
@@ -824,7 +840,10 @@ int render_bwd_impl(const gs_camera* cams, int32_t views, const gs_settings* set
     a.contrib = const_cast<uint8_t*>(contrib);
     a.dL_dimage = dL_dimage; a.grad2d = grad2d;
     a.sched = tile_order;
-    hipLaunchKernelGGL(k_render_bwd, dim3(render_grid(cams, views)), dim3(64), 0, s, a);
+    if (views * tiles_x(cams) * tiles_y(cams) < kBwdSplitBelow)
+        hipLaunchKernelGGL(k_render_bwd<2>, dim3(2 * render_grid(cams, views)), dim3(64), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_render_bwd<4>, dim3(render_grid(cams, views)), dim3(64), 0, s, a);
     return launch_status();
 }
 
