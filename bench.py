@@ -48,6 +48,9 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 FLOPS_EVAL, FLOPS_FWD_BLEND, FLOPS_BWD_BLEND = 14, 10, 47
 
 
+WORKLOADS = ("train1m", "tiny", "ball100k", "clusters1m", "plane3m")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,7 +63,7 @@ def parse():
                     help="work moved to a second stream: none, the SH colour pass (color), or the colour pass and "
                          "the SH half of the Adam tail (sh)")
     ap.add_argument("--cpu-tile-fraction", type=float, default=1.0)
-    ap.add_argument("--workload", default="train1m",
+    ap.add_argument("--workload", default="train1m", choices=WORKLOADS,
                     help="train1m (the training step, the default bench line) or tiny / ball100k / clusters1m / "
                          "plane3m: the rasterizer's fwd+bwd alone on that scene")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -557,8 +560,8 @@ def rasterizer_workload(name, steps, warmup):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on a single "
-              "MI355X; see DESIGN.md for how the path would shard).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the library runs on a "
+              "single MI355X.", file=sys.stderr)
         sys.exit(2)
     import torch
     from differentiable_gaussian_splatting_dgs_amd import scenes
