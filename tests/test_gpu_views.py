@@ -83,6 +83,15 @@ def test_views_match_single_view_calls(views, deg):
     _compare_with_single(sc, views)
 
 
+def test_views_cross_the_backward_split():
+    """640 tiles per view: each single-view backward runs two waves per tile (below 1024 tiles), the
+    2-view batch (1280 tiles) one wave per tile; the 2D gradients still agree to atomic-order noise."""
+    sc = scenes.random_small(91, n=3000, width=512, height=320, f=400.0, sh_degree=3)
+    rv = _compare_with_single(sc, 2)
+    assert rv.ntiles == 2 * 32 * 20
+    log("K over 2 views of 512x320", int(rv.num_keys.item()))
+
+
 def test_views_match_single_view_calls_1080p():
     """Four views of 100k Gaussians at 1080p-like size: every property above at scale."""
     sc = scenes.clusters1m(n=100_000, width=1920, height=1080)
