@@ -347,6 +347,23 @@ def test_two_stream_steps_match_one_stream():
             assert e < 1e-5 and d < 2e-2, (k, e, d)
 
 
+def test_bench_scene_mode(capsys):
+    """bench.py --workload on the smallest scene: one JSON line with the metric's fields, the stage times of
+    the five rasterizer stages, pair counts that order as they must, and the stage roofline."""
+    import json
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    bench.rasterizer_workload("tiny", 3, 1)
+    d = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert d["n_gpus"] == 1 and d["higher_is_better"] and d["value"] > 0
+    assert list(d["stage_ms"]) == ["preprocess", "bin_sort", "render_fwd", "render_bwd", "preprocess_bwd"]
+    assert all(v > 0 for v in d["stage_ms"].values())
+    p = d["pairs"]
+    assert p["fwd_evaluated"] >= p["blended"] > 0 and p["bwd_walked"] >= p["blended"] and p["keys"] > 0
+    assert 0 < d["roofline"]["frac"] < 1 and d["config"]["gaussians"] == 256
+
+
 def test_backward_accumulate():
     """accumulate=1 adds the call's gradients to what grad2d holds; accumulate=0 overwrites."""
     import torch
