@@ -122,6 +122,9 @@ CASES = {
     "tiny": (scenes.tiny, 1),
     "random_sh1": (lambda: scenes.random_small(21, n=300, width=61, height=45, sh_degree=1, scale_mu=-2.0), 1),
     "random_sh2": (lambda: scenes.random_small(22, n=500, width=100, height=77, sh_degree=2, scale_mu=-2.2), 1),
+    # either side of the backward's two-waves-per-tile threshold: 33 x 31 = 1023 tiles, 32 x 32 = 1024
+    "tiles1023": (lambda: scenes.random_small(23, n=4000, width=528, height=496, f=420.0, sh_degree=3), 1),
+    "tiles1024": (lambda: scenes.random_small(24, n=4000, width=512, height=512, f=420.0, sh_degree=3), 1),
     "ball100k": (scenes.ball100k, 1),
     "clusters1m": (scenes.clusters1m, 3),
     "plane3m": (scenes.plane3m, 8),
