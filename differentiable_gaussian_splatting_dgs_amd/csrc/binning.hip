@@ -25,6 +25,7 @@
 // offsets) follows Adinets and Merrill, "Onesweep" (2022), with partitions
 // claimed from an atomic ticket so look-back only waits on running blocks.
 #include <algorithm>
+#include <atomic>
 
 #include "gs_internal.h"
 
@@ -49,7 +50,7 @@ constexpr int kRadix = 256;
 constexpr uint32_t kFlagAgg = 1u << 30;
 constexpr uint32_t kFlagInc = 2u << 30;
 constexpr uint32_t kValMask = (1u << 30) - 1u;
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kWaitLimit = 1u << 22;        // default look-back waits before a pass gives up
 
 constexpr int kEmitThreads = 256;
 constexpr int kEmitIPT = 4;
@@ -215,7 +216,11 @@ struct PassArgs {
     int hist_bin;
     uint32_t* status;      // [parts][256], zeroed
     uint32_t* ticket;      // [kTicketGroups][kTicketStride], zeroed
-    uint32_t* err;
+    uint32_t* err;         // bit p set when a partition of pass p gave up waiting for its predecessors
+    uint32_t err_bit;      // this pass's bit
+    uint32_t err_before;   // bits of the earlier passes: if any is set the pass does nothing
+    const uint32_t* skip;  // optional: the pass does nothing when *skip != 0 (list overflow)
+    uint32_t wait_limit;   // waits per look-back before giving up
     int shift;
 };
 
@@ -247,6 +252,9 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
     __shared__ uint32_t s_part;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool digit_thread = tid < kRadix;
+    // An earlier pass failed, or the list overflowed: the sort is void.  Both words
+    // were written by earlier kernels, so every block of the grid reads the same.
+    if ((*p.err & p.err_before) != 0u || (p.skip && *p.skip != 0u)) return;
 
     if (tid == 0) {
         const uint32_t grp = blockIdx.x % kTicketGroups;
@@ -329,6 +337,10 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
             int j = (int)part - 1;
             uint32_t spins = 0;
             while (true) {
+                if (spins >= p.wait_limit) {  // give up: the pass's result is void and flagged
+                    atomicOr(p.err, p.err_bit);
+                    break;
+                }
                 uint32_t sv[kLookWindow];
 #pragma unroll
                 for (int w = 0; w < kLookWindow; ++w)
@@ -346,7 +358,7 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
                 if (found) break;
                 j -= used;
                 if (stall) {
-                    if (++spins > kSpinLimit) { atomicOr(p.err, 1u); break; }
+                    ++spins;
                     __builtin_amdgcn_s_sleep(1);
                 }
             }
@@ -405,6 +417,7 @@ struct EmitArgs {
     uint32_t* stripes;       // [kStripes][kHistBins] striped digit counts
     uint32_t* num_keys;
     uint32_t* overflow;
+    const uint32_t* err;     // look-back failures of the depth passes
 };
 
 __device__ inline void unpack_rect(uint2 r, int& x0, int& y0, int& x1, int& y1) {
@@ -487,7 +500,8 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_offsets(EmitArgs a) {
     if (blockIdx.x == gridDim.x - 1 && tid == 0) {
         const uint32_t K = pbase + total;
         *a.num_keys = K;
-        *a.overflow = K > a.cap ? 1u : 0u;
+        // bit 0: more entries than capacity; bit 1: the depth sort failed (its order is void)
+        *a.overflow = (K > a.cap ? 1u : 0u) | (*a.err != 0u ? 2u : 0u);
     }
 #pragma unroll
     for (int k = 0; k < kEmitIPT; ++k) {
@@ -597,8 +611,12 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
 // reads kRangeIPT consecutive keys with vector loads, plus one neighbour on
 // each side.
 __global__ __launch_bounds__(256) void k_ranges(const uint32_t* tkeys, const uint32_t* num_keys, uint32_t cap,
-                                                const uint32_t* overflow, uint32_t* ranges, uint32_t ntiles) {
-    if (*overflow) return;
+                                                uint32_t* overflow, const uint32_t* err, uint32_t* ranges,
+                                                uint32_t ntiles) {
+    // a failed tile pass voids the lists: report it with the overflow word and leave the ranges empty
+    const bool failed = *err != 0u;
+    if (failed && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(overflow, 2u);
+    if (failed || *overflow) return;
     const uint32_t K = min(*num_keys, cap);
     const uint32_t k0 = (blockIdx.x * blockDim.x + threadIdx.x) * (uint32_t)kRangeIPT;
     if (k0 >= K) return;
@@ -638,6 +656,16 @@ __global__ void k_keys(const uint32_t* ranges, const uint32_t* list, const float
 }  // namespace gs
 
 using namespace gs;
+
+namespace {
+std::atomic<uint32_t> g_wait_limit{kWaitLimit};  // look-back waits before a sort pass gives up
+}
+
+extern "C" int64_t gs_debug_sort_wait_limit(int64_t limit) {
+    const uint32_t prev = g_wait_limit.load();
+    if (limit >= 0) g_wait_limit.store(limit > (int64_t)UINT32_MAX ? UINT32_MAX : (uint32_t)limit);
+    return (int64_t)prev;
+}
 
 extern "C" int gs_bin_workspace_size_views(int32_t n, const gs_camera* cams, int32_t views, int64_t key_capacity,
                                            size_t* bytes) {
@@ -693,7 +721,8 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
 
     uint32_t* tickets = U(L.tickets);
     auto ticket = [&](int pass) { return tickets + (size_t)pass * kTicketGroups * kTicketStride; };
-    uint32_t* err = U(L.err);
+    uint32_t* err = U(L.err);  // bit p: sort pass p gave up (passes 0-3 depth, 4-5 tile)
+    const uint32_t wait_limit = g_wait_limit.load();
     const int key_blocks = (int)((n + 256 * kKeyIPT - 1) / (256 * kKeyIPT));
     hipLaunchKernelGGL(k_depth_keys, dim3(key_blocks), dim3(256), 0, s, n, depth, tiles_touched, U(L.dkeys0),
                        U(L.dvals0), U(L.stripes));
@@ -709,7 +738,8 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
         p.stripes = U(L.stripes); p.hist_bin = pass * kRadix;
         p.status = U(L.dstatus) + (size_t)pass * L.dparts * kRadix;
         p.ticket = ticket(pass);
-        p.err = err;
+        p.err = err; p.err_bit = 1u << pass; p.err_before = (1u << pass) - 1u; p.skip = nullptr;
+        p.wait_limit = wait_limit;
         p.shift = 8 * pass;
         hipLaunchKernelGGL((k_onesweep<kDepthThreads, kDepthIPT>), dim3(L.dparts), dim3(kDepthThreads), 0, s, p);
     }
@@ -725,13 +755,15 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
     e.part = U(L.etotal); e.goff = U(L.goff); e.bstart = U(L.bstart);
     e.tkeys = U(L.tkeys0); e.tvals = tile_passes == 1 ? U(L.tvals0) : point_list;
     e.stripes = U(L.stripes);
-    e.num_keys = num_keys_dev; e.overflow = overflow_dev;
+    e.num_keys = num_keys_dev; e.overflow = overflow_dev; e.err = err;
     hipLaunchKernelGGL(k_emit_count, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
     hipLaunchKernelGGL(k_emit_offsets, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
     if (key_capacity == 0) return launch_status();
     hipLaunchKernelGGL(k_emit_expand, dim3(L.xblocks), dim3(kEmitThreads), 0, s, e);
     PassArgs p;
-    p.count_dev = num_keys_dev; p.count_host = 0; p.cap = (uint32_t)key_capacity; p.err = err;
+    p.count_dev = num_keys_dev; p.count_host = 0; p.cap = (uint32_t)key_capacity;
+    // the tile passes skip when the emission found an overflow or a failed depth sort
+    p.err = err; p.err_bit = 1u << 4; p.err_before = 0u; p.skip = overflow_dev; p.wait_limit = wait_limit;
     p.keys_in = U(L.tkeys0); p.vals_in = e.tvals;
     p.keys_out = U(L.tkeys1); p.vals_out = tile_passes == 1 ? point_list : U(L.tvals0);
     p.stripes = U(L.stripes); p.hist_bin = 4 * kRadix; p.status = U(L.tstatus); p.ticket = ticket(4); p.shift = 0;
@@ -743,12 +775,13 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
         p2.keys_out = U(L.tkeys0); p2.vals_out = point_list;
         p2.hist_bin = 5 * kRadix; p2.status = U(L.tstatus) + (size_t)L.tparts * kRadix;
         p2.ticket = ticket(5); p2.shift = 8;
+        p2.err_bit = 1u << 5; p2.err_before = 1u << 4;
         hipLaunchKernelGGL((k_onesweep<kTileThreads, kTileIPT>), dim3(L.tparts), dim3(kTileThreads), 0, s, p2);
         tk_final = U(L.tkeys0);
     }
     const uint32_t rblocks = (uint32_t)((key_capacity + 256 * kRangeIPT - 1) / (256 * kRangeIPT));
     hipLaunchKernelGGL(k_ranges, dim3(rblocks), dim3(256), 0, s, tk_final, num_keys_dev, (uint32_t)key_capacity,
-                       overflow_dev, tile_ranges, (uint32_t)ntiles);
+                       overflow_dev, err, tile_ranges, (uint32_t)ntiles);
     return launch_status();
 }
 

@@ -11,6 +11,7 @@
 // quote achieved bandwidth and flop rates against what the chip delivers as
 // well as against its published figures.
 #include "gs_internal.h"
+#include "gs_measure.h"
 
 namespace gs {
 namespace {

@@ -111,47 +111,22 @@ __device__ __forceinline__ void shade(const CamArgs& c, double mx, double my, do
         if (rgb[ch] < 0.0) { cm |= (uint8_t)(1u << ch); rgb[ch] = 0.0; }
 }
 
-// Colour only: the SH colour pass on its own (rgb row of the splat record and
-// the clamp mask), for every Gaussian, culled or not.
+// One thread per Gaussian: projection, tile rectangle and the SH colour, for
+// each view in turn (the parameters are read once; the view-free parts --
+// opacity, M = R S -- are computed once).
 template <int DEG, bool VEC>
-__global__ __launch_bounds__(kPreBlock) void k_shade(PreArgs a) {
+__global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     constexpr int J = 3 * (DEG + 1) * (DEG + 1);
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= a.n) return;
     float shv[J];
     load_sh<DEG, VEC>(a.sh, i, shv);
-    const double mx = a.means[3 * i], my = a.means[3 * i + 1], mz = a.means[3 * i + 2];
-    for (int view = 0; view < a.views; ++view) {
-        const size_t o = (size_t)view * a.n + i;
-        double rgb[3];
-        uint8_t cm;
-        shade<DEG>(a.cams[view], mx, my, mz, shv, rgb, cm);
-        reinterpret_cast<float4*>(a.splats + o * GS_SPLAT_STRIDE)[2] =
-            make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
-        a.clamp[o] = cm;
-    }
-}
-
-// One thread per Gaussian: projection, tile rectangle and (with COLOR) the SH
-// colour, for each view in turn (the parameters are read once; the view-free
-// parts -- opacity, M = R S -- are computed once).  Without COLOR the rgb row
-// of the splat record and the clamp mask are left alone (k_shade writes them).
-template <int DEG, bool VEC, bool COLOR>
-__global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
-    constexpr int J = 3 * (DEG + 1) * (DEG + 1);
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= a.n) return;
-    float shv[COLOR ? J : 1];
-    if constexpr (COLOR) load_sh<DEG, VEC>(a.sh, i, shv);
 
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     auto cull = [&](size_t o) {
         float4* sp = reinterpret_cast<float4*>(a.splats + o * GS_SPLAT_STRIDE);
-        sp[0] = z4; sp[1] = z4;
-        if constexpr (COLOR) {
-            sp[2] = z4;
-            a.clamp[o] = 0;
-        }
+        sp[0] = z4; sp[1] = z4; sp[2] = z4;
+        a.clamp[o] = 0;
         a.depth[o] = 0.f;
         reinterpret_cast<uint2*>(a.rect)[o] = make_uint2(0u, 0u);
         a.tiles_touched[o] = 0;
@@ -232,7 +207,7 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
         // colour: max(0, sum sh Y(dir) + 0.5), dir from the camera centre
         double rgb[3];
         uint8_t cm = 0;
-        if constexpr (COLOR) shade<DEG>(c, mx, my, mz, shv, rgb, cm);
+        shade<DEG>(c, mx, my, mz, shv, rgb, cm);
 
         // Cholesky factor of the conic, scaled so that G = exp2(-|L^T d|^2):
         // conic = [[cc, -cb], [-cb, ca]] / det = L L^T with
@@ -246,10 +221,8 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
         const float uf = (float)u, vf = (float)v;
         sp[0] = make_float4(uf, vf, (float)(u - (double)uf), (float)(v - (double)vf));
         sp[1] = make_float4((float)l00, (float)l10, (float)l11, (float)sigma);
-        if constexpr (COLOR) {
-            sp[2] = make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
-            a.clamp[o] = cm;
-        }
+        sp[2] = make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
+        a.clamp[o] = cm;
         a.depth[o] = (float)tz;
         const uint32_t r0 = (uint32_t)(uint16_t)tx0 | ((uint32_t)(uint16_t)ty0 << 16);
         const uint32_t r1 = (uint32_t)(uint16_t)tx1 | ((uint32_t)(uint16_t)ty1 << 16);
@@ -266,46 +239,38 @@ using namespace gs;
 namespace gs {
 namespace {
 
-enum class Part { kAll, kGeometry, kColor };
-
 template <int DEG, bool VEC>
-void launch_pre(Part part, dim3 grid, dim3 block, hipStream_t s, const PreArgs& a) {
-    switch (part) {
-        case Part::kAll: hipLaunchKernelGGL((k_preprocess<DEG, VEC, true>), grid, block, 0, s, a); break;
-        case Part::kGeometry: hipLaunchKernelGGL((k_preprocess<DEG, false, false>), grid, block, 0, s, a); break;
-        case Part::kColor: hipLaunchKernelGGL((k_shade<DEG, VEC>), grid, block, 0, s, a); break;
-    }
+void launch_pre(dim3 grid, dim3 block, hipStream_t s, const PreArgs& a) {
+    hipLaunchKernelGGL((k_preprocess<DEG, VEC>), grid, block, 0, s, a);
 }
 
-int preprocess_impl(Part part, const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
+int preprocess_impl(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                     int32_t sh_degree, const float* means, const float* log_scales, const float* quats,
                     const float* opacity_logits, const float* sh, float* splats, float* depth, int16_t* rect,
                     int32_t* tiles_touched, uint8_t* clamp_mask, void* stream) {
     if (!views_ok(cams, views) || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
     if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
-    if (part != Part::kColor && !set) return GS_EINVAL;
+    if (!set) return GS_EINVAL;
     if (n == 0) return GS_OK;
-    if (!means || !splats) return GS_EINVAL;
-    if (part != Part::kColor && (!log_scales || !quats || !opacity_logits || !depth || !rect || !tiles_touched))
+    if (!means || !splats || !log_scales || !quats || !opacity_logits || !depth || !rect || !tiles_touched || !sh ||
+        !clamp_mask)
         return GS_EINVAL;
-    if (part != Part::kGeometry && (!sh || !clamp_mask)) return GS_EINVAL;
-    if (!aligned16(splats)) return GS_EALIGN;
-    if (part != Part::kColor && (!aligned16(quats) || !aligned16(rect))) return GS_EALIGN;
+    if (!aligned16(splats) || !aligned16(quats) || !aligned16(rect)) return GS_EALIGN;
     PreArgs a{};
     for (int v = 0; v < views; ++v) a.cams[v] = cam_args(cams + v);
     a.views = views;
-    if (set) { a.near_z = set->near_z; a.alpha_min = set->alpha_min; a.dilation = set->dilation; }
+    a.near_z = set->near_z; a.alpha_min = set->alpha_min; a.dilation = set->dilation;
     a.n = n;
     a.means = means; a.log_scales = log_scales; a.quats = quats; a.opac = opacity_logits; a.sh = sh;
     a.splats = splats; a.depth = depth; a.rect = rect; a.tiles_touched = tiles_touched; a.clamp = clamp_mask;
     const dim3 grid((n + kPreBlock - 1) / kPreBlock), block(kPreBlock);
     hipStream_t s = as_stream(stream);
-    const bool vec = sh && aligned16(sh);
+    const bool vec = aligned16(sh);
     switch (sh_degree) {
-        case 0: launch_pre<0, false>(part, grid, block, s, a); break;
-        case 1: vec ? launch_pre<1, true>(part, grid, block, s, a) : launch_pre<1, false>(part, grid, block, s, a); break;
-        case 2: launch_pre<2, false>(part, grid, block, s, a); break;
-        default: vec ? launch_pre<3, true>(part, grid, block, s, a) : launch_pre<3, false>(part, grid, block, s, a); break;
+        case 0: launch_pre<0, false>(grid, block, s, a); break;
+        case 1: vec ? launch_pre<1, true>(grid, block, s, a) : launch_pre<1, false>(grid, block, s, a); break;
+        case 2: launch_pre<2, false>(grid, block, s, a); break;
+        default: vec ? launch_pre<3, true>(grid, block, s, a) : launch_pre<3, false>(grid, block, s, a); break;
     }
     return launch_status();
 }
@@ -317,7 +282,7 @@ extern "C" int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32
                              const float* means, const float* log_scales, const float* quats,
                              const float* opacity_logits, const float* sh, float* splats, float* depth,
                              int16_t* rect, int32_t* tiles_touched, uint8_t* clamp_mask, void* stream) {
-    return preprocess_impl(Part::kAll, cam, 1, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
+    return preprocess_impl(cam, 1, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
                            splats, depth, rect, tiles_touched, clamp_mask, stream);
 }
 
@@ -326,19 +291,6 @@ extern "C" int gs_preprocess_views(const gs_camera* cams, int32_t views, const g
                                    const float* quats, const float* opacity_logits, const float* sh, float* splats,
                                    float* depth, int16_t* rect, int32_t* tiles_touched, uint8_t* clamp_mask,
                                    void* stream) {
-    return preprocess_impl(Part::kAll, cams, views, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
+    return preprocess_impl(cams, views, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
                            splats, depth, rect, tiles_touched, clamp_mask, stream);
-}
-
-extern "C" int gs_project(const gs_camera* cam, const gs_settings* set, int32_t n, const float* means,
-                          const float* log_scales, const float* quats, const float* opacity_logits, float* splats,
-                          float* depth, int16_t* rect, int32_t* tiles_touched, void* stream) {
-    return preprocess_impl(Part::kGeometry, cam, 1, set, n, 0, means, log_scales, quats, opacity_logits, nullptr,
-                           splats, depth, rect, tiles_touched, nullptr, stream);
-}
-
-extern "C" int gs_shade(const gs_camera* cam, int32_t n, int32_t sh_degree, const float* means, const float* sh,
-                        float* splats, uint8_t* clamp_mask, void* stream) {
-    return preprocess_impl(Part::kColor, cam, 1, nullptr, n, sh_degree, means, nullptr, nullptr, nullptr, sh,
-                           splats, nullptr, nullptr, nullptr, clamp_mask, stream);
 }

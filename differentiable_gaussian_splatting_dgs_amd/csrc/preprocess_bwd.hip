@@ -45,7 +45,6 @@ struct BwdArgs {
     float* dsh;
     float* accum;   // densification statistic, optional
     int32_t* count;
-    float* view_dir;  // [n,3] unit camera-to-mean directions the SH gradient uses (split tail)
     AdamHyper adam;
 };
 
@@ -158,19 +157,29 @@ __device__ __forceinline__ ViewIn load_view(const BwdArgs& a, size_t iv) {
     return w;
 }
 
+// 1 / x and 1 / sqrt(x) in float64 for a positive, finite x: the hardware
+// float64 approximation refined by Newton steps (each doubles the correct bits),
+// a few operations where the correctly rounded division is a long sequence.
+__device__ __forceinline__ double rcp_f64(double x) {
+    double r = __builtin_amdgcn_rcp(x);
+    r = r * (2.0 - x * r);
+    r = r * (2.0 - x * r);
+    return r;
+}
+__device__ __forceinline__ double rsqrt_f64(double x) {
+    double r = __builtin_amdgcn_rsq(x);
+    r = r * (1.5 - 0.5 * x * r * r);
+    r = r * (1.5 - 0.5 * x * r * r);
+    return r;
+}
+
 // Gaussian i seen by camera c, with that view's inputs w.
 template <int DEG>
 __device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i, const ViewIn& w, const float* s_sh,
                                       int col, int ldg, float dmu[3], float dls[3], float dq[4], float& dop,
-                                      float Y[16], float drgb[3], float dir[3]) {
+                                      float Y[16], float drgb[3]) {
     constexpr int K = (DEG + 1) * (DEG + 1);
-    const float Rv[9] = {(float)c.R[0], (float)c.R[1], (float)c.R[2], (float)c.R[3], (float)c.R[4],
-                         (float)c.R[5], (float)c.R[6], (float)c.R[7], (float)c.R[8]};
-    const float fx = (float)c.fx, fy = (float)c.fy;
     const float mx = a.means[3 * i], my = a.means[3 * i + 1], mz = a.means[3 * i + 2];
-    const float tx = Rv[0] * mx + Rv[1] * my + Rv[2] * mz + (float)c.t[0];
-    const float ty = Rv[3] * mx + Rv[4] * my + Rv[5] * mz + (float)c.t[1];
-    const float tz = Rv[6] * mx + Rv[7] * my + Rv[8] * mz + (float)c.t[2];
 
     const float4 g0 = w.g0, g1 = w.g1, g2 = w.g2;
     const float du = g0.x, dv = g0.y, dA = g0.z, dB = g0.w, dC = g1.x, dsig = g1.y;
@@ -187,7 +196,6 @@ __device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i,
     const float vx = mx - cpx, vy = my - cpy, vz = mz - cpz;
     const float il = 1.f / sqrtf(vx * vx + vy * vy + vz * vz);
     const float dx = vx * il, dy = vy * il, dz = vz * il;
-    dir[0] = dx; dir[1] = dy; dir[2] = dz;
     const uint8_t cm = w.cm;
 #pragma unroll
     for (int ch = 0; ch < 3; ++ch)
@@ -203,109 +211,107 @@ __device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i,
     const float dot = dx * gdx + dy * gdy + dz * gdz;
     float dmx = (gdx - dx * dot) * il, dmy = (gdy - dy * dot) * il, dmz = (gdz - dz * dot) * il;
 
+    // The geometric part of the chain runs in float64.  Its intermediates span many
+    // orders of magnitude for strongly anisotropic Gaussians, and several steps are
+    // differences of nearly equal products: the 2D covariance's determinant for a
+    // flat Gaussian seen edge-on, and dT = 2 dA Sigma t0 + dB Sigma t1 when Sigma is
+    // dominated by one long axis.  float64 runs at the float32 rate per instruction
+    // on CDNA4, and this kernel is bound by memory, not by these few hundred operations.
     // rotation and scale: M = R(q/|q|) diag(s)
-    const float4 q = reinterpret_cast<const float4*>(a.quats)[i];
-    const float iq = 1.f / sqrtf(q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w);
-    const float qw = q.x * iq, qx = q.y * iq, qy = q.z * iq, qz = q.w * iq;
-    const float s[3] = {__expf(a.log_scales[3 * i]), __expf(a.log_scales[3 * i + 1]), __expf(a.log_scales[3 * i + 2])};
-    float R[9];
-    R[0] = 1.f - 2.f * (qy * qy + qz * qz); R[1] = 2.f * (qx * qy - qw * qz); R[2] = 2.f * (qx * qz + qw * qy);
-    R[3] = 2.f * (qx * qy + qw * qz); R[4] = 1.f - 2.f * (qx * qx + qz * qz); R[5] = 2.f * (qy * qz - qw * qx);
-    R[6] = 2.f * (qx * qz - qw * qy); R[7] = 2.f * (qy * qz + qw * qx); R[8] = 1.f - 2.f * (qx * qx + qy * qy);
-    float M[9];
+    const float4 q4 = reinterpret_cast<const float4*>(a.quats)[i];
+    const double qn2 = (double)q4.x * q4.x + (double)q4.y * q4.y + (double)q4.z * q4.z + (double)q4.w * q4.w;
+    const double iq = rsqrt_f64(qn2);
+    const double qw = q4.x * iq, qx = q4.y * iq, qy = q4.z * iq, qz = q4.w * iq;
+    // a float32 scale differs from exp(log-scale) by a relative 2^-24, which only rescales its axis
+    const double s[3] = {__expf(a.log_scales[3 * i]), __expf(a.log_scales[3 * i + 1]), __expf(a.log_scales[3 * i + 2])};
+    double R[9];
+    R[0] = 1.0 - 2.0 * (qy * qy + qz * qz); R[1] = 2.0 * (qx * qy - qw * qz); R[2] = 2.0 * (qx * qz + qw * qy);
+    R[3] = 2.0 * (qx * qy + qw * qz); R[4] = 1.0 - 2.0 * (qx * qx + qz * qz); R[5] = 2.0 * (qy * qz - qw * qx);
+    R[6] = 2.0 * (qx * qz - qw * qy); R[7] = 2.0 * (qy * qz + qw * qx); R[8] = 1.0 - 2.0 * (qx * qx + qy * qy);
+    double M[9];
 #pragma unroll
     for (int r = 0; r < 3; ++r)
 #pragma unroll
         for (int k = 0; k < 3; ++k) M[3 * r + k] = R[3 * r + k] * s[k];
-    float Sig[9];
-#pragma unroll
-    for (int r = 0; r < 3; ++r)
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-            Sig[3 * r + k] = M[3 * r] * M[3 * k] + M[3 * r + 1] * M[3 * k + 1] + M[3 * r + 2] * M[3 * k + 2];
 
-    // T = J R_view
-    const float iz = 1.f / tz, iz2 = iz * iz;
-    const float j00 = fx * iz, j02 = -fx * tx * iz2, j11 = fy * iz, j12 = -fy * ty * iz2;
-    float t0[3], t1[3];
+    // T = J R_view with rows t0, t1; u = M^T t0, v = M^T t1: Sigma t0 = M u, Sigma t1 = M v, and the
+    // 2D covariance before dilation is [[u.u, u.v], [u.v, v.v]]
+    const double tx = c.R[0] * mx + c.R[1] * my + c.R[2] * mz + c.t[0];
+    const double ty = c.R[3] * mx + c.R[4] * my + c.R[5] * mz + c.t[1];
+    const double tz = c.R[6] * mx + c.R[7] * my + c.R[8] * mz + c.t[2];
+    const double iz = rcp_f64(tz), iz2 = iz * iz, iz3 = iz2 * iz;
+    const double j00 = c.fx * iz, j02 = -c.fx * tx * iz2, j11 = c.fy * iz, j12 = -c.fy * ty * iz2;
+    double t0[3], t1[3], u[3], v[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        t0[k] = j00 * Rv[k] + j02 * Rv[6 + k];
-        t1[k] = j11 * Rv[3 + k] + j12 * Rv[6 + k];
+        t0[k] = j00 * c.R[k] + j02 * c.R[6 + k];
+        t1[k] = j11 * c.R[3 + k] + j12 * c.R[6 + k];
     }
-    float St0[3], St1[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        u[k] = M[k] * t0[0] + M[3 + k] * t0[1] + M[6 + k] * t0[2];
+        v[k] = M[k] * t1[0] + M[3 + k] * t1[1] + M[6 + k] * t1[2];
+    }
+    const double dil = a.dilation;
+    const double ca = u[0] * u[0] + u[1] * u[1] + u[2] * u[2] + dil;
+    const double cb = u[0] * v[0] + u[1] * v[1] + u[2] * v[2];
+    const double cc = v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + dil;
+    const double D = ca * cc - cb * cb;
+    const double iD = rcp_f64(D), iD2 = iD * iD;
+    // conic = [[cc, -cb], [-cb, ca]] / D  ->  dL/d(2D covariance)
+    const double da = (-cc * cc * dA + cb * cc * dB - cb * cb * dC) * iD2;
+    const double db = (2.0 * cb * cc * dA - (ca * cc + cb * cb) * dB + 2.0 * ca * cb * dC) * iD2;
+    const double dc = (-cb * cb * dA + ca * cb * dB - ca * ca * dC) * iD2;
+
+    // dSigma = da t0 t0^T + db (t0 t1^T + t1 t0^T) / 2 + dc t1 t1^T.  With w0 = 2 da u + db v and
+    // w1 = db u + 2 dc v (u = M^T t0, v = M^T t1):
+    //   dT = dL/d(t0, t1) = 2 dSigma' -> (M w0, M w1)      (dT0 = 2 da Sigma t0 + db Sigma t1, ...)
+    //   dM = 2 dSigma M = t0 w0^T + t1 w1^T                (Sigma = M M^T)
+    double w0[3], w1[3], dT0[3], dT1[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        w0[k] = 2.0 * da * u[k] + db * v[k];
+        w1[k] = db * u[k] + 2.0 * dc * v[k];
+    }
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
-        St0[r] = Sig[3 * r] * t0[0] + Sig[3 * r + 1] * t0[1] + Sig[3 * r + 2] * t0[2];
-        St1[r] = Sig[3 * r] * t1[0] + Sig[3 * r + 1] * t1[1] + Sig[3 * r + 2] * t1[2];
-    }
-    const float ca = t0[0] * St0[0] + t0[1] * St0[1] + t0[2] * St0[2] + a.dilation;
-    const float cb = t0[0] * St1[0] + t0[1] * St1[1] + t0[2] * St1[2];
-    const float cc = t1[0] * St1[0] + t1[1] * St1[1] + t1[2] * St1[2] + a.dilation;
-    const float D = ca * cc - cb * cb;
-    const float iD2 = 1.f / (D * D);
-    // conic = [[cc, -cb], [-cb, ca]] / D
-    const float da = (-cc * cc * dA + cb * cc * dB - cb * cb * dC) * iD2;
-    const float db = (2.f * cb * cc * dA - (ca * cc + cb * cb) * dB + 2.f * ca * cb * dC) * iD2;
-    const float dc = (-cb * cb * dA + ca * cb * dB - ca * ca * dC) * iD2;
-
-    // dSigma (symmetric) and dT
-    float dS[9];
-#pragma unroll
-    for (int r = 0; r < 3; ++r)
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-            dS[3 * r + k] = da * t0[r] * t0[k] + 0.5f * db * (t0[r] * t1[k] + t1[r] * t0[k]) + dc * t1[r] * t1[k];
-    float dT0[3], dT1[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        dT0[k] = 2.f * da * St0[k] + db * St1[k];
-        dT1[k] = db * St0[k] + 2.f * dc * St1[k];
+        dT0[r] = M[3 * r] * w0[0] + M[3 * r + 1] * w0[1] + M[3 * r + 2] * w0[2];
+        dT1[r] = M[3 * r] * w1[0] + M[3 * r + 1] * w1[1] + M[3 * r + 2] * w1[2];
     }
     // T = J R_view  ->  dJ = dT R_view^T (only the four non-zero entries of J matter)
-    const float dJ00 = dT0[0] * Rv[0] + dT0[1] * Rv[1] + dT0[2] * Rv[2];
-    const float dJ02 = dT0[0] * Rv[6] + dT0[1] * Rv[7] + dT0[2] * Rv[8];
-    const float dJ11 = dT1[0] * Rv[3] + dT1[1] * Rv[4] + dT1[2] * Rv[5];
-    const float dJ12 = dT1[0] * Rv[6] + dT1[1] * Rv[7] + dT1[2] * Rv[8];
-    const float iz3 = iz2 * iz;
-    const float dtx = -fx * iz2 * dJ02 + fx * iz * du;
-    const float dty = -fy * iz2 * dJ12 + fy * iz * dv;
-    const float dtz = -fx * iz2 * dJ00 + 2.f * fx * tx * iz3 * dJ02 - fy * iz2 * dJ11 + 2.f * fy * ty * iz3 * dJ12 -
-                      fx * tx * iz2 * du - fy * ty * iz2 * dv;
-    dmx += Rv[0] * dtx + Rv[3] * dty + Rv[6] * dtz;
-    dmy += Rv[1] * dtx + Rv[4] * dty + Rv[7] * dtz;
-    dmz += Rv[2] * dtx + Rv[5] * dty + Rv[8] * dtz;
-    dmu[0] = dmx; dmu[1] = dmy; dmu[2] = dmz;
+    const double dJ00 = dT0[0] * c.R[0] + dT0[1] * c.R[1] + dT0[2] * c.R[2];
+    const double dJ02 = dT0[0] * c.R[6] + dT0[1] * c.R[7] + dT0[2] * c.R[8];
+    const double dJ11 = dT1[0] * c.R[3] + dT1[1] * c.R[4] + dT1[2] * c.R[5];
+    const double dJ12 = dT1[0] * c.R[6] + dT1[1] * c.R[7] + dT1[2] * c.R[8];
+    const double dtx = -c.fx * iz2 * dJ02 + c.fx * iz * du;
+    const double dty = -c.fy * iz2 * dJ12 + c.fy * iz * dv;
+    const double dtz = -c.fx * iz2 * dJ00 + 2.0 * c.fx * tx * iz3 * dJ02 - c.fy * iz2 * dJ11 +
+                       2.0 * c.fy * ty * iz3 * dJ12 - c.fx * tx * iz2 * du - c.fy * ty * iz2 * dv;
+    dmu[0] = (float)(dmx + c.R[0] * dtx + c.R[3] * dty + c.R[6] * dtz);
+    dmu[1] = (float)(dmy + c.R[1] * dtx + c.R[4] * dty + c.R[7] * dtz);
+    dmu[2] = (float)(dmz + c.R[2] * dtx + c.R[5] * dty + c.R[8] * dtz);
 
-    // Sigma = M M^T -> dM = 2 dSigma M; M = R S -> dR, ds
-    float dM[9];
+    // M = R S: dL/ds_k = sum_r dM_rk R_rk and (R^T t0)_k = u_k / s_k, so the log-scale gradient
+    // s_k dL/ds_k = w0_k u_k + w1_k v_k; dR_rk = dM_rk s_k
+#pragma unroll
+    for (int k = 0; k < 3; ++k) dls[k] = (float)(w0[k] * u[k] + w1[k] * v[k]);
+    double dR[9];
 #pragma unroll
     for (int r = 0; r < 3; ++r)
 #pragma unroll
-        for (int k = 0; k < 3; ++k)
-            dM[3 * r + k] = 2.f * (dS[3 * r] * M[k] + dS[3 * r + 1] * M[3 + k] + dS[3 * r + 2] * M[6 + k]);
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        const float ds = dM[k] * R[k] + dM[3 + k] * R[3 + k] + dM[6 + k] * R[6 + k];
-        dls[k] = ds * s[k];
-    }
-    float dR[9];
-#pragma unroll
-    for (int r = 0; r < 3; ++r)
-#pragma unroll
-        for (int k = 0; k < 3; ++k) dR[3 * r + k] = dM[3 * r + k] * s[k];
-    const float gw = 2.f * (-qz * dR[1] + qy * dR[2] + qz * dR[3] - qx * dR[5] - qy * dR[6] + qx * dR[7]);
-    const float gx = 2.f * (qy * dR[1] + qz * dR[2] + qy * dR[3] - 2.f * qx * dR[4] - qw * dR[5] + qz * dR[6] +
-                            qw * dR[7] - 2.f * qx * dR[8]);
-    const float gy = 2.f * (-2.f * qy * dR[0] + qx * dR[1] + qw * dR[2] + qx * dR[3] + qz * dR[5] - qw * dR[6] +
-                            qz * dR[7] - 2.f * qy * dR[8]);
-    const float gz = 2.f * (-2.f * qz * dR[0] - qw * dR[1] + qx * dR[2] + qw * dR[3] - 2.f * qz * dR[4] +
-                            qy * dR[5] + qx * dR[6] + qy * dR[7]);
-    const float pr = qw * gw + qx * gx + qy * gy + qz * gz;
-    dq[0] = (gw - qw * pr) * iq;
-    dq[1] = (gx - qx * pr) * iq;
-    dq[2] = (gy - qy * pr) * iq;
-    dq[3] = (gz - qz * pr) * iq;
+        for (int k = 0; k < 3; ++k) dR[3 * r + k] = (t0[r] * w0[k] + t1[r] * w1[k]) * s[k];
+    const double gw = 2.0 * (-qz * dR[1] + qy * dR[2] + qz * dR[3] - qx * dR[5] - qy * dR[6] + qx * dR[7]);
+    const double gx = 2.0 * (qy * dR[1] + qz * dR[2] + qy * dR[3] - 2.0 * qx * dR[4] - qw * dR[5] + qz * dR[6] +
+                             qw * dR[7] - 2.0 * qx * dR[8]);
+    const double gy = 2.0 * (-2.0 * qy * dR[0] + qx * dR[1] + qw * dR[2] + qx * dR[3] + qz * dR[5] - qw * dR[6] +
+                             qz * dR[7] - 2.0 * qy * dR[8]);
+    const double gz = 2.0 * (-2.0 * qz * dR[0] - qw * dR[1] + qx * dR[2] + qw * dR[3] - 2.0 * qz * dR[4] +
+                             qy * dR[5] + qx * dR[6] + qy * dR[7]);
+    const double pr = qw * gw + qx * gx + qy * gy + qz * gz;
+    dq[0] = (float)((gw - qw * pr) * iq);
+    dq[1] = (float)((gx - qx * pr) * iq);
+    dq[2] = (float)((gy - qy * pr) * iq);
+    dq[3] = (float)((gz - qz * pr) * iq);
 }
 
 // Element-wise SH part: the gradient Y_k dL/dc of each coefficient in HBM order
@@ -368,12 +374,10 @@ __device__ __forceinline__ void sh_elements(const BwdArgs& a, const float* s_sh,
 //           densification statistic, and leaves Y and the colour gradient in LDS;
 //  phase 2: the SH gradients Y_k dL/dc, element by element in HBM order, so
 //           gradient writes and the Adam read-modify-write are coalesced.
-// SH = false: the geometry half of the tail (no phase 2); the view directions
-// go to a.view_dir (zero for Gaussians outside every tile) for k_grad3d_sh.
 // MV: a batch of a.views views; phase 1 runs the chain once per view in which
 // the Gaussian touches a tile and sums the gradients (and the statistic over
 // the views), and keeps the summed SH gradient itself in LDS for phase 2.
-template <int DEG, bool ADAM, bool SH = true, bool MV = false>
+template <int DEG, bool ADAM, bool MV = false>
 __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
     constexpr int K = (DEG + 1) * (DEG + 1);
     constexpr int J = 3 * K;
@@ -435,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
         int32_t nvis = 0;
         if (a.accum) { acc = a.accum[i]; nvis = a.count[i]; }
         float dmu[3] = {0.f, 0.f, 0.f}, dls[3] = {0.f, 0.f, 0.f}, dq[4] = {0.f, 0.f, 0.f, 0.f}, dop = 0.f;
-        float Y[16], drgb[3] = {0.f, 0.f, 0.f}, dir[3] = {0.f, 0.f, 0.f};
+        float Y[16], drgb[3] = {0.f, 0.f, 0.f};
         if constexpr (MV) {
 #pragma unroll
             for (int j = 0; j < J; ++j) s_y[j * LDG + t] = 0.f;
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
                 if (cur.tt <= 0) { cur = nxt; continue; }
                 seen = true;
                 float vmu[3], vls[3], vq[4], vop;
-                chain<DEG>(a, a.cams[view], i, cur, s_sh, t, LDG, vmu, vls, vq, vop, Y, drgb, dir);
+                chain<DEG>(a, a.cams[view], i, cur, s_sh, t, LDG, vmu, vls, vq, vop, Y, drgb);
 #pragma unroll
                 for (int k = 0; k < 3; ++k) { dmu[k] += vmu[k]; dls[k] += vls[k]; }
 #pragma unroll
@@ -471,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
         } else {
             const bool vis = a.tt[i] > 0;
             if (vis) {
-                chain<DEG>(a, a.cams[0], i, load_view(a, (size_t)i), s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb, dir);
+                chain<DEG>(a, a.cams[0], i, load_view(a, (size_t)i), s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb);
                 if (a.accum) {
                     const float2 d2 = *reinterpret_cast<const float2*>(a.grad2d + (size_t)i * GS_GRAD2D_STRIDE);
                     a.accum[i] = acc + sqrtf(d2.x * d2.x + d2.y * d2.y);
@@ -482,17 +486,12 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
                 for (int k = 0; k < K; ++k) Y[k] = 0.f;
             }
         }
-        if constexpr (MV) {
-        } else if constexpr (SH) {
+        if constexpr (!MV) {
 #pragma unroll
             for (int k = 0; k < K; ++k) s_y[k * LDG + t] = Y[k];
             s_c[t] = drgb[0];
             s_c[LDG + t] = drgb[1];
             s_c[2 * LDG + t] = drgb[2];
-        } else {
-            a.view_dir[3 * (size_t)i] = dir[0];
-            a.view_dir[3 * (size_t)i + 1] = dir[1];
-            a.view_dir[3 * (size_t)i + 2] = dir[2];
         }
         if (a.dmeans) {
             a.dmeans[3 * (size_t)i] = dmu[0]; a.dmeans[3 * (size_t)i + 1] = dmu[1]; a.dmeans[3 * (size_t)i + 2] = dmu[2];
@@ -528,65 +527,18 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
             a.opac[i] = po; nt_st(mo, &h.m[3][i]); nt_st(vo, &h.v[3][i]);
         }
     }
-    if constexpr (!SH) return;
     __syncthreads();
     sh_elements<DEG, ADAM, MV>(a, s_sh, LDG, s_y, s_c, cnt, base, t);
 }
 
-// The SH half of the tail on its own: Y from the stored view direction, the
-// clamp-masked colour gradient from grad2d, then the same element-wise update
-// as the fused kernel (so both give the same bits).
-template <int DEG>
-__global__ __launch_bounds__(kThreads) void k_grad3d_sh(BwdArgs a) {
-    constexpr int K = (DEG + 1) * (DEG + 1);
-    constexpr int J = 3 * K;
-    constexpr int LDG = kG + 1;
-    __shared__ float s_y[K * LDG];
-    __shared__ float s_c[3 * LDG];
-    const int t = threadIdx.x;
-    const int g0 = blockIdx.x * kG;
-    const int ng = min(kG, a.n - g0);
-    const int cnt = ng * J;
-    const size_t base = (size_t)g0 * J;
-    if (t < ng) {
-        const int i = g0 + t;
-        float Y[16];
-        sh_values<DEG>(a.view_dir[3 * (size_t)i], a.view_dir[3 * (size_t)i + 1], a.view_dir[3 * (size_t)i + 2], Y);
-        const float4 g1 = reinterpret_cast<const float4*>(a.grad2d)[3 * (size_t)i + 1];
-        const float4 g2 = reinterpret_cast<const float4*>(a.grad2d)[3 * (size_t)i + 2];
-        const uint8_t cm = a.clamp[i];
-        float drgb[3] = {g1.z, g1.w, g2.x};
-#pragma unroll
-        for (int ch = 0; ch < 3; ++ch)
-            if ((cm >> ch) & 1u) drgb[ch] = 0.f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) s_y[k * LDG + t] = Y[k];
-        s_c[t] = drgb[0];
-        s_c[LDG + t] = drgb[1];
-        s_c[2 * LDG + t] = drgb[2];
-    }
-    __syncthreads();
-    sh_elements<DEG, true>(a, nullptr, LDG, s_y, s_c, cnt, base, t);
-}
-
-template <bool ADAM, bool SH = true, bool MV = false>
+template <bool ADAM, bool MV = false>
 inline void launch_grad3d(int deg, const BwdArgs& a, hipStream_t s) {
     const dim3 grid((a.n + kG - 1) / kG), block(kThreads);
     switch (deg) {
-        case 0: hipLaunchKernelGGL((k_grad3d<0, ADAM, SH, MV>), grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL((k_grad3d<1, ADAM, SH, MV>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_grad3d<2, ADAM, SH, MV>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((k_grad3d<3, ADAM, SH, MV>), grid, block, 0, s, a); break;
-    }
-}
-
-inline void launch_grad3d_sh(int deg, const BwdArgs& a, hipStream_t s) {
-    const dim3 grid((a.n + kG - 1) / kG), block(kThreads);
-    switch (deg) {
-        case 0: hipLaunchKernelGGL((k_grad3d_sh<0>), grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL((k_grad3d_sh<1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_grad3d_sh<2>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((k_grad3d_sh<3>), grid, block, 0, s, a); break;
+        case 0: hipLaunchKernelGGL((k_grad3d<0, ADAM, MV>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((k_grad3d<1, ADAM, MV>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_grad3d<2, ADAM, MV>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_grad3d<3, ADAM, MV>), grid, block, 0, s, a); break;
     }
 }
 
@@ -663,52 +615,6 @@ extern "C" int gs_preprocess_bwd_adam(const gs_camera* cam, const gs_settings* s
     return launch_status();
 }
 
-extern "C" int gs_preprocess_bwd_adam_geom(const gs_camera* cam, const gs_settings* set, int32_t n,
-                                           int32_t sh_degree, float* means, float* log_scales, float* quats,
-                                           float* opacity_logits, const float* sh, const int32_t* tiles_touched,
-                                           const uint8_t* clamp_mask, const float* grad2d,
-                                           const gs_adam_state* adam, float* densify_accum,
-                                           int32_t* densify_count, float* view_dir, void* stream) {
-    if (!camera_ok(cam) || !set || !adam || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE)
-        return GS_EINVAL;
-    if (adam->step < 1) return GS_EINVAL;
-    if (n == 0) return GS_OK;
-    if (!means || !log_scales || !quats || !opacity_logits || !sh || !tiles_touched || !clamp_mask || !grad2d ||
-        !view_dir)
-        return GS_EINVAL;
-    for (int k = 0; k < 4; ++k)
-        if (!adam->exp_avg[k] || !adam->exp_avg_sq[k]) return GS_EINVAL;
-    if ((densify_accum == nullptr) != (densify_count == nullptr)) return GS_EINVAL;
-    if (!aligned16(quats) || !aligned16(grad2d)) return GS_EALIGN;
-    if (!aligned16(adam->exp_avg[2]) || !aligned16(adam->exp_avg_sq[2])) return GS_EALIGN;
-    BwdArgs a;
-    fill_common(a, cam, 1, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
-    a.accum = densify_accum; a.count = densify_count;
-    a.view_dir = view_dir;
-    fill_adam(a, adam);
-    launch_grad3d<true, false>(sh_degree, a, as_stream(stream));
-    return launch_status();
-}
-
-extern "C" int gs_preprocess_bwd_adam_sh(int32_t n, int32_t sh_degree, float* sh, const uint8_t* clamp_mask,
-                                         const float* grad2d, const float* view_dir, const gs_adam_state* adam,
-                                         void* stream) {
-    if (!adam || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
-    if (adam->step < 1) return GS_EINVAL;
-    if (n == 0) return GS_OK;
-    if (!sh || !clamp_mask || !grad2d || !view_dir || !adam->exp_avg[4] || !adam->exp_avg_sq[4]) return GS_EINVAL;
-    if (!aligned16(grad2d)) return GS_EALIGN;
-    BwdArgs a{};
-    a.n = n;
-    a.sh = sh;
-    a.clamp = clamp_mask;
-    a.grad2d = grad2d;
-    a.view_dir = const_cast<float*>(view_dir);
-    fill_adam(a, adam);
-    launch_grad3d_sh(sh_degree, a, as_stream(stream));
-    return launch_status();
-}
-
 extern "C" int gs_preprocess_bwd_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                                        int32_t sh_degree, const float* means, const float* log_scales,
                                        const float* quats, const float* opacity_logits, const float* sh,
@@ -726,7 +632,7 @@ extern "C" int gs_preprocess_bwd_views(const gs_camera* cams, int32_t views, con
     fill_common(a, cams, views, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask,
                 grad2d);
     a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
-    launch_grad3d<false, true, true>(sh_degree, a, as_stream(stream));
+    launch_grad3d<false, true>(sh_degree, a, as_stream(stream));
     return launch_status();
 }
 
@@ -757,6 +663,6 @@ extern "C" int gs_preprocess_bwd_adam_views(const gs_camera* cams, int32_t views
     a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
     a.accum = densify_accum; a.count = densify_count;
     fill_adam(a, adam);
-    launch_grad3d<true, true, true>(sh_degree, a, as_stream(stream));
+    launch_grad3d<true, true>(sh_degree, a, as_stream(stream));
     return launch_status();
 }

@@ -721,8 +721,9 @@ __global__ void k_zero_f32(float* p, size_t count) {
     for (; i < count; i += stride) p[i] = 0.f;
 }
 
-// Pair counts: one thread per pixel, walking the whole tile list.
-__global__ __launch_bounds__(256) void k_count_pairs(RenderArgs a, unsigned long long* counts) {
+// Pair counts: one thread per pixel, walking the whole tile list.  ev_px
+// (optional, [views, H, W]) receives each pixel's evaluated entries.
+__global__ __launch_bounds__(256) void k_count_pairs(RenderArgs a, unsigned long long* counts, int32_t* ev_px) {
     __shared__ unsigned long long s_c[3];
     const BlendArgs& b = a.b;
     if (threadIdx.x < 3) s_c[threadIdx.x] = 0;
@@ -752,6 +753,7 @@ __global__ __launch_bounds__(256) void k_count_pairs(RenderArgs a, unsigned long
             ++nb;
             nc = k - range.x + 1;
         }
+        if (ev_px) ev_px[((size_t)blockIdx.z * b.height + py) * b.width + px] = (int32_t)ev;
     }
     atomicAdd(&s_c[0], ev);
     atomicAdd(&s_c[1], nc);
@@ -901,7 +903,7 @@ int render_bwd_impl(const gs_camera* cams, int32_t views, const gs_settings* set
 
 int count_pairs_impl(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                      const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats, int64_t* counts,
-                     void* stream) {
+                     int32_t* evaluated_px, void* stream) {
     int rc = render_common_checks(cams, views, set, tile_ranges, splats);
     if (rc) return rc;
     if (!counts || n < 0) return GS_EINVAL;
@@ -913,7 +915,8 @@ int count_pairs_impl(const gs_camera* cams, int32_t views, const gs_settings* se
     a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
     auto* c = reinterpret_cast<unsigned long long*>(counts);
     hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(64), 0, s, c, 3);
-    hipLaunchKernelGGL(k_count_pairs, dim3(tiles_x(cams), tiles_y(cams), views), dim3(256), 0, s, a, c);
+    hipLaunchKernelGGL(k_count_pairs, dim3(tiles_x(cams), tiles_y(cams), views), dim3(256), 0, s, a, c,
+                       evaluated_px);
     return launch_status();
 }
 
@@ -973,12 +976,13 @@ extern "C" int gs_render_bwd_views(const gs_camera* cams, int32_t views, const g
 }
 
 extern "C" int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
-                              const uint32_t* point_list, const float* splats, int64_t* counts, void* stream) {
-    return count_pairs_impl(cam, 1, set, n, tile_ranges, point_list, splats, counts, stream);
+                              const uint32_t* point_list, const float* splats, int64_t* counts,
+                              int32_t* evaluated_px, void* stream) {
+    return count_pairs_impl(cam, 1, set, n, tile_ranges, point_list, splats, counts, evaluated_px, stream);
 }
 
 extern "C" int gs_count_pairs_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                                     const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
-                                    int64_t* counts, void* stream) {
-    return count_pairs_impl(cams, views, set, n, tile_ranges, point_list, splats, counts, stream);
+                                    int64_t* counts, int32_t* evaluated_px, void* stream) {
+    return count_pairs_impl(cams, views, set, n, tile_ranges, point_list, splats, counts, evaluated_px, stream);
 }

@@ -58,15 +58,13 @@ class GsGaussianSet(C.Structure):
                 ("exp_avg_sq", C.c_void_p * 5), ("densify_accum", C.c_void_p), ("densify_count", C.c_void_p)]
 
 
-SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_project", "gs_shade",
-           "gs_bin_workspace_size", "gs_bin_sort", "gs_bin_keys", "gs_render_fwd", "gs_render_fwd_loss",
-           "gs_render_bwd", "gs_preprocess_bwd", "gs_preprocess_bwd_adam", "gs_preprocess_bwd_adam_geom",
-           "gs_preprocess_bwd_adam_sh", "gs_image_loss", "gs_densify_accum", "gs_adam_step", "gs_count_pairs",
-           "gs_densify_workspace_size", "gs_densify", "gs_opacity_reset",
+SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_bin_workspace_size",
+           "gs_bin_sort", "gs_debug_sort_wait_limit", "gs_bin_keys", "gs_render_fwd", "gs_render_fwd_loss",
+           "gs_render_bwd", "gs_preprocess_bwd", "gs_preprocess_bwd_adam", "gs_image_loss", "gs_densify_accum",
+           "gs_adam_step", "gs_count_pairs", "gs_densify_workspace_size", "gs_densify", "gs_opacity_reset",
            "gs_preprocess_views", "gs_bin_workspace_size_views", "gs_bin_sort_views", "gs_render_fwd_views",
            "gs_render_fwd_loss_views", "gs_render_bwd_views", "gs_preprocess_bwd_views",
-           "gs_preprocess_bwd_adam_views", "gs_count_pairs_views", "gs_stream_copy", "gs_fma_loop",
-           "gs_count_nonfinite"]
+           "gs_preprocess_bwd_adam_views", "gs_count_pairs_views", "gs_count_nonfinite"]
 MAX_VIEWS = 8
 PARAM_ORDER = ("means", "log_scales", "quats", "opacity_logits", "sh")
 
@@ -93,21 +91,17 @@ def load_library(path=LIB_PATH):
     lib.gs_bin_workspace_size.argtypes = [_i32, P(GsCamera), _i64, P(C.c_size_t)]
     lib.gs_bin_sort.argtypes = [P(GsCamera), _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
     lib.gs_bin_keys.argtypes = [P(GsCamera), _vp, _vp, _vp, _vp, _vp]
+    lib.gs_debug_sort_wait_limit.argtypes = [_i64]
     lib.gs_render_fwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_vp]
     lib.gs_render_fwd_loss.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_i32] + [_vp] * 4 + [_vp]
     lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 9 + [_i32, _vp]
     lib.gs_preprocess_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
     lib.gs_preprocess_bwd_adam.argtypes = ([P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 8 +
                                            [P(GsAdamState)] + [_vp] * 7 + [_vp])
-    lib.gs_preprocess_bwd_adam_geom.argtypes = ([P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 8 +
-                                                [P(GsAdamState)] + [_vp] * 3 + [_vp])
-    lib.gs_preprocess_bwd_adam_sh.argtypes = [_i32, _i32] + [_vp] * 4 + [P(GsAdamState), _vp]
-    lib.gs_project.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_vp]
-    lib.gs_shade.argtypes = [P(GsCamera), _i32, _i32] + [_vp] * 4 + [_vp]
     lib.gs_image_loss.argtypes = [_i32, _i64, _vp, _vp, _vp, _vp, _vp]
     lib.gs_densify_accum.argtypes = [_i32, _vp, _vp, _vp, _vp, _vp]
     lib.gs_adam_step.argtypes = [_i32, P(GsAdamGroup), C.c_float, C.c_float, C.c_float, _i32, _vp]
-    lib.gs_count_pairs.argtypes = [P(GsCamera), P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.gs_count_pairs.argtypes = [P(GsCamera), P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.gs_densify_workspace_size.argtypes = [_i32, P(C.c_size_t)]
     lib.gs_densify.argtypes = [P(GsDensifyParams), _i32, _i32, P(GsGaussianSet), _i64, P(GsGaussianSet),
                                _vp, _vp, _vp, _vp, C.c_size_t, _vp]
@@ -122,13 +116,12 @@ def load_library(path=LIB_PATH):
     lib.gs_preprocess_bwd_views.argtypes = V + [P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
     lib.gs_preprocess_bwd_adam_views.argtypes = (V + [P(GsSettings), _i32, _i32] + [_vp] * 8 + [P(GsAdamState)] +
                                                  [_vp] * 7 + [_vp])
-    lib.gs_count_pairs_views.argtypes = V + [P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp]
-    lib.gs_stream_copy.argtypes = [_vp, _vp, _i64, _vp]
+    lib.gs_count_pairs_views.argtypes = V + [P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.gs_count_nonfinite.argtypes = [_vp, _i64, _vp, _vp]
-    lib.gs_fma_loop.argtypes = [_i32, _i32, C.c_float, C.c_float, _vp, _vp]
     for name in SYMBOLS:
         if name not in ("gs_error_string",):
             getattr(lib, name).restype = C.c_int
+    lib.gs_debug_sort_wait_limit.restype = _i64
     _lib = lib
     return lib
 
@@ -231,6 +224,28 @@ def gs_bin_keys(cam, tile_ranges, point_list, depth, keys):
     _check(rc, "gs_bin_keys")
 
 
+def gs_debug_sort_wait_limit(limit=-1):
+    """Sets the radix sort's look-back wait limit for later binning calls (limit < 0:
+    leave it); returns the previous limit.  0 makes every sort report failure."""
+    return int(load_library().gs_debug_sort_wait_limit(int(limit)))
+
+
+BIN_OVERFLOW = 1     # bit 0 of the binning status word: more list entries than capacity
+BIN_SORT_FAILED = 2  # bit 1: the radix sort gave up waiting; the lists are void
+
+
+def check_bin_status(word, what="gs_bin_sort"):
+    """Reads the status word gs_bin_sort leaves in overflow_dev: raises GsError when the
+    sort failed (bit 1), returns True when the lists overflowed their capacity (bit 0)
+    and the call should be repeated with a larger one, False when the lists are valid."""
+    word = int(word)
+    if word & BIN_SORT_FAILED:
+        raise GsError(f"{what}: a radix-sort pass gave up waiting for its predecessors; the tile lists are void")
+    if word & ~(BIN_OVERFLOW | BIN_SORT_FAILED):
+        raise GsError(f"{what}: unknown status word {word:#x}")
+    return bool(word & BIN_OVERFLOW)
+
+
 def gs_render_fwd(cam, settings, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
                   tile_order=None):
     rc = load_library().gs_render_fwd(
@@ -326,51 +341,6 @@ def _adam_struct(exp_avg, exp_avg_sq, lr, step, beta1, beta2, eps):
     return st
 
 
-def gs_preprocess_bwd_adam_geom(cam, settings, sh_degree, params, tiles_touched, clamp_mask, grad2d, exp_avg,
-                                exp_avg_sq, lr, step, view_dir, beta1=0.9, beta2=0.999, eps=1e-8,
-                                densify_accum=None, densify_count=None):
-    """Geometry half of the fused tail: mean / log-scale / quaternion / opacity gradients and Adam in place,
-    densification statistic, and the view directions [n,3] the SH half needs."""
-    f32, n = torch.float32, params["means"].shape[0]
-    st = _adam_struct(exp_avg, exp_avg_sq, lr, step, beta1, beta2, eps)
-    rc = load_library().gs_preprocess_bwd_adam_geom(
-        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, sh_degree,
-        *[_p(params[k], f32, k) for k in PARAM_ORDER], _p(tiles_touched, torch.int32, "tiles_touched"),
-        _p(clamp_mask, torch.uint8, "clamp_mask"), _p(grad2d, f32, "grad2d"), C.byref(st),
-        _p(densify_accum, f32, "densify_accum"), _p(densify_count, torch.int32, "densify_count"),
-        _p(view_dir, f32, "view_dir"), _stream())
-    _check(rc, "gs_preprocess_bwd_adam_geom")
-
-
-def gs_preprocess_bwd_adam_sh(sh_degree, sh, clamp_mask, grad2d, view_dir, exp_avg, exp_avg_sq, lr, step,
-                              beta1=0.9, beta2=0.999, eps=1e-8):
-    """SH half of the fused tail: SH gradients and Adam on sh in place (exp_avg / exp_avg_sq: the sh moments)."""
-    f32 = torch.float32
-    st = _adam_struct({"sh": exp_avg}, {"sh": exp_avg_sq}, lr, step, beta1, beta2, eps)
-    rc = load_library().gs_preprocess_bwd_adam_sh(
-        sh.shape[0], sh_degree, _p(sh, f32, "sh"), _p(clamp_mask, torch.uint8, "clamp_mask"),
-        _p(grad2d, f32, "grad2d"), _p(view_dir, f32, "view_dir"), C.byref(st), _stream())
-    _check(rc, "gs_preprocess_bwd_adam_sh")
-
-
-def gs_project(cam, settings, params, splats, depth, rect, tiles_touched):
-    f32, n = torch.float32, params["means"].shape[0]
-    rc = load_library().gs_project(
-        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(params["means"], f32, "means"),
-        _p(params["log_scales"], f32, "log_scales"), _p(params["quats"], f32, "quats"),
-        _p(params["opacity_logits"], f32, "opacity_logits"), _p(splats, f32, "splats"), _p(depth, f32, "depth"),
-        _p(rect, torch.int16, "rect"), _p(tiles_touched, torch.int32, "tiles_touched"), _stream())
-    _check(rc, "gs_project")
-
-
-def gs_shade(cam, sh_degree, means, sh, splats, clamp_mask):
-    f32 = torch.float32
-    rc = load_library().gs_shade(C.byref(camera_struct(cam)), means.shape[0], sh_degree, _p(means, f32, "means"),
-                                 _p(sh, f32, "sh"), _p(splats, f32, "splats"),
-                                 _p(clamp_mask, torch.uint8, "clamp_mask"), _stream())
-    _check(rc, "gs_shade")
-
-
 def gs_image_loss(mode, pred, target, dL_dpred, loss):
     """loss: float64 CUDA tensor with at least 1 + LOSS_PARTIALS entries; loss[0] receives L."""
     m = {"l1": 1, "l2": 2}[mode] if isinstance(mode, str) else int(mode)
@@ -403,10 +373,11 @@ def gs_adam_step(groups, beta1, beta2, eps, step):
     _check(rc, "gs_adam_step")
 
 
-def gs_count_pairs(cam, settings, n, tile_ranges, point_list, splats, counts):
+def gs_count_pairs(cam, settings, n, tile_ranges, point_list, splats, counts, evaluated_px=None):
     rc = load_library().gs_count_pairs(C.byref(camera_struct(cam)), C.byref(settings.struct()), n,
                                        _p(tile_ranges, torch.int32), _p(point_list, torch.int32),
-                                       _p(splats, torch.float32), _p(counts, torch.int64), _stream())
+                                       _p(splats, torch.float32), _p(counts, torch.int64),
+                                       _p(evaluated_px, torch.int32, "evaluated_px"), _stream())
     _check(rc, "gs_count_pairs")
 
 
@@ -429,24 +400,6 @@ def check_finite(tensors):
             bad.append(f"{name} ({c} of {t.numel()})")
     if bad:
         raise GsError("non-finite values in " + ", ".join(bad))
-
-
-def gs_stream_copy(src, dst):
-    """dst <- src (float32, numel a multiple of 4) with the library's 16-byte non-temporal copy kernel."""
-    if src.numel() != dst.numel():
-        raise GsError("gs_stream_copy: src and dst differ in size")
-    _check(load_library().gs_stream_copy(_p(src, torch.float32, "src"), _p(dst, torch.float32, "dst"), src.numel(),
-                                         _stream()), "gs_stream_copy")
-
-
-FMA_LOOP_THREADS, FMA_LOOP_FLOPS_PER_ITER = 256, 128
-
-
-def gs_fma_loop(blocks, iters, a, b, out):
-    """The fp32 FMA loop kernel: blocks * 256 * iters * 128 flops; out holds blocks * 256 floats."""
-    if out.numel() < blocks * FMA_LOOP_THREADS:
-        raise GsError("gs_fma_loop: out holds fewer than blocks * 256 floats")
-    _check(load_library().gs_fma_loop(blocks, iters, a, b, _p(out, torch.float32, "out"), _stream()), "gs_fma_loop")
 
 
 @dataclass
@@ -672,11 +625,12 @@ def gs_preprocess_bwd_adam_views(cams, settings, sh_degree, params, tiles_touche
     _check(rc, "gs_preprocess_bwd_adam_views")
 
 
-def gs_count_pairs_views(cams, settings, n, tile_ranges, point_list, splats, counts):
+def gs_count_pairs_views(cams, settings, n, tile_ranges, point_list, splats, counts, evaluated_px=None):
     arr, v = camera_array(cams)
     rc = load_library().gs_count_pairs_views(arr, v, C.byref(settings.struct()), n, _p(tile_ranges, torch.int32),
                                              _p(point_list, torch.int32), _p(splats, torch.float32),
-                                             _p(counts, torch.int64), _stream())
+                                             _p(counts, torch.int64), _p(evaluated_px, torch.int32, "evaluated_px"),
+                                             _stream())
     _check(rc, "gs_count_pairs_views")
 
 
@@ -692,7 +646,9 @@ class Rasterizer:
     The number of (tile, Gaussian) pairs K is data dependent: the list buffer has
     `key_capacity` entries and binning raises a device flag when K exceeds it.
     `forward(check=True)` synchronises once, grows the capacity and re-bins when
-    that happened; with check=False nothing synchronises.
+    that happened, and raises GsError when binning reports a failed sort; with
+    check=False nothing synchronises (check_bin_status(r.overflow.item()) does
+    the same check later).
     debug=True checks the parameters before the forward, and the image and the
     gradients after each pass, for NaN and infinite values (gs_count_nonfinite),
     raising GsError with the names of the tensors that hold them.
@@ -722,6 +678,7 @@ class Rasterizer:
         self.final_T = torch.empty((H, W), dtype=torch.float32, device=dev)
         self.n_contrib = torch.empty((H, W), dtype=torch.int32, device=dev)
         self.grad2d = torch.empty((n, GRAD2D_STRIDE), dtype=torch.float32, device=dev)
+        self.generation = 0  # forward passes run so far; the autograd wrapper checks it
         self._alloc_lists(key_capacity if key_capacity is not None else max(4 * n, 1 << 16))
 
     def _alloc_lists(self, cap):
@@ -756,13 +713,15 @@ class Rasterizer:
     def forward(self, p, check=True):
         if self.debug:
             check_finite({k: p[k] for k in PARAM_ORDER})
+        self.generation += 1
         self.preprocess(p)
         self.bin()
-        if check and int(self.overflow.item()) != 0:
+        if check and check_bin_status(self.overflow.item()):
             K = int(self.num_keys.item())
             self._alloc_lists(int(K * 1.25) + 1024)
             self.bin()
-            assert int(self.overflow.item()) == 0
+            if check_bin_status(self.overflow.item()):
+                raise GsError("gs_bin_sort overflowed a capacity of 1.25 K")
         self.render()
         if self.debug:
             check_finite({"image": self.image, "final_T": self.final_T})
@@ -785,14 +744,22 @@ class Rasterizer:
             check_finite({"dL_dimage": dL_dimage, "grad2d": self.grad2d, **{"d" + k: v for k, v in out.items()}})
         return out
 
-    def count_pairs(self):
+    def count_pairs(self, per_pixel=False):
+        """Device int64 [3]: evaluated, walked and blended pairs; with per_pixel also the [H, W]
+        int32 evaluated count of each pixel."""
         c = torch.zeros(3, dtype=torch.int64, device=self.device)
-        gs_count_pairs(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, c)
-        return c
+        ev = torch.empty_like(self.n_contrib) if per_pixel else None
+        gs_count_pairs(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, c, ev)
+        return (c, ev) if per_pixel else c
 
 
 class RasterizeFunction(torch.autograd.Function):
-    """image = rasterize(means, log_scales, quats, opacity_logits, sh) for one Rasterizer."""
+    """image = rasterize(means, log_scales, quats, opacity_logits, sh) for one Rasterizer.
+
+    The backward reuses the forward's intermediates (lists, ranges, final_T,
+    n_contrib, flags), which the Rasterizer keeps in its own buffers: one
+    backward per forward, before the Rasterizer renders again.  A backward after
+    a newer forward on the same Rasterizer raises GsError."""
 
     @staticmethod
     def forward(ctx, rast, means, log_scales, quats, opacity_logits, sh):
@@ -800,11 +767,15 @@ class RasterizeFunction(torch.autograd.Function):
                  opacity_logits=opacity_logits.contiguous(), sh=sh.contiguous())
         img = rast.forward(p).clone()
         ctx.rast = rast
+        ctx.generation = rast.generation
         ctx.save_for_backward(p["means"], p["log_scales"], p["quats"], p["opacity_logits"], p["sh"])
         return img
 
     @staticmethod
     def backward(ctx, dL_dimage):
+        if ctx.rast.generation != ctx.generation:
+            raise GsError("rasterize: the Rasterizer ran another forward pass since this one; its buffers no "
+                          "longer hold this pass's intermediates (use one Rasterizer per pending backward)")
         m, s, q, o, c = ctx.saved_tensors
         p = dict(means=m, log_scales=s, quats=q, opacity_logits=o, sh=c)
         g = ctx.rast.backward(p, dL_dimage.contiguous())
@@ -881,11 +852,12 @@ class RasterizerViews:
     def forward(self, p, check=True):
         self.preprocess(p)
         self.bin()
-        if check and int(self.overflow.item()) != 0:
+        if check and check_bin_status(self.overflow.item(), "gs_bin_sort_views"):
             K = int(self.num_keys.item())
             self._alloc_lists(int(K * 1.25) + 1024)
             self.bin()
-            assert int(self.overflow.item()) == 0
+            if check_bin_status(self.overflow.item(), "gs_bin_sort_views"):
+                raise GsError("gs_bin_sort_views overflowed a capacity of 1.25 K")
         self.render()
         return self.image
 
@@ -908,3 +880,89 @@ class RasterizerViews:
         c = torch.zeros(3, dtype=torch.int64, device=self.device)
         gs_count_pairs_views(self.cams, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, c)
         return c
+
+
+class Trainer:
+    """The training loop of one view over the library's calls ([P4] E.1): each
+    iteration renders with the image loss fused into the forward, back-propagates,
+    and takes the fused 2D->3D backward + densification statistic + Adam step
+    (bias-corrected at the iteration count); every `densify_interval` iterations
+    the Gaussians are densified and pruned (N changes: the Rasterizer is rebuilt
+    for the new count, the Adam moments follow their rows, the statistic
+    restarts), and every `reset_interval` iterations every opacity is scaled by
+    `reset_factor` (the opacity's moments restart).
+
+    Plumbing only: buffers and the order of the calls.  params: dict of device
+    tensors (updated in place between densifications, replaced at them)."""
+
+    def __init__(self, cam, params, sh_degree, target, lr, densify=None, densify_interval=100,
+                 reset_interval=3000, reset_factor=OPACITY_RESET_FACTOR, loss="l1", settings=None):
+        self.cam, self.deg, self.lr = cam, int(sh_degree), dict(lr)
+        self.target, self.loss_mode = target, loss
+        self.densify_params = densify
+        self.densify_interval, self.reset_interval, self.reset_factor = densify_interval, reset_interval, reset_factor
+        self.settings = settings or Settings()
+        self.p = {k: params[k].contiguous() for k in PARAM_ORDER}
+        self.m = {k: torch.zeros_like(v) for k, v in self.p.items()}
+        self.v = {k: torch.zeros_like(v) for k, v in self.p.items()}
+        self.t = 0
+        self.events = []  # (iteration, "densify" | "reset", detail)
+        self._rebuild()
+
+    @property
+    def n(self):
+        return self.p["means"].shape[0]
+
+    def _rebuild(self):
+        dev = self.p["means"].device
+        self.rast = Rasterizer(self.cam, self.n, self.deg, settings=self.settings, device=dev)
+        self.accum = torch.zeros(self.n, dtype=torch.float32, device=dev)
+        self.count = torch.zeros(self.n, dtype=torch.int32, device=dev)
+        self.dL = torch.empty_like(self.target)
+        self.loss = torch.zeros(1 + self.rast.ntiles, dtype=torch.float64, device=dev)
+        self._sized = False
+
+    def step(self, dL_hook=None, grads=None, after_update=None):
+        """One iteration.  dL_hook(dL), if given, sees (and may change in place) the loss gradient
+        the forward wrote before the backward reads it; grads (dict of tensors shaped like the
+        parameters) receives the iteration's 3D gradients; after_update(self) runs after the Adam
+        update and before densification and the opacity reset."""
+        r = self.rast
+        r.generation += 1
+        r.preprocess(self.p)
+        r.bin()
+        if not self._sized or dL_hook is not None:  # size the lists on the first pass after a rebuild
+            if check_bin_status(r.overflow.item()):
+                r._alloc_lists(int(int(r.num_keys.item()) * 1.25) + 1024)
+                r.bin()
+                if check_bin_status(r.overflow.item()):
+                    raise GsError("gs_bin_sort overflowed a capacity of 1.25 K")
+            self._sized = True
+        r.render_loss(self.target, self.loss_mode, self.dL, self.loss, clear_grad2d=True)
+        if dL_hook is not None:
+            dL_hook(self.dL)
+        r.backward_2d(self.dL, accumulate=True)
+        self.t += 1
+        gs_preprocess_bwd_adam(self.cam, self.settings, self.deg, self.p, r.tiles_touched, r.clamp, r.grad2d, self.m,
+                               self.v, self.lr, self.t, densify_accum=self.accum, densify_count=self.count,
+                               grads=grads)
+        if after_update is not None:
+            after_update(self)
+        if self.densify_params is not None and self.densify_interval and self.t % self.densify_interval == 0:
+            self.densify()
+        if self.reset_interval and self.t % self.reset_interval == 0:
+            self.reset_opacity()
+
+    def densify(self):
+        n0 = self.n
+        p, ea, eq, _, _, action = densify_and_prune(self.densify_params, self.deg, self.p, self.accum, self.count,
+                                                    self.m, self.v)
+        self.p, self.m, self.v = ({k: t.contiguous() for k, t in d.items()} for d in (p, ea, eq))
+        self.last_action = action
+        self.events.append((self.t, "densify", (n0, self.n)))
+        self._rebuild()
+
+    def reset_opacity(self):
+        gs_opacity_reset(self.p["opacity_logits"], self.reset_factor, self.m["opacity_logits"],
+                         self.v["opacity_logits"])
+        self.events.append((self.t, "reset", self.reset_factor))

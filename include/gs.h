@@ -114,23 +114,6 @@ int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32_t n, int32
                   float* splats, float* depth, int16_t* rect, int32_t* tiles_touched,
                   uint8_t* clamp_mask, void* stream);
 
-/*
- * gs_project and gs_shade -- the two halves of gs_preprocess, for callers that
- * run the SH colour on another stream while the geometry goes on to binning.
- * gs_project writes rows 0-1 of each splat record (mean, conic factor,
- * opacity), depth, rect and tiles_touched exactly as gs_preprocess does, and
- * leaves row 2 and the clamp mask alone.  gs_shade writes row 2 (r, g, b, 0)
- * and clamp_mask for every Gaussian, culled or not (the colour of a culled
- * Gaussian is computed but never read); for a visible Gaussian both equal
- * gs_preprocess's bit for bit.  Writes of the two calls touch disjoint bytes.
- */
-int gs_project(const gs_camera* cam, const gs_settings* set, int32_t n,
-               const float* means, const float* log_scales, const float* quats,
-               const float* opacity_logits, float* splats, float* depth, int16_t* rect,
-               int32_t* tiles_touched, void* stream);
-int gs_shade(const gs_camera* cam, int32_t n, int32_t sh_degree, const float* means, const float* sh,
-             float* splats, uint8_t* clamp_mask, void* stream);
-
 /* Bytes of workspace gs_bin_sort needs for n Gaussians and key_capacity list
    entries. */
 int gs_bin_workspace_size(int32_t n, const gs_camera* cam, int64_t key_capacity, size_t* bytes);
@@ -145,17 +128,37 @@ int gs_bin_workspace_size(int32_t n, const gs_camera* cam, int64_t key_capacity,
  * holds the lists tile after tile; tile_ranges [tiles, 2] uint32 holds each
  * tile's [begin, end) in point_list ([0, 0) when empty).
  * num_keys_dev [1] uint32 receives K = sum of tiles_touched (device memory; the
- * call does not read it back).  If K > key_capacity, *overflow_dev is set to 1,
- * every range is written empty and point_list holds no valid list: the caller
- * checks overflow_dev after its next synchronisation and retries with a larger
- * capacity.  Otherwise *overflow_dev = 0.
+ * call does not read it back).  *overflow_dev [1] uint32 receives a status word:
+ *   0      the lists and ranges are valid;
+ *   bit 0  K > key_capacity: retry with a capacity of at least K;
+ *   bit 1  a pass of the radix sort gave up waiting for the partitions before
+ *          it (see gs_debug_sort_wait_limit; not expected in normal operation):
+ *          the sort is void and a retry may succeed.
+ * When the word is not 0, every range is written empty and point_list holds no
+ * valid list.  The caller checks the word after its next synchronisation.
  * workspace: device scratch of at least gs_bin_workspace_size() bytes, 256-byte
  * aligned; its contents on entry do not matter.
+ * Limits: GS_ECAPACITY when the image has more than 65536 tiles (the tile sort
+ * takes two 8-bit digit passes; 65536 tiles is 4096 x 4096 pixels) or when
+ * key_capacity or n exceeds 2^30 - 1.
  */
 int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, const int16_t* rect,
                 const int32_t* tiles_touched, int64_t key_capacity,
                 uint32_t* point_list, uint32_t* tile_ranges, uint32_t* num_keys_dev,
                 uint32_t* overflow_dev, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gs_debug_sort_wait_limit -- test hook for the sort's failure report.  Each
+ * radix-sort pass (an LSD "onesweep" pass: partitions add their digit counts to
+ * a running prefix published by the partitions before them) waits a bounded
+ * number of times for a predecessor's prefix; past the limit the partition
+ * gives up and the call reports bit 1 in *overflow_dev.  Sets the limit for
+ * later gs_bin_sort calls in this process (limit < 0: leave it) and returns
+ * the previous one.  Default 4194304 waits; 0 makes every partition but the
+ * first give up at once, so a sort deterministically reports failure while
+ * every kernel still runs to completion.
+ */
+int64_t gs_debug_sort_wait_limit(int64_t limit);
 
 /* Diagnostic: the 64-bit sort keys (tile << 32 | float32 depth bits) of the
    sorted list, keys [key_capacity]; entries at and beyond K are left alone. */
@@ -323,32 +326,6 @@ int gs_preprocess_bwd_adam(const gs_camera* cam, const gs_settings* set, int32_t
                            float* dsh, void* stream);
 
 /*
- * gs_preprocess_bwd_adam_geom and gs_preprocess_bwd_adam_sh -- the two halves
- * of gs_preprocess_bwd_adam (without the optional gradient outputs), for
- * callers that move the SH update off the critical path: the SH coefficients
- * are needed again only by the next step's colour pass, not by its projection
- * and binning.
- * _geom: the mean / log-scale / quaternion / opacity gradients (the mean's
- * includes the view-direction term, which reads sh), their Adam step in place,
- * the densification statistic, and view_dir [n,3] float32: each Gaussian's
- * unit camera-to-mean direction (0 for Gaussians with tiles_touched == 0).
- * _sh: the SH gradients from view_dir, the clamp mask and grad2d, and their
- * Adam step on sh in place (moments exp_avg[4], exp_avg_sq[4], lr[4], lr[5]).
- * Ordering the caller keeps: _sh after _geom (it reads view_dir and _geom
- * reads sh), and before anything that rewrites grad2d, clamp_mask or
- * view_dir, or reads sh.  Together they give gs_preprocess_bwd_adam's result
- * bit for bit.
- */
-int gs_preprocess_bwd_adam_geom(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
-                                float* means, float* log_scales, float* quats, float* opacity_logits,
-                                const float* sh, const int32_t* tiles_touched, const uint8_t* clamp_mask,
-                                const float* grad2d, const gs_adam_state* adam, float* densify_accum,
-                                int32_t* densify_count, float* view_dir, void* stream);
-int gs_preprocess_bwd_adam_sh(int32_t n, int32_t sh_degree, float* sh, const uint8_t* clamp_mask,
-                              const float* grad2d, const float* view_dir, const gs_adam_state* adam,
-                              void* stream);
-
-/*
  * Densification, pruning and opacity reset ([P4] D.1: Gaussians whose
  * accumulated position gradient is large are densified, a split replacing one
  * Gaussian by two smaller ones; D.2: split along the long axis when Sigma is
@@ -427,10 +404,13 @@ int gs_opacity_reset(int32_t n, float factor, float* opacity_logits, float* exp_
  * gs_count_pairs -- diagnostic pair counts of a forward pass (device int64
  * counters, overwritten): counts[0] = evaluated pairs (entries walked by the
  * forward up to and including the one that stops a pixel), counts[1] = sum of
- * n_contrib (entries walked by the backward), counts[2] = blended pairs.
+ * n_contrib (entries walked by the backward, [P3] section 3: the reverse walk
+ * starts at the last contributor), counts[2] = blended pairs.  evaluated_px
+ * [H, W] int32 (optional, NULL to skip): each pixel's share of counts[0].
  */
 int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
-                   const uint32_t* point_list, const float* splats, int64_t* counts, void* stream);
+                   const uint32_t* point_list, const float* splats, int64_t* counts, int32_t* evaluated_px,
+                   void* stream);
 
 /*
  * gs_count_nonfinite -- *out (device int64, overwritten) = the number of NaN
@@ -442,24 +422,6 @@ int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, cons
  * reaches the image.
  */
 int gs_count_nonfinite(const float* x, int64_t count, int64_t* out, void* stream);
-
-/*
- * Measurement helpers.  They compute nothing of the method: a benchmark times
- * them to quote the rates this GPU delivers beside its published peaks.
- *
- * gs_stream_copy -- dst[i] = src[i] for i < count (float32, count a multiple
- * of 4, both arrays 16-byte aligned, not overlapping), read and written with
- * non-temporal 16-byte accesses: 8 count bytes of HBM traffic.
- *
- * gs_fma_loop -- `blocks` blocks of 256 lanes, each running 8 independent
- * chains f <- f a + b (fp32 FMA), 8 steps of each chain per iteration for
- * `iters` iterations, then writing the sum of its chains to
- * out[block * 256 + lane] (out holds blocks * 256 floats):
- * blocks * 256 * iters * 128 flops.  With a = 1, b = 0 each lane writes
- * 8 lane + 28 exactly.
- */
-int gs_stream_copy(const float* src, float* dst, int64_t count, void* stream);
-int gs_fma_loop(int32_t blocks, int32_t iters, float a, float b, float* out, void* stream);
 
 /*
  * Batched views ([P4] E.1 steps 1-3: an iteration renders a batch of views,
@@ -519,7 +481,7 @@ int gs_preprocess_bwd_adam_views(const gs_camera* cams, int32_t views, const gs_
                                  float* dquats, float* dopacity_logits, float* dsh, void* stream);
 int gs_count_pairs_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                          const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
-                         int64_t* counts, void* stream);
+                         int64_t* counts, int32_t* evaluated_px /* [views, H, W] or NULL */, void* stream);
 
 #ifdef __cplusplus
 }

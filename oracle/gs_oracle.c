@@ -415,7 +415,8 @@ static int walk_pixel(const orc_settings* set, double px, double py, const int* 
 }
 
 /* counts[0] = P_fwd (evaluated pairs), counts[1] = sum of n_contrib (walked by
-   the backward), counts[2] = blended pairs.  With tile_mask != NULL only the
+   the backward), counts[2] = blended pairs; evaluated_px (optional, [H, W])
+   receives each pixel's share of counts[0].  With tile_mask != NULL only the
    pixels of tiles whose mask byte is non-zero are composited (the others are
    left untouched); the backward then equals the full backward for an upstream
    gradient that is zero outside those tiles. */
@@ -424,7 +425,7 @@ int orc_render_fwd(const orc_camera* cam, const orc_settings* set, int global_li
                    const double* uv, const double* conic, const double* opacity, const double* rgb,
                    double* image, double* final_T, int* n_contrib, double* wsum,
                    unsigned char* ambiguous, double amb_rel, uint64_t* decision_hash, int64_t* counts,
-                   const unsigned char* tile_mask)
+                   const unsigned char* tile_mask, int64_t* evaluated_px)
 {
     const int W = cam->width, H = cam->height, ts = set->tile;
     const int tx = (W + ts - 1) / ts;
@@ -447,6 +448,7 @@ int orc_render_fwd(const orc_camera* cam, const orc_settings* set, int global_li
             if (wsum) wsum[p] = ws;
             if (ambiguous) ambiguous[p] = (unsigned char)amb;
             if (decision_hash) decision_hash[p] = h;
+            if (evaluated_px) evaluated_px[p] = ev;
             counts[0] += ev;
             counts[1] += nc;
             counts[2] += nb;
@@ -468,7 +470,7 @@ int orc_render_bwd(const orc_camera* cam, const orc_settings* set, int global_li
                    const int* point_list, const int64_t* ranges,
                    const double* uv, const double* conic, const double* opacity, const double* rgb,
                    const double* dL_dimage, double* dL_dxy, double* dL_dconic, double* dL_dopacity,
-                   double* dL_drgb, int N, const unsigned char* tile_mask)
+                   double* dL_drgb, int N, const unsigned char* tile_mask, double* abs_sum)
 {
     const int W = cam->width, H = cam->height, ts = set->tile;
     const int tx = (W + ts - 1) / ts;
@@ -476,6 +478,7 @@ int orc_render_bwd(const orc_camera* cam, const orc_settings* set, int global_li
     memset(dL_dconic, 0, sizeof(double) * 3 * (size_t)N);
     memset(dL_dopacity, 0, sizeof(double) * (size_t)N);
     memset(dL_drgb, 0, sizeof(double) * 3 * (size_t)N);
+    if (abs_sum) memset(abs_sum, 0, sizeof(double) * 9 * (size_t)N);
     int64_t maxlen = 0;
     if (global_list) maxlen = ranges[1] - ranges[0];
     else {
@@ -501,12 +504,15 @@ int orc_render_bwd(const orc_camera* cam, const orc_settings* set, int global_li
                 const orc_blend* s = &st[k];
                 int g = s->idx;
                 const double* c = rgb + 3 * g;
-                double dalpha = 0;
+                double dalpha = 0, adalpha = 0;
                 for (int ch = 0; ch < 3; ++ch) {
                     dL_drgb[3 * g + ch] += s->T * s->alpha * gp[ch];
                     dalpha += gp[ch] * (c[ch] - Cn[ch]);
+                    adalpha += fabs(gp[ch]) * (fabs(c[ch]) + fabs(Cn[ch]));
+                    if (abs_sum) abs_sum[9 * g + 6 + ch] += fabs(s->T * s->alpha * gp[ch]);
                 }
                 dalpha *= s->T;
+                adalpha *= s->T;
                 for (int ch = 0; ch < 3; ++ch) Cn[ch] = s->alpha * c[ch] + (1.0 - s->alpha) * Cn[ch];
                 if (s->clamped) continue;          /* alpha = alpha_max: no dependence on sigma or G */
                 dL_dopacity[g] += s->G * dalpha;
@@ -519,6 +525,18 @@ int orc_render_bwd(const orc_camera* cam, const orc_settings* set, int global_li
                 /* d = pixel - mean: d power / d mean = (A dx + B dy, B dx + C dy) */
                 dL_dxy[2 * g]     += (A * s->dx + B * s->dy) * dpow;
                 dL_dxy[2 * g + 1] += (B * s->dx + Cc * s->dy) * dpow;
+                if (abs_sum) {
+                    /* the size of each term added above, from |dL/dalpha|'s own terms: a
+                       scale for the rounding a float32 evaluation of the same sums carries */
+                    const double ap = s->G * opacity[g] * adalpha;  /* |dpow| from |dL/dalpha| */
+                    double* a = abs_sum + 9 * g;
+                    a[0] += (fabs(A * s->dx) + fabs(B * s->dy)) * ap;
+                    a[1] += (fabs(B * s->dx) + fabs(Cc * s->dy)) * ap;
+                    a[2] += 0.5 * s->dx * s->dx * ap;
+                    a[3] += fabs(s->dx * s->dy) * ap;
+                    a[4] += 0.5 * s->dy * s->dy * ap;
+                    a[5] += s->G * adalpha;
+                }
             }
         }
     free(st);

@@ -168,28 +168,36 @@ def render_fwd(cam, pre, point_list, ranges, s: Settings = None, brute=False, am
     W, H = cam.width, cam.height
     out = dict(image=np.zeros((3, H, W)), final_T=np.zeros((H, W)), n_contrib=np.zeros((H, W), np.int32),
                wsum=np.zeros((H, W)), ambiguous=np.zeros((H, W), np.uint8), hash=np.zeros((H, W), np.uint64),
-               counts=np.zeros(3, np.int64))
+               counts=np.zeros(3, np.int64), evaluated=np.zeros((H, W), np.int64))
     pl = np.ascontiguousarray(point_list, dtype=np.int32)
     rg = np.ascontiguousarray(ranges, dtype=np.int64)
     lib().orc_render_fwd(C.byref(cam_struct(cam)), C.byref(set_struct(s)), C.c_int(1 if brute else 0),
                          _p(pl, C.c_int), _p(rg, C.c_int64), _p(_d(pre["uv"])), _p(_d(pre["conic"])),
                          _p(_d(pre["opacity"])), _p(_d(pre["rgb"])), _p(out["image"]), _p(out["final_T"]),
                          _p(out["n_contrib"], C.c_int), _p(out["wsum"]), _p(out["ambiguous"], C.c_uint8),
-                         C.c_double(amb_rel), _p(out["hash"], C.c_uint64), _p(out["counts"], C.c_int64), tmp)
+                         C.c_double(amb_rel), _p(out["hash"], C.c_uint64), _p(out["counts"], C.c_int64), tmp,
+                         _p(out["evaluated"], C.c_int64))
     return out
 
 
-def render_bwd(cam, pre, point_list, ranges, dL_dimage, s: Settings = None, brute=False, tile_mask=None):
+def render_bwd(cam, pre, point_list, ranges, dL_dimage, s: Settings = None, brute=False, tile_mask=None,
+               with_abs=False):
+    """2D gradients; with_abs also returns abs [N, 9]: per Gaussian and component (du, dv, dA, dB,
+    dC, dopacity, dr, dg, db) the sum of the absolute sizes of the terms added, a scale for the
+    rounding error of a float32 evaluation of the same sums."""
     s = s or Settings()
     tm, tmp = _tmask(tile_mask)
     N = pre["uv"].shape[0]
     out = dict(dxy=np.zeros((N, 2)), dconic=np.zeros((N, 3)), dopacity=np.zeros(N), drgb=np.zeros((N, 3)))
+    if with_abs:
+        out["abs"] = np.zeros((N, 9))
     pl = np.ascontiguousarray(point_list, dtype=np.int32)
     rg = np.ascontiguousarray(ranges, dtype=np.int64)
     lib().orc_render_bwd(C.byref(cam_struct(cam)), C.byref(set_struct(s)), C.c_int(1 if brute else 0),
                          _p(pl, C.c_int), _p(rg, C.c_int64), _p(_d(pre["uv"])), _p(_d(pre["conic"])),
                          _p(_d(pre["opacity"])), _p(_d(pre["rgb"])), _p(_d(dL_dimage)),
-                         _p(out["dxy"]), _p(out["dconic"]), _p(out["dopacity"]), _p(out["drgb"]), C.c_int(N), tmp)
+                         _p(out["dxy"]), _p(out["dconic"]), _p(out["dopacity"]), _p(out["drgb"]), C.c_int(N), tmp,
+                         _p(out["abs"]) if with_abs else None)
     return out
 
 

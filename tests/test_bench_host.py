@@ -36,6 +36,13 @@ def test_workloads_are_the_scene_generators():
 PEAKS = dict(hbm_gbs=dict(measured=4000.0), fp32_tflops=dict(measured=100.0))
 
 
+def test_blend_flops_use_the_scope_figures():
+    """20 flops per evaluated forward pair; 72 per walked backward pair that blends, 16 per one that does not."""
+    f, b = bench.blend_flops(1000, 600, 200)
+    assert f == 20 * 1000
+    assert b == 72 * 200 + 16 * 400
+
+
 def test_raster_roofline_fraction_is_bound_over_time():
     r = bench.raster_roofline(1_000_000, 5e6, 3, 3e8, 3e8, 1e8, 1.0, PEAKS)
     # the fraction is the summed stage bounds over the measured time

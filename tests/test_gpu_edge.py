@@ -256,112 +256,23 @@ def test_fused_forward_loss_matches_separate_calls(mode):
         assert float(dl_b[:, :5, :5].abs().max()) == 0.0
 
 
-def test_split_preprocess_matches_combined():
-    """gs_project + gs_shade == gs_preprocess: geometry for every Gaussian, colour and clamp mask for
-    the visible ones, bit for bit."""
-    import torch
-    gs = _gs()
-    sc = scenes.random_small(36, n=1500, width=96, height=72, sh_degree=3, scale_mu=-2.4)
-    p = to_dev(sc.params())
-    r = gs.Rasterizer(sc.cam, sc.n, 3)
-    r.preprocess(p)
-    ref = {k: getattr(r, k).clone() for k in ("splats", "depth", "rect", "tiles_touched", "clamp")}
-    r.splats.fill_(-1.0)
-    r.clamp.fill_(255)
-    gs.gs_shade(r.cam, 3, p["means"], p["sh"], r.splats, r.clamp)
-    gs.gs_project(r.cam, r.settings, p, r.splats, r.depth, r.rect, r.tiles_touched)
-    torch.cuda.synchronize()
-    vis = ref["tiles_touched"] > 0
-    assert int(vis.sum()) > 100
-    for k in ("depth", "rect", "tiles_touched"):
-        assert torch.equal(getattr(r, k), ref[k]), k
-    assert torch.equal(r.splats[:, :8], ref["splats"][:, :8])
-    assert torch.equal(r.splats[vis], ref["splats"][vis])
-    assert torch.equal(r.clamp[vis], ref["clamp"][vis])
-
-
-def test_split_tail_matches_fused():
-    """gs_preprocess_bwd_adam_geom + gs_preprocess_bwd_adam_sh == gs_preprocess_bwd_adam from the same
-    state and 2D gradients: parameters, moments and densification statistic bit for bit."""
-    import torch
-    gs = _gs()
-    sc = scenes.random_small(37, n=1300, width=96, height=72, sh_degree=3, scale_mu=-2.4)
-    N = sc.n
-    lr = scenes.ADAM_LR
-    p0 = to_dev(sc.params())
-    r = gs.Rasterizer(sc.cam, N, 3)
-    r.forward(p0)
-    r.backward_2d(torch.from_numpy(sc.dL_dimage).cuda())
-    rng = np.random.default_rng(8)
-    m0 = {k: torch.from_numpy(rng.normal(0, 1e-3, v.shape).astype(np.float32)).cuda() for k, v in p0.items()}
-    v0 = {k: torch.from_numpy(rng.uniform(0, 1e-6, v.shape).astype(np.float32)).cuda() for k, v in p0.items()}
-    out = []
-    for split in (False, True):
-        p = {k: v.clone() for k, v in p0.items()}
-        m = {k: v.clone() for k, v in m0.items()}
-        v = {k: x.clone() for k, x in v0.items()}
-        acc = torch.zeros(N, device="cuda")
-        cnt = torch.zeros(N, dtype=torch.int32, device="cuda")
-        if split:
-            vd = torch.full((N, 3), float("nan"), device="cuda")
-            gs.gs_preprocess_bwd_adam_geom(r.cam, r.settings, 3, p, r.tiles_touched, r.clamp, r.grad2d, m, v, lr,
-                                           3, vd, densify_accum=acc, densify_count=cnt)
-            gs.gs_preprocess_bwd_adam_sh(3, p["sh"], r.clamp, r.grad2d, vd, m["sh"], v["sh"], lr, 3)
-            assert not torch.isnan(vd).any()
-        else:
-            gs.gs_preprocess_bwd_adam(r.cam, r.settings, 3, p, r.tiles_touched, r.clamp, r.grad2d, m, v, lr, 3,
-                                      densify_accum=acc, densify_count=cnt)
-        out.append((p, m, v, acc, cnt))
-    torch.cuda.synchronize()
-    (pa, ma, va, aa, ca), (pb, mb, vb, ab, cb) = out
-    for k in pa:
-        assert torch.equal(pa[k], pb[k]), k
-        assert torch.equal(ma[k], mb[k]), k
-        assert torch.equal(va[k], vb[k]), k
-    assert torch.equal(aa, ab) and torch.equal(ca, cb)
-
-
-def test_two_stream_steps_match_one_stream():
-    """Training steps with the SH work on a second stream compute what the single-stream steps compute
-    (up to the order of the backward's atomic additions)."""
-    import sys
-    import torch
-    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
-    import bench
-    sc = scenes.random_small(38, n=3000, width=160, height=96, sh_degree=3, scale_mu=-2.4)
-    sc.target = np.random.default_rng(4).uniform(0, 1, (3, 96, 160)).astype(np.float32)
-    res = []
-    for overlap in ("none", "color", "sh"):
-        st = bench.Step(sc, overlap=overlap)
-        st.run(check=True)
-        for _ in range(3):
-            st.run()
-        st.finish()
-        torch.cuda.synchronize()
-        res.append({k: v.cpu().numpy() for k, v in st.p.items()})
-    for other in res[1:]:
-        for k in res[0]:
-            p0 = np.asarray(sc.params()[k])
-            e = rel_l2(other[k], res[0][k])           # the parameters
-            d = rel_l2(other[k] - p0, res[0][k] - p0)  # the updates (Adam may flip the sign of a near-zero gradient)
-            assert e < 1e-5 and d < 2e-2, (k, e, d)
-
-
-def test_bench_scene_mode(capsys):
-    """bench.py --workload on the smallest scene: one JSON line with the metric's fields, the stage times of
-    the five rasterizer stages, pair counts that order as they must, and the stage roofline."""
-    import json
+def test_bench_scene_mode():
+    """bench.py's rasterizer line on the smallest scene: the metric's fields, the stage times of the five
+    rasterizer stages, pair counts that order as they must, the stage roofline and the dominant kernel's."""
     import sys
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     import bench
-    bench.rasterizer_workload("tiny", 3, 1)
-    d = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
-    assert d["n_gpus"] == 1 and d["higher_is_better"] and d["value"] > 0
+    peaks = dict(hbm_gbs=dict(spec=8000.0, measured=5000.0), fp32_tflops=dict(spec=157.3, measured=110.0))
+    d, sc = bench.raster_line("tiny", 3, 1, peaks)
+    assert d["n_gpus"] == 1 and d["higher_is_better"] and d["value"] > 0 and d["ms_per_step"] > 0
     assert list(d["stage_ms"]) == ["preprocess", "bin_sort", "render_fwd", "render_bwd", "preprocess_bwd"]
     assert all(v > 0 for v in d["stage_ms"].values())
     p = d["pairs"]
     assert p["fwd_evaluated"] >= p["blended"] > 0 and p["bwd_walked"] >= p["blended"] and p["keys"] > 0
-    assert 0 < d["roofline"]["frac"] < 1 and d["config"]["gaussians"] == 256
+    assert 0 < d["stage_roofline"]["frac"] < 1 and d["config"]["gaussians"] == 256
+    rf = d["roofline"]
+    assert rf["bound"] == "alu" and rf["kernel"] in ("render_fwd", "render_bwd") and 0 < rf["frac"] < 1
+    assert rf["achieved"] == pytest.approx(rf["flops_per_launch"] / (rf["launch_ms"] * 1e-3) / 1e12, rel=1e-2)
 
 
 def test_backward_accumulate():
@@ -503,7 +414,7 @@ def test_measurement_kernels():
     what their header says: an exact copy, and with a = 1, b = 0 each lane's sum of
     its eight untouched chain seeds, 8 lane + 28."""
     import torch
-    gs = _gs()
+    from differentiable_gaussian_splatting_dgs_amd import measure as gs
     n = (1 << 20) + 36  # several grid strides plus a ragged tail of float4s
     src = torch.arange(n, dtype=torch.float32, device="cuda") * 0.5 - 7.0
     dst = torch.full_like(src, float("nan"))
@@ -590,3 +501,65 @@ def test_determinism():
     for k in PARAM_KEYS:
         assert rel_l2(a["g3"][k].cpu().numpy(), b["g3"][k].cpu().numpy()) <= 1e-6, k
     log("determinism ok")
+
+
+def test_sort_failure_is_reported():
+    """With the look-back wait limit at 0 every sort partition after the first gives up at once:
+    each kernel still runs to completion, the status word reports bit 1, every range is empty and
+    the Rasterizer raises.  With the default limit restored the same call bins correctly again."""
+    import torch
+    gs = _gs()
+    sc = scenes.random_small(70, n=20000, width=320, height=240, f=200.0, sh_degree=1, scale_mu=-3.0)
+    p = to_dev(sc.params())
+    r = gs.Rasterizer(sc.cam, sc.n, 1)
+    r.forward(p, check=True)
+    torch.cuda.synchronize()
+    K = int(r.num_keys.item())
+    ref_pl, ref_rg = r.point_list[:K].clone(), r.tile_ranges.clone()
+    assert K > 4096 and int(r.overflow.item()) == 0
+    prev = gs.gs_debug_sort_wait_limit(0)
+    try:
+        log("[sort failure] binning with wait limit 0")
+        r.preprocess(p)
+        r.bin()
+        torch.cuda.synchronize()
+        word = int(r.overflow.item())
+        assert word & gs.BIN_SORT_FAILED, word
+        assert int(r.tile_ranges.abs().sum()) == 0
+        with pytest.raises(gs.GsError, match="gave up"):
+            gs.check_bin_status(word)
+        with pytest.raises(gs.GsError, match="gave up"):
+            r.forward(p, check=True)
+    finally:
+        gs.gs_debug_sort_wait_limit(prev)
+    r.forward(p, check=True)
+    torch.cuda.synchronize()
+    assert int(r.overflow.item()) == 0
+    assert torch.equal(r.point_list[:K], ref_pl) and torch.equal(r.tile_ranges, ref_rg)
+    log("sort failure reported")
+
+
+def test_rasterize_autograd():
+    """torch autograd through gs.rasterize gives Rasterizer.backward's gradients; a backward after a
+    newer forward on the same Rasterizer raises instead of using the newer pass's buffers."""
+    import torch
+    gs = _gs()
+    sc = scenes.random_small(71, n=600, width=80, height=64, sh_degree=2, scale_mu=-2.2)
+    dL = torch.from_numpy(sc.dL_dimage).cuda()
+    p = to_dev(sc.params())
+    leaves = {k: v.clone().requires_grad_(True) for k, v in p.items()}
+    r = gs.Rasterizer(sc.cam, sc.n, 2)
+    img = gs.rasterize(r, *(leaves[k] for k in gs.PARAM_ORDER))
+    (img * dL).sum().backward()
+    ref = gs.Rasterizer(sc.cam, sc.n, 2)
+    ref.forward(p)
+    g = ref.backward(p, dL)
+    torch.cuda.synchronize()
+    assert torch.equal(img.detach(), ref.image)
+    for k in gs.PARAM_ORDER:
+        assert rel_l2(leaves[k].grad.cpu().numpy(), g[k].cpu().numpy()) <= 1e-5, k
+    a = gs.rasterize(r, *(leaves[k] for k in gs.PARAM_ORDER))
+    gs.rasterize(r, *(leaves[k] for k in gs.PARAM_ORDER))  # overwrites r's buffers
+    with pytest.raises(gs.GsError, match="another forward"):
+        (a * dL).sum().backward()
+    log("rasterize autograd ok")
