@@ -26,6 +26,7 @@
 // claimed from an atomic ticket so look-back only waits on running blocks.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "gs_internal.h"
 
@@ -783,6 +784,58 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
     hipLaunchKernelGGL(k_ranges, dim3(rblocks), dim3(256), 0, s, tk_final, num_keys_dev, (uint32_t)key_capacity,
                        overflow_dev, err, tile_ranges, (uint32_t)ntiles);
     return launch_status();
+}
+
+// ---- the allocation-free variant: gs_bin_sort with the library's own scratch ----
+
+namespace gs {
+namespace {
+constexpr size_t kScratchBytes = (size_t)128 << 20;  // the binning workspace the variant can use
+constexpr int kMaxDevices = 64;
+}  // namespace
+}  // namespace gs
+
+// Device scratch of the allocation-free binning call: one copy per GPU, held
+// until the process ends.  Host code never uses this name as an address (in
+// host code it is a stand-in, not device memory); it uses the per-device
+// address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[gs::kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[gs::kMaxDevices] = {};
+}  // namespace
+
+// The current device's copy of `scratch`, looked up once per device.
+static int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return GS_EHIP;
+    if (dev < 0 || dev >= gs::kMaxDevices) return GS_EINVAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GS_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GS_OK;
+}
+
+extern "C" int64_t gs_bin_scratch_bytes(void) { return (int64_t)gs::kScratchBytes; }
+
+extern "C" int gs_bin_sort_noalloc(const gs_camera* cam, int32_t n, const float* depth, const int16_t* rect,
+                                   const int32_t* tiles_touched, int64_t key_capacity, uint32_t* point_list,
+                                   uint32_t* tile_ranges, uint32_t* num_keys_dev, uint32_t* overflow_dev,
+                                   void* stream) {
+    size_t need = 0;
+    int rc = gs_bin_workspace_size(n, cam, key_capacity, &need);
+    if (rc) return rc;
+    if (need > gs::kScratchBytes) return GS_EWORKSPACE;
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    return gs_bin_sort(cam, n, depth, rect, tiles_touched, key_capacity, point_list, tile_ranges, num_keys_dev,
+                       overflow_dev, ws, gs::kScratchBytes, stream);
 }
 
 extern "C" int gs_bin_keys(const gs_camera* cam, const uint32_t* tile_ranges, const uint32_t* point_list,

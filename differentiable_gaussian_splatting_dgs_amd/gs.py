@@ -59,7 +59,7 @@ class GsGaussianSet(C.Structure):
 
 
 SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_bin_workspace_size",
-           "gs_bin_sort", "gs_debug_sort_wait_limit", "gs_bin_keys", "gs_render_fwd", "gs_render_fwd_loss",
+           "gs_bin_sort", "gs_bin_sort_noalloc", "gs_bin_scratch_bytes", "gs_debug_sort_wait_limit", "gs_bin_keys", "gs_render_fwd", "gs_render_fwd_loss",
            "gs_render_bwd", "gs_preprocess_bwd", "gs_preprocess_bwd_adam", "gs_image_loss", "gs_densify_accum",
            "gs_adam_step", "gs_count_pairs", "gs_densify_workspace_size", "gs_densify", "gs_opacity_reset",
            "gs_preprocess_views", "gs_bin_workspace_size_views", "gs_bin_sort_views", "gs_render_fwd_views",
@@ -92,6 +92,8 @@ def load_library(path=LIB_PATH):
     lib.gs_bin_sort.argtypes = [P(GsCamera), _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
     lib.gs_bin_keys.argtypes = [P(GsCamera), _vp, _vp, _vp, _vp, _vp]
     lib.gs_debug_sort_wait_limit.argtypes = [_i64]
+    lib.gs_bin_sort_noalloc.argtypes = [P(GsCamera), _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp]
+    lib.gs_bin_scratch_bytes.argtypes = []
     lib.gs_render_fwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_vp]
     lib.gs_render_fwd_loss.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_i32] + [_vp] * 4 + [_vp]
     lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 9 + [_i32, _vp]
@@ -122,6 +124,7 @@ def load_library(path=LIB_PATH):
         if name not in ("gs_error_string",):
             getattr(lib, name).restype = C.c_int
     lib.gs_debug_sort_wait_limit.restype = _i64
+    lib.gs_bin_scratch_bytes.restype = _i64
     _lib = lib
     return lib
 
@@ -222,6 +225,21 @@ def gs_bin_keys(cam, tile_ranges, point_list, depth, keys):
     rc = load_library().gs_bin_keys(C.byref(camera_struct(cam)), _p(tile_ranges, torch.int32), _p(point_list, torch.int32),
                                     _p(depth, torch.float32), _p(keys, torch.int64), _stream())
     _check(rc, "gs_bin_keys")
+
+
+def gs_bin_sort_noalloc(cam, n, depth, rect, tiles_touched, key_capacity, point_list, tile_ranges, num_keys,
+                        overflow):
+    """gs_bin_sort on the library's own per-GPU scratch (no workspace, nothing allocated)."""
+    rc = load_library().gs_bin_sort_noalloc(
+        C.byref(camera_struct(cam)), n, _p(depth, torch.float32, "depth"), _p(rect, torch.int16, "rect"),
+        _p(tiles_touched, torch.int32, "tiles_touched"), key_capacity, _p(point_list, torch.int32, "point_list"),
+        _p(tile_ranges, torch.int32, "tile_ranges"), _p(num_keys, torch.int32, "num_keys"),
+        _p(overflow, torch.int32, "overflow"), _stream())
+    _check(rc, "gs_bin_sort_noalloc")
+
+
+def gs_bin_scratch_bytes():
+    return int(load_library().gs_bin_scratch_bytes())
 
 
 def gs_debug_sort_wait_limit(limit=-1):

@@ -160,6 +160,25 @@ int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, const int16
  */
 int64_t gs_debug_sort_wait_limit(int64_t limit);
 
+/*
+ * gs_bin_sort_noalloc -- gs_bin_sort for callers that cannot allocate device
+ * memory or hand over a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and status
+ * word as gs_bin_sort, without the workspace: the call uses a scratch buffer of
+ * gs_bin_scratch_bytes() (128 MiB) that the library holds on each GPU for the
+ * life of the process, and allocates nothing.  GS_EWORKSPACE when
+ * gs_bin_workspace_size(n, cam, key_capacity) exceeds it (about n = 1M
+ * Gaussians with 8M list entries).  The first call on a device looks the
+ * buffer's address up (hipGetSymbolAddress) and must run on the device the
+ * stream belongs to; make it outside graph capture.  Every call on one GPU uses
+ * the same buffer: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.
+ */
+int gs_bin_sort_noalloc(const gs_camera* cam, int32_t n, const float* depth, const int16_t* rect,
+                        const int32_t* tiles_touched, int64_t key_capacity, uint32_t* point_list,
+                        uint32_t* tile_ranges, uint32_t* num_keys_dev, uint32_t* overflow_dev, void* stream);
+int64_t gs_bin_scratch_bytes(void);
+
 /* Diagnostic: the 64-bit sort keys (tile << 32 | float32 depth bits) of the
    sorted list, keys [key_capacity]; entries at and beyond K are left alone. */
 int gs_bin_keys(const gs_camera* cam, const uint32_t* tile_ranges, const uint32_t* point_list,
