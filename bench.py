@@ -207,22 +207,25 @@ class RasterPass:
             self.dL = torch.from_numpy(np.ascontiguousarray(sc.dL_dimage)).to(dev)
 
     def run(self, ev=None):
+        """ev: None, or a list of events (None entries skipped) recorded at the stage boundaries
+        0 preprocess 1 bin 2 forward 3 backward blend 4 2D->3D backward 5."""
         gs, r, p, g3 = self.gs, self.r, self.p, self.g3
 
         def mark(i):
-            if ev is not None:
+            if ev is not None and ev[i] is not None:
                 ev[i].record()
         mark(0)
         r.preprocess(p)
         mark(1)
         r.bin()
         mark(2)
+        # the forward also clears the 2D-gradient buffer the backward then accumulates into
         if self.target is not None:
-            r.render_loss(self.target, self.sc.loss, self.dL, self.loss, clear_grad2d=False)
+            r.render_loss(self.target, self.sc.loss, self.dL, self.loss, clear_grad2d=True)
         else:
-            r.render()
+            r.render(clear_grad2d=True)
         mark(3)
-        r.backward_2d(self.dL)
+        r.backward_2d(self.dL, accumulate=True)
         mark(4)
         gs.gs_preprocess_bwd(r.cam, r.settings, r.deg, p["means"], p["log_scales"], p["quats"],
                              p["opacity_logits"], p["sh"], r.tiles_touched, r.clamp, r.grad2d, g3["means"],
@@ -230,27 +233,55 @@ class RasterPass:
         mark(5)
 
 
-def time_passes(run, nstages, steps, warmup, first=None):
+def time_passes(run, nstages, steps, warmup, first=None, watch=None, drifts=False):
     """Warm-up, then `steps` timed passes: host clock over all of them (device synchronised on both
-    sides) and HIP events between the stages of each, recorded on the stream the kernels use."""
+    sides).  An event records a stream marker that drains the pipeline (about 5 us of idle GPU
+    each), so inside the timed passes events bracket only stage `watch` (the dominant kernel, for
+    its launch duration); a second run of `steps` passes with events at every stage boundary gives
+    the per-stage times and the per-pass percentiles.  Events are recorded on the stream the kernels
+    use.  Returns (host ms per pass, per-stage ms, percentiles, ms of stage `watch` in the timed
+    passes).  drifts: each pass changes the state the next one sees (a training step), so a second
+    run would measure other work: then the timed passes themselves carry the events at every stage
+    boundary."""
     import torch
     if first is not None:
         first()
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nstages + 1)] for _ in range(steps)]
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    if drifts:
+        evs = [[mk() for _ in range(nstages + 1)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            run(evs[i])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        stage = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(nstages)]
+        step_ev = np.array([e[0].elapsed_time(e[nstages]) for e in evs])
+        pct = dict(p10=round(float(np.percentile(step_ev, 10)), 4), median=round(float(np.median(step_ev)), 4),
+                   p90=round(float(np.percentile(step_ev, 90)), 4))
+        return ms, stage, pct, (stage[watch] if watch is not None else None)
+    watched = [[mk() if j in (watch, watch + 1) else None for j in range(nstages + 1)] if watch is not None else None
+               for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        run(evs[i])
+        run(watched[i])
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    watch_ms = (float(np.mean([w[watch].elapsed_time(w[watch + 1]) for w in watched])) if watch is not None
+                else None)
+    evs = [[mk() for _ in range(nstages + 1)] for _ in range(steps)]
+    for i in range(steps):
+        run(evs[i])
+    torch.cuda.synchronize()
     stage = [float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])) for j in range(nstages)]
     step_ev = np.array([evs[i][0].elapsed_time(evs[i][nstages]) for i in range(steps)])
     pct = dict(p10=round(float(np.percentile(step_ev, 10)), 4), median=round(float(np.median(step_ev)), 4),
                p90=round(float(np.percentile(step_ev, 90)), 4))
-    return ms, stage, pct
+    return ms, stage, pct, watch_ms
 
 
 def raster_line(name, steps, warmup, peaks):
@@ -262,11 +293,13 @@ def raster_line(name, steps, warmup, peaks):
           flush=True)
     rp = RasterPass(sc)
     r = rp.r
-    ms, stage, pct = time_passes(rp.run, len(STAGES), steps, warmup, first=lambda: r.forward(rp.p, check=True))
+    ms, stage, pct, bwd_ms = time_passes(rp.run, len(STAGES), steps, warmup,
+                                         first=lambda: r.forward(rp.p, check=True), watch=STAGES.index("render_bwd"))
     if gs.check_bin_status(r.overflow.item()):
         raise gs.GsError("list capacity overflow during timing")
     p_fwd, p_bwd, p_blend = (float(x) for x in r.count_pairs().cpu().numpy())
     stage_ms = dict(zip(STAGES, stage))
+    timed_ms = dict(stage_ms, render_bwd=bwd_ms)  # the backward blend as timed inside the timed passes
     K = float(r.num_keys.item())
     entries = walked_entries(r)
     line = dict(metric=METRIC, value=(p_fwd + p_bwd) / (ms * 1e-3), unit="blend pairs/s", n_gpus=1, steps=steps,
@@ -283,8 +316,8 @@ def raster_line(name, steps, warmup, peaks):
                            bwd_pairs_per_s=p_bwd / (stage_ms["render_bwd"] * 1e-3),
                            bwd_walked_entries=entries, bwd_float_atomics=9 * entries,
                            bwd_atomics_per_s=9 * entries / (stage_ms["render_bwd"] * 1e-3)),
-                stage_roofline=raster_roofline(sc.n, K, sc.sh_degree, p_fwd, p_bwd, p_blend, pct["median"], peaks),
-                roofline=kernel_roofline(stage_ms, p_fwd, p_bwd, p_blend, peaks, name),
+                stage_roofline=raster_roofline(sc.n, K, sc.sh_degree, p_fwd, p_bwd, p_blend, ms, peaks),
+                roofline=kernel_roofline(timed_ms, p_fwd, p_bwd, p_blend, peaks, name),
                 peaks=peaks)
     return line, sc
 
@@ -317,7 +350,7 @@ class TrainStep:
         self.step_no += 1
 
         def mark(i):
-            if ev is not None:
+            if ev is not None and ev[i] is not None:
                 ev[i].record()
         mark(0)
         r.preprocess(p)
@@ -347,7 +380,7 @@ def train_measure(steps, warmup):
     for _ in range(max(0, warmup - 1)):
         st.run()
     c0 = st.rast.count_pairs().cpu().numpy()
-    ms, stage, pct = time_passes(st.run, len(TrainStep.STAGES), steps, 0)
+    ms, stage, pct, _ = time_passes(st.run, len(TrainStep.STAGES), steps, 0, drifts=True)
     if gs.check_bin_status(st.rast.overflow.item()):
         raise gs.GsError("list capacity overflow during timing")
     c1 = st.rast.count_pairs().cpu().numpy()
@@ -437,7 +470,7 @@ def views_measure(views, steps, warmup):
         step_no[0] += 1
 
         def mark(i):
-            if ev is not None:
+            if ev is not None and ev[i] is not None:
                 ev[i].record()
         mark(0)
         rv.preprocess(p)
@@ -459,7 +492,7 @@ def views_measure(views, steps, warmup):
     for _ in range(max(0, warmup - 1)):
         run()
     c0 = rv.count_pairs().cpu().numpy()
-    ms, stage, _ = time_passes(run, len(stages), steps, 0)
+    ms, stage, _, _ = time_passes(run, len(stages), steps, 0, drifts=True)
     if gs.check_bin_status(rv.overflow.item(), "gs_bin_sort_views"):
         raise gs.GsError("list capacity overflow during the batched timing")
     c1 = rv.count_pairs().cpu().numpy()

@@ -116,7 +116,7 @@ struct Layout {
     size_t dkeys0, dvals0, dkeys1, dvals1;  // uint32 [n] each
     size_t goff;                            // uint32 [n] first output slot, depth order
     size_t bstart;                          // uint32 [xblocks + 1] first Gaussian (depth order) of each expand block
-    size_t tkeys0, tkeys1, tvals0;          // uint32 [cap] each
+    size_t tkeys0, tkeys1, tvals0;          // uint16 [cap] tile ids (two), uint32 [cap] values
     size_t total;
     uint32_t dparts, eparts, tparts, xblocks;
 };
@@ -143,8 +143,8 @@ inline Layout make_layout(int32_t n, int64_t cap) {
     L.dvals1 = o; o = up256(o + (size_t)n * 4);
     L.goff = o; o = up256(o + (size_t)n * 4);
     L.bstart = o; o = up256(o + ((size_t)L.xblocks + 1) * 4);
-    L.tkeys0 = o; o = up256(o + (size_t)cap * 4);
-    L.tkeys1 = o; o = up256(o + (size_t)cap * 4);
+    L.tkeys0 = o; o = up256(o + (size_t)cap * 2);
+    L.tkeys1 = o; o = up256(o + (size_t)cap * 2);
     L.tvals0 = o; o = up256(o + (size_t)cap * 4);
     L.total = o;
     return L;
@@ -206,9 +206,9 @@ __global__ __launch_bounds__(256) void k_depth_keys(int32_t n, const float* dept
 }
 
 struct PassArgs {
-    const uint32_t* keys_in;
+    const void* keys_in;   // KeyT [count]: uint32 depth keys or uint16 tile ids
     const uint32_t* vals_in;
-    uint32_t* keys_out;  // may be null: keys not needed after this pass
+    void* keys_out;        // KeyT, may be null: keys not needed after this pass
     uint32_t* vals_out;
     const uint32_t* count_dev;  // items = min(*count_dev, cap) when non-null, else count_host
     uint32_t count_host;
@@ -238,7 +238,7 @@ __device__ inline uint32_t wave_incl_sum(uint32_t v) {
 // 2/4. one onesweep pass over 8 bits of a 32-bit key, THREADS threads with IPT
 // items each.  Threads 0..255 (waves 0-3) also own one digit each for the
 // histogram scan and the look-back.
-template <int THREADS, int IPT>
+template <int THREADS, int IPT, typename KeyT>
 __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
     constexpr int kWaves = THREADS / 64;
     constexpr int kSortPart = THREADS * IPT;
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
     __shared__ uint32_t s_wave[kWaves][kRadix]; // per-wave digit counts -> prefixes
     __shared__ uint32_t s_base[kRadix];         // global offset of this partition's first item of digit d
     __shared__ uint32_t s_blk[kRadix];          // block-local exclusive digit offsets
-    __shared__ uint32_t s_keys[kSortPart];      // partition in digit order
+    __shared__ KeyT s_keys[kSortPart];          // partition in digit order
     __shared__ uint32_t s_vals[kSortPart];
     __shared__ uint32_t s_wsum[2][4];
     __shared__ uint32_t s_part;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
         const uint32_t idx = base + i * 64 + lane;
-        key[i] = idx < count ? p.keys_in[idx] : 0u;
+        key[i] = idx < count ? (uint32_t) static_cast<const KeyT*>(p.keys_in)[idx] : 0u;
         val[i] = idx < count ? p.vals_in[idx] : 0u;
     }
     const uint64_t lt = lanemask_lt();
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
             const uint32_t d = (key[i] >> p.shift) & 255u;
             const uint32_t q = s_blk[d] + s_wave[wave][d] + rank[i];
             if (q < (uint32_t)kSortPart) {  // always true for a consistent ranking
-                s_keys[q] = key[i];
+                s_keys[q] = (KeyT)key[i];
                 s_vals[q] = val[i];
             }
         }
@@ -388,10 +388,10 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
     for (int i = 0; i < IPT; ++i) {
         const uint32_t q = (uint32_t)(i * THREADS + tid);
         if (q < nloc) {
-            const uint32_t k = s_keys[q];
+            const uint32_t k = (uint32_t)s_keys[q];
             const uint32_t pos = s_base[(k >> p.shift) & 255u] + q;
             if (pos < count) {  // always true for a consistent histogram; guards the buffers
-                if (p.keys_out) p.keys_out[pos] = k;
+                if (p.keys_out) static_cast<KeyT*>(p.keys_out)[pos] = (KeyT)k;
                 p.vals_out[pos] = s_vals[q];
             }
         }
@@ -413,7 +413,7 @@ struct EmitArgs {
     uint32_t* part;          // [eparts] entries per scan partition -> exclusive offsets
     uint32_t* goff;          // [n] tile count, then first output slot, of the j-th Gaussian in depth order
     uint32_t* bstart;        // [xblocks + 1] depth-order index of each expand block's first Gaussian
-    uint32_t* tkeys;         // [cap] tile id
+    uint16_t* tkeys;         // [cap] tile id (at most 65536 tiles)
     uint32_t* tvals;         // [cap] Gaussian
     uint32_t* stripes;       // [kStripes][kHistBins] striped digit counts
     uint32_t* num_keys;
@@ -593,7 +593,7 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
                 const uint32_t r = base + s - s_goff[q];
                 const uint32_t ry = r / w;
                 tile = (uint32_t)(y0 + (int)ry) * (uint32_t)a.tiles_x + (uint32_t)x0 + (r - ry * w);
-                a.tkeys[base + s] = tile;
+                a.tkeys[base + s] = (uint16_t)tile;
                 a.tvals[base + s] = s_gid[q];
             }
             if (ok) {
@@ -609,9 +609,9 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
 }
 
 // 5. tile ranges from sorted tile ids (ranges zeroed beforehand).  Each thread
-// reads kRangeIPT consecutive keys with vector loads, plus one neighbour on
+// reads kRangeIPT consecutive keys with one vector load, plus one neighbour on
 // each side.
-__global__ __launch_bounds__(256) void k_ranges(const uint32_t* tkeys, const uint32_t* num_keys, uint32_t cap,
+__global__ __launch_bounds__(256) void k_ranges(const uint16_t* tkeys, const uint32_t* num_keys, uint32_t cap,
                                                 uint32_t* overflow, const uint32_t* err, uint32_t* ranges,
                                                 uint32_t ntiles) {
     // a failed tile pass voids the lists: report it with the overflow word and leave the ranges empty
@@ -622,17 +622,22 @@ __global__ __launch_bounds__(256) void k_ranges(const uint32_t* tkeys, const uin
     const uint32_t k0 = (blockIdx.x * blockDim.x + threadIdx.x) * (uint32_t)kRangeIPT;
     if (k0 >= K) return;
     constexpr uint32_t kNone = 0xffffffffu;  // never a tile id
+    static_assert(kRangeIPT == 8, "one 16-byte load of eight 16-bit keys per thread");
     uint32_t t[kRangeIPT];
     if (k0 + kRangeIPT <= K) {  // tkeys is 256-byte aligned and k0 a multiple of 8
         const uint4 a = *reinterpret_cast<const uint4*>(tkeys + k0);
-        const uint4 b = *reinterpret_cast<const uint4*>(tkeys + k0 + 4);
-        t[0] = a.x; t[1] = a.y; t[2] = a.z; t[3] = a.w; t[4] = b.x; t[5] = b.y; t[6] = b.z; t[7] = b.w;
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            t[2 * u] = w[u] & 0xffffu;
+            t[2 * u + 1] = w[u] >> 16;
+        }
     } else {
 #pragma unroll
-        for (int u = 0; u < kRangeIPT; ++u) t[u] = k0 + u < K ? tkeys[k0 + u] : kNone;
+        for (int u = 0; u < kRangeIPT; ++u) t[u] = k0 + u < K ? (uint32_t)tkeys[k0 + u] : kNone;
     }
-    const uint32_t prev = k0 > 0 ? tkeys[k0 - 1] : kNone;
-    const uint32_t next = k0 + kRangeIPT < K ? tkeys[k0 + kRangeIPT] : kNone;
+    const uint32_t prev = k0 > 0 ? (uint32_t)tkeys[k0 - 1] : kNone;
+    const uint32_t next = k0 + kRangeIPT < K ? (uint32_t)tkeys[k0 + kRangeIPT] : kNone;
 #pragma unroll
     for (int u = 0; u < kRangeIPT; ++u) {
         const uint32_t k = k0 + u, cur = t[u];
@@ -708,6 +713,7 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
     hipStream_t s = as_stream(stream);
     char* ws = static_cast<char*>(workspace);
     auto U = [&](size_t off) { return reinterpret_cast<uint32_t*>(ws + off); };
+    auto H = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
 
     // zero counters, histograms, look-back status, ranges, K and the overflow flag
     {
@@ -742,7 +748,7 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
         p.err = err; p.err_bit = 1u << pass; p.err_before = (1u << pass) - 1u; p.skip = nullptr;
         p.wait_limit = wait_limit;
         p.shift = 8 * pass;
-        hipLaunchKernelGGL((k_onesweep<kDepthThreads, kDepthIPT>), dim3(L.dparts), dim3(kDepthThreads), 0, s, p);
+        hipLaunchKernelGGL((k_onesweep<kDepthThreads, kDepthIPT, uint32_t>), dim3(L.dparts), dim3(kDepthThreads), 0, s, p);
     }
     // emit (tile, Gaussian) pairs in depth order, then the stable tile sort.
     // Buffers are routed so the final values land in point_list:
@@ -754,7 +760,7 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
     e.xblocks = L.xblocks;
     e.order = dv[0]; e.rect = rect; e.tt = tiles_touched;
     e.part = U(L.etotal); e.goff = U(L.goff); e.bstart = U(L.bstart);
-    e.tkeys = U(L.tkeys0); e.tvals = tile_passes == 1 ? U(L.tvals0) : point_list;
+    e.tkeys = H(L.tkeys0); e.tvals = tile_passes == 1 ? U(L.tvals0) : point_list;
     e.stripes = U(L.stripes);
     e.num_keys = num_keys_dev; e.overflow = overflow_dev; e.err = err;
     hipLaunchKernelGGL(k_emit_count, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
@@ -765,20 +771,20 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
     p.count_dev = num_keys_dev; p.count_host = 0; p.cap = (uint32_t)key_capacity;
     // the tile passes skip when the emission found an overflow or a failed depth sort
     p.err = err; p.err_bit = 1u << 4; p.err_before = 0u; p.skip = overflow_dev; p.wait_limit = wait_limit;
-    p.keys_in = U(L.tkeys0); p.vals_in = e.tvals;
-    p.keys_out = U(L.tkeys1); p.vals_out = tile_passes == 1 ? point_list : U(L.tvals0);
+    p.keys_in = H(L.tkeys0); p.vals_in = e.tvals;
+    p.keys_out = H(L.tkeys1); p.vals_out = tile_passes == 1 ? point_list : U(L.tvals0);
     p.stripes = U(L.stripes); p.hist_bin = 4 * kRadix; p.status = U(L.tstatus); p.ticket = ticket(4); p.shift = 0;
-    hipLaunchKernelGGL((k_onesweep<kTileThreads, kTileIPT>), dim3(L.tparts), dim3(kTileThreads), 0, s, p);
-    const uint32_t* tk_final = U(L.tkeys1);
+    hipLaunchKernelGGL((k_onesweep<kTileThreads, kTileIPT, uint16_t>), dim3(L.tparts), dim3(kTileThreads), 0, s, p);
+    const uint16_t* tk_final = H(L.tkeys1);
     if (tile_passes == 2) {
         PassArgs p2 = p;
-        p2.keys_in = U(L.tkeys1); p2.vals_in = U(L.tvals0);
-        p2.keys_out = U(L.tkeys0); p2.vals_out = point_list;
+        p2.keys_in = H(L.tkeys1); p2.vals_in = U(L.tvals0);
+        p2.keys_out = H(L.tkeys0); p2.vals_out = point_list;
         p2.hist_bin = 5 * kRadix; p2.status = U(L.tstatus) + (size_t)L.tparts * kRadix;
         p2.ticket = ticket(5); p2.shift = 8;
         p2.err_bit = 1u << 5; p2.err_before = 1u << 4;
-        hipLaunchKernelGGL((k_onesweep<kTileThreads, kTileIPT>), dim3(L.tparts), dim3(kTileThreads), 0, s, p2);
-        tk_final = U(L.tkeys0);
+        hipLaunchKernelGGL((k_onesweep<kTileThreads, kTileIPT, uint16_t>), dim3(L.tparts), dim3(kTileThreads), 0, s, p2);
+        tk_final = H(L.tkeys0);
     }
     const uint32_t rblocks = (uint32_t)((key_capacity + 256 * kRangeIPT - 1) / (256 * kRangeIPT));
     hipLaunchKernelGGL(k_ranges, dim3(rblocks), dim3(256), 0, s, tk_final, num_keys_dev, (uint32_t)key_capacity,

@@ -23,7 +23,10 @@
 // float32 rounding error of the exponent proportional to sqrt(condition) of the
 // 2D covariance instead of its condition number, and the tile-relative mean
 // (float32 mean + float32 residual, less the tile origin) keeps the pixel
-// offset d accurate at 4K.
+// offset d accurate at 4K.  Per list entry the staging precomputes the offsets
+// of e at the tile origin and -log2(opacity), so a pair costs
+//   e1 = L00 x + L10 y + c1,  e2 = L11 y + c2,  opacity G = exp2(-(e1^2 + e2^2 - log2 opacity))
+// for the pixel centre (x, y): three FMAs for e and two for the exponent.
 #include "gs_internal.h"
 
 namespace gs {
@@ -69,22 +72,46 @@ __device__ __forceinline__ int block_tile(const int32_t* sched, int ntiles) {
 
 // The alpha of one (pixel, Gaussian) pair.  Shared verbatim by the forward,
 // the backward and the pair counter so all three take identical decisions.
+// g0 = (L00, L10, L11, c1), g1 = (c2, -log2 opacity, r, g) as staged by
+// stage_record; (fx, fy) is the pixel centre relative to the tile origin.
 struct Pair {
-    float dx, dy, e1, e2, G, sG, alpha;
+    float e1, e2, sG, alpha;  // e = L^T d; sG = opacity G; alpha = min(alpha_max, sG)
 };
 
 __device__ __forceinline__ Pair eval_pair(float fx, float fy, float4 g0, float4 g1, float amax) {
 #pragma clang fp contract(off)
     Pair p;
-    p.dx = fx - g0.x;
-    p.dy = fy - g0.y;
-    p.e1 = __builtin_fmaf(g0.z, p.dx, g0.w * p.dy);
-    p.e2 = g1.x * p.dy;
-    const float q = __builtin_fmaf(p.e1, p.e1, p.e2 * p.e2);
-    p.G = __builtin_amdgcn_exp2f(-q);
-    p.sG = g1.y * p.G;
+    p.e1 = __builtin_fmaf(g0.x, fx, __builtin_fmaf(g0.y, fy, g0.w));
+    p.e2 = __builtin_fmaf(g0.z, fy, g1.x);
+    const float q = __builtin_fmaf(p.e1, p.e1, __builtin_fmaf(p.e2, p.e2, g1.y));
+    p.sG = __builtin_amdgcn_exp2f(-q);
     p.alpha = fminf(amax, p.sG);
     return p;
+}
+
+// The per-entry record the blends stage in LDS, from a splat record (three
+// float4 rows: mean, mean residual; L00, L10, L11, opacity; r, g, b, 0) and the
+// tile origin.  Every kernel that evaluates pairs builds it with this function,
+// so they all round identically.
+struct Staged {
+    float4 g0, g1;
+    float b;
+    float ut, vt;  // the mean relative to the tile origin
+};
+
+__device__ __forceinline__ Staged stage_record(float4 r0, float4 r1, float4 r2, float x0, float y0) {
+#pragma clang fp contract(off)
+    Staged st;
+    st.ut = (r0.x - x0) + r0.z;
+    st.vt = (r0.y - y0) + r0.w;
+    const float l00 = r1.x, l10 = r1.y, l11 = r1.z;
+    // e1 = L00 (x - ut) + L10 (y - vt) = L00 x + L10 y + c1; e2 = L11 (y - vt) = L11 y + c2
+    const float c1 = -__builtin_fmaf(l00, st.ut, l10 * st.vt);
+    const float c2 = -(l11 * st.vt);
+    st.g0 = make_float4(l00, l10, l11, c1);
+    st.g1 = make_float4(c2, -__log2f(r1.w), r2.x, r2.y);  // opacity 0 gives +inf: G = 0
+    st.b = r2.z;
+    return st;
 }
 
 // Transmittance after blending alpha: T (1 - alpha) as one fused operation.  The
@@ -97,15 +124,6 @@ struct Stage {
     float4* g1;
     float* g2;
 };
-
-// Stages one entry's tile-relative data into LDS slot `slot` (no culling test).
-__device__ __forceinline__ void stage_data(const RenderArgs& a, uint32_t g, float x0, float y0, Stage st, int slot) {
-    const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
-    const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
-    st.g0[slot] = make_float4((r0.x - x0) + r0.z, (r0.y - y0) + r0.w, r1.x, r1.y);
-    st.g1[slot] = make_float4(r1.z, r1.w, r2.x, r2.y);
-    st.g2[slot] = r2.z;
-}
 
 // Minimum over the segment t in [t0, t1] of (a*c + b*t)^2 + (l*t)^2, the exponent
 // |L^T d|^2 along an axis-parallel edge of a rectangle (c is the fixed coordinate).
@@ -120,11 +138,11 @@ __device__ __forceinline__ uint32_t stage_entry(const RenderArgs& a, uint32_t g,
                                                 float inv_amin, Stage st, int slot) {
     const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
     const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
-    const float ut = (r0.x - x0) + r0.z;
-    const float vt = (r0.y - y0) + r0.w;
-    st.g0[slot] = make_float4(ut, vt, r1.x, r1.y);
-    st.g1[slot] = make_float4(r1.z, r1.w, r2.x, r2.y);
-    st.g2[slot] = r2.z;
+    const Staged rec = stage_record(r0, r1, r2, x0, y0);
+    const float ut = rec.ut, vt = rec.vt;
+    st.g0[slot] = rec.g0;
+    st.g1[slot] = rec.g1;
+    st.g2[slot] = rec.b;
     // A quadrant can see the Gaussian only if min over its pixel centres of
     // q = |L^T d|^2 (d = p - mean) is <= k2 = log2(opacity / alpha_min).  The test
     // is exact for the rectangle of pixel centres; the threshold gets a relative
@@ -424,11 +442,12 @@ __device__ __forceinline__ float reduce2x9(float a[9], float b[9], float& z, int
 // happen once per entry rather than once per quadrant.
 //
 // The accumulators hold moments: S_t = sum dpow dx, S_s = sum dpow dy,
-// sum dpow dx^2, sum dpow dx dy, sum dpow dy^2 (dpow = dL/dpower), the opacity
-// and colour sums.  After the reduction they become gradients with the entry's
-// conic (A, B, C): dL/dmean2D = (A S_t + B S_s, B S_t + C S_s) since
-// dpower/dmean = conic d, and dL/d(A, B, C) = (-1/2, -1, -1/2) times the second
-// moments.
+// sum dpow dx^2, sum dpow dx dy, sum dpow dy^2 (dpow = dL/dpower, d = pixel -
+// mean), sum dpow and the colour sums.  After the reduction they become
+// gradients with the entry's conic (A, B, C): dL/dmean2D = (A S_t + B S_s,
+// B S_t + C S_s) since dpower/dmean = conic d, dL/d(A, B, C) = (-1/2, -1, -1/2)
+// times the second moments, and dL/dopacity = sum dpow / opacity (dpower is
+// dL/d(opacity G) times opacity G).
 constexpr int kBwdBatch = 64;
 // Below this many tiles the backward runs two waves per tile: with one wave per
 // tile some of the 1024 SIMDs (256 CUs) would have none.  Above it the second
@@ -439,9 +458,10 @@ template <int QPW>
 __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     static_assert(QPW == 4 || QPW == 2, "four or two quadrants per wave");
     constexpr int kSplit = 4 / QPW;
-    __shared__ float4 s_g0[kBwdBatch];   // u', v', L00, L10
-    __shared__ float4 s_g1[kBwdBatch];   // L11, opacity, r, g
-    __shared__ float4 s_g2[kBwdBatch];   // b, A, B, C (conic)
+    __shared__ float4 s_g0[kBwdBatch];   // L00, L10, L11, c1 (stage_record)
+    __shared__ float4 s_g1[kBwdBatch];   // c2, -log2 opacity, r, g
+    __shared__ float4 s_g2[kBwdBatch];   // b, tile-relative mean (u, v), 1 / opacity
+    __shared__ float4 s_g3[kBwdBatch];   // conic A, B, C (for the mean gradient after the reduction), 0
     __shared__ uint32_t s_gid[kBwdBatch];
     __shared__ uint16_t s_list[kBwdBatch];  // slot | quadrant mask << 8, in walk order
 
@@ -516,15 +536,16 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
                 const float dalpha = T[q] * dS;
                 S[q] = __builtin_fmaf(ae, dS, S[q]);
                 const float dsG = (ok && !(p.sG > b.alpha_max)) ? dalpha : 0.f;  // clamped: no dependence
-                // dL/dopacity = dsG G; dL/dpower = dsG opacity G, G = exp(power)
+                // dL/dpower = dsG opacity G (G = exp(power)); dL/dopacity = dsG G = dL/dpower / opacity
                 const float dpow = dsG * p.sG;
-                const float t = dpow * p.dx, sy = dpow * p.dy;
+                const float dx = fxq[q] - G2.y, dy = fyq[q] - G2.z;  // d = pixel - mean
+                const float t = dpow * dx, sy = dpow * dy;
                 v[0] += t;
                 v[1] += sy;
-                v[2] = __builtin_fmaf(t, p.dx, v[2]);
-                v[3] = __builtin_fmaf(t, p.dy, v[3]);
-                v[4] = __builtin_fmaf(sy, p.dy, v[4]);
-                v[5] = __builtin_fmaf(dsG, p.G, v[5]);
+                v[2] = __builtin_fmaf(t, dx, v[2]);
+                v[3] = __builtin_fmaf(t, dy, v[3]);
+                v[4] = __builtin_fmaf(sy, dy, v[4]);
+                v[5] += dpow;
                 v[6] = __builtin_fmaf(w, gp0[q], v[6]);
                 v[7] = __builtin_fmaf(w, gp1[q], v[7]);
                 v[8] = __builtin_fmaf(w, gp2[q], v[8]);
@@ -543,11 +564,13 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
                 if (m) {
                     const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
                     const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
-                    s_g0[lane] = make_float4((r0.x - x0) + r0.z, (r0.y - y0) + r0.w, r1.x, r1.y);
-                    s_g1[lane] = make_float4(r1.z, r1.w, r2.x, r2.y);
+                    const Staged rec = stage_record(r0, r1, r2, x0, y0);
+                    s_g0[lane] = rec.g0;
+                    s_g1[lane] = rec.g1;
+                    s_g2[lane] = make_float4(rec.b, rec.ut, rec.vt, __builtin_amdgcn_rcpf(r1.w));
                     const float l00 = r1.x, l10 = r1.y, l11 = r1.z;
-                    s_g2[lane] = make_float4(r2.z, k2ln2 * (l00 * l00), k2ln2 * (l00 * l10),
-                                             k2ln2 * __builtin_fmaf(l10, l10, l11 * l11));
+                    s_g3[lane] = make_float4(k2ln2 * (l00 * l00), k2ln2 * (l00 * l10),
+                                             k2ln2 * __builtin_fmaf(l10, l10, l11 * l11), 0.f);
                     s_gid[lane] = g;
                 }
             }
@@ -576,12 +599,13 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
             walk(eb, lb >> 8, top - eb, vb);  // no quadrant when there is no second entry
             float z;
             const float wv = reduce2x9(va, vb, z, lane);
-            // quads 0 / 8: A S_t + B S_s; quads 1 / 9: C S_s + B S_t; others: scale * moment
+            // quads 0 / 8: A S_t + B S_s; quads 1 / 9: C S_s + B S_t; 2-4: scale * moment;
+            // 5: sum dpow / opacity (dL/dopacity = dsG G); 6, 7 and the ninth: as summed
             const int e = entb ? eb : ea;
-            const float4 G2 = s_g2[e];
+            const float4 Q = s_g3[e];
             const float x = dpp<kRowHalfMirror>(wv);  // the other first moment of the same entry
-            const float P = vi == 0 ? G2.y : (vi == 1 ? G2.w : scl);
-            const float Bx = vi < 2 ? G2.z * x : 0.f;
+            const float P = vi == 0 ? Q.x : (vi == 1 ? Q.z : (vi == 5 ? s_g2[e].w : scl));
+            const float Bx = vi < 2 ? Q.y * x : 0.f;
             const float out = ninth ? z : __builtin_fmaf(P, wv, Bx);
             if (writer && (two || !entb))
                 unsafeAtomicAdd(a.grad2d + (size_t)s_gid[e] * GS_GRAD2D_STRIDE + widx, out);
@@ -741,10 +765,8 @@ __global__ __launch_bounds__(256) void k_count_pairs(RenderArgs a, unsigned long
             const uint32_t g = a.list[k];
             if (g >= a.n) continue;
             const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
-            const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
-            const float4 g0 = make_float4((r0.x - x0) + r0.z, (r0.y - y0) + r0.w, r1.x, r1.y);
-            const float4 g1 = make_float4(r1.z, r1.w, r2.x, r2.y);
-            const Pair p = eval_pair(fx, fy, g0, g1, b.alpha_max);
+            const Staged rec = stage_record(sp[0], sp[1], sp[2], x0, y0);
+            const Pair p = eval_pair(fx, fy, rec.g0, rec.g1, b.alpha_max);
             ++ev;
             if (p.alpha < b.alpha_min) continue;
             const float Tn = trans_after(T, p.alpha);
@@ -853,18 +875,18 @@ int render_fwd_loss_impl(const gs_camera* cams, int32_t views, const gs_settings
     const int rc = fwd_args(cams, views, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
                             a);
     if (rc) return rc;
-    if (loss_mode == 0) return render_fwd_impl(cams, a, tile_order, nullptr, as_stream(stream));
-    if (loss_mode != 1 && loss_mode != 2) return GS_EINVAL;
-    if (!target || !dL_dimage || !loss_dev) return GS_EINVAL;
     if (grad2d_clear && !aligned16(grad2d_clear)) return GS_EALIGN;
-    a.loss_mode = loss_mode;
-    a.target = target;
-    a.dL_out = dL_dimage;
-    a.loss_part = loss_dev + 1;
     if (grad2d_clear && n > 0) {
         a.clear = reinterpret_cast<float4*>(grad2d_clear);
         a.clear4 = (size_t)a.n * GS_GRAD2D_STRIDE / 4;
     }
+    if (loss_mode == 0) return render_fwd_impl(cams, a, tile_order, nullptr, as_stream(stream));
+    if (loss_mode != 1 && loss_mode != 2) return GS_EINVAL;
+    if (!target || !dL_dimage || !loss_dev) return GS_EINVAL;
+    a.loss_mode = loss_mode;
+    a.target = target;
+    a.dL_out = dL_dimage;
+    a.loss_part = loss_dev + 1;
     return render_fwd_impl(cams, a, tile_order, loss_dev, as_stream(stream));
 }
 
@@ -925,17 +947,18 @@ int count_pairs_impl(const gs_camera* cams, int32_t views, const gs_settings* se
 
 extern "C" int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                              const uint32_t* point_list, const float* splats, float* image, float* final_T,
-                             int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order, void* stream) {
+                             int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order, float* grad2d_clear,
+                             void* stream) {
     return render_fwd_loss_impl(cam, 1, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
-                                tile_order, 0, nullptr, nullptr, nullptr, nullptr, stream);
+                                tile_order, 0, nullptr, nullptr, nullptr, grad2d_clear, stream);
 }
 
 extern "C" int gs_render_fwd_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                                    const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
                                    float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
-                                   int32_t* tile_order, void* stream) {
+                                   int32_t* tile_order, float* grad2d_clear, void* stream) {
     return render_fwd_loss_impl(cams, views, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib,
-                                contrib, tile_order, 0, nullptr, nullptr, nullptr, nullptr, stream);
+                                contrib, tile_order, 0, nullptr, nullptr, nullptr, grad2d_clear, stream);
 }
 
 extern "C" int gs_render_fwd_loss(const gs_camera* cam, const gs_settings* set, int32_t n,

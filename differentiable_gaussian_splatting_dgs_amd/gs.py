@@ -94,7 +94,7 @@ def load_library(path=LIB_PATH):
     lib.gs_debug_sort_wait_limit.argtypes = [_i64]
     lib.gs_bin_sort_noalloc.argtypes = [P(GsCamera), _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp]
     lib.gs_bin_scratch_bytes.argtypes = []
-    lib.gs_render_fwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_vp]
+    lib.gs_render_fwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 9 + [_vp]
     lib.gs_render_fwd_loss.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_i32] + [_vp] * 4 + [_vp]
     lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 9 + [_i32, _vp]
     lib.gs_preprocess_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
@@ -112,7 +112,7 @@ def load_library(path=LIB_PATH):
     lib.gs_preprocess_views.argtypes = V + [P(GsSettings), _i32, _i32] + [_vp] * 10 + [_vp]
     lib.gs_bin_workspace_size_views.argtypes = [_i32, P(GsCamera), _i32, _i64, P(C.c_size_t)]
     lib.gs_bin_sort_views.argtypes = V + [_i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
-    lib.gs_render_fwd_views.argtypes = V + [P(GsSettings), _i32] + [_vp] * 8 + [_vp]
+    lib.gs_render_fwd_views.argtypes = V + [P(GsSettings), _i32] + [_vp] * 9 + [_vp]
     lib.gs_render_fwd_loss_views.argtypes = V + [P(GsSettings), _i32] + [_vp] * 8 + [_i32] + [_vp] * 4 + [_vp]
     lib.gs_render_bwd_views.argtypes = V + [P(GsSettings), _i32] + [_vp] * 9 + [_i32, _vp]
     lib.gs_preprocess_bwd_views.argtypes = V + [P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
@@ -265,13 +265,13 @@ def check_bin_status(word, what="gs_bin_sort"):
 
 
 def gs_render_fwd(cam, settings, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
-                  tile_order=None):
+                  tile_order=None, grad2d_clear=None):
     rc = load_library().gs_render_fwd(
         C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
         _p(point_list, torch.int32, "point_list"), _p(splats, torch.float32, "splats"),
         _p(image, torch.float32, "image"), _p(final_T, torch.float32, "final_T"),
         _p(n_contrib, torch.int32, "n_contrib"), _p(contrib, torch.uint8, "contrib"),
-        _p(tile_order, torch.int32, "tile_order"), _stream())
+        _p(tile_order, torch.int32, "tile_order"), _p(grad2d_clear, torch.float32, "grad2d_clear"), _stream())
     _check(rc, "gs_render_fwd")
 
 
@@ -584,7 +584,8 @@ def gs_render_fwd_views(cams, settings, n, tile_ranges, point_list, splats, imag
               _p(n_contrib, torch.int32, "n_contrib"), _p(contrib, torch.uint8, "contrib"),
               _p(tile_order, torch.int32, "tile_order"))
     if mode is None:
-        _check(load_library().gs_render_fwd_views(*common, _stream()), "gs_render_fwd_views")
+        _check(load_library().gs_render_fwd_views(*common, _p(grad2d_clear, torch.float32, "grad2d_clear"),
+                                                  _stream()), "gs_render_fwd_views")
         return
     tx, ty = gs_tile_grid(cams[0])
     if loss_dev.numel() < 1 + v * tx * ty:
@@ -717,9 +718,12 @@ class Rasterizer:
         gs_bin_sort(self.cam, self.n, self.depth, self.rect, self.tiles_touched, self.key_capacity, self.point_list,
                     self.tile_ranges, self.num_keys, self.overflow, self.workspace)
 
-    def render(self):
+    def render(self, clear_grad2d=False):
+        """Forward blend; with clear_grad2d the 2D-gradient buffer is zeroed by the same kernel, for
+        backward_2d(..., accumulate=True)."""
         gs_render_fwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, self.image,
-                      self.final_T, self.n_contrib, self.contrib, self.tile_order)
+                      self.final_T, self.n_contrib, self.contrib, self.tile_order,
+                      self.grad2d if clear_grad2d else None)
 
     def render_loss(self, target, mode, dL_dimage, loss_dev, clear_grad2d=True):
         """Forward blend with the fused image loss; with clear_grad2d the 2D-gradient buffer is zeroed too,

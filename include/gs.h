@@ -201,11 +201,14 @@ int gs_bin_keys(const gs_camera* cam, const uint32_t* tile_ranges, const uint32_
  * tiles start first.  Row 0 is the forward's own (work = list length), row 1
  * the backward's (work estimated from the flags): pass tile_order + tiles to
  * gs_render_bwd.
+ * grad2d_clear [n,12] float32, optional: set to zero by the same kernel (its
+ * memory traffic overlaps the blending), for a gs_render_bwd call with
+ * accumulate = 1, which then needs no clearing pass of its own.
  */
 int gs_render_fwd(const gs_camera* cam, const gs_settings* set, int32_t n,
                   const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
                   float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
-                  int32_t* tile_order, void* stream);
+                  int32_t* tile_order, float* grad2d_clear, void* stream);
 
 /*
  * gs_render_fwd_loss -- gs_render_fwd with the image loss of gs_image_loss
@@ -476,7 +479,8 @@ int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n, const flo
                       size_t workspace_bytes, void* stream);
 int gs_render_fwd_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                         const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats, float* image,
-                        float* final_T, int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order, void* stream);
+                        float* final_T, int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order,
+                        float* grad2d_clear, void* stream);
 int gs_render_fwd_loss_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                              const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
                              float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,

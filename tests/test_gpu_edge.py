@@ -165,9 +165,9 @@ def test_abi_errors():
     assert lib.gs_bin_workspace_size(n, C.byref(cam), 1 << 31, C.byref(sz)) == -5
     bad = gs.camera_struct(scenes.Camera.identity(32, 32, 30.0))
     bad.width = 0
-    assert lib.gs_render_fwd(C.byref(bad), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None, None) == -1
+    assert lib.gs_render_fwd(C.byref(bad), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None, None, None) == -1
     # missing contrib buffer
-    assert lib.gs_render_fwd(C.byref(cam), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, None, None, None) == -1
+    assert lib.gs_render_fwd(C.byref(cam), C.byref(st), n, ptr, ptr, ptr, ptr, ptr, ptr, None, None, None, None) == -1
     # accumulate must be 0 or 1
     assert lib.gs_render_bwd(C.byref(cam), C.byref(st), n, *([ptr] * 9), 2, None) == -1
     assert lib.gs_error_string(-3) == b"workspace too small"
@@ -286,10 +286,15 @@ def test_backward_accumulate():
     g1 = r.backward_2d(dL).clone()
     g2 = r.backward_2d(dL, accumulate=True).clone()
     g3 = r.backward_2d(dL).clone()
+    # the forward's fused clear, then an accumulating backward
+    r.grad2d.fill_(7.0)
+    r.render(clear_grad2d=True)
+    g4 = r.backward_2d(dL, accumulate=True).clone()
     torch.cuda.synchronize()
     assert float(g1.abs().sum()) > 0
     assert rel_l2(g2.cpu().numpy(), 2 * g1.cpu().numpy()) < 1e-6
     assert rel_l2(g3.cpu().numpy(), g1.cpu().numpy()) < 1e-6
+    assert rel_l2(g4.cpu().numpy(), g1.cpu().numpy()) < 1e-6
 
 
 def test_training_tail_matches_oracle():
