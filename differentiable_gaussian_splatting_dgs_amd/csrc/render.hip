@@ -85,7 +85,7 @@ __device__ __forceinline__ Pair eval_pair(float fx, float fy, float4 g0, float4 
     p.e2 = __builtin_fmaf(g0.z, fy, g1.x);
     const float q = __builtin_fmaf(p.e1, p.e1, __builtin_fmaf(p.e2, p.e2, g1.y));
     p.sG = __builtin_amdgcn_exp2f(-q);
-    p.alpha = fminf(amax, p.sG);
+    p.alpha = __builtin_amdgcn_fmed3f(p.sG, 0.f, amax);  // min(amax, sG) for sG >= 0, one instruction
     return p;
 }
 
@@ -135,7 +135,7 @@ __device__ __forceinline__ float edge_min(float a, float b, float l, float c, fl
 }
 
 __device__ __forceinline__ uint32_t stage_entry(const RenderArgs& a, uint32_t g, float x0, float y0,
-                                                float inv_amin, Stage st, int slot) {
+                                                float log2_amin_inv, Stage st, int slot) {
     const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
     const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
     const Staged rec = stage_record(r0, r1, r2, x0, y0);
@@ -149,10 +149,11 @@ __device__ __forceinline__ uint32_t stage_entry(const RenderArgs& a, uint32_t g,
     // margin of 1/64 plus 1/16 so float32 rounding can only keep extra entries,
     // never drop one that a pixel would blend.
     const float l00 = r1.x, l10 = r1.y, l11 = r1.z;
-    const float k2 = fmaxf(__log2f(r1.w * inv_amin), 0.f);
+    const float k2 = fmaxf(log2_amin_inv - rec.g1.y, 0.f);  // log2(opacity / alpha_min)
     const float kq = __builtin_fmaf(k2, 1.f + 1.f / 64.f, 1.f / 16.f);
-    const float sv = -l00 * l10 / __builtin_fmaf(l10, l10, l11 * l11);  // minimiser slope on vertical edges
-    const float sh = -l10 / l00;                                         // and on horizontal edges
+    // minimiser slopes on vertical and horizontal edges (approximate reciprocals: the test has a margin)
+    const float sv = -l00 * l10 * __builtin_amdgcn_rcpf(__builtin_fmaf(l10, l10, l11 * l11));
+    const float sh = -l10 * __builtin_amdgcn_rcpf(l00);
     uint32_t m = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
     const bool inside = px < b.width && py < b.height;
     const float fx = (float)lx + 0.5f, fy = (float)ly + 0.5f;
     const float x0 = (float)(tx * kTile), y0 = (float)(ty * kTile);
-    const float inv_amin = 1.f / b.alpha_min;
+    const float log2_amin_inv = -__log2f(b.alpha_min);
     const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
     const Stage st{s_g0, s_g1, s_g2};
 
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
         uint32_t m = 0;
         if (k < range.y) {
             const uint32_t g = a.list[k];
-            if (g < a.n) m = stage_entry(a, g, x0, y0, inv_amin, st, tid);
+            if (g < a.n) m = stage_entry(a, g, x0, y0, log2_amin_inv, st, tid);
         }
         // the previous batch's flags are final (the loop ends with a barrier)
         if (kprev != 0xffffffffu) flag_out(kprev);
