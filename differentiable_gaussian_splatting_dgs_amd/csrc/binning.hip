@@ -16,14 +16,22 @@
 //   3. emit: an exclusive scan of tiles_touched in depth order gives every
 //      Gaussian its first output slot; then fixed-size blocks of output slots
 //      each write (tile id, Gaussian) for their slots (balanced however many
-//      tiles a Gaussian covers) and count the tile digits.
-//   4. LSD onesweep radix sort of (tile id, Gaussian) over K, 1-2 x 8-bit passes.
-//      Stable, so each tile keeps the depth order of step 2.
+//      tiles a Gaussian covers) and count the tile digits, in total and per
+//      block.
+//   4. LSD radix sort of (tile id, Gaussian) over K, 1-2 x 8-bit passes, by
+//      reduce-then-scan: per-block digit counts (from step 3 for the first
+//      digit, a counting pass for the second), a scan of them into output
+//      positions, and a scatter pass that ranks and writes each partition on
+//      its own.  Stable, so each tile keeps the depth order of step 2.
 //   5. tile ranges from the sorted tile ids.
 // The onesweep pass (one kernel per digit: stable wave-level ranking by
 // ballot matching, then decoupled look-back across partitions for the digit
 // offsets) follows Adinets and Merrill, "Onesweep" (2022), with partitions
 // claimed from an atomic ticket so look-back only waits on running blocks.
+// Over N it fits in one wave of blocks; over K (several waves of blocks) the
+// look-back's serial chain costs more than the tile sort's counting and
+// scanning, and without waits between partitions the scatter can hand each
+// XCD a contiguous range of partitions.
 #include <algorithm>
 #include <atomic>
 #include <mutex>
@@ -48,6 +56,7 @@ constexpr int kStripes = 32;                        // histogram copies that blo
 constexpr int kHistBins = 6 * 256;                  // 4 depth digits + 2 tile digits
 constexpr int kLookWindow = 8;                      // predecessors read at once per digit
 constexpr int kRadix = 256;
+constexpr uint32_t kXcds = 8;                       // accelerator complex dies: blocks are dealt to them round-robin
 constexpr uint32_t kFlagAgg = 1u << 30;
 constexpr uint32_t kFlagInc = 2u << 30;
 constexpr uint32_t kValMask = (1u << 30) - 1u;
@@ -58,6 +67,7 @@ constexpr int kEmitIPT = 4;
 constexpr int kEmitPart = kEmitThreads * kEmitIPT;  // 1024 Gaussians per scan partition
 constexpr int kSlotsPT = 8;
 constexpr int kSlots = kEmitThreads * kSlotsPT;     // 2048 output slots per expand block
+static_assert(kTilePart % kSlots == 0, "expand blocks tile the tile sort's partitions");
 
 __device__ inline uint32_t ld_acquire(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -71,21 +81,33 @@ __device__ inline uint64_t lanemask_lt() {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Lanes whose 8-bit value equals this lane's (among lanes with valid set).
-__device__ inline uint64_t match8(uint32_t d, bool valid) {
-    uint64_t m = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const uint64_t bb = __ballot((d >> b) & 1u);
-        m &= ((d >> b) & 1u) ? bb : ~bb;
-    }
-    return m;
+// Bit b of d sign-extended: 0 or ~0.  Written as one VALU instruction the
+// compiler cannot see through, so the ballot on it below compares it with 0
+// instead of shifting d again.
+template <int B>
+__device__ inline uint32_t bit_mask(uint32_t d) {
+    uint32_t s;
+    asm volatile("v_bfe_i32 %0, %1, %2, 1" : "=v"(s) : "v"(d), "n"(B));
+    return s;
 }
 
-// s_hist[bin] += 1 for every valid lane, one LDS atomic per distinct bin.
-__device__ inline void wave_hist_add(uint32_t* s_hist, uint32_t bin, bool valid) {
-    const uint64_t m = match8(bin, valid);
-    if (valid && (m & lanemask_lt()) == 0) atomicAdd(&s_hist[bin], (uint32_t)__popcll(m));
+// Lanes whose 8-bit digit equals this lane's (among lanes with valid set),
+// when the digits of all items can differ only in the bits of vm (uniform).
+// A lane matches when, for every bit of vm, its bit equals ours: the XOR of
+// that bit's ballot with our bit replicated is 0 in its position.
+__device__ inline uint64_t match_digits(uint32_t d, bool valid, uint32_t vm) {
+    uint32_t xlo = 0, xhi = 0;
+#define GS_MATCH_BIT(B)                                   \
+    if (vm & (1u << B)) {                                 \
+        const uint32_t sb = bit_mask<B>(d);               \
+        const uint64_t bb = __ballot(sb != 0u);           \
+        xlo |= (uint32_t)bb ^ sb;                         \
+        xhi |= (uint32_t)(bb >> 32) ^ sb;                 \
+    }
+    GS_MATCH_BIT(0) GS_MATCH_BIT(1) GS_MATCH_BIT(2) GS_MATCH_BIT(3)
+    GS_MATCH_BIT(4) GS_MATCH_BIT(5) GS_MATCH_BIT(6) GS_MATCH_BIT(7)
+#undef GS_MATCH_BIT
+    return __ballot(valid) & ~(((uint64_t)xhi << 32) | xlo);
 }
 
 // Sum over the kStripes histogram copies of bin b.
@@ -106,14 +128,16 @@ constexpr int kTicketStride = 16;  // one 64-byte line per counter
 
 // Workspace layout (all offsets 256-byte aligned).
 struct Layout {
-    size_t tickets;     // uint32 [6 passes][kTicketGroups][kTicketStride] partition tickets
+    size_t tickets;     // uint32 [4 depth passes][kTicketGroups][kTicketStride] partition tickets
     size_t err;         // uint32 [1] look-back spin-limit flag
     size_t dstatus;     // uint32 [4][dparts][256]
     size_t etotal;      // uint32 [eparts] entries per emit partition, then their exclusive offsets
-    size_t tstatus;     // uint32 [2][tparts][256]
+    size_t vmw;         // uint32 [2 passes][2] OR of the tile digits present, OR of their complements
     size_t zero_end;    // everything above is zeroed per call
     size_t stripes;     // uint32 [kStripes][kHistBins] striped digit counts (zeroed)
     size_t dkeys0, dvals0, dkeys1, dvals1;  // uint32 [n] each
+    size_t tcnt0, tpre0;                    // uint32 [xblocks][256] tile digit-0 counts per expand block, [256][xblocks] prefixes
+    size_t tcnt1, tpre1;                    // uint32 [tparts][256] tile digit-1 counts per partition, [256][tparts] prefixes
     size_t goff;                            // uint32 [n] first output slot, depth order
     size_t bstart;                          // uint32 [xblocks + 1] first Gaussian (depth order) of each expand block
     size_t tkeys0, tkeys1, tvals0;          // uint16 [cap] tile ids (two), uint32 [cap] values
@@ -130,17 +154,21 @@ inline Layout make_layout(int32_t n, int64_t cap) {
     L.tparts = (uint32_t)((cap + kTilePart - 1) / kTilePart);
     L.xblocks = (uint32_t)((cap + kSlots - 1) / kSlots);
     size_t o = 0;
-    L.tickets = o; o = up256(o + (size_t)6 * kTicketGroups * kTicketStride * 4);
+    L.tickets = o; o = up256(o + (size_t)4 * kTicketGroups * kTicketStride * 4);
     L.err = o; o = up256(o + 4);
     L.dstatus = o; o = up256(o + (size_t)4 * L.dparts * kRadix * 4);
     L.etotal = o; o = up256(o + (size_t)L.eparts * 4);
-    L.tstatus = o; o = up256(o + (size_t)2 * L.tparts * kRadix * 4);
+    L.vmw = o; o = up256(o + 4 * 4);
     L.stripes = o; o = up256(o + (size_t)kStripes * kHistBins * 4);
     L.zero_end = o;
     L.dkeys0 = o; o = up256(o + (size_t)n * 4);
     L.dvals0 = o; o = up256(o + (size_t)n * 4);
     L.dkeys1 = o; o = up256(o + (size_t)n * 4);
     L.dvals1 = o; o = up256(o + (size_t)n * 4);
+    L.tcnt0 = o; o = up256(o + (size_t)kRadix * L.xblocks * 4);
+    L.tpre0 = o; o = up256(o + (size_t)kRadix * L.xblocks * 4);
+    L.tcnt1 = o; o = up256(o + (size_t)kRadix * L.tparts * 4);
+    L.tpre1 = o; o = up256(o + (size_t)kRadix * L.tparts * 4);
     L.goff = o; o = up256(o + (size_t)n * 4);
     L.bstart = o; o = up256(o + ((size_t)L.xblocks + 1) * 4);
     L.tkeys0 = o; o = up256(o + (size_t)cap * 2);
@@ -223,6 +251,11 @@ struct PassArgs {
     const uint32_t* skip;  // optional: the pass does nothing when *skip != 0 (list overflow)
     uint32_t wait_limit;   // waits per look-back before giving up
     int shift;
+    // passes with precomputed prefixes (k_pass_scatter)
+    const uint32_t* prefix;   // [256][stride]: items of digit d before column c (k_digit_scan)
+    uint32_t stride;
+    uint32_t cols_per_part;   // columns per partition: partition p starts at column p cols_per_part
+    const uint32_t* vmw;      // [2]: OR of the digits present, OR of their complements (k_digit_scan)
 };
 
 // Inclusive sum over the 64 lanes of a wave.
@@ -250,6 +283,7 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
     __shared__ KeyT s_keys[kSortPart];          // partition in digit order
     __shared__ uint32_t s_vals[kSortPart];
     __shared__ uint32_t s_wsum[2][4];
+    __shared__ uint32_t s_dig[2][4];            // OR and AND of the digits present, per digit wave
     __shared__ uint32_t s_part;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool digit_thread = tid < kRadix;
@@ -268,8 +302,23 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
         h = stripe_sum(p.stripes, p.hist_bin + tid);
         hx = wave_incl_sum(h);
         if (lane == 63) s_wsum[0][wave] = hx;
+        // the digits present in this pass (tid is the digit)
+        uint32_t dor = h ? (uint32_t)tid : 0u, dand = h ? (uint32_t)tid : 255u;
+        for (int o = 32; o >= 1; o >>= 1) {
+            dor |= __shfl_xor(dor, o, 64);
+            dand &= __shfl_xor(dand, o, 64);
+        }
+        if (lane == 0) { s_dig[0][wave] = dor; s_dig[1][wave] = dand; }
     }
     __syncthreads();
+    // bits in which the pass's digits differ: only these need matching
+    uint32_t vm;
+    {
+        uint32_t dor = 0, dand = 255u;
+#pragma unroll
+        for (int w = 0; w < kRadix / 64; ++w) { dor |= s_dig[0][w]; dand &= s_dig[1][w]; }
+        vm = (dor ^ dand) & 255u;
+    }
     if (digit_thread) {
         uint32_t add = 0;
         for (int w = 0; w < wave; ++w) add += s_wsum[0][w];
@@ -295,7 +344,7 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
     for (int i = 0; i < IPT; ++i) {
         const bool valid = (base + i * 64 + lane) < count;
         const uint32_t d = (key[i] >> p.shift) & 255u;
-        const uint64_t m = match8(d, valid);
+        const uint64_t m = match_digits(d, valid, vm);
         const uint32_t below = (uint32_t)__popcll(m & lt);
         const uint32_t prev = valid ? s_wave[wave][d] : 0u;
         rank[i] = prev + below;
@@ -416,6 +465,7 @@ struct EmitArgs {
     uint16_t* tkeys;         // [cap] tile id (at most 65536 tiles)
     uint32_t* tvals;         // [cap] Gaussian
     uint32_t* stripes;       // [kStripes][kHistBins] striped digit counts
+    uint32_t* tcnt0;         // [xblocks][256] tile digit-0 counts of each expand block
     uint32_t* num_keys;
     uint32_t* overflow;
     const uint32_t* err;     // look-back failures of the depth passes
@@ -444,6 +494,195 @@ __device__ inline uint32_t block_excl_sum(uint32_t v, uint32_t* s_wsum, uint32_t
         total += s_wsum[w];
     }
     return x - v + add;
+}
+
+// Tile sort passes by reduce-then-scan: the digit counts of every block of
+// the pass's input are known before the pass (the emission counts digit 0 per
+// expand block, k_digit_count digit 1 per partition), k_digit_scan turns them
+// into per-digit prefixes, and k_pass_scatter ranks and writes each partition
+// with no wait on other partitions.  Same partitions, ranking and output as
+// k_onesweep.
+
+// Digit counts of every partition of the pass's input: cnt[part][d].  Every
+// entry is written (zeros past the items).
+template <int THREADS, int IPT>
+__global__ __launch_bounds__(THREADS) void k_digit_count(const uint16_t* keys, const uint32_t* count_dev, uint32_t cap,
+                                                         int shift, uint32_t* cnt, const uint32_t* skip) {
+    static_assert(IPT == 8, "one 16-byte load of eight 16-bit keys per thread");
+    __shared__ uint32_t h[kRadix];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kRadix; i += THREADS) h[i] = 0;
+    __syncthreads();
+    if (*skip == 0u) {
+        const uint32_t count = min(*count_dev, cap);
+        const uint32_t k0 = blockIdx.x * (uint32_t)(THREADS * IPT) + (uint32_t)tid * IPT;
+        uint32_t k[IPT];
+        if (k0 + IPT <= count) {  // keys are 256-byte aligned and k0 a multiple of 8
+            const uint4 v = *reinterpret_cast<const uint4*>(keys + k0);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { k[2 * u] = w[u] & 0xffffu; k[2 * u + 1] = w[u] >> 16; }
+        } else {
+#pragma unroll
+            for (int u = 0; u < IPT; ++u) k[u] = k0 + u < count ? (uint32_t)keys[k0 + u] : 0xffffffffu;
+        }
+#pragma unroll
+        for (int u = 0; u < IPT; ++u)
+            if (k[u] != 0xffffffffu) atomicAdd(&h[(k[u] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    for (int d = tid; d < kRadix; d += THREADS) cnt[(size_t)blockIdx.x * kRadix + d] = h[d];
+}
+
+// One block per digit d: pre[d][c] = the output position of the first item
+// of digit d in block c of the pass's input: the items of smaller digits in
+// the whole pass (from the pass histogram) plus the items of digit d in the
+// blocks before c (from the counts cnt[c][d]; column reads, row writes, so
+// both sides write whole cache lines).  Every load of a chunk of columns is
+// issued before the scan.  Also records which digits occur, for the
+// ranking's bit mask.
+constexpr int kScanCols = 16;  // columns per thread per chunk
+__global__ __launch_bounds__(kRadix) void k_digit_scan(const uint32_t* stripes, int hist_bin, const uint32_t* cnt,
+                                                       uint32_t* pre, uint32_t cols, uint32_t* vmw,
+                                                       const uint32_t* skip) {
+    __shared__ uint32_t s_wsum[4];
+    __shared__ uint32_t s_base;
+    if (*skip != 0u) return;
+    const int tid = threadIdx.x;
+    const uint32_t d = blockIdx.x;
+    uint32_t* row = pre + (size_t)d * cols;
+    uint32_t run = 0;
+    for (uint32_t c0 = 0; c0 < cols; c0 += kScanCols * kRadix) {
+        const uint32_t j0 = c0 + kScanCols * tid;
+        uint32_t c[kScanCols];
+#pragma unroll
+        for (int k = 0; k < kScanCols; ++k) c[k] = j0 + k < cols ? cnt[(size_t)(j0 + k) * kRadix + d] : 0u;
+        if (c0 == 0) {
+            // digit base: thread t sums the histogram of digit t, the block scans them
+            uint32_t tot;
+            const uint32_t h = stripe_sum(stripes, hist_bin + tid);
+            const uint32_t ex = block_excl_sum(h, s_wsum, tot);
+            if ((uint32_t)tid == d) {
+                s_base = ex;
+                if (h) {
+                    atomicOr(&vmw[0], d);
+                    atomicOr(&vmw[1], ~d & 255u);
+                }
+            }
+            __syncthreads();
+            run = s_base;
+        }
+        uint32_t sum = 0;
+#pragma unroll
+        for (int k = 0; k < kScanCols; ++k) sum += c[k];
+        uint32_t ctot;
+        uint32_t off = run + block_excl_sum(sum, s_wsum, ctot);
+#pragma unroll
+        for (int k = 0; k < kScanCols; ++k) {
+            if (j0 + k < cols) row[j0 + k] = off;
+            off += c[k];
+        }
+        run += ctot;
+    }
+}
+
+template <int THREADS, int IPT, typename KeyT>
+__global__ __launch_bounds__(THREADS) void k_pass_scatter(PassArgs p) {
+    constexpr int kWaves = THREADS / 64;
+    constexpr int kSortPart = THREADS * IPT;
+    static_assert(THREADS >= kRadix && THREADS % 64 == 0, "one thread per digit");
+    __shared__ uint32_t s_wave[kWaves][kRadix];  // per-wave digit counts -> prefixes
+    __shared__ uint32_t s_base[kRadix];          // output position of local slot q of digit d: s_base[d] + q
+    __shared__ uint32_t s_blk[kRadix];           // block-local exclusive digit offsets
+    __shared__ KeyT s_keys[kSortPart];           // partition in digit order
+    __shared__ uint32_t s_vals[kSortPart];
+    __shared__ uint32_t s_wsum[kRadix / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (p.skip && *p.skip != 0u) return;  // the list overflowed or the depth sort failed
+    uint32_t count = p.count_dev ? *p.count_dev : p.count_host;
+    if (count > p.cap) count = p.cap;
+    // Blocks go to the 8 XCDs round-robin; give each XCD a contiguous range of
+    // partitions, so that the output runs of one digit from neighbouring
+    // partitions meet in one L2 and leave it as whole lines.
+    const uint32_t per_xcd = gridDim.x / kXcds;  // the grid is a multiple of kXcds
+    const uint32_t part = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (part * (uint32_t)kSortPart >= count) return;  // uniform over the block
+    const uint32_t vm = (p.vmw[0] ^ (~p.vmw[1] & 255u)) & 255u;  // bits in which the digits differ
+    for (int i = tid; i < kWaves * kRadix; i += THREADS) (&s_wave[0][0])[i] = 0;
+    const uint32_t base = part * kSortPart + wave * 64 * IPT;
+    uint32_t key[IPT], val[IPT], rank[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const uint32_t idx = base + i * 64 + lane;
+        key[i] = idx < count ? (uint32_t) static_cast<const KeyT*>(p.keys_in)[idx] : 0u;
+        val[i] = idx < count ? p.vals_in[idx] : 0u;
+    }
+    // digit thread d: output position of this partition's first item of digit d
+    const uint32_t first = tid < kRadix ? p.prefix[(size_t)tid * p.stride + (size_t)part * p.cols_per_part] : 0u;
+    __syncthreads();
+    const uint64_t lt = lanemask_lt();
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const bool valid = (base + i * 64 + lane) < count;
+        const uint32_t d = (key[i] >> p.shift) & 255u;
+        const uint64_t m = match_digits(d, valid, vm);
+        const uint32_t below = (uint32_t)__popcll(m & lt);
+        const uint32_t prev = valid ? s_wave[wave][d] : 0u;
+        rank[i] = prev + below;
+        __builtin_amdgcn_wave_barrier();
+        if (valid && below == 0) s_wave[wave][d] = prev + (uint32_t)__popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    uint32_t total = 0, tx = 0;
+    if (tid < kRadix) {
+        const int d = tid;
+        uint32_t run = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t c = s_wave[w][d];
+            s_wave[w][d] = run;
+            run += c;
+        }
+        total = run;
+        tx = wave_incl_sum(total);
+        if (lane == 63) s_wsum[wave] = tx;
+    }
+    __syncthreads();
+    if (tid < kRadix) {
+        const int d = tid;
+        uint32_t add = 0;
+        for (int w = 0; w < wave; ++w) add += s_wsum[w];
+        const uint32_t blk = tx - total + add;
+        s_blk[d] = blk;
+        s_base[d] = first - blk;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        if (base + i * 64 + lane < count) {
+            const uint32_t d = (key[i] >> p.shift) & 255u;
+            const uint32_t q = s_blk[d] + s_wave[wave][d] + rank[i];
+            if (q < (uint32_t)kSortPart) {  // always true for a consistent ranking
+                s_keys[q] = (KeyT)key[i];
+                s_vals[q] = val[i];
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t nloc = min((uint32_t)kSortPart, count - part * kSortPart);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        const uint32_t q = (uint32_t)(i * THREADS + tid);
+        if (q < nloc) {
+            const uint32_t kq = (uint32_t)s_keys[q];
+            const uint32_t pos = s_base[(kq >> p.shift) & 255u] + q;
+            if (pos < count) {  // always true for consistent counts; guards the buffers
+                if (p.keys_out) static_cast<KeyT*>(p.keys_out)[pos] = (KeyT)kq;
+                p.vals_out[pos] = s_vals[q];
+            }
+        }
+    }
 }
 
 __device__ inline uint32_t tiles_of(const EmitArgs& a, int64_t j) {
@@ -535,6 +774,8 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
     const uint32_t base = blockIdx.x * (uint32_t)kSlots;
     const bool active = !*a.overflow && base < K;
     for (int i = tid; i < 2 * kRadix; i += kEmitThreads) s_hist[i] = 0;
+    if (!active)  // the tile sort reads every block's counts
+        for (int i = tid; i < kRadix; i += kEmitThreads) a.tcnt0[(size_t)blockIdx.x * kRadix + i] = 0u;
     if (active) {
         const uint32_t nout = min((uint32_t)kSlots, K - base);
         const uint32_t jb = a.bstart[blockIdx.x];
@@ -603,8 +844,10 @@ __global__ __launch_bounds__(kEmitThreads) void k_emit_expand(EmitArgs a) {
         }
         __syncthreads();
         uint32_t* out = a.stripes + (size_t)(blockIdx.x % kStripes) * kHistBins + 4 * kRadix;
-        for (int i = tid; i < 2 * kRadix; i += kEmitThreads)
+        for (int i = tid; i < 2 * kRadix; i += kEmitThreads) {
             if (s_hist[i]) atomicAdd(&out[i], s_hist[i]);
+            if (i < kRadix) a.tcnt0[(size_t)blockIdx.x * kRadix + i] = s_hist[i];
+        }
     }
 }
 
@@ -728,7 +971,7 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
 
     uint32_t* tickets = U(L.tickets);
     auto ticket = [&](int pass) { return tickets + (size_t)pass * kTicketGroups * kTicketStride; };
-    uint32_t* err = U(L.err);  // bit p: sort pass p gave up (passes 0-3 depth, 4-5 tile)
+    uint32_t* err = U(L.err);  // bit p: depth sort pass p gave up
     const uint32_t wait_limit = g_wait_limit.load();
     const int key_blocks = (int)((n + 256 * kKeyIPT - 1) / (256 * kKeyIPT));
     hipLaunchKernelGGL(k_depth_keys, dim3(key_blocks), dim3(256), 0, s, n, depth, tiles_touched, U(L.dkeys0),
@@ -761,29 +1004,37 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
     e.order = dv[0]; e.rect = rect; e.tt = tiles_touched;
     e.part = U(L.etotal); e.goff = U(L.goff); e.bstart = U(L.bstart);
     e.tkeys = H(L.tkeys0); e.tvals = tile_passes == 1 ? U(L.tvals0) : point_list;
-    e.stripes = U(L.stripes);
+    e.stripes = U(L.stripes); e.tcnt0 = U(L.tcnt0);
     e.num_keys = num_keys_dev; e.overflow = overflow_dev; e.err = err;
     hipLaunchKernelGGL(k_emit_count, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
     hipLaunchKernelGGL(k_emit_offsets, dim3(L.eparts), dim3(kEmitThreads), 0, s, e);
     if (key_capacity == 0) return launch_status();
     hipLaunchKernelGGL(k_emit_expand, dim3(L.xblocks), dim3(kEmitThreads), 0, s, e);
-    PassArgs p;
+    // the tile passes: offsets from the partition counts, then a scatter per digit;
+    // everything skips when the emission found an overflow or a failed depth sort
+    uint32_t* vmw = U(L.vmw);
+    hipLaunchKernelGGL(k_digit_scan, dim3(kRadix), dim3(kRadix), 0, s, (const uint32_t*)U(L.stripes), 4 * kRadix,
+                       (const uint32_t*)U(L.tcnt0), U(L.tpre0), L.xblocks, vmw, (const uint32_t*)overflow_dev);
+    PassArgs p = {};
     p.count_dev = num_keys_dev; p.count_host = 0; p.cap = (uint32_t)key_capacity;
-    // the tile passes skip when the emission found an overflow or a failed depth sort
-    p.err = err; p.err_bit = 1u << 4; p.err_before = 0u; p.skip = overflow_dev; p.wait_limit = wait_limit;
+    p.skip = overflow_dev;
     p.keys_in = H(L.tkeys0); p.vals_in = e.tvals;
     p.keys_out = H(L.tkeys1); p.vals_out = tile_passes == 1 ? point_list : U(L.tvals0);
-    p.stripes = U(L.stripes); p.hist_bin = 4 * kRadix; p.status = U(L.tstatus); p.ticket = ticket(4); p.shift = 0;
-    hipLaunchKernelGGL((k_onesweep<kTileThreads, kTileIPT, uint16_t>), dim3(L.tparts), dim3(kTileThreads), 0, s, p);
+    p.shift = 0; p.prefix = U(L.tpre0); p.stride = L.xblocks; p.cols_per_part = kTilePart / kSlots; p.vmw = vmw;
+    const uint32_t sgrid = (L.tparts + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((k_pass_scatter<kTileThreads, kTileIPT, uint16_t>), dim3(sgrid), dim3(kTileThreads), 0, s, p);
     const uint16_t* tk_final = H(L.tkeys1);
     if (tile_passes == 2) {
+        hipLaunchKernelGGL((k_digit_count<kTileThreads, kTileIPT>), dim3(L.tparts), dim3(kTileThreads), 0, s,
+                           (const uint16_t*)H(L.tkeys1), (const uint32_t*)num_keys_dev, (uint32_t)key_capacity, 8,
+                           U(L.tcnt1), (const uint32_t*)overflow_dev);
+        hipLaunchKernelGGL(k_digit_scan, dim3(kRadix), dim3(kRadix), 0, s, (const uint32_t*)U(L.stripes), 5 * kRadix,
+                           (const uint32_t*)U(L.tcnt1), U(L.tpre1), L.tparts, vmw + 2, (const uint32_t*)overflow_dev);
         PassArgs p2 = p;
         p2.keys_in = H(L.tkeys1); p2.vals_in = U(L.tvals0);
         p2.keys_out = H(L.tkeys0); p2.vals_out = point_list;
-        p2.hist_bin = 5 * kRadix; p2.status = U(L.tstatus) + (size_t)L.tparts * kRadix;
-        p2.ticket = ticket(5); p2.shift = 8;
-        p2.err_bit = 1u << 5; p2.err_before = 1u << 4;
-        hipLaunchKernelGGL((k_onesweep<kTileThreads, kTileIPT, uint16_t>), dim3(L.tparts), dim3(kTileThreads), 0, s, p2);
+        p2.shift = 8; p2.prefix = U(L.tpre1); p2.stride = L.tparts; p2.cols_per_part = 1; p2.vmw = vmw + 2;
+        hipLaunchKernelGGL((k_pass_scatter<kTileThreads, kTileIPT, uint16_t>), dim3(sgrid), dim3(kTileThreads), 0, s, p2);
         tk_final = H(L.tkeys0);
     }
     const uint32_t rblocks = (uint32_t)((key_capacity + 256 * kRangeIPT - 1) / (256 * kRangeIPT));

@@ -131,9 +131,9 @@ int gs_bin_workspace_size(int32_t n, const gs_camera* cam, int64_t key_capacity,
  * call does not read it back).  *overflow_dev [1] uint32 receives a status word:
  *   0      the lists and ranges are valid;
  *   bit 0  K > key_capacity: retry with a capacity of at least K;
- *   bit 1  a pass of the radix sort gave up waiting for the partitions before
- *          it (see gs_debug_sort_wait_limit; not expected in normal operation):
- *          the sort is void and a retry may succeed.
+ *   bit 1  a pass of the depth radix sort gave up waiting for the partitions
+ *          before it (see gs_debug_sort_wait_limit; not expected in normal
+ *          operation): the sort is void and a retry may succeed.
  * When the word is not 0, every range is written empty and point_list holds no
  * valid list.  The caller checks the word after its next synchronisation.
  * workspace: device scratch of at least gs_bin_workspace_size() bytes, 256-byte
@@ -149,10 +149,10 @@ int gs_bin_sort(const gs_camera* cam, int32_t n, const float* depth, const int16
 
 /*
  * gs_debug_sort_wait_limit -- test hook for the sort's failure report.  Each
- * radix-sort pass (an LSD "onesweep" pass: partitions add their digit counts to
- * a running prefix published by the partitions before them) waits a bounded
- * number of times for a predecessor's prefix; past the limit the partition
- * gives up and the call reports bit 1 in *overflow_dev.  Sets the limit for
+ * pass of the depth radix sort (an LSD "onesweep" pass: partitions add their
+ * digit counts to a running prefix published by the partitions before them)
+ * waits a bounded number of times for a predecessor's prefix; past the limit
+ * the partition gives up and the call reports bit 1 in *overflow_dev.  Sets the limit for
  * later gs_bin_sort calls in this process (limit < 0: leave it) and returns
  * the previous one.  Default 4194304 waits; 0 makes every partition but the
  * first give up at once, so a sort deterministically reports failure while
