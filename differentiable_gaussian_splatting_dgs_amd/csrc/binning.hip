@@ -55,6 +55,7 @@ constexpr int kRangeIPT = 8;                        // tile-range pass: keys per
 constexpr int kStripes = 32;                        // histogram copies that blocks add into
 constexpr int kHistBins = 6 * 256;                  // 4 depth digits + 2 tile digits
 constexpr int kLookWindow = 8;                      // predecessors read at once per digit
+constexpr uint32_t kLookGroup = 16;                 // partitions per look-back group
 constexpr int kRadix = 256;
 constexpr uint32_t kXcds = 8;                       // accelerator complex dies: blocks are dealt to them round-robin
 constexpr uint32_t kFlagAgg = 1u << 30;
@@ -131,6 +132,7 @@ struct Layout {
     size_t tickets;     // uint32 [4 depth passes][kTicketGroups][kTicketStride] partition tickets
     size_t err;         // uint32 [1] look-back spin-limit flag
     size_t dstatus;     // uint32 [4][dparts][256]
+    size_t dgstatus;    // uint32 [4][dgroups][256]
     size_t etotal;      // uint32 [eparts] entries per emit partition, then their exclusive offsets
     size_t vmw;         // uint32 [2 passes][2] OR of the tile digits present, OR of their complements
     size_t zero_end;    // everything above is zeroed per call
@@ -157,6 +159,7 @@ inline Layout make_layout(int32_t n, int64_t cap) {
     L.tickets = o; o = up256(o + (size_t)4 * kTicketGroups * kTicketStride * 4);
     L.err = o; o = up256(o + 4);
     L.dstatus = o; o = up256(o + (size_t)4 * L.dparts * kRadix * 4);
+    L.dgstatus = o; o = up256(o + (size_t)4 * ((L.dparts + kLookGroup - 1) / kLookGroup) * kRadix * 4);
     L.etotal = o; o = up256(o + (size_t)L.eparts * 4);
     L.vmw = o; o = up256(o + 4 * 4);
     L.stripes = o; o = up256(o + (size_t)kStripes * kHistBins * 4);
@@ -244,6 +247,7 @@ struct PassArgs {
     const uint32_t* stripes;  // striped digit counts; this pass's bins start at hist_bin
     int hist_bin;
     uint32_t* status;      // [parts][256], zeroed
+    uint32_t* gstatus;     // [groups of kLookGroup parts][256], zeroed
     uint32_t* ticket;      // [kTicketGroups][kTicketStride], zeroed
     uint32_t* err;         // bit p set when a partition of pass p gave up waiting for its predecessors
     uint32_t err_bit;      // this pass's bit
@@ -375,45 +379,92 @@ __global__ __launch_bounds__(THREADS) void k_onesweep(PassArgs p) {
         const uint32_t blk = tx - total + add;
         s_blk[d] = blk;
 
-        // decoupled look-back over the earlier partitions
-        uint32_t* st = p.status + (size_t)part * kRadix + d;
-        uint32_t prefix = 0;
-        if (part == 0) {
-            st_release(st, kFlagInc | total);
-        } else {
-            st_release(st, kFlagAgg | total);
-            // look back with kLookWindow loads in flight; partitions below 0 read
-            // as an inclusive prefix of 0
-            int j = (int)part - 1;
-            uint32_t spins = 0;
-            while (true) {
-                if (spins >= p.wait_limit) {  // give up: the pass's result is void and flagged
-                    atomicOr(p.err, p.err_bit);
-                    break;
-                }
-                uint32_t sv[kLookWindow];
+        // Two-level look-back.  Every partition publishes its own digit count.  The
+        // last partition of each group of kLookGroup adds up its group, publishes the
+        // group's count and looks back over the earlier groups for the group's
+        // inclusive prefix.  Every other partition needs only the counts of its
+        // group's earlier partitions and the previous group's inclusive prefix.  All
+        // waits are on lower partitions, claimed earlier, and bounded.
+        const uint32_t grp = part / kLookGroup, first = grp * kLookGroup;
+        const uint32_t last = min(first + kLookGroup, nparts) - 1u;
+        st_release(p.status + (size_t)part * kRadix + d, kFlagAgg | total);
+        uint32_t spins = 0;
+        bool failed = false;
+        auto give_up = [&]() {  // the pass's result is void and flagged
+            atomicOr(p.err, p.err_bit);
+            failed = true;
+        };
+        if (part > 0 && p.wait_limit == 0) give_up();  // a limit of 0: every partition but the first gives up at once
+        // counts of the group's partitions before this one, kLookWindow loads in flight
+        uint32_t within = 0;
+        for (uint32_t q = first; q < part && !failed;) {
+            uint32_t sv[kLookWindow];
 #pragma unroll
-                for (int w = 0; w < kLookWindow; ++w)
-                    sv[w] = j - w >= 0 ? ld_acquire(p.status + (size_t)(j - w) * kRadix + d) : kFlagInc;
-                int used = 0;
-                bool found = false, stall = false;
+            for (int w = 0; w < kLookWindow; ++w)
+                sv[w] = q + w < part ? ld_acquire(p.status + (size_t)(q + w) * kRadix + d) : kFlagAgg;
+            bool stall = false;
 #pragma unroll
-                for (int w = 0; w < kLookWindow; ++w) {
-                    if (found || stall) continue;
-                    if ((sv[w] & ~kValMask) == 0u) { stall = true; continue; }
-                    prefix += sv[w] & kValMask;
-                    ++used;
-                    if (sv[w] & kFlagInc) found = true;
-                }
-                if (found) break;
-                j -= used;
-                if (stall) {
-                    ++spins;
-                    __builtin_amdgcn_s_sleep(1);
-                }
+            for (int w = 0; w < kLookWindow; ++w) {
+                if (stall || q + w >= part) continue;
+                if ((sv[w] & ~kValMask) == 0u) { stall = true; continue; }
+                within += sv[w] & kValMask;
             }
-            st_release(st, kFlagInc | ((prefix + total) & kValMask));
+            uint32_t adv = 0;
+#pragma unroll
+            for (int w = 0; w < kLookWindow; ++w)
+                if (adv == (uint32_t)w && q + w < part && (sv[w] & ~kValMask) != 0u) ++adv;
+            q += adv;
+            if (stall) {
+                if (++spins >= p.wait_limit) give_up();
+                __builtin_amdgcn_s_sleep(1);
+            }
         }
+        uint32_t gprefix = 0;
+        uint32_t* gst = p.gstatus + (size_t)grp * kRadix + d;
+        if (part == last) {
+            const uint32_t gtotal = within + total;
+            if (grp == 0) {
+                st_release(gst, kFlagInc | gtotal);
+            } else {
+                st_release(gst, kFlagAgg | gtotal);
+                // look back over the groups with kLookWindow loads in flight; groups
+                // below 0 read as an inclusive prefix of 0
+                int j = (int)grp - 1;
+                while (!failed) {
+                    uint32_t sv[kLookWindow];
+#pragma unroll
+                    for (int w = 0; w < kLookWindow; ++w)
+                        sv[w] = j - w >= 0 ? ld_acquire(p.gstatus + (size_t)(j - w) * kRadix + d) : kFlagInc;
+                    int used = 0;
+                    bool found = false, stall = false;
+#pragma unroll
+                    for (int w = 0; w < kLookWindow; ++w) {
+                        if (found || stall) continue;
+                        if ((sv[w] & ~kValMask) == 0u) { stall = true; continue; }
+                        gprefix += sv[w] & kValMask;
+                        ++used;
+                        if (sv[w] & kFlagInc) found = true;
+                    }
+                    if (found) break;
+                    j -= used;
+                    if (stall) {
+                        if (++spins >= p.wait_limit) give_up();
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
+                st_release(gst, kFlagInc | ((gprefix + gtotal) & kValMask));
+            }
+        } else if (grp > 0) {
+            // the previous group's inclusive prefix
+            const uint32_t* pg = p.gstatus + (size_t)(grp - 1) * kRadix + d;
+            while (!failed) {
+                const uint32_t v = ld_acquire(pg);
+                if (v & kFlagInc) { gprefix = v & kValMask; break; }
+                if (++spins >= p.wait_limit) give_up();
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        const uint32_t prefix = gprefix + within;
         // global position of local slot q (digit d) = s_base[d] + q
         s_base[d] = s_off[d] + prefix - blk;
     }
@@ -987,6 +1038,7 @@ extern "C" int gs_bin_sort_views(const gs_camera* cams, int32_t views, int32_t n
         p.count_dev = nullptr; p.count_host = (uint32_t)n; p.cap = (uint32_t)n;
         p.stripes = U(L.stripes); p.hist_bin = pass * kRadix;
         p.status = U(L.dstatus) + (size_t)pass * L.dparts * kRadix;
+        p.gstatus = U(L.dgstatus) + (size_t)pass * ((L.dparts + kLookGroup - 1) / kLookGroup) * kRadix;
         p.ticket = ticket(pass);
         p.err = err; p.err_bit = 1u << pass; p.err_before = (1u << pass) - 1u; p.skip = nullptr;
         p.wait_limit = wait_limit;
