@@ -33,6 +33,28 @@ pytestmark = pytest.mark.gpu
 B1, B2, EPS = (float(np.float32(x)) for x in (0.9, 0.999, 1e-8))
 
 
+def _loop_bars(cam, deg, params, tt, g2o, g3o, s):
+    """Per-tensor relative L2 bars of a training-loop check: 1e-3, or the error a float32 evaluation
+    of the same gradients can carry, whichever is larger.  Each 2D gradient component is a sum of
+    per-pixel terms (the oracle's `abs` holds their absolute sizes); rounding each term to float32
+    moves it by a few units of 2^-24 of its size, so the model perturbs every component by
+    4 * 2^-24 of its terms' size with random signs and takes the 3D chain of that perturbation
+    (linear for fixed parameters), the largest of four draws.  Early iterations give a model far
+    under 1e-3; after thousands of iterations towards one target the gradients are sums of terms
+    that cancel (the mean gradients by a factor of thousands), and the model rises above it."""
+    from oracle import oracle as O
+    from gpu_cases import grad2d_dict
+    a = np.asarray(g2o["abs"], np.float64)
+    rng = np.random.default_rng(0)
+    bars = {k: 1e-3 for k in PARAM_KEYS}
+    for _ in range(4):
+        d = 4.0 * 2.0 ** -24 * a * rng.choice([-1.0, 1.0], a.shape)
+        d3 = O.preprocess_bwd(cam, deg, params, tt, grad2d_dict(d), s)
+        for k in PARAM_KEYS:
+            bars[k] = max(bars[k], float(np.linalg.norm(d3[k]) / max(np.linalg.norm(g3o[k]), 1e-300)))
+    return bars
+
+
 def _oracle_adam(O, params, g3, lr, deg):
     """The oracle's step-1 Adam on every group, SH band 0 and the higher bands at their own rates,
     then the quaternion renormalisation."""
@@ -152,7 +174,10 @@ def test_training_loop_across_densify_and_reset():
     right after them (the first at the new N), and the reset at 3000 -- the oracle recomputes the
     iteration from the GPU state before it, stage by stage: image, loss sign, 3D gradients, the
     Adam update from the GPU's gradients, the statistic, the densification from the GPU's
-    updated state, and the reset."""
+    updated state, and the reset.  The 3D gradients meet 1e-3 relative L2 per tensor, or the
+    float32 error model of _loop_bars where the state's gradients are sums of cancelling terms;
+    every 2D component stays within 1e-3 of its terms' size and every chain row within the
+    chain guard."""
     import json
     import os
     import torch
@@ -214,8 +239,11 @@ def test_training_loop_across_densify_and_reset():
                      **{"g_" + k: v for k, v in seen["g"].items()})
         guard_2d(seen["g2"], g2o, f"t={t}")
         guard_chain(sc.cam, deg, params, seen["tt"], seen["g2"], seen["g"], f"t={t}")
+        bars = _loop_bars(sc.cam, deg, params, o["pre"]["tiles_touched"], g2o, g3o, s)
         for k in PARAM_KEYS:
-            assert rel_l2(seen["g"][k], g3o[k]) <= 1e-3, (t, k)
+            e = rel_l2(seen["g"][k], g3o[k])
+            assert e <= bars[k], (t, k, e, bars[k])
+        log(f"t={t}: relative L2 bars {', '.join(f'{k} {v:.1e}' for k, v in bars.items())}")
         # Adam at iteration t from the GPU's own gradients: the update's arithmetic alone
         post = seen["post"]
         for k in PARAM_KEYS:
