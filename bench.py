@@ -168,9 +168,10 @@ def kernel_roofline(stage_ms, p_fwd, p_bwd, p_blend, peaks, workload):
 
 
 def walked_entries(r):
-    """List entries the backward blend walks with at least one flagged quadrant: each
-    costs one nine-value reduction and nine float atomics (two entries share one
-    atomic instruction).  Counted on the device from the last pass's buffers."""
+    """List entries the backward blend walks with at least one flagged quadrant (each
+    costs one nine-value reduction and nine float atomics; two entries share one
+    atomic instruction) and the flagged quadrants of those entries (each a 64-pixel
+    recursion step).  Counted on the device from the last pass's buffers."""
     import torch
     K = int(r.num_keys.item())
     T = r.ntiles
@@ -181,8 +182,10 @@ def walked_entries(r):
     ncmax = nc.view(r.tiles_y, 16, r.tiles_x, 16).amax(dim=(1, 3)).reshape(-1).long()
     tile_of = torch.repeat_interleave(torch.arange(T, device=rng.device), rng[:, 1] - rng[:, 0])
     pos = torch.arange(K, device=rng.device) - rng[tile_of, 0]
-    walked = (pos < ncmax[tile_of]) & (r.contrib[:K] != 0)
-    return int(walked.sum().item())
+    flags = r.contrib[:K].long()
+    walked = (pos < ncmax[tile_of]) & (flags != 0)
+    quads = ((flags & 1) + ((flags >> 1) & 1) + ((flags >> 2) & 1) + ((flags >> 3) & 1)) * walked
+    return int(walked.sum().item()), int(quads.sum().item())
 
 
 class RasterPass:
@@ -301,7 +304,7 @@ def raster_line(name, steps, warmup, peaks):
     stage_ms = dict(zip(STAGES, stage))
     timed_ms = dict(stage_ms, render_bwd=bwd_ms)  # the backward blend as timed inside the timed passes
     K = float(r.num_keys.item())
-    entries = walked_entries(r)
+    entries, quads = walked_entries(r)
     line = dict(metric=METRIC, value=(p_fwd + p_bwd) / (ms * 1e-3), unit="blend pairs/s", n_gpus=1, steps=steps,
                 warmup=warmup, ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
                 dtype="f32", data="synthetic",
@@ -314,7 +317,7 @@ def raster_line(name, steps, warmup, peaks):
                 pairs=dict(fwd_evaluated=p_fwd, bwd_walked=p_bwd, blended=p_blend, keys=int(K)),
                 blend=dict(fwd_pairs_per_s=p_fwd / (stage_ms["render_fwd"] * 1e-3),
                            bwd_pairs_per_s=p_bwd / (stage_ms["render_bwd"] * 1e-3),
-                           bwd_walked_entries=entries, bwd_float_atomics=9 * entries,
+                           bwd_walked_entries=entries, bwd_walked_quadrants=quads, bwd_float_atomics=9 * entries,
                            bwd_atomics_per_s=9 * entries / (stage_ms["render_bwd"] * 1e-3)),
                 stage_roofline=raster_roofline(sc.n, K, sc.sh_degree, p_fwd, p_bwd, p_blend, ms, peaks),
                 roofline=kernel_roofline(timed_ms, p_fwd, p_bwd, p_blend, peaks, name),

@@ -430,6 +430,128 @@ __device__ __forceinline__ float reduce2x9(float a[9], float b[9], float& z, int
     return w;
 }
 
+// ---- backward walk of one entry, specialised on its quadrant mask (QPW = 4) ----
+// One staged entry as the walk reads it (s_g0, s_g1, s_g2 of the backward).
+struct BwdEntry {
+    float4 g0, g1, g2;
+};
+
+// Per-lane state of a wave that owns all four quadrants of its tile: pixel q of
+// the lane has inverse transmittance U[q] = 1 / T, S[q] = dL/dpixel . C_next,
+// dL/dpixel gp*[q], last contributor nc[q]; its centre is (fx[q & 1], fy[q >> 1]).
+// Walking back over an entry, U <- (1 - alpha) U is one fused multiply-add,
+// where T <- T / (1 - alpha) would take a subtraction and a reciprocal besides
+// the product; T itself is then one reciprocal of U.
+struct BwdLane4 {
+    float U[4], S[4], gp0[4], gp1[4], gp2[4];
+    int nc[4];
+    float fx[2], fy[2];
+};
+
+// One flagged quadrant Q of entry E at list position pos.  e1r and pr are the
+// row terms of eval_pair (L10 y + c1 and e2^2 - log2 opacity), dx and dy the
+// pixel's offset from the mean, so alpha and the blend decision are those of
+// eval_pair bit for bit.  FIRST: the first flagged quadrant of the entry, which
+// writes the nine accumulators instead of adding to them.  CL: the entry's
+// opacity can exceed alpha_max, so opacity G may be clamped; otherwise
+// alpha = opacity G wherever the pair blends, and the clamp test drops out.
+template <int Q, bool FIRST, bool CL>
+__device__ __forceinline__ void bwd_quad(BwdLane4& L, const BwdEntry& E, int pos, float e1r, float pr, float dx,
+                                         float dy, float amin, float amax, float v[9]) {
+    const float e1 = __builtin_fmaf(E.g0.x, L.fx[Q & 1], e1r);
+    const float sG = __builtin_amdgcn_exp2f(-__builtin_fmaf(e1, e1, pr));
+    const float alpha = __builtin_amdgcn_fmed3f(sG, 0.f, amax);
+    const bool ok = pos < L.nc[Q] && alpha >= amin;
+    const float ae = ok ? alpha : 0.f;
+    L.U[Q] = __builtin_fmaf(-ae, L.U[Q], L.U[Q]);  // before the entry; unchanged where ae = 0
+    const float T = __builtin_amdgcn_rcpf(L.U[Q]);
+    const float w = ae * T;
+    const float gc = __builtin_fmaf(L.gp2[Q], E.g2.x, __builtin_fmaf(L.gp1[Q], E.g1.w, L.gp0[Q] * E.g1.z));
+    const float dS = gc - L.S[Q];
+    const float dalpha = T * dS;
+    L.S[Q] = __builtin_fmaf(ae, dS, L.S[Q]);
+    float dpow;  // dL/dpower = dL/d(opacity G) opacity G
+    if constexpr (CL) {
+        const float dsG = (ok && !(sG > amax)) ? dalpha : 0.f;  // clamped: no dependence
+        dpow = dsG * sG;
+    } else {
+        dpow = dalpha * ae;  // ae = opacity G where the pair blends, 0 elsewhere
+    }
+    const float t = dpow * dx, sy = dpow * dy;
+    if constexpr (FIRST) {
+        v[0] = t;
+        v[1] = sy;
+        v[2] = t * dx;
+        v[3] = t * dy;
+        v[4] = sy * dy;
+        v[5] = dpow;
+        v[6] = w * L.gp0[Q];
+        v[7] = w * L.gp1[Q];
+        v[8] = w * L.gp2[Q];
+    } else {
+        v[0] += t;
+        v[1] += sy;
+        v[2] = __builtin_fmaf(t, dx, v[2]);
+        v[3] = __builtin_fmaf(t, dy, v[3]);
+        v[4] = __builtin_fmaf(sy, dy, v[4]);
+        v[5] += dpow;
+        v[6] = __builtin_fmaf(w, L.gp0[Q], v[6]);
+        v[7] = __builtin_fmaf(w, L.gp1[Q], v[7]);
+        v[8] = __builtin_fmaf(w, L.gp2[Q], v[8]);
+    }
+}
+
+// The quadrants of mask M (a compile-time constant): the row terms are computed
+// once per row and the column terms once per column that a flagged quadrant uses.
+template <int M, bool CL>
+__device__ __forceinline__ void bwd_mask(BwdLane4& L, const BwdEntry& E, int pos, float amin, float amax,
+                                         float v[9]) {
+    float e1r[2] = {0.f, 0.f}, pr[2] = {0.f, 0.f}, dy[2] = {0.f, 0.f}, dx[2] = {0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+        if ((M >> (2 * r)) & 3) {
+            e1r[r] = __builtin_fmaf(E.g0.y, L.fy[r], E.g0.w);
+            const float e2 = __builtin_fmaf(E.g0.z, L.fy[r], E.g1.x);
+            pr[r] = __builtin_fmaf(e2, e2, E.g1.y);
+            dy[r] = L.fy[r] - E.g2.z;
+        }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+        if ((M >> c) & 5) dx[c] = L.fx[c] - E.g2.y;
+    if constexpr ((M & 1) != 0) bwd_quad<0, true, CL>(L, E, pos, e1r[0], pr[0], dx[0], dy[0], amin, amax, v);
+    if constexpr ((M & 2) != 0) bwd_quad<1, (M & 1) == 0, CL>(L, E, pos, e1r[0], pr[0], dx[1], dy[0], amin, amax, v);
+    if constexpr ((M & 4) != 0) bwd_quad<2, (M & 3) == 0, CL>(L, E, pos, e1r[1], pr[1], dx[0], dy[1], amin, amax, v);
+    if constexpr ((M & 8) != 0) bwd_quad<3, (M & 7) == 0, CL>(L, E, pos, e1r[1], pr[1], dx[1], dy[1], amin, amax, v);
+}
+
+// Entry E with quadrant mask m (wave-uniform) into v; no quadrant (m = 0) leaves
+// the additive identity -0 in every accumulator.
+template <bool CL>
+__device__ __forceinline__ void bwd_walk4(BwdLane4& L, const BwdEntry& E, uint32_t m, int pos, float amin,
+                                          float amax, float v[9]) {
+    switch (m) {
+        case 1: bwd_mask<1, CL>(L, E, pos, amin, amax, v); break;
+        case 2: bwd_mask<2, CL>(L, E, pos, amin, amax, v); break;
+        case 3: bwd_mask<3, CL>(L, E, pos, amin, amax, v); break;
+        case 4: bwd_mask<4, CL>(L, E, pos, amin, amax, v); break;
+        case 5: bwd_mask<5, CL>(L, E, pos, amin, amax, v); break;
+        case 6: bwd_mask<6, CL>(L, E, pos, amin, amax, v); break;
+        case 7: bwd_mask<7, CL>(L, E, pos, amin, amax, v); break;
+        case 8: bwd_mask<8, CL>(L, E, pos, amin, amax, v); break;
+        case 9: bwd_mask<9, CL>(L, E, pos, amin, amax, v); break;
+        case 10: bwd_mask<10, CL>(L, E, pos, amin, amax, v); break;
+        case 11: bwd_mask<11, CL>(L, E, pos, amin, amax, v); break;
+        case 12: bwd_mask<12, CL>(L, E, pos, amin, amax, v); break;
+        case 13: bwd_mask<13, CL>(L, E, pos, amin, amax, v); break;
+        case 14: bwd_mask<14, CL>(L, E, pos, amin, amax, v); break;
+        case 15: bwd_mask<15, CL>(L, E, pos, amin, amax, v); break;
+        default:
+#pragma unroll
+            for (int i = 0; i < 9; ++i) v[i] = -0.f;
+            break;
+    }
+}
+
 // Backward: one wave64 per tile (QPW = 4), each lane owning one pixel of each of
 // the four 8x8 quadrants (pixel q of lane l sits at ((q & 1) 8 + l % 8,
 // (q >> 1) 8 + l / 8)); or, for images with few tiles, two waves per tile
@@ -450,6 +572,7 @@ __device__ __forceinline__ float reduce2x9(float a[9], float b[9], float& z, int
 // times the second moments, and dL/dopacity = sum dpow / opacity (dpower is
 // dL/d(opacity G) times opacity G).
 constexpr int kBwdBatch = 64;
+constexpr uint32_t kBwdClamp = 1u << 12;  // list flag: the entry's opacity can exceed alpha_max
 // Below this many tiles the backward runs two waves per tile: with one wave per
 // tile some of the 1024 SIMDs (256 CUs) would have none.  Above it the second
 // reduction and atomic update per entry cost more than the extra waves give.
@@ -461,10 +584,10 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     constexpr int kSplit = 4 / QPW;
     __shared__ float4 s_g0[kBwdBatch];   // L00, L10, L11, c1 (stage_record)
     __shared__ float4 s_g1[kBwdBatch];   // c2, -log2 opacity, r, g
-    __shared__ float4 s_g2[kBwdBatch];   // b, tile-relative mean (u, v), 1 / opacity
-    __shared__ float4 s_g3[kBwdBatch];   // conic A, B, C (for the mean gradient after the reduction), 0
-    __shared__ uint32_t s_gid[kBwdBatch];
-    __shared__ uint16_t s_list[kBwdBatch];  // slot | quadrant mask << 8, in walk order
+    __shared__ float4 s_g2[kBwdBatch];   // b, tile-relative mean (u, v), 0
+    // after the reduction: conic A, C, 1 / opacity, conic B, then the Gaussian's index (bits)
+    __shared__ float4 s_tab[2 * kBwdBatch];
+    __shared__ uint16_t s_list[kBwdBatch];  // slot | quadrant mask << 8 | kBwdClamp, in walk order
 
     const BlendArgs& b = a.b;
     const int ntv = b.tiles_x * b.tiles_y;
@@ -477,13 +600,17 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     const float x0 = (float)(tx * kTile), y0 = (float)(ty * kTile);
     const uint2 range = reinterpret_cast<const uint2*>(a.ranges)[tile];
     constexpr float k2ln2 = 1.3862943611198906f;  // conic = 2 ln2 L L^T
+    // an entry whose opacity is at most this has opacity G < alpha_max at every
+    // pixel: G <= 1, and the float exponent and logarithm are within a few ulp
+    const float op_noclamp = b.alpha_max * (1.f - 1.f / 65536.f);
 
-    // Per pixel: T, S = dL/dpixel . C_next (the colour accumulated behind the
+    // Per pixel: U = 1 / T, S = dL/dpixel . C_next (the colour accumulated behind the
     // current entry, starting at the background), dL/dpixel and the centre.
     // dL/dalpha = T (dL/dpixel . c - S) and S <- S + alpha (dL/dpixel . c - S)
     // is C_next <- alpha c + (1 - alpha) C_next dotted with dL/dpixel.
-    float T[QPW], S[QPW], gp0[QPW], gp1[QPW], gp2[QPW], fxq[QPW], fyq[QPW];
-    int nc[QPW];
+    // Pixel q of the lane (q < QPW) is in quadrant qbase + q at (fx[q & 1], fy[q >> 1]).
+    BwdLane4 L;
+    L.fy[1] = 0.f;
     int ncmax = 0;
     const size_t plane = (size_t)b.width * b.height;
 #pragma unroll
@@ -491,55 +618,62 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
         const int qg = qbase + q;
         const int lx = (qg & 1) * 8 + (lane & 7), ly = (qg >> 1) * 8 + (lane >> 3);
         const int px = tx * kTile + lx, py = ty * kTile + ly;
-        fxq[q] = (float)lx + 0.5f;
-        fyq[q] = (float)ly + 0.5f;
-        T[q] = 1.f; nc[q] = 0; gp0[q] = gp1[q] = gp2[q] = 0.f;
+        L.fx[q & 1] = (float)lx + 0.5f;
+        L.fy[q >> 1] = (float)ly + 0.5f;
+        L.U[q] = 1.f; L.nc[q] = 0; L.gp0[q] = L.gp1[q] = L.gp2[q] = 0.f;
         if (px < b.width && py < b.height) {
             const size_t pix = (size_t)py * b.width + px + (size_t)view * plane;
             const size_t pix3 = pix + (size_t)view * 2 * plane;
-            T[q] = a.final_T[pix];
-            nc[q] = a.n_contrib[pix];
-            gp0[q] = a.dL_dimage[pix3];
-            gp1[q] = a.dL_dimage[plane + pix3];
-            gp2[q] = a.dL_dimage[2 * plane + pix3];
+            // final T >= T_min > 0 after a blended entry; a zero (T_min = 0) is kept
+            // finite so that (1 - alpha) U stays a number and T stays 0
+            L.U[q] = fminf(1.f / a.final_T[pix], 3.4028235e38f);
+            L.nc[q] = a.n_contrib[pix];
+            L.gp0[q] = a.dL_dimage[pix3];
+            L.gp1[q] = a.dL_dimage[plane + pix3];
+            L.gp2[q] = a.dL_dimage[2 * plane + pix3];
         }
-        S[q] = __builtin_fmaf(gp2[q], b.bg[2], __builtin_fmaf(gp1[q], b.bg[1], gp0[q] * b.bg[0]));
-        ncmax = max(ncmax, nc[q]);
+        L.S[q] = __builtin_fmaf(L.gp2[q], b.bg[2], __builtin_fmaf(L.gp1[q], b.bg[1], L.gp0[q] * b.bg[0]));
+        ncmax = max(ncmax, L.nc[q]);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) ncmax = max(ncmax, __shfl_xor(ncmax, o, 64));
 
     // Per-lane roles after a two-entry reduction: quad q (lanes 4q..4q+3) holds
     // value q & 7 of entry q >> 3; its first lane writes it, and lanes 1 and 33
-    // write the two ninth values.
+    // write the two ninth values.  The value is turned into its gradient with
+    // the entry's s_tab row: slot psel gives the factor for values 0 (conic A),
+    // 1 (conic C) and 5 (1 / opacity); the others take the constant scl.
     const int vi = (lane >> 2) & 7;
     const bool entb = lane >= 32;
     const bool ninth = (lane & 31) == 1;
     const bool writer = (lane & 3) == 0 || ninth;
     const int widx = ninth ? 8 : vi;
     const float scl = vi == 2 ? -0.5f : vi == 3 ? -1.f : vi == 4 ? -0.5f : 1.f;
+    const bool pvar = vi == 0 || vi == 1 || vi == 5;
+    const int psel = vi == 0 ? 0 : vi == 1 ? 1 : vi == 5 ? 2 : 3;
 
-    // One entry's flagged quadrants, accumulated into v[0..8].
+    // One entry's flagged quadrants, accumulated into v[0..8] (any QPW, any opacity).
     auto walk = [&](int e, uint32_t mm, int pos, float v[9]) {
         const float4 G0 = s_g0[e], G1 = s_g1[e], G2 = s_g2[e];
 #pragma unroll
         for (int q = 0; q < QPW; ++q) {
             if (mm & (1u << q)) {
-                const Pair p = eval_pair(fxq[q], fyq[q], G0, G1, b.alpha_max);
-                const bool ok = pos < nc[q] && p.alpha >= b.alpha_min;
+                const float fx = L.fx[q & 1], fy = L.fy[q >> 1];
+                const Pair p = eval_pair(fx, fy, G0, G1, b.alpha_max);
+                const bool ok = pos < L.nc[q] && p.alpha >= b.alpha_min;
                 const float ae = ok ? p.alpha : 0.f;
-                // transmittance before the entry; a pair that is not blended divides by
-                // 1 - 0 = 1, whose reciprocal is exact, so T is left as it was
-                T[q] = T[q] * __builtin_amdgcn_rcpf(1.f - ae);
-                const float w = ae * T[q];
-                const float gc = __builtin_fmaf(gp2[q], G2.x, __builtin_fmaf(gp1[q], G1.w, gp0[q] * G1.z));
-                const float dS = gc - S[q];
-                const float dalpha = T[q] * dS;
-                S[q] = __builtin_fmaf(ae, dS, S[q]);
+                // transmittance before the entry; a pair that is not blended leaves U as it was
+                L.U[q] = __builtin_fmaf(-ae, L.U[q], L.U[q]);
+                const float T = __builtin_amdgcn_rcpf(L.U[q]);
+                const float w = ae * T;
+                const float gc = __builtin_fmaf(L.gp2[q], G2.x, __builtin_fmaf(L.gp1[q], G1.w, L.gp0[q] * G1.z));
+                const float dS = gc - L.S[q];
+                const float dalpha = T * dS;
+                L.S[q] = __builtin_fmaf(ae, dS, L.S[q]);
                 const float dsG = (ok && !(p.sG > b.alpha_max)) ? dalpha : 0.f;  // clamped: no dependence
                 // dL/dpower = dsG opacity G (G = exp(power)); dL/dopacity = dsG G = dL/dpower / opacity
                 const float dpow = dsG * p.sG;
-                const float dx = fxq[q] - G2.y, dy = fyq[q] - G2.z;  // d = pixel - mean
+                const float dx = fx - G2.y, dy = fy - G2.z;  // d = pixel - mean
                 const float t = dpow * dx, sy = dpow * dy;
                 v[0] += t;
                 v[1] += sy;
@@ -547,17 +681,28 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
                 v[3] = __builtin_fmaf(t, dy, v[3]);
                 v[4] = __builtin_fmaf(sy, dy, v[4]);
                 v[5] += dpow;
-                v[6] = __builtin_fmaf(w, gp0[q], v[6]);
-                v[7] = __builtin_fmaf(w, gp1[q], v[7]);
-                v[8] = __builtin_fmaf(w, gp2[q], v[8]);
+                v[6] = __builtin_fmaf(w, L.gp0[q], v[6]);
+                v[7] = __builtin_fmaf(w, L.gp1[q], v[7]);
+                v[8] = __builtin_fmaf(w, L.gp2[q], v[8]);
             }
         }
+    };
+    // The same for a wave that owns the whole tile, through the code specialised on
+    // the entry's mask and on whether its opacity can be clamped.
+    auto walk4 = [&](int e, uint32_t l, int pos, float v[9]) {
+        const BwdEntry E{s_g0[e], s_g1[e], s_g2[e]};
+        const uint32_t mm = (l >> 8) & 15u;
+        if (l & kBwdClamp)
+            bwd_walk4<true>(L, E, mm, pos, b.alpha_min, b.alpha_max, v);
+        else
+            bwd_walk4<false>(L, E, mm, pos, b.alpha_min, b.alpha_max, v);
     };
 
     const uint32_t end = range.x + (uint32_t)ncmax;
     for (int32_t hi = (int32_t)end; hi > (int32_t)range.x; hi -= kBwdBatch) {
         const int32_t k = hi - 1 - lane;  // slot `lane` holds list position k (descending)
         uint32_t m = 0;
+        bool cl = false;
         if (k >= (int32_t)range.x) {
             const uint32_t g = a.list[k];
             if (g < a.n) {
@@ -568,18 +713,19 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
                     const Staged rec = stage_record(r0, r1, r2, x0, y0);
                     s_g0[lane] = rec.g0;
                     s_g1[lane] = rec.g1;
-                    s_g2[lane] = make_float4(rec.b, rec.ut, rec.vt, __builtin_amdgcn_rcpf(r1.w));
+                    s_g2[lane] = make_float4(rec.b, rec.ut, rec.vt, 0.f);
                     const float l00 = r1.x, l10 = r1.y, l11 = r1.z;
-                    s_g3[lane] = make_float4(k2ln2 * (l00 * l00), k2ln2 * (l00 * l10),
-                                             k2ln2 * __builtin_fmaf(l10, l10, l11 * l11), 0.f);
-                    s_gid[lane] = g;
+                    s_tab[2 * lane] = make_float4(k2ln2 * (l00 * l00), k2ln2 * __builtin_fmaf(l10, l10, l11 * l11),
+                                                  __builtin_amdgcn_rcpf(r1.w), k2ln2 * (l00 * l10));
+                    s_tab[2 * lane + 1] = make_float4(__uint_as_float(g), 0.f, 0.f, 0.f);
+                    cl = !(r1.w <= op_noclamp);
                 }
             }
         }
         const uint64_t bal = __ballot(m != 0);
         if (m) {
             const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            s_list[at] = (uint16_t)(lane | (m << 8));
+            s_list[at] = (uint16_t)(lane | (m << 8) | (cl ? kBwdClamp : 0u));
         }
         const int cnt = __popcll(bal);
         __syncthreads();
@@ -591,25 +737,31 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
             const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)s_list[j]);
             const uint32_t lb = two ? __builtin_amdgcn_readfirstlane((uint32_t)s_list[j + 1]) : 0u;
             const int ea = (int)(la & 63u), eb = (int)(lb & 63u);
-            // -0 is the additive identity (x + -0 == x for every x), so the first
-            // quadrant's accumulation folds to a plain product
             float va[9], vb[9];
+            if constexpr (QPW == 4) {
+                walk4(ea, la, top - ea, va);
+                walk4(eb, lb, top - eb, vb);  // no quadrant when there is no second entry
+            } else {
+                // -0 is the additive identity (x + -0 == x for every x)
 #pragma unroll
-            for (int i = 0; i < 9; ++i) { va[i] = -0.f; vb[i] = -0.f; }
-            walk(ea, la >> 8, top - ea, va);
-            walk(eb, lb >> 8, top - eb, vb);  // no quadrant when there is no second entry
+                for (int i = 0; i < 9; ++i) { va[i] = -0.f; vb[i] = -0.f; }
+                walk(ea, la >> 8, top - ea, va);
+                walk(eb, lb >> 8, top - eb, vb);
+            }
             float z;
             const float wv = reduce2x9(va, vb, z, lane);
             // quads 0 / 8: A S_t + B S_s; quads 1 / 9: C S_s + B S_t; 2-4: scale * moment;
             // 5: sum dpow / opacity (dL/dopacity = dsG G); 6, 7 and the ninth: as summed
             const int e = entb ? eb : ea;
-            const float4 Q = s_g3[e];
+            const float* tab = reinterpret_cast<const float*>(s_tab) + 8 * e;
+            const float pv = tab[psel], bv = tab[3];
+            const uint32_t gid = __float_as_uint(tab[4]);
             const float x = dpp<kRowHalfMirror>(wv);  // the other first moment of the same entry
-            const float P = vi == 0 ? Q.x : (vi == 1 ? Q.z : (vi == 5 ? s_g2[e].w : scl));
-            const float Bx = vi < 2 ? Q.y * x : 0.f;
+            const float P = pvar ? pv : scl;
+            const float Bx = vi < 2 ? bv * x : 0.f;
             const float out = ninth ? z : __builtin_fmaf(P, wv, Bx);
             if (writer && (two || !entb))
-                unsafeAtomicAdd(a.grad2d + (size_t)s_gid[e] * GS_GRAD2D_STRIDE + widx, out);
+                unsafeAtomicAdd(a.grad2d + (size_t)gid * GS_GRAD2D_STRIDE + widx, out);
         }
         __syncthreads();
     }

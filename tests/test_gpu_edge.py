@@ -103,6 +103,46 @@ def test_huge_splat_and_deep_lists():
     assert (rg[:, 1] - rg[:, 0]).max() > 256
 
 
+def test_opaque_entries_clamp():
+    """Opacities just below, at and above alpha_max on Gaussians wide enough that
+    opacity G exceeds alpha_max at the pixels nearest their centres: there alpha is
+    clamped and carries no gradient; opacities below alpha_max never clamp.  The
+    backward takes a separate path for entries whose opacity can clamp; 2D and 3D
+    gradients against the oracle, pixels within rounding of a decision masked
+    (3DGS backward, section 2: alpha = min(0.99, opacity G))."""
+    import torch
+    from oracle import oracle as O
+    gs = _gs()
+    sc = scenes.random_small(36, n=240, width=64, height=48, scale_mu=-2.4)
+    k = np.arange(sc.n) % 6
+    for j, op in enumerate([0.98999, 0.99, 0.995, 0.9999]):
+        sc.opacity_logits[k == j] = np.float32(math.log(op / (1.0 - op)))
+    sc.log_scales[k < 4] = np.float32(math.log(0.4))
+    p = to_dev(sc.params())
+    r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
+    r.forward(p, check=True)
+    o = O.render(sc.cam, sc.sh_degree, sc.params(), backward=False)
+    amb = o["ambiguous"] > 0
+    clamp_px = int(((o["ambiguous"] & 4) > 0).sum())
+    dL = np.asarray(sc.dL_dimage, np.float64) * (~amb)[None]
+    g3 = r.backward(p, torch.from_numpy(dL.astype(np.float32)).cuda())
+    o2 = O.render_bwd(sc.cam, o["pre"], o["point_list"], o["ranges"], dL)
+    o3 = O.preprocess_bwd(sc.cam, sc.sh_degree, sc.params(), o["pre"]["tiles_touched"], o2)
+    g2 = r.grad2d.cpu().numpy()
+    vis = o["pre"]["tiles_touched"] > 0
+    for key, got in [("dxy", g2[:, 0:2]), ("dconic", g2[:, 2:5]), ("dopacity", g2[:, 5]), ("drgb", g2[:, 6:9])]:
+        e = rel_l2(got[vis], o2[key][vis])
+        assert e <= 1e-3, (key, e)
+    for key in PARAM_KEYS:
+        e = rel_l2(g3[key].cpu().numpy(), o3[key])
+        assert e <= 1e-3, (key, e)
+    # the oracle's blend of the same scene with alpha_max at 1 (no clamping) differs:
+    # some pixel does clamp, so the clamp's zero gradient is exercised
+    o_nc = O.render(sc.cam, sc.sh_degree, sc.params(), O.Settings(alpha_max=1.0), backward=False)
+    assert np.abs(o_nc["image"] - o["image"]).max() > 1e-4
+    log(f"opaque entries: {clamp_px} pixels within rounding of the clamp masked")
+
+
 def test_capacity_overflow_flag():
     """K > key_capacity: the flag is raised, no range is written, nothing is written out of bounds."""
     import torch
