@@ -552,6 +552,42 @@ __device__ __forceinline__ void bwd_walk4(BwdLane4& L, const BwdEntry& E, uint32
     }
 }
 
+// The same result as reduce2x9 with the tree's row levels done through LDS:
+// after the half-wave exchange each lane holds, for value k < 8, a sum of two
+// partials of entry a (lanes 0-31) or b (lanes 32-63); it stores them to
+// red[k][lane] (a wave-private 8 x 64 float block), and lane l then sums the 8
+// contiguous partials of value l / 4 that start at red[(l / 4) % 8][32 (l / 32)
+// + 8 (l % 4)], and its quad finishes the sum.  Plain adds and two quad DPP
+// steps replace the row-exchange, select and row-DPP instructions of the tree.
+__device__ __forceinline__ float reduce2x9_lds(float a[9], float b[9], float& z, int lane, float* red) {
+    float s[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        xchg32(a[k], b[k]);
+        s[k] = a[k] + b[k];  // lanes 0-31: a_k, lanes 32-63: b_k
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) red[k * 64 + lane] = s[k];
+    const float4* p = reinterpret_cast<const float4*>(red + ((lane >> 2) & 7) * 64 + (lane >> 5) * 32 + (lane & 3) * 8);
+    const float4 x0 = p[0], x1 = p[1];
+    float w = ((x0.x + x0.y) + (x0.z + x0.w)) + ((x1.x + x1.y) + (x1.z + x1.w));
+    w += dpp<kQuadXor1>(w);
+    w += dpp<kQuadXor2>(w);
+    // ninth values
+    float p9 = a[8], r9 = b[8];
+    xchg32(p9, r9);
+    float y = p9 + r9;  // lanes 0-31: a8, 32-63: b8
+    float y2 = y;
+    xchg16(y, y2);
+    y += y2;
+    y += dpp<kRowRor8>(y);
+    y += dpp<kRowHalfMirror>(y);
+    y += dpp<kQuadXor1>(y);
+    y += dpp<kQuadXor2>(y);
+    z = y;
+    return w;
+}
+
 // Backward: one wave64 per tile (QPW = 4), each lane owning one pixel of each of
 // the four 8x8 quadrants (pixel q of lane l sits at ((q & 1) 8 + l % 8,
 // (q >> 1) 8 + l / 8)); or, for images with few tiles, two waves per tile
@@ -588,6 +624,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     // after the reduction: conic A, C, 1 / opacity, conic B, then the Gaussian's index (bits)
     __shared__ float4 s_tab[2 * kBwdBatch];
     __shared__ uint16_t s_list[kBwdBatch];  // slot | quadrant mask << 8 | kBwdClamp, in walk order
+    __shared__ float4 s_red[8 * 64 / 4];     // the reduction's exchange block (reduce2x9_lds)
 
     const BlendArgs& b = a.b;
     const int ntv = b.tiles_x * b.tiles_y;
@@ -749,7 +786,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
                 walk(eb, lb >> 8, top - eb, vb);
             }
             float z;
-            const float wv = reduce2x9(va, vb, z, lane);
+            const float wv = reduce2x9_lds(va, vb, z, lane, reinterpret_cast<float*>(s_red));
             // quads 0 / 8: A S_t + B S_s; quads 1 / 9: C S_s + B S_t; 2-4: scale * moment;
             // 5: sum dpow / opacity (dL/dopacity = dsG G); 6, 7 and the ninth: as summed
             const int e = entb ? eb : ea;
