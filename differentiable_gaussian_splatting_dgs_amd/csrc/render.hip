@@ -460,7 +460,8 @@ __device__ __forceinline__ void bwd_quad(BwdLane4& L, const BwdEntry& E, int pos
                                          float dy, float amin, float amax, float v[9]) {
     const float e1 = __builtin_fmaf(E.g0.x, L.fx[Q & 1], e1r);
     const float sG = __builtin_amdgcn_exp2f(-__builtin_fmaf(e1, e1, pr));
-    const float alpha = __builtin_amdgcn_fmed3f(sG, 0.f, amax);
+    // 0 <= opacity G <= alpha_max without CL: eval_pair's clamp is the identity there
+    const float alpha = CL ? __builtin_amdgcn_fmed3f(sG, 0.f, amax) : sG;
     const bool ok = pos < L.nc[Q] && alpha >= amin;
     const float ae = ok ? alpha : 0.f;
     L.U[Q] = __builtin_fmaf(-ae, L.U[Q], L.U[Q]);  // before the entry; unchanged where ae = 0
@@ -555,10 +556,14 @@ __device__ __forceinline__ void bwd_walk4(BwdLane4& L, const BwdEntry& E, uint32
 // The same result as reduce2x9 with the tree's row levels done through LDS:
 // after the half-wave exchange each lane holds, for value k < 8, a sum of two
 // partials of entry a (lanes 0-31) or b (lanes 32-63); it stores them to
-// red[k][lane] (a wave-private 8 x 64 float block), and lane l then sums the 8
-// contiguous partials of value l / 4 that start at red[(l / 4) % 8][32 (l / 32)
-// + 8 (l % 4)], and its quad finishes the sum.  Plain adds and two quad DPP
-// steps replace the row-exchange, select and row-DPP instructions of the tree.
+// red[k][lane] (a wave-private block of 8 rows of kRedRow floats).  Lane l then
+// sums 8 of the 32 partials of value l / 4 (row (l / 4) % 8, half l / 32): the
+// 4-float groups l % 4 and l % 4 + 4, so that a quad's first reads cover 16
+// contiguous floats and its second reads the next 16; the quad finishes the sum.
+// Plain adds and two quad DPP steps replace the row-exchange, select and
+// row-DPP instructions of the tree.  A row stride of 80 floats puts the 16-float
+// spans of four neighbouring rows in different banks.
+constexpr int kRedRow = 80;  // floats per row of the reduction's LDS block (64 partials + 16)
 __device__ __forceinline__ float reduce2x9_lds(float a[9], float b[9], float& z, int lane, float* red) {
     float s[8];
 #pragma unroll
@@ -567,9 +572,9 @@ __device__ __forceinline__ float reduce2x9_lds(float a[9], float b[9], float& z,
         s[k] = a[k] + b[k];  // lanes 0-31: a_k, lanes 32-63: b_k
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) red[k * 64 + lane] = s[k];
-    const float4* p = reinterpret_cast<const float4*>(red + ((lane >> 2) & 7) * 64 + (lane >> 5) * 32 + (lane & 3) * 8);
-    const float4 x0 = p[0], x1 = p[1];
+    for (int k = 0; k < 8; ++k) red[k * kRedRow + lane] = s[k];
+    const float4* p = reinterpret_cast<const float4*>(red + ((lane >> 2) & 7) * kRedRow + (lane >> 5) * 32) + (lane & 3);
+    const float4 x0 = p[0], x1 = p[4];
     float w = ((x0.x + x0.y) + (x0.z + x0.w)) + ((x1.x + x1.y) + (x1.z + x1.w));
     w += dpp<kQuadXor1>(w);
     w += dpp<kQuadXor2>(w);
@@ -620,11 +625,10 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     constexpr int kSplit = 4 / QPW;
     __shared__ float4 s_g0[kBwdBatch];   // L00, L10, L11, c1 (stage_record)
     __shared__ float4 s_g1[kBwdBatch];   // c2, -log2 opacity, r, g
-    __shared__ float4 s_g2[kBwdBatch];   // b, tile-relative mean (u, v), 0
-    // after the reduction: conic A, C, 1 / opacity, conic B, then the Gaussian's index (bits)
-    __shared__ float4 s_tab[2 * kBwdBatch];
+    __shared__ float4 s_g2[kBwdBatch];   // b, tile-relative mean (u, v), the Gaussian's index (bits)
+    __shared__ float4 s_tab[kBwdBatch];  // for after the reduction: conic A, C, 1 / opacity, conic B
     __shared__ uint16_t s_list[kBwdBatch];  // slot | quadrant mask << 8 | kBwdClamp, in walk order
-    __shared__ float4 s_red[8 * 64 / 4];     // the reduction's exchange block (reduce2x9_lds)
+    __shared__ float4 s_red[8 * kRedRow / 4];  // the reduction's exchange block (reduce2x9_lds)
 
     const BlendArgs& b = a.b;
     const int ntv = b.tiles_x * b.tiles_y;
@@ -688,6 +692,7 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     const float scl = vi == 2 ? -0.5f : vi == 3 ? -1.f : vi == 4 ? -0.5f : 1.f;
     const bool pvar = vi == 0 || vi == 1 || vi == 5;
     const int psel = vi == 0 ? 0 : vi == 1 ? 1 : vi == 5 ? 2 : 3;
+    const int bmask = entb ? -1 : 0;
 
     // One entry's flagged quadrants, accumulated into v[0..8] (any QPW, any opacity).
     auto walk = [&](int e, uint32_t mm, int pos, float v[9]) {
@@ -750,11 +755,10 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
                     const Staged rec = stage_record(r0, r1, r2, x0, y0);
                     s_g0[lane] = rec.g0;
                     s_g1[lane] = rec.g1;
-                    s_g2[lane] = make_float4(rec.b, rec.ut, rec.vt, 0.f);
+                    s_g2[lane] = make_float4(rec.b, rec.ut, rec.vt, __uint_as_float(g));
                     const float l00 = r1.x, l10 = r1.y, l11 = r1.z;
-                    s_tab[2 * lane] = make_float4(k2ln2 * (l00 * l00), k2ln2 * __builtin_fmaf(l10, l10, l11 * l11),
+                    s_tab[lane] = make_float4(k2ln2 * (l00 * l00), k2ln2 * __builtin_fmaf(l10, l10, l11 * l11),
                                                   __builtin_amdgcn_rcpf(r1.w), k2ln2 * (l00 * l10));
-                    s_tab[2 * lane + 1] = make_float4(__uint_as_float(g), 0.f, 0.f, 0.f);
                     cl = !(r1.w <= op_noclamp);
                 }
             }
@@ -789,10 +793,12 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
             const float wv = reduce2x9_lds(va, vb, z, lane, reinterpret_cast<float*>(s_red));
             // quads 0 / 8: A S_t + B S_s; quads 1 / 9: C S_s + B S_t; 2-4: scale * moment;
             // 5: sum dpow / opacity (dL/dopacity = dsG G); 6, 7 and the ninth: as summed
-            const int e = entb ? eb : ea;
-            const float* tab = reinterpret_cast<const float*>(s_tab) + 8 * e;
+            // the entry's s_tab row: ea's in lanes 0-31, eb's in lanes 32-63 (bmask selects
+            // the difference of the two rows' offsets; the offsets are scalar)
+            const int row = 4 * ea + (bmask & (4 * (eb - ea)));
+            const float* tab = reinterpret_cast<const float*>(s_tab) + row;
             const float pv = tab[psel], bv = tab[3];
-            const uint32_t gid = __float_as_uint(tab[4]);
+            const uint32_t gid = __float_as_uint(reinterpret_cast<const float*>(s_g2)[row + 3]);
             const float x = dpp<kRowHalfMirror>(wv);  // the other first moment of the same entry
             const float P = pvar ? pv : scl;
             const float Bx = vi < 2 ? bv * x : 0.f;
