@@ -185,9 +185,10 @@ __device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i,
     const float du = g0.x, dv = g0.y, dA = g0.z, dB = g0.w, dC = g1.x, dsig = g1.y;
     drgb[0] = g1.z; drgb[1] = g1.w; drgb[2] = g2.x;
 
-    // opacity
-    const float sig = 1.f / (1.f + __expf(-a.opac[i]));
-    dop = dsig * sig * (1.f - sig);
+    // opacity: the sigmoid and its derivative in float64, so that a saturated opacity
+    // (sigma within 1e-5 of 1) keeps the relative accuracy of sigma (1 - sigma)
+    const double sig = 1.0 / (1.0 + exp(-(double)a.opac[i]));
+    dop = (float)((double)dsig * (sig * (1.0 - sig)));
 
     // colour -> SH; the view direction depends on the mean
     const float cpx = -(float)(c.R[0] * c.t[0] + c.R[3] * c.t[1] + c.R[6] * c.t[2]);
@@ -222,8 +223,10 @@ __device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i,
     const double qn2 = (double)q4.x * q4.x + (double)q4.y * q4.y + (double)q4.z * q4.z + (double)q4.w * q4.w;
     const double iq = rsqrt_f64(qn2);
     const double qw = q4.x * iq, qx = q4.y * iq, qy = q4.z * iq, qz = q4.w * iq;
-    // a float32 scale differs from exp(log-scale) by a relative 2^-24, which only rescales its axis
-    const double s[3] = {__expf(a.log_scales[3 * i]), __expf(a.log_scales[3 * i + 1]), __expf(a.log_scales[3 * i + 2])};
+    // the scales in float64 like the rest of this part: where the scale gradient's two terms
+    // cancel, a float32 scale's 2^-24 would be amplified by the cancellation
+    const double s[3] = {exp((double)a.log_scales[3 * i]), exp((double)a.log_scales[3 * i + 1]),
+                         exp((double)a.log_scales[3 * i + 2])};
     double R[9];
     R[0] = 1.0 - 2.0 * (qy * qy + qz * qz); R[1] = 2.0 * (qx * qy - qw * qz); R[2] = 2.0 * (qx * qz + qw * qy);
     R[3] = 2.0 * (qx * qy + qw * qz); R[4] = 1.0 - 2.0 * (qx * qx + qz * qz); R[5] = 2.0 * (qy * qz - qw * qx);
