@@ -263,11 +263,12 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
                 const bool stop = pass && Tn < b.T_min;  // ok = pass and not stop (stop implies pass)
                 done = done || stop;
                 const bool ok = pass != stop;
-                const float w = ok ? pa.alpha * T : 0.f;
+                const float Tb = ok ? Tn : T;
+                const float w = T - Tb;  // the weight alpha T as the transmittance drop; 0 if not blended
                 C0 = __builtin_fmaf(w, ga1.z, C0);
                 C1 = __builtin_fmaf(w, ga1.w, C1);
                 C2 = __builtin_fmaf(w, cba, C2);
-                T = ok ? Tn : T;
+                T = Tb;
                 last = ok ? base + ea + 1 : last;
                 if (ok) fb[4 * ea] = 1;  // lanes that blend all store the same byte
             }
@@ -277,11 +278,12 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
                 const bool stop = pass && Tn < b.T_min;  // ok = pass and not stop (stop implies pass)
                 done = done || stop;
                 const bool ok = pass != stop;
-                const float w = ok ? pb.alpha * T : 0.f;
+                const float Tb = ok ? Tn : T;
+                const float w = T - Tb;  // the weight alpha T as the transmittance drop; 0 if not blended
                 C0 = __builtin_fmaf(w, gb1.z, C0);
                 C1 = __builtin_fmaf(w, gb1.w, C1);
                 C2 = __builtin_fmaf(w, cbb, C2);
-                T = ok ? Tn : T;
+                T = Tb;
                 last = ok ? base + eb + 1 : last;
                 if (ok) fb[4 * eb] = 1;
             }
