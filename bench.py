@@ -125,21 +125,26 @@ def blend_flops(p_fwd, p_bwd, p_blend):
             FLOPS_BWD_BLENDED * p_blend + FLOPS_BWD_SKIPPED * (p_bwd - p_blend))
 
 
-def raster_roofline(N, K, deg, p_fwd, p_bwd, p_blend, raster_ms, peaks):
+def raster_roofline(N, K, deg, p_fwd, p_bwd, p_blend, raster_ms, peaks, colorjac=False):
     """The rasterizer's roofline fraction: the sum over its stages of the least time the binding peak allows
     for the stage's algorithmic bytes (preprocess, binning, 2D->3D backward) or flops (the two blends), over
-    the measured fwd+bwd time; against the published peaks and against the measured ones."""
+    the measured fwd+bwd time; against the published peaks and against the measured ones.  colorjac: the
+    preprocess also writes the 36-byte colour-direction Jacobian, which the 2D->3D backward reads instead
+    of the SH coefficients."""
     hbm = PEAK_HBM_GBS * 1e9
     fl = PEAK_FP32_TFLOPS * 1e12
-    par = 4.0 * (3 + 3 + 4 + 1 + 3 * (deg + 1) ** 2)                      # parameter bytes per Gaussian
+    sh = 4.0 * 3 * (deg + 1) ** 2
+    par = 4.0 * (3 + 3 + 4 + 1) + sh                                      # parameter bytes per Gaussian
+    jac = 36.0 if colorjac else 0.0
     f_fwd, f_bwd = blend_flops(p_fwd, p_bwd, p_blend)
     tmin = dict(
-        preprocess=(par + 65.0) * N / hbm,                                 # parameters in, 65 B records out
+        preprocess=(par + 65.0 + jac) * N / hbm,                           # parameters in, 65 B records out
         bin_sort=(16 * N + 4 * 16 * N + 20 * N + 8 * K + 2 * 16 * K + 4 * K) / hbm,  # keys, 4 depth passes,
                                                                            # emission, 2 tile passes, ranges
         render_fwd=f_fwd / fl,
         render_bwd=f_bwd / fl,
-        preprocess_bwd=(2 * par + 41.0) * N / hbm)  # parameters + 36 B 2D gradients + 5 B count/clamp in, grads out
+        # parameters (without the SH with the Jacobian) + 36 B 2D gradients + 5 B count/clamp in, gradients out
+        preprocess_bwd=((par - sh + jac if colorjac else par) + 41.0 + par) * N / hbm)
     scale = dict(preprocess=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"],
                  bin_sort=PEAK_HBM_GBS / peaks["hbm_gbs"]["measured"],
                  render_fwd=PEAK_FP32_TFLOPS / peaks["fp32_tflops"]["measured"],
@@ -230,9 +235,7 @@ class RasterPass:
         mark(3)
         r.backward_2d(self.dL, accumulate=True)
         mark(4)
-        gs.gs_preprocess_bwd(r.cam, r.settings, r.deg, p["means"], p["log_scales"], p["quats"],
-                             p["opacity_logits"], p["sh"], r.tiles_touched, r.clamp, r.grad2d, g3["means"],
-                             g3["log_scales"], g3["quats"], g3["opacity_logits"], g3["sh"])
+        r.backward_3d(p, g3)
         mark(5)
 
 
@@ -319,7 +322,8 @@ def raster_line(name, steps, warmup, peaks):
                            bwd_pairs_per_s=p_bwd / (stage_ms["render_bwd"] * 1e-3),
                            bwd_walked_entries=entries, bwd_walked_quadrants=quads, bwd_float_atomics=9 * entries,
                            bwd_atomics_per_s=9 * entries / (stage_ms["render_bwd"] * 1e-3)),
-                stage_roofline=raster_roofline(sc.n, K, sc.sh_degree, p_fwd, p_bwd, p_blend, ms, peaks),
+                stage_roofline=raster_roofline(sc.n, K, sc.sh_degree, p_fwd, p_bwd, p_blend, ms, peaks,
+                                               colorjac=r.colorjac is not None),
                 roofline=kernel_roofline(timed_ms, p_fwd, p_bwd, p_blend, peaks, name),
                 peaks=peaks)
     return line, sc

@@ -35,6 +35,40 @@ inline bool views_ok(const gs_camera* cams, int32_t views) {
 inline int tiles_x(const gs_camera* c) { return (c->width + kTile - 1) / kTile; }
 inline int tiles_y(const gs_camera* c) { return (c->height + kTile - 1) / kTile; }
 
+// Gradient of sum_k w[k] Y_k with respect to the components (x, y, z) of the
+// direction, Y the real SH basis of degree DEG taken as polynomials of three free
+// variables (Gaussian Splatting backward CUDA page (lshu.cn), section 4: the colour
+// gradient reaches the view direction through the SH basis); the projection onto
+// the sphere is left to the caller.
+template <int DEG>
+__device__ __forceinline__ void sh_grad(float x, float y, float z, const float* w, float& gx, float& gy,
+                                        float& gz) {
+    gx = gy = gz = 0.f;
+    if (DEG >= 1) {
+        const float c1 = 0.48860251190291992f;
+        gx -= c1 * w[3];
+        gy -= c1 * w[1];
+        gz += c1 * w[2];
+    }
+    if (DEG >= 2) {
+        const float A = 1.0925484305920792f, B = 0.31539156525252005f, E = 0.54627421529603959f;
+        gx += A * y * w[4] - 2.f * B * x * w[6] - A * z * w[7] + 2.f * E * x * w[8];
+        gy += A * x * w[4] - A * z * w[5] - 2.f * B * y * w[6] - 2.f * E * y * w[8];
+        gz += -A * y * w[5] + 4.f * B * z * w[6] - A * x * w[7];
+    }
+    if (DEG >= 3) {
+        const float P = 0.59004358992664352f, Q = 2.8906114426405538f, R = 0.45704579946446572f;
+        const float S = 0.37317633259011540f, U = 1.4453057213202769f;
+        const float xx = x * x, yy = y * y, zz = z * z;
+        gx += -6.f * P * x * y * w[9] + Q * y * z * w[10] + 2.f * R * x * y * w[11] - 6.f * S * x * z * w[12] -
+              R * (4.f * zz - 3.f * xx - yy) * w[13] + 2.f * U * x * z * w[14] - 3.f * P * (xx - yy) * w[15];
+        gy += -3.f * P * (xx - yy) * w[9] + Q * x * z * w[10] - R * (4.f * zz - xx - 3.f * yy) * w[11] -
+              6.f * S * y * z * w[12] + 2.f * R * x * y * w[13] - 2.f * U * y * z * w[14] + 6.f * P * x * y * w[15];
+        gz += Q * x * y * w[10] - 8.f * R * y * z * w[11] + S * (6.f * zz - 3.f * xx - 3.f * yy) * w[12] -
+              8.f * R * x * z * w[13] + U * (xx - yy) * w[14];
+    }
+}
+
 // Camera and settings as plain kernel arguments.
 struct CamArgs {
     double fx, fy, cx, cy;

@@ -29,6 +29,7 @@ struct PreArgs {
     int16_t* rect;
     int32_t* tiles_touched;
     uint8_t* clamp;
+    float* cjac;  // optional [views, n, 9]: d colour_c / d dir_j before the clamp, row-major by c
 };
 
 // Real spherical harmonics with the Condon-Shortley phase as polynomials of
@@ -89,7 +90,7 @@ __device__ __forceinline__ void load_sh(const float* sh, int i, float* shv) {
 // camera centre -R^T t to the mean; cm gets bit c when channel c was clamped.
 template <int DEG>
 __device__ __forceinline__ void shade(const CamArgs& c, double mx, double my, double mz, const float* shv,
-                                      double rgb[3], uint8_t& cm) {
+                                      double rgb[3], uint8_t& cm, double dir[3]) {
     constexpr int K = (DEG + 1) * (DEG + 1);
     const double cpx = -(c.R[0] * c.t[0] + c.R[3] * c.t[1] + c.R[6] * c.t[2]);
     const double cpy = -(c.R[1] * c.t[0] + c.R[4] * c.t[1] + c.R[7] * c.t[2]);
@@ -97,6 +98,7 @@ __device__ __forceinline__ void shade(const CamArgs& c, double mx, double my, do
     double dx = mx - cpx, dy = my - cpy, dz = mz - cpz;
     const double dinv = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
     dx *= dinv; dy *= dinv; dz *= dinv;
+    dir[0] = dx; dir[1] = dy; dir[2] = dz;
     double Y[16];
     sh_eval<DEG>(dx, dy, dz, Y);
     rgb[0] = rgb[1] = rgb[2] = 0.5;
@@ -113,8 +115,9 @@ __device__ __forceinline__ void shade(const CamArgs& c, double mx, double my, do
 
 // One thread per Gaussian: projection, tile rectangle and the SH colour, for
 // each view in turn (the parameters are read once; the view-free parts --
-// opacity, M = R S -- are computed once).
-template <int DEG, bool VEC>
+// opacity, M = R S -- are computed once).  CJ: also the colour's gradient with
+// respect to the view direction (a.cjac).
+template <int DEG, bool VEC, bool CJ>
 __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     constexpr int J = 3 * (DEG + 1) * (DEG + 1);
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -126,6 +129,8 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     auto cull = [&](size_t o) {
         float4* sp = reinterpret_cast<float4*>(a.splats + o * GS_SPLAT_STRIDE);
         sp[0] = z4; sp[1] = z4; sp[2] = z4;
+        if constexpr (CJ)
+            for (int k = 0; k < 9; ++k) a.cjac[9 * o + k] = 0.f;
         a.clamp[o] = 0;
         a.depth[o] = 0.f;
         reinterpret_cast<uint2*>(a.rect)[o] = make_uint2(0u, 0u);
@@ -205,9 +210,23 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
         }
 
         // colour: max(0, sum sh Y(dir) + 0.5), dir from the camera centre
-        double rgb[3];
+        double rgb[3], dir[3];
         uint8_t cm = 0;
-        shade<DEG>(c, mx, my, mz, shv, rgb, cm);
+        shade<DEG>(c, mx, my, mz, shv, rgb, cm, dir);
+        if constexpr (CJ) {
+            // the colour's gradient with respect to the direction, for the 2D -> 3D backward
+            // (computed in float32 from the float32 coefficients, as that backward would)
+            float* jo = a.cjac + 9 * o;
+#pragma unroll
+            for (int ch = 0; ch < 3; ++ch) {
+                float w[16];
+#pragma unroll
+                for (int k = 0; k < (DEG + 1) * (DEG + 1); ++k) w[k] = shv[3 * k + ch];
+                float gx, gy, gz;
+                sh_grad<DEG>((float)dir[0], (float)dir[1], (float)dir[2], w, gx, gy, gz);
+                jo[3 * ch] = gx; jo[3 * ch + 1] = gy; jo[3 * ch + 2] = gz;
+            }
+        }
 
         // Cholesky factor of the conic, scaled so that G = exp2(-|L^T d|^2):
         // conic = [[cc, -cb], [-cb, ca]] / det = L L^T with
@@ -241,13 +260,16 @@ namespace {
 
 template <int DEG, bool VEC>
 void launch_pre(dim3 grid, dim3 block, hipStream_t s, const PreArgs& a) {
-    hipLaunchKernelGGL((k_preprocess<DEG, VEC>), grid, block, 0, s, a);
+    if (a.cjac)
+        hipLaunchKernelGGL((k_preprocess<DEG, VEC, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_preprocess<DEG, VEC, false>), grid, block, 0, s, a);
 }
 
 int preprocess_impl(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                     int32_t sh_degree, const float* means, const float* log_scales, const float* quats,
                     const float* opacity_logits, const float* sh, float* splats, float* depth, int16_t* rect,
-                    int32_t* tiles_touched, uint8_t* clamp_mask, void* stream) {
+                    int32_t* tiles_touched, uint8_t* clamp_mask, float* cjac, void* stream) {
     if (!views_ok(cams, views) || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
     if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
     if (!set) return GS_EINVAL;
@@ -263,6 +285,7 @@ int preprocess_impl(const gs_camera* cams, int32_t views, const gs_settings* set
     a.n = n;
     a.means = means; a.log_scales = log_scales; a.quats = quats; a.opac = opacity_logits; a.sh = sh;
     a.splats = splats; a.depth = depth; a.rect = rect; a.tiles_touched = tiles_touched; a.clamp = clamp_mask;
+    a.cjac = cjac;
     const dim3 grid((n + kPreBlock - 1) / kPreBlock), block(kPreBlock);
     hipStream_t s = as_stream(stream);
     const bool vec = aligned16(sh);
@@ -283,7 +306,17 @@ extern "C" int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32
                              const float* opacity_logits, const float* sh, float* splats, float* depth,
                              int16_t* rect, int32_t* tiles_touched, uint8_t* clamp_mask, void* stream) {
     return preprocess_impl(cam, 1, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
-                           splats, depth, rect, tiles_touched, clamp_mask, stream);
+                           splats, depth, rect, tiles_touched, clamp_mask, nullptr, stream);
+}
+
+extern "C" int gs_preprocess_colorjac(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                                      const float* means, const float* log_scales, const float* quats,
+                                      const float* opacity_logits, const float* sh, float* splats, float* depth,
+                                      int16_t* rect, int32_t* tiles_touched, uint8_t* clamp_mask, float* colorjac,
+                                      void* stream) {
+    if (!colorjac && n > 0) return GS_EINVAL;
+    return preprocess_impl(cam, 1, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
+                           splats, depth, rect, tiles_touched, clamp_mask, colorjac, stream);
 }
 
 extern "C" int gs_preprocess_views(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
@@ -292,5 +325,5 @@ extern "C" int gs_preprocess_views(const gs_camera* cams, int32_t views, const g
                                    float* depth, int16_t* rect, int32_t* tiles_touched, uint8_t* clamp_mask,
                                    void* stream) {
     return preprocess_impl(cams, views, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
-                           splats, depth, rect, tiles_touched, clamp_mask, stream);
+                           splats, depth, rect, tiles_touched, clamp_mask, nullptr, stream);
 }

@@ -45,11 +45,11 @@ struct BwdArgs {
     float* dsh;
     float* accum;   // densification statistic, optional
     int32_t* count;
+    const float* cjac;  // the CJ variant: [n, 9] d colour_c / d dir_j from the forward preprocess
     AdamHyper adam;
 };
 
-// SH values Y[k] at unit direction (x, y, z) and the gradient of
-// sum_k w[k] Y_k with respect to (x, y, z).
+// SH values Y[k] at unit direction (x, y, z).
 template <int DEG>
 __device__ __forceinline__ void sh_values(float x, float y, float z, float* Y) {
     // no contraction: the fused tail and its SH half must round these identically
@@ -76,35 +76,6 @@ __device__ __forceinline__ void sh_values(float x, float y, float z, float* Y) {
             Y[14] = 1.4453057213202769f * z * (xx - yy);
             Y[15] = -0.59004358992664352f * x * (xx - 3.f * yy);
         }
-    }
-}
-
-template <int DEG>
-__device__ __forceinline__ void sh_grad(float x, float y, float z, const float* w, float& gx, float& gy,
-                                        float& gz) {
-    gx = gy = gz = 0.f;
-    if (DEG >= 1) {
-        const float c1 = 0.48860251190291992f;
-        gx -= c1 * w[3];
-        gy -= c1 * w[1];
-        gz += c1 * w[2];
-    }
-    if (DEG >= 2) {
-        const float A = 1.0925484305920792f, B = 0.31539156525252005f, E = 0.54627421529603959f;
-        gx += A * y * w[4] - 2.f * B * x * w[6] - A * z * w[7] + 2.f * E * x * w[8];
-        gy += A * x * w[4] - A * z * w[5] - 2.f * B * y * w[6] - 2.f * E * y * w[8];
-        gz += -A * y * w[5] + 4.f * B * z * w[6] - A * x * w[7];
-    }
-    if (DEG >= 3) {
-        const float P = 0.59004358992664352f, Q = 2.8906114426405538f, R = 0.45704579946446572f;
-        const float S = 0.37317633259011540f, U = 1.4453057213202769f;
-        const float xx = x * x, yy = y * y, zz = z * z;
-        gx += -6.f * P * x * y * w[9] + Q * y * z * w[10] + 2.f * R * x * y * w[11] - 6.f * S * x * z * w[12] -
-              R * (4.f * zz - 3.f * xx - yy) * w[13] + 2.f * U * x * z * w[14] - 3.f * P * (xx - yy) * w[15];
-        gy += -3.f * P * (xx - yy) * w[9] + Q * x * z * w[10] - R * (4.f * zz - xx - 3.f * yy) * w[11] -
-              6.f * S * y * z * w[12] + 2.f * R * x * y * w[13] - 2.f * U * y * z * w[14] + 6.f * P * x * y * w[15];
-        gz += Q * x * y * w[10] - 8.f * R * y * z * w[11] + S * (6.f * zz - 3.f * xx - 3.f * yy) * w[12] -
-              8.f * R * x * z * w[13] + U * (xx - yy) * w[14];
     }
 }
 
@@ -173,8 +144,9 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
     return r;
 }
 
-// Gaussian i seen by camera c, with that view's inputs w.
-template <int DEG>
+// Gaussian i seen by camera c, with that view's inputs w.  CJ: the colour's
+// direction gradient comes from a.cjac instead of the SH coefficients in s_sh.
+template <int DEG, bool CJ = false>
 __device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i, const ViewIn& w, const float* s_sh,
                                       int col, int ldg, float dmu[3], float dls[3], float dq[4], float& dop,
                                       float Y[16], float drgb[3]) {
@@ -202,13 +174,25 @@ __device__ __forceinline__ void chain(const BwdArgs& a, const CamArgs& c, int i,
     for (int ch = 0; ch < 3; ++ch)
         if ((cm >> ch) & 1u) drgb[ch] = 0.f;
     sh_values<DEG>(dx, dy, dz, Y);
-    float wk[16];
+    float gdx = 0.f, gdy = 0.f, gdz = 0.f;
+    if constexpr (CJ) {
+        if constexpr (DEG > 0) {  // the gradient is the drgb-weighted sum of the colour rows
+            const float* jr = a.cjac + 9 * (size_t)i;
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-        wk[k] = drgb[0] * s_sh[(3 * k) * ldg + col] + drgb[1] * s_sh[(3 * k + 1) * ldg + col] +
-                drgb[2] * s_sh[(3 * k + 2) * ldg + col];
-    float gdx, gdy, gdz;
-    sh_grad<DEG>(dx, dy, dz, wk, gdx, gdy, gdz);
+            for (int ch = 0; ch < 3; ++ch) {
+                gdx = __builtin_fmaf(drgb[ch], jr[3 * ch], gdx);
+                gdy = __builtin_fmaf(drgb[ch], jr[3 * ch + 1], gdy);
+                gdz = __builtin_fmaf(drgb[ch], jr[3 * ch + 2], gdz);
+            }
+        }
+    } else {
+        float wk[16];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            wk[k] = drgb[0] * s_sh[(3 * k) * ldg + col] + drgb[1] * s_sh[(3 * k + 1) * ldg + col] +
+                    drgb[2] * s_sh[(3 * k + 2) * ldg + col];
+        sh_grad<DEG>(dx, dy, dz, wk, gdx, gdy, gdz);
+    }
     const float dot = dx * gdx + dy * gdy + dz * gdz;
     float dmx = (gdx - dx * dot) * il, dmy = (gdy - dy * dot) * il, dmz = (gdz - dz * dot) * il;
 
@@ -380,12 +364,15 @@ __device__ __forceinline__ void sh_elements(const BwdArgs& a, const float* s_sh,
 // MV: a batch of a.views views; phase 1 runs the chain once per view in which
 // the Gaussian touches a tile and sums the gradients (and the statistic over
 // the views), and keeps the summed SH gradient itself in LDS for phase 2.
-template <int DEG, bool ADAM, bool MV = false>
+// CJ (one view, no Adam): the chain takes the colour's direction gradient from
+// a.cjac, so phase 0 and the SH coefficients are not needed at all.
+template <int DEG, bool ADAM, bool MV = false, bool CJ = false>
 __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
+    static_assert(!CJ || (!ADAM && !MV), "the colour-Jacobian variant is the one-view gradient pass");
     constexpr int K = (DEG + 1) * (DEG + 1);
     constexpr int J = 3 * K;
     constexpr int LDG = kG + 1;
-    __shared__ float s_sh[J * LDG];
+    __shared__ float s_sh[CJ ? 1 : J * LDG];
     __shared__ float s_y[(MV ? J : K) * LDG];
     __shared__ float s_c[(MV ? 1 : 3) * LDG];
     const int t = threadIdx.x;
@@ -394,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
     const int cnt = ng * J;
     const size_t base = (size_t)g0 * J;
 
-    {
+    if constexpr (!CJ) {
         // every load of the thread's share is issued before the first LDS store,
         // so the block waits for one memory latency instead of one per batch
         constexpr int kPer = (J * kG + kThreads - 1) / kThreads;
@@ -478,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
         } else {
             const bool vis = a.tt[i] > 0;
             if (vis) {
-                chain<DEG>(a, a.cams[0], i, load_view(a, (size_t)i), s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb);
+                chain<DEG, CJ>(a, a.cams[0], i, load_view(a, (size_t)i), s_sh, t, LDG, dmu, dls, dq, dop, Y, drgb);
                 if (a.accum) {
                     const float2 d2 = *reinterpret_cast<const float2*>(a.grad2d + (size_t)i * GS_GRAD2D_STRIDE);
                     a.accum[i] = acc + sqrtf(d2.x * d2.x + d2.y * d2.y);
@@ -531,17 +518,17 @@ __global__ __launch_bounds__(kThreads) void k_grad3d(BwdArgs a) {
         }
     }
     __syncthreads();
-    sh_elements<DEG, ADAM, MV>(a, s_sh, LDG, s_y, s_c, cnt, base, t);
+    sh_elements<DEG, ADAM, MV>(a, CJ ? nullptr : s_sh, LDG, s_y, s_c, cnt, base, t);
 }
 
-template <bool ADAM, bool MV = false>
+template <bool ADAM, bool MV = false, bool CJ = false>
 inline void launch_grad3d(int deg, const BwdArgs& a, hipStream_t s) {
     const dim3 grid((a.n + kG - 1) / kG), block(kThreads);
     switch (deg) {
-        case 0: hipLaunchKernelGGL((k_grad3d<0, ADAM, MV>), grid, block, 0, s, a); break;
-        case 1: hipLaunchKernelGGL((k_grad3d<1, ADAM, MV>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_grad3d<2, ADAM, MV>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((k_grad3d<3, ADAM, MV>), grid, block, 0, s, a); break;
+        case 0: hipLaunchKernelGGL((k_grad3d<0, ADAM, MV, CJ>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((k_grad3d<1, ADAM, MV, CJ>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_grad3d<2, ADAM, MV, CJ>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((k_grad3d<3, ADAM, MV, CJ>), grid, block, 0, s, a); break;
     }
 }
 
@@ -587,6 +574,27 @@ extern "C" int gs_preprocess_bwd(const gs_camera* cam, const gs_settings* set, i
     fill_common(a, cam, 1, set, n, means, log_scales, quats, opacity_logits, sh, tiles_touched, clamp_mask, grad2d);
     a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
     launch_grad3d<false>(sh_degree, a, as_stream(stream));
+    return launch_status();
+}
+
+extern "C" int gs_preprocess_bwd_colorjac(const gs_camera* cam, const gs_settings* set, int32_t n,
+                                          int32_t sh_degree, const float* means, const float* log_scales,
+                                          const float* quats, const float* opacity_logits, const float* colorjac,
+                                          const int32_t* tiles_touched, const uint8_t* clamp_mask,
+                                          const float* grad2d, float* dmeans, float* dlog_scales, float* dquats,
+                                          float* dopacity_logits, float* dsh, void* stream) {
+    if (!camera_ok(cam) || !set || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
+    if (n == 0) return GS_OK;
+    if (!means || !log_scales || !quats || !opacity_logits || !colorjac || !tiles_touched || !clamp_mask ||
+        !grad2d || !dmeans || !dlog_scales || !dquats || !dopacity_logits || !dsh)
+        return GS_EINVAL;
+    if (!aligned16(quats) || !aligned16(grad2d) || !aligned16(dquats)) return GS_EALIGN;
+    BwdArgs a;
+    fill_common(a, cam, 1, set, n, means, log_scales, quats, opacity_logits, nullptr, tiles_touched, clamp_mask,
+                grad2d);
+    a.dmeans = dmeans; a.dls = dlog_scales; a.dquats = dquats; a.dopac = dopacity_logits; a.dsh = dsh;
+    a.cjac = colorjac;
+    launch_grad3d<false, false, true>(sh_degree, a, as_stream(stream));
     return launch_status();
 }
 

@@ -58,9 +58,11 @@ class GsGaussianSet(C.Structure):
                 ("exp_avg_sq", C.c_void_p * 5), ("densify_accum", C.c_void_p), ("densify_count", C.c_void_p)]
 
 
-SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_bin_workspace_size",
+SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs_preprocess_colorjac",
+           "gs_bin_workspace_size",
            "gs_bin_sort", "gs_bin_sort_noalloc", "gs_bin_scratch_bytes", "gs_debug_sort_wait_limit", "gs_bin_keys", "gs_render_fwd", "gs_render_fwd_loss",
-           "gs_render_bwd", "gs_preprocess_bwd", "gs_preprocess_bwd_adam", "gs_image_loss", "gs_densify_accum",
+           "gs_render_bwd", "gs_preprocess_bwd", "gs_preprocess_bwd_colorjac", "gs_preprocess_bwd_adam",
+           "gs_image_loss", "gs_densify_accum",
            "gs_adam_step", "gs_count_pairs", "gs_densify_workspace_size", "gs_densify", "gs_opacity_reset",
            "gs_preprocess_views", "gs_bin_workspace_size_views", "gs_bin_sort_views", "gs_render_fwd_views",
            "gs_render_fwd_loss_views", "gs_render_bwd_views", "gs_preprocess_bwd_views",
@@ -88,6 +90,7 @@ def load_library(path=LIB_PATH):
     lib.gs_version.argtypes = []
     lib.gs_tile_grid.argtypes = [P(GsCamera), P(_i32), P(_i32)]
     lib.gs_preprocess.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 10 + [_vp]
+    lib.gs_preprocess_colorjac.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 11 + [_vp]
     lib.gs_bin_workspace_size.argtypes = [_i32, P(GsCamera), _i64, P(C.c_size_t)]
     lib.gs_bin_sort.argtypes = [P(GsCamera), _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
     lib.gs_bin_keys.argtypes = [P(GsCamera), _vp, _vp, _vp, _vp, _vp]
@@ -98,6 +101,7 @@ def load_library(path=LIB_PATH):
     lib.gs_render_fwd_loss.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 8 + [_i32] + [_vp] * 4 + [_vp]
     lib.gs_render_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 9 + [_i32, _vp]
     lib.gs_preprocess_bwd.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
+    lib.gs_preprocess_bwd_colorjac.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 13 + [_vp]
     lib.gs_preprocess_bwd_adam.argtypes = ([P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 8 +
                                            [P(GsAdamState)] + [_vp] * 7 + [_vp])
     lib.gs_image_loss.argtypes = [_i32, _i64, _vp, _vp, _vp, _vp, _vp]
@@ -202,6 +206,18 @@ def gs_preprocess(cam, settings, sh_degree, means, log_scales, quats, opacity_lo
         _p(depth, f32, "depth"), _p(rect, torch.int16, "rect"), _p(tiles_touched, torch.int32, "tiles_touched"),
         _p(clamp_mask, torch.uint8, "clamp_mask"), _stream())
     _check(rc, "gs_preprocess")
+
+
+def gs_preprocess_colorjac(cam, settings, sh_degree, means, log_scales, quats, opacity_logits, sh,
+                           splats, depth, rect, tiles_touched, clamp_mask, colorjac):
+    f32, n = torch.float32, means.shape[0]
+    rc = load_library().gs_preprocess_colorjac(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, sh_degree,
+        _p(means, f32, "means"), _p(log_scales, f32, "log_scales"), _p(quats, f32, "quats"),
+        _p(opacity_logits, f32, "opacity_logits"), _p(sh, f32, "sh"), _p(splats, f32, "splats"),
+        _p(depth, f32, "depth"), _p(rect, torch.int16, "rect"), _p(tiles_touched, torch.int32, "tiles_touched"),
+        _p(clamp_mask, torch.uint8, "clamp_mask"), _p(colorjac, f32, "colorjac"), _stream())
+    _check(rc, "gs_preprocess_colorjac")
 
 
 def gs_bin_workspace_size(n, cam, key_capacity):
@@ -316,6 +332,19 @@ def gs_preprocess_bwd(cam, settings, sh_degree, means, log_scales, quats, opacit
         _p(grad2d, f32, "grad2d"), _p(dmeans, f32, "dmeans"), _p(dlog_scales, f32, "dlog_scales"),
         _p(dquats, f32, "dquats"), _p(dopacity_logits, f32, "dopacity_logits"), _p(dsh, f32, "dsh"), _stream())
     _check(rc, "gs_preprocess_bwd")
+
+
+def gs_preprocess_bwd_colorjac(cam, settings, sh_degree, means, log_scales, quats, opacity_logits, colorjac,
+                               tiles_touched, clamp_mask, grad2d, dmeans, dlog_scales, dquats, dopacity_logits, dsh):
+    f32, n = torch.float32, means.shape[0]
+    rc = load_library().gs_preprocess_bwd_colorjac(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, sh_degree,
+        _p(means, f32, "means"), _p(log_scales, f32, "log_scales"), _p(quats, f32, "quats"),
+        _p(opacity_logits, f32, "opacity_logits"), _p(colorjac, f32, "colorjac"),
+        _p(tiles_touched, torch.int32, "tiles_touched"), _p(clamp_mask, torch.uint8, "clamp_mask"),
+        _p(grad2d, f32, "grad2d"), _p(dmeans, f32, "dmeans"), _p(dlog_scales, f32, "dlog_scales"),
+        _p(dquats, f32, "dquats"), _p(dopacity_logits, f32, "dopacity_logits"), _p(dsh, f32, "dsh"), _stream())
+    _check(rc, "gs_preprocess_bwd_colorjac")
 
 
 LOSS_PARTIALS = 1024
@@ -662,6 +691,10 @@ class Rasterizer:
 
     forward(params) runs gs_preprocess, gs_bin_sort and gs_render_fwd;
     backward(params, dL_dimage) runs gs_render_bwd and gs_preprocess_bwd.
+    With colorjac (the default, at SH degree >= 1) the preprocess is
+    gs_preprocess_colorjac and the 2D -> 3D backward gs_preprocess_bwd_colorjac:
+    the forward keeps each Gaussian's colour gradient with respect to the view
+    direction (9 floats), so the backward does not read the SH coefficients again.
     The number of (tile, Gaussian) pairs K is data dependent: the list buffer has
     `key_capacity` entries and binning raises a device flag when K exceeds it.
     `forward(check=True)` synchronises once, grows the capacity and re-bins when
@@ -673,7 +706,8 @@ class Rasterizer:
     raising GsError with the names of the tensors that hold them.
     """
 
-    def __init__(self, cam, n, sh_degree, settings=None, key_capacity=None, device="cuda", debug=False):
+    def __init__(self, cam, n, sh_degree, settings=None, key_capacity=None, device="cuda", debug=False,
+                 colorjac=True):
         load_library()
         self.cam, self.n, self.deg = cam, int(n), int(sh_degree)
         self.debug = bool(debug)
@@ -697,6 +731,8 @@ class Rasterizer:
         self.final_T = torch.empty((H, W), dtype=torch.float32, device=dev)
         self.n_contrib = torch.empty((H, W), dtype=torch.int32, device=dev)
         self.grad2d = torch.empty((n, GRAD2D_STRIDE), dtype=torch.float32, device=dev)
+        self.colorjac = (torch.empty((n, 9), dtype=torch.float32, device=dev)
+                         if colorjac and self.deg > 0 else None)
         self.generation = 0  # forward passes run so far; the autograd wrapper checks it
         self._alloc_lists(key_capacity if key_capacity is not None else max(4 * n, 1 << 16))
 
@@ -710,9 +746,14 @@ class Rasterizer:
         self.workspace = self.workspace[off:off + ws]
 
     def preprocess(self, p):
-        gs_preprocess(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
-                      p["opacity_logits"], p["sh"], self.splats, self.depth, self.rect, self.tiles_touched,
-                      self.clamp)
+        if self.colorjac is not None:
+            gs_preprocess_colorjac(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
+                                   p["opacity_logits"], p["sh"], self.splats, self.depth, self.rect,
+                                   self.tiles_touched, self.clamp, self.colorjac)
+        else:
+            gs_preprocess(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
+                          p["opacity_logits"], p["sh"], self.splats, self.depth, self.rect, self.tiles_touched,
+                          self.clamp)
 
     def bin(self):
         gs_bin_sort(self.cam, self.n, self.depth, self.rect, self.tiles_touched, self.key_capacity, self.point_list,
@@ -755,13 +796,24 @@ class Rasterizer:
                       self.tile_order[1])
         return self.grad2d
 
+    def backward_3d(self, p, out):
+        """The 2D -> 3D backward of the last forward's parameters p into out (from self.grad2d)."""
+        if self.colorjac is not None:
+            gs_preprocess_bwd_colorjac(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
+                                       p["opacity_logits"], self.colorjac, self.tiles_touched, self.clamp,
+                                       self.grad2d, out["means"], out["log_scales"], out["quats"],
+                                       out["opacity_logits"], out["sh"])
+        else:
+            gs_preprocess_bwd(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
+                              p["opacity_logits"], p["sh"], self.tiles_touched, self.clamp, self.grad2d,
+                              out["means"], out["log_scales"], out["quats"], out["opacity_logits"], out["sh"])
+        return out
+
     def backward(self, p, dL_dimage, out=None):
         self.backward_2d(dL_dimage)
         if out is None:
             out = {k: torch.empty_like(p[k]) for k in ("means", "log_scales", "quats", "opacity_logits", "sh")}
-        gs_preprocess_bwd(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
-                          p["opacity_logits"], p["sh"], self.tiles_touched, self.clamp, self.grad2d,
-                          out["means"], out["log_scales"], out["quats"], out["opacity_logits"], out["sh"])
+        self.backward_3d(p, out)
         if self.debug:
             check_finite({"dL_dimage": dL_dimage, "grad2d": self.grad2d, **{"d" + k: v for k, v in out.items()}})
         return out
@@ -937,7 +989,7 @@ class Trainer:
 
     def _rebuild(self):
         dev = self.p["means"].device
-        self.rast = Rasterizer(self.cam, self.n, self.deg, settings=self.settings, device=dev)
+        self.rast = Rasterizer(self.cam, self.n, self.deg, settings=self.settings, device=dev, colorjac=False)
         self.accum = torch.zeros(self.n, dtype=torch.float32, device=dev)
         self.count = torch.zeros(self.n, dtype=torch.int32, device=dev)
         self.dL = torch.empty_like(self.target)

@@ -114,6 +114,25 @@ int gs_preprocess(const gs_camera* cam, const gs_settings* set, int32_t n, int32
                   float* splats, float* depth, int16_t* rect, int32_t* tiles_touched,
                   uint8_t* clamp_mask, void* stream);
 
+/*
+ * gs_preprocess_colorjac -- gs_preprocess that also keeps, for the 2D -> 3D
+ * backward, the gradient of each colour channel with respect to the viewing
+ * direction ([P3] section 4: the colour gradient reaches the mean through the
+ * SH basis evaluated at the direction from the camera centre).
+ * Out, besides gs_preprocess's: colorjac [n,9] float32, row-major by channel:
+ *   colorjac[9 i + 3 c + j] = d(sum_k sh[i,k,c] Y_k(d)) / d d_j at the unit
+ *   direction d of Gaussian i, the Y_k taken as polynomials of (d_x, d_y, d_z)
+ *   (before the clamp at 0 and the +0.5; zero for culled Gaussians and at SH
+ *   degree 0).  Caller-owned, 4-byte aligned; NULL is an error.
+ * gs_preprocess_bwd_colorjac then needs no SH coefficients: 36 bytes per
+ * Gaussian replace its (deg+1)^2 * 12 bytes of coefficients.
+ */
+int gs_preprocess_colorjac(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                           const float* means, const float* log_scales, const float* quats,
+                           const float* opacity_logits, const float* sh,
+                           float* splats, float* depth, int16_t* rect, int32_t* tiles_touched,
+                           uint8_t* clamp_mask, float* colorjac, void* stream);
+
 /* Bytes of workspace gs_bin_sort needs for n Gaussians and key_capacity list
    entries. */
 int gs_bin_workspace_size(int32_t n, const gs_camera* cam, int64_t key_capacity, size_t* bytes);
@@ -264,6 +283,22 @@ int gs_preprocess_bwd(const gs_camera* cam, const gs_settings* set, int32_t n, i
                       const int32_t* tiles_touched, const uint8_t* clamp_mask, const float* grad2d,
                       float* dmeans, float* dlog_scales, float* dquats, float* dopacity_logits,
                       float* dsh, void* stream);
+
+/*
+ * gs_preprocess_bwd_colorjac -- gs_preprocess_bwd with the colour's direction
+ * gradient read from colorjac (gs_preprocess_colorjac of the same parameters
+ * and camera) instead of being rebuilt from the SH coefficients, which it does
+ * not read.  The view-direction term of dmeans is
+ * sum_c drgb_c colorjac[i, c, :] projected onto the sphere, drgb_c = 0 for a
+ * channel clamped at 0 (clamp_mask).  Same outputs, shapes and errors as
+ * gs_preprocess_bwd; colorjac NULL is an error.
+ */
+int gs_preprocess_bwd_colorjac(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                               const float* means, const float* log_scales, const float* quats,
+                               const float* opacity_logits, const float* colorjac,
+                               const int32_t* tiles_touched, const uint8_t* clamp_mask, const float* grad2d,
+                               float* dmeans, float* dlog_scales, float* dquats, float* dopacity_logits,
+                               float* dsh, void* stream);
 
 /*
  * gs_image_loss -- image reconstruction loss ([P4] E.1).  mode 1: L1,

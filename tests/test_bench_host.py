@@ -64,6 +64,16 @@ def test_raster_roofline_scales_with_the_work():
     assert c["t_min_us"]["render_fwd"] == a["t_min_us"]["render_fwd"]
 
 
+def test_raster_roofline_with_the_colour_jacobian():
+    """With the colour-direction Jacobian the preprocess writes 36 more bytes per Gaussian and the
+    2D->3D backward reads them instead of the SH coefficients (192 bytes at degree 3)."""
+    a = bench.raster_roofline(1_000_000, 5e6, 3, 3e8, 3e8, 1e8, 1.0, PEAKS)
+    j = bench.raster_roofline(1_000_000, 5e6, 3, 3e8, 3e8, 1e8, 1.0, PEAKS, colorjac=True)
+    hbm = bench.PEAK_HBM_GBS * 1e3  # bytes per us
+    assert (j["t_min_us"]["preprocess"] - a["t_min_us"]["preprocess"]) * hbm == pytest.approx(36e6, rel=2e-3)
+    assert (a["t_min_us"]["preprocess_bwd"] - j["t_min_us"]["preprocess_bwd"]) * hbm == pytest.approx(156e6, rel=2e-3)
+
+
 def test_host_cpu_description():
     h = bench.host_cpu()
     assert isinstance(h["cpu_model"], str) and h["cpu_model"]

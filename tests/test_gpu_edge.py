@@ -143,6 +143,37 @@ def test_opaque_entries_clamp():
     log(f"opaque entries: {clamp_px} pixels within rounding of the clamp masked")
 
 
+@pytest.mark.parametrize("deg", [0, 1, 2, 3])
+def test_colorjac_backward_matches_sh_backward(deg):
+    """gs_preprocess_colorjac + gs_preprocess_bwd_colorjac (the colour's direction gradient kept
+    from the forward, no SH re-read) against gs_preprocess + gs_preprocess_bwd on the same scene,
+    parameters and upstream gradient, and both against the oracle (3DGS backward, section 4)."""
+    import torch
+    from oracle import oracle as O
+    gs = _gs()
+    sc = scenes.random_small(60 + deg, n=400, width=72, height=56, sh_degree=deg)
+    p = to_dev(sc.params())
+    o = O.render(sc.cam, sc.sh_degree, sc.params(), backward=False)
+    amb = o["ambiguous"] > 0
+    dL = np.asarray(sc.dL_dimage, np.float64) * (~amb)[None]
+    dL_dev = torch.from_numpy(dL.astype(np.float32)).cuda()
+    out = {}
+    for cj in (True, False):
+        r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree, colorjac=cj)
+        assert (r.colorjac is not None) == (cj and deg > 0)
+        r.forward(p, check=True)
+        out[cj] = {k: v.cpu().numpy() for k, v in r.backward(p, dL_dev).items()}
+        if cj and deg > 0:
+            jac = r.colorjac.cpu().numpy()
+            assert np.all(jac[r.tiles_touched.cpu().numpy() == 0] == 0)
+            assert np.abs(jac).max() > 0
+    o2 = O.render_bwd(sc.cam, o["pre"], o["point_list"], o["ranges"], dL)
+    o3 = O.preprocess_bwd(sc.cam, sc.sh_degree, sc.params(), o["pre"]["tiles_touched"], o2)
+    for k in PARAM_KEYS:
+        assert rel_l2(out[True][k], out[False][k]) <= 1e-5, k
+        assert rel_l2(out[True][k], o3[k]) <= 1e-3, k
+
+
 def test_capacity_overflow_flag():
     """K > key_capacity: the flag is raised, no range is written, nothing is written out of bounds."""
     import torch
@@ -198,6 +229,10 @@ def test_abi_errors():
     assert lib.gs_preprocess(C.byref(cam), C.byref(st), n, 0, None, *([ptr] * 9), None) == -1
     # misaligned quats
     assert lib.gs_preprocess(C.byref(cam), C.byref(st), n, 0, ptr, ptr, mis, *([ptr] * 7), None) == -2
+    # the colour-Jacobian variants need their buffer
+    assert lib.gs_preprocess_colorjac(C.byref(cam), C.byref(st), n, 1, *([ptr] * 10), None, None) == -1
+    assert lib.gs_preprocess_bwd_colorjac(C.byref(cam), C.byref(st), n, 1, *([ptr] * 4), None,
+                                          *([ptr] * 8), None) == -1
     # workspace too small
     assert lib.gs_bin_sort(C.byref(cam), n, ptr, ptr, ptr, 16, ptr, ptr, ptr, ptr, ptr, 8, None) == -3
     # capacity over the index limit
