@@ -342,7 +342,8 @@ class TrainStep:
         dev = "cuda"
         self.p = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in sc.params().items()}
         self.target = torch.from_numpy(sc.target).to(dev)
-        self.rast = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
+        # the fused Adam tail reads the SH coefficients anyway: no colour-direction Jacobian
+        self.rast = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree, colorjac=False)
         self.dL = torch.empty_like(self.target)
         self.loss = torch.zeros(1 + self.rast.ntiles, dtype=torch.float64, device=dev)
         self.m = {k: torch.zeros_like(v) for k, v in self.p.items()}
