@@ -817,3 +817,84 @@ void orc_opacity_reset(int N, double factor, double* logit)
         logit[i] = log(y / (1.0 - y));
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* 16-bit splat records.  [P3] section 5 stores some intermediate values as   */
+/* 16-bit floats to save memory traffic; section 7 runs the rendering path in */
+/* FP16 and keeps gradient accumulation in FP32.  The record this models      */
+/* keeps the 2D mean in float32 and stores the conic (as its scaled Cholesky  */
+/* factor), the opacity and the colour in IEEE 754 binary16.                  */
+/* ------------------------------------------------------------------------- */
+
+/* The binary16 number nearest to x, ties to the even significand (IEEE 754
+ * binary16: 11-bit significand, exponents -14..15, subnormal spacing 2^-24,
+ * largest finite 65504).  |x| >= 65520, the midpoint between 65504 and 2^16,
+ * rounds to infinity.  Computed by scaling x to an integer multiple of its
+ * binade's spacing, which is exact in double. */
+double orc_round_binary16(double x)
+{
+    if (x != x || x == 0.0) return x;
+    double a = fabs(x);
+    if (a >= 65520.0) return x > 0 ? INFINITY : -INFINITY;
+    int k;
+    frexp(a, &k);              /* a = m 2^k, 0.5 <= m < 1: the binade is [2^(k-1), 2^k) */
+    int e = k - 1;
+    if (e < -14) e = -14;      /* subnormals share the spacing of the lowest binade */
+    double s = ldexp(1.0, e - 10);
+    double q = a / s;          /* exact: s is a power of two */
+    double r = floor(q), f = q - r;
+    if (f > 0.5 || (f == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    double y = r * s;
+    return x < 0 ? -y : y;
+}
+
+/* A value as the record stores it: the binary16 rounding of its float32
+ * rounding (the record is written from the float32 projection). */
+static double rec16(double v) { return orc_round_binary16((double)(float)v); }
+
+/*
+ * The 2D quantities a blend reads from a 16-bit record, for every Gaussian
+ * (zero where valid[i] == 0).  The record holds
+ *   u, v              the 2D mean rounded to float32;
+ *   L00, L10, L11     the lower Cholesky factor of the conic A = Sigma'^-1
+ *                     (Sigma' = [[a, b], [b, c]] the 2D covariance, det =
+ *                     a c - b^2) scaled by s = sqrt(log2(e) / 2), so that
+ *                     |L^T d|^2 = log2(e) d^T A d / 2:
+ *                     L00 = s sqrt(c / det), L10 = -s b / sqrt(c det),
+ *                     L11 = s / sqrt(c);
+ *   opacity, r, g, b;
+ * each of the last seven as rec16 gives it.  Out: uv16 = (u, v); conic16 =
+ * the conic that record represents, L L^T / s^2 = (L00^2, L00 L10,
+ * L10^2 + L11^2) / s^2 as (A, B, C); opacity16, rgb16.
+ */
+void orc_record16(int N, const double* uv, const double* cov2d, const double* opacity, const double* rgb,
+                  const unsigned char* valid, double* uv16, double* conic16, double* opacity16, double* rgb16)
+{
+    const double s2 = 0.5 / log(2.0); /* s^2 = log2(e) / 2 */
+    const double s = sqrt(s2);
+    for (int i = 0; i < N; ++i) {
+        uv16[2 * i] = uv16[2 * i + 1] = 0;
+        conic16[3 * i] = conic16[3 * i + 1] = conic16[3 * i + 2] = 0;
+        opacity16[i] = 0;
+        rgb16[3 * i] = rgb16[3 * i + 1] = rgb16[3 * i + 2] = 0;
+        if (!valid[i]) continue;
+        const double a = cov2d[3 * i], b = cov2d[3 * i + 1], c = cov2d[3 * i + 2];
+        const double det = a * c - b * b;
+        const double l00 = rec16(s * sqrt(c / det));
+        const double l10 = rec16(-s * b / sqrt(c * det));
+        const double l11 = rec16(s / sqrt(c));
+        uv16[2 * i] = (float)uv[2 * i];
+        uv16[2 * i + 1] = (float)uv[2 * i + 1];
+        conic16[3 * i] = l00 * l00 / s2;
+        conic16[3 * i + 1] = l00 * l10 / s2;
+        conic16[3 * i + 2] = (l10 * l10 + l11 * l11) / s2;
+        opacity16[i] = rec16(opacity[i]);
+        for (int ch = 0; ch < 3; ++ch) rgb16[3 * i + ch] = rec16(rgb[3 * i + ch]);
+    }
+}
+
+/* orc_round_binary16 over an array (out may alias in). */
+void orc_round_binary16_array(int64_t n, const double* in, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_round_binary16(in[i]);
+}

@@ -353,3 +353,27 @@ def opacity_reset(logits, factor):
     x = _d(logits).copy()
     lib().orc_opacity_reset(C.c_int(x.size), C.c_double(factor), _p(x))
     return x
+
+
+def round_binary16(x):
+    """The nearest IEEE 754 binary16 values (ties to even; |x| >= 65520 to inf), as float64."""
+    x = _d(x)
+    out = np.zeros_like(x)
+    lib().orc_round_binary16_array(C.c_int64(x.size), _p(x), _p(out))
+    return out
+
+
+def record16(pre):
+    """The 2D quantities the blends read from 16-bit splat records ([P3] sections 5
+    and 7): float32 mean; conic (through its scaled Cholesky factor), opacity and
+    colour rounded to float32 and then to binary16.  Returns a copy of `pre` with
+    uv, conic, opacity and rgb replaced; rect, tiles_touched, depth and the cull
+    flags stay those of the full-precision projection."""
+    N = pre["uv"].shape[0]
+    out = dict(pre)
+    out.update(uv=np.zeros((N, 2)), conic=np.zeros((N, 3)), opacity=np.zeros(N), rgb=np.zeros((N, 3)))
+    valid = np.ascontiguousarray(pre["valid"], dtype=np.uint8)
+    lib().orc_record16(C.c_int(N), _p(_d(pre["uv"])), _p(_d(pre["cov2d"])), _p(_d(pre["opacity"])),
+                       _p(_d(pre["rgb"])), _p(valid, C.c_uint8), _p(out["uv"]), _p(out["conic"]),
+                       _p(out["opacity"]), _p(out["rgb"]))
+    return out
