@@ -198,13 +198,13 @@ class RasterPass:
     preprocess, bin, forward (with the scene's loss fused in when it has one, else the given
     upstream gradient), backward blend, 2D->3D backward with the gradients written out."""
 
-    def __init__(self, sc):
+    def __init__(self, sc, record16=False):
         import torch
         from differentiable_gaussian_splatting_dgs_amd import gs
         self.gs, self.torch, self.sc = gs, torch, sc
         dev = "cuda"
         self.p = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in sc.params().items()}
-        self.r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree)
+        self.r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree, record16=record16)
         self.g3 = {k: torch.empty_like(v) for k, v in self.p.items()}
         self.loss = torch.zeros(1 + self.r.ntiles, dtype=torch.float64, device=dev)
         if sc.loss:
@@ -327,6 +327,34 @@ def raster_line(name, steps, warmup, peaks):
                 roofline=kernel_roofline(timed_ms, p_fwd, p_bwd, p_blend, peaks, name),
                 peaks=peaks)
     return line, sc
+
+
+def record16_measure(sc, steps, warmup, ref):
+    """The same fwd+bwd pass with 16-bit splat records (24 bytes gathered per list entry instead of
+    48; conic factor, opacity and colour in binary16), timed like the main line; ref is the main
+    line, for the stage-by-stage comparison."""
+    import torch
+    from differentiable_gaussian_splatting_dgs_amd import gs
+    assert sc.loss is None, "the 16-bit record pass takes a given upstream gradient"
+    rp = RasterPass(sc, record16=True)
+    r = rp.r
+    ms, stage, pct, bwd_ms = time_passes(rp.run, len(STAGES), steps, warmup,
+                                         first=lambda: r.forward(rp.p, check=True), watch=STAGES.index("render_bwd"))
+    if gs.check_bin_status(r.overflow.item()):
+        raise gs.GsError("list capacity overflow during timing")
+    p_fwd, p_bwd, p_blend = (float(x) for x in r.count_pairs().cpu().numpy())
+    K = float(r.num_keys.item())
+    stage_ms = dict(zip(STAGES, stage))
+    out = dict(ms_per_step=round(ms, 4), value=(p_fwd + p_bwd) / (ms * 1e-3), unit="blend pairs/s",
+               stage_ms={k: round(v, 4) for k, v in stage_ms.items()}, step_ms_events=pct,
+               render_bwd_timed_ms=round(bwd_ms, 4),
+               pairs=dict(fwd_evaluated=p_fwd, bwd_walked=p_bwd, blended=p_blend, keys=int(K)),
+               record_bytes=24, record_bytes_float32=48,
+               speedup_vs_float32={k: round(ref["stage_ms"][k] / v, 4) for k, v in stage_ms.items() if v > 0})
+    out["speedup_vs_float32"]["step"] = round(ref["ms_per_step"] / ms, 4)
+    del rp
+    torch.cuda.empty_cache()
+    return out
 
 
 class TrainStep:
@@ -594,6 +622,8 @@ def main():
         return
     line, sc = raster_line(args.workload, args.steps, args.warmup, peaks)
     if args.workload == "clusters1m" and not args.no_extras:
+        print("# 16-bit splat records ...", file=sys.stderr, flush=True)
+        line["record16"] = record16_measure(sc, args.steps, args.warmup, line)
         print("# training step ...", file=sys.stderr, flush=True)
         tr, st = train_measure(args.steps, args.warmup)
         line["train1m"] = tr

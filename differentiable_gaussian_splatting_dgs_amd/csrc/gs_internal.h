@@ -16,6 +16,7 @@ constexpr float kLog2e = 1.4426950408889634f;  // log2(e)
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? GS_OK : GS_EHIP; }
 

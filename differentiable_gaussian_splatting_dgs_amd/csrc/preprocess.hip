@@ -30,7 +30,15 @@ struct PreArgs {
     int32_t* tiles_touched;
     uint8_t* clamp;
     float* cjac;  // optional [views, n, 9]: d colour_c / d dir_j before the clamp, row-major by c
+    bool h16;     // splats holds 16-bit records (GS_SPLAT16_STRIDE floats each)
 };
+
+// Two floats as one word of binary16 values, lo in the low half; each is the
+// binary16 number nearest to the float (ties to even, the hardware conversion).
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
 
 // Real spherical harmonics with the Condon-Shortley phase as polynomials of
 // the unit direction: Y[l*l + l + m].  Constants are the normalisations
@@ -116,8 +124,9 @@ __device__ __forceinline__ void shade(const CamArgs& c, double mx, double my, do
 // One thread per Gaussian: projection, tile rectangle and the SH colour, for
 // each view in turn (the parameters are read once; the view-free parts --
 // opacity, M = R S -- are computed once).  CJ: also the colour's gradient with
-// respect to the view direction (a.cjac).
-template <int DEG, bool VEC, bool CJ>
+// respect to the view direction (a.cjac).  H16: 16-bit splat records (the
+// float32 mean, then the conic factor, opacity and colour in binary16).
+template <int DEG, bool VEC, bool CJ, bool H16>
 __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
     constexpr int J = 3 * (DEG + 1) * (DEG + 1);
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -127,8 +136,13 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
 
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
     auto cull = [&](size_t o) {
-        float4* sp = reinterpret_cast<float4*>(a.splats + o * GS_SPLAT_STRIDE);
-        sp[0] = z4; sp[1] = z4; sp[2] = z4;
+        if constexpr (H16) {
+            uint2* sp = reinterpret_cast<uint2*>(a.splats + o * GS_SPLAT16_STRIDE);
+            sp[0] = sp[1] = sp[2] = make_uint2(0u, 0u);
+        } else {
+            float4* sp = reinterpret_cast<float4*>(a.splats + o * GS_SPLAT_STRIDE);
+            sp[0] = z4; sp[1] = z4; sp[2] = z4;
+        }
         if constexpr (CJ)
             for (int k = 0; k < 9; ++k) a.cjac[9 * o + k] = 0.f;
         a.clamp[o] = 0;
@@ -236,11 +250,22 @@ __global__ __launch_bounds__(kPreBlock) void k_preprocess(PreArgs a) {
         const double l10 = -cb / sqrt(cc * det) * sc;
         const double l11 = sc / sqrt(cc);
 
-        float4* sp = reinterpret_cast<float4*>(a.splats + o * GS_SPLAT_STRIDE);
         const float uf = (float)u, vf = (float)v;
-        sp[0] = make_float4(uf, vf, (float)(u - (double)uf), (float)(v - (double)vf));
-        sp[1] = make_float4((float)l00, (float)l10, (float)l11, (float)sigma);
-        sp[2] = make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
+        if constexpr (H16) {
+            // binary16 of the float32 value: the record is the float32 one, rounded.  Without
+            // contraction the two roundings stay two (with it they may be folded into one
+            // double -> binary16 rounding, which differs near binary16 ties).
+#pragma clang fp contract(off)
+            uint2* sp = reinterpret_cast<uint2*>(a.splats + o * GS_SPLAT16_STRIDE);
+            sp[0] = make_uint2(__float_as_uint(uf), __float_as_uint(vf));
+            sp[1] = make_uint2(pack_h2((float)l00, (float)l10), pack_h2((float)l11, (float)sigma));
+            sp[2] = make_uint2(pack_h2((float)rgb[0], (float)rgb[1]), pack_h2((float)rgb[2], 0.f));
+        } else {
+            float4* sp = reinterpret_cast<float4*>(a.splats + o * GS_SPLAT_STRIDE);
+            sp[0] = make_float4(uf, vf, (float)(u - (double)uf), (float)(v - (double)vf));
+            sp[1] = make_float4((float)l00, (float)l10, (float)l11, (float)sigma);
+            sp[2] = make_float4((float)rgb[0], (float)rgb[1], (float)rgb[2], 0.f);
+        }
         a.clamp[o] = cm;
         a.depth[o] = (float)tz;
         const uint32_t r0 = (uint32_t)(uint16_t)tx0 | ((uint32_t)(uint16_t)ty0 << 16);
@@ -258,18 +283,26 @@ using namespace gs;
 namespace gs {
 namespace {
 
+template <int DEG, bool VEC, bool H16>
+void launch_pre_rec(dim3 grid, dim3 block, hipStream_t s, const PreArgs& a) {
+    if (a.cjac)
+        hipLaunchKernelGGL((k_preprocess<DEG, VEC, true, H16>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((k_preprocess<DEG, VEC, false, H16>), grid, block, 0, s, a);
+}
+
 template <int DEG, bool VEC>
 void launch_pre(dim3 grid, dim3 block, hipStream_t s, const PreArgs& a) {
-    if (a.cjac)
-        hipLaunchKernelGGL((k_preprocess<DEG, VEC, true>), grid, block, 0, s, a);
+    if (a.h16)
+        launch_pre_rec<DEG, VEC, true>(grid, block, s, a);
     else
-        hipLaunchKernelGGL((k_preprocess<DEG, VEC, false>), grid, block, 0, s, a);
+        launch_pre_rec<DEG, VEC, false>(grid, block, s, a);
 }
 
 int preprocess_impl(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                     int32_t sh_degree, const float* means, const float* log_scales, const float* quats,
                     const float* opacity_logits, const float* sh, float* splats, float* depth, int16_t* rect,
-                    int32_t* tiles_touched, uint8_t* clamp_mask, float* cjac, void* stream) {
+                    int32_t* tiles_touched, uint8_t* clamp_mask, float* cjac, void* stream, bool h16 = false) {
     if (!views_ok(cams, views) || n < 0 || sh_degree < 0 || sh_degree > GS_MAX_SH_DEGREE) return GS_EINVAL;
     if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
     if (!set) return GS_EINVAL;
@@ -277,7 +310,7 @@ int preprocess_impl(const gs_camera* cams, int32_t views, const gs_settings* set
     if (!means || !splats || !log_scales || !quats || !opacity_logits || !depth || !rect || !tiles_touched || !sh ||
         !clamp_mask)
         return GS_EINVAL;
-    if (!aligned16(splats) || !aligned16(quats) || !aligned16(rect)) return GS_EALIGN;
+    if (!(h16 ? aligned8(splats) : aligned16(splats)) || !aligned16(quats) || !aligned16(rect)) return GS_EALIGN;
     PreArgs a{};
     for (int v = 0; v < views; ++v) a.cams[v] = cam_args(cams + v);
     a.views = views;
@@ -286,6 +319,7 @@ int preprocess_impl(const gs_camera* cams, int32_t views, const gs_settings* set
     a.means = means; a.log_scales = log_scales; a.quats = quats; a.opac = opacity_logits; a.sh = sh;
     a.splats = splats; a.depth = depth; a.rect = rect; a.tiles_touched = tiles_touched; a.clamp = clamp_mask;
     a.cjac = cjac;
+    a.h16 = h16;
     const dim3 grid((n + kPreBlock - 1) / kPreBlock), block(kPreBlock);
     hipStream_t s = as_stream(stream);
     const bool vec = aligned16(sh);
@@ -326,4 +360,13 @@ extern "C" int gs_preprocess_views(const gs_camera* cams, int32_t views, const g
                                    void* stream) {
     return preprocess_impl(cams, views, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
                            splats, depth, rect, tiles_touched, clamp_mask, nullptr, stream);
+}
+
+extern "C" int gs_preprocess_h16(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                                 const float* means, const float* log_scales, const float* quats,
+                                 const float* opacity_logits, const float* sh, float* splats16, float* depth,
+                                 int16_t* rect, int32_t* tiles_touched, uint8_t* clamp_mask, float* colorjac,
+                                 void* stream) {
+    return preprocess_impl(cam, 1, set, n, sh_degree, means, log_scales, quats, opacity_logits, sh,
+                           splats16, depth, rect, tiles_touched, clamp_mask, colorjac, stream, true);
 }

@@ -114,6 +114,28 @@ __device__ __forceinline__ Staged stage_record(float4 r0, float4 r1, float4 r2, 
     return st;
 }
 
+// The three float4 rows stage_record takes, from splat record g.  H16: a 16-bit
+// record (u, v in float32; then L00, L10 | L11, opacity | r, g | b, 0 as binary16
+// pairs, low half first), read as three 8-byte words and widened exactly; its
+// mean residual is zero.
+template <bool H16>
+__device__ __forceinline__ void load_record(const float* splats, uint32_t g, float4& r0, float4& r1, float4& r2) {
+    if constexpr (H16) {
+        const uint2* sp = reinterpret_cast<const uint2*>(splats + (size_t)g * GS_SPLAT16_STRIDE);
+        const uint2 w0 = sp[0], w1 = sp[1], w2 = sp[2];
+        auto lo = [](uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); };
+        auto hi = [](uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); };
+        r0 = make_float4(__uint_as_float(w0.x), __uint_as_float(w0.y), 0.f, 0.f);
+        r1 = make_float4(lo(w1.x), hi(w1.x), lo(w1.y), hi(w1.y));
+        r2 = make_float4(lo(w2.x), hi(w2.x), lo(w2.y), 0.f);
+    } else {
+        const float4* sp = reinterpret_cast<const float4*>(splats + (size_t)g * GS_SPLAT_STRIDE);
+        r0 = sp[0];
+        r1 = sp[1];
+        r2 = sp[2];
+    }
+}
+
 // Transmittance after blending alpha: T (1 - alpha) as one fused operation.  The
 // forward and the pair counter both use it, so they stop at the same entry.
 __device__ __forceinline__ float trans_after(float T, float alpha) { return __builtin_fmaf(-alpha, T, T); }
@@ -134,10 +156,11 @@ __device__ __forceinline__ float edge_min(float a, float b, float l, float c, fl
     return __builtin_fmaf(e1, e1, e2 * e2);
 }
 
+template <bool H16>
 __device__ __forceinline__ uint32_t stage_entry(const RenderArgs& a, uint32_t g, float x0, float y0,
                                                 float log2_amin_inv, Stage st, int slot) {
-    const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
-    const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
+    float4 r0, r1, r2;
+    load_record<H16>(a.splats, g, r0, r1, r2);
     const Staged rec = stage_record(r0, r1, r2, x0, y0);
     const float ut = rec.ut, vt = rec.vt;
     st.g0[slot] = rec.g0;
@@ -189,6 +212,7 @@ __device__ __forceinline__ int compact(const uint8_t* s_mask, uint16_t* list, in
     return cnt;
 }
 
+template <bool H16>
 __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
     __shared__ float4 s_g0[kBlock];
     __shared__ float4 s_g1[kBlock];
@@ -238,7 +262,7 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
         uint32_t m = 0;
         if (k < range.y) {
             const uint32_t g = a.list[k];
-            if (g < a.n) m = stage_entry(a, g, x0, y0, log2_amin_inv, st, tid);
+            if (g < a.n) m = stage_entry<H16>(a, g, x0, y0, log2_amin_inv, st, tid);
         }
         // the previous batch's flags are final (the loop ends with a barrier)
         if (kprev != 0xffffffffu) flag_out(kprev);
@@ -621,7 +645,7 @@ constexpr uint32_t kBwdClamp = 1u << 12;  // list flag: the entry's opacity can 
 // reduction and atomic update per entry cost more than the extra waves give.
 constexpr int kBwdSplitBelow = 1024;
 
-template <int QPW>
+template <int QPW, bool H16>
 __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
     static_assert(QPW == 4 || QPW == 2, "four or two quadrants per wave");
     constexpr int kSplit = 4 / QPW;
@@ -752,8 +776,8 @@ __global__ __launch_bounds__(64) void k_render_bwd(RenderArgs a) {
             if (g < a.n) {
                 m = ((uint32_t)a.contrib[k] >> qbase) & ((1u << QPW) - 1u);  // this wave's quadrants
                 if (m) {
-                    const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
-                    const float4 r0 = sp[0], r1 = sp[1], r2 = sp[2];
+                    float4 r0, r1, r2;
+                    load_record<H16>(a.splats, g, r0, r1, r2);
                     const Staged rec = stage_record(r0, r1, r2, x0, y0);
                     s_g0[lane] = rec.g0;
                     s_g1[lane] = rec.g1;
@@ -945,6 +969,7 @@ __global__ void k_zero_f32(float* p, size_t count) {
 
 // Pair counts: one thread per pixel, walking the whole tile list.  ev_px
 // (optional, [views, H, W]) receives each pixel's evaluated entries.
+template <bool H16>
 __global__ __launch_bounds__(256) void k_count_pairs(RenderArgs a, unsigned long long* counts, int32_t* ev_px) {
     __shared__ unsigned long long s_c[3];
     const BlendArgs& b = a.b;
@@ -962,8 +987,9 @@ __global__ __launch_bounds__(256) void k_count_pairs(RenderArgs a, unsigned long
         for (uint32_t k = range.x; k < range.y; ++k) {
             const uint32_t g = a.list[k];
             if (g >= a.n) continue;
-            const float4* sp = reinterpret_cast<const float4*>(a.splats + (size_t)g * GS_SPLAT_STRIDE);
-            const Staged rec = stage_record(sp[0], sp[1], sp[2], x0, y0);
+            float4 r0, r1, r2;
+            load_record<H16>(a.splats, g, r0, r1, r2);
+            const Staged rec = stage_record(r0, r1, r2, x0, y0);
             const Pair p = eval_pair(fx, fy, rec.g0, rec.g1, b.alpha_max);
             ++ev;
             if (p.alpha < b.alpha_min) continue;
@@ -987,9 +1013,9 @@ __global__ void k_zero_i64(unsigned long long* p, int n) {
 }
 
 inline int render_common_checks(const gs_camera* cams, int32_t views, const gs_settings* set,
-                                const uint32_t* ranges, const float* splats) {
+                                const uint32_t* ranges, const float* splats, bool h16 = false) {
     if (!views_ok(cams, views) || !set || !ranges) return GS_EINVAL;
-    if (!aligned16(splats) || !aligned16(ranges)) return GS_EALIGN;
+    if (!(h16 ? aligned8(splats) : aligned16(splats)) || !aligned16(ranges)) return GS_EALIGN;
     return GS_OK;
 }
 
@@ -1013,7 +1039,9 @@ namespace gs {
 namespace {
 
 // Forward blend, its tile schedules and, when a.loss_mode != 0, the fused loss.
-int render_fwd_impl(const gs_camera* cam, RenderArgs& a, int32_t* tile_order, double* loss_dev, hipStream_t s) {
+int render_fwd_impl(const gs_camera* cam, RenderArgs& a, int32_t* tile_order, double* loss_dev, hipStream_t s,
+                    bool h16) {
+    const auto fwd = h16 ? k_render_fwd<true> : k_render_fwd<false>;
     const int views = a.b.views;
     const int ntiles = views * tiles_x(cam) * tiles_y(cam);
     if (tile_order && ntiles <= kOrderMaxTiles) {
@@ -1028,11 +1056,11 @@ int render_fwd_impl(const gs_camera* cam, RenderArgs& a, int32_t* tile_order, do
                                ntiles, nullptr, nullptr);
         a.sched = fwd_order;
         a.work = bwd_order;
-        hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam, views)), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL(fwd, dim3(render_grid(cam, views)), dim3(kBlock), 0, s, a);
         hipLaunchKernelGGL(k_tile_order<false>, dim3(1), dim3(kOrderThreads), 0, s, nullptr, bwd_order, bwd_order, ntiles,
                            a.loss_part, loss_dev);
     } else {
-        hipLaunchKernelGGL(k_render_fwd, dim3(render_grid(cam, views)), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL(fwd, dim3(render_grid(cam, views)), dim3(kBlock), 0, s, a);
         if (tile_order)  // too many tiles for the one-block sort: image order
             hipLaunchKernelGGL(k_iota, dim3((2 * ntiles + 255) / 256), dim3(256), 0, s, tile_order, ntiles);
         if (a.loss_mode)
@@ -1044,8 +1072,8 @@ int render_fwd_impl(const gs_camera* cam, RenderArgs& a, int32_t* tile_order, do
 // n: Gaussians per view; the splat records are [views, n, 12] and list entries index them.
 int fwd_args(const gs_camera* cam, int32_t views, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
              const uint32_t* point_list, const float* splats, float* image, float* final_T, int32_t* n_contrib,
-             uint8_t* contrib, RenderArgs& a) {
-    int rc = render_common_checks(cam, views, set, tile_ranges, splats);
+             uint8_t* contrib, RenderArgs& a, bool h16) {
+    int rc = render_common_checks(cam, views, set, tile_ranges, splats, h16);
     if (rc) return rc;
     if (n < 0 || !image || !final_T || !n_contrib) return GS_EINVAL;
     if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
@@ -1068,31 +1096,31 @@ int render_fwd_loss_impl(const gs_camera* cams, int32_t views, const gs_settings
                          const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats, float* image,
                          float* final_T, int32_t* n_contrib, uint8_t* contrib, int32_t* tile_order,
                          int32_t loss_mode, const float* target, float* dL_dimage, double* loss_dev,
-                         float* grad2d_clear, void* stream) {
+                         float* grad2d_clear, void* stream, bool h16 = false) {
     RenderArgs a;
     const int rc = fwd_args(cams, views, set, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
-                            a);
+                            a, h16);
     if (rc) return rc;
     if (grad2d_clear && !aligned16(grad2d_clear)) return GS_EALIGN;
     if (grad2d_clear && n > 0) {
         a.clear = reinterpret_cast<float4*>(grad2d_clear);
         a.clear4 = (size_t)a.n * GS_GRAD2D_STRIDE / 4;
     }
-    if (loss_mode == 0) return render_fwd_impl(cams, a, tile_order, nullptr, as_stream(stream));
+    if (loss_mode == 0) return render_fwd_impl(cams, a, tile_order, nullptr, as_stream(stream), h16);
     if (loss_mode != 1 && loss_mode != 2) return GS_EINVAL;
     if (!target || !dL_dimage || !loss_dev) return GS_EINVAL;
     a.loss_mode = loss_mode;
     a.target = target;
     a.dL_out = dL_dimage;
     a.loss_part = loss_dev + 1;
-    return render_fwd_impl(cams, a, tile_order, loss_dev, as_stream(stream));
+    return render_fwd_impl(cams, a, tile_order, loss_dev, as_stream(stream), h16);
 }
 
 int render_bwd_impl(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                     const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
                     const float* final_T, const int32_t* n_contrib, const uint8_t* contrib, const int32_t* tile_order,
-                    const float* dL_dimage, float* grad2d, int32_t accumulate, void* stream) {
-    int rc = render_common_checks(cams, views, set, tile_ranges, splats);
+                    const float* dL_dimage, float* grad2d, int32_t accumulate, void* stream, bool h16 = false) {
+    int rc = render_common_checks(cams, views, set, tile_ranges, splats, h16);
     if (rc) return rc;
     if (n < 0 || !final_T || !n_contrib || !dL_dimage) return GS_EINVAL;
     if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
@@ -1114,17 +1142,19 @@ int render_bwd_impl(const gs_camera* cams, int32_t views, const gs_settings* set
     a.contrib = const_cast<uint8_t*>(contrib);
     a.dL_dimage = dL_dimage; a.grad2d = grad2d;
     a.sched = tile_order;
+    const auto bwd2 = h16 ? k_render_bwd<2, true> : k_render_bwd<2, false>;
+    const auto bwd4 = h16 ? k_render_bwd<4, true> : k_render_bwd<4, false>;
     if (views * tiles_x(cams) * tiles_y(cams) < kBwdSplitBelow)
-        hipLaunchKernelGGL(k_render_bwd<2>, dim3(2 * render_grid(cams, views)), dim3(64), 0, s, a);
+        hipLaunchKernelGGL(bwd2, dim3(2 * render_grid(cams, views)), dim3(64), 0, s, a);
     else
-        hipLaunchKernelGGL(k_render_bwd<4>, dim3(render_grid(cams, views)), dim3(64), 0, s, a);
+        hipLaunchKernelGGL(bwd4, dim3(render_grid(cams, views)), dim3(64), 0, s, a);
     return launch_status();
 }
 
 int count_pairs_impl(const gs_camera* cams, int32_t views, const gs_settings* set, int32_t n,
                      const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats, int64_t* counts,
-                     int32_t* evaluated_px, void* stream) {
-    int rc = render_common_checks(cams, views, set, tile_ranges, splats);
+                     int32_t* evaluated_px, void* stream, bool h16 = false) {
+    int rc = render_common_checks(cams, views, set, tile_ranges, splats, h16);
     if (rc) return rc;
     if (!counts || n < 0) return GS_EINVAL;
     if ((int64_t)views * n > (int64_t)INT32_MAX) return GS_ECAPACITY;
@@ -1135,8 +1165,8 @@ int count_pairs_impl(const gs_camera* cams, int32_t views, const gs_settings* se
     a.ranges = tile_ranges; a.list = point_list; a.splats = splats;
     auto* c = reinterpret_cast<unsigned long long*>(counts);
     hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(64), 0, s, c, 3);
-    hipLaunchKernelGGL(k_count_pairs, dim3(tiles_x(cams), tiles_y(cams), views), dim3(256), 0, s, a, c,
-                       evaluated_px);
+    const auto count = h16 ? k_count_pairs<true> : k_count_pairs<false>;
+    hipLaunchKernelGGL(count, dim3(tiles_x(cams), tiles_y(cams), views), dim3(256), 0, s, a, c, evaluated_px);
     return launch_status();
 }
 
@@ -1206,4 +1236,28 @@ extern "C" int gs_count_pairs_views(const gs_camera* cams, int32_t views, const 
                                     const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats,
                                     int64_t* counts, int32_t* evaluated_px, void* stream) {
     return count_pairs_impl(cams, views, set, n, tile_ranges, point_list, splats, counts, evaluated_px, stream);
+}
+
+// 16-bit splat records (gs_preprocess_h16): the single-view forward, backward and pair count.
+extern "C" int gs_render_fwd_h16(const gs_camera* cam, const gs_settings* set, int32_t n,
+                                 const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats16,
+                                 float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
+                                 int32_t* tile_order, float* grad2d_clear, void* stream) {
+    return render_fwd_loss_impl(cam, 1, set, n, tile_ranges, point_list, splats16, image, final_T, n_contrib,
+                                contrib, tile_order, 0, nullptr, nullptr, nullptr, grad2d_clear, stream, true);
+}
+
+extern "C" int gs_render_bwd_h16(const gs_camera* cam, const gs_settings* set, int32_t n,
+                                 const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats16,
+                                 const float* final_T, const int32_t* n_contrib, const uint8_t* contrib,
+                                 const int32_t* tile_order, const float* dL_dimage, float* grad2d, int32_t accumulate,
+                                 void* stream) {
+    return render_bwd_impl(cam, 1, set, n, tile_ranges, point_list, splats16, final_T, n_contrib, contrib,
+                           tile_order, dL_dimage, grad2d, accumulate, stream, true);
+}
+
+extern "C" int gs_count_pairs_h16(const gs_camera* cam, const gs_settings* set, int32_t n,
+                                  const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats16,
+                                  int64_t* counts, int32_t* evaluated_px, void* stream) {
+    return count_pairs_impl(cam, 1, set, n, tile_ranges, point_list, splats16, counts, evaluated_px, stream, true);
 }

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(PKG, "libgs.so")
 TILE = 16
 SPLAT_STRIDE = 12
 GRAD2D_STRIDE = 12
+SPLAT16_STRIDE = 6  # 4-byte words per 16-bit splat record (24 bytes)
 
 
 class GsError(RuntimeError):
@@ -66,7 +67,8 @@ SYMBOLS = ["gs_error_string", "gs_version", "gs_tile_grid", "gs_preprocess", "gs
            "gs_adam_step", "gs_count_pairs", "gs_densify_workspace_size", "gs_densify", "gs_opacity_reset",
            "gs_preprocess_views", "gs_bin_workspace_size_views", "gs_bin_sort_views", "gs_render_fwd_views",
            "gs_render_fwd_loss_views", "gs_render_bwd_views", "gs_preprocess_bwd_views",
-           "gs_preprocess_bwd_adam_views", "gs_count_pairs_views", "gs_count_nonfinite"]
+           "gs_preprocess_bwd_adam_views", "gs_count_pairs_views", "gs_count_nonfinite",
+           "gs_preprocess_h16", "gs_render_fwd_h16", "gs_render_bwd_h16", "gs_count_pairs_h16"]
 MAX_VIEWS = 8
 PARAM_ORDER = ("means", "log_scales", "quats", "opacity_logits", "sh")
 
@@ -124,6 +126,10 @@ def load_library(path=LIB_PATH):
                                                  [_vp] * 7 + [_vp])
     lib.gs_count_pairs_views.argtypes = V + [P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.gs_count_nonfinite.argtypes = [_vp, _i64, _vp, _vp]
+    lib.gs_preprocess_h16.argtypes = [P(GsCamera), P(GsSettings), _i32, _i32] + [_vp] * 11 + [_vp]
+    lib.gs_render_fwd_h16.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 9 + [_vp]
+    lib.gs_render_bwd_h16.argtypes = [P(GsCamera), P(GsSettings), _i32] + [_vp] * 9 + [_i32, _vp]
+    lib.gs_count_pairs_h16.argtypes = [P(GsCamera), P(GsSettings), _i32, _vp, _vp, _vp, _vp, _vp, _vp]
     for name in SYMBOLS:
         if name not in ("gs_error_string",):
             getattr(lib, name).restype = C.c_int
@@ -220,6 +226,19 @@ def gs_preprocess_colorjac(cam, settings, sh_degree, means, log_scales, quats, o
     _check(rc, "gs_preprocess_colorjac")
 
 
+def gs_preprocess_h16(cam, settings, sh_degree, means, log_scales, quats, opacity_logits, sh,
+                      splats16, depth, rect, tiles_touched, clamp_mask, colorjac=None):
+    """gs_preprocess writing 16-bit splat records (splats16 [n, 6] float32 storage); colorjac optional."""
+    f32, n = torch.float32, means.shape[0]
+    rc = load_library().gs_preprocess_h16(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, sh_degree,
+        _p(means, f32, "means"), _p(log_scales, f32, "log_scales"), _p(quats, f32, "quats"),
+        _p(opacity_logits, f32, "opacity_logits"), _p(sh, f32, "sh"), _p(splats16, f32, "splats16"),
+        _p(depth, f32, "depth"), _p(rect, torch.int16, "rect"), _p(tiles_touched, torch.int32, "tiles_touched"),
+        _p(clamp_mask, torch.uint8, "clamp_mask"), _p(colorjac, f32, "colorjac"), _stream())
+    _check(rc, "gs_preprocess_h16")
+
+
 def gs_bin_workspace_size(n, cam, key_capacity):
     b = C.c_size_t()
     _check(load_library().gs_bin_workspace_size(n, C.byref(camera_struct(cam)), key_capacity, C.byref(b)),
@@ -291,6 +310,17 @@ def gs_render_fwd(cam, settings, n, tile_ranges, point_list, splats, image, fina
     _check(rc, "gs_render_fwd")
 
 
+def gs_render_fwd_h16(cam, settings, n, tile_ranges, point_list, splats16, image, final_T, n_contrib, contrib,
+                      tile_order=None, grad2d_clear=None):
+    rc = load_library().gs_render_fwd_h16(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
+        _p(point_list, torch.int32, "point_list"), _p(splats16, torch.float32, "splats16"),
+        _p(image, torch.float32, "image"), _p(final_T, torch.float32, "final_T"),
+        _p(n_contrib, torch.int32, "n_contrib"), _p(contrib, torch.uint8, "contrib"),
+        _p(tile_order, torch.int32, "tile_order"), _p(grad2d_clear, torch.float32, "grad2d_clear"), _stream())
+    _check(rc, "gs_render_fwd_h16")
+
+
 def gs_render_fwd_loss(cam, settings, n, tile_ranges, point_list, splats, image, final_T, n_contrib, contrib,
                        tile_order, mode, target, dL_dimage, loss_dev, grad2d_clear=None):
     """gs_render_fwd with the L1/L2 image loss fused in (loss_dev [1 + tiles] float64; loss_dev[0] = loss)."""
@@ -319,6 +349,18 @@ def gs_render_bwd(cam, settings, n, tile_ranges, point_list, splats, final_T, n_
         _p(dL_dimage, torch.float32, "dL_dimage"),
         _p(grad2d, torch.float32, "grad2d"), 1 if accumulate else 0, _stream())
     _check(rc, "gs_render_bwd")
+
+
+def gs_render_bwd_h16(cam, settings, n, tile_ranges, point_list, splats16, final_T, n_contrib, contrib, dL_dimage,
+                      grad2d, accumulate=False, tile_order=None):
+    rc = load_library().gs_render_bwd_h16(
+        C.byref(camera_struct(cam)), C.byref(settings.struct()), n, _p(tile_ranges, torch.int32, "tile_ranges"),
+        _p(point_list, torch.int32, "point_list"), _p(splats16, torch.float32, "splats16"),
+        _p(final_T, torch.float32, "final_T"), _p(n_contrib, torch.int32, "n_contrib"),
+        _p(contrib, torch.uint8, "contrib"), _p(tile_order, torch.int32, "tile_order"),
+        _p(dL_dimage, torch.float32, "dL_dimage"),
+        _p(grad2d, torch.float32, "grad2d"), 1 if accumulate else 0, _stream())
+    _check(rc, "gs_render_bwd_h16")
 
 
 def gs_preprocess_bwd(cam, settings, sh_degree, means, log_scales, quats, opacity_logits, sh, tiles_touched,
@@ -426,6 +468,14 @@ def gs_count_pairs(cam, settings, n, tile_ranges, point_list, splats, counts, ev
                                        _p(splats, torch.float32), _p(counts, torch.int64),
                                        _p(evaluated_px, torch.int32, "evaluated_px"), _stream())
     _check(rc, "gs_count_pairs")
+
+
+def gs_count_pairs_h16(cam, settings, n, tile_ranges, point_list, splats16, counts, evaluated_px=None):
+    rc = load_library().gs_count_pairs_h16(C.byref(camera_struct(cam)), C.byref(settings.struct()), n,
+                                           _p(tile_ranges, torch.int32), _p(point_list, torch.int32),
+                                           _p(splats16, torch.float32), _p(counts, torch.int64),
+                                           _p(evaluated_px, torch.int32, "evaluated_px"), _stream())
+    _check(rc, "gs_count_pairs_h16")
 
 
 def gs_count_nonfinite(x, out=None):
@@ -704,10 +754,13 @@ class Rasterizer:
     debug=True checks the parameters before the forward, and the image and the
     gradients after each pass, for NaN and infinite values (gs_count_nonfinite),
     raising GsError with the names of the tensors that hold them.
+    record16=True keeps 16-bit splat records (gs_preprocess_h16 and the _h16
+    blends): the blends gather 24 bytes per list entry instead of 48, and compute
+    with the conic factor, opacity and colour rounded to binary16.
     """
 
     def __init__(self, cam, n, sh_degree, settings=None, key_capacity=None, device="cuda", debug=False,
-                 colorjac=True):
+                 colorjac=True, record16=False):
         load_library()
         self.cam, self.n, self.deg = cam, int(n), int(sh_degree)
         self.debug = bool(debug)
@@ -716,7 +769,9 @@ class Rasterizer:
         dev, n = self.device, self.n
         self.tiles_x, self.tiles_y = gs_tile_grid(cam)
         self.ntiles = self.tiles_x * self.tiles_y
-        self.splats = torch.empty((n, SPLAT_STRIDE), dtype=torch.float32, device=dev)
+        self.record16 = bool(record16)
+        self.splats = torch.empty((n, SPLAT16_STRIDE if self.record16 else SPLAT_STRIDE), dtype=torch.float32,
+                                  device=dev)
         self.depth = torch.empty(n, dtype=torch.float32, device=dev)
         self.rect = torch.empty((n, 4), dtype=torch.int16, device=dev)
         self.tiles_touched = torch.empty(n, dtype=torch.int32, device=dev)
@@ -746,7 +801,11 @@ class Rasterizer:
         self.workspace = self.workspace[off:off + ws]
 
     def preprocess(self, p):
-        if self.colorjac is not None:
+        if self.record16:
+            gs_preprocess_h16(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
+                              p["opacity_logits"], p["sh"], self.splats, self.depth, self.rect,
+                              self.tiles_touched, self.clamp, self.colorjac)
+        elif self.colorjac is not None:
             gs_preprocess_colorjac(self.cam, self.settings, self.deg, p["means"], p["log_scales"], p["quats"],
                                    p["opacity_logits"], p["sh"], self.splats, self.depth, self.rect,
                                    self.tiles_touched, self.clamp, self.colorjac)
@@ -762,13 +821,15 @@ class Rasterizer:
     def render(self, clear_grad2d=False):
         """Forward blend; with clear_grad2d the 2D-gradient buffer is zeroed by the same kernel, for
         backward_2d(..., accumulate=True)."""
-        gs_render_fwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, self.image,
-                      self.final_T, self.n_contrib, self.contrib, self.tile_order,
-                      self.grad2d if clear_grad2d else None)
+        fwd = gs_render_fwd_h16 if self.record16 else gs_render_fwd
+        fwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, self.image,
+            self.final_T, self.n_contrib, self.contrib, self.tile_order, self.grad2d if clear_grad2d else None)
 
     def render_loss(self, target, mode, dL_dimage, loss_dev, clear_grad2d=True):
         """Forward blend with the fused image loss; with clear_grad2d the 2D-gradient buffer is zeroed too,
         for backward_2d(..., accumulate=True).  loss_dev: [1 + ntiles] float64."""
+        if self.record16:
+            raise GsError("the fused-loss forward reads float32 splat records (record16=False)")
         gs_render_fwd_loss(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats,
                            self.image, self.final_T, self.n_contrib, self.contrib, self.tile_order, mode, target,
                            dL_dimage, loss_dev, self.grad2d if clear_grad2d else None)
@@ -791,9 +852,9 @@ class Rasterizer:
         return self.image
 
     def backward_2d(self, dL_dimage, accumulate=False):
-        gs_render_bwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats,
-                      self.final_T, self.n_contrib, self.contrib, dL_dimage, self.grad2d, accumulate,
-                      self.tile_order[1])
+        bwd = gs_render_bwd_h16 if self.record16 else gs_render_bwd
+        bwd(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, self.final_T,
+            self.n_contrib, self.contrib, dL_dimage, self.grad2d, accumulate, self.tile_order[1])
         return self.grad2d
 
     def backward_3d(self, p, out):
@@ -823,7 +884,8 @@ class Rasterizer:
         int32 evaluated count of each pixel."""
         c = torch.zeros(3, dtype=torch.int64, device=self.device)
         ev = torch.empty_like(self.n_contrib) if per_pixel else None
-        gs_count_pairs(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, c, ev)
+        count = gs_count_pairs_h16 if self.record16 else gs_count_pairs
+        count(self.cam, self.settings, self.n, self.tile_ranges, self.point_list, self.splats, c, ev)
         return (c, ev) if per_pixel else c
 
 

@@ -46,6 +46,7 @@ extern "C" {
 #define GS_TILE 16
 #define GS_SPLAT_STRIDE 12  /* floats per projected-Gaussian record */
 #define GS_GRAD2D_STRIDE 12 /* floats per 2D-gradient record */
+#define GS_SPLAT16_STRIDE 6 /* 4-byte words per 16-bit projected-Gaussian record (24 bytes) */
 #define GS_MAX_SH_DEGREE 3
 #define GS_MAX_VIEWS 8      /* views one batched call renders */
 
@@ -468,6 +469,50 @@ int gs_opacity_reset(int32_t n, float factor, float* opacity_logits, float* exp_
 int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
                    const uint32_t* point_list, const float* splats, int64_t* counts, int32_t* evaluated_px,
                    void* stream);
+
+/*
+ * 16-bit splat records ([P3] section 5: some intermediate values stored as
+ * 16-bit floats to save memory traffic; section 7: FP16 on the rendering path,
+ * gradient sums in FP32).  The same calls as gs_preprocess / gs_render_fwd /
+ * gs_render_bwd / gs_count_pairs with splats16 [n,6] in place of splats
+ * [n,12]: a 24-byte record per Gaussian that a blend gathers per list entry,
+ * half the 48 bytes of the float32 record.  Words 0-1: u, v (the 2D mean,
+ * float32, no residual); words 2-5: binary16 pairs, low half first: (L00, L10),
+ * (L11, opacity), (r, g), (b, 0), each the binary16 number nearest to the
+ * float32 value gs_preprocess stores (ties to even).  Culled Gaussians have an
+ * all-zero record.  splats16 must be 8-byte aligned (GS_EALIGN otherwise).
+ *
+ * Precision contract: the blends compute in float32 from the record's values,
+ * so their results are those of the float32 path for the Gaussians the record
+ * represents: conic = L L^T 2 ln 2 from the rounded factor, opacity and colour
+ * rounded.  Against the float32 record each alpha moves by a relative amount
+ * of order 2^-11 (1 + condition number of the conic) ln(opacity / alpha_min),
+ * which can flip skip and stop decisions of pairs at the thresholds.  The 2D
+ * gradients are those at the rounded values; gs_preprocess_bwd and
+ * gs_preprocess_bwd_colorjac take them as they take the float32 path's.
+ * Binning is unchanged: rect, tiles_touched and depth are those of
+ * gs_preprocess, bit for bit.
+ *
+ * gs_preprocess_h16: colorjac is optional here (NULL: not written); given, it
+ * is gs_preprocess_colorjac's.
+ */
+int gs_preprocess_h16(const gs_camera* cam, const gs_settings* set, int32_t n, int32_t sh_degree,
+                      const float* means, const float* log_scales, const float* quats,
+                      const float* opacity_logits, const float* sh,
+                      float* splats16, float* depth, int16_t* rect, int32_t* tiles_touched,
+                      uint8_t* clamp_mask, float* colorjac, void* stream);
+int gs_render_fwd_h16(const gs_camera* cam, const gs_settings* set, int32_t n,
+                      const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats16,
+                      float* image, float* final_T, int32_t* n_contrib, uint8_t* contrib,
+                      int32_t* tile_order, float* grad2d_clear, void* stream);
+int gs_render_bwd_h16(const gs_camera* cam, const gs_settings* set, int32_t n,
+                      const uint32_t* tile_ranges, const uint32_t* point_list, const float* splats16,
+                      const float* final_T, const int32_t* n_contrib, const uint8_t* contrib,
+                      const int32_t* tile_order, const float* dL_dimage, float* grad2d, int32_t accumulate,
+                      void* stream);
+int gs_count_pairs_h16(const gs_camera* cam, const gs_settings* set, int32_t n, const uint32_t* tile_ranges,
+                       const uint32_t* point_list, const float* splats16, int64_t* counts, int32_t* evaluated_px,
+                       void* stream);
 
 /*
  * gs_count_nonfinite -- *out (device int64, overwritten) = the number of NaN
