@@ -48,6 +48,7 @@ FLOPS_BWD_BLENDED, FLOPS_BWD_SKIPPED = 72, 16
 RASTER_WORKLOADS = ("clusters1m", "tiny", "ball100k", "plane3m")
 WORKLOADS = RASTER_WORKLOADS + ("train1m",)
 STAGES = ("preprocess", "bin_sort", "render_fwd", "render_bwd", "preprocess_bwd")
+EXTRAS = ("record16", "train", "densify", "views")
 
 
 def parse():
@@ -57,13 +58,20 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="only the rasterizer line: no training step, densify or views fields")
+                    help="only the rasterizer line: no record16, training step, densify or views fields")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="comma-separated extra fields of the clusters1m line, from " + ", ".join(EXTRAS) +
+                         " (densify and views need train)")
     ap.add_argument("--views", type=int, default=4,
                     help="views of the batched training step measured beside the main line (1 skips it)")
     ap.add_argument("--workload", default="clusters1m", choices=WORKLOADS,
                     help="clusters1m (the default line: 1M Gaussians at 1080p) or tiny / ball100k / plane3m: the "
                          "rasterizer's fwd+bwd on that scene; train1m: the training step as the line")
-    return ap.parse_args()
+    args = ap.parse_args()
+    args.extra_set = set() if args.no_extras else {e for e in args.extras.split(",") if e}
+    if args.extra_set - set(EXTRAS):
+        ap.error(f"unknown extras: {sorted(args.extra_set - set(EXTRAS))}")
+    return args
 
 
 def sha_of(path):
@@ -621,16 +629,19 @@ def main():
         print(json.dumps(line))
         return
     line, sc = raster_line(args.workload, args.steps, args.warmup, peaks)
-    if args.workload == "clusters1m" and not args.no_extras:
+    extras = args.extra_set
+    if args.workload == "clusters1m" and "record16" in extras:
         print("# 16-bit splat records ...", file=sys.stderr, flush=True)
         line["record16"] = record16_measure(sc, args.steps, args.warmup, line)
+    if args.workload == "clusters1m" and "train" in extras:
         print("# training step ...", file=sys.stderr, flush=True)
         tr, st = train_measure(args.steps, args.warmup)
         line["train1m"] = tr
-        line["densify"] = densify_measure(st, max(3, min(args.steps, 10)))
+        if "densify" in extras:
+            line["densify"] = densify_measure(st, max(3, min(args.steps, 10)))
         del st
         torch.cuda.empty_cache()
-        if args.views > 1:
+        if args.views > 1 and "views" in extras:
             print("# batched views ...", file=sys.stderr, flush=True)
             line["views"] = views_measure(args.views, args.steps, args.warmup)
     if not args.no_cpu_baseline and args.workload != "plane3m":

@@ -28,6 +28,12 @@ def test_unknown_workload_is_refused():
     assert "invalid choice" in r.stderr
 
 
+def test_unknown_extra_is_refused():
+    r = _run("--extras", "record16,no-such-field")
+    assert r.returncode == 2
+    assert "unknown extras" in r.stderr
+
+
 def test_workloads_are_the_scene_generators():
     from differentiable_gaussian_splatting_dgs_amd import scenes
     assert set(bench.WORKLOADS) == set(scenes.WORKLOADS)
