@@ -272,6 +272,7 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
         __syncthreads();
         const int cnt = wave_done ? 0 : compact(s_mask, s_list[wave], wave, lane);
         const int base = (int)(start - range.x);
+        int lslot = -1;  // the batch's last blended slot (walked in slot order): last = base + lslot + 1
         for (int j = 0; j < cnt; j += 2) {
             const bool has2 = j + 1 < cnt;
             const int ea = s_list[wave][j];
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
                 C1 = __builtin_fmaf(w, ga1.w, C1);
                 C2 = __builtin_fmaf(w, cba, C2);
                 T = Tb;
-                last = ok ? base + ea + 1 : last;
+                lslot = ok ? ea : lslot;
                 if (ok) fb[4 * ea] = 1;  // lanes that blend all store the same byte
             }
             {
@@ -308,11 +309,12 @@ __global__ __launch_bounds__(kBlock) void k_render_fwd(RenderArgs a) {
                 C1 = __builtin_fmaf(w, gb1.w, C1);
                 C2 = __builtin_fmaf(w, cbb, C2);
                 T = Tb;
-                last = ok ? base + eb + 1 : last;
+                lslot = ok ? eb : lslot;
                 if (ok) fb[4 * eb] = 1;
             }
             if ((j & 2) && __ballot(!done) == 0) break;  // checked every other pair
         }
+        if (lslot >= 0) last = base + lslot + 1;
         wave_done = __ballot(!done) == 0;
         if (__syncthreads_count(done ? 1 : 0) == kBlock) break;
     }
