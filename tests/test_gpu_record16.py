@@ -23,7 +23,7 @@ from gpu_cases import CASES, PARAM_KEYS, guard_2d, log, rel_l2, to_dev
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["tiny", "random_sh1", "random_sh2", "tiles1023", "tiles1024", "ball100k", "clusters1m"]
+NAMES = ["tiny", "random_sh1", "random_sh2", "tiles1023", "tiles1024", "ball100k", "clusters1m", "plane3m"]
 _CACHE = {}
 S2 = 0.5 / np.log(2.0)  # s^2: L L^T = s^2 conic
 
