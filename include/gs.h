@@ -481,6 +481,11 @@ int gs_count_pairs(const gs_camera* cam, const gs_settings* set, int32_t n, cons
  * (L11, opacity), (r, g), (b, 0), each the binary16 number nearest to the
  * float32 value gs_preprocess stores (ties to even).  Culled Gaussians have an
  * all-zero record.  splats16 must be 8-byte aligned (GS_EALIGN otherwise).
+ * Range: binary16 holds magnitudes up to 65504 and, below 2^-14, only fixed
+ * steps of 2^-24.  L00 and L11 stay in the normal range for any Gaussian from
+ * the low-pass dilation's width up to about 10^4 pixels; L10, near zero for an
+ * axis-aligned one, then has an absolute step of 2^-24.  A colour above 65504
+ * (extreme SH coefficients) is stored as infinity.
  *
  * Precision contract: the blends compute in float32 from the record's values,
  * so their results are those of the float32 path for the Gaussians the record

@@ -191,3 +191,30 @@ def test_record16_argument_checks():
         r.render_loss(torch.zeros_like(r.image), "l1", torch.zeros_like(r.image),
                       torch.zeros(1 + r.ntiles, dtype=torch.float64, device="cuda"))
     torch.cuda.synchronize()
+
+
+def test_record16_empty_and_all_culled():
+    """No Gaussians, and Gaussians that are all culled: empty lists, the background, zero gradients."""
+    import torch
+    from differentiable_gaussian_splatting_dgs_amd import gs, scenes
+    cam = scenes.Camera.identity(40, 24, 30.0)
+    r = gs.Rasterizer(cam, 0, 0, key_capacity=16, record16=True)
+    p = {k: torch.zeros((0,) + s, device="cuda") for k, s in
+         dict(means=(3,), log_scales=(3,), quats=(4,), opacity_logits=(), sh=(1, 3)).items()}
+    r.forward(p)
+    torch.cuda.synchronize()
+    assert int(r.num_keys.item()) == 0 and int(r.overflow.item()) == 0
+    assert torch.all(r.image == 0) and torch.all(r.final_T == 1) and torch.all(r.n_contrib == 0)
+    sc = scenes.random_small(31, n=100, width=33, height=17)
+    sc.means[:50, 2] = 0.1          # inside the near plane
+    sc.means[50:, 2] = -3.0         # behind the camera
+    p = to_dev(sc.params())
+    r = gs.Rasterizer(sc.cam, sc.n, sc.sh_degree, record16=True)
+    r.forward(p)
+    g3 = r.backward(p, torch.ones_like(r.image))
+    torch.cuda.synchronize()
+    assert int(r.num_keys.item()) == 0
+    assert torch.all(r.image == 0)
+    assert torch.all(r.splats.view(torch.int32) == 0)
+    for k, v in g3.items():
+        assert torch.all(v == 0), k
